@@ -1,0 +1,426 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test checks the oracle against something other than itself: a library
+routine on the CPU, a closed form, a brute-force formulation written
+differently, a hand-worked fixture, or an exhaustive search.  Together they
+are chosen so that a dropped term, a wrong sign, a transposed operand or a
+wrong index in the oracle fails at least one of them.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import WORKLOADS, make_inputs, scaled
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 rounding
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_matches_torch_on_float32_values():
+    rng = _rng(1)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+        rng.standard_normal(2000) * 1e-39,  # float32 subnormals
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38]),
+    ]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(vals.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_round_bf16_ties_and_overflow():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties go to the even one
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert O.round_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -30)) == -(1.0 + 2.0 ** -7)
+    big = (2.0 - 2.0 ** -7) * 2.0 ** 127  # largest finite bfloat16
+    assert O.round_bf16(big) == big
+    assert np.isinf(O.round_bf16((2.0 - 2.0 ** -8) * 2.0 ** 127))
+    assert np.isnan(O.round_bf16(np.nan))
+    # fp64 value just above a float32 tie: direct rounding goes up
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -40
+    assert O.round_bf16(x) == 1.0 + 2.0 ** -7
+
+
+# ---------------------------------------------------------------------------
+# projection and depthwise branches
+# ---------------------------------------------------------------------------
+
+def test_qkv_projection_is_a_plain_matmul():
+    rng = _rng(2)
+    x = rng.standard_normal((2, 5, 4))
+    w = rng.standard_normal((4, 12))
+    got = O.qkv_projection(x, w)
+    for b in range(2):
+        for n in range(5):
+            for c in range(12):
+                ref = sum(x[b, n, i] * w[i, c] for i in range(4))
+                assert abs(got[b, n, c] - ref) < 1e-12
+
+
+@pytest.mark.parametrize("k", [3, 5, 7])
+def test_dwconv_matches_torch_conv2d(k):
+    rng = _rng(3 + k)
+    B, gh, gw, Ch = 2, 9, 13, 6
+    t = rng.standard_normal((B, gh * gw, Ch))
+    w = rng.standard_normal((Ch, k, k))
+    got = O.dwconv_same(t, w, gh, gw)
+    inp = torch.from_numpy(t.reshape(B, gh, gw, Ch)).permute(0, 3, 1, 2)
+    ref = torch.nn.functional.conv2d(inp, torch.from_numpy(w)[:, None],
+                                     padding=(k - 1) // 2, groups=Ch)
+    ref = ref.permute(0, 2, 3, 1).reshape(B, gh * gw, Ch).numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_multiscale_delta_kernels_give_scaled_identity():
+    rng = _rng(4)
+    B, gh, gw, Ch = 1, 6, 7, 5
+    t = rng.standard_normal((B, gh * gw, Ch))
+    d3 = np.zeros((Ch, 3, 3)); d3[:, 1, 1] = 1.0
+    d5 = np.zeros((Ch, 5, 5)); d5[:, 2, 2] = 1.0
+    got = O.multiscale_branches(t, [d3, d5], gh, gw)
+    np.testing.assert_allclose(got, 3.0 * t, rtol=0, atol=1e-14)
+    # a shifted delta moves every channel by one column, with zero fill
+    s3 = np.zeros((Ch, 3, 3)); s3[:, 1, 2] = 1.0
+    got = O.dwconv_same(t, s3, gh, gw).reshape(B, gh, gw, Ch)
+    img = t.reshape(B, gh, gw, Ch)
+    np.testing.assert_array_equal(got[:, :, :-1], img[:, :, 1:])
+    np.testing.assert_array_equal(got[:, :, -1], 0.0)
+
+
+# ---------------------------------------------------------------------------
+# global linear attention
+# ---------------------------------------------------------------------------
+
+def _brute_linear(qh, kh, vh, heads):
+    """sum_m (phi(q_n).phi(k_m)) v_m / sum_m phi(q_n).phi(k_m), O(N^2)."""
+    B, N, C = qh.shape
+    d = C // heads
+    out = np.zeros_like(qh)
+    for b in range(B):
+        for h in range(heads):
+            sl = slice(h * d, (h + 1) * d)
+            fq = np.maximum(qh[b, :, sl], 0)
+            fk = np.maximum(kh[b, :, sl], 0)
+            a = fq @ fk.T  # [N, N] kernel scores
+            den = a.sum(axis=1)
+            num = a @ vh[b, :, sl]
+            for n in range(N):
+                out[b, n, sl] = num[n] / den[n] if den[n] > 0 else 0.0
+    return out
+
+
+def test_linear_attention_equals_brute_force_quadratic_form():
+    rng = _rng(5)
+    B, N, H, d = 2, 37, 3, 8
+    C = H * d
+    qkvh = rng.standard_normal((B, N, 3 * C))
+    qkvh[0, 4, 0:C] = -np.abs(qkvh[0, 4, 0:C])  # a query with phi(q) = 0
+    got, Z, D = O.linear_attention(qkvh, H)
+    ref = _brute_linear(qkvh[..., :C], qkvh[..., C:2 * C], qkvh[..., 2 * C:], H)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+    assert np.all(got[0, 4] == 0.0)
+    assert Z.shape == (B, H, d, d) and D.shape == (B, H, d)
+
+
+def test_linear_attention_scale_invariance():
+    rng = _rng(6)
+    B, N, H, d = 1, 20, 2, 4
+    C = H * d
+    qkvh = rng.standard_normal((B, N, 3 * C))
+    base, _, _ = O.linear_attention(qkvh, H)
+    for lo, hi, s in [(0, C, 3.5), (C, 2 * C, 0.25)]:
+        alt = qkvh.copy()
+        alt[..., lo:hi] *= s
+        got, _, _ = O.linear_attention(alt, H)
+        np.testing.assert_allclose(got, base, rtol=1e-12, atol=1e-13)
+    # scaling V scales the output (V enters linearly, without phi)
+    alt = qkvh.copy()
+    alt[..., 2 * C:] *= -2.0
+    got, _, _ = O.linear_attention(alt, H)
+    np.testing.assert_allclose(got, -2.0 * base, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# hand-worked fixtures
+# ---------------------------------------------------------------------------
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_fixture_refine_1x3():
+    fx = _load("refine_1x3.json")
+    qkv = np.array(fx["qkv"])
+    qkvh = np.array(fx["qkv_hat"])
+    e = fx["expected"]
+    o_lin, Z, D = O.linear_attention(qkvh, 1)
+    assert abs(Z[0, 0, 0, 0] - e["Z"]) < 1e-12 and abs(D[0, 0, 0] - e["D"]) < 1e-12
+    np.testing.assert_allclose(o_lin[0, :, 0], e["o_lin"], atol=1e-12)
+    kw = dict(grid_h=1, grid_w=3, heads=1, block=1, window=3)
+    o_all = O.refine_selected(qkv, qkvh, o_lin, np.array([[0, 1, 2]]), **kw)
+    np.testing.assert_allclose(o_all[0, :, 0], e["o_all_selected"], atol=1e-12)
+    o_one = O.refine_selected(qkv, qkvh, o_lin, np.array([[1]]), **kw)
+    np.testing.assert_allclose(o_one[0, :, 0], e["o_select_block1"], atol=1e-12)
+
+
+def test_fixture_gate_2x4():
+    fx = _load("gate_2x4.json")
+    qkvh = np.array(fx["qkv_hat"])
+    m = O.gate_scores(qkvh, np.array(fx["gate_w"]), np.array(fx["gate_b"]),
+                      grid_h=2, grid_w=4, block=2, heads=2)
+    np.testing.assert_allclose(m[0], fx["expected"]["scores"], atol=1e-14)
+    assert O.select_blocks(m, 1)[0].tolist() == fx["expected"]["top1"]
+
+
+# ---------------------------------------------------------------------------
+# gate
+# ---------------------------------------------------------------------------
+
+def test_gate_zero_weights_gives_mean_sigmoid_of_bias():
+    rng = _rng(7)
+    H, d = 3, 4
+    qkvh = rng.standard_normal((2, 8 * 8, 3 * H * d))
+    b = np.array([0.3, -1.2, 2.0])
+    m = O.gate_scores(qkvh, np.zeros((H, 3 * d)), b, 8, 8, 4, H)
+    ref = np.mean(1.0 / (1.0 + np.exp(-b)))
+    np.testing.assert_allclose(m, ref, rtol=0, atol=1e-15)
+
+
+def test_gate_block_mean_is_per_block():
+    """A feature constant on each block with a one-hot weight reproduces the
+    per-block constant as the logit (block numbering and pooling window)."""
+    H, d, Bs, gh, gw = 2, 2, 2, 4, 6
+    C = H * d
+    T = (gh // Bs) * (gw // Bs)
+    vals = np.arange(T) * 0.1 - 0.2
+    qkvh = np.zeros((1, gh * gw, 3 * C))
+    for n in range(gh * gw):
+        y, x = divmod(n, gw)
+        t = (y // Bs) * (gw // Bs) + x // Bs
+        qkvh[0, n, C + 1 * d + 1] = vals[t]  # k channel 1 of head 1
+    w = np.zeros((H, 3 * d)); w[1, d + 1] = 1.0  # head 1 weights its k_1
+    m = O.gate_scores(qkvh, w, np.zeros(H), gh, gw, Bs, H)
+    ref = 0.5 * (0.5 + 1.0 / (1.0 + np.exp(-vals)))
+    np.testing.assert_allclose(m[0], ref, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def _is_valid_topk(scores, subset):
+    inside = set(subset)
+    for i in inside:
+        for j in range(len(scores)):
+            if j in inside:
+                continue
+            if not (scores[i] > scores[j] or (scores[i] == scores[j] and i < j)):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_blocks_exhaustive(seed):
+    rng = _rng(100 + seed)
+    T = 9
+    # few distinct values so ties are frequent
+    scores = rng.integers(0, 4, size=(3, T)).astype(np.float64) / 4.0
+    for k in range(T + 1):
+        sel = O.select_blocks(scores, k)
+        for b in range(3):
+            valid = [s for s in itertools.combinations(range(T), k)
+                     if _is_valid_topk(scores[b], s)]
+            assert len(valid) == 1
+            assert tuple(sel[b].tolist()) == valid[0]
+
+
+# ---------------------------------------------------------------------------
+# refinement
+# ---------------------------------------------------------------------------
+
+def _window_member(t, n, grid_w, block, window):
+    """Key token n lies in block t's window iff its row and column are each
+    within p tokens of the block's extent (Chebyshev-style distance)."""
+    p = (window - block) // 2
+    nbc = grid_w // block
+    r0, c0 = (t // nbc) * block, (t % nbc) * block
+    y, x = divmod(n, grid_w)
+    dy = max(0, r0 - y, y - (r0 + block - 1))
+    dx = max(0, c0 - x, x - (c0 + block - 1))
+    return dy <= p and dx <= p
+
+
+def _dense_refine(qkv, qkvh, o_lin, sel, gh, gw, H, Bs, w):
+    """Refinement written over the full token set with a mask per query."""
+    B, N, C3 = qkv.shape
+    C = C3 // 3
+    d = C // H
+    out = o_lin.copy()
+    for b in range(B):
+        for t in sel[b]:
+            mask = np.array([_window_member(t, n, gw, Bs, w) for n in range(N)])
+            queries = [n for n in range(N)
+                       if (n // gw) // Bs * (gw // Bs) + (n % gw) // Bs == t]
+            for h in range(H):
+                sl = slice(h * d, (h + 1) * d)
+                q = qkv[b, :, sl]
+                k = qkv[b, :, C + h * d:C + (h + 1) * d]
+                v = qkv[b, :, 2 * C + h * d:2 * C + (h + 1) * d]
+                fq = np.maximum(qkvh[b, :, sl], 0)
+                fk = np.maximum(qkvh[b, :, C + h * d:C + (h + 1) * d], 0)
+                vh = qkvh[b, :, 2 * C + h * d:2 * C + (h + 1) * d]
+                for i in queries:
+                    s = np.where(mask, k @ q[i] / math.sqrt(d), -np.inf)
+                    p = np.exp(s - s.max())
+                    loc = (p / p.sum()) @ v
+                    a = np.where(mask, fk @ fq[i], 0.0)
+                    ll = (a @ vh) / a.sum() if a.sum() > 0 else np.zeros(d)
+                    out[b, i, sl] = o_lin[b, i, sl] + loc - ll
+    return out
+
+
+@pytest.mark.parametrize("Bs,w,gh,gw", [(2, 6, 6, 8), (2, 2, 4, 6), (3, 7, 9, 6)])
+def test_refine_matches_masked_dense_form(Bs, w, gh, gw):
+    rng = _rng(8 + w)
+    B, H, d = 2, 2, 3
+    C = H * d
+    N = gh * gw
+    qkv = rng.standard_normal((B, N, 3 * C))
+    qkvh = rng.standard_normal((B, N, 3 * C))
+    o_lin, _, _ = O.linear_attention(qkvh, H)
+    T = (gh // Bs) * (gw // Bs)
+    sel = np.stack([np.sort(rng.choice(T, size=T // 2, replace=False))
+                    for _ in range(B)])
+    got = O.refine_selected(qkv, qkvh, o_lin, sel, gh, gw, H, Bs, w)
+    ref = _dense_refine(qkv, qkvh, o_lin, sel, gh, gw, H, Bs, w)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_window_bounds_against_membership():
+    for (gh, gw, Bs, w) in [(8, 12, 4, 8), (16, 16, 4, 12), (9, 9, 3, 3)]:
+        T = (gh // Bs) * (gw // Bs)
+        for t in range(T):
+            r_lo, r_hi, c_lo, c_hi = O.window_bounds(t, gh, gw, Bs, w)
+            for n in range(gh * gw):
+                y, x = divmod(n, gw)
+                inside = r_lo <= y < r_hi and c_lo <= x < c_hi
+                assert inside == _window_member(t, n, gw, Bs, w)
+
+
+def _module_kwargs(gh, gw, H, Bs, w, k):
+    return dict(grid_h=gh, grid_w=gw, heads=H, block=Bs, window=w,
+                keep_blocks=k)
+
+
+def test_keep_zero_is_pure_linear_attention():
+    wl = scaled(WORKLOADS["tiny"], keep=0.0)
+    inp = make_inputs(wl)
+    r = O.hsmla_forward(inp["x"], inp, **wl.kwargs())
+    assert r["sel"].shape == (1, 0)
+    np.testing.assert_array_equal(r["o"], r["o_lin"])
+    np.testing.assert_allclose(r["y"], r["o_lin"] @ inp["w_o"], atol=1e-13)
+
+
+def test_keep_all_with_covering_window_is_full_softmax():
+    """Z_W = Z when the window covers the grid, so the linear terms cancel
+    and the output is textbook softmax attention over raw Q, K, V."""
+    wl = scaled(WORKLOADS["tiny"], keep=1.0, window=4 + 2 * 16)
+    inp = make_inputs(wl)
+    r = O.hsmla_module(inp["x"], inp, **wl.kwargs())
+    assert r["sel"].shape == (1, wl.num_blocks)
+    qkv = torch.from_numpy(r["qkv"])
+    B, N, C3 = qkv.shape
+    C = C3 // 3
+    H, d = wl.heads, wl.head_dim
+    q, k, v = (qkv[..., s * C:(s + 1) * C].reshape(B, N, H, d).transpose(1, 2)
+               for s in range(3))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+    ref = ref.transpose(1, 2).reshape(B, N, C).numpy()
+    np.testing.assert_allclose(r["o"], ref, rtol=1e-10, atol=1e-11)
+
+
+def test_keep_all_window_equal_block_is_block_local():
+    """window = block: every block attends only to itself, and the linear
+    correction is the linear attention restricted to the block."""
+    rng = _rng(9)
+    gh, gw, Bs, H, d = 8, 8, 4, 2, 4
+    C = H * d
+    qkv = rng.standard_normal((1, gh * gw, 3 * C))
+    qkvh = rng.standard_normal((1, gh * gw, 3 * C))
+    o_lin, _, _ = O.linear_attention(qkvh, H)
+    T = 4
+    got = O.refine_selected(qkv, qkvh, o_lin, np.arange(T)[None], gh, gw, H,
+                            Bs, Bs)
+    # reference: per block, gather its tokens and apply textbook formulas
+    ref = o_lin.copy()
+    for t in range(T):
+        ys, xs = (t // 2) * 4 + np.arange(4), (t % 2) * 4 + np.arange(4)
+        ids = (ys[:, None] * gw + xs[None, :]).reshape(-1)
+        sub = qkv[:, ids]
+        subh = qkvh[:, ids]
+        qq, kk, vv = (torch.from_numpy(sub[..., s * C:(s + 1) * C])
+                      .reshape(1, 16, H, d).transpose(1, 2) for s in range(3))
+        soft = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)
+        soft = soft.transpose(1, 2).reshape(1, 16, C).numpy()
+        lin = _brute_linear(subh[..., :C], subh[..., C:2 * C], subh[..., 2 * C:], H)
+        ref[:, ids] = o_lin[:, ids] + soft - lin
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# block wrapper pieces and staging
+# ---------------------------------------------------------------------------
+
+def test_layer_norm_and_gelu_match_torch():
+    rng = _rng(10)
+    x = rng.standard_normal((3, 7, 24)) * 3 + 1
+    g = rng.standard_normal(24)
+    b = rng.standard_normal(24)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (24,),
+                                         torch.from_numpy(g),
+                                         torch.from_numpy(b), eps=1e-5).numpy()
+    np.testing.assert_allclose(O.layer_norm(x, g, b), ref, atol=1e-12)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x)).numpy()
+    np.testing.assert_allclose(O.gelu(x), ref, atol=1e-13)
+
+
+def test_staged_mode_rounds_and_stays_close():
+    wl = scaled(WORKLOADS["street"], batch=1, grid_h=16, grid_w=32)
+    inp = make_inputs(wl)
+    ex = O.hsmla_forward(inp["x"], inp, **wl.kwargs())
+    st = O.hsmla_forward(inp["x"], inp, staged=True, sel=ex["sel"],
+                         **wl.kwargs())
+    for key in ("qkv", "qkv_hat", "o_lin", "o", "y"):
+        np.testing.assert_array_equal(O.round_bf16(st[key]), st[key])
+        np.testing.assert_allclose(st[key], ex[key], rtol=3e-2, atol=3e-2)
+
+
+def test_block_forward_keep_zero_composition():
+    wl = scaled(WORKLOADS["block"], batch=1, grid_h=16, grid_w=16,
+                channels=64, heads=2, keep=0.0)
+    inp = make_inputs(wl)
+    r = O.hsmla_block_forward(inp["x"], inp, **wl.kwargs())
+    xn1 = O.layer_norm(inp["x"], 1.0, 0.0)
+    lin, _, _ = O.linear_attention(
+        O.multiscale_branches(xn1 @ inp["w_qkv"], inp["dw"], 16, 16), 2)
+    x1 = inp["x"] + lin @ inp["w_o"]
+    np.testing.assert_allclose(r["x1"], x1, atol=1e-12)
+    h = O.gelu(O.dwconv_same(O.layer_norm(x1, 1.0, 0.0) @ inp["w1"],
+                             inp["dw_ffn"], 16, 16))
+    np.testing.assert_allclose(r["out"], x1 + h @ inp["w2"], atol=1e-12)
