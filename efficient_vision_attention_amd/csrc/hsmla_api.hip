@@ -1,0 +1,373 @@
+// C ABI of libhsmla.so: argument validation, workspace layout and the launch
+// order of the forward pass on the caller's stream.  Declarations and the
+// contract of every entry point are in include/hsmla.h.
+#include "../../include/hsmla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace {
+
+using hsmla::kv_chunks;
+
+constexpr int kHeadDim = 32;
+constexpr int kMaxBlock = 16;
+constexpr int kMaxBlocks = 8192;
+constexpr int kMaxChannels = 2048;
+constexpr int kMaxBranchK = 7;
+constexpr size_t kAlign = 256;  // section alignment inside a workspace
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Dims {
+  int B, gh, gw, N, C, H, T, k, Bs, w, kmax;
+  size_t P;   // B * N tokens
+  size_t e;   // bytes per activation element
+  bool bf;
+};
+
+hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
+  if (!d) return HSMLA_ERR_NULL;
+  if (d->dtype != HSMLA_F32 && d->dtype != HSMLA_BF16) return HSMLA_ERR_DTYPE;
+  if (d->batch < 1 || d->grid_h < 1 || d->grid_w < 1) return HSMLA_ERR_SHAPE;
+  if (d->head_dim != kHeadDim || d->heads < 1) return HSMLA_ERR_SHAPE;
+  if ((int64_t)d->heads * d->head_dim != d->channels) return HSMLA_ERR_SHAPE;
+  if (d->channels > kMaxChannels) return HSMLA_ERR_SHAPE;
+  if (d->n_branches < 0 || d->n_branches > 3) return HSMLA_ERR_SHAPE;
+  int kmax = 1;
+  for (int i = 0; i < d->n_branches; ++i) {
+    const int k = d->branch_k[i];
+    if (k < 1 || k > kMaxBranchK || k % 2 == 0) return HSMLA_ERR_SHAPE;
+    if (k > kmax) kmax = k;
+  }
+  if (d->block < 1 || d->block > kMaxBlock) return HSMLA_ERR_SHAPE;
+  if (d->grid_h % d->block || d->grid_w % d->block) return HSMLA_ERR_SHAPE;
+  if (d->window < d->block || (d->window - d->block) % 2) return HSMLA_ERR_SHAPE;
+  const int64_t T = (int64_t)(d->grid_h / d->block) * (d->grid_w / d->block);
+  if (T > kMaxBlocks) return HSMLA_ERR_SHAPE;
+  if (d->keep_blocks < 0 || d->keep_blocks > T) return HSMLA_ERR_SHAPE;
+  const int64_t N = (int64_t)d->grid_h * d->grid_w;
+  // every element index must fit a 32-bit grid dimension and size_t math
+  if (N * d->batch * 4 * (int64_t)d->channels > ((int64_t)1 << 40)) return HSMLA_ERR_SHAPE;
+  if (N * d->batch > INT32_MAX / 2) return HSMLA_ERR_SHAPE;
+  if (out) {
+    out->B = d->batch;
+    out->gh = d->grid_h;
+    out->gw = d->grid_w;
+    out->N = (int)N;
+    out->C = d->channels;
+    out->H = d->heads;
+    out->T = (int)T;
+    out->k = d->keep_blocks;
+    out->Bs = d->block;
+    out->w = d->window;
+    out->kmax = kmax;
+    out->P = (size_t)N * d->batch;
+    out->bf = d->dtype == HSMLA_BF16;
+    out->e = out->bf ? 2 : 4;
+  }
+  return HSMLA_OK;
+}
+
+// Workspace sections, in this order (each start rounded up to 256 bytes):
+//   qkv [P][3C], qkv_hat [P][3C], o [P][C], kv [B][H][d][d] f32,
+//   ksum [B][H][d] f32, kv partials f32, dw taps [kmax^2][3C] f32,
+//   scores [B][T] f32, sel [B][k] i32,
+//   (block only) xn [P][C], x1 [P][C], h1 [P][4C], h2 [P][4C],
+//   ffn taps [9][4C] f32.
+struct Layout {
+  size_t qkv, qkv_hat, o, kv, ksum, part, taps, scores, sel;
+  size_t xn, x1, h1, h2, ffn_taps;
+  size_t total;
+};
+
+Layout layout(const Dims& D, int op) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&off](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes);
+    return at;
+  };
+  const size_t bh = (size_t)D.B * D.H;
+  const size_t part_bytes =
+      bh * kv_chunks(D.B, D.H, D.N) * (kHeadDim * kHeadDim + kHeadDim) * 4;
+  const size_t tap_bytes = (size_t)D.kmax * D.kmax * 3 * D.C * 4;
+  if (op == HSMLA_OP_QKV) {
+    L.taps = take(tap_bytes);
+  } else if (op == HSMLA_OP_LINEAR) {
+    L.part = take(part_bytes);
+  } else {
+    L.qkv = take(D.P * 3 * D.C * D.e);
+    L.qkv_hat = take(D.P * 3 * D.C * D.e);
+    L.o = take(D.P * D.C * D.e);
+    L.kv = take(bh * kHeadDim * kHeadDim * 4);
+    L.ksum = take(bh * kHeadDim * 4);
+    L.part = take(part_bytes);
+    L.taps = take(tap_bytes);
+    L.scores = take((size_t)D.B * D.T * 4);
+    L.sel = take((size_t)D.B * D.k * 4 + 4);
+    if (op == HSMLA_OP_BLOCK) {
+      L.xn = take(D.P * D.C * D.e);
+      L.x1 = take(D.P * D.C * D.e);
+      L.h1 = take(D.P * 4 * D.C * D.e);
+      L.h2 = take(D.P * 4 * D.C * D.e);
+      L.ffn_taps = take((size_t)9 * 4 * D.C * 4);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+inline char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+hsmla_status hip_status(hipError_t e) {
+  return e == hipSuccess ? HSMLA_OK : HSMLA_ERR_HIP;
+}
+
+#define HSMLA_TRY(expr)                                      \
+  do {                                                       \
+    const hipError_t e_ = (expr);                            \
+    if (e_ != hipSuccess) return HSMLA_ERR_HIP;              \
+  } while (0)
+
+hsmla_status check_weights(const hsmla_desc* d, const hsmla_weights* w) {
+  if (!w || !w->w_qkv || !w->w_o || !w->gate_w || !w->gate_b) return HSMLA_ERR_NULL;
+  for (int i = 0; i < d->n_branches; ++i)
+    if (!w->dw[i]) return HSMLA_ERR_NULL;
+  if (!aligned(w->w_qkv, 16) || !aligned(w->w_o, 16)) return HSMLA_ERR_ALIGN;
+  for (int i = 0; i < d->n_branches; ++i)
+    if (!aligned(w->dw[i], 4)) return HSMLA_ERR_ALIGN;
+  if (!aligned(w->gate_w, 4) || !aligned(w->gate_b, 4)) return HSMLA_ERR_ALIGN;
+  return HSMLA_OK;
+}
+
+// Steps 1-2 with caller-provided buffers.
+hsmla_status run_qkv(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
+                     const void* x, void* qkv, void* qkv_hat, float* taps,
+                     hipStream_t s) {
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, x, w->w_qkv, nullptr, qkv, (int)D.P,
+                               3 * D.C, D.C, s));
+  HSMLA_TRY(hsmla::launch_dw_taps(D.bf, w->dw, d->branch_k, d->n_branches,
+                                  D.kmax, 3 * D.C, 1, taps, s));
+  HSMLA_TRY(hsmla::launch_dwconv(D.bf, qkv, qkv_hat, taps, D.kmax, D.B, D.gh,
+                                 D.gw, 3 * D.C, false, s));
+  return HSMLA_OK;
+}
+
+// Steps 1-5 into the workspace views (o holds the refined output).
+hsmla_status run_module(const Dims& D, const hsmla_desc* d,
+                        const hsmla_weights* w, const void* x, void* ws,
+                        const Layout& L, hipStream_t s) {
+  void* qkv = at(ws, L.qkv);
+  void* qkvh = at(ws, L.qkv_hat);
+  void* o = at(ws, L.o);
+  float* kv = reinterpret_cast<float*>(at(ws, L.kv));
+  float* ksum = reinterpret_cast<float*>(at(ws, L.ksum));
+  float* part = reinterpret_cast<float*>(at(ws, L.part));
+  float* taps = reinterpret_cast<float*>(at(ws, L.taps));
+  float* scores = reinterpret_cast<float*>(at(ws, L.scores));
+  int32_t* sel = reinterpret_cast<int32_t*>(at(ws, L.sel));
+  hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, s);
+  if (st != HSMLA_OK) return st;
+  HSMLA_TRY(hsmla::launch_kv_state(D.bf, qkvh, kv, ksum, part, D.B, D.N, D.H, s));
+  HSMLA_TRY(hsmla::launch_lin_apply(D.bf, qkvh, kv, ksum, o, D.B, D.N, D.H, s));
+  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b, scores,
+                                      D.B, D.gh, D.gw, D.H, D.Bs, s));
+  HSMLA_TRY(hsmla::launch_topk(scores, nullptr, sel, D.B, D.T, D.k, s));
+  HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, sel, o, D.B, D.gh, D.gw, D.H,
+                                 D.Bs, D.w, D.k, s));
+  return HSMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hsmla_status_string(int32_t status) {
+  switch (status) {
+    case HSMLA_OK: return "ok";
+    case HSMLA_ERR_NULL: return "a required pointer is NULL";
+    case HSMLA_ERR_SHAPE: return "sizes violate the library limits";
+    case HSMLA_ERR_DTYPE: return "unknown dtype";
+    case HSMLA_ERR_ALIGN: return "pointer not aligned as required";
+    case HSMLA_ERR_WORKSPACE: return "workspace too small";
+    case HSMLA_ERR_HIP: return "HIP launch failed";
+    case HSMLA_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+hsmla_status hsmla_workspace_bytes(const hsmla_desc* desc, int32_t op,
+                                   size_t* bytes) {
+  if (!bytes) return HSMLA_ERR_NULL;
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (op < HSMLA_OP_QKV || op > HSMLA_OP_BLOCK) return HSMLA_ERR_ARG;
+  *bytes = layout(D, op).total;
+  return HSMLA_OK;
+}
+
+hsmla_status hsmla_workspace_views(const hsmla_desc* desc, int32_t op,
+                                   void* ws, hsmla_views* v) {
+  if (!ws || !v) return HSMLA_ERR_NULL;
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (op != HSMLA_OP_FORWARD && op != HSMLA_OP_BLOCK) return HSMLA_ERR_ARG;
+  const Layout L = layout(D, op);
+  v->qkv = at(ws, L.qkv);
+  v->qkv_hat = at(ws, L.qkv_hat);
+  v->o = at(ws, L.o);
+  v->kv = reinterpret_cast<float*>(at(ws, L.kv));
+  v->ksum = reinterpret_cast<float*>(at(ws, L.ksum));
+  v->scores = reinterpret_cast<float*>(at(ws, L.scores));
+  v->sel = reinterpret_cast<int32_t*>(at(ws, L.sel));
+  v->x1 = op == HSMLA_OP_BLOCK ? at(ws, L.x1) : nullptr;
+  return HSMLA_OK;
+}
+
+hsmla_status hsmla_qkv_branches(const hsmla_desc* desc, const hsmla_weights* w,
+                                const void* x, void* qkv, void* qkv_hat,
+                                void* ws, size_t ws_bytes, void* stream) {
+  Dims D;
+  hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!x || !qkv || !qkv_hat || !ws) return HSMLA_ERR_NULL;
+  if ((st = check_weights(desc, w)) != HSMLA_OK) return st;
+  if (!aligned(x, 16) || !aligned(qkv, 16) || !aligned(qkv_hat, 16) ||
+      !aligned(ws, 16))
+    return HSMLA_ERR_ALIGN;
+  const Layout L = layout(D, HSMLA_OP_QKV);
+  if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
+  return run_qkv(D, desc, w, x, qkv, qkv_hat,
+                 reinterpret_cast<float*>(at(ws, L.taps)),
+                 static_cast<hipStream_t>(stream));
+}
+
+hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
+                               void* o, float* kv, float* ksum, void* ws,
+                               size_t ws_bytes, void* stream) {
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!qkv_hat || !o || !kv || !ksum || !ws) return HSMLA_ERR_NULL;
+  if (!aligned(qkv_hat, 16) || !aligned(o, 16) || !aligned(ws, 16) ||
+      !aligned(kv, 4) || !aligned(ksum, 4))
+    return HSMLA_ERR_ALIGN;
+  const Layout L = layout(D, HSMLA_OP_LINEAR);
+  if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HSMLA_TRY(hsmla::launch_kv_state(D.bf, qkv_hat, kv, ksum,
+                                   reinterpret_cast<float*>(at(ws, L.part)),
+                                   D.B, D.N, D.H, s));
+  return hip_status(
+      hsmla::launch_lin_apply(D.bf, qkv_hat, kv, ksum, o, D.B, D.N, D.H, s));
+}
+
+hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
+                               const float* gate_w, const float* gate_b,
+                               const float* scores_in, float* scores_out,
+                               int32_t* sel, void* stream) {
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (D.k > 0 && !sel) return HSMLA_ERR_NULL;
+  if (!scores_in && (!qkv_hat || !gate_w || !gate_b || !scores_out))
+    return HSMLA_ERR_NULL;
+  if ((qkv_hat && !aligned(qkv_hat, 16)) || (sel && !aligned(sel, 4)) ||
+      (scores_in && !aligned(scores_in, 4)) ||
+      (scores_out && !aligned(scores_out, 4)) ||
+      (gate_w && !aligned(gate_w, 4)) || (gate_b && !aligned(gate_b, 4)))
+    return HSMLA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (scores_in)
+    return hip_status(
+        hsmla::launch_topk(scores_in, scores_out, sel, D.B, D.T, D.k, s));
+  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkv_hat, gate_w, gate_b, scores_out,
+                                      D.B, D.gh, D.gw, D.H, D.Bs, s));
+  return hip_status(hsmla::launch_topk(scores_out, nullptr, sel, D.B, D.T, D.k, s));
+}
+
+hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
+                                  const void* qkv_hat, const int32_t* sel,
+                                  void* o, void* stream) {
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!qkv || !qkv_hat || !o || (D.k > 0 && !sel)) return HSMLA_ERR_NULL;
+  if (!aligned(qkv, 16) || !aligned(qkv_hat, 16) || !aligned(o, 16) ||
+      (sel && !aligned(sel, 4)))
+    return HSMLA_ERR_ALIGN;
+  return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, o, D.B, D.gh,
+                                         D.gw, D.H, D.Bs, D.w, D.k,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
+                           const void* x, void* y, void* ws, size_t ws_bytes,
+                           void* stream) {
+  Dims D;
+  hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!x || !y || !ws) return HSMLA_ERR_NULL;
+  if ((st = check_weights(desc, w)) != HSMLA_OK) return st;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 16)) return HSMLA_ERR_ALIGN;
+  const Layout L = layout(D, HSMLA_OP_FORWARD);
+  if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_module(D, desc, w, x, ws, L, s)) != HSMLA_OK) return st;
+  return hip_status(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, nullptr, y,
+                                       (int)D.P, D.C, D.C, s));
+}
+
+hsmla_status hsmla_block_forward(const hsmla_desc* desc, const hsmla_weights* w,
+                                 const hsmla_ffn_weights* f, const void* x,
+                                 void* out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  Dims D;
+  hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!x || !out || !ws || !f) return HSMLA_ERR_NULL;
+  if ((st = check_weights(desc, w)) != HSMLA_OK) return st;
+  if (!f->ln1_g || !f->ln1_b || !f->ln2_g || !f->ln2_b || !f->w1 ||
+      !f->dw_ffn || !f->w2)
+    return HSMLA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 16) ||
+      !aligned(f->w1, 16) || !aligned(f->w2, 16) || !aligned(f->dw_ffn, 4) ||
+      !aligned(f->ln1_g, 4) || !aligned(f->ln1_b, 4) || !aligned(f->ln2_g, 4) ||
+      !aligned(f->ln2_b, 4))
+    return HSMLA_ERR_ALIGN;
+  const Layout L = layout(D, HSMLA_OP_BLOCK);
+  if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int P = (int)D.P, C = D.C;
+  void* xn = at(ws, L.xn);
+  void* x1 = at(ws, L.x1);
+  void* h1 = at(ws, L.h1);
+  void* h2 = at(ws, L.h2);
+  float* ftaps = reinterpret_cast<float*>(at(ws, L.ffn_taps));
+  HSMLA_TRY(hsmla::launch_layernorm(D.bf, x, f->ln1_g, f->ln1_b, xn, P, C, s));
+  if ((st = run_module(D, desc, w, xn, ws, L, s)) != HSMLA_OK) return st;
+  // x1 = x + O W_o (residual fused into the projection epilogue)
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, x, x1, P, C, C, s));
+  HSMLA_TRY(hsmla::launch_layernorm(D.bf, x1, f->ln2_g, f->ln2_b, xn, P, C, s));
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, xn, f->w1, nullptr, h1, P, 4 * C, C, s));
+  const void* ffn_k[1] = {f->dw_ffn};
+  const int ffn_ks[1] = {3};
+  HSMLA_TRY(hsmla::launch_dw_taps(D.bf, ffn_k, ffn_ks, 1, 3, 4 * C, 0, ftaps, s));
+  HSMLA_TRY(hsmla::launch_dwconv(D.bf, h1, h2, ftaps, 3, D.B, D.gh, D.gw, 4 * C,
+                                 true, s));
+  return hip_status(hsmla::launch_gemm(D.bf, h2, f->w2, x1, out, P, C, 4 * C, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Block-level gate and selection.
+//
+// Scores (FT 3.2 head-level score and block-level aggregation):
+//   f_t^(h) = mean over the block's tokens of [Q_hat; K_hat; V_hat]^(h)
+//   M_t     = (1/H) sum_h sigmoid(w^(h) . f_t^(h) + b^(h))
+// Selection: the keep largest M_t per image, equal scores to the lower
+// block index, written in ascending block order -- the compacted tile list
+// the refinement kernel runs over (FT 3.6 stage 3).  A fixed count replaces
+// the paper's threshold so the refinement grid size is known on the host.
+#include "common.h"
+#include "kernels.h"
+
+namespace hsmla {
+namespace {
+
+constexpr int kD = 32;
+
+// grid (blocks per image, batch), 256 threads.  Channel sums over the
+// block's tokens go to LDS (fixed token order per channel), then one wave
+// forms each head's logit with a wave reduction in fixed lane order.
+template <typename T>
+__global__ __launch_bounds__(256) void gate_scores_kernel(
+    const T* __restrict__ qkvh, const float* __restrict__ gw,
+    const float* __restrict__ gb, float* __restrict__ scores, int gh, int gwid,
+    int heads, int block) {
+  extern __shared__ float sh[];
+  const int C = heads * kD, C3 = 3 * C;
+  float* fsum = sh;          // [3C]
+  float* gsig = sh + C3;     // [heads]
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int nbc = gwid / block;
+  const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
+  const size_t img = (size_t)b * gh * gwid;
+  for (int c = threadIdx.x; c < C3; c += blockDim.x) {
+    float s = 0.f;
+    for (int yy = 0; yy < block; ++yy)
+      for (int xx = 0; xx < block; ++xx)
+        s += to_f32(qkvh[(img + (size_t)(r0 + yy) * gwid + c0 + xx) * C3 + c]);
+    fsum[c] = s;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const float inv_cnt = 1.f / (float)(block * block);
+  for (int h = wave; h < heads; h += blockDim.x / 64) {
+    float p = 0.f;
+    for (int f = lane; f < 3 * kD; f += 64) {
+      const int s = f / kD, j = f % kD;
+      p = fmaf(gw[h * 3 * kD + f], fsum[s * C + h * kD + j] * inv_cnt, p);
+    }
+    p = wave_sum(p);
+    if (lane == 0) gsig[h] = 1.f / (1.f + expf(-(p + gb[h])));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.f;
+    for (int h = 0; h < heads; ++h) m += gsig[h];
+    scores[(size_t)b * gridDim.x + t] = m / (float)heads;
+  }
+}
+
+// grid (batch), 1024 threads.  rank(t) = #{u : s_u > s_t or (s_u == s_t and
+// u < t)}; block t is kept iff rank(t) < keep, and its slot in the output is
+// the number of kept blocks below it.  Exact and order-independent.
+__global__ __launch_bounds__(1024) void topk_kernel(
+    const float* __restrict__ scores, float* __restrict__ scores_copy,
+    int32_t* __restrict__ sel, int nblocks, int keep) {
+  extern __shared__ float sh[];
+  float* s = sh;                                           // [nblocks]
+  int* kept = reinterpret_cast<int*>(sh + nblocks);        // [nblocks]
+  const int b = blockIdx.x;
+  const float* src = scores + (size_t)b * nblocks;
+  for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
+    const float v = src[t];
+    s[t] = v;
+    if (scores_copy) scores_copy[(size_t)b * nblocks + t] = v;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
+    const float v = s[t];
+    int rank = 0;
+    for (int u = 0; u < nblocks; ++u) {
+      const float w = s[u];
+      rank += (w > v) || (w == v && u < t);
+    }
+    kept[t] = rank < keep;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
+    if (!kept[t]) continue;
+    int pos = 0;
+    for (int u = 0; u < t; ++u) pos += kept[u];
+    sel[(size_t)b * keep + pos] = t;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
+                              const float* gate_w, const float* gate_b,
+                              float* scores, int batch, int gh, int gw,
+                              int heads, int block, hipStream_t s) {
+  const int nblocks = (gh / block) * (gw / block);
+  dim3 grid(nblocks, batch);
+  const size_t lds = (size_t)(3 * heads * kD + heads) * sizeof(float);
+  if (bf)
+    gate_scores_kernel<bf16><<<grid, 256, lds, s>>>(
+        static_cast<const bf16*>(qkv_hat), gate_w, gate_b, scores, gh, gw, heads,
+        block);
+  else
+    gate_scores_kernel<float><<<grid, 256, lds, s>>>(
+        static_cast<const float*>(qkv_hat), gate_w, gate_b, scores, gh, gw,
+        heads, block);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
+                       int batch, int nblocks, int keep, hipStream_t s) {
+  if (keep == 0 && scores_copy == nullptr) return hipSuccess;
+  const size_t lds = (size_t)nblocks * (sizeof(float) + sizeof(int));
+  topk_kernel<<<batch, 1024, lds, s>>>(scores, scores_copy, sel, nblocks, keep);
+  return hipGetLastError();
+}
+
+}  // namespace hsmla

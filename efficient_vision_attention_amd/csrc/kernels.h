@@ -1,0 +1,61 @@
+// Host-side launchers of the HSMLA kernels.  Each returns hipSuccess or the
+// launch error.  Shapes are validated by the caller (hsmla_api.hip); the
+// launchers assume them.  `bf` selects bfloat16 (true) or float32 storage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hsmla {
+
+// C[M][N] = A[M][K] . B[K][N] (+ R[M][N] when R != nullptr), row-major.
+hipError_t launch_gemm(bool bf, const void* A, const void* B, const void* R,
+                       void* C, int M, int N, int K, hipStream_t s);
+
+// Effective depthwise taps: weff[tap][ch] (float32, kmax x kmax taps) =
+// identity (centre tap += 1 when `identity`) + sum of the given kernels,
+// each zero-padded to kmax.  kernels[i] is [ch][k_i][k_i].
+hipError_t launch_dw_taps(bool bf, const void* const* kernels, const int* ks,
+                          int nk, int kmax, int ch, int identity, float* weff,
+                          hipStream_t s);
+
+// out[b][y][x][c] = act(sum_tap weff[tap][c] * in[b][y+dy-r][x+dx-r][c]),
+// zero padding, r = (kmax-1)/2; act = exact GELU when `gelu`.
+hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
+                         int kmax, int batch, int gh, int gw, int ch,
+                         bool gelu, hipStream_t s);
+
+// Number of token chunks the KV-state reduction splits each image into.
+int kv_chunks(int batch, int heads, int tokens);
+
+// Z/D partials per chunk, then a fixed-order combine into kv and ksum.
+hipError_t launch_kv_state(bool bf, const void* qkv_hat, float* kv,
+                           float* ksum, float* partials, int batch, int tokens,
+                           int heads, hipStream_t s);
+
+// o = relu(q_hat) Z / (relu(q_hat) . D), zero when the denominator is 0.
+hipError_t launch_lin_apply(bool bf, const void* qkv_hat, const float* kv,
+                            const float* ksum, void* o, int batch, int tokens,
+                            int heads, hipStream_t s);
+
+// Gate scores per block, then top-k selection.
+hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
+                              const float* gate_w, const float* gate_b,
+                              float* scores, int batch, int gh, int gw,
+                              int heads, int block, hipStream_t s);
+hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
+                       int batch, int nblocks, int keep, hipStream_t s);
+
+// Windowed softmax refinement of the selected blocks, in place on o.
+hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
+                         const int32_t* sel, void* o, int batch, int gh,
+                         int gw, int heads, int block, int window, int keep,
+                         hipStream_t s);
+
+// y = LN(x) . gamma + beta over the channel dimension.
+hipError_t launch_layernorm(bool bf, const void* x, const float* gamma,
+                            const float* beta, void* y, int rows, int ch,
+                            hipStream_t s);
+
+}  // namespace hsmla

@@ -1,0 +1,200 @@
+/*
+ * hsmla.h -- C ABI of libhsmla.so, the HSMLA attention forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources named below:
+ *   FT = "HSMLA: Hierarchical Softmax Multi-scale Linear Attention for
+ *        Efficient Vision Transformers", full text (paperpeel.com rendering).
+ *   EX = the gist.science explainer of the same paper, section
+ *        "Technische Samenvatting".
+ *
+ * Module computed (FT 3.1-3.3, 3.5, 3.6):
+ *   QKV     = X W_qkv                                  (projection, no bias)
+ *   T_hat   = T + sum_s DWConv_{k_s}(T)  for T in Q,K,V (multi-scale branches)
+ *   Z, D    = sum_j relu(K_hat_j)^T V_hat_j, sum_j relu(K_hat_j)   (per head)
+ *   O_lin   = relu(Q_hat) Z / (relu(Q_hat) . D)           (0 when the sum is 0)
+ *   M_t     = mean_h sigmoid(w_h . meanpool_t[Q_hat;K_hat;V_hat]_h + b_h)
+ *   sel     = the keep_blocks blocks with the largest M_t (ties -> lower t)
+ *   O_i     = O_lin_i + softmax-attn(q_i, K_W, V_W) - lin-local_i  on sel
+ *   Y       = O W_o
+ *
+ * Conventions shared by every entry point:
+ *   - Layout: a token grid of grid_h x grid_w tokens, token n = y*grid_w + x.
+ *     Activations are row-major [batch][n][channels].  The projected tensor
+ *     is [batch][n][3C] with channel s*C + h*head_dim + j holding component
+ *     s (0 = Q, 1 = K, 2 = V) of head h.  Blocks are block x block tiles,
+ *     numbered row-major over the block grid.
+ *   - Element type: desc->dtype selects float32 or bfloat16 for activations
+ *     and weights (the `const void*` arguments).  Gate weights, LayerNorm
+ *     parameters, Z, D and scores are always float32.  All arithmetic
+ *     accumulates in float32; bfloat16 results are rounded to nearest even.
+ *   - Ownership: the caller allocates every buffer (device memory).  The
+ *     library allocates nothing, frees nothing and keeps no pointer after a
+ *     call returns.  Buffers must stay valid until the stream reaches the
+ *     work.  Inputs and outputs must not overlap unless stated.
+ *   - Asynchrony: every call only enqueues work on `stream` (a hipStream_t;
+ *     NULL = the default stream) and never synchronises.
+ *   - Errors: argument errors are detected on the host before any HIP call
+ *     and returned as a negative hsmla_status; nothing is launched then.  A
+ *     failed launch returns HSMLA_ERR_HIP.  No exception crosses the ABI.
+ *   - Alignment: activation, weight and workspace pointers must be 16-byte
+ *     aligned; float32 parameter and index pointers 4-byte aligned.
+ *   - Threading: no mutable global state; calls on different streams may
+ *     run concurrently if their buffers do not overlap.
+ *   - Limits: head_dim must be 32; block <= 16; window >= block with
+ *     (window - block) even; grid_h and grid_w multiples of block;
+ *     0 <= keep_blocks <= number of blocks <= 8192; channels <= 2048;
+ *     up to 3 depthwise branches of odd size <= 7.
+ */
+#ifndef HSMLA_H_
+#define HSMLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSMLA_OK = 0,
+  HSMLA_ERR_NULL = -1,      /* a required pointer is NULL                  */
+  HSMLA_ERR_SHAPE = -2,     /* sizes violate the limits above              */
+  HSMLA_ERR_DTYPE = -3,     /* unknown dtype                               */
+  HSMLA_ERR_ALIGN = -4,     /* a pointer is not aligned as required        */
+  HSMLA_ERR_WORKSPACE = -5, /* workspace smaller than hsmla_workspace_bytes */
+  HSMLA_ERR_HIP = -6,       /* a kernel launch failed                      */
+  HSMLA_ERR_ARG = -7        /* other invalid argument (e.g. unknown op)    */
+} hsmla_status;
+
+typedef enum { HSMLA_F32 = 0, HSMLA_BF16 = 1 } hsmla_dtype;
+
+/* Which entry point a workspace is sized for. */
+typedef enum {
+  HSMLA_OP_QKV = 0,     /* hsmla_qkv_branches   */
+  HSMLA_OP_LINEAR = 1,  /* hsmla_linear_attn    */
+  HSMLA_OP_FORWARD = 2, /* hsmla_forward        */
+  HSMLA_OP_BLOCK = 3    /* hsmla_block_forward  */
+} hsmla_op;
+
+typedef struct {
+  int32_t batch, grid_h, grid_w; /* N = grid_h * grid_w tokens per image  */
+  int32_t channels, heads, head_dim; /* channels == heads * head_dim     */
+  int32_t n_branches;            /* depthwise branches besides identity  */
+  int32_t branch_k[3];           /* their (odd) kernel sizes              */
+  int32_t block;                 /* block side Bs                          */
+  int32_t window;                /* softmax window side w                  */
+  int32_t keep_blocks;           /* refined blocks per image, 0..T         */
+  int32_t dtype;                 /* hsmla_dtype                            */
+} hsmla_desc;
+
+typedef struct {
+  const void* w_qkv;   /* [C][3C], used as x . W                        */
+  const void* w_o;     /* [C][C]                                        */
+  const void* dw[3];   /* branch s: [3C][k_s][k_s] cross-correlation     */
+  const float* gate_w; /* [H][3*head_dim]: weights on [q; k; v] means    */
+  const float* gate_b; /* [H]                                            */
+} hsmla_weights;
+
+typedef struct {
+  const float* ln1_g; const float* ln1_b; /* [C] LayerNorm before HSMLA */
+  const float* ln2_g; const float* ln2_b; /* [C] LayerNorm before FFN   */
+  const void* w1;      /* [C][4C]                                       */
+  const void* dw_ffn;  /* [4C][3][3]                                    */
+  const void* w2;      /* [4C][C]                                       */
+} hsmla_ffn_weights;
+
+/* Pointers into a forward/block workspace, for inspection. */
+typedef struct {
+  void* qkv;      /* [B][N][3C] projected Q, K, V                      */
+  void* qkv_hat;  /* [B][N][3C] after the depthwise branches            */
+  void* o;        /* [B][N][C]  attention output before W_o             */
+  float* kv;      /* [B][H][d][d] Z                                     */
+  float* ksum;    /* [B][H][d]   D                                      */
+  float* scores;  /* [B][T] gate scores M                               */
+  int32_t* sel;   /* [B][keep_blocks] selected blocks, ascending        */
+  void* x1;       /* block only: [B][N][C] X + HSMLA(LN1(X))            */
+} hsmla_views;
+
+/* Bytes of workspace `op` needs for `desc` (written to *bytes). */
+hsmla_status hsmla_workspace_bytes(const hsmla_desc* desc, int32_t op,
+                                   size_t* bytes);
+
+/* Fills `views` with the intermediate tensors that hsmla_forward (op =
+ * HSMLA_OP_FORWARD) or hsmla_block_forward (HSMLA_OP_BLOCK) leave in `ws`
+ * once the stream has completed.  Host-only pointer arithmetic. */
+hsmla_status hsmla_workspace_views(const hsmla_desc* desc, int32_t op,
+                                   void* ws, hsmla_views* views);
+
+/* Steps 1-2 (FT 3.1 projection; abstract and EX section 2 for the
+ * multi-scale depthwise branches): qkv = x W_qkv and
+ * qkv_hat = qkv + sum_s DWConv_{k_s}(qkv), zero padding (k-1)/2, no bias.
+ * x [B][N][C]; qkv, qkv_hat [B][N][3C]; ws sized for HSMLA_OP_QKV. */
+hsmla_status hsmla_qkv_branches(const hsmla_desc* desc,
+                                const hsmla_weights* w, const void* x,
+                                void* qkv, void* qkv_hat, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Step 3, the global linear path (FT 3.1 Z/D sums; FT 3.3 lin-local ratio
+ * taken over all tokens).  qkv_hat [B][N][3C] in; o [B][N][C] out
+ * (O_lin); kv [B][H][d][d] = Z (row: key feature, column: value feature)
+ * and ksum [B][H][d] = D out, float32.  The reduction over tokens is split
+ * in fixed chunks and combined in a fixed order, so results are bitwise
+ * reproducible.  ws sized for HSMLA_OP_LINEAR. */
+hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
+                               void* o, float* kv, float* ksum, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Step 4, block gate and selection (FT 3.2 head-level score and block-level
+ * aggregation; gate shared by all heads per EX section 2).  With
+ * scores_in == NULL the scores M [B][T] are pooled from qkv_hat and written
+ * to scores_out (required).  With scores_in != NULL those float32 scores are
+ * ranked instead (qkv_hat, gate_w, gate_b may be NULL) and copied to
+ * scores_out if it is not NULL.  sel [B][keep_blocks] receives, per image,
+ * the indices of the keep_blocks largest scores (equal scores: lower index
+ * first), in ascending order.  Scores must not be NaN. */
+hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
+                               const float* gate_w, const float* gate_b,
+                               const float* scores_in, float* scores_out,
+                               int32_t* sel, void* stream);
+
+/* Step 5, local softmax refinement of the selected blocks with the two-path
+ * residual (FT 3.3 local-neighbourhood, lin-local and residual equations;
+ * scatter of the sparse residual, FT 3.6 stage 5).  For every block in sel
+ * and every head, each query i of the block gets
+ *   o_i <- o_i + softmax_j(q_i.k_j / sqrt(d)) v_j - lin-local_i
+ * over the window x window keys centred on the block and clipped to the
+ * grid, with raw q, k, v from qkv and lin-local from qkv_hat.  o holds O_lin
+ * on entry; tokens of unselected blocks are not touched.  sel entries must
+ * be distinct valid block indices. */
+hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
+                                  const void* qkv_hat, const int32_t* sel,
+                                  void* o, void* stream);
+
+/* The whole module: y = HSMLA(x) = O W_o, steps 1-5 then the output
+ * projection (FT 3.6 stages 1-5).  x, y [B][N][C]; ws sized for
+ * HSMLA_OP_FORWARD; intermediates readable through hsmla_workspace_views. */
+hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
+                           const void* x, void* y, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* One block (FT 3.5 block equation, with its depthwise and FFN steps fused
+ * into one FFN-DWConv sandwich):
+ *   x1  = x + HSMLA(LN1(x))
+ *   out = x1 + W2 GELU(DWConv3x3(W1 LN2(x1)))
+ * LayerNorm: biased variance, eps 1e-5; GELU: exact erf form.  x, out
+ * [B][N][C] (must not overlap); ws sized for HSMLA_OP_BLOCK. */
+hsmla_status hsmla_block_forward(const hsmla_desc* desc,
+                                 const hsmla_weights* w,
+                                 const hsmla_ffn_weights* f, const void* x,
+                                 void* out, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Static description of a status code. */
+const char* hsmla_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSMLA_H_ */

@@ -1,0 +1,176 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/hsmla.h declares, and rejects bad arguments with the documented
+status before any HIP call.
+
+The argument-error cases pass placeholder device addresses; they run only
+where no GPU is visible, so a validation bug can never turn into a launch
+on real memory.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from efficient_vision_attention_amd import hsmla as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(hsmla_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = H.library()
+    declared = _declared_functions()
+    assert declared == set(H.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(0, -8, -1):
+        assert H.status_string(code)
+    assert H.status_string(-99) == "unknown status"
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+cpu_only = pytest.mark.skipif(not _no_gpu(), reason="argument-error cases run on hosts without a GPU")
+
+FAKE = 0x10000  # 16-byte aligned placeholder address, never dereferenced
+
+
+def _desc(**kw):
+    base = dict(batch=2, grid_h=16, grid_w=32, channels=64, heads=2,
+                branches=(3, 5), block=4, window=8, keep_blocks=4, dtype="bf16")
+    base.update(kw)
+    return H.make_desc(**base)
+
+
+def _ws_bytes(desc, op):
+    n = ctypes.c_size_t(0)
+    st = H.library().hsmla_workspace_bytes(ctypes.byref(desc), op, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(head_dim=16, channels=32), -2),
+    (dict(channels=96), -2),              # heads * head_dim != channels
+    (dict(grid_w=30), -2),                # not a multiple of the block
+    (dict(window=9), -2),                 # (window - block) odd
+    (dict(window=2), -2),                 # window smaller than block
+    (dict(keep_blocks=33), -2),           # keep > T = 32
+    (dict(keep_blocks=-1), -2),
+    (dict(block=32, grid_h=32, window=32), -2),  # block > 16
+    (dict(branches=(4,)), -2),            # even kernel size
+    (dict(branches=(9,)), -2),            # kernel > 7
+    (dict(dtype=7), -3),
+    (dict(batch=0), -2),
+])
+def test_desc_validation(change, status):
+    d = _desc(**{k: v for k, v in change.items() if k != "head_dim"})
+    if "head_dim" in change:
+        d.head_dim = change["head_dim"]
+    st, _ = _ws_bytes(d, H.HSMLA_OP_FORWARD)
+    assert st == status
+
+
+def test_workspace_bytes_and_bad_op():
+    d = _desc()
+    st, n = _ws_bytes(d, H.HSMLA_OP_FORWARD)
+    assert st == 0 and n > 0
+    st_b, nb = _ws_bytes(d, H.HSMLA_OP_BLOCK)
+    assert st_b == 0 and nb > n
+    assert _ws_bytes(d, 9)[0] == -7
+    lib = H.library()
+    assert lib.hsmla_workspace_bytes(None, 2, ctypes.byref(ctypes.c_size_t())) == -1
+    assert lib.hsmla_workspace_bytes(ctypes.byref(d), 2, None) == -1
+
+
+def _weights():
+    w = H.hsmla_weights()
+    w.w_qkv = w.w_o = FAKE
+    w.dw[0] = w.dw[1] = FAKE
+    w.gate_w = w.gate_b = FAKE
+    return w
+
+
+@cpu_only
+def test_forward_argument_errors():
+    lib = H.library()
+    d = _desc()
+    st, need = _ws_bytes(d, H.HSMLA_OP_FORWARD)
+    w = _weights()
+    f = lib.hsmla_forward
+    assert f(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, need - 1, None) == -5
+    assert f(ctypes.byref(d), ctypes.byref(w), None, FAKE, FAKE, need, None) == -1
+    assert f(ctypes.byref(d), ctypes.byref(w), FAKE + 2, FAKE, FAKE, need, None) == -4
+    assert f(ctypes.byref(d), None, FAKE, FAKE, FAKE, need, None) == -1
+    w.dw[1] = None
+    assert f(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, need, None) == -1
+    bad = _desc(window=7)
+    assert f(ctypes.byref(bad), ctypes.byref(_weights()), FAKE, FAKE, FAKE, need, None) == -2
+
+
+@cpu_only
+def test_stage_argument_errors():
+    lib = H.library()
+    d = _desc()
+    st, need = _ws_bytes(d, H.HSMLA_OP_LINEAR)
+    assert lib.hsmla_linear_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 need - 1, None) == -5
+    assert lib.hsmla_linear_attn(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE,
+                                 need, None) == -1
+    assert lib.hsmla_linear_attn(ctypes.byref(d), FAKE, FAKE, FAKE + 2, FAKE, FAKE,
+                                 need, None) == -4
+    # gate: pooled scores need qkv_hat, weights and scores_out
+    assert lib.hsmla_gate_select(ctypes.byref(d), None, FAKE, FAKE, None, FAKE,
+                                 FAKE, None) == -1
+    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE, FAKE, FAKE, None, None,
+                                 FAKE, None) == -1
+    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE,
+                                 None, None) == -1
+    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE + 8, FAKE, FAKE, None, FAKE,
+                                 FAKE, None) == -4
+    assert lib.hsmla_sparse_softmax(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == -1
+    assert lib.hsmla_sparse_softmax(ctypes.byref(d), FAKE, FAKE + 4, FAKE, FAKE,
+                                    None) == -4
+    st, need_q = _ws_bytes(d, H.HSMLA_OP_QKV)
+    assert lib.hsmla_qkv_branches(ctypes.byref(d), ctypes.byref(_weights()), FAKE,
+                                  FAKE, FAKE, FAKE, need_q - 1, None) == -5
+    ffn = H.hsmla_ffn_weights()
+    st, need_b = _ws_bytes(d, H.HSMLA_OP_BLOCK)
+    assert lib.hsmla_block_forward(ctypes.byref(d), ctypes.byref(_weights()),
+                                   ctypes.byref(ffn), FAKE, FAKE, FAKE, need_b,
+                                   None) == -1
+
+
+def test_workspace_views_layout():
+    d = _desc()
+    st, need = _ws_bytes(d, H.HSMLA_OP_FORWARD)
+    v = H.hsmla_views()
+    base = 1 << 20
+    assert H.library().hsmla_workspace_views(ctypes.byref(d), H.HSMLA_OP_FORWARD,
+                                             base, ctypes.byref(v)) == 0
+    offs = [getattr(v, n) - base for n in ("qkv", "qkv_hat", "o", "kv", "ksum",
+                                           "scores", "sel")]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and offs[-1] < need
+    assert v.x1 is None

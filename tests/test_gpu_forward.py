@@ -1,0 +1,115 @@
+"""End-to-end GPU parity of hsmla_forward and hsmla_block_forward against
+the oracle (bfloat16-staged for bf16 runs, exact for float32 runs), plus
+the degenerate cases of the method."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import WORKLOADS, make_inputs, scaled
+
+from gpu_harness import (Run, assert_close, oracle_kwargs,
+                         selection_band_check, staged)
+from test_gpu_stages import STAGE_CASES
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_module(wl, inp, g, k=None):
+    """Compare every forward intermediate with the oracle; a selection that
+    differs inside the near-tie band is injected into the oracle."""
+    kw = oracle_kwargs(wl, k)
+    st = staged(wl)
+    ref = O.hsmla_forward(inp["x"], inp, staged=st, **kw)
+    kk = kw["keep_blocks"]
+    sel_g = g["sel"][:, :kk]
+    if not np.array_equal(sel_g, ref["sel"]):
+        rep = selection_band_check(ref["scores"], g["scores"], ref["sel"], sel_g, kk)
+        print("selection differs inside the tie band:", rep)
+        ref = O.hsmla_forward(inp["x"], inp, staged=st, sel=sel_g, **kw)
+    for key in ("qkv", "qkv_hat", "o", "y"):
+        assert_close(g[key], ref[key], wl.dtype, key)
+    np.testing.assert_allclose(g["scores"], ref["scores"], rtol=0, atol=5e-5)
+    return ref
+
+
+@pytest.mark.parametrize("name", list(STAGE_CASES))
+def test_forward_end_to_end(name):
+    wl = STAGE_CASES[name]
+    inp = make_inputs(wl)
+    g = Run(wl, inp).forward()
+    _check_module(wl, inp, g)
+
+
+def test_forward_is_bitwise_deterministic():
+    wl = STAGE_CASES["street_small"]
+    inp = make_inputs(wl)
+    r = Run(wl, inp)
+    a, b = r.forward(), r.forward()
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_bf16"])
+def test_keep_zero_is_linear_attention(name):
+    wl = STAGE_CASES[name]
+    inp = make_inputs(wl)
+    g = Run(wl, inp, keep_blocks=0).forward()
+    np.testing.assert_array_equal(g["o"], g["o"])  # readable
+    ref = _check_module(wl, inp, g, k=0)
+    np.testing.assert_array_equal(ref["o"], ref["o_lin"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_keep_all_covering_window_is_full_softmax(dtype):
+    """Every block refined with a window covering the grid: the linear terms
+    cancel and the module output is softmax attention over raw Q, K, V."""
+    wl = scaled(WORKLOADS["tiny"], dtype=dtype, window=4 + 2 * 16, keep=1.0)
+    inp = make_inputs(wl)
+    g = Run(wl, inp).forward()
+    ref = _check_module(wl, inp, g)
+    qkv = torch.from_numpy(g["qkv"])
+    B, N, C3 = qkv.shape
+    C = C3 // 3
+    q, k, v = (qkv[..., s * C:(s + 1) * C].reshape(B, N, 2, 32).transpose(1, 2)
+               for s in range(3))
+    full = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+    full = full.transpose(1, 2).reshape(B, N, C).numpy()
+    tol = 5e-2 if dtype == "bf16" else 1e-4
+    np.testing.assert_allclose(g["o"], full, rtol=tol, atol=tol)
+    assert ref["sel"].shape[1] == wl.num_blocks
+
+
+def test_window_equal_block_keep_all():
+    wl = scaled(STAGE_CASES["ragged_bf16"], window=4, keep=1.0)
+    inp = make_inputs(wl)
+    _check_module(wl, inp, Run(wl, inp).forward())
+
+
+@pytest.mark.parametrize("keep", [0.0, 0.05, 0.5, 1.0])
+def test_block_forward(keep):
+    wl = scaled(STAGE_CASES["block_small"], keep=keep)
+    inp = make_inputs(wl)
+    g = Run(wl, inp).block_forward()
+    kw = oracle_kwargs(wl)
+    ref = O.hsmla_block_forward(inp["x"], inp, staged=True, **kw)
+    kk = kw["keep_blocks"]
+    if not np.array_equal(g["sel"][:, :kk], ref["sel"]):
+        selection_band_check(ref["scores"], g["scores"], ref["sel"],
+                             g["sel"][:, :kk], kk)
+        ref = O.hsmla_block_forward(inp["x"], inp, staged=True,
+                                    sel=g["sel"][:, :kk], **kw)
+    for key in ("qkv", "qkv_hat", "o", "x1"):
+        assert_close(g[key], ref[key], wl.dtype, key)
+    assert_close(g["out"], ref["out"], wl.dtype, "out")
+
+
+def test_block_forward_f32():
+    wl = scaled(STAGE_CASES["block_small"], dtype="f32", grid_h=16, grid_w=32,
+                channels=64, heads=2)
+    inp = make_inputs(wl)
+    g = Run(wl, inp).block_forward()
+    ref = O.hsmla_block_forward(inp["x"], inp, **oracle_kwargs(wl))
+    np.testing.assert_array_equal(g["sel"][:, :wl.keep_blocks], ref["sel"])
+    assert_close(g["out"], ref["out"], "f32", "out")

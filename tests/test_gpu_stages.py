@@ -1,0 +1,174 @@
+"""Stage-wise GPU parity: each C entry point gets the same inputs as the
+oracle stage it implements.  Inputs of a stage are taken from the previous
+stage's GPU output so errors do not compound."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from efficient_vision_attention_amd import hsmla as H
+from efficient_vision_attention_amd.device import (DeviceModel, to_device,
+                                                   to_f32, to_host)
+from workloads import WORKLOADS, make_inputs, scaled
+
+from gpu_harness import (announce, assert_close, rnd_for, selection_band_check,
+                         shape_of)
+
+pytestmark = pytest.mark.gpu
+
+# Reduced shapes of the five workloads plus ragged ones: several tiles per
+# kernel, token counts and channel counts that are not tile multiples.
+STAGE_CASES = {
+    "tiny": WORKLOADS["tiny"],
+    "street_small": scaled(WORKLOADS["street"], batch=2, grid_h=32, grid_w=64),
+    "ct_small": scaled(WORKLOADS["ct"], batch=3, grid_h=48, grid_w=48),
+    "pathology_small": scaled(WORKLOADS["pathology"], batch=1, grid_h=64,
+                              grid_w=64),
+    "block_small": scaled(WORKLOADS["block"], batch=1, grid_h=32, grid_w=64,
+                          keep=0.25),
+    "ragged_bf16": scaled(WORKLOADS["street"], name="ragged_bf16", batch=3,
+                          grid_h=20, grid_w=36, channels=96, heads=3, block=4,
+                          window=10, keep=0.3),
+    "ragged_f32": scaled(WORKLOADS["tiny"], name="ragged_f32", batch=2,
+                         grid_h=12, grid_w=28, channels=96, heads=3,
+                         branches=(3, 5, 7), block=4, window=10, keep=0.4),
+}
+
+
+def _case(name):
+    wl = STAGE_CASES[name]
+    return wl, make_inputs(wl)
+
+
+@pytest.mark.parametrize("name", list(STAGE_CASES))
+def test_qkv_branches(name):
+    wl, inp = _case(name)
+    m = DeviceModel(shape_of(wl), inp)
+    x = to_device(inp["x"], wl.dtype)
+    qkv, qkvh = m.act(3), m.act(3)
+    ws = m.workspace(H.HSMLA_OP_QKV)
+    announce(f"hsmla_qkv_branches {name}")
+    H.hsmla_qkv_branches(m.desc, m.weights, x, qkv, qkvh, ws)
+    torch.cuda.synchronize()
+    rnd = rnd_for(wl)
+    g_qkv = to_host(qkv)
+    assert_close(g_qkv, rnd(O.qkv_projection(inp["x"], inp["w_qkv"])), wl.dtype, "qkv")
+    ref = rnd(O.multiscale_branches(g_qkv, inp["dw"], wl.grid_h, wl.grid_w))
+    assert_close(to_host(qkvh), ref, wl.dtype, "qkv_hat")
+
+
+def _oracle_qkv_hat(wl, inp):
+    rnd = rnd_for(wl)
+    qkv = rnd(O.qkv_projection(inp["x"], inp["w_qkv"]))
+    return qkv, rnd(O.multiscale_branches(qkv, inp["dw"], wl.grid_h, wl.grid_w))
+
+
+@pytest.mark.parametrize("name", list(STAGE_CASES))
+def test_linear_attn(name):
+    wl, inp = _case(name)
+    _, qkvh_ref = _oracle_qkv_hat(wl, inp)
+    m = DeviceModel(shape_of(wl), inp)
+    qkvh = to_device(qkvh_ref, wl.dtype)
+    o = m.act()
+    B, Hh = wl.batch, wl.heads
+    kv = torch.empty((B, Hh, 32, 32), dtype=torch.float32, device="cuda")
+    ksum = torch.empty((B, Hh, 32), dtype=torch.float32, device="cuda")
+    ws = m.workspace(H.HSMLA_OP_LINEAR)
+    announce(f"hsmla_linear_attn {name}")
+    H.hsmla_linear_attn(m.desc, qkvh, o, kv, ksum, ws)
+    torch.cuda.synchronize()
+    o_ref, Z, D = O.linear_attention(qkvh_ref, wl.heads)
+    # Z and D are float32 sums of exact products: relative error ~ 1e-6
+    scale = np.abs(Z).max()
+    np.testing.assert_allclose(to_host(kv), Z, rtol=1e-4, atol=1e-5 * scale)
+    np.testing.assert_allclose(to_host(ksum), D, rtol=1e-5, atol=1e-5)
+    assert_close(to_host(o), rnd_for(wl)(o_ref), wl.dtype, "o_lin")
+    # bitwise reproducible
+    o2 = m.act()
+    kv2 = torch.empty_like(kv)
+    ks2 = torch.empty_like(ksum)
+    H.hsmla_linear_attn(m.desc, qkvh, o2, kv2, ks2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(kv, kv2) and torch.equal(ksum, ks2)
+
+
+@pytest.mark.parametrize("name", list(STAGE_CASES))
+def test_gate_select_pooled(name):
+    wl, inp = _case(name)
+    _, qkvh_ref = _oracle_qkv_hat(wl, inp)
+    m = DeviceModel(shape_of(wl), inp)
+    qkvh = to_device(qkvh_ref, wl.dtype)
+    T, k = wl.num_blocks, wl.keep_blocks
+    scores = torch.empty((wl.batch, T), dtype=torch.float32, device="cuda")
+    sel = torch.empty((wl.batch, max(k, 1)), dtype=torch.int32, device="cuda")
+    announce(f"hsmla_gate_select pooled {name}")
+    H.hsmla_gate_select(m.desc, qkvh, m.t["gate_w"], m.t["gate_b"], None,
+                        scores, sel)
+    torch.cuda.synchronize()
+    ref = O.gate_scores(qkvh_ref, inp["gate_w"], inp["gate_b"], wl.grid_h,
+                        wl.grid_w, wl.block, wl.heads)
+    g = to_host(scores)
+    np.testing.assert_allclose(g, ref, rtol=0, atol=2e-6)
+    sel_g = sel.cpu().numpy()[:, :k]
+    # ranking decided in float32 on both sides
+    sel_ref = O.select_blocks(ref.astype(np.float32), k)
+    if not np.array_equal(sel_g, sel_ref):
+        selection_band_check(ref, g, sel_ref, sel_g, k)
+    # the GPU's own scores ranked by the oracle give the GPU's selection
+    np.testing.assert_array_equal(sel_g, O.select_blocks(g.astype(np.float32), k))
+
+
+@pytest.mark.parametrize("T,k,levels", [(16, 4, 3), (45, 14, 5), (1024, 52, 9),
+                                         (2000, 700, 17), (7, 7, 2), (64, 0, 4)])
+def test_gate_select_injected_scores_exact(T, k, levels):
+    """Exact float32 scores with many ties: the index list must equal the
+    oracle's bit for bit (ties to the lower block index, ascending)."""
+    rng = np.random.default_rng(T + k)
+    B = 3
+    scores = (rng.integers(0, levels, size=(B, T)) / levels).astype(np.float32)
+    desc = H.make_desc(batch=B, grid_h=1, grid_w=T, channels=32, heads=1,
+                       branches=(), block=1, window=1, keep_blocks=k, dtype="bf16")
+    s_in = torch.from_numpy(scores).cuda()
+    s_out = torch.zeros_like(s_in)
+    sel = torch.full((B, max(k, 1)), -1, dtype=torch.int32, device="cuda")
+    announce(f"hsmla_gate_select injected T={T} k={k}")
+    H.hsmla_gate_select(desc, None, None, None, s_in, s_out, sel)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy()[:, :k],
+                                  O.select_blocks(scores, k))
+    assert torch.equal(s_out, s_in)
+
+
+@pytest.mark.parametrize("name", list(STAGE_CASES))
+def test_sparse_softmax(name):
+    wl, inp = _case(name)
+    qkv_ref, qkvh_ref = _oracle_qkv_hat(wl, inp)
+    rnd = rnd_for(wl)
+    o_lin, _, _ = O.linear_attention(qkvh_ref, wl.heads)
+    o_lin = rnd(o_lin)
+    scores = O.gate_scores(qkvh_ref, inp["gate_w"], inp["gate_b"], wl.grid_h,
+                           wl.grid_w, wl.block, wl.heads)
+    k = wl.keep_blocks
+    sel_ref = O.select_blocks(scores.astype(np.float32), k)
+    m = DeviceModel(shape_of(wl), inp)
+    qkv = to_device(qkv_ref, wl.dtype)
+    qkvh = to_device(qkvh_ref, wl.dtype)
+    o = to_device(o_lin, wl.dtype)
+    o_before = o.clone()
+    sel = torch.from_numpy(sel_ref.astype(np.int32)).cuda().contiguous()
+    announce(f"hsmla_sparse_softmax {name} k={k}")
+    H.hsmla_sparse_softmax(m.desc, qkv, qkvh, sel, o)
+    torch.cuda.synchronize()
+    ref = O.refine_selected(qkv_ref, qkvh_ref, o_lin, sel_ref, wl.grid_h,
+                            wl.grid_w, wl.heads, wl.block, wl.window, rnd=rnd)
+    g = to_host(o)
+    assert_close(g, ref, wl.dtype, "o refined")
+    # tokens of unselected blocks are bitwise untouched
+    nbc = wl.grid_w // wl.block
+    ys, xs = np.divmod(np.arange(wl.tokens), wl.grid_w)
+    tblk = (ys // wl.block) * nbc + xs // wl.block
+    for b in range(wl.batch):
+        untouched = ~np.isin(tblk, sel_ref[b])
+        assert torch.equal(o[b][torch.from_numpy(untouched).cuda()],
+                           o_before[b][torch.from_numpy(untouched).cuda()])
