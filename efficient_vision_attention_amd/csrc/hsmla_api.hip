@@ -129,6 +129,31 @@ Layout layout(const Dims& D, int op) {
 
 inline char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// Optional per-launch event recording for the *_timed entry points: mark()
+// records events[i] on the stream just before launch i (and once more after
+// the last launch); without events it does nothing.
+struct Rec {
+  hipEvent_t* ev = nullptr;
+  const char** names = nullptr;
+  int cap = 0;
+  int n = 0;
+  hipStream_t s = nullptr;
+  bool ok = true;
+  void mark(const char* name) {
+    if (ev && n < cap) {
+      if (hipEventRecord(ev[n], s) != hipSuccess) ok = false;
+      if (names) names[n] = name;
+    }
+    ++n;
+  }
+  void end() {
+    if (ev && n < cap) {
+      if (hipEventRecord(ev[n], s) != hipSuccess) ok = false;
+      if (names) names[n] = "end";
+    }
+  }
+};
+
 hsmla_status hip_status(hipError_t e) {
   return e == hipSuccess ? HSMLA_OK : HSMLA_ERR_HIP;
 }
@@ -153,11 +178,14 @@ hsmla_status check_weights(const hsmla_desc* d, const hsmla_weights* w) {
 // Steps 1-2 with caller-provided buffers.
 hsmla_status run_qkv(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
                      const void* x, void* qkv, void* qkv_hat, float* taps,
-                     hipStream_t s) {
+                     hipStream_t s, Rec& r) {
+  r.mark("qkv_gemm");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, x, w->w_qkv, nullptr, qkv, (int)D.P,
                                3 * D.C, D.C, s));
+  r.mark("dw_taps");
   HSMLA_TRY(hsmla::launch_dw_taps(D.bf, w->dw, d->branch_k, d->n_branches,
                                   D.kmax, 3 * D.C, 1, taps, s));
+  r.mark("dwconv_qkv");
   HSMLA_TRY(hsmla::launch_dwconv(D.bf, qkv, qkv_hat, taps, D.kmax, D.B, D.gh,
                                  D.gw, 3 * D.C, false, s));
   return HSMLA_OK;
@@ -166,7 +194,7 @@ hsmla_status run_qkv(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
 // Steps 1-5 into the workspace views (o holds the refined output).
 hsmla_status run_module(const Dims& D, const hsmla_desc* d,
                         const hsmla_weights* w, const void* x, void* ws,
-                        const Layout& L, hipStream_t s) {
+                        const Layout& L, hipStream_t s, Rec& r) {
   void* qkv = at(ws, L.qkv);
   void* qkvh = at(ws, L.qkv_hat);
   void* o = at(ws, L.o);
@@ -176,13 +204,18 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
   float* taps = reinterpret_cast<float*>(at(ws, L.taps));
   float* scores = reinterpret_cast<float*>(at(ws, L.scores));
   int32_t* sel = reinterpret_cast<int32_t*>(at(ws, L.sel));
-  hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, s);
+  hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, s, r);
   if (st != HSMLA_OK) return st;
+  r.mark("kv_state");
   HSMLA_TRY(hsmla::launch_kv_state(D.bf, qkvh, kv, ksum, part, D.B, D.N, D.H, s));
+  r.mark("lin_apply");
   HSMLA_TRY(hsmla::launch_lin_apply(D.bf, qkvh, kv, ksum, o, D.B, D.N, D.H, s));
+  r.mark("gate_scores");
   HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b, scores,
                                       D.B, D.gh, D.gw, D.H, D.Bs, s));
+  r.mark("topk");
   HSMLA_TRY(hsmla::launch_topk(scores, nullptr, sel, D.B, D.T, D.k, s));
+  r.mark("sparse_softmax");
   HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, sel, o, D.B, D.gh, D.gw, D.H,
                                  D.Bs, D.w, D.k, s));
   return HSMLA_OK;
@@ -249,9 +282,10 @@ hsmla_status hsmla_qkv_branches(const hsmla_desc* desc, const hsmla_weights* w,
     return HSMLA_ERR_ALIGN;
   const Layout L = layout(D, HSMLA_OP_QKV);
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
+  Rec r;
   return run_qkv(D, desc, w, x, qkv, qkv_hat,
                  reinterpret_cast<float*>(at(ws, L.taps)),
-                 static_cast<hipStream_t>(stream));
+                 static_cast<hipStream_t>(stream), r);
 }
 
 hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
@@ -313,9 +347,13 @@ hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
                                          static_cast<hipStream_t>(stream)));
 }
 
-hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
-                           const void* x, void* y, void* ws, size_t ws_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+hsmla_status forward_impl(const hsmla_desc* desc, const hsmla_weights* w,
+                          const void* x, void* y, void* ws, size_t ws_bytes,
+                          hipStream_t s, Rec& r) {
   Dims D;
   hsmla_status st = check_desc(desc, &D);
   if (st != HSMLA_OK) return st;
@@ -324,16 +362,17 @@ hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 16)) return HSMLA_ERR_ALIGN;
   const Layout L = layout(D, HSMLA_OP_FORWARD);
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = run_module(D, desc, w, x, ws, L, s)) != HSMLA_OK) return st;
-  return hip_status(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, nullptr, y,
-                                       (int)D.P, D.C, D.C, s));
+  if ((st = run_module(D, desc, w, x, ws, L, s, r)) != HSMLA_OK) return st;
+  r.mark("out_proj");
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, nullptr, y, (int)D.P,
+                               D.C, D.C, s));
+  r.end();
+  return r.ok ? HSMLA_OK : HSMLA_ERR_HIP;
 }
 
-hsmla_status hsmla_block_forward(const hsmla_desc* desc, const hsmla_weights* w,
-                                 const hsmla_ffn_weights* f, const void* x,
-                                 void* out, void* ws, size_t ws_bytes,
-                                 void* stream) {
+hsmla_status block_impl(const hsmla_desc* desc, const hsmla_weights* w,
+                        const hsmla_ffn_weights* f, const void* x, void* out,
+                        void* ws, size_t ws_bytes, hipStream_t s, Rec& r) {
   Dims D;
   hsmla_status st = check_desc(desc, &D);
   if (st != HSMLA_OK) return st;
@@ -349,25 +388,94 @@ hsmla_status hsmla_block_forward(const hsmla_desc* desc, const hsmla_weights* w,
     return HSMLA_ERR_ALIGN;
   const Layout L = layout(D, HSMLA_OP_BLOCK);
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int P = (int)D.P, C = D.C;
   void* xn = at(ws, L.xn);
   void* x1 = at(ws, L.x1);
   void* h1 = at(ws, L.h1);
   void* h2 = at(ws, L.h2);
   float* ftaps = reinterpret_cast<float*>(at(ws, L.ffn_taps));
+  r.mark("layernorm1");
   HSMLA_TRY(hsmla::launch_layernorm(D.bf, x, f->ln1_g, f->ln1_b, xn, P, C, s));
-  if ((st = run_module(D, desc, w, xn, ws, L, s)) != HSMLA_OK) return st;
+  if ((st = run_module(D, desc, w, xn, ws, L, s, r)) != HSMLA_OK) return st;
   // x1 = x + O W_o (residual fused into the projection epilogue)
+  r.mark("out_proj_residual");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, x, x1, P, C, C, s));
+  r.mark("layernorm2");
   HSMLA_TRY(hsmla::launch_layernorm(D.bf, x1, f->ln2_g, f->ln2_b, xn, P, C, s));
+  r.mark("ffn1_gemm");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, xn, f->w1, nullptr, h1, P, 4 * C, C, s));
   const void* ffn_k[1] = {f->dw_ffn};
   const int ffn_ks[1] = {3};
+  r.mark("ffn_dw_taps");
   HSMLA_TRY(hsmla::launch_dw_taps(D.bf, ffn_k, ffn_ks, 1, 3, 4 * C, 0, ftaps, s));
+  r.mark("ffn_dwconv_gelu");
   HSMLA_TRY(hsmla::launch_dwconv(D.bf, h1, h2, ftaps, 3, D.B, D.gh, D.gw, 4 * C,
                                  true, s));
-  return hip_status(hsmla::launch_gemm(D.bf, h2, f->w2, x1, out, P, C, 4 * C, s));
+  r.mark("ffn2_gemm_residual");
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, h2, f->w2, x1, out, P, C, 4 * C, s));
+  r.end();
+  return r.ok ? HSMLA_OK : HSMLA_ERR_HIP;
+}
+
+Rec make_rec(void* const* events, const char** names, int32_t n_events,
+             hipStream_t s) {
+  Rec r;
+  r.ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  r.names = names;
+  r.cap = n_events;
+  r.s = s;
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
+                           const void* x, void* y, void* ws, size_t ws_bytes,
+                           void* stream) {
+  Rec r;
+  return forward_impl(desc, w, x, y, ws, ws_bytes,
+                      static_cast<hipStream_t>(stream), r);
+}
+
+hsmla_status hsmla_block_forward(const hsmla_desc* desc, const hsmla_weights* w,
+                                 const hsmla_ffn_weights* f, const void* x,
+                                 void* out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  Rec r;
+  return block_impl(desc, w, f, x, out, ws, ws_bytes,
+                    static_cast<hipStream_t>(stream), r);
+}
+
+hsmla_status hsmla_forward_timed(const hsmla_desc* desc, const hsmla_weights* w,
+                                 const void* x, void* y, void* ws,
+                                 size_t ws_bytes, void* stream,
+                                 void* const* events, const char** names,
+                                 int32_t n_events, int32_t* n_launches) {
+  if (!events || !n_launches || n_events < 1) return HSMLA_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Rec r = make_rec(events, names, n_events, s);
+  const hsmla_status st = forward_impl(desc, w, x, y, ws, ws_bytes, s, r);
+  *n_launches = r.n;
+  if (st == HSMLA_OK && r.n + 1 > n_events) return HSMLA_ERR_ARG;
+  return st;
+}
+
+hsmla_status hsmla_block_forward_timed(const hsmla_desc* desc,
+                                       const hsmla_weights* w,
+                                       const hsmla_ffn_weights* f,
+                                       const void* x, void* out, void* ws,
+                                       size_t ws_bytes, void* stream,
+                                       void* const* events, const char** names,
+                                       int32_t n_events, int32_t* n_launches) {
+  if (!events || !n_launches || n_events < 1) return HSMLA_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Rec r = make_rec(events, names, n_events, s);
+  const hsmla_status st = block_impl(desc, w, f, x, out, ws, ws_bytes, s, r);
+  *n_launches = r.n;
+  if (st == HSMLA_OK && r.n + 1 > n_events) return HSMLA_ERR_ARG;
+  return st;
 }
 
 }  // extern "C"

@@ -29,6 +29,8 @@ EXPORTED = (
     "hsmla_sparse_softmax",
     "hsmla_forward",
     "hsmla_block_forward",
+    "hsmla_forward_timed",
+    "hsmla_block_forward_timed",
     "hsmla_status_string",
 )
 
@@ -101,6 +103,11 @@ def library():
             "hsmla_forward": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, SZ, VP],
             "hsmla_block_forward": [P(hsmla_desc), P(hsmla_weights), P(hsmla_ffn_weights),
                                     VP, VP, VP, SZ, VP],
+            "hsmla_forward_timed": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, SZ, VP,
+                                    P(VP), P(ctypes.c_char_p), I32, P(I32)],
+            "hsmla_block_forward_timed": [P(hsmla_desc), P(hsmla_weights),
+                                          P(hsmla_ffn_weights), VP, VP, VP, SZ, VP,
+                                          P(VP), P(ctypes.c_char_p), I32, P(I32)],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -220,3 +227,29 @@ def hsmla_block_forward(desc, weights, ffn, x, out, ws):
                                          _ptr(ws), ws.numel() * ws.element_size(),
                                          _stream()),
            "hsmla_block_forward")
+
+
+def _timed(fn, where, args, events):
+    n = len(events)
+    ev = (ctypes.c_void_p * n)(*events)
+    names = (ctypes.c_char_p * n)()
+    count = ctypes.c_int32(0)
+    _check(fn(*args, ev, names, n, ctypes.byref(count)), where)
+    return [names[i].decode() for i in range(count.value + 1)]
+
+
+def hsmla_forward_timed(desc, weights, x, y, ws, events):
+    """hsmla_forward with an event recorded before every launch and after the
+    last; `events` are raw hipEvent_t handles.  Returns the launch names."""
+    lib = library()
+    return _timed(lib.hsmla_forward_timed, "hsmla_forward_timed",
+                  (ctypes.byref(desc), ctypes.byref(weights), _ptr(x), _ptr(y),
+                   _ptr(ws), ws.numel() * ws.element_size(), _stream()), events)
+
+
+def hsmla_block_forward_timed(desc, weights, ffn, x, out, ws, events):
+    lib = library()
+    return _timed(lib.hsmla_block_forward_timed, "hsmla_block_forward_timed",
+                  (ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(ffn),
+                   _ptr(x), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                   _stream()), events)

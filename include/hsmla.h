@@ -190,6 +190,29 @@ hsmla_status hsmla_block_forward(const hsmla_desc* desc,
                                  void* out, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Same work, kernels and stream order as hsmla_forward /
+ * hsmla_block_forward, plus an event recorded on `stream` before each kernel
+ * launch and one after the last, for per-kernel timing by the caller.
+ * events: n_events hipEvent_t handles created by the caller; names
+ * (nullable): receives a static name per recorded event ("end" for the
+ * last).  *n_launches receives the number of kernel launches L; events
+ * 0..L are recorded when n_events >= L + 1, otherwise only the first
+ * n_events and HSMLA_ERR_ARG is returned after the work is enqueued. */
+hsmla_status hsmla_forward_timed(const hsmla_desc* desc,
+                                 const hsmla_weights* w, const void* x,
+                                 void* y, void* ws, size_t ws_bytes,
+                                 void* stream, void* const* events,
+                                 const char** names, int32_t n_events,
+                                 int32_t* n_launches);
+hsmla_status hsmla_block_forward_timed(const hsmla_desc* desc,
+                                       const hsmla_weights* w,
+                                       const hsmla_ffn_weights* f,
+                                       const void* x, void* out, void* ws,
+                                       size_t ws_bytes, void* stream,
+                                       void* const* events,
+                                       const char** names, int32_t n_events,
+                                       int32_t* n_launches);
+
 /* Static description of a status code. */
 const char* hsmla_status_string(int32_t status);
 
