@@ -6,6 +6,14 @@
 // identity and all branches are folded into one kmax x kmax tap set per
 // channel before the convolution runs.  The FFN's 3x3 depthwise conv (FT 3.5
 // block equation) uses the same kernel with a GELU epilogue.
+//
+// Kernel shape: a workgroup owns 16 columns x 64 channels of a strip of 32
+// output rows.  It streams the input rows of the strip (plus the vertical
+// halo) through a double-buffered LDS row that carries the horizontal halo;
+// each thread keeps the kmax partial output rows that the current input row
+// feeds in registers, so every input element is read from HBM once and from
+// LDS kmax times.  Each thread handles 4 consecutive channels (8-byte bf16
+// accesses, 128 contiguous bytes per 16 lanes).
 #include "common.h"
 #include "kernels.h"
 
@@ -41,46 +49,159 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
 }
 
-// One thread per output element, channels fastest (coalesced).
-template <typename T, bool GELU>
-__global__ __launch_bounds__(256) void dwconv_simple(
+constexpr int TW = 16;   // output columns per workgroup
+constexpr int CG = 16;   // 4-channel groups per workgroup (64 channels)
+constexpr int TH = 32;   // output rows per workgroup strip
+
+struct f4 {
+  float v[4];
+};
+
+template <typename T>
+__device__ __forceinline__ f4 load4(const T* p);
+template <>
+__device__ __forceinline__ f4 load4<bf16>(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  f4 r;
+  r.v[0] = __uint_as_float(u.x << 16);
+  r.v[1] = __uint_as_float(u.x & 0xffff0000u);
+  r.v[2] = __uint_as_float(u.y << 16);
+  r.v[3] = __uint_as_float(u.y & 0xffff0000u);
+  return r;
+}
+template <>
+__device__ __forceinline__ f4 load4<float>(const float* p) {
+  const float4 u = *reinterpret_cast<const float4*>(p);
+  return f4{{u.x, u.y, u.z, u.w}};
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float* v);
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, const float* v) {
+  uint2 o;
+  o.x = (uint32_t)from_f32<bf16>(v[0]).u | ((uint32_t)from_f32<bf16>(v[1]).u << 16);
+  o.y = (uint32_t)from_f32<bf16>(v[2]).u | ((uint32_t)from_f32<bf16>(v[3]).u << 16);
+  *reinterpret_cast<uint2*>(p) = o;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// grid: (column tiles * channel tiles, row strips, batch); 256 threads.
+template <typename T, int K, bool GELU>
+__global__ __launch_bounds__(256) void dwconv_rows(
     const T* __restrict__ in, T* __restrict__ out,
-    const float* __restrict__ weff, int kmax, int batch, int gh, int gw,
-    int ch) {
-  const size_t total = (size_t)batch * gh * gw * ch;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int c = idx % ch;
-  size_t rest = idx / ch;
-  const int x = rest % gw;
-  rest /= gw;
-  const int y = rest % gh;
-  const int b = rest / gh;
-  const int r = (kmax - 1) / 2;
-  float acc = 0.f;
-  for (int dy = 0; dy < kmax; ++dy) {
-    const int yy = y + dy - r;
-    if (yy < 0 || yy >= gh) continue;
-    for (int dx = 0; dx < kmax; ++dx) {
-      const int xx = x + dx - r;
-      if (xx < 0 || xx >= gw) continue;
-      acc = fmaf(weff[(size_t)(dy * kmax + dx) * ch + c],
-                 to_f32(in[(((size_t)b * gh + yy) * gw + xx) * ch + c]), acc);
+    const float* __restrict__ weff, int gh, int gw, int ch, int col_tiles) {
+  constexpr int R = (K - 1) / 2;
+  constexpr int SEG = TW + 2 * R;  // columns held per LDS row
+  __shared__ float4 row[2][SEG * CG];
+
+  const int tc = threadIdx.x % CG;   // channel group within the tile
+  const int tx = threadIdx.x / CG;   // output column within the tile
+  const int x0 = (blockIdx.x % col_tiles) * TW;
+  const int c0 = (blockIdx.x / col_tiles) * (CG * 4);
+  const int y0 = blockIdx.y * TH;
+  const int b = blockIdx.z;
+  const int c = c0 + tc * 4;
+  const bool c_ok = c < ch;
+  const int x = x0 + tx;
+  const size_t img = (size_t)b * gh * gw;
+
+  // this thread's taps, K x K x 4 channels
+  float w[K][K][4];
+#pragma unroll
+  for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+    for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[ky][kx][j] = c_ok ? weff[(size_t)(ky * K + kx) * ch + c + j] : 0.f;
+
+  float acc[K][4];
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+  const int y_end = min(gh, y0 + TH);
+  const int r_begin = y0 - R, r_end = y_end + R;
+
+  auto fill = [&](int buf, int r) {
+    for (int e = threadIdx.x; e < SEG * CG; e += 256) {
+      const int sx = e / CG, sc = e % CG;
+      const int gx = x0 - R + sx, gc = c0 + sc * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r >= 0 && r < gh && gx >= 0 && gx < gw && gc < ch) {
+        const f4 q = load4<T>(in + (img + (size_t)r * gw + gx) * ch + gc);
+        v = make_float4(q.v[0], q.v[1], q.v[2], q.v[3]);
+      }
+      row[buf][e] = v;
     }
+  };
+
+  fill(0, r_begin);
+  __syncthreads();
+  for (int r = r_begin; r < r_end; ++r) {
+    const int buf = (r - r_begin) & 1;
+    if (r + 1 < r_end) fill(buf ^ 1, r + 1);
+    float xin[K][4];
+#pragma unroll
+    for (int kx = 0; kx < K; ++kx) {
+      const float4 v = row[buf][(tx + kx) * CG + tc];
+      xin[kx][0] = v.x;
+      xin[kx][1] = v.y;
+      xin[kx][2] = v.z;
+      xin[kx][3] = v.w;
+    }
+    // input row r feeds output row r - R + i with vertical tap K - 1 - i
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+#pragma unroll
+      for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = fmaf(w[K - 1 - i][kx][j], xin[kx][j], acc[i][j]);
+    const int yo = r - R;  // completed output row
+    if (yo >= y0 && yo < y_end && x < gw && c_ok) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = GELU ? gelu_erf(acc[0][j]) : acc[0][j];
+      store4<T>(out + (img + (size_t)yo * gw + x) * ch + c, v);
+    }
+#pragma unroll
+    for (int i = 0; i + 1 < K; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = acc[i + 1][j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[K - 1][j] = 0.f;
+    __syncthreads();
   }
-  if (GELU) acc = gelu_erf(acc);
-  out[idx] = from_f32<T>(acc);
+}
+
+template <typename T, int K, bool GELU>
+hipError_t run_dw(const void* in, void* out, const float* weff, int batch,
+                  int gh, int gw, int ch, hipStream_t s) {
+  const int col_tiles = (gw + TW - 1) / TW;
+  const int ch_tiles = (ch + CG * 4 - 1) / (CG * 4);
+  dim3 grid(col_tiles * ch_tiles, (gh + TH - 1) / TH, batch);
+  dwconv_rows<T, K, GELU><<<grid, 256, 0, s>>>(
+      static_cast<const T*>(in), static_cast<T*>(out), weff, gh, gw, ch,
+      col_tiles);
+  return hipGetLastError();
 }
 
 template <typename T, bool GELU>
-hipError_t run_dw(const void* in, void* out, const float* weff, int kmax,
-                  int batch, int gh, int gw, int ch, hipStream_t s) {
-  const size_t total = (size_t)batch * gh * gw * ch;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
-  dwconv_simple<T, GELU><<<blocks, 256, 0, s>>>(
-      static_cast<const T*>(in), static_cast<T*>(out), weff, kmax, batch, gh,
-      gw, ch);
-  return hipGetLastError();
+hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
+                      int batch, int gh, int gw, int ch, hipStream_t s) {
+  switch (kmax) {
+    case 1: return run_dw<T, 1, GELU>(in, out, weff, batch, gh, gw, ch, s);
+    case 3: return run_dw<T, 3, GELU>(in, out, weff, batch, gh, gw, ch, s);
+    case 5: return run_dw<T, 5, GELU>(in, out, weff, batch, gh, gw, ch, s);
+    case 7: return run_dw<T, 7, GELU>(in, out, weff, batch, gh, gw, ch, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -105,10 +226,10 @@ hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
                          int kmax, int batch, int gh, int gw, int ch,
                          bool gelu, hipStream_t s) {
   if (bf)
-    return gelu ? run_dw<bf16, true>(in, out, weff, kmax, batch, gh, gw, ch, s)
-                : run_dw<bf16, false>(in, out, weff, kmax, batch, gh, gw, ch, s);
-  return gelu ? run_dw<float, true>(in, out, weff, kmax, batch, gh, gw, ch, s)
-              : run_dw<float, false>(in, out, weff, kmax, batch, gh, gw, ch, s);
+    return gelu ? dispatch_k<bf16, true>(kmax, in, out, weff, batch, gh, gw, ch, s)
+                : dispatch_k<bf16, false>(kmax, in, out, weff, batch, gh, gw, ch, s);
+  return gelu ? dispatch_k<float, true>(kmax, in, out, weff, batch, gh, gw, ch, s)
+              : dispatch_k<float, false>(kmax, in, out, weff, batch, gh, gw, ch, s);
 }
 
 }  // namespace hsmla

@@ -9,8 +9,9 @@
 
 namespace hsmla {
 
-// C[M][N] = A[M][K] . B[K][N] (+ R[M][N] when R != nullptr), row-major.
-hipError_t launch_gemm(bool bf, const void* A, const void* B, const void* R,
+// C[M][N] = A[M][K] . W[N][K]^T (+ R[M][N] when R != nullptr), row-major.
+// N and K must be multiples of 32 (8-element chunks are loaded whole).
+hipError_t launch_gemm(bool bf, const void* A, const void* W, const void* R,
                        void* C, int M, int N, int K, hipStream_t s);
 
 // Effective depthwise taps: weff[tap][ch] (float32, kmax x kmax taps) =

@@ -9,14 +9,14 @@
  *        "Technische Samenvatting".
  *
  * Module computed (FT 3.1-3.3, 3.5, 3.6):
- *   QKV     = X W_qkv                                  (projection, no bias)
+ *   QKV     = X W_qkv^T                                (projection, no bias)
  *   T_hat   = T + sum_s DWConv_{k_s}(T)  for T in Q,K,V (multi-scale branches)
  *   Z, D    = sum_j relu(K_hat_j)^T V_hat_j, sum_j relu(K_hat_j)   (per head)
  *   O_lin   = relu(Q_hat) Z / (relu(Q_hat) . D)           (0 when the sum is 0)
  *   M_t     = mean_h sigmoid(w_h . meanpool_t[Q_hat;K_hat;V_hat]_h + b_h)
  *   sel     = the keep_blocks blocks with the largest M_t (ties -> lower t)
  *   O_i     = O_lin_i + softmax-attn(q_i, K_W, V_W) - lin-local_i  on sel
- *   Y       = O W_o
+ *   Y       = O W_o^T
  *
  * Conventions shared by every entry point:
  *   - Layout: a token grid of grid_h x grid_w tokens, token n = y*grid_w + x.
@@ -37,6 +37,8 @@
  *   - Errors: argument errors are detected on the host before any HIP call
  *     and returned as a negative hsmla_status; nothing is launched then.  A
  *     failed launch returns HSMLA_ERR_HIP.  No exception crosses the ABI.
+ *   - Weights of the dense projections are [out][in] row-major (the layout
+ *     of torch.nn.Linear.weight) and are applied as y = x . W^T.
  *   - Alignment: activation, weight and workspace pointers must be 16-byte
  *     aligned; float32 parameter and index pointers 4-byte aligned.
  *   - Threading: no mutable global state; calls on different streams may
@@ -89,8 +91,8 @@ typedef struct {
 } hsmla_desc;
 
 typedef struct {
-  const void* w_qkv;   /* [C][3C], used as x . W                        */
-  const void* w_o;     /* [C][C]                                        */
+  const void* w_qkv;   /* [3C][C]: qkv = x . w_qkv^T                    */
+  const void* w_o;     /* [C][C]:  y = o . w_o^T                        */
   const void* dw[3];   /* branch s: [3C][k_s][k_s] cross-correlation     */
   const float* gate_w; /* [H][3*head_dim]: weights on [q; k; v] means    */
   const float* gate_b; /* [H]                                            */
@@ -99,9 +101,9 @@ typedef struct {
 typedef struct {
   const float* ln1_g; const float* ln1_b; /* [C] LayerNorm before HSMLA */
   const float* ln2_g; const float* ln2_b; /* [C] LayerNorm before FFN   */
-  const void* w1;      /* [C][4C]                                       */
+  const void* w1;      /* [4C][C]                                       */
   const void* dw_ffn;  /* [4C][3][3]                                    */
-  const void* w2;      /* [4C][C]                                       */
+  const void* w2;      /* [C][4C]                                       */
 } hsmla_ffn_weights;
 
 /* Pointers into a forward/block workspace, for inspection. */
@@ -127,7 +129,7 @@ hsmla_status hsmla_workspace_views(const hsmla_desc* desc, int32_t op,
                                    void* ws, hsmla_views* views);
 
 /* Steps 1-2 (FT 3.1 projection; abstract and EX section 2 for the
- * multi-scale depthwise branches): qkv = x W_qkv and
+ * multi-scale depthwise branches): qkv = x W_qkv^T and
  * qkv_hat = qkv + sum_s DWConv_{k_s}(qkv), zero padding (k-1)/2, no bias.
  * x [B][N][C]; qkv, qkv_hat [B][N][3C]; ws sized for HSMLA_OP_QKV. */
 hsmla_status hsmla_qkv_branches(const hsmla_desc* desc,
@@ -171,7 +173,7 @@ hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
                                   const void* qkv_hat, const int32_t* sel,
                                   void* o, void* stream);
 
-/* The whole module: y = HSMLA(x) = O W_o, steps 1-5 then the output
+/* The whole module: y = HSMLA(x) = O W_o^T, steps 1-5 then the output
  * projection (FT 3.6 stages 1-5).  x, y [B][N][C]; ws sized for
  * HSMLA_OP_FORWARD; intermediates readable through hsmla_workspace_views. */
 hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
@@ -181,7 +183,7 @@ hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
 /* One block (FT 3.5 block equation, with its depthwise and FFN steps fused
  * into one FFN-DWConv sandwich):
  *   x1  = x + HSMLA(LN1(x))
- *   out = x1 + W2 GELU(DWConv3x3(W1 LN2(x1)))
+ *   out = x1 + GELU(DWConv3x3(LN2(x1) W1^T)) W2^T
  * LayerNorm: biased variance, eps 1e-5; GELU: exact erf form.  x, out
  * [B][N][C] (must not overlap); ws sized for HSMLA_OP_BLOCK. */
 hsmla_status hsmla_block_forward(const hsmla_desc* desc,
