@@ -99,7 +99,7 @@ Layout layout(const Dims& D, int op) {
   };
   const size_t bh = (size_t)D.B * D.H;
   const size_t part_bytes =
-      bh * kv_chunks(D.B, D.H, D.N) * (kHeadDim * kHeadDim + kHeadDim) * 4;
+      bh * kv_chunks(D.bf, D.B, D.H, D.N) * (kHeadDim * kHeadDim + kHeadDim) * 4;
   const size_t tap_bytes = (size_t)D.kmax * D.kmax * 3 * D.C * 4;
   if (op == HSMLA_OP_QKV) {
     L.taps = take(tap_bytes);

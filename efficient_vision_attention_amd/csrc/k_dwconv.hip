@@ -25,24 +25,23 @@ struct KernelSet {
   int k[3];
 };
 
+// grid covers kmax*kmax taps x ch channels, one (tap, channel) per thread.
 template <typename T>
 __global__ void dw_taps_kernel(KernelSet ks, int nk, int kmax, int ch,
                                int identity, float* __restrict__ weff) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= ch) return;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= kmax * kmax * ch) return;
+  const int c = idx % ch, tap = idx / ch;
+  const int dy = tap / kmax, dx = tap % kmax;
   const int rmax = (kmax - 1) / 2;
-  for (int dy = 0; dy < kmax; ++dy) {
-    for (int dx = 0; dx < kmax; ++dx) {
-      float v = (identity && dy == rmax && dx == rmax) ? 1.f : 0.f;
-      for (int i = 0; i < nk; ++i) {
-        const int k = ks.k[i], r = (k - 1) / 2;
-        const int ky = dy - rmax + r, kx = dx - rmax + r;
-        if (ky >= 0 && ky < k && kx >= 0 && kx < k)
-          v += to_f32(static_cast<const T*>(ks.p[i])[((size_t)c * k + ky) * k + kx]);
-      }
-      weff[(size_t)(dy * kmax + dx) * ch + c] = v;
-    }
+  float v = (identity && dy == rmax && dx == rmax) ? 1.f : 0.f;
+  for (int i = 0; i < nk; ++i) {
+    const int k = ks.k[i], r = (k - 1) / 2;
+    const int ky = dy - rmax + r, kx = dx - rmax + r;
+    if (ky >= 0 && ky < k && kx >= 0 && kx < k)
+      v += to_f32(static_cast<const T*>(ks.p[i])[((size_t)c * k + ky) * k + kx]);
   }
+  weff[idx] = v;
 }
 
 __device__ __forceinline__ float gelu_erf(float x) {
@@ -128,24 +127,38 @@ __global__ __launch_bounds__(256) void dwconv_rows(
   const int y_end = min(gh, y0 + TH);
   const int r_begin = y0 - R, r_end = y_end + R;
 
-  auto fill = [&](int buf, int r) {
-    for (int e = threadIdx.x; e < SEG * CG; e += 256) {
+  // Each thread stages up to two 4-channel vectors of an input row segment.
+  // Loads for row r+1 are issued one iteration ahead and written to LDS
+  // after the compute of row r, so their latency overlaps that compute.
+  constexpr int kFill = (SEG * CG + 255) / 256;
+  auto issue = [&](f4 (&st)[kFill], int r) {
+#pragma unroll
+    for (int i = 0; i < kFill; ++i) {
+      const int e = threadIdx.x + 256 * i;
       const int sx = e / CG, sc = e % CG;
       const int gx = x0 - R + sx, gc = c0 + sc * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r >= 0 && r < gh && gx >= 0 && gx < gw && gc < ch) {
-        const f4 q = load4<T>(in + (img + (size_t)r * gw + gx) * ch + gc);
-        v = make_float4(q.v[0], q.v[1], q.v[2], q.v[3]);
-      }
-      row[buf][e] = v;
+      if (e < SEG * CG && r >= 0 && r < gh && gx >= 0 && gx < gw && gc < ch)
+        st[i] = load4<T>(in + (img + (size_t)r * gw + gx) * ch + gc);
+      else
+        st[i] = f4{{0.f, 0.f, 0.f, 0.f}};
+    }
+  };
+  auto commit = [&](const f4 (&st)[kFill], int buf) {
+#pragma unroll
+    for (int i = 0; i < kFill; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      if (e < SEG * CG)
+        row[buf][e] = make_float4(st[i].v[0], st[i].v[1], st[i].v[2], st[i].v[3]);
     }
   };
 
-  fill(0, r_begin);
+  f4 stage[kFill];
+  issue(stage, r_begin);
+  commit(stage, 0);
+  if (r_begin + 1 < r_end) issue(stage, r_begin + 1);
   __syncthreads();
   for (int r = r_begin; r < r_end; ++r) {
     const int buf = (r - r_begin) & 1;
-    if (r + 1 < r_end) fill(buf ^ 1, r + 1);
     float xin[K][4];
 #pragma unroll
     for (int kx = 0; kx < K; ++kx) {
@@ -154,6 +167,11 @@ __global__ __launch_bounds__(256) void dwconv_rows(
       xin[kx][1] = v.y;
       xin[kx][2] = v.z;
       xin[kx][3] = v.w;
+    }
+    // row r+1 (already in flight) goes to the other buffer; row r+2 is issued
+    if (r + 1 < r_end) {
+      commit(stage, buf ^ 1);
+      if (r + 2 < r_end) issue(stage, r + 2);
     }
     // input row r feeds output row r - R + i with vertical tap K - 1 - i
 #pragma unroll
@@ -214,7 +232,7 @@ hipError_t launch_dw_taps(bool bf, const void* const* kernels, const int* ks,
     set.p[i] = kernels[i];
     set.k[i] = ks[i];
   }
-  const unsigned blocks = (unsigned)((ch + 255) / 256);
+  const unsigned blocks = (unsigned)((kmax * kmax * ch + 255) / 256);
   if (bf)
     dw_taps_kernel<bf16><<<blocks, 256, 0, s>>>(set, nk, kmax, ch, identity, weff);
   else

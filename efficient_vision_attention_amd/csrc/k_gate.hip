@@ -31,12 +31,24 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(
   const int nbc = gwid / block;
   const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
   const size_t img = (size_t)b * gh * gwid;
-  for (int c = threadIdx.x; c < C3; c += blockDim.x) {
-    float s = 0.f;
-    for (int yy = 0; yy < block; ++yy)
-      for (int xx = 0; xx < block; ++xx)
-        s += to_f32(qkvh[(img + (size_t)(r0 + yy) * gwid + c0 + xx) * C3 + c]);
-    fsum[c] = s;
+  // 16-byte vectors of channels, summed over the block's tokens in row-major
+  // token order
+  constexpr int V = 16 / sizeof(T);
+  for (int cv = threadIdx.x; cv < C3 / V; cv += blockDim.x) {
+    float s[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) s[j] = 0.f;
+    for (int yy = 0; yy < block; ++yy) {
+      const T* rowp = qkvh + (img + (size_t)(r0 + yy) * gwid + c0) * C3 + cv * V;
+      for (int xx = 0; xx < block; ++xx) {
+        const uint4 u = *reinterpret_cast<const uint4*>(rowp + (size_t)xx * C3);
+        const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+        for (int j = 0; j < V; ++j) s[j] += to_f32(e[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) fsum[cv * V + j] = s[j];
   }
   __syncthreads();
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;

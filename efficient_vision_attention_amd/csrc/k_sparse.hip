@@ -106,6 +106,254 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bfloat16 MFMA kernel
+//
+// Workgroup = one (selected block, head); 2 * nqt waves for nqt tiles of 32
+// queries.  Wave w works on query tile w % nqt along one of two paths:
+//   path 0 (softmax): S^T = K Q^T tile by tile, online softmax per query,
+//                     O_local^T += V^T P^T;
+//   path 1 (linear):  A^T = relu(K^) relu(Q^)^T, den += column sums,
+//                     O_linloc^T += V^^T A^T.
+// Every 32x32 accumulator tile holds one query per lane column, so row
+// statistics of a query live in one lane pair (l, l ^ 32).  The P^T / A^T
+// accumulator registers are fed back as the B operand of the next MFMA with
+// the key order they already have; V and V^ are staged transposed in LDS in
+// that same order.  Keys are streamed in tiles of 64 through double-buffered
+// LDS.  Path 1 hands its normalised result to path 0 through LDS, and path 0
+// writes O_lin + O_local - O_linloc.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int KT = 64;            // keys per LDS tile
+constexpr int KS = kD + 8;        // bf16 stride of key-major rows
+constexpr int VS = KT + 8;        // bf16 stride of channel-major rows
+
+struct __attribute__((aligned(16))) SparseTile {
+  bf16 k[KT * KS];    // raw K,   [key][channel]
+  bf16 kh[KT * KS];   // K_hat,   [key][channel]
+  bf16 vt[kD * VS];   // raw V,   [channel][key]
+  bf16 vht[kD * VS];  // V_hat,   [channel][key]
+};
+
+__device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
+  return (u & 0x8000u) ? 0 : u;  // bf16 max(x, 0); -0 and negatives -> +0
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)from_f32<bf16>(a).u | ((uint32_t)from_f32<bf16>(b).u << 16);
+}
+
+template <int NQT>
+__global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ qkvh,
+    const int32_t* __restrict__ sel, bf16* __restrict__ o, int gh, int gw,
+    int heads, int block, int window, int keep) {
+  constexpr int NT = 64 * 2 * NQT;
+  __shared__ SparseTile tiles[2];
+  __shared__ float linloc[NQT * 32][kD + 1];
+
+  const int b = blockIdx.y, h = blockIdx.z;
+  const int C = heads * kD, C3 = 3 * C;
+  const int t = sel[(size_t)b * keep + blockIdx.x];
+  const int nbc = gw / block;
+  if (t < 0 || t >= (gh / block) * nbc) return;  // invalid entry: no access
+  const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
+  const int p = (window - block) / 2;
+  const int rlo = max(0, r0 - p), rhi = min(gh, r0 + block + p);
+  const int clo = max(0, c0 - p), chi = min(gw, c0 + block + p);
+  const int wcols = chi - clo;
+  const int nwin = (rhi - rlo) * wcols;
+  const int nq = block * block;
+  const size_t img = (size_t)b * gh * gw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int qt = wave % NQT, path = wave / NQT;
+  const int g = lane >> 5;           // lane group (0/1)
+  const int ql = qt * 32 + (lane & 31);  // query index within the block
+  const bool q_ok = ql < nq;
+  const int qn = q_ok ? (r0 + ql / block) * gw + c0 + ql % block : 0;
+
+  // B operand of S^T: this lane's query, channels 8g..8g+7 and 16+8g..
+  bf16x8 qf[2];
+  {
+    const bf16* src = (path == 0 ? qkv : qkvh) + (img + qn) * C3 + h * kD;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 u = q_ok ? *reinterpret_cast<const uint4*>(src + 16 * ks + 8 * g)
+                     : uint4{0, 0, 0, 0};
+      if (path == 1) {  // relu on the hatted query
+        uint16_t* hv = reinterpret_cast<uint16_t*>(&u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = relu_bits(hv[i]);
+      }
+      qf[ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  // tile loader: 64 keys x (K, K^, V, V^) x 32 channels = 1024 chunks of 8
+  constexpr int kLoads = (1024 + NT - 1) / NT;
+  uint4 stg[kLoads];
+  auto issue = [&](int w0) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int cidx = tid + NT * i;
+      const int tensor = cidx >> 8;      // 0 K, 1 K^, 2 V, 3 V^
+      const int key = (cidx >> 2) & 63, cg = cidx & 3;
+      const int wi = w0 + key;
+      uint4 u = {0, 0, 0, 0};
+      if (cidx < 1024 && wi < nwin) {
+        const size_t tok = img + (size_t)(rlo + wi / wcols) * gw + clo + wi % wcols;
+        const bf16* base = (tensor & 1) ? qkvh : qkv;
+        const int comp = (tensor < 2) ? 1 : 2;
+        u = *reinterpret_cast<const uint4*>(base + tok * C3 + comp * C + h * kD + 8 * cg);
+      }
+      stg[i] = u;
+    }
+  };
+  auto commit = [&](int buf) {
+    SparseTile& T = tiles[buf];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int cidx = tid + NT * i;
+      if (cidx >= 1024) break;
+      const int tensor = cidx >> 8;
+      const int key = (cidx >> 2) & 63, cg = cidx & 3;
+      uint4 u = stg[i];
+      if (tensor == 0) {
+        *reinterpret_cast<uint4*>(&T.k[key * KS + 8 * cg]) = u;
+      } else if (tensor == 1) {
+        uint16_t* hv = reinterpret_cast<uint16_t*>(&u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hv[j] = relu_bits(hv[j]);
+        *reinterpret_cast<uint4*>(&T.kh[key * KS + 8 * cg]) = u;
+      } else {
+        bf16* dst = tensor == 2 ? T.vt : T.vht;
+        const uint16_t* hv = reinterpret_cast<const uint16_t*>(&u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[(8 * cg + j) * VS + key].u = hv[j];
+      }
+    }
+  };
+
+  f32x16 oacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) oacc[r] = 0.f;
+  float run_max = -INFINITY;  // softmax path: running max (shared by l, l^32)
+  float run_sum = 0.f;        // this lane's share of the column sum
+  const float sc = 1.4426950408889634f / sqrtf((float)kD);  // log2(e)/sqrt(d)
+
+  const int ntiles = (nwin + KT - 1) / KT;
+  issue(0);
+  commit(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) issue((it + 1) * KT);
+    const SparseTile& T = tiles[buf];
+    const bf16* kmat = path == 0 ? T.k : T.kh;
+    const bf16* vmat = path == 0 ? T.vt : T.vht;
+#pragma unroll
+    for (int sub = 0; sub < KT / 32; ++sub) {
+      const int kbase = it * KT + sub * 32;
+      if (kbase >= nwin) break;
+      // S^T (or A^T) tile: rows = 32 keys, columns = 32 queries
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 kf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(
+                        &kmat[(sub * 32 + (lane & 31)) * KS + 16 * ks + 8 * g]));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+      }
+      // lane holds keys kbase + 8(r/4) + 4g + r%4 of its query
+      if (path == 0) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
+          s[r] = key < nwin ? s[r] * sc : -INFINITY;
+          mx = fmaxf(mx, s[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(run_max, mx);
+        const float corr = exp2f(run_max - mnew);
+        run_max = mnew;
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] = exp2f(s[r] - mnew);
+          ps += s[r];
+        }
+        run_sum = run_sum * corr + ps;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[r] *= corr;
+      } else {
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ps += s[r];
+        run_sum += ps;
+      }
+      // O^T += V^T P^T over two 16-key slabs, keys in accumulator order
+#pragma unroll
+      for (int slab = 0; slab < 2; ++slab) {
+        uint4 pb;
+        pb.x = pack2(s[8 * slab + 0], s[8 * slab + 1]);
+        pb.y = pack2(s[8 * slab + 2], s[8 * slab + 3]);
+        pb.z = pack2(s[8 * slab + 4], s[8 * slab + 5]);
+        pb.w = pack2(s[8 * slab + 6], s[8 * slab + 7]);
+        const bf16* vrow = &vmat[(lane & 31) * VS + sub * 32 + 16 * slab + 4 * g];
+        uint4 va;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+        va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
+        oacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb), oacc,
+            0, 0, 0);
+      }
+    }
+    // tiles[buf ^ 1] was last read before the previous barrier
+    if (it + 1 < ntiles) commit(buf ^ 1);
+    __syncthreads();
+  }
+
+  // column totals over both lane groups
+  const float total = run_sum + __shfl_xor(run_sum, 32, 64);
+  // lane holds channels 8(r/4) + 4g + r%4 of query ql
+  if (path == 1) {
+    const float inv = total > 0.f ? 1.f / total : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      linloc[ql][8 * (r >> 2) + 4 * g + (r & 3)] = total > 0.f ? oacc[r] * inv : 0.f;
+  }
+  __syncthreads();
+  if (path == 0 && q_ok) {
+    const float inv = 1.f / total;
+    bf16* orow = o + (img + qn) * C + h * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ch = 8 * j + 4 * g;
+      const uint2 prev = *reinterpret_cast<const uint2*>(orow + ch);
+      float v[4];
+      v[0] = __uint_as_float(prev.x << 16);
+      v[1] = __uint_as_float(prev.x & 0xffff0000u);
+      v[2] = __uint_as_float(prev.y << 16);
+      v[3] = __uint_as_float(prev.y & 0xffff0000u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += oacc[4 * j + i] * inv - linloc[ql][ch + i];
+      uint2 outv;
+      outv.x = pack2(v[0], v[1]);
+      outv.y = pack2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(orow + ch) = outv;
+    }
+  }
+}
+
 template <typename T>
 hipError_t run(const void* qkv, const void* qkvh, const int32_t* sel, void* o,
                int batch, int gh, int gw, int heads, int block, int window,
@@ -124,6 +372,20 @@ hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
                          int gw, int heads, int block, int window, int keep,
                          hipStream_t s) {
   if (keep == 0) return hipSuccess;
+  const int nqt = (block * block + 31) / 32;
+  if (bf && nqt <= 4) {
+    dim3 grid(keep, batch, heads);
+    const bf16* q = static_cast<const bf16*>(qkv);
+    const bf16* qh = static_cast<const bf16*>(qkv_hat);
+    bf16* out = static_cast<bf16*>(o);
+    switch (nqt) {
+      case 1: sparse_mfma_kernel<1><<<grid, 128, 0, s>>>(q, qh, sel, out, gh, gw, heads, block, window, keep); break;
+      case 2: sparse_mfma_kernel<2><<<grid, 256, 0, s>>>(q, qh, sel, out, gh, gw, heads, block, window, keep); break;
+      case 3: sparse_mfma_kernel<3><<<grid, 384, 0, s>>>(q, qh, sel, out, gh, gw, heads, block, window, keep); break;
+      default: sparse_mfma_kernel<4><<<grid, 512, 0, s>>>(q, qh, sel, out, gh, gw, heads, block, window, keep); break;
+    }
+    return hipGetLastError();
+  }
   return bf ? run<bf16>(qkv, qkv_hat, sel, o, batch, gh, gw, heads, block,
                         window, keep, s)
             : run<float>(qkv, qkv_hat, sel, o, batch, gh, gw, heads, block,

@@ -28,7 +28,7 @@ hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
                          bool gelu, hipStream_t s);
 
 // Number of token chunks the KV-state reduction splits each image into.
-int kv_chunks(int batch, int heads, int tokens);
+int kv_chunks(bool bf, int batch, int heads, int tokens);
 
 // Z/D partials per chunk, then a fixed-order combine into kv and ksum.
 hipError_t launch_kv_state(bool bf, const void* qkv_hat, float* kv,

@@ -102,7 +102,18 @@ def test_block_forward(keep):
                                     sel=g["sel"][:, :kk], **kw)
     for key in ("qkv", "qkv_hat", "o", "x1"):
         assert_close(g[key], ref[key], wl.dtype, key)
-    assert_close(g["out"], ref["out"], wl.dtype, "out")
+    # The FFN sandwich is checked on the GPU's own x1 (same inputs on both
+    # sides), so bfloat16 rounding differences of the module stages are not
+    # carried through four more rounded stages.
+    assert_close(g["out"], _oracle_ffn(g["x1"], inp, wl), wl.dtype, "out")
+
+
+def _oracle_ffn(x1, inp, wl):
+    r = O.round_bf16
+    xn2 = r(O.layer_norm(x1, inp["ln2_g"], inp["ln2_b"]))
+    h1 = r(xn2 @ inp["w1"])
+    h2 = r(O.gelu(O.dwconv_same(h1, inp["dw_ffn"], wl.grid_h, wl.grid_w)))
+    return r(x1 + h2 @ inp["w2"])
 
 
 def test_block_forward_f32():
