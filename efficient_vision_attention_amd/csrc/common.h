@@ -25,16 +25,20 @@ __device__ __forceinline__ float from_f32<float>(float x) {
   return x;
 }
 
-// Round float32 to bfloat16, nearest even.  Adding 0x7fff plus the lowest
-// kept bit to the pattern carries into the kept bits exactly when the
-// dropped half is above one half ulp, or equal to it with an odd kept part.
-// NaN is kept quiet.
+typedef __bf16 hw_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float hw_f32x2 __attribute__((ext_vector_type(2)));
+
+// Round float32 to bfloat16, nearest even, with gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32, default round mode; NaN stays NaN).
 template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16{static_cast<uint16_t>((u >> 16) | 0x40u)};
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16{static_cast<uint16_t>(u >> 16)};
+  return bf16{__builtin_bit_cast(uint16_t, static_cast<__bf16>(x))};
+}
+
+// Two floats -> two bfloat16 in one 32-bit word (a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const hw_f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_bf16x2));
 }
 
 __device__ __forceinline__ float relu(float x) { return x > 0.f ? x : 0.f; }

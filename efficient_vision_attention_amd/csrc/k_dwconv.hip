@@ -8,12 +8,9 @@
 // block equation) uses the same kernel with a GELU epilogue.
 //
 // Kernel shape: a workgroup owns 16 columns x 64 channels of a strip of 32
-// output rows.  It streams the input rows of the strip (plus the vertical
-// halo) through a double-buffered LDS row that carries the horizontal halo;
-// each thread keeps the kmax partial output rows that the current input row
-// feeds in registers, so every input element is read from HBM once and from
-// LDS kmax times.  Each thread handles 4 consecutive channels (8-byte bf16
-// accesses, 128 contiguous bytes per 16 lanes).
+// output rows; each thread handles 4 consecutive channels of one column
+// (8-byte bf16 accesses, 128 contiguous bytes per 16 lanes) and keeps the
+// kmax partial output rows that the current input row feeds in registers.
 #include "common.h"
 #include "kernels.h"
 
@@ -51,36 +48,40 @@ __device__ __forceinline__ float gelu_erf(float x) {
 constexpr int TW = 16;   // output columns per workgroup
 constexpr int CG = 16;   // 4-channel groups per workgroup (64 channels)
 constexpr int TH = 32;   // output rows per workgroup strip
+constexpr int kXcds = 8;
 
 struct f4 {
   float v[4];
 };
 
+// Raw 4-channel vectors as loaded from memory, converted to float at use.
 template <typename T>
-__device__ __forceinline__ f4 load4(const T* p);
+struct Raw;
 template <>
-__device__ __forceinline__ f4 load4<bf16>(const bf16* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
-  f4 r;
-  r.v[0] = __uint_as_float(u.x << 16);
-  r.v[1] = __uint_as_float(u.x & 0xffff0000u);
-  r.v[2] = __uint_as_float(u.y << 16);
-  r.v[3] = __uint_as_float(u.y & 0xffff0000u);
-  return r;
-}
+struct Raw<bf16> {
+  uint2 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void zero() { u = uint2{0, 0}; }
+  __device__ __forceinline__ f4 cvt() const {
+    return f4{{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)}};
+  }
+};
 template <>
-__device__ __forceinline__ f4 load4<float>(const float* p) {
-  const float4 u = *reinterpret_cast<const float4*>(p);
-  return f4{{u.x, u.y, u.z, u.w}};
-}
+struct Raw<float> {
+  float4 u;
+  __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void zero() { u = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ f4 cvt() const { return f4{{u.x, u.y, u.z, u.w}}; }
+};
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, const float* v);
 template <>
 __device__ __forceinline__ void store4<bf16>(bf16* p, const float* v) {
   uint2 o;
-  o.x = (uint32_t)from_f32<bf16>(v[0]).u | ((uint32_t)from_f32<bf16>(v[1]).u << 16);
-  o.y = (uint32_t)from_f32<bf16>(v[2]).u | ((uint32_t)from_f32<bf16>(v[3]).u << 16);
+  o.x = pack_bf16x2(v[0], v[1]);
+  o.y = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<uint2*>(p) = o;
 }
 template <>
@@ -88,27 +89,40 @@ __device__ __forceinline__ void store4<float>(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// grid: (column tiles * channel tiles, row strips, batch); 256 threads.
+// A thread owns one output column x and 4 channels of a 32-row strip and
+// walks down the input rows of the strip.  For each input row it loads the
+// K horizontal neighbours it needs (the K-fold reuse across neighbouring
+// threads is served by the L1), and the row feeds the K partial output rows
+// it belongs to, kept in registers.  Two rows are in flight at any time;
+// there is no LDS and no barrier, so every wave streams independently.
+// Grid: 1-D over (batch, strip, channel tile, column tile) with the column
+// tile fastest, remapped so each XCD walks a contiguous run of neighbouring
+// tiles (their halo columns then hit in that XCD's L2).
 template <typename T, int K, bool GELU>
-__global__ __launch_bounds__(256) void dwconv_rows(
+__global__ __launch_bounds__(256) void dwconv_stream(
     const T* __restrict__ in, T* __restrict__ out,
-    const float* __restrict__ weff, int gh, int gw, int ch, int col_tiles) {
+    const float* __restrict__ weff, int gh, int gw, int ch, int col_tiles,
+    int ch_tiles, int strips, int total, int per_xcd) {
   constexpr int R = (K - 1) / 2;
-  constexpr int SEG = TW + 2 * R;  // columns held per LDS row
-  __shared__ float4 row[2][SEG * CG];
+  const int bid = blockIdx.x;
+  const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
+  if (tile >= total) return;
+  int rest = tile;
+  const int col_t = rest % col_tiles;
+  rest /= col_tiles;
+  const int ch_t = rest % ch_tiles;
+  rest /= ch_tiles;
+  const int strip = rest % strips;
+  const int b = rest / strips;
 
-  const int tc = threadIdx.x % CG;   // channel group within the tile
-  const int tx = threadIdx.x / CG;   // output column within the tile
-  const int x0 = (blockIdx.x % col_tiles) * TW;
-  const int c0 = (blockIdx.x / col_tiles) * (CG * 4);
-  const int y0 = blockIdx.y * TH;
-  const int b = blockIdx.z;
-  const int c = c0 + tc * 4;
+  const int tc = threadIdx.x % CG;
+  const int tx = threadIdx.x / CG;
+  const int x = col_t * TW + tx;
+  const int c = ch_t * (CG * 4) + tc * 4;
   const bool c_ok = c < ch;
-  const int x = x0 + tx;
+  const int y0 = strip * TH;
   const size_t img = (size_t)b * gh * gw;
 
-  // this thread's taps, K x K x 4 channels
   float w[K][K][4];
 #pragma unroll
   for (int ky = 0; ky < K; ++ky)
@@ -127,74 +141,73 @@ __global__ __launch_bounds__(256) void dwconv_rows(
   const int y_end = min(gh, y0 + TH);
   const int r_begin = y0 - R, r_end = y_end + R;
 
-  // Each thread stages up to two 4-channel vectors of an input row segment.
-  // Loads for row r+1 are issued one iteration ahead and written to LDS
-  // after the compute of row r, so their latency overlaps that compute.
-  constexpr int kFill = (SEG * CG + 255) / 256;
-  auto issue = [&](f4 (&st)[kFill], int r) {
+  // Branch-free row loads: addresses are clamped into the tensor and the
+  // values of out-of-grid taps are zeroed afterwards.
+  const int cc = c_ok ? c : ch - 4;
+  bool col_ok[K];
+  int col_off[K];
 #pragma unroll
-    for (int i = 0; i < kFill; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      const int sx = e / CG, sc = e % CG;
-      const int gx = x0 - R + sx, gc = c0 + sc * 4;
-      if (e < SEG * CG && r >= 0 && r < gh && gx >= 0 && gx < gw && gc < ch)
-        st[i] = load4<T>(in + (img + (size_t)r * gw + gx) * ch + gc);
-      else
-        st[i] = f4{{0.f, 0.f, 0.f, 0.f}};
-    }
-  };
-  auto commit = [&](const f4 (&st)[kFill], int buf) {
+  for (int kx = 0; kx < K; ++kx) {
+    const int xx = x + kx - R;
+    col_ok[kx] = xx >= 0 && xx < gw;
+    col_off[kx] = min(max(xx, 0), gw - 1) * ch + cc;
+  }
+  auto load_row = [&](Raw<T> (&rr)[K], int r) {
+    const T* base = in + (img + (size_t)min(max(r, 0), gh - 1) * gw) * ch;
 #pragma unroll
-    for (int i = 0; i < kFill; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      if (e < SEG * CG)
-        row[buf][e] = make_float4(st[i].v[0], st[i].v[1], st[i].v[2], st[i].v[3]);
-    }
+    for (int kx = 0; kx < K; ++kx) rr[kx].load(base + col_off[kx]);
   };
+  auto row_valid = [&](int r) { return r >= 0 && r < gh; };
+  // only tiles touching the left/right border have lanes with invalid taps
+  const bool edge_tile = col_t * TW - R < 0 || col_t * TW + TW + R > gw;
 
-  f4 stage[kFill];
-  issue(stage, r_begin);
-  commit(stage, 0);
-  if (r_begin + 1 < r_end) issue(stage, r_begin + 1);
-  __syncthreads();
-  for (int r = r_begin; r < r_end; ++r) {
-    const int buf = (r - r_begin) & 1;
-    float xin[K][4];
+  Raw<T> ra[K], rb[K];
+  load_row(ra, r_begin);
+  load_row(rb, r_begin + 1);
+  // Rows are processed in groups of 2K so that both the accumulator ring
+  // slot ((row - r_begin) mod K) and the staging buffer (row parity) are
+  // compile-time constants of the unrolled body.
+  for (int r0 = r_begin; r0 < r_end; r0 += 2 * K) {
 #pragma unroll
-    for (int kx = 0; kx < K; ++kx) {
-      const float4 v = row[buf][(tx + kx) * CG + tc];
-      xin[kx][0] = v.x;
-      xin[kx][1] = v.y;
-      xin[kx][2] = v.z;
-      xin[kx][3] = v.w;
+    for (int u = 0; u < 2 * K; ++u) {
+      const int r = r0 + u;
+      if (r >= r_end) break;
+      Raw<T>(&cur)[K] = (u % 2 == 0) ? ra : rb;
+      const bool rv = row_valid(r);
+      f4 xin[K];
+#pragma unroll
+      for (int kx = 0; kx < K; ++kx) xin[kx] = cur[kx].cvt();
+      if (!rv) {  // uniform: a halo row outside the grid
+#pragma unroll
+        for (int kx = 0; kx < K; ++kx) xin[kx] = f4{{0.f, 0.f, 0.f, 0.f}};
+      } else if (edge_tile) {
+#pragma unroll
+        for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xin[kx].v[j] = col_ok[kx] ? xin[kx].v[j] : 0.f;
+      }
+      if (r + 2 < r_end) load_row(cur, r + 2);
+      // input row r feeds output row r - R + i with vertical tap K - 1 - i
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const int slot = (u - R + i + 2 * K) % K;
+#pragma unroll
+        for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[slot][j] = fmaf(w[K - 1 - i][kx][j], xin[kx].v[j], acc[slot][j]);
+      }
+      const int done = (u - R + 2 * K) % K;  // slot of output row r - R
+      const int yo = r - R;
+      if (yo >= y0 && yo < y_end && x < gw && c_ok) {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = GELU ? gelu_erf(acc[done][j]) : acc[done][j];
+        store4<T>(out + (img + (size_t)yo * gw + x) * ch + c, v);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[done][j] = 0.f;
     }
-    // row r+1 (already in flight) goes to the other buffer; row r+2 is issued
-    if (r + 1 < r_end) {
-      commit(stage, buf ^ 1);
-      if (r + 2 < r_end) issue(stage, r + 2);
-    }
-    // input row r feeds output row r - R + i with vertical tap K - 1 - i
-#pragma unroll
-    for (int i = 0; i < K; ++i)
-#pragma unroll
-      for (int kx = 0; kx < K; ++kx)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = fmaf(w[K - 1 - i][kx][j], xin[kx][j], acc[i][j]);
-    const int yo = r - R;  // completed output row
-    if (yo >= y0 && yo < y_end && x < gw && c_ok) {
-      float v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = GELU ? gelu_erf(acc[0][j]) : acc[0][j];
-      store4<T>(out + (img + (size_t)yo * gw + x) * ch + c, v);
-    }
-#pragma unroll
-    for (int i = 0; i + 1 < K; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = acc[i + 1][j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[K - 1][j] = 0.f;
-    __syncthreads();
   }
 }
 
@@ -203,10 +216,12 @@ hipError_t run_dw(const void* in, void* out, const float* weff, int batch,
                   int gh, int gw, int ch, hipStream_t s) {
   const int col_tiles = (gw + TW - 1) / TW;
   const int ch_tiles = (ch + CG * 4 - 1) / (CG * 4);
-  dim3 grid(col_tiles * ch_tiles, (gh + TH - 1) / TH, batch);
-  dwconv_rows<T, K, GELU><<<grid, 256, 0, s>>>(
+  const int strips = (gh + TH - 1) / TH;
+  const int total = col_tiles * ch_tiles * strips * batch;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  dwconv_stream<T, K, GELU><<<per_xcd * kXcds, 256, 0, s>>>(
       static_cast<const T*>(in), static_cast<T*>(out), weff, gh, gw, ch,
-      col_tiles);
+      col_tiles, ch_tiles, strips, total, per_xcd);
   return hipGetLastError();
 }
 

@@ -143,8 +143,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_bf16(
           v[3] += __uint_as_float(rr.y & 0xffff0000u);
         }
         uint2 o;
-        o.x = (uint32_t)from_f32<bf16>(v[0]).u | ((uint32_t)from_f32<bf16>(v[1]).u << 16);
-        o.y = (uint32_t)from_f32<bf16>(v[2]).u | ((uint32_t)from_f32<bf16>(v[3]).u << 16);
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(C + off) = o;
       }
     }

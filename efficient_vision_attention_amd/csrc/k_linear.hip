@@ -306,10 +306,8 @@ __global__ __launch_bounds__(256) void lin_apply_mfma(
     for (int j = 0; j < 4; ++j) {
       const int c = 8 * j + 4 * g;
       uint2 w;
-      w.x = (uint32_t)from_f32<bf16>(acc[4 * j + 0] * inv).u |
-            ((uint32_t)from_f32<bf16>(acc[4 * j + 1] * inv).u << 16);
-      w.y = (uint32_t)from_f32<bf16>(acc[4 * j + 2] * inv).u |
-            ((uint32_t)from_f32<bf16>(acc[4 * j + 3] * inv).u << 16);
+      w.x = pack_bf16x2(acc[4 * j + 0] * inv, acc[4 * j + 1] * inv);
+      w.y = pack_bf16x2(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
       *reinterpret_cast<uint2*>(orow + c) = w;
     }
   }

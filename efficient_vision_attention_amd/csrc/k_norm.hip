@@ -29,8 +29,7 @@ struct Vec<bf16> {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)from_f32<bf16>(v[2 * i]).u |
-             ((uint32_t)from_f32<bf16>(v[2 * i + 1]).u << 16);
+      w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<uint4*>(p) = uint4{w[0], w[1], w[2], w[3]};
   }
 };

@@ -142,10 +142,6 @@ __device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
   return (u & 0x8000u) ? 0 : u;  // bf16 max(x, 0); -0 and negatives -> +0
 }
 
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)from_f32<bf16>(a).u | ((uint32_t)from_f32<bf16>(b).u << 16);
-}
-
 template <int NQT>
 __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ qkvh,
@@ -303,10 +299,10 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
 #pragma unroll
       for (int slab = 0; slab < 2; ++slab) {
         uint4 pb;
-        pb.x = pack2(s[8 * slab + 0], s[8 * slab + 1]);
-        pb.y = pack2(s[8 * slab + 2], s[8 * slab + 3]);
-        pb.z = pack2(s[8 * slab + 4], s[8 * slab + 5]);
-        pb.w = pack2(s[8 * slab + 6], s[8 * slab + 7]);
+        pb.x = pack_bf16x2(s[8 * slab + 0], s[8 * slab + 1]);
+        pb.y = pack_bf16x2(s[8 * slab + 2], s[8 * slab + 3]);
+        pb.z = pack_bf16x2(s[8 * slab + 4], s[8 * slab + 5]);
+        pb.w = pack_bf16x2(s[8 * slab + 6], s[8 * slab + 7]);
         const bf16* vrow = &vmat[(lane & 31) * VS + sub * 32 + 16 * slab + 4 * g];
         uint4 va;
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
@@ -347,8 +343,8 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] += oacc[4 * j + i] * inv - linloc[ql][ch + i];
       uint2 outv;
-      outv.x = pack2(v[0], v[1]);
-      outv.y = pack2(v[2], v[3]);
+      outv.x = pack_bf16x2(v[0], v[1]);
+      outv.y = pack_bf16x2(v[2], v[3]);
       *reinterpret_cast<uint2*>(orow + ch) = outv;
     }
   }
