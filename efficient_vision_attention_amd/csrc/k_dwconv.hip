@@ -45,65 +45,86 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
 }
 
-constexpr int TW = 16;   // output columns per workgroup
-constexpr int CG = 16;   // 4-channel groups per workgroup (64 channels)
 constexpr int TH = 32;   // output rows per workgroup strip
 constexpr int kXcds = 8;
+constexpr int kWgChannels = 64;  // channels per workgroup
 
-struct f4 {
-  float v[4];
-};
-
-// Raw 4-channel vectors as loaded from memory, converted to float at use.
-template <typename T>
+// V consecutive channels as loaded from memory (V = 2 or 4), converted to
+// float at use.
+template <typename T, int V>
 struct Raw;
 template <>
-struct Raw<bf16> {
+struct Raw<bf16, 4> {
   uint2 u;
   __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ void zero() { u = uint2{0, 0}; }
-  __device__ __forceinline__ f4 cvt() const {
-    return f4{{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)}};
+  __device__ __forceinline__ void cvt(float* f) const {
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xffff0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xffff0000u);
   }
 };
 template <>
-struct Raw<float> {
+struct Raw<bf16, 2> {
+  uint32_t u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ void cvt(float* f) const {
+    f[0] = __uint_as_float(u << 16);
+    f[1] = __uint_as_float(u & 0xffff0000u);
+  }
+};
+template <>
+struct Raw<float, 4> {
   float4 u;
   __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
-  __device__ __forceinline__ void zero() { u = make_float4(0.f, 0.f, 0.f, 0.f); }
-  __device__ __forceinline__ f4 cvt() const { return f4{{u.x, u.y, u.z, u.w}}; }
+  __device__ __forceinline__ void cvt(float* f) const {
+    f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+  }
+};
+template <>
+struct Raw<float, 2> {
+  float2 u;
+  __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float2*>(p); }
+  __device__ __forceinline__ void cvt(float* f) const { f[0] = u.x; f[1] = u.y; }
 };
 
-template <typename T>
-__device__ __forceinline__ void store4(T* p, const float* v);
+template <typename T, int V>
+__device__ __forceinline__ void storev(T* p, const float* v);
 template <>
-__device__ __forceinline__ void store4<bf16>(bf16* p, const float* v) {
-  uint2 o;
-  o.x = pack_bf16x2(v[0], v[1]);
-  o.y = pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<uint2*>(p) = o;
+__device__ __forceinline__ void storev<bf16, 4>(bf16* p, const float* v) {
+  *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 template <>
-__device__ __forceinline__ void store4<float>(float* p, const float* v) {
+__device__ __forceinline__ void storev<bf16, 2>(bf16* p, const float* v) {
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v[0], v[1]);
+}
+template <>
+__device__ __forceinline__ void storev<float, 4>(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
+template <>
+__device__ __forceinline__ void storev<float, 2>(float* p, const float* v) {
+  *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+}
 
-// A thread owns one output column x and 4 channels of a 32-row strip and
-// walks down the input rows of the strip.  For each input row it loads the
-// K horizontal neighbours it needs (the K-fold reuse across neighbouring
-// threads is served by the L1), and the row feeds the K partial output rows
-// it belongs to, kept in registers.  Two rows are in flight at any time;
-// there is no LDS and no barrier, so every wave streams independently.
+// A thread owns one output column x and V consecutive channels of a 32-row
+// strip and walks down the input rows of the strip.  For each input row it
+// loads the K horizontal neighbours it needs (the K-fold reuse across
+// neighbouring threads is served by the L1), and the row feeds the K partial
+// output rows it belongs to, kept in registers.  Two rows are in flight at
+// any time; there is no LDS and no barrier, so every wave streams
+// independently.  A workgroup covers 64 channels x (256 V / 64) columns.
 // Grid: 1-D over (batch, strip, channel tile, column tile) with the column
 // tile fastest, remapped so each XCD walks a contiguous run of neighbouring
 // tiles (their halo columns then hit in that XCD's L2).
-template <typename T, int K, bool GELU>
+template <typename T, int K, bool GELU, int V>
 __global__ __launch_bounds__(256) void dwconv_stream(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, int gh, int gw, int ch, int col_tiles,
     int ch_tiles, int strips, int total, int per_xcd) {
   constexpr int R = (K - 1) / 2;
+  constexpr int CG = kWgChannels / V;  // channel groups per workgroup
+  constexpr int TW = 256 / CG;         // columns per workgroup
   const int bid = blockIdx.x;
   const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
   if (tile >= total) return;
@@ -118,32 +139,32 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   const int tc = threadIdx.x % CG;
   const int tx = threadIdx.x / CG;
   const int x = col_t * TW + tx;
-  const int c = ch_t * (CG * 4) + tc * 4;
+  const int c = ch_t * kWgChannels + tc * V;
   const bool c_ok = c < ch;
   const int y0 = strip * TH;
   const size_t img = (size_t)b * gh * gw;
 
-  float w[K][K][4];
+  float w[K][K][V];
 #pragma unroll
   for (int ky = 0; ky < K; ++ky)
 #pragma unroll
     for (int kx = 0; kx < K; ++kx)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < V; ++j)
         w[ky][kx][j] = c_ok ? weff[(size_t)(ky * K + kx) * ch + c + j] : 0.f;
 
-  float acc[K][4];
+  float acc[K][V];
 #pragma unroll
   for (int i = 0; i < K; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int j = 0; j < V; ++j) acc[i][j] = 0.f;
 
   const int y_end = min(gh, y0 + TH);
   const int r_begin = y0 - R, r_end = y_end + R;
 
   // Branch-free row loads: addresses are clamped into the tensor and the
   // values of out-of-grid taps are zeroed afterwards.
-  const int cc = c_ok ? c : ch - 4;
+  const int cc = c_ok ? c : ch - V;
   bool col_ok[K];
   int col_off[K];
 #pragma unroll
@@ -152,16 +173,15 @@ __global__ __launch_bounds__(256) void dwconv_stream(
     col_ok[kx] = xx >= 0 && xx < gw;
     col_off[kx] = min(max(xx, 0), gw - 1) * ch + cc;
   }
-  auto load_row = [&](Raw<T> (&rr)[K], int r) {
+  auto load_row = [&](Raw<T, V> (&rr)[K], int r) {
     const T* base = in + (img + (size_t)min(max(r, 0), gh - 1) * gw) * ch;
 #pragma unroll
     for (int kx = 0; kx < K; ++kx) rr[kx].load(base + col_off[kx]);
   };
-  auto row_valid = [&](int r) { return r >= 0 && r < gh; };
   // only tiles touching the left/right border have lanes with invalid taps
   const bool edge_tile = col_t * TW - R < 0 || col_t * TW + TW + R > gw;
 
-  Raw<T> ra[K], rb[K];
+  Raw<T, V> ra[K], rb[K];
   load_row(ra, r_begin);
   load_row(rb, r_begin + 1);
   // Rows are processed in groups of 2K so that both the accumulator ring
@@ -172,19 +192,20 @@ __global__ __launch_bounds__(256) void dwconv_stream(
     for (int u = 0; u < 2 * K; ++u) {
       const int r = r0 + u;
       if (r >= r_end) break;
-      Raw<T>(&cur)[K] = (u % 2 == 0) ? ra : rb;
-      const bool rv = row_valid(r);
-      f4 xin[K];
+      Raw<T, V>(&cur)[K] = (u % 2 == 0) ? ra : rb;
+      float xin[K][V];
 #pragma unroll
-      for (int kx = 0; kx < K; ++kx) xin[kx] = cur[kx].cvt();
-      if (!rv) {  // uniform: a halo row outside the grid
+      for (int kx = 0; kx < K; ++kx) cur[kx].cvt(xin[kx]);
+      if (r < 0 || r >= gh) {  // uniform: a halo row outside the grid
 #pragma unroll
-        for (int kx = 0; kx < K; ++kx) xin[kx] = f4{{0.f, 0.f, 0.f, 0.f}};
+        for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+          for (int j = 0; j < V; ++j) xin[kx][j] = 0.f;
       } else if (edge_tile) {
 #pragma unroll
         for (int kx = 0; kx < K; ++kx)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) xin[kx].v[j] = col_ok[kx] ? xin[kx].v[j] : 0.f;
+          for (int j = 0; j < V; ++j) xin[kx][j] = col_ok[kx] ? xin[kx][j] : 0.f;
       }
       if (r + 2 < r_end) load_row(cur, r + 2);
       // input row r feeds output row r - R + i with vertical tap K - 1 - i
@@ -194,45 +215,48 @@ __global__ __launch_bounds__(256) void dwconv_stream(
 #pragma unroll
         for (int kx = 0; kx < K; ++kx)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[slot][j] = fmaf(w[K - 1 - i][kx][j], xin[kx].v[j], acc[slot][j]);
+          for (int j = 0; j < V; ++j)
+            acc[slot][j] = fmaf(w[K - 1 - i][kx][j], xin[kx][j], acc[slot][j]);
       }
       const int done = (u - R + 2 * K) % K;  // slot of output row r - R
       const int yo = r - R;
       if (yo >= y0 && yo < y_end && x < gw && c_ok) {
-        float v[4];
+        float v[V];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = GELU ? gelu_erf(acc[done][j]) : acc[done][j];
-        store4<T>(out + (img + (size_t)yo * gw + x) * ch + c, v);
+        for (int j = 0; j < V; ++j) v[j] = GELU ? gelu_erf(acc[done][j]) : acc[done][j];
+        storev<T, V>(out + (img + (size_t)yo * gw + x) * ch + c, v);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[done][j] = 0.f;
+      for (int j = 0; j < V; ++j) acc[done][j] = 0.f;
     }
   }
 }
 
-template <typename T, int K, bool GELU>
+template <typename T, int K, bool GELU, int V>
 hipError_t run_dw(const void* in, void* out, const float* weff, int batch,
                   int gh, int gw, int ch, hipStream_t s) {
+  constexpr int TW = 256 / (kWgChannels / V);
   const int col_tiles = (gw + TW - 1) / TW;
-  const int ch_tiles = (ch + CG * 4 - 1) / (CG * 4);
+  const int ch_tiles = (ch + kWgChannels - 1) / kWgChannels;
   const int strips = (gh + TH - 1) / TH;
   const int total = col_tiles * ch_tiles * strips * batch;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  dwconv_stream<T, K, GELU><<<per_xcd * kXcds, 256, 0, s>>>(
+  dwconv_stream<T, K, GELU, V><<<per_xcd * kXcds, 256, 0, s>>>(
       static_cast<const T*>(in), static_cast<T*>(out), weff, gh, gw, ch,
       col_tiles, ch_tiles, strips, total, per_xcd);
   return hipGetLastError();
 }
 
+// Wider kernels keep fewer channels per thread so their taps fit in
+// registers at useful occupancy.
 template <typename T, bool GELU>
 hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
                       int batch, int gh, int gw, int ch, hipStream_t s) {
   switch (kmax) {
-    case 1: return run_dw<T, 1, GELU>(in, out, weff, batch, gh, gw, ch, s);
-    case 3: return run_dw<T, 3, GELU>(in, out, weff, batch, gh, gw, ch, s);
-    case 5: return run_dw<T, 5, GELU>(in, out, weff, batch, gh, gw, ch, s);
-    case 7: return run_dw<T, 7, GELU>(in, out, weff, batch, gh, gw, ch, s);
+    case 1: return run_dw<T, 1, GELU, 4>(in, out, weff, batch, gh, gw, ch, s);
+    case 3: return run_dw<T, 3, GELU, 4>(in, out, weff, batch, gh, gw, ch, s);
+    case 5: return run_dw<T, 5, GELU, 2>(in, out, weff, batch, gh, gw, ch, s);
+    case 7: return run_dw<T, 7, GELU, 2>(in, out, weff, batch, gh, gw, ch, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -71,37 +71,52 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(
 }
 
 // grid (batch), 1024 threads.  rank(t) = #{u : s_u > s_t or (s_u == s_t and
-// u < t)}; block t is kept iff rank(t) < keep, and its slot in the output is
-// the number of kept blocks below it.  Exact and order-independent.
+// u < t)}; block t is kept iff rank(t) < keep.  Its slot in the output is
+// the number of kept blocks below it, formed with wave ballots and a prefix
+// over the 16 wave totals.  Exact and order-independent.
 __global__ __launch_bounds__(1024) void topk_kernel(
     const float* __restrict__ scores, float* __restrict__ scores_copy,
     int32_t* __restrict__ sel, int nblocks, int keep) {
   extern __shared__ float sh[];
-  float* s = sh;                                           // [nblocks]
-  int* kept = reinterpret_cast<int*>(sh + nblocks);        // [nblocks]
+  float* s = sh;  // [nblocks]
+  __shared__ int wave_tot[16];
+  __shared__ int base_all;
   const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* src = scores + (size_t)b * nblocks;
   for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
     const float v = src[t];
     s[t] = v;
     if (scores_copy) scores_copy[(size_t)b * nblocks + t] = v;
   }
+  if (threadIdx.x == 0) base_all = 0;
   __syncthreads();
-  for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
-    const float v = s[t];
-    int rank = 0;
-    for (int u = 0; u < nblocks; ++u) {
-      const float w = s[u];
-      rank += (w > v) || (w == v && u < t);
+  for (int t0 = 0; t0 < nblocks; t0 += blockDim.x) {
+    const int t = t0 + threadIdx.x;
+    bool kept = false;
+    if (t < nblocks) {
+      const float v = s[t];
+      int rank = 0;
+      for (int u = 0; u < nblocks; ++u) {
+        const float w = s[u];
+        rank += (w > v) || (w == v && u < t);
+      }
+      kept = rank < keep;
     }
-    kept[t] = rank < keep;
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
-    if (!kept[t]) continue;
-    int pos = 0;
-    for (int u = 0; u < t; ++u) pos += kept[u];
-    sel[(size_t)b * keep + pos] = t;
+    const uint64_t m = __ballot(kept);
+    const int below = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[wave] = __popcll(m);
+    __syncthreads();
+    int off = base_all;
+    for (int w2 = 0; w2 < wave; ++w2) off += wave_tot[w2];
+    if (kept) sel[(size_t)b * keep + off + below] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int tot = 0;
+      for (int w2 = 0; w2 < 16; ++w2) tot += wave_tot[w2];
+      base_all += tot;
+    }
+    __syncthreads();
   }
 }
 
@@ -128,7 +143,7 @@ hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
                        int batch, int nblocks, int keep, hipStream_t s) {
   if (keep == 0 && scores_copy == nullptr) return hipSuccess;
-  const size_t lds = (size_t)nblocks * (sizeof(float) + sizeof(int));
+  const size_t lds = (size_t)nblocks * sizeof(float);
   topk_kernel<<<batch, 1024, lds, s>>>(scores, scores_copy, sel, nblocks, keep);
   return hipGetLastError();
 }

@@ -124,122 +124,118 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kHG = 4;          // heads per workgroup
-constexpr int kTT = 32;         // tokens per LDS tile
-constexpr int kTS = kTT + 8;    // bf16 stride of channel-major rows
+constexpr int kTT = 32;         // tokens per tile
 constexpr int kChunkTok = 512;  // tokens per partial (bf16 path)
+constexpr int kApplyTok = 128;  // tokens per wave in the readout
 
 __device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
   return (u & 0x8000u) ? 0 : u;
 }
 
-// Z^T tile per head: lane holds Z[i][c] for column c = lane % 32 and rows
-// i = 8(r/4) + 4g + r%4; the token contraction runs through LDS copies of
-// relu(K^) and V^ stored [channel][token].
-// grid (chunks, ceil(heads/4), batch), 256 threads.
+// One wave per head, tiles of 32 tokens, no LDS and no barrier.  A tile is
+// loaded token-major (lane = token, 8 consecutive features per 16 bytes),
+// which is the MFMA A-operand layout; multiplying it by the 32x32 identity
+// returns it in the accumulator layout, where a lane owns one feature and 16
+// tokens -- i.e. transposed, exactly (one nonzero product per output).  The
+// transposed relu(K^) and V^ tiles then feed Z += relu(K^)^T V^ with the
+// token order the accumulator layout already has.
+// grid (chunks, ceil(heads/4), batch), 256 threads = 4 heads.
 __global__ __launch_bounds__(256) void kv_partial_mfma(
     const bf16* __restrict__ qkvh, float* __restrict__ part, int tokens,
     int heads, int nchunks) {
-  __shared__ __attribute__((aligned(16))) bf16 kt[kHG * kD * kTS];
-  __shared__ __attribute__((aligned(16))) bf16 vt[kHG * kD * kTS];
-  __shared__ float dsum[kHG][kD];
-  __shared__ float dpart[256][8];
   const int chunk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
-  const int C = heads * kD, C3 = 3 * C;
-  const int h0 = hg * kHG;
-  const int nh = min(kHG, heads - h0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5;
+  const int h = hg * kHG + wave;
+  if (h >= heads) return;
+  const int C = heads * kD, C3 = 3 * C;
+  const int g = lane >> 5, col = lane & 31;
   const int n_begin = chunk * kChunkTok;
   const int n_end = min(tokens, n_begin + kChunkTok);
-  const bf16* base = qkvh + (size_t)b * tokens * C3;
+  const bf16* base = qkvh + (size_t)b * tokens * C3 + h * kD + 8 * g;
 
-  // loader: 32 tokens x 4 heads x 4 chunks of 8 channels x 2 tensors
-  // = 1024 chunks; thread -> 4 of them.  chunk id: tensor | token | head | cg
-  uint4 stg[4];
-  float dacc[8];
+  // identity as the B operand: column col, k = 16 ks + 8 g + e
+  bf16x8 eye[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dacc[j] = 0.f;
+  for (int ks = 0; ks < 2; ++ks) {
+    uint16_t e16[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) e16[e] = (16 * ks + 8 * g + e == col) ? 0x3f80 : 0;
+    eye[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(e16));
+  }
+
+  // staged loads of one tile: [K^ ks0, K^ ks1, V^ ks0, V^ ks1]
+  uint4 st[4];
   auto issue = [&](int n0) {
+    const int n = n0 + col;
+    const bool ok = n < n_end;
+    const bf16* row = base + (size_t)(ok ? n : n_begin) * C3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cidx = tid + 256 * i;
-      const int tensor = cidx >> 9, tok = (cidx >> 4) & 31;
-      const int hh = (cidx >> 2) & 3, cg = cidx & 3;
-      const int n = n0 + tok;
-      uint4 u = {0, 0, 0, 0};
-      if (n < n_end && hh < nh)
-        u = *reinterpret_cast<const uint4*>(base + (size_t)n * C3 + (1 + tensor) * C +
-                                            (h0 + hh) * kD + 8 * cg);
-      stg[i] = u;
-    }
-  };
-  auto commit = [&]() {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cidx = tid + 256 * i;
-      const int tensor = cidx >> 9, tok = (cidx >> 4) & 31;
-      const int hh = (cidx >> 2) & 3, cg = cidx & 3;
-      uint16_t* hv = reinterpret_cast<uint16_t*>(&stg[i]);
-      bf16* dst = tensor == 0 ? kt : vt;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint16_t v = hv[j];
-        if (tensor == 0) {
-          v = relu_bits(v);
-          dacc[j] += __uint_as_float((uint32_t)v << 16);
-        }
-        dst[((hh * kD) + 8 * cg + j) * kTS + tok].u = v;
-      }
-    }
+      for (int ks = 0; ks < 2; ++ks)
+        st[2 * t + ks] = ok ? *reinterpret_cast<const uint4*>(row + (1 + t) * C + 16 * ks)
+                            : uint4{0, 0, 0, 0};
   };
 
-  f32x16 acc;
+  f32x16 z;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const bf16* ka = kt + wave * kD * kTS;
-  const bf16* va = vt + wave * kD * kTS;
-  if (n_begin < n_end) issue(n_begin);
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  float dacc = 0.f;
+  issue(n_begin);
   for (int n0 = n_begin; n0 < n_end; n0 += kTT) {
-    commit();
-    __syncthreads();
+    uint4 cur[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = st[i];
     if (n0 + kTT < n_end) issue(n0 + kTT);
 #pragma unroll
-    for (int ks = 0; ks < kTT / 16; ++ks) {
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(&ka[(lane & 31) * kTS + 16 * ks + 8 * g]));
-      const bf16x8 v = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(&va[(lane & 31) * kTS + 16 * ks + 8 * g]));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v, acc, 0, 0, 0);
-    }
-    __syncthreads();
-  }
-  // D: thread t summed channels 8cg..8cg+7 of head hh for its tokens, where
-  // (hh, cg) = ((t >> 2) & 3, t & 3); the 16 threads sharing t & 15 are
-  // added in thread order.
+    for (int ks = 0; ks < 2; ++ks) {  // relu on K^ (bf16 sign bit)
+      uint16_t* hv = reinterpret_cast<uint16_t*>(&cur[ks]);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dpart[tid][j] = dacc[j];
-  __syncthreads();
-  if (tid < kHG * kD) {
-    const int hh = tid / kD, ch = tid % kD, cg = ch / 8, j = ch % 8;
-    float sum = 0.f;
-    for (int t2 = hh * 4 + cg; t2 < 256; t2 += 16) sum += dpart[t2][j];
-    dsum[hh][ch] = sum;
-  }
-  __syncthreads();
-  if (wave < nh) {
-    float* out = part + ((size_t)(b * heads + h0 + wave) * nchunks + chunk) * kPart;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 8 * (r >> 2) + 4 * g + (r & 3);
-      out[i * kD + (lane & 31)] = acc[r];
+      for (int e = 0; e < 8; ++e) hv[e] = relu_bits(hv[e]);
     }
-    if (lane < kD) out[kD * kD + lane] = dsum[wave][lane];
+    f32x16 kt, vt;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) kt[r] = vt[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      kt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur[ks]),
+                                                   eye[ks], kt, 0, 0, 0);
+      vt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur[2 + ks]),
+                                                   eye[ks], vt, 0, 0, 0);
+    }
+    // kt[r], vt[r]: feature col of token 8(r/4) + 4g + r%4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dacc += kt[r];
+#pragma unroll
+    for (int slab = 0; slab < 2; ++slab) {
+      uint4 ka, vb;
+      ka.x = pack_bf16x2(kt[8 * slab + 0], kt[8 * slab + 1]);
+      ka.y = pack_bf16x2(kt[8 * slab + 2], kt[8 * slab + 3]);
+      ka.z = pack_bf16x2(kt[8 * slab + 4], kt[8 * slab + 5]);
+      ka.w = pack_bf16x2(kt[8 * slab + 6], kt[8 * slab + 7]);
+      vb.x = pack_bf16x2(vt[8 * slab + 0], vt[8 * slab + 1]);
+      vb.y = pack_bf16x2(vt[8 * slab + 2], vt[8 * slab + 3]);
+      vb.z = pack_bf16x2(vt[8 * slab + 4], vt[8 * slab + 5]);
+      vb.w = pack_bf16x2(vt[8 * slab + 6], vt[8 * slab + 7]);
+      z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka),
+                                                  __builtin_bit_cast(bf16x8, vb), z,
+                                                  0, 0, 0);
+    }
   }
+  dacc += __shfl_xor(dacc, 32, 64);
+  // z[r] = Z[i][c] with c = col, i = 8(r/4) + 4g + r%4
+  float* out = part + ((size_t)(b * heads + h) * nchunks + chunk) * kPart;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = 8 * (r >> 2) + 4 * g + (r & 3);
+    out[i * kD + col] = z[r];
+  }
+  if (g == 0) out[kD * kD + col] = dacc;
 }
 
 // O^T = Z^T relu(Q^)^T with Z split into bf16 hi + lo parts, normalised by
-// relu(q^) . D.  grid (ceil(tokens/64), ceil(heads/4), batch), 256 threads;
-// wave = head, two 32-token tiles per wave.
+// relu(q^) . D.  grid (ceil(tokens/128), ceil(heads/4), batch), 256
+// threads; wave = head, four 32-token tiles per wave, next tile prefetched.
 __global__ __launch_bounds__(256) void lin_apply_mfma(
     const bf16* __restrict__ qkvh, const float* __restrict__ kv,
     const float* __restrict__ ksum, bf16* __restrict__ o, int tokens,
@@ -276,30 +272,39 @@ __global__ __launch_bounds__(256) void lin_apply_mfma(
     zlo[ks] = __builtin_bit_cast(bf16x8, uint4{lw[0], lw[1], lw[2], lw[3]});
   }
 
-  for (int tt = 0; tt < 2; ++tt) {
-    const int n = blockIdx.x * 64 + tt * 32 + col;
+  const int n_base = blockIdx.x * kApplyTok;
+  const bf16* qbase = qkvh + (size_t)b * tokens * C3 + h * kD + 8 * g;
+  uint4 st[2];
+  auto issue = [&](int n) {
     const bool ok = n < tokens;
-    const bf16* qrow = qkvh + ((size_t)b * tokens + (ok ? n : 0)) * C3 + h * kD;
+    const bf16* qrow = qbase + (size_t)(ok ? n : 0) * C3;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      st[ks] = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks) : uint4{0, 0, 0, 0};
+  };
+  issue(n_base + col);
+  for (int tt = 0; tt < kApplyTok / 32; ++tt) {
+    const int n = n_base + tt * 32 + col;
+    uint4 cur[2] = {st[0], st[1]};
+    if (tt + 1 < kApplyTok / 32) issue(n + 32);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     float den = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      uint4 u = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * g)
-                   : uint4{0, 0, 0, 0};
-      uint16_t* hv = reinterpret_cast<uint16_t*>(&u);
+      uint16_t* hv = reinterpret_cast<uint16_t*>(&cur[ks]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         hv[e] = relu_bits(hv[e]);
         den = fmaf(__uint_as_float((uint32_t)hv[e] << 16), dreg[ks][e], den);
       }
-      const bf16x8 qb = __builtin_bit_cast(bf16x8, u);
+      const bf16x8 qb = __builtin_bit_cast(bf16x8, cur[ks]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zhi[ks], qb, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zlo[ks], qb, acc, 0, 0, 0);
     }
     den += __shfl_xor(den, 32, 64);
-    if (!ok) continue;
+    if (n >= tokens) continue;
     const float inv = den > 0.f ? 1.f / den : 0.f;
     bf16* orow = o + ((size_t)b * tokens + n) * C + h * kD;
 #pragma unroll
@@ -352,7 +357,7 @@ hipError_t launch_lin_apply(bool bf, const void* qkv_hat, const float* kv,
                             const float* ksum, void* o, int batch, int tokens,
                             int heads, hipStream_t s) {
   if (bf) {
-    dim3 grid((tokens + 63) / 64, (heads + kHG - 1) / kHG, batch);
+    dim3 grid((tokens + kApplyTok - 1) / kApplyTok, (heads + kHG - 1) / kHG, batch);
     lin_apply_mfma<<<grid, 256, 0, s>>>(static_cast<const bf16*>(qkv_hat), kv,
                                         ksum, static_cast<bf16*>(o), tokens, heads);
     return hipGetLastError();

@@ -45,58 +45,90 @@ struct Vec<float> {
   }
 };
 
-// One wavefront per row; lane l handles 16-byte vectors l, l + 64, ...
-template <typename T>
+// One wavefront per row, kRows rows per wave with all loads issued first;
+// lane l handles the 16-byte vectors l, l + 64, ... of a row.
+constexpr int kRows = 4;
+
+// NI = 16-byte vectors per lane (ceil(ch / V / 64)).
+template <typename T, int NI>
 __global__ __launch_bounds__(256) void layernorm_kernel(
     const T* __restrict__ x, const float* __restrict__ g,
     const float* __restrict__ be, T* __restrict__ y, int rows, int ch) {
   constexpr int V = Vec<T>::N;
-  constexpr int NI = kMaxPerLane / V;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= rows) return;
+  const int row0 = (blockIdx.x * 4 + wave) * kRows;
   const int nvec = ch / V;
-  const T* xr = x + (size_t)row * ch;
-  float v[NI][V];
-  float s = 0.f;
+  float v[kRows][NI][V];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int vi = lane + 64 * i;
-    if (vi < nvec) {
-      Vec<T>::load(xr + vi * V, v[i]);
-    } else {
+  for (int q = 0; q < kRows; ++q) {
+    const int row = row0 + q;
+    const T* xr = x + (size_t)(row < rows ? row : 0) * ch;
 #pragma unroll
-      for (int j = 0; j < V; ++j) v[i][j] = 0.f;
-    }
+    for (int i = 0; i < NI; ++i) {
+      const int vi = lane + 64 * i;
+      if (vi < nvec && row < rows) {
+        Vec<T>::load(xr + vi * V, v[q][i]);
+      } else {
 #pragma unroll
-    for (int j = 0; j < V; ++j) s += v[i][j];
-  }
-  const float mean = wave_sum(s) / (float)ch;
-  float q = 0.f;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (lane + 64 * i < nvec) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const float dlt = v[i][j] - mean;
-        q = fmaf(dlt, dlt, q);
+        for (int j = 0; j < V; ++j) v[q][i][j] = 0.f;
       }
     }
   }
-  const float rstd = rsqrtf(wave_sum(q) / (float)ch + 1e-5f);
-  T* yr = y + (size_t)row * ch;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int vi = lane + 64 * i;
-    if (vi >= nvec) continue;
-    float o[V];
+  for (int q = 0; q < kRows; ++q) {
+    const int row = row0 + q;
+    float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int c = vi * V + j;
-      o[j] = (v[i][j] - mean) * rstd * g[c] + be[c];
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < V; ++j) s += v[q][i][j];
+    const float mean = wave_sum(s) / (float)ch;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (lane + 64 * i < nvec) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const float dlt = v[q][i][j] - mean;
+          sq = fmaf(dlt, dlt, sq);
+        }
+      }
     }
-    Vec<T>::store(yr + vi * V, o);
+    const float rstd = rsqrtf(wave_sum(sq) / (float)ch + 1e-5f);
+    if (row >= rows) continue;
+    T* yr = y + (size_t)row * ch;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int vi = lane + 64 * i;
+      if (vi >= nvec) continue;
+      float o[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int c = vi * V + j;
+        o[j] = (v[q][i][j] - mean) * rstd * g[c] + be[c];
+      }
+      Vec<T>::store(yr + vi * V, o);
+    }
   }
+}
+
+template <typename T>
+hipError_t run_ln(const void* x, const float* gamma, const float* beta, void* y,
+                  int rows, int ch, hipStream_t s) {
+  const unsigned blocks = (unsigned)((rows + 4 * kRows - 1) / (4 * kRows));
+  const int ni = (ch / Vec<T>::N + 63) / 64;
+  const T* xi = static_cast<const T*>(x);
+  T* yo = static_cast<T*>(y);
+  if (ni <= 1)
+    layernorm_kernel<T, 1><<<blocks, 256, 0, s>>>(xi, gamma, beta, yo, rows, ch);
+  else if (ni <= 2)
+    layernorm_kernel<T, 2><<<blocks, 256, 0, s>>>(xi, gamma, beta, yo, rows, ch);
+  else if (ni <= 4)
+    layernorm_kernel<T, 4><<<blocks, 256, 0, s>>>(xi, gamma, beta, yo, rows, ch);
+  else
+    layernorm_kernel<T, kMaxPerLane / Vec<T>::N><<<blocks, 256, 0, s>>>(
+        xi, gamma, beta, yo, rows, ch);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -104,16 +136,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
 hipError_t launch_layernorm(bool bf, const void* x, const float* gamma,
                             const float* beta, void* y, int rows, int ch,
                             hipStream_t s) {
-  const unsigned blocks = (unsigned)((rows + 3) / 4);
-  if (bf)
-    layernorm_kernel<bf16><<<blocks, 256, 0, s>>>(static_cast<const bf16*>(x),
-                                                  gamma, beta,
-                                                  static_cast<bf16*>(y), rows, ch);
-  else
-    layernorm_kernel<float><<<blocks, 256, 0, s>>>(static_cast<const float*>(x),
-                                                   gamma, beta,
-                                                   static_cast<float*>(y), rows, ch);
-  return hipGetLastError();
+  return bf ? run_ln<bf16>(x, gamma, beta, y, rows, ch, s)
+            : run_ln<float>(x, gamma, beta, y, rows, ch, s);
 }
 
 }  // namespace hsmla
