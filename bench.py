@@ -30,6 +30,9 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, GB/s
 MFMA_BF16_TFLOPS = 2500.0  # dense bf16 matrix peak, TFLOP/s
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -39,6 +42,9 @@ def parse():
     ap.add_argument("--keep", type=float, default=0.10)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first copy 1 GiB with a plain device copy (a known "
+                         "byte count for calibrating HBM traffic counters)")
     ap.add_argument("--cpu-rows", type=int, default=128,
                     help="token rows of the crop the CPU oracle is timed on")
     return ap.parse_args()
@@ -156,6 +162,35 @@ def roofline_entry(name, wl, sel, avg_ms):
                 unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
 
 
+def measured_traffic(launch):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated), or None when there is none for
+    this launch or its kernel sources changed since the counters were taken.
+    Summary lines read: 'traffic: launch=<name> bytes=<B> sources=<f1,f2>
+    sha256=<hex of the concatenated sources>'."""
+    import hashlib
+    import glob
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(tok.split("=", 1) for tok in line.split()[1:])
+                if kv.get("launch") != launch:
+                    continue
+                h = hashlib.sha256()
+                try:
+                    for src in kv["sources"].split(","):
+                        with open(os.path.join(ROOT, src), "rb") as g:
+                            h.update(g.read())
+                except OSError:
+                    return None
+                if h.hexdigest() != kv.get("sha256"):
+                    return None
+                return int(kv["bytes"])
+    return None
+
+
 # ---------------------------------------------------------------------------
 # CPU oracle baseline (bounded crop of the same workload)
 # ---------------------------------------------------------------------------
@@ -199,6 +234,13 @@ def main():
     from workloads import WORKLOADS, keep_blocks_for, make_inputs, scaled
 
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     base = scaled(WORKLOADS["block"], keep=args.keep)
     inp = make_inputs(base)
     x = to_device(inp["x"], base.dtype)
@@ -260,6 +302,7 @@ def main():
     dominant = max(kernels, key=lambda n: kernels[n]["avg_us"])
     roof = roofline_entry(dominant, base, sel, kernels[dominant]["avg_us"] * 1e-3)
     roof["kernel"] = dominant
+    roof["traffic"] = measured_traffic(dominant)
     by, fl = algorithmic_work(dominant, base, sel)
     roof["work_per_launch"] = {"bytes": int(by), "flops": int(fl)}
 

@@ -181,7 +181,7 @@ hsmla_status run_qkv(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
                      hipStream_t s, Rec& r) {
   r.mark("qkv_gemm");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, x, w->w_qkv, nullptr, qkv, (int)D.P,
-                               3 * D.C, D.C, s));
+                               3 * D.C, D.C, s, hsmla::GemmSite::kQkv));
   r.mark("dw_taps");
   HSMLA_TRY(hsmla::launch_dw_taps(D.bf, w->dw, d->branch_k, d->n_branches,
                                   D.kmax, 3 * D.C, 1, taps, s));
@@ -365,7 +365,7 @@ hsmla_status forward_impl(const hsmla_desc* desc, const hsmla_weights* w,
   if ((st = run_module(D, desc, w, x, ws, L, s, r)) != HSMLA_OK) return st;
   r.mark("out_proj");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, nullptr, y, (int)D.P,
-                               D.C, D.C, s));
+                               D.C, D.C, s, hsmla::GemmSite::kOut));
   r.end();
   return r.ok ? HSMLA_OK : HSMLA_ERR_HIP;
 }
@@ -399,11 +399,13 @@ hsmla_status block_impl(const hsmla_desc* desc, const hsmla_weights* w,
   if ((st = run_module(D, desc, w, xn, ws, L, s, r)) != HSMLA_OK) return st;
   // x1 = x + O W_o (residual fused into the projection epilogue)
   r.mark("out_proj_residual");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, x, x1, P, C, C, s));
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, x, x1, P, C, C, s,
+                               hsmla::GemmSite::kOut));
   r.mark("layernorm2");
   HSMLA_TRY(hsmla::launch_layernorm(D.bf, x1, f->ln2_g, f->ln2_b, xn, P, C, s));
   r.mark("ffn1_gemm");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, xn, f->w1, nullptr, h1, P, 4 * C, C, s));
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, xn, f->w1, nullptr, h1, P, 4 * C, C, s,
+                               hsmla::GemmSite::kFfn1));
   const void* ffn_k[1] = {f->dw_ffn};
   const int ffn_ks[1] = {3};
   r.mark("ffn_dw_taps");
@@ -412,7 +414,8 @@ hsmla_status block_impl(const hsmla_desc* desc, const hsmla_weights* w,
   HSMLA_TRY(hsmla::launch_dwconv(D.bf, h1, h2, ftaps, 3, D.B, D.gh, D.gw, 4 * C,
                                  true, s));
   r.mark("ffn2_gemm_residual");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, h2, f->w2, x1, out, P, C, 4 * C, s));
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, h2, f->w2, x1, out, P, C, 4 * C, s,
+                               hsmla::GemmSite::kFfn2));
   r.end();
   return r.ok ? HSMLA_OK : HSMLA_ERR_HIP;
 }

@@ -33,6 +33,9 @@ __device__ __forceinline__ uint4 ld16(const bf16* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// SITE only names the call site (one kernel symbol per projection, so
+// profiles tell the four GEMMs apart); the code is the same.
+template <int SITE>
 __global__ __launch_bounds__(256, 2) void gemm_mfma_bf16(
     const bf16* __restrict__ A, const bf16* __restrict__ W,
     const bf16* __restrict__ R, bf16* __restrict__ C, int M, int N, int K,
@@ -209,19 +212,32 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ A,
   }
 }
 
+
+template <int SITE>
+void run_mfma(const void* A, const void* W, const void* R, void* C, int M,
+              int N, int K, hipStream_t s) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int total = tiles_m * tiles_n;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  gemm_mfma_bf16<SITE><<<per_xcd * kXcds, 256, 0, s>>>(
+      static_cast<const bf16*>(A), static_cast<const bf16*>(W),
+      static_cast<const bf16*>(R), static_cast<bf16*>(C), M, N, K, tiles_n,
+      total, per_xcd);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(bool bf, const void* A, const void* W, const void* R,
-                       void* C, int M, int N, int K, hipStream_t s) {
+                       void* C, int M, int N, int K, hipStream_t s,
+                       GemmSite site) {
   if (M == 0 || N == 0) return hipSuccess;
   if (bf) {
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const int total = tiles_m * tiles_n;
-    const int per_xcd = (total + kXcds - 1) / kXcds;
-    gemm_mfma_bf16<<<per_xcd * kXcds, 256, 0, s>>>(
-        static_cast<const bf16*>(A), static_cast<const bf16*>(W),
-        static_cast<const bf16*>(R), static_cast<bf16*>(C), M, N, K, tiles_n,
-        total, per_xcd);
+    switch (site) {
+      case GemmSite::kQkv: run_mfma<0>(A, W, R, C, M, N, K, s); break;
+      case GemmSite::kOut: run_mfma<1>(A, W, R, C, M, N, K, s); break;
+      case GemmSite::kFfn1: run_mfma<2>(A, W, R, C, M, N, K, s); break;
+      default: run_mfma<3>(A, W, R, C, M, N, K, s); break;
+    }
   } else {
     dim3 grid((N + kTN - 1) / kTN, (M + kTM - 1) / kTM);
     gemm_f32<<<grid, 256, 0, s>>>(static_cast<const float*>(A),

@@ -9,10 +9,14 @@
 
 namespace hsmla {
 
+// Which projection a GEMM launch is (only used to name the kernel symbol).
+enum class GemmSite { kQkv, kOut, kFfn1, kFfn2 };
+
 // C[M][N] = A[M][K] . W[N][K]^T (+ R[M][N] when R != nullptr), row-major.
 // N and K must be multiples of 32 (8-element chunks are loaded whole).
 hipError_t launch_gemm(bool bf, const void* A, const void* W, const void* R,
-                       void* C, int M, int N, int K, hipStream_t s);
+                       void* C, int M, int N, int K, hipStream_t s,
+                       GemmSite site);
 
 // Effective depthwise taps: weff[tap][ch] (float32, kmax x kmax taps) =
 // identity (centre tap += 1 when `identity`) + sum of the given kernels,
