@@ -41,8 +41,21 @@ __global__ void dw_taps_kernel(KernelSet ks, int nk, int kmax, int ch,
   weff[idx] = v;
 }
 
+// GELU(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)) with erf from
+// Abramowitz & Stegun 7.1.26 (Hastings' rational approximation):
+//   erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2),
+//   t = 1 / (1 + p z),  z >= 0,  |error| <= 1.5e-7,
+// extended to z < 0 by oddness.  Far below the bfloat16 output precision.
 __device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+  constexpr float p = 0.3275911f, a1 = 0.254829592f, a2 = -0.284496736f,
+                  a3 = 1.421413741f, a4 = -1.453152027f, a5 = 1.061405429f;
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(p, z, 1.f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+  const float erf_abs = fmaf(-poly, e, 1.f);
+  const float erf_v = copysignf(erf_abs, x);
+  return 0.5f * x * (1.f + erf_v);
 }
 
 constexpr int TH = 32;   // output rows per workgroup strip
@@ -193,31 +206,30 @@ __global__ __launch_bounds__(256) void dwconv_stream(
       const int r = r0 + u;
       if (r >= r_end) break;
       Raw<T, V>(&cur)[K] = (u % 2 == 0) ? ra : rb;
-      float xin[K][V];
+      // A halo row outside the grid contributes nothing: skip it (uniform).
+      if (r >= 0 && r < gh) {
+        float xin[K][V];
 #pragma unroll
-      for (int kx = 0; kx < K; ++kx) cur[kx].cvt(xin[kx]);
-      if (r < 0 || r >= gh) {  // uniform: a halo row outside the grid
+        for (int kx = 0; kx < K; ++kx) cur[kx].cvt(xin[kx]);
+        if (edge_tile) {
 #pragma unroll
-        for (int kx = 0; kx < K; ++kx)
+          for (int kx = 0; kx < K; ++kx)
 #pragma unroll
-          for (int j = 0; j < V; ++j) xin[kx][j] = 0.f;
-      } else if (edge_tile) {
+            for (int j = 0; j < V; ++j) xin[kx][j] = col_ok[kx] ? xin[kx][j] : 0.f;
+        }
+        // input row r feeds output row r - R + i with vertical tap K - 1 - i
 #pragma unroll
-        for (int kx = 0; kx < K; ++kx)
+        for (int i = 0; i < K; ++i) {
+          const int slot = (u - R + i + 2 * K) % K;
 #pragma unroll
-          for (int j = 0; j < V; ++j) xin[kx][j] = col_ok[kx] ? xin[kx][j] : 0.f;
+          for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+              acc[slot][j] = fmaf(w[K - 1 - i][kx][j], xin[kx][j], acc[slot][j]);
+        }
       }
-      if (r + 2 < r_end) load_row(cur, r + 2);
-      // input row r feeds output row r - R + i with vertical tap K - 1 - i
-#pragma unroll
-      for (int i = 0; i < K; ++i) {
-        const int slot = (u - R + i + 2 * K) % K;
-#pragma unroll
-        for (int kx = 0; kx < K; ++kx)
-#pragma unroll
-          for (int j = 0; j < V; ++j)
-            acc[slot][j] = fmaf(w[K - 1 - i][kx][j], xin[kx][j], acc[slot][j]);
-      }
+      // unconditional (clamped) prefetch keeps the load/wait pattern regular
+      load_row(cur, r + 2);
       const int done = (u - R + 2 * K) % K;  // slot of output row r - R
       const int yo = r - R;
       if (yo >= y0 && yo < y_end && x < gw && c_ok) {

@@ -71,14 +71,17 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(
 }
 
 // grid (batch), 1024 threads.  rank(t) = #{u : s_u > s_t or (s_u == s_t and
-// u < t)}; block t is kept iff rank(t) < keep.  Its slot in the output is
-// the number of kept blocks below it, formed with wave ballots and a prefix
-// over the 16 wave totals.  Exact and order-independent.
+// u < t)}; block t is kept iff rank(t) < keep.  P = 1024 / T threads share
+// one candidate (each scans a strided part of the scores, combined by a
+// wave reduction).  The slot of a kept block in the output is the number of
+// kept blocks below it, formed with wave ballots and a prefix over the 16
+// wave totals.  Exact and order-independent.
 __global__ __launch_bounds__(1024) void topk_kernel(
     const float* __restrict__ scores, float* __restrict__ scores_copy,
-    int32_t* __restrict__ sel, int nblocks, int keep) {
+    int32_t* __restrict__ sel, int nblocks, int keep, int lanes_per) {
   extern __shared__ float sh[];
-  float* s = sh;  // [nblocks]
+  float* s = sh;                                        // [nblocks]
+  unsigned char* kept = reinterpret_cast<unsigned char*>(sh + nblocks);  // [nblocks]
   __shared__ int wave_tot[16];
   __shared__ int base_all;
   const int b = blockIdx.x;
@@ -91,25 +94,33 @@ __global__ __launch_bounds__(1024) void topk_kernel(
   }
   if (threadIdx.x == 0) base_all = 0;
   __syncthreads();
+  const int per_pass = blockDim.x / lanes_per;
+  const int part = threadIdx.x % lanes_per;
+  for (int t0 = 0; t0 < nblocks; t0 += per_pass) {
+    const int t = t0 + threadIdx.x / lanes_per;
+    int rank = 0;
+    if (t < nblocks) {
+      // blocks below t count when >= v, blocks above t only when > v
+      const float v = s[t];
+      for (int u = part; u < nblocks; u += lanes_per) {
+        const float w = s[u];
+        rank += u < t ? (w >= v) : (w > v);
+      }
+    }
+    for (int off = lanes_per >> 1; off >= 1; off >>= 1) rank += __shfl_xor(rank, off, 64);
+    if (t < nblocks && part == 0) kept[t] = rank < keep;
+  }
+  __syncthreads();
   for (int t0 = 0; t0 < nblocks; t0 += blockDim.x) {
     const int t = t0 + threadIdx.x;
-    bool kept = false;
-    if (t < nblocks) {
-      const float v = s[t];
-      int rank = 0;
-      for (int u = 0; u < nblocks; ++u) {
-        const float w = s[u];
-        rank += (w > v) || (w == v && u < t);
-      }
-      kept = rank < keep;
-    }
-    const uint64_t m = __ballot(kept);
+    const bool k = t < nblocks && kept[t];
+    const uint64_t m = __ballot(k);
     const int below = __popcll(m & ((1ull << lane) - 1ull));
     if (lane == 0) wave_tot[wave] = __popcll(m);
     __syncthreads();
     int off = base_all;
     for (int w2 = 0; w2 < wave; ++w2) off += wave_tot[w2];
-    if (kept) sel[(size_t)b * keep + off + below] = t;
+    if (k) sel[(size_t)b * keep + off + below] = t;
     __syncthreads();
     if (threadIdx.x == 0) {
       int tot = 0;
@@ -143,8 +154,11 @@ hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
                        int batch, int nblocks, int keep, hipStream_t s) {
   if (keep == 0 && scores_copy == nullptr) return hipSuccess;
-  const size_t lds = (size_t)nblocks * sizeof(float);
-  topk_kernel<<<batch, 1024, lds, s>>>(scores, scores_copy, sel, nblocks, keep);
+  const size_t lds = (size_t)nblocks * (sizeof(float) + 1);
+  int lanes_per = 1;
+  while (lanes_per < 64 && lanes_per * 2 * nblocks <= 1024) lanes_per *= 2;
+  topk_kernel<<<batch, 1024, lds, s>>>(scores, scores_copy, sel, nblocks, keep,
+                                       lanes_per);
   return hipGetLastError();
 }
 

@@ -73,8 +73,17 @@ __global__ __launch_bounds__(64) void kv_combine_kernel(
   const float* p = part + (size_t)bh * nchunks * kPart;
   const int e = blockIdx.y * 64 + threadIdx.x;
   if (e < kPart) {
+    // loads issued 8 at a time, added strictly in chunk order
     float s = 0.f;
-    for (int c = 0; c < nchunks; ++c) s += p[(size_t)c * kPart + e];
+    int c = 0;
+    for (; c + 8 <= nchunks; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = p[(size_t)(c + i) * kPart + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; c < nchunks; ++c) s += p[(size_t)c * kPart + e];
     if (e < kD * kD)
       kv[(size_t)bh * kD * kD + e] = s;
     else
