@@ -47,6 +47,7 @@ __all__ = [
     "block_features",
     "gate_scores",
     "select_blocks",
+    "select_threshold",
     "window_bounds",
     "refine_selected",
     "hsmla_module",
@@ -294,6 +295,25 @@ def select_blocks(scores, keep_blocks):
     return out
 
 
+def select_threshold(scores, tau):
+    """Blocks whose score exceeds tau, per image, ascending (FT 3.2, the
+    alpha equation: the routed set is {b : M_b > tau}, a strict inequality).
+
+    scores: [B, T].  Returns (sel [B, T] int64 padded with -1, counts [B]).
+    Pinned by: a brute-force membership loop, and agreement with
+    select_blocks when tau lies strictly between the k-th and (k+1)-th score.
+    """
+    s = np.asarray(scores)
+    B, T = s.shape
+    sel = np.full((B, T), -1, dtype=np.int64)
+    counts = np.zeros(B, dtype=np.int64)
+    for bi in range(B):
+        idx = np.nonzero(s[bi] > tau)[0]
+        counts[bi] = idx.size
+        sel[bi, :idx.size] = idx
+    return sel, counts
+
+
 # ---------------------------------------------------------------------------
 # step 5: local softmax refinement of the selected blocks
 # ---------------------------------------------------------------------------
@@ -350,6 +370,8 @@ def refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads, block,
     scale = 1.0 / math.sqrt(d)
     for bi in range(B):
         for t in np.asarray(sel[bi]).tolist():
+            if t < 0:  # padding of a thresholded selection
+                continue
             nbc = grid_w // block
             r0, c0 = (t // nbc) * block, (t % nbc) * block
             qi = _tokens(r0, r0 + block, c0, c0 + block, grid_w)
@@ -384,7 +406,8 @@ def refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads, block,
 # ---------------------------------------------------------------------------
 
 def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
-                 keep_blocks, staged=False, sel=None, scores_f32=True):
+                 keep_blocks, staged=False, sel=None, scores_f32=True,
+                 tau=None):
     """Steps 1-5 of the module (everything before the output projection).
 
     Follows the five inference stages FT 3.6 lists: global linear path,
@@ -394,7 +417,9 @@ def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
 
     ``sel`` injects a selection (used when a GPU run picks a different block
     inside a near-tie band).  ``scores_f32`` ranks the float64 scores after
-    rounding them to float32, the precision the GPU ranks in.
+    rounding them to float32, the precision the GPU ranks in.  With ``tau``
+    set, blocks are routed by the threshold M_t > tau instead of the top
+    keep_blocks; ``sel`` is then padded with -1 and "counts" is returned.
     """
     rnd = round_bf16 if staged else _identity
     C = x.shape[-1]
@@ -404,14 +429,17 @@ def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
     o_lin = rnd(o_lin_raw)
     scores = gate_scores(qkv_hat, weights["gate_w"], weights["gate_b"],
                          grid_h, grid_w, block, heads)
-    if sel is None:
-        rank_on = scores.astype(np.float32) if scores_f32 else scores
+    counts = None
+    rank_on = scores.astype(np.float32) if scores_f32 else scores
+    if sel is None and tau is not None:
+        sel, counts = select_threshold(rank_on, np.float32(tau) if scores_f32 else tau)
+    elif sel is None:
         sel = select_blocks(rank_on, keep_blocks)
     o = refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads,
                         block, window, rnd=rnd)
     assert o.shape[-1] == C
     return dict(qkv=qkv, qkv_hat=qkv_hat, Z=Z, D=D, o_lin=o_lin,
-                scores=scores, sel=np.asarray(sel), o=o)
+                scores=scores, sel=np.asarray(sel), o=o, counts=counts)
 
 
 def hsmla_forward(x, weights, *, staged=False, **kw):

@@ -424,3 +424,49 @@ def test_block_forward_keep_zero_composition():
     h = O.gelu(O.dwconv_same(O.layer_norm(x1, 1.0, 0.0) @ inp["w1"],
                              inp["dw_ffn"], 16, 16))
     np.testing.assert_allclose(r["out"], x1 + h @ inp["w2"], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# threshold routing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_select_threshold_brute_force(seed):
+    rng = _rng(300 + seed)
+    scores = rng.integers(0, 6, size=(3, 23)) / 5.0
+    for tau in (-1.0, 0.0, 0.2, 0.5, 0.6, 1.0, 2.0):
+        sel, counts = O.select_threshold(scores, tau)
+        for b in range(3):
+            want = [t for t in range(23) if scores[b, t] > tau]  # strict
+            assert counts[b] == len(want)
+            assert sel[b, :counts[b]].tolist() == want
+            assert np.all(sel[b, counts[b]:] == -1)
+
+
+def test_threshold_between_kth_and_next_equals_topk():
+    rng = _rng(310)
+    scores = rng.random((4, 40))
+    for k in (0, 1, 7, 39, 40):
+        srt = np.sort(scores, axis=1)[:, ::-1]
+        for b in range(4):
+            hi = srt[b, k - 1] if k > 0 else 2.0
+            lo = srt[b, k] if k < 40 else -1.0
+            tau = 0.5 * (hi + lo)
+            sel, counts = O.select_threshold(scores[b:b + 1], tau)
+            assert counts[0] == k
+            assert sel[0, :k].tolist() == O.select_blocks(scores[b:b + 1], k)[0].tolist()
+
+
+def test_threshold_module_matches_topk_module():
+    """A threshold placed between the k-th and (k+1)-th score routes the same
+    blocks as top-k, so the module outputs agree exactly."""
+    wl = WORKLOADS["tiny"]
+    inp = make_inputs(wl)
+    ref = O.hsmla_forward(inp["x"], inp, **wl.kwargs())
+    s = np.sort(ref["scores"].astype(np.float32)[0])[::-1]
+    k = wl.keep_blocks
+    tau = float(0.5 * (np.float64(s[k - 1]) + np.float64(s[k])))
+    thr = O.hsmla_forward(inp["x"], inp, tau=tau, **wl.kwargs())
+    assert thr["counts"][0] == k
+    np.testing.assert_array_equal(thr["sel"][0, :k], ref["sel"][0])
+    np.testing.assert_array_equal(thr["y"], ref["y"])
