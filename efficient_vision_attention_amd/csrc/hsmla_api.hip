@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -29,9 +30,12 @@ inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Dims {
   int B, gh, gw, N, C, H, T, k, Bs, w, kmax;
+  int sw;     // width of a sel row: k (top-k) or T (threshold)
   size_t P;   // B * N tokens
   size_t e;   // bytes per activation element
   bool bf;
+  bool thr;   // threshold routing
+  float tau;
 };
 
 hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
@@ -54,6 +58,9 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
   const int64_t T = (int64_t)(d->grid_h / d->block) * (d->grid_w / d->block);
   if (T > kMaxBlocks) return HSMLA_ERR_SHAPE;
   if (d->keep_blocks < 0 || d->keep_blocks > T) return HSMLA_ERR_SHAPE;
+  if (d->routing != HSMLA_ROUTE_TOPK && d->routing != HSMLA_ROUTE_THRESHOLD)
+    return HSMLA_ERR_ARG;
+  if (d->routing == HSMLA_ROUTE_THRESHOLD && isnan(d->tau)) return HSMLA_ERR_ARG;
   const int64_t N = (int64_t)d->grid_h * d->grid_w;
   // every element index must fit a 32-bit grid dimension and size_t math
   if (N * d->batch * 4 * (int64_t)d->channels > ((int64_t)1 << 40)) return HSMLA_ERR_SHAPE;
@@ -72,6 +79,9 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
     out->kmax = kmax;
     out->P = (size_t)N * d->batch;
     out->bf = d->dtype == HSMLA_BF16;
+    out->thr = d->routing == HSMLA_ROUTE_THRESHOLD;
+    out->tau = d->tau;
+    out->sw = out->thr ? (int)T : d->keep_blocks;
     out->e = out->bf ? 2 : 4;
   }
   return HSMLA_OK;
@@ -80,11 +90,11 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
 // Workspace sections, in this order (each start rounded up to 256 bytes):
 //   qkv [P][3C], qkv_hat [P][3C], o [P][C], kv [B][H][d][d] f32,
 //   ksum [B][H][d] f32, kv partials f32, dw taps [kmax^2][3C] f32,
-//   scores [B][T] f32, sel [B][k] i32,
+//   scores [B][T] f32, sel [B][k] i32 (threshold: [B][T] i32, counts [B] i32),
 //   (block only) xn [P][C], x1 [P][C], h1 [P][4C], h2 [P][4C],
 //   ffn taps [9][4C] f32.
 struct Layout {
-  size_t qkv, qkv_hat, o, kv, ksum, part, taps, scores, sel;
+  size_t qkv, qkv_hat, o, kv, ksum, part, taps, scores, sel, counts;
   size_t xn, x1, h1, h2, ffn_taps;
   size_t total;
 };
@@ -114,7 +124,8 @@ Layout layout(const Dims& D, int op) {
     L.part = take(part_bytes);
     L.taps = take(tap_bytes);
     L.scores = take((size_t)D.B * D.T * 4);
-    L.sel = take((size_t)D.B * D.k * 4 + 4);
+    L.sel = take((size_t)D.B * D.sw * 4 + 4);
+    if (D.thr) L.counts = take((size_t)D.B * 4);
     if (op == HSMLA_OP_BLOCK) {
       L.xn = take(D.P * D.C * D.e);
       L.x1 = take(D.P * D.C * D.e);
@@ -204,6 +215,7 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
   float* taps = reinterpret_cast<float*>(at(ws, L.taps));
   float* scores = reinterpret_cast<float*>(at(ws, L.scores));
   int32_t* sel = reinterpret_cast<int32_t*>(at(ws, L.sel));
+  int32_t* counts = D.thr ? reinterpret_cast<int32_t*>(at(ws, L.counts)) : nullptr;
   hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, s, r);
   if (st != HSMLA_OK) return st;
   r.mark("kv_state");
@@ -213,11 +225,17 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
   r.mark("gate_scores");
   HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b, scores,
                                       D.B, D.gh, D.gw, D.H, D.Bs, s));
-  r.mark("topk");
-  HSMLA_TRY(hsmla::launch_topk(scores, nullptr, sel, D.B, D.T, D.k, s));
+  if (D.thr) {
+    r.mark("threshold");
+    HSMLA_TRY(hsmla::launch_threshold(scores, nullptr, sel, counts, D.B, D.T,
+                                      D.tau, s));
+  } else {
+    r.mark("topk");
+    HSMLA_TRY(hsmla::launch_topk(scores, nullptr, sel, D.B, D.T, D.k, s));
+  }
   r.mark("sparse_softmax");
-  HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, sel, o, D.B, D.gh, D.gw, D.H,
-                                 D.Bs, D.w, D.k, s));
+  HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, sel, counts, o, D.B, D.gh,
+                                 D.gw, D.H, D.Bs, D.w, D.sw, D.sw, s));
   return HSMLA_OK;
 }
 
@@ -265,6 +283,7 @@ hsmla_status hsmla_workspace_views(const hsmla_desc* desc, int32_t op,
   v->ksum = reinterpret_cast<float*>(at(ws, L.ksum));
   v->scores = reinterpret_cast<float*>(at(ws, L.scores));
   v->sel = reinterpret_cast<int32_t*>(at(ws, L.sel));
+  v->counts = D.thr ? reinterpret_cast<int32_t*>(at(ws, L.counts)) : nullptr;
   v->x1 = op == HSMLA_OP_BLOCK ? at(ws, L.x1) : nullptr;
   return HSMLA_OK;
 }
@@ -315,6 +334,7 @@ hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
   Dims D;
   const hsmla_status st = check_desc(desc, &D);
   if (st != HSMLA_OK) return st;
+  if (D.thr) return HSMLA_ERR_ARG;
   if (D.k > 0 && !sel) return HSMLA_ERR_NULL;
   if (!scores_in && (!qkv_hat || !gate_w || !gate_b || !scores_out))
     return HSMLA_ERR_NULL;
@@ -332,19 +352,64 @@ hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
   return hip_status(hsmla::launch_topk(scores_out, nullptr, sel, D.B, D.T, D.k, s));
 }
 
+hsmla_status hsmla_gate_threshold(const hsmla_desc* desc, const void* qkv_hat,
+                                  const float* gate_w, const float* gate_b,
+                                  const float* scores_in, float* scores_out,
+                                  int32_t* sel, int32_t* counts, void* stream) {
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!D.thr) return HSMLA_ERR_ARG;
+  if (!sel || !counts) return HSMLA_ERR_NULL;
+  if (!scores_in && (!qkv_hat || !gate_w || !gate_b || !scores_out))
+    return HSMLA_ERR_NULL;
+  if ((qkv_hat && !aligned(qkv_hat, 16)) || !aligned(sel, 4) ||
+      !aligned(counts, 4) || (scores_in && !aligned(scores_in, 4)) ||
+      (scores_out && !aligned(scores_out, 4)) ||
+      (gate_w && !aligned(gate_w, 4)) || (gate_b && !aligned(gate_b, 4)))
+    return HSMLA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (scores_in)
+    return hip_status(hsmla::launch_threshold(scores_in, scores_out, sel, counts,
+                                              D.B, D.T, D.tau, s));
+  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkv_hat, gate_w, gate_b, scores_out,
+                                      D.B, D.gh, D.gw, D.H, D.Bs, s));
+  return hip_status(hsmla::launch_threshold(scores_out, nullptr, sel, counts,
+                                            D.B, D.T, D.tau, s));
+}
+
 hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
                                   const void* qkv_hat, const int32_t* sel,
                                   void* o, void* stream) {
   Dims D;
   const hsmla_status st = check_desc(desc, &D);
   if (st != HSMLA_OK) return st;
+  if (D.thr) return HSMLA_ERR_ARG;
   if (!qkv || !qkv_hat || !o || (D.k > 0 && !sel)) return HSMLA_ERR_NULL;
   if (!aligned(qkv, 16) || !aligned(qkv_hat, 16) || !aligned(o, 16) ||
       (sel && !aligned(sel, 4)))
     return HSMLA_ERR_ALIGN;
-  return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, o, D.B, D.gh,
-                                         D.gw, D.H, D.Bs, D.w, D.k,
-                                         static_cast<hipStream_t>(stream)));
+  return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, nullptr, o,
+                                         D.B, D.gh, D.gw, D.H, D.Bs, D.w, D.k,
+                                         D.k, static_cast<hipStream_t>(stream)));
+}
+
+hsmla_status hsmla_sparse_softmax_counted(const hsmla_desc* desc,
+                                          const void* qkv, const void* qkv_hat,
+                                          const int32_t* sel,
+                                          const int32_t* counts, void* o,
+                                          void* stream) {
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!D.thr) return HSMLA_ERR_ARG;
+  if (!qkv || !qkv_hat || !o || !sel || !counts) return HSMLA_ERR_NULL;
+  if (!aligned(qkv, 16) || !aligned(qkv_hat, 16) || !aligned(o, 16) ||
+      !aligned(sel, 4) || !aligned(counts, 4))
+    return HSMLA_ERR_ALIGN;
+  return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, counts, o,
+                                         D.B, D.gh, D.gw, D.H, D.Bs, D.w, D.T,
+                                         D.T, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

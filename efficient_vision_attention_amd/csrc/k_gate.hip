@@ -3,10 +3,13 @@
 // Scores (FT 3.2 head-level score and block-level aggregation):
 //   f_t^(h) = mean over the block's tokens of [Q_hat; K_hat; V_hat]^(h)
 //   M_t     = (1/H) sum_h sigmoid(w^(h) . f_t^(h) + b^(h))
-// Selection: the keep largest M_t per image, equal scores to the lower
-// block index, written in ascending block order -- the compacted tile list
-// the refinement kernel runs over (FT 3.6 stage 3).  A fixed count replaces
-// the paper's threshold so the refinement grid size is known on the host.
+// Selection, written in ascending block order -- the compacted tile list the
+// refinement kernel runs over (FT 3.6 stage 3) -- either
+//   top-k:     the keep largest M_t per image, equal scores to the lower block
+//              index (the count is fixed, so the grid size is known on the
+//              host), or
+//   threshold: every block with M_t > tau (FT 3.2 gating equation); the
+//              per-image count goes to device memory.
 #include "common.h"
 #include "kernels.h"
 
@@ -70,6 +73,39 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(
   }
 }
 
+// Workgroup-wide stream compaction (1024 threads, 16 waves): writes every
+// t in [0, n) with keep(t) to out[0 ..) in ascending order and returns the
+// number written (same value in every thread).  The slot of a kept t is the
+// number of kept entries below it: a wave ballot gives the rank inside the
+// wave, a prefix over the 16 wave totals the offset of the wave.
+template <typename Pred>
+__device__ int compact_ascending(Pred keep, int n, int32_t* __restrict__ out) {
+  __shared__ int wave_tot[16];
+  __shared__ int base_all;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x == 0) base_all = 0;
+  __syncthreads();
+  for (int t0 = 0; t0 < n; t0 += blockDim.x) {
+    const int t = t0 + threadIdx.x;
+    const bool k = t < n && keep(t);
+    const uint64_t m = __ballot(k);
+    const int below = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[wave] = __popcll(m);
+    __syncthreads();
+    int off = base_all;
+    for (int w2 = 0; w2 < wave; ++w2) off += wave_tot[w2];
+    if (k) out[off + below] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int tot = 0;
+      for (int w2 = 0; w2 < 16; ++w2) tot += wave_tot[w2];
+      base_all += tot;
+    }
+    __syncthreads();
+  }
+  return base_all;
+}
+
 // grid (batch), 1024 threads.  rank(t) = #{u : s_u > s_t or (s_u == s_t and
 // u < t)}; block t is kept iff rank(t) < keep.  P = 1024 / T threads share
 // one candidate (each scans a strided part of the scores, combined by a
@@ -82,17 +118,13 @@ __global__ __launch_bounds__(1024) void topk_kernel(
   extern __shared__ float sh[];
   float* s = sh;                                        // [nblocks]
   unsigned char* kept = reinterpret_cast<unsigned char*>(sh + nblocks);  // [nblocks]
-  __shared__ int wave_tot[16];
-  __shared__ int base_all;
   const int b = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* src = scores + (size_t)b * nblocks;
   for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
     const float v = src[t];
     s[t] = v;
     if (scores_copy) scores_copy[(size_t)b * nblocks + t] = v;
   }
-  if (threadIdx.x == 0) base_all = 0;
   __syncthreads();
   const int per_pass = blockDim.x / lanes_per;
   const int part = threadIdx.x % lanes_per;
@@ -111,24 +143,25 @@ __global__ __launch_bounds__(1024) void topk_kernel(
     if (t < nblocks && part == 0) kept[t] = rank < keep;
   }
   __syncthreads();
-  for (int t0 = 0; t0 < nblocks; t0 += blockDim.x) {
-    const int t = t0 + threadIdx.x;
-    const bool k = t < nblocks && kept[t];
-    const uint64_t m = __ballot(k);
-    const int below = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tot[wave] = __popcll(m);
-    __syncthreads();
-    int off = base_all;
-    for (int w2 = 0; w2 < wave; ++w2) off += wave_tot[w2];
-    if (k) sel[(size_t)b * keep + off + below] = t;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int tot = 0;
-      for (int w2 = 0; w2 < 16; ++w2) tot += wave_tot[w2];
-      base_all += tot;
-    }
-    __syncthreads();
-  }
+  compact_ascending([&](int t) { return kept[t] != 0; }, nblocks,
+                    sel + (size_t)b * keep);
+}
+
+// grid (batch), 1024 threads: sel[b][0 .. n) = ascending blocks with
+// M_t > tau, counts[b] = n.  Float32 comparison, so a score equal to tau is
+// not routed.
+__global__ __launch_bounds__(1024) void threshold_kernel(
+    const float* __restrict__ scores, float* __restrict__ scores_copy,
+    int32_t* __restrict__ sel, int32_t* __restrict__ counts, int nblocks,
+    float tau) {
+  const int b = blockIdx.x;
+  const float* src = scores + (size_t)b * nblocks;
+  if (scores_copy)
+    for (int t = threadIdx.x; t < nblocks; t += blockDim.x)
+      scores_copy[(size_t)b * nblocks + t] = src[t];
+  const int n = compact_ascending([&](int t) { return src[t] > tau; }, nblocks,
+                                  sel + (size_t)b * nblocks);
+  if (threadIdx.x == 0) counts[b] = n;
 }
 
 }  // namespace
@@ -159,6 +192,14 @@ hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
   while (lanes_per < 64 && lanes_per * 2 * nblocks <= 1024) lanes_per *= 2;
   topk_kernel<<<batch, 1024, lds, s>>>(scores, scores_copy, sel, nblocks, keep,
                                        lanes_per);
+  return hipGetLastError();
+}
+
+hipError_t launch_threshold(const float* scores, float* scores_copy,
+                            int32_t* sel, int32_t* counts, int batch,
+                            int nblocks, float tau, hipStream_t s) {
+  threshold_kernel<<<batch, 1024, 0, s>>>(scores, scores_copy, sel, counts,
+                                          nblocks, tau);
   return hipGetLastError();
 }
 

@@ -51,12 +51,19 @@ hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
                               int heads, int block, hipStream_t s);
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
                        int batch, int nblocks, int keep, hipStream_t s);
+// Threshold routing: sel[b][0 .. counts[b]) = ascending blocks with score >
+// tau; sel rows are nblocks wide.
+hipError_t launch_threshold(const float* scores, float* scores_copy,
+                            int32_t* sel, int32_t* counts, int batch,
+                            int nblocks, float tau, hipStream_t s);
 
-// Windowed softmax refinement of the selected blocks, in place on o.
+// Windowed softmax refinement of the selected blocks, in place on o.  The
+// grid covers `entries` entries of each sel row (row stride `stride`); with
+// counts != nullptr only the first counts[b] of image b are refined.
 hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
-                         const int32_t* sel, void* o, int batch, int gh,
-                         int gw, int heads, int block, int window, int keep,
-                         hipStream_t s);
+                         const int32_t* sel, const int32_t* counts, void* o,
+                         int batch, int gh, int gw, int heads, int block,
+                         int window, int entries, int stride, hipStream_t s);
 
 // y = LN(x) . gamma + beta over the channel dimension.
 hipError_t launch_layernorm(bool bf, const void* x, const float* gamma,

@@ -32,7 +32,8 @@ class DeviceModel:
     """Device weights and descriptor for one shape.
 
     shape: mapping with batch, grid_h, grid_w, channels, heads, branches,
-    block, window, keep_blocks, dtype.  weights: dict of float64 numpy
+    block, window, keep_blocks, dtype, and optionally tau (threshold
+    routing when given).  weights: dict of float64 numpy
     arrays (w_qkv, w_o, dw list, gate_w, gate_b, and for the block ln1_g,
     ln1_b, ln2_g, ln2_b, w1, dw_ffn, w2), dense weights given [in][out]
     (y = x @ W); they are stored on the device transposed, as the library
@@ -82,7 +83,8 @@ class DeviceModel:
         s = self.shape
         B, N, C, Hh = s["batch"], s["grid_h"] * s["grid_w"], s["channels"], s["heads"]
         T = (s["grid_h"] // s["block"]) * (s["grid_w"] // s["block"])
-        k = s["keep_blocks"]
+        thr = s.get("tau") is not None
+        k = T if thr else s["keep_blocks"]
         off = H.hsmla_workspace_views(self.desc, op, ws)
         adt = TORCH_DTYPE[self.dtype]
         esz = torch.tensor([], dtype=adt).element_size()
@@ -100,6 +102,8 @@ class DeviceModel:
             "scores": sl("scores", B * T, torch.float32, 4).view(B, T),
             "sel": sl("sel", B * k, torch.int32, 4).view(B, k),
         }
+        if thr:
+            out["counts"] = sl("counts", B, torch.int32, 4)
         if off.get("x1") is not None:
             out["x1"] = sl("x1", B * N * C, adt, esz).view(B, N, C)
         return out

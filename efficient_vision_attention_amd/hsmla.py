@@ -18,6 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhsmla.s
 
 HSMLA_F32, HSMLA_BF16 = 0, 1
 HSMLA_OP_QKV, HSMLA_OP_LINEAR, HSMLA_OP_FORWARD, HSMLA_OP_BLOCK = 0, 1, 2, 3
+HSMLA_ROUTE_TOPK, HSMLA_ROUTE_THRESHOLD = 0, 1
 
 # Every symbol include/hsmla.h declares.
 EXPORTED = (
@@ -26,7 +27,9 @@ EXPORTED = (
     "hsmla_qkv_branches",
     "hsmla_linear_attn",
     "hsmla_gate_select",
+    "hsmla_gate_threshold",
     "hsmla_sparse_softmax",
+    "hsmla_sparse_softmax_counted",
     "hsmla_forward",
     "hsmla_block_forward",
     "hsmla_forward_timed",
@@ -49,6 +52,7 @@ class hsmla_desc(ctypes.Structure):
         ("n_branches", ctypes.c_int32), ("branch_k", ctypes.c_int32 * 3),
         ("block", ctypes.c_int32), ("window", ctypes.c_int32),
         ("keep_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("routing", ctypes.c_int32), ("tau", ctypes.c_float),
     ]
 
 
@@ -74,7 +78,8 @@ class hsmla_views(ctypes.Structure):
         ("qkv", ctypes.c_void_p), ("qkv_hat", ctypes.c_void_p),
         ("o", ctypes.c_void_p), ("kv", ctypes.c_void_p),
         ("ksum", ctypes.c_void_p), ("scores", ctypes.c_void_p),
-        ("sel", ctypes.c_void_p), ("x1", ctypes.c_void_p),
+        ("sel", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+        ("x1", ctypes.c_void_p),
     ]
 
 
@@ -99,7 +104,9 @@ def library():
             "hsmla_qkv_branches": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, VP, SZ, VP],
             "hsmla_linear_attn": [P(hsmla_desc), VP, VP, VP, VP, VP, SZ, VP],
             "hsmla_gate_select": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP],
+            "hsmla_gate_threshold": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP],
             "hsmla_sparse_softmax": [P(hsmla_desc), VP, VP, VP, VP, VP],
+            "hsmla_sparse_softmax_counted": [P(hsmla_desc), VP, VP, VP, VP, VP, VP],
             "hsmla_forward": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, SZ, VP],
             "hsmla_block_forward": [P(hsmla_desc), P(hsmla_weights), P(hsmla_ffn_weights),
                                     VP, VP, VP, SZ, VP],
@@ -140,7 +147,9 @@ def _stream():
 
 
 def make_desc(*, batch, grid_h, grid_w, channels, heads, branches, block,
-              window, keep_blocks, dtype, head_dim=32):
+              window, keep_blocks, dtype, head_dim=32, tau=None):
+    """tau=None: top-k routing (keep_blocks per image); a number: threshold
+    routing (every block with score > tau)."""
     d = hsmla_desc()
     d.batch, d.grid_h, d.grid_w = batch, grid_h, grid_w
     d.channels, d.heads, d.head_dim = channels, heads, head_dim
@@ -149,6 +158,8 @@ def make_desc(*, batch, grid_h, grid_w, channels, heads, branches, block,
         d.branch_k[i] = k
     d.block, d.window, d.keep_blocks = block, window, keep_blocks
     d.dtype = {"f32": HSMLA_F32, "bf16": HSMLA_BF16}.get(dtype, dtype)
+    d.routing = HSMLA_ROUTE_TOPK if tau is None else HSMLA_ROUTE_THRESHOLD
+    d.tau = 0.0 if tau is None else float(tau)
     return d
 
 
@@ -205,6 +216,22 @@ def hsmla_gate_select(desc, qkv_hat, gate_w, gate_b, scores_in, scores_out, sel)
                                        _ptr(gate_w), _ptr(gate_b), _ptr(scores_in),
                                        _ptr(scores_out), _ptr(sel), _stream()),
            "hsmla_gate_select")
+
+
+def hsmla_gate_threshold(desc, qkv_hat, gate_w, gate_b, scores_in, scores_out,
+                         sel, counts):
+    _check(library().hsmla_gate_threshold(ctypes.byref(desc), _ptr(qkv_hat),
+                                          _ptr(gate_w), _ptr(gate_b),
+                                          _ptr(scores_in), _ptr(scores_out),
+                                          _ptr(sel), _ptr(counts), _stream()),
+           "hsmla_gate_threshold")
+
+
+def hsmla_sparse_softmax_counted(desc, qkv, qkv_hat, sel, counts, o):
+    _check(library().hsmla_sparse_softmax_counted(ctypes.byref(desc), _ptr(qkv),
+                                                  _ptr(qkv_hat), _ptr(sel),
+                                                  _ptr(counts), _ptr(o), _stream()),
+           "hsmla_sparse_softmax_counted")
 
 
 def hsmla_sparse_softmax(desc, qkv, qkv_hat, sel, o):

@@ -14,7 +14,8 @@
  *   Z, D    = sum_j relu(K_hat_j)^T V_hat_j, sum_j relu(K_hat_j)   (per head)
  *   O_lin   = relu(Q_hat) Z / (relu(Q_hat) . D)           (0 when the sum is 0)
  *   M_t     = mean_h sigmoid(w_h . meanpool_t[Q_hat;K_hat;V_hat]_h + b_h)
- *   sel     = the keep_blocks blocks with the largest M_t (ties -> lower t)
+ *   sel     = the keep_blocks blocks with the largest M_t (ties -> lower t),
+ *             or, with threshold routing, every block with M_t > tau
  *   O_i     = O_lin_i + softmax-attn(q_i, K_W, V_W) - lin-local_i  on sel
  *   Y       = O W_o^T
  *
@@ -46,7 +47,10 @@
  *   - Limits: head_dim must be 32; block <= 16; window >= block with
  *     (window - block) even; grid_h and grid_w multiples of block;
  *     0 <= keep_blocks <= number of blocks <= 8192; channels <= 2048;
- *     up to 3 depthwise branches of odd size <= 7.
+ *     up to 3 depthwise branches of odd size <= 7; routing is
+ *     HSMLA_ROUTE_TOPK or HSMLA_ROUTE_THRESHOLD (otherwise HSMLA_ERR_ARG),
+ *     and tau is not NaN under threshold routing (keep_blocks is then
+ *     unused but still range-checked).
  */
 #ifndef HSMLA_H_
 #define HSMLA_H_
@@ -71,6 +75,12 @@ typedef enum {
 
 typedef enum { HSMLA_F32 = 0, HSMLA_BF16 = 1 } hsmla_dtype;
 
+/* How blocks are routed to the softmax path (FT 3.2).  TOPK keeps the
+ * keep_blocks highest scores per image; THRESHOLD keeps every block whose
+ * score exceeds desc->tau (the routed set {b : M_b > tau}), a per-image count
+ * known only on the device. */
+typedef enum { HSMLA_ROUTE_TOPK = 0, HSMLA_ROUTE_THRESHOLD = 1 } hsmla_routing;
+
 /* Which entry point a workspace is sized for. */
 typedef enum {
   HSMLA_OP_QKV = 0,     /* hsmla_qkv_branches   */
@@ -86,8 +96,10 @@ typedef struct {
   int32_t branch_k[3];           /* their (odd) kernel sizes              */
   int32_t block;                 /* block side Bs                          */
   int32_t window;                /* softmax window side w                  */
-  int32_t keep_blocks;           /* refined blocks per image, 0..T         */
+  int32_t keep_blocks;           /* refined blocks per image, 0..T (TOPK)  */
   int32_t dtype;                 /* hsmla_dtype                            */
+  int32_t routing;               /* hsmla_routing                          */
+  float tau;                     /* threshold of HSMLA_ROUTE_THRESHOLD     */
 } hsmla_desc;
 
 typedef struct {
@@ -114,7 +126,8 @@ typedef struct {
   float* kv;      /* [B][H][d][d] Z                                     */
   float* ksum;    /* [B][H][d]   D                                      */
   float* scores;  /* [B][T] gate scores M                               */
-  int32_t* sel;   /* [B][keep_blocks] selected blocks, ascending        */
+  int32_t* sel;   /* [B][keep_blocks] (TOPK) or [B][T] (THRESHOLD)      */
+  int32_t* counts; /* THRESHOLD: [B] routed blocks per image; else NULL   */
   void* x1;       /* block only: [B][N][C] X + HSMLA(LN1(X))            */
 } hsmla_views;
 
@@ -154,11 +167,26 @@ hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
  * ranked instead (qkv_hat, gate_w, gate_b may be NULL) and copied to
  * scores_out if it is not NULL.  sel [B][keep_blocks] receives, per image,
  * the indices of the keep_blocks largest scores (equal scores: lower index
- * first), in ascending order.  Scores must not be NaN. */
+ * first), in ascending order.  Scores must not be NaN.  desc->routing must be
+ * HSMLA_ROUTE_TOPK (HSMLA_ERR_ARG otherwise). */
 hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
                                const float* gate_w, const float* gate_b,
                                const float* scores_in, float* scores_out,
                                int32_t* sel, void* stream);
+
+/* Step 4 with threshold routing (FT 3.2, the routed set B_tau of the
+ * activation-ratio equation; FT 3.3 routing case G > tau; EX section 2
+ * "Routing").  Scores as in hsmla_gate_select; desc->routing must be
+ * HSMLA_ROUTE_THRESHOLD (HSMLA_ERR_ARG otherwise).  sel[b][0 .. counts[b])
+ * receives, in ascending order, every block of image b whose float32 score
+ * is strictly greater than desc->tau; entries of sel beyond counts[b] are
+ * left as they were.  sel [B][T] int32 (T = number of blocks), counts [B]
+ * int32, both device memory written by the kernel: the count is not known
+ * on the host. */
+hsmla_status hsmla_gate_threshold(const hsmla_desc* desc, const void* qkv_hat,
+                                  const float* gate_w, const float* gate_b,
+                                  const float* scores_in, float* scores_out,
+                                  int32_t* sel, int32_t* counts, void* stream);
 
 /* Step 5, local softmax refinement of the selected blocks with the two-path
  * residual (FT 3.3 local-neighbourhood, lin-local and residual equations;
@@ -168,14 +196,29 @@ hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
  * over the window x window keys centred on the block and clipped to the
  * grid, with raw q, k, v from qkv and lin-local from qkv_hat.  o holds O_lin
  * on entry; tokens of unselected blocks are not touched.  sel entries must
- * be distinct valid block indices. */
+ * be distinct valid block indices.  desc->routing must be HSMLA_ROUTE_TOPK
+ * (HSMLA_ERR_ARG otherwise; see hsmla_sparse_softmax_counted). */
 hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
                                   const void* qkv_hat, const int32_t* sel,
                                   void* o, void* stream);
 
+/* Step 5 over a device-counted selection (the threshold-routed set, FT 3.3
+ * sparse residual over |B_tau| blocks): as hsmla_sparse_softmax, for the
+ * first counts[b] entries of sel[b][0 .. T) (T = number of blocks), which
+ * hsmla_gate_threshold writes.  desc->routing must be HSMLA_ROUTE_THRESHOLD
+ * (HSMLA_ERR_ARG otherwise).  The launch covers T entries per image; work
+ * items at or beyond counts[b] exit before reading sel. */
+hsmla_status hsmla_sparse_softmax_counted(const hsmla_desc* desc,
+                                          const void* qkv, const void* qkv_hat,
+                                          const int32_t* sel,
+                                          const int32_t* counts, void* o,
+                                          void* stream);
+
 /* The whole module: y = HSMLA(x) = O W_o^T, steps 1-5 then the output
  * projection (FT 3.6 stages 1-5).  x, y [B][N][C]; ws sized for
- * HSMLA_OP_FORWARD; intermediates readable through hsmla_workspace_views. */
+ * HSMLA_OP_FORWARD; intermediates readable through hsmla_workspace_views.
+ * desc->routing picks top-k or threshold selection (then the workspace
+ * also holds the per-image counts, and sel rows are T wide). */
 hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
                            const void* x, void* y, void* ws, size_t ws_bytes,
                            void* stream);

@@ -23,12 +23,12 @@ def announce(msg: str):
     sys.stdout.flush()
 
 
-def shape_of(wl: Workload, keep_blocks=None) -> dict:
+def shape_of(wl: Workload, keep_blocks=None, tau=None) -> dict:
     return dict(batch=wl.batch, grid_h=wl.grid_h, grid_w=wl.grid_w,
                 channels=wl.channels, heads=wl.heads, branches=wl.branches,
                 block=wl.block, window=wl.window,
                 keep_blocks=wl.keep_blocks if keep_blocks is None else keep_blocks,
-                dtype=wl.dtype)
+                dtype=wl.dtype, tau=tau)
 
 
 def assert_close(gpu, ref, dtype, what=""):
@@ -82,15 +82,54 @@ def selection_band_check(scores_ref, scores_gpu, sel_ref, sel_gpu, k):
     return report
 
 
-class Run:
-    """Device model + buffers for one workload, with numpy readback."""
+def routed_lists(sel, counts):
+    """Per-image selections of a threshold run: sel[b][:counts[b]]."""
+    return [np.asarray(sel[b][:int(counts[b])]) for b in range(len(counts))]
 
-    def __init__(self, wl: Workload, inputs: dict, keep_blocks=None):
+
+def padded(lists, width):
+    """Per-image index lists -> [B, width] array padded with -1 (the form the
+    oracle takes as an injected selection)."""
+    out = np.full((len(lists), width), -1, dtype=np.int64)
+    for b, l in enumerate(lists):
+        out[b, :len(l)] = l
+    return out
+
+
+def threshold_band_check(scores_ref, scores_gpu, tau, ref_lists, gpu_lists):
+    """Accept a differing threshold selection only for blocks whose score is
+    within 2 max|dM| of tau.  Returns a list of (image, max_dM, n_diff)."""
+    report = []
+    for b in range(len(ref_lists)):
+        dm = float(np.max(np.abs(scores_ref[b] - scores_gpu[b])))
+        diff = set(ref_lists[b].tolist()) ^ set(gpu_lists[b].tolist())
+        for t in diff:
+            assert abs(scores_ref[b][t] - tau) <= 2 * dm + 1e-12, (
+                f"image {b}: block {t} routed differently outside the tie band "
+                f"(|M-tau|={abs(scores_ref[b][t] - tau):.3e}, max dM={dm:.3e})")
+        report.append((b, dm, len(diff)))
+    return report
+
+
+def tau_between(scores, quantile):
+    """A float32 threshold halfway between two adjacent distinct float32
+    scores near the given quantile of all scores (so no score equals it)."""
+    v = np.unique(np.asarray(scores, np.float32).ravel())
+    i = min(max(int(quantile * (v.size - 1)), 0), v.size - 2)
+    return float(np.float32((np.float64(v[i]) + np.float64(v[i + 1])) / 2))
+
+
+class Run:
+    """Device model + buffers for one workload, with numpy readback.  With
+    tau set, the model routes by threshold and the readback holds counts."""
+
+    def __init__(self, wl: Workload, inputs: dict, keep_blocks=None, tau=None):
         self.wl = wl
         self.inputs = inputs
-        self.model = DeviceModel(shape_of(wl, keep_blocks), inputs)
+        self.model = DeviceModel(shape_of(wl, keep_blocks, tau), inputs)
         self.desc = self.model.desc
-        self.k = self.model.shape["keep_blocks"]
+        self.tau = tau
+        self.k = self.model.shape["keep_blocks"] if tau is None else f"tau={tau:.6g}"
         self.x = to_device(inputs["x"], wl.dtype)
 
     def forward(self):

@@ -92,6 +92,21 @@ def test_desc_validation(change, status):
     assert st == status
 
 
+def test_routing_validation():
+    d = _desc()
+    d.routing = 2
+    assert _ws_bytes(d, H.HSMLA_OP_FORWARD)[0] == -7
+    assert _ws_bytes(_desc(tau=float("nan")), H.HSMLA_OP_FORWARD)[0] == -7
+    # tau is not looked at under top-k routing
+    d = _desc()
+    d.tau = float("nan")
+    assert _ws_bytes(d, H.HSMLA_OP_FORWARD)[0] == 0
+    # threshold: sel rows are T wide and the counts follow them
+    st_k, n_k = _ws_bytes(_desc(keep_blocks=4), H.HSMLA_OP_FORWARD)
+    st_t, n_t = _ws_bytes(_desc(tau=0.5), H.HSMLA_OP_FORWARD)
+    assert st_k == 0 and st_t == 0 and n_t > n_k
+
+
 def test_workspace_bytes_and_bad_op():
     d = _desc()
     st, n = _ws_bytes(d, H.HSMLA_OP_FORWARD)
@@ -155,6 +170,24 @@ def test_stage_argument_errors():
     st, need_q = _ws_bytes(d, H.HSMLA_OP_QKV)
     assert lib.hsmla_qkv_branches(ctypes.byref(d), ctypes.byref(_weights()), FAKE,
                                   FAKE, FAKE, FAKE, need_q - 1, None) == -5
+    # routing must match the entry point
+    dt = _desc(tau=0.5)
+    assert lib.hsmla_gate_select(ctypes.byref(dt), FAKE, FAKE, FAKE, None, FAKE,
+                                 FAKE, None) == -7
+    assert lib.hsmla_sparse_softmax(ctypes.byref(dt), FAKE, FAKE, FAKE, FAKE,
+                                    None) == -7
+    assert lib.hsmla_gate_threshold(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE,
+                                    FAKE, FAKE, None) == -7
+    assert lib.hsmla_sparse_softmax_counted(ctypes.byref(d), FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, None) == -7
+    assert lib.hsmla_gate_threshold(ctypes.byref(dt), FAKE, FAKE, FAKE, None, FAKE,
+                                    FAKE, None, None) == -1
+    assert lib.hsmla_gate_threshold(ctypes.byref(dt), FAKE, FAKE, FAKE, None, FAKE,
+                                    FAKE + 2, FAKE, None) == -4
+    assert lib.hsmla_sparse_softmax_counted(ctypes.byref(dt), FAKE, FAKE, FAKE,
+                                            None, FAKE, None) == -1
+    assert lib.hsmla_sparse_softmax_counted(ctypes.byref(dt), FAKE, FAKE, FAKE + 2,
+                                            FAKE, FAKE, None) == -4
     ffn = H.hsmla_ffn_weights()
     st, need_b = _ws_bytes(d, H.HSMLA_OP_BLOCK)
     assert lib.hsmla_block_forward(ctypes.byref(d), ctypes.byref(_weights()),
@@ -173,4 +206,11 @@ def test_workspace_views_layout():
                                            "scores", "sel")]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs) and offs[-1] < need
-    assert v.x1 is None
+    assert v.x1 is None and v.counts is None
+    dt = _desc(tau=0.5)
+    st, need_t = _ws_bytes(dt, H.HSMLA_OP_FORWARD)
+    assert H.library().hsmla_workspace_views(ctypes.byref(dt), H.HSMLA_OP_FORWARD,
+                                             base, ctypes.byref(v)) == 0
+    T = (16 // 4) * (32 // 4)
+    assert v.counts - v.sel >= 2 * T * 4 and (v.counts - base) % 256 == 0
+    assert v.counts - base < need_t

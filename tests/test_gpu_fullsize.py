@@ -14,7 +14,8 @@ import pytest
 import oracle as O
 from workloads import WORKLOADS, make_inputs, scaled
 
-from gpu_harness import Run, assert_close, selection_band_check
+from gpu_harness import (Run, assert_close, routed_lists, selection_band_check,
+                         threshold_band_check)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +44,7 @@ def _sampled_branches(qkv, kernels, gh, gw, b, tokens):
     return out[:, r * side + r]
 
 
-def _check_module_fullsize(wl, inp, g):
+def _check_module_fullsize(wl, inp, g, tau=None):
     B, N, C = wl.batch, wl.tokens, wl.channels
     rnd = O.round_bf16
     x = inp["x"]
@@ -66,27 +67,41 @@ def _check_module_fullsize(wl, inp, g):
     scores = O.gate_scores(g["qkv_hat"], inp["gate_w"], inp["gate_b"], wl.grid_h,
                            wl.grid_w, wl.block, wl.heads)
     np.testing.assert_allclose(g["scores"], scores, rtol=0, atol=2e-6)
-    k = wl.keep_blocks
-    sel_g = g["sel"][:, :k]
-    np.testing.assert_array_equal(sel_g, O.select_blocks(g["scores"].astype(np.float32), k))
-    sel_ref = O.select_blocks(scores.astype(np.float32), k)
-    if not np.array_equal(sel_g, sel_ref):
-        selection_band_check(scores, g["scores"], sel_ref, sel_g, k)
+    if tau is None:
+        k = wl.keep_blocks
+        sel_g = g["sel"][:, :k]
+        np.testing.assert_array_equal(
+            sel_g, O.select_blocks(g["scores"].astype(np.float32), k))
+        sel_ref = O.select_blocks(scores.astype(np.float32), k)
+        if not np.array_equal(sel_g, sel_ref):
+            selection_band_check(scores, g["scores"], sel_ref, sel_g, k)
+        lists = list(sel_g)
+    else:
+        lists = routed_lists(g["sel"], g["counts"])
+        own_sel, own_cnt = O.select_threshold(g["scores"].astype(np.float32),
+                                              np.float32(tau))
+        np.testing.assert_array_equal(g["counts"], own_cnt)
+        for b in range(B):
+            np.testing.assert_array_equal(lists[b], own_sel[b, :own_cnt[b]])
+        ref_sel, ref_cnt = O.select_threshold(scores.astype(np.float32),
+                                              np.float32(tau))
+        threshold_band_check(scores, g["scores"], tau,
+                             routed_lists(ref_sel, ref_cnt), lists)
     # S3b on sampled unselected tokens
     nbc = wl.grid_w // wl.block
     ys, xs = np.divmod(np.arange(N), wl.grid_w)
     tblk = (ys // wl.block) * nbc + xs // wl.block
     for b in range(B):
-        unsel = np.nonzero(~np.isin(tblk, sel_g[b]))[0]
+        unsel = np.nonzero(~np.isin(tblk, lists[b]))[0]
         toks = np.sort(RNG.choice(unsel, size=min(256, unsel.size), replace=False))
         ref = rnd(O.linear_readout(g["qkv_hat"][b:b + 1, toks, :C], Z[b:b + 1],
                                    D[b:b + 1], wl.heads))[0]
         assert_close(g["o"][b, toks], ref, "bf16", f"o_lin image {b}")
     # S5 on sampled selected blocks (GPU qkv, qkv_hat in; O_lin recomputed)
     for b in range(B):
-        if k == 0:
-            break
-        pick = np.sort(RNG.choice(sel_g[b], size=min(6, k), replace=False))
+        if len(lists[b]) == 0:
+            continue
+        pick = np.sort(RNG.choice(lists[b], size=min(6, len(lists[b])), replace=False))
         toks = np.nonzero(np.isin(tblk, pick))[0]
         o_lin = np.zeros((1, N, C))
         o_lin[0, toks] = rnd(O.linear_readout(g["qkv_hat"][b:b + 1, toks, :C],
