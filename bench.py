@@ -10,7 +10,8 @@ batch, i.e. every kernel of the path.  Inputs are seeded synthetic data
 
 Prints one JSON line: tokens/s, the per-kernel breakdown from HIP events
 recorded between the launches of the step, the roofline of the dominant
-kernel, a keep-ratio sweep, and the CPU oracle timed on a bounded crop.
+kernel, a keep-ratio sweep with two threshold-routing points, and the CPU
+oracle timed on a bounded crop.
 
     python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
 """
@@ -245,11 +246,11 @@ def main():
     inp = make_inputs(base)
     x = to_device(inp["x"], base.dtype)
 
-    def shape(wl):
+    def shape(wl, tau=None):
         return dict(batch=wl.batch, grid_h=wl.grid_h, grid_w=wl.grid_w,
                     channels=wl.channels, heads=wl.heads, branches=wl.branches,
                     block=wl.block, window=wl.window, keep_blocks=wl.keep_blocks,
-                    dtype=wl.dtype)
+                    dtype=wl.dtype, tau=tau)
 
     def time_steps(model, fn, steps, warmup):
         ws = model.workspace(H.HSMLA_OP_BLOCK)
@@ -275,7 +276,9 @@ def main():
     model = DeviceModel(shape(base), inp)
     ms, ws = time_steps(model, block_step, args.steps, args.warmup)
     tokens = base.batch * base.tokens
-    sel = model.views(H.HSMLA_OP_BLOCK, ws)["sel"].cpu().numpy()
+    base_views = model.views(H.HSMLA_OP_BLOCK, ws)
+    sel = base_views["sel"].cpu().numpy()
+    base_scores = base_views["scores"].cpu().numpy()
 
     # per-kernel durations from events recorded between the launches
     hev = HipEvents()
@@ -314,6 +317,23 @@ def main():
             ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 3)
             ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
             sweep.append(dict(keep=r, keep_blocks=keep_blocks_for(r, wl.num_blocks),
+                              block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
+                              block_ms=round(ms_b, 4),
+                              module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
+                              module_ms=round(ms_m, 4)))
+            del m
+        # threshold routing (blocks with score > tau), tau placed between two
+        # adjacent scores of the run above at the given quantile
+        uniq = np.unique(base_scores.astype(np.float32))
+        for q in (0.9, 0.7):
+            i = min(int(q * (uniq.size - 1)), uniq.size - 2)
+            tau = float(np.float32((np.float64(uniq[i]) + np.float64(uniq[i + 1])) / 2))
+            m = DeviceModel(shape(base, tau=tau), inp)
+            ms_b, ws_t = time_steps(m, block_step, max(10, args.steps // 2), 3)
+            routed = int(m.views(H.HSMLA_OP_BLOCK, ws_t)["counts"].sum().item())
+            ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
+            sweep.append(dict(routing="threshold", tau=tau,
+                              routed_fraction=round(routed / (base.batch * base.num_blocks), 4),
                               block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
                               block_ms=round(ms_b, 4),
                               module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),

@@ -239,8 +239,8 @@ def block_features(qkv_hat, grid_h, grid_w, block, heads):
 
     Returns [B, T, H, 3d] with the q features first, then k, then v.
     FT 3.2 (head-level score equation, the AvgPool of the block's hatted
-    tokens).  The extra depthwise 3x3 inside that equation is not applied:
-    the gate used here is a linear logit on mean-pooled block features.
+    tokens).  The depthwise 3x3 inside that equation, when used, is applied
+    by gate_scores before this pooling.
     """
     x = np.asarray(qkv_hat, np.float64)
     B, N, C3 = x.shape
@@ -252,18 +252,30 @@ def block_features(qkv_hat, grid_h, grid_w, block, heads):
     return f.reshape(B, nbr * nbc, heads, 3 * d)
 
 
-def gate_scores(qkv_hat, gate_w, gate_b, grid_h, grid_w, block, heads):
+def gate_scores(qkv_hat, gate_w, gate_b, grid_h, grid_w, block, heads,
+                gate_dw=None):
     """M_t = (1/H) sum_h sigmoid(w^(h) . f_t^(h) + b^(h)), shared by all heads.
 
     FT 3.2: head-level scores G_b^(h) and their mean M_b in [0, 1] (only the
     first equality of the block-level aggregation equation is used; its
     second equality is not consistent with the first).  EX section 2 says
     the aggregated gate is shared.  gate_w: [H, 3d], gate_b: [H].
+
+    gate_dw: None, or [3C, 3, 3] depthwise weights.  When given, the head
+    score follows FT 3.2's equation in full: f_t^(h) is the block average of
+    DWConv3x3([Q_hat; K_hat; V_hat]), the convolution taken over the whole
+    token grid with zero padding at the image border (the reading of
+    "DWConv of the block's tokens" in which neighbouring blocks supply the
+    halo, as for every other convolution of the module), no bias.  When
+    None, the block average of the hatted tokens themselves.
     Returns M: [B, T] float64.
-    Parity unpinned by the pages for the exact gate form (their score applies
-    an extra depthwise conv); pinned here by hand-worked fixtures and by the
-    w = 0 case (every score equals the mean of sigmoid(b)).
+    Pinned by hand-worked fixtures, the w = 0 case (every score equals the
+    mean of sigmoid(b)), a delta gate kernel (equal to no kernel), loops
+    over the definition on tiny inputs, and a constant field with a ones
+    kernel (closed form at border and interior blocks).
     """
+    if gate_dw is not None:
+        qkv_hat = dwconv_same(qkv_hat, gate_dw, grid_h, grid_w)
     f = block_features(qkv_hat, grid_h, grid_w, block, heads)
     w = np.asarray(gate_w, np.float64)
     b = np.asarray(gate_b, np.float64)
@@ -428,7 +440,8 @@ def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
     o_lin_raw, Z, D = linear_attention(qkv_hat, heads)
     o_lin = rnd(o_lin_raw)
     scores = gate_scores(qkv_hat, weights["gate_w"], weights["gate_b"],
-                         grid_h, grid_w, block, heads)
+                         grid_h, grid_w, block, heads,
+                         gate_dw=weights.get("gate_dw"))
     counts = None
     rank_on = scores.astype(np.float32) if scores_f32 else scores
     if sel is None and tau is not None:

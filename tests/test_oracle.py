@@ -235,6 +235,70 @@ def _is_valid_topk(scores, subset):
     return True
 
 
+def test_gate_delta_kernel_equals_plain_gate():
+    rng = _rng(11)
+    H, d, gh, gw, Bs = 2, 4, 8, 12, 4
+    qkvh = rng.normal(size=(2, gh * gw, 3 * H * d))
+    w, b = rng.normal(size=(H, 3 * d)), rng.normal(size=H)
+    delta = np.zeros((3 * H * d, 3, 3))
+    delta[:, 1, 1] = 1.0
+    np.testing.assert_allclose(
+        O.gate_scores(qkvh, w, b, gh, gw, Bs, H, gate_dw=delta),
+        O.gate_scores(qkvh, w, b, gh, gw, Bs, H), rtol=1e-14, atol=1e-15)
+
+
+def test_gate_conv_matches_loops_over_the_definition():
+    """G_b^(h) = sigmoid(w . AvgPool_b(DWConv3x3(x)) + b), written as plain
+    loops: each token of the block, each tap, zero outside the grid."""
+    rng = _rng(12)
+    H, d, gh, gw, Bs = 2, 2, 6, 4, 2
+    C3 = 3 * H * d
+    qkvh = rng.normal(size=(1, gh * gw, C3))
+    gdw = rng.normal(size=(C3, 3, 3))
+    w, b = rng.normal(size=(H, 3 * d)), rng.normal(size=H)
+    got = O.gate_scores(qkvh, w, b, gh, gw, Bs, H, gate_dw=gdw)
+    nbc = gw // Bs
+    for t in range(got.shape[1]):
+        r0, c0 = (t // nbc) * Bs, (t % nbc) * Bs
+        gs = []
+        for h in range(H):
+            feats = []
+            for part in range(3):  # q, k, v
+                for j in range(d):
+                    ch = part * H * d + h * d + j
+                    acc = 0.0
+                    for y in range(r0, r0 + Bs):
+                        for x in range(c0, c0 + Bs):
+                            for dy in range(3):
+                                for dx in range(3):
+                                    yy, xx = y + dy - 1, x + dx - 1
+                                    if 0 <= yy < gh and 0 <= xx < gw:
+                                        acc += gdw[ch, dy, dx] * qkvh[0, yy * gw + xx, ch]
+                    feats.append(acc / (Bs * Bs))
+            z = sum(w[h][i] * feats[i] for i in range(3 * d)) + b[h]
+            gs.append(1.0 / (1.0 + math.exp(-z)))
+        assert abs(got[0, t] - sum(gs) / H) < 1e-12
+
+
+def test_gate_conv_constant_field_closed_form():
+    """All-ones input and kernel on a 4 x 4 grid, 2 x 2 blocks: a token sees
+    as many in-grid neighbours (itself included) as its 3x3 window holds, so
+    every block averages 4, 6, 6 and 9 -> 25 / 4 (each block touches two
+    borders).  On 6 x 6 the centre block's tokens see 9 each, and the
+    top-middle block's border row 6 each, its inner row 9 each."""
+    H, d = 1, 1
+    w = np.array([[1.0, 0.0, 0.0]])  # logit = the q feature
+    ones = np.ones((3, 3, 3))
+    m4 = O.gate_scores(np.ones((1, 16, 3)), w, np.zeros(1), 4, 4, 2, H, gate_dw=ones)
+    np.testing.assert_allclose(m4, 1.0 / (1.0 + np.exp(-6.25)), rtol=1e-14)
+    m6 = O.gate_scores(np.ones((1, 36, 3)), w, np.zeros(1), 6, 6, 2, H, gate_dw=ones)
+    # centre block (t = 4): 9 per token; corner block: 25/4 as on 4 x 4
+    assert abs(m6[0, 4] - 1.0 / (1.0 + math.exp(-9.0))) < 1e-14
+    edge = (6 + 6 + 9 + 9) / 4  # top-middle block: border row 6 each, inner row 9 each
+    assert abs(m6[0, 1] - 1.0 / (1.0 + math.exp(-edge))) < 1e-14
+    assert abs(m6[0, 0] - 1.0 / (1.0 + math.exp(-6.25))) < 1e-14
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_select_blocks_exhaustive(seed):
     rng = _rng(100 + seed)

@@ -44,6 +44,7 @@ class Workload:
     keep: float  # fraction of blocks refined per image
     field: str  # "gauss" | "street" | "ct" | "pathology"
     full_block: bool = False  # LN/FFN sandwich around the module
+    gate_conv: bool = False  # depthwise 3x3 inside the gate's head score
     seed: int = 0
     keep_override: int | None = None  # explicit block count (edge cases)
 
@@ -196,7 +197,9 @@ def make_inputs(wl: Workload, seed: int | None = None):
       dw: list of [3C, k, k] ~ N(0, 1/k^2), gate_w [H, 3d] ~ N(0, 1/(3d)),
       gate_b [H] = 0, and for the full block ln1_g/ln2_g = 1, ln1_b/ln2_b =
       0, w1 [C, 4C] ~ N(0, 1/C), dw_ffn [4C, 3, 3] ~ N(0, 1/9),
-      w2 [4C, C] ~ N(0, 1/(4C)).
+      w2 [4C, C] ~ N(0, 1/(4C)); with gate_conv, gate_dw [3C, 3, 3] ~
+      N(0, 1/9), drawn from its own generator (seeded by [seed, 1]) so the
+      other inputs do not change.
     """
     rng = np.random.default_rng(wl.seed if seed is None else seed)
     B, gh, gw, C, H = wl.batch, wl.grid_h, wl.grid_w, wl.channels, wl.heads
@@ -218,4 +221,7 @@ def make_inputs(wl: Workload, seed: int | None = None):
         out.update(ln1_g=np.ones(C), ln1_b=np.zeros(C), ln2_g=np.ones(C),
                    ln2_b=np.zeros(C), w1=_to_dtype(w1, dt),
                    dw_ffn=_to_dtype(dw_ffn, dt), w2=_to_dtype(w2, dt))
+    if wl.gate_conv:
+        grng = np.random.default_rng([wl.seed if seed is None else seed, 1])
+        out["gate_dw"] = _to_dtype(grng.normal(0.0, 1.0 / 3.0, size=(3 * C, 3, 3)), dt)
     return out
