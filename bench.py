@@ -10,8 +10,9 @@ batch, i.e. every kernel of the path.  Inputs are seeded synthetic data
 
 Prints one JSON line: tokens/s, the per-kernel breakdown from HIP events
 recorded between the launches of the step, the roofline of the dominant
-kernel, a keep-ratio sweep with two threshold-routing points, and the CPU
-oracle timed on a bounded crop.
+kernel, a keep-ratio sweep with two threshold-routing points and the
+exact-gate / three-branch variant, and the CPU oracle timed on a bounded
+crop.
 
     python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
 """
@@ -339,6 +340,20 @@ def main():
                               module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
                               module_ms=round(ms_m, 4)))
             del m
+
+        # the gate's depthwise 3x3 (FT 3.2 head-level score) with the
+        # identity + 3x3 + 5x5 + 7x7 branches, top-k at the base keep ratio
+        wl = scaled(base, branches=(3, 5, 7), gate_conv=True)
+        m = DeviceModel(shape(wl), make_inputs(wl))
+        ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 3)
+        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
+        sweep.append(dict(variant="gate_dwconv3x3+branches_3_5_7", keep=base.keep,
+                          keep_blocks=base.keep_blocks,
+                          block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
+                          block_ms=round(ms_b, 4),
+                          module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
+                          module_ms=round(ms_m, 4)))
+        del m
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(base, args.cpu_rows)
 

@@ -183,6 +183,7 @@ hsmla_status check_weights(const hsmla_desc* d, const hsmla_weights* w) {
   for (int i = 0; i < d->n_branches; ++i)
     if (!aligned(w->dw[i], 4)) return HSMLA_ERR_ALIGN;
   if (!aligned(w->gate_w, 4) || !aligned(w->gate_b, 4)) return HSMLA_ERR_ALIGN;
+  if (w->gate_dw && !aligned(w->gate_dw, 16)) return HSMLA_ERR_ALIGN;
   return HSMLA_OK;
 }
 
@@ -223,8 +224,9 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
   r.mark("lin_apply");
   HSMLA_TRY(hsmla::launch_lin_apply(D.bf, qkvh, kv, ksum, o, D.B, D.N, D.H, s));
   r.mark("gate_scores");
-  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b, scores,
-                                      D.B, D.gh, D.gw, D.H, D.Bs, s));
+  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b,
+                                      w->gate_dw, scores, D.B, D.gh, D.gw, D.H,
+                                      D.Bs, s));
   if (D.thr) {
     r.mark("threshold");
     HSMLA_TRY(hsmla::launch_threshold(scores, nullptr, sel, counts, D.B, D.T,
@@ -329,8 +331,8 @@ hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
 
 hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
                                const float* gate_w, const float* gate_b,
-                               const float* scores_in, float* scores_out,
-                               int32_t* sel, void* stream) {
+                               const void* gate_dw, const float* scores_in,
+                               float* scores_out, int32_t* sel, void* stream) {
   Dims D;
   const hsmla_status st = check_desc(desc, &D);
   if (st != HSMLA_OK) return st;
@@ -341,21 +343,23 @@ hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
   if ((qkv_hat && !aligned(qkv_hat, 16)) || (sel && !aligned(sel, 4)) ||
       (scores_in && !aligned(scores_in, 4)) ||
       (scores_out && !aligned(scores_out, 4)) ||
-      (gate_w && !aligned(gate_w, 4)) || (gate_b && !aligned(gate_b, 4)))
+      (gate_w && !aligned(gate_w, 4)) || (gate_b && !aligned(gate_b, 4)) ||
+      (gate_dw && !aligned(gate_dw, 16)))
     return HSMLA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (scores_in)
     return hip_status(
         hsmla::launch_topk(scores_in, scores_out, sel, D.B, D.T, D.k, s));
-  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkv_hat, gate_w, gate_b, scores_out,
-                                      D.B, D.gh, D.gw, D.H, D.Bs, s));
+  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkv_hat, gate_w, gate_b, gate_dw,
+                                      scores_out, D.B, D.gh, D.gw, D.H, D.Bs, s));
   return hip_status(hsmla::launch_topk(scores_out, nullptr, sel, D.B, D.T, D.k, s));
 }
 
 hsmla_status hsmla_gate_threshold(const hsmla_desc* desc, const void* qkv_hat,
                                   const float* gate_w, const float* gate_b,
-                                  const float* scores_in, float* scores_out,
-                                  int32_t* sel, int32_t* counts, void* stream) {
+                                  const void* gate_dw, const float* scores_in,
+                                  float* scores_out, int32_t* sel,
+                                  int32_t* counts, void* stream) {
   Dims D;
   const hsmla_status st = check_desc(desc, &D);
   if (st != HSMLA_OK) return st;
@@ -366,14 +370,15 @@ hsmla_status hsmla_gate_threshold(const hsmla_desc* desc, const void* qkv_hat,
   if ((qkv_hat && !aligned(qkv_hat, 16)) || !aligned(sel, 4) ||
       !aligned(counts, 4) || (scores_in && !aligned(scores_in, 4)) ||
       (scores_out && !aligned(scores_out, 4)) ||
-      (gate_w && !aligned(gate_w, 4)) || (gate_b && !aligned(gate_b, 4)))
+      (gate_w && !aligned(gate_w, 4)) || (gate_b && !aligned(gate_b, 4)) ||
+      (gate_dw && !aligned(gate_dw, 16)))
     return HSMLA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (scores_in)
     return hip_status(hsmla::launch_threshold(scores_in, scores_out, sel, counts,
                                               D.B, D.T, D.tau, s));
-  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkv_hat, gate_w, gate_b, scores_out,
-                                      D.B, D.gh, D.gw, D.H, D.Bs, s));
+  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkv_hat, gate_w, gate_b, gate_dw,
+                                      scores_out, D.B, D.gh, D.gw, D.H, D.Bs, s));
   return hip_status(hsmla::launch_threshold(scores_out, nullptr, sel, counts,
                                             D.B, D.T, D.tau, s));
 }

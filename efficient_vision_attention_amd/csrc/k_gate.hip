@@ -1,7 +1,10 @@
 // Block-level gate and selection.
 //
 // Scores (FT 3.2 head-level score and block-level aggregation):
-//   f_t^(h) = mean over the block's tokens of [Q_hat; K_hat; V_hat]^(h)
+//   f_t^(h) = mean over the block's tokens of [Q_hat; K_hat; V_hat]^(h),
+//             or, with the gate's depthwise 3x3 kernel g, of
+//             DWConv3x3_g([Q_hat; K_hat; V_hat])^(h) (zero padding at the
+//             image border)
 //   M_t     = (1/H) sum_h sigmoid(w^(h) . f_t^(h) + b^(h))
 // Selection, written in ascending block order -- the compacted tile list the
 // refinement kernel runs over (FT 3.6 stage 3) -- either
@@ -17,6 +20,31 @@ namespace hsmla {
 namespace {
 
 constexpr int kD = 32;
+constexpr int kXcds = 8;
+
+// Per-head logits from the channel sums of one block (fsum[3C], already in
+// LDS), then M_t; one wave per head, wave reduction in fixed lane order.
+__device__ void gate_tail(const float* fsum, float* gsig,
+                          const float* __restrict__ gw,
+                          const float* __restrict__ gb, int heads, int C,
+                          float inv_cnt, float* score) {
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  for (int h = wave; h < heads; h += blockDim.x / 64) {
+    float p = 0.f;
+    for (int f = lane; f < 3 * kD; f += 64) {
+      const int s = f / kD, j = f % kD;
+      p = fmaf(gw[h * 3 * kD + f], fsum[s * C + h * kD + j] * inv_cnt, p);
+    }
+    p = wave_sum(p);
+    if (lane == 0) gsig[h] = 1.f / (1.f + expf(-(p + gb[h])));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.f;
+    for (int h = 0; h < heads; ++h) m += gsig[h];
+    *score = m / (float)heads;
+  }
+}
 
 // grid (blocks per image, batch), 256 threads.  Channel sums over the
 // block's tokens go to LDS (fixed token order per channel), then one wave
@@ -54,23 +82,113 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(
     for (int j = 0; j < V; ++j) fsum[cv * V + j] = s[j];
   }
   __syncthreads();
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const float inv_cnt = 1.f / (float)(block * block);
-  for (int h = wave; h < heads; h += blockDim.x / 64) {
-    float p = 0.f;
-    for (int f = lane; f < 3 * kD; f += 64) {
-      const int s = f / kD, j = f % kD;
-      p = fmaf(gw[h * 3 * kD + f], fsum[s * C + h * kD + j] * inv_cnt, p);
+  gate_tail(fsum, gsig, gw, gb, heads, C, 1.f / (float)(block * block),
+            scores + (size_t)b * gridDim.x + t);
+}
+
+// Four consecutive channels of one token as float32 (8-byte bf16 or 16-byte
+// float32 vector load).
+__device__ __forceinline__ void load4(const bf16* p, float* v) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(u.x << 16);
+  v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16);
+  v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load4(const float* p, float* v) {
+  const float4 u = *reinterpret_cast<const float4*>(p);
+  v[0] = u.x;
+  v[1] = u.y;
+  v[2] = u.z;
+  v[3] = u.w;
+}
+
+// Gate with the depthwise 3x3 inside the head score.  The block sum of the
+// convolution is linear in the input, so it is formed without the
+// convolved map: with the block's rows r0..r0+Bs-1 and columns c0..,
+//   sum_{p in block} conv(p) = sum_{dy,dx} g[dy][dx] * S(dy, dx),
+// where S(dy, dx) sums the input over the block shifted by (dy-1, dx-1)
+// (zero outside the image).  Per halo row y the three column-shifted sums
+// U_dx(y) are built from the row's Bs + 2 tokens, and row y feeds the
+// vertical shifts dy whose shifted block contains it.  One thread owns 4
+// channels and keeps their 36 taps in registers.
+// Grid: 1-D over (batch, block) remapped so each XCD walks a contiguous run
+// of neighbouring blocks, whose halos then hit in that XCD's L2.
+template <typename T>
+__global__ __launch_bounds__(1024) void gate_scores_conv_kernel(
+    const T* __restrict__ qkvh, const T* __restrict__ gdw,
+    const float* __restrict__ gw, const float* __restrict__ gb,
+    float* __restrict__ scores, int gh, int gwid, int heads, int block,
+    int nblocks, int total, int per_xcd) {
+  extern __shared__ float sh[];
+  const int C = heads * kD, C3 = 3 * C;
+  float* fsum = sh;       // [3C]
+  float* gsig = sh + C3;  // [heads]
+  const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (tile >= total) return;
+  const int b = tile / nblocks, t = tile % nblocks;
+  const int nbc = gwid / block;
+  const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
+  const size_t img = (size_t)b * gh * gwid;
+  for (int cv = threadIdx.x; cv < C3 / 4; cv += blockDim.x) {
+    float g[4][9];
+    {
+      float tmp[36];
+#pragma unroll
+      for (int i = 0; i < 9; ++i) load4(gdw + (size_t)cv * 36 + 4 * i, tmp + 4 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 9; ++i) g[j][i] = tmp[9 * j + i];
     }
-    p = wave_sum(p);
-    if (lane == 0) gsig[h] = 1.f / (1.f + expf(-(p + gb[h])));
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const int ylo = max(r0 - 1, 0), yhi = min(r0 + block, gh - 1);
+    for (int y = ylo; y <= yhi; ++y) {
+      const T* rowp = qkvh + (img + (size_t)y * gwid) * C3 + cv * 4;
+      float vl[4] = {0.f, 0.f, 0.f, 0.f}, vr[4] = {0.f, 0.f, 0.f, 0.f};
+      float v0[4], vb1[4], inner[4] = {0.f, 0.f, 0.f, 0.f};
+      if (c0 > 0) load4(rowp + (size_t)(c0 - 1) * C3, vl);
+      if (c0 + block < gwid) load4(rowp + (size_t)(c0 + block) * C3, vr);
+      load4(rowp + (size_t)c0 * C3, v0);
+      load4(rowp + (size_t)(c0 + block - 1) * C3, vb1);
+      for (int x = c0 + 1; x < c0 + block - 1; ++x) {
+        float v[4];
+        load4(rowp + (size_t)x * C3, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) inner[j] += v[j];
+      }
+      // vertical shifts dy whose shifted block holds row y
+      const int yl = y - r0;
+      const int dylo = max(0, yl + 2 - block), dyhi = min(2, yl + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float u0, u1, u2;
+        if (block == 1) {
+          u0 = vl[j];
+          u1 = v0[j];
+          u2 = vr[j];
+        } else {
+          u0 = vl[j] + v0[j] + inner[j];
+          u1 = v0[j] + inner[j] + vb1[j];
+          u2 = inner[j] + vb1[j] + vr[j];
+        }
+        float a = acc[j];
+#pragma unroll
+        for (int dy = 0; dy < 3; ++dy) {
+          if (dy < dylo || dy > dyhi) continue;  // uniform over the workgroup
+          a = fmaf(g[j][3 * dy + 0], u0, a);
+          a = fmaf(g[j][3 * dy + 1], u1, a);
+          a = fmaf(g[j][3 * dy + 2], u2, a);
+        }
+        acc[j] = a;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fsum[cv * 4 + j] = acc[j];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float m = 0.f;
-    for (int h = 0; h < heads; ++h) m += gsig[h];
-    scores[(size_t)b * gridDim.x + t] = m / (float)heads;
-  }
+  gate_tail(fsum, gsig, gw, gb, heads, C, 1.f / (float)(block * block),
+            scores + (size_t)b * nblocks + t);
 }
 
 // Workgroup-wide stream compaction (1024 threads, 16 waves): writes every
@@ -168,11 +286,27 @@ __global__ __launch_bounds__(1024) void threshold_kernel(
 
 hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
                               const float* gate_w, const float* gate_b,
-                              float* scores, int batch, int gh, int gw,
-                              int heads, int block, hipStream_t s) {
+                              const void* gate_dw, float* scores, int batch,
+                              int gh, int gw, int heads, int block,
+                              hipStream_t s) {
   const int nblocks = (gh / block) * (gw / block);
   dim3 grid(nblocks, batch);
   const size_t lds = (size_t)(3 * heads * kD + heads) * sizeof(float);
+  if (gate_dw) {
+    const int total = nblocks * batch;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int vecs = 3 * heads * kD / 4;
+    const int threads = min(1024, (vecs + 63) / 64 * 64);
+    if (bf)
+      gate_scores_conv_kernel<bf16><<<per_xcd * kXcds, threads, lds, s>>>(
+          static_cast<const bf16*>(qkv_hat), static_cast<const bf16*>(gate_dw),
+          gate_w, gate_b, scores, gh, gw, heads, block, nblocks, total, per_xcd);
+    else
+      gate_scores_conv_kernel<float><<<per_xcd * kXcds, threads, lds, s>>>(
+          static_cast<const float*>(qkv_hat), static_cast<const float*>(gate_dw),
+          gate_w, gate_b, scores, gh, gw, heads, block, nblocks, total, per_xcd);
+    return hipGetLastError();
+  }
   if (bf)
     gate_scores_kernel<bf16><<<grid, 256, lds, s>>>(
         static_cast<const bf16*>(qkv_hat), gate_w, gate_b, scores, gh, gw, heads,

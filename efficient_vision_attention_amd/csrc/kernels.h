@@ -45,10 +45,13 @@ hipError_t launch_lin_apply(bool bf, const void* qkv_hat, const float* kv,
                             int heads, hipStream_t s);
 
 // Gate scores per block, then top-k selection.
+// gate_dw: nullptr, or the gate's depthwise 3x3 kernel [3C][3][3] in the
+// activation type (16-byte aligned).
 hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
                               const float* gate_w, const float* gate_b,
-                              float* scores, int batch, int gh, int gw,
-                              int heads, int block, hipStream_t s);
+                              const void* gate_dw, float* scores, int batch,
+                              int gh, int gw, int heads, int block,
+                              hipStream_t s);
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
                        int batch, int nblocks, int keep, hipStream_t s);
 // Threshold routing: sel[b][0 .. counts[b]) = ascending blocks with score >

@@ -34,7 +34,8 @@ class DeviceModel:
     shape: mapping with batch, grid_h, grid_w, channels, heads, branches,
     block, window, keep_blocks, dtype, and optionally tau (threshold
     routing when given).  weights: dict of float64 numpy
-    arrays (w_qkv, w_o, dw list, gate_w, gate_b, and for the block ln1_g,
+    arrays (w_qkv, w_o, dw list, gate_w, gate_b, optionally gate_dw, and
+    for the block ln1_g,
     ln1_b, ln2_g, ln2_b, w1, dw_ffn, w2), dense weights given [in][out]
     (y = x @ W); they are stored on the device transposed, as the library
     expects.
@@ -54,9 +55,11 @@ class DeviceModel:
             "gate_w": to_f32(weights["gate_w"], device),
             "gate_b": to_f32(weights["gate_b"], device),
         }
+        self.t["gate_dw"] = (to_device(weights["gate_dw"], dt, device)
+                             if weights.get("gate_dw") is not None else None)
         self.weights = H.make_weights(self.t["w_qkv"], self.t["w_o"],
                                       self.t["dw"], self.t["gate_w"],
-                                      self.t["gate_b"])
+                                      self.t["gate_b"], self.t["gate_dw"])
         self.ffn = None
         if "w1" in weights:
             for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b"):

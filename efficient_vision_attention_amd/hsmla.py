@@ -60,7 +60,7 @@ class hsmla_weights(ctypes.Structure):
     _fields_ = [
         ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p),
         ("dw", ctypes.c_void_p * 3), ("gate_w", ctypes.c_void_p),
-        ("gate_b", ctypes.c_void_p),
+        ("gate_b", ctypes.c_void_p), ("gate_dw", ctypes.c_void_p),
     ]
 
 
@@ -103,8 +103,8 @@ def library():
             "hsmla_workspace_views": [P(hsmla_desc), I32, VP, P(hsmla_views)],
             "hsmla_qkv_branches": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, VP, SZ, VP],
             "hsmla_linear_attn": [P(hsmla_desc), VP, VP, VP, VP, VP, SZ, VP],
-            "hsmla_gate_select": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP],
-            "hsmla_gate_threshold": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP],
+            "hsmla_gate_select": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP],
+            "hsmla_gate_threshold": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP, VP],
             "hsmla_sparse_softmax": [P(hsmla_desc), VP, VP, VP, VP, VP],
             "hsmla_sparse_softmax_counted": [P(hsmla_desc), VP, VP, VP, VP, VP, VP],
             "hsmla_forward": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, SZ, VP],
@@ -163,12 +163,13 @@ def make_desc(*, batch, grid_h, grid_w, channels, heads, branches, block,
     return d
 
 
-def make_weights(w_qkv, w_o, dw, gate_w, gate_b):
+def make_weights(w_qkv, w_o, dw, gate_w, gate_b, gate_dw=None):
     w = hsmla_weights()
     w.w_qkv, w.w_o = _ptr(w_qkv), _ptr(w_o)
     for i, t in enumerate(dw):
         w.dw[i] = _ptr(t)
     w.gate_w, w.gate_b = _ptr(gate_w), _ptr(gate_b)
+    w.gate_dw = _ptr(gate_dw)
     return w
 
 
@@ -211,17 +212,19 @@ def hsmla_linear_attn(desc, qkv_hat, o, kv, ksum, ws):
            "hsmla_linear_attn")
 
 
-def hsmla_gate_select(desc, qkv_hat, gate_w, gate_b, scores_in, scores_out, sel):
+def hsmla_gate_select(desc, qkv_hat, gate_w, gate_b, scores_in, scores_out, sel,
+                      gate_dw=None):
     _check(library().hsmla_gate_select(ctypes.byref(desc), _ptr(qkv_hat),
-                                       _ptr(gate_w), _ptr(gate_b), _ptr(scores_in),
-                                       _ptr(scores_out), _ptr(sel), _stream()),
+                                       _ptr(gate_w), _ptr(gate_b), _ptr(gate_dw),
+                                       _ptr(scores_in), _ptr(scores_out), _ptr(sel),
+                                       _stream()),
            "hsmla_gate_select")
 
 
 def hsmla_gate_threshold(desc, qkv_hat, gate_w, gate_b, scores_in, scores_out,
-                         sel, counts):
+                         sel, counts, gate_dw=None):
     _check(library().hsmla_gate_threshold(ctypes.byref(desc), _ptr(qkv_hat),
-                                          _ptr(gate_w), _ptr(gate_b),
+                                          _ptr(gate_w), _ptr(gate_b), _ptr(gate_dw),
                                           _ptr(scores_in), _ptr(scores_out),
                                           _ptr(sel), _ptr(counts), _stream()),
            "hsmla_gate_threshold")

@@ -13,7 +13,8 @@
  *   T_hat   = T + sum_s DWConv_{k_s}(T)  for T in Q,K,V (multi-scale branches)
  *   Z, D    = sum_j relu(K_hat_j)^T V_hat_j, sum_j relu(K_hat_j)   (per head)
  *   O_lin   = relu(Q_hat) Z / (relu(Q_hat) . D)           (0 when the sum is 0)
- *   M_t     = mean_h sigmoid(w_h . meanpool_t[Q_hat;K_hat;V_hat]_h + b_h)
+ *   M_t     = mean_h sigmoid(w_h . meanpool_t[Q_hat;K_hat;V_hat]_h + b_h),
+ *             or, with the gate kernel g, meanpool_t of DWConv3x3_g(...)
  *   sel     = the keep_blocks blocks with the largest M_t (ties -> lower t),
  *             or, with threshold routing, every block with M_t > tau
  *   O_i     = O_lin_i + softmax-attn(q_i, K_W, V_W) - lin-local_i  on sel
@@ -108,6 +109,8 @@ typedef struct {
   const void* dw[3];   /* branch s: [3C][k_s][k_s] cross-correlation     */
   const float* gate_w; /* [H][3*head_dim]: weights on [q; k; v] means    */
   const float* gate_b; /* [H]                                            */
+  const void* gate_dw; /* NULL, or [3C][3][3]: the gate's depthwise 3x3   */
+                       /* (FT 3.2 head-level score), 16-byte aligned      */
 } hsmla_weights;
 
 typedef struct {
@@ -163,7 +166,10 @@ hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
 /* Step 4, block gate and selection (FT 3.2 head-level score and block-level
  * aggregation; gate shared by all heads per EX section 2).  With
  * scores_in == NULL the scores M [B][T] are pooled from qkv_hat and written
- * to scores_out (required).  With scores_in != NULL those float32 scores are
+ * to scores_out (required); gate_dw NULL pools the hatted tokens, gate_dw
+ * [3C][3][3] (activation type, 16-byte aligned) pools their depthwise 3x3
+ * convolution, taken over the whole grid with zero padding at the image
+ * border, as in the head-level score equation.  With scores_in != NULL those float32 scores are
  * ranked instead (qkv_hat, gate_w, gate_b may be NULL) and copied to
  * scores_out if it is not NULL.  sel [B][keep_blocks] receives, per image,
  * the indices of the keep_blocks largest scores (equal scores: lower index
@@ -171,8 +177,8 @@ hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
  * HSMLA_ROUTE_TOPK (HSMLA_ERR_ARG otherwise). */
 hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
                                const float* gate_w, const float* gate_b,
-                               const float* scores_in, float* scores_out,
-                               int32_t* sel, void* stream);
+                               const void* gate_dw, const float* scores_in,
+                               float* scores_out, int32_t* sel, void* stream);
 
 /* Step 4 with threshold routing (FT 3.2, the routed set B_tau of the
  * activation-ratio equation; FT 3.3 routing case G > tau; EX section 2
@@ -185,8 +191,9 @@ hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
  * on the host. */
 hsmla_status hsmla_gate_threshold(const hsmla_desc* desc, const void* qkv_hat,
                                   const float* gate_w, const float* gate_b,
-                                  const float* scores_in, float* scores_out,
-                                  int32_t* sel, int32_t* counts, void* stream);
+                                  const void* gate_dw, const float* scores_in,
+                                  float* scores_out, int32_t* sel,
+                                  int32_t* counts, void* stream);
 
 /* Step 5, local softmax refinement of the selected blocks with the two-path
  * residual (FT 3.3 local-neighbourhood, lin-local and residual equations;

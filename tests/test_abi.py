@@ -138,6 +138,9 @@ def test_forward_argument_errors():
     assert f(ctypes.byref(d), ctypes.byref(w), None, FAKE, FAKE, need, None) == -1
     assert f(ctypes.byref(d), ctypes.byref(w), FAKE + 2, FAKE, FAKE, need, None) == -4
     assert f(ctypes.byref(d), None, FAKE, FAKE, FAKE, need, None) == -1
+    w.gate_dw = FAKE + 8
+    assert f(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, need, None) == -4
+    w.gate_dw = None
     w.dw[1] = None
     assert f(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, need, None) == -1
     bad = _desc(window=7)
@@ -156,14 +159,17 @@ def test_stage_argument_errors():
     assert lib.hsmla_linear_attn(ctypes.byref(d), FAKE, FAKE, FAKE + 2, FAKE, FAKE,
                                  need, None) == -4
     # gate: pooled scores need qkv_hat, weights and scores_out
-    assert lib.hsmla_gate_select(ctypes.byref(d), None, FAKE, FAKE, None, FAKE,
+    assert lib.hsmla_gate_select(ctypes.byref(d), None, FAKE, FAKE, None, None, FAKE,
                                  FAKE, None) == -1
-    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE, FAKE, FAKE, None, None,
+    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, None,
                                  FAKE, None) == -1
-    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE,
+    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE,
                                  None, None) == -1
-    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE + 8, FAKE, FAKE, None, FAKE,
+    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE + 8, FAKE, FAKE, None, None, FAKE,
                                  FAKE, None) == -4
+    # the gate's depthwise kernel must be 16-byte aligned
+    assert lib.hsmla_gate_select(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 8, None,
+                                 FAKE, FAKE, None) == -4
     assert lib.hsmla_sparse_softmax(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == -1
     assert lib.hsmla_sparse_softmax(ctypes.byref(d), FAKE, FAKE + 4, FAKE, FAKE,
                                     None) == -4
@@ -172,17 +178,17 @@ def test_stage_argument_errors():
                                   FAKE, FAKE, FAKE, need_q - 1, None) == -5
     # routing must match the entry point
     dt = _desc(tau=0.5)
-    assert lib.hsmla_gate_select(ctypes.byref(dt), FAKE, FAKE, FAKE, None, FAKE,
+    assert lib.hsmla_gate_select(ctypes.byref(dt), FAKE, FAKE, FAKE, None, None, FAKE,
                                  FAKE, None) == -7
     assert lib.hsmla_sparse_softmax(ctypes.byref(dt), FAKE, FAKE, FAKE, FAKE,
                                     None) == -7
-    assert lib.hsmla_gate_threshold(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE,
+    assert lib.hsmla_gate_threshold(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE,
                                     FAKE, FAKE, None) == -7
     assert lib.hsmla_sparse_softmax_counted(ctypes.byref(d), FAKE, FAKE, FAKE,
                                             FAKE, FAKE, None) == -7
-    assert lib.hsmla_gate_threshold(ctypes.byref(dt), FAKE, FAKE, FAKE, None, FAKE,
+    assert lib.hsmla_gate_threshold(ctypes.byref(dt), FAKE, FAKE, FAKE, None, None, FAKE,
                                     FAKE, None, None) == -1
-    assert lib.hsmla_gate_threshold(ctypes.byref(dt), FAKE, FAKE, FAKE, None, FAKE,
+    assert lib.hsmla_gate_threshold(ctypes.byref(dt), FAKE, FAKE, FAKE, None, None, FAKE,
                                     FAKE + 2, FAKE, None) == -4
     assert lib.hsmla_sparse_softmax_counted(ctypes.byref(dt), FAKE, FAKE, FAKE,
                                             None, FAKE, None) == -1

@@ -65,7 +65,7 @@ def _check_module_fullsize(wl, inp, g, tau=None):
     np.testing.assert_allclose(g["ksum"], D, rtol=1e-5, atol=1e-5)
     # S4 over everything
     scores = O.gate_scores(g["qkv_hat"], inp["gate_w"], inp["gate_b"], wl.grid_h,
-                           wl.grid_w, wl.block, wl.heads)
+                           wl.grid_w, wl.block, wl.heads, gate_dw=inp.get("gate_dw"))
     np.testing.assert_allclose(g["scores"], scores, rtol=0, atol=2e-6)
     if tau is None:
         k = wl.keep_blocks
@@ -157,3 +157,13 @@ def test_block_forward_full_size(keep):
             h2 = rnd(O.gelu(O.dwconv_same(h1[None], inp["dw_ffn"], 3, 3)))[0, 4]
             outs.append(rnd(x1[y, x] + h2 @ inp["w2"]))
         assert_close(g["out"][b, toks], np.array(outs), "bf16", f"out image {b}")
+
+
+def test_block_forward_full_size_exact_gate_three_branches():
+    """The benchmark's block workload with the gate's depthwise 3x3 and the
+    identity + 3x3 + 5x5 + 7x7 branches, stage-wise as above."""
+    wl = scaled(WORKLOADS["block"], branches=(3, 5, 7), gate_conv=True)
+    inp = make_inputs(wl)
+    g = Run(wl, inp).block_forward()
+    xn1 = O.round_bf16(O.layer_norm(inp["x"], inp["ln1_g"], inp["ln1_b"]))
+    _check_module_fullsize(wl, dict(inp, x=xn1), g)

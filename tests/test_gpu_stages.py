@@ -33,6 +33,15 @@ STAGE_CASES = {
     "ragged_f32": scaled(WORKLOADS["tiny"], name="ragged_f32", batch=2,
                          grid_h=12, grid_w=28, channels=96, heads=3,
                          branches=(3, 5, 7), block=4, window=10, keep=0.4),
+    # the gate's depthwise 3x3 (FT 3.2 head-level score) with the three
+    # branch sizes 3, 5, 7
+    "exact_gate_bf16": scaled(WORKLOADS["street"], name="exact_gate_bf16",
+                              batch=2, grid_h=24, grid_w=40, branches=(3, 5, 7),
+                              gate_conv=True),
+    "exact_gate_f32": scaled(WORKLOADS["tiny"], name="exact_gate_f32", batch=2,
+                             grid_h=10, grid_w=14, channels=96, heads=3,
+                             branches=(3, 5, 7), block=2, window=6, keep=0.3,
+                             gate_conv=True),
 }
 
 
@@ -104,10 +113,10 @@ def test_gate_select_pooled(name):
     sel = torch.empty((wl.batch, max(k, 1)), dtype=torch.int32, device="cuda")
     announce(f"hsmla_gate_select pooled {name}")
     H.hsmla_gate_select(m.desc, qkvh, m.t["gate_w"], m.t["gate_b"], None,
-                        scores, sel)
+                        scores, sel, gate_dw=m.t["gate_dw"])
     torch.cuda.synchronize()
     ref = O.gate_scores(qkvh_ref, inp["gate_w"], inp["gate_b"], wl.grid_h,
-                        wl.grid_w, wl.block, wl.heads)
+                        wl.grid_w, wl.block, wl.heads, gate_dw=inp.get("gate_dw"))
     g = to_host(scores)
     np.testing.assert_allclose(g, ref, rtol=0, atol=2e-6)
     sel_g = sel.cpu().numpy()[:, :k]
@@ -148,7 +157,7 @@ def test_sparse_softmax(name):
     o_lin, _, _ = O.linear_attention(qkvh_ref, wl.heads)
     o_lin = rnd(o_lin)
     scores = O.gate_scores(qkvh_ref, inp["gate_w"], inp["gate_b"], wl.grid_h,
-                           wl.grid_w, wl.block, wl.heads)
+                           wl.grid_w, wl.block, wl.heads, gate_dw=inp.get("gate_dw"))
     k = wl.keep_blocks
     sel_ref = O.select_blocks(scores.astype(np.float32), k)
     m = DeviceModel(shape_of(wl), inp)

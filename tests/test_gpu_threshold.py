@@ -64,7 +64,8 @@ def test_threshold_injected_scores_exact(T, levels, tau):
     assert torch.equal(s_out, s_in)
 
 
-@pytest.mark.parametrize("name", ["tiny", "street_small", "ragged_bf16", "ragged_f32"])
+@pytest.mark.parametrize("name", ["tiny", "street_small", "ragged_bf16", "ragged_f32",
+                                  "exact_gate_bf16"])
 def test_gate_threshold_pooled(name):
     wl = STAGE_CASES[name]
     inp = make_inputs(wl)
@@ -72,7 +73,8 @@ def test_gate_threshold_pooled(name):
     qkvh_ref = rnd(O.multiscale_branches(rnd(O.qkv_projection(inp["x"], inp["w_qkv"])),
                                          inp["dw"], wl.grid_h, wl.grid_w))
     ref_scores = O.gate_scores(qkvh_ref, inp["gate_w"], inp["gate_b"], wl.grid_h,
-                               wl.grid_w, wl.block, wl.heads)
+                               wl.grid_w, wl.block, wl.heads,
+                               gate_dw=inp.get("gate_dw"))
     tau = tau_between(ref_scores, 0.7)
     m = DeviceModel(shape_of(wl, tau=tau), inp)
     qkvh = to_device(qkvh_ref, wl.dtype)
@@ -82,7 +84,7 @@ def test_gate_threshold_pooled(name):
     counts = torch.empty((wl.batch,), dtype=torch.int32, device="cuda")
     announce(f"hsmla_gate_threshold pooled {name} tau={tau:.6g}")
     H.hsmla_gate_threshold(m.desc, qkvh, m.t["gate_w"], m.t["gate_b"], None,
-                           scores, sel, counts)
+                           scores, sel, counts, gate_dw=m.t["gate_dw"])
     torch.cuda.synchronize()
     g = to_host(scores)
     np.testing.assert_allclose(g, ref_scores, rtol=0, atol=2e-6)
