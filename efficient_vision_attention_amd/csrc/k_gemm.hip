@@ -7,11 +7,15 @@
 // (output x input channels, the nn.Linear layout), so both MFMA operands read
 // eight consecutive k values per lane straight from a row.
 //
-// bfloat16: 128x128 output tile per 256-thread workgroup (2x2 waves of 64x64,
-// each a 2x2 grid of 32x32x16 MFMAs), K staged through double-buffered LDS in
-// steps of 64, workgroups mapped so that each XCD walks whole row panels of A
+// bfloat16: 256x128 output tile per 256-thread workgroup (2x2 waves of
+// 128x64, each a 4x2 grid of 32x32x16 MFMAs: the tall wave tile reads fewer
+// LDS bytes per MFMA than a square 64x64 one), K staged through
+// double-buffered LDS in steps of 32 with the global loads of two steps in
+// flight, workgroups mapped so that each XCD walks whole row panels of A
 // (its L2 then serves the A panel to every column tile).
 // float32: a plain LDS-tiled FMA kernel (small shapes only).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -26,11 +30,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 //
 // Workgroup tile BM x BN, WGM x WGN waves each owning (BM/WGM) x (BN/WGN) =
 // FM x FN fragments of 32 x 32 (v_mfma_f32_32x32x16_bf16).  A and W tiles of
-// BK k go through double-buffered LDS (16-byte loads staged in registers one
-// tile ahead, rows padded by 16 bytes).  The MFMA computes the transposed
-// tile so each lane ends up with runs of 4 consecutive output columns; the
-// finished tile is staged in LDS as float32 and written back row by row with
-// 16-byte stores.  Tiles are remapped so each XCD walks whole row panels of A.
+// BK k go through double-buffered LDS (16-byte loads staged in registers,
+// PF steps ahead; rows padded by 16 bytes).  With NKT > 0 the K loop is
+// unrolled completely (K = NKT * BK), which keeps the compiler's wait counts
+// exact across iterations so the PF = 2 prefetch really stays in flight.
+// The MFMA computes the transposed tile so each lane ends up with runs of 4
+// consecutive output columns; the finished tile is staged in LDS as float32
+// and written back row by row with 16-byte stores.  Tiles are remapped so
+// each XCD walks whole row panels of A.
 // ---------------------------------------------------------------------------
 
 constexpr int kXcds = 8;
@@ -41,7 +48,7 @@ __device__ __forceinline__ uint4 ld16(const bf16* p) {
 
 // SITE only names the call site (one kernel symbol per projection, so
 // profiles tell the four GEMMs apart); the code is the same.
-template <int BM, int BN, int BK, int WGM, int WGN, int SITE>
+template <int BM, int BN, int BK, int WGM, int WGN, int SITE, int PF, bool EDGE, int NKT>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
     const bf16* __restrict__ A, const bf16* __restrict__ W,
     const bf16* __restrict__ R, bf16* __restrict__ C, int M, int N, int K,
@@ -72,33 +79,42 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = (wave / WGN) * (BM / WGM), wn = (wave % WGN) * (BN / WGN);
 
-  uint4 ra[LA], rw[LW];
-  auto load_tile = [&](int k0) {
+  uint4 ra[PF][LA], rw[PF][LW];
+  // Without EDGE (M, N, K multiples of the tile) loads and LDS writes are
+  // unconditional: no divergent branches, so the wait counts stay exact and
+  // the loads stay in flight during the MFMAs.  With EDGE the address is
+  // clamped into the matrix and chunks outside it are zeroed at the LDS
+  // write.
+  auto load_tile = [&](uint4 (&xa)[LA], uint4 (&xw)[LW], int k0) {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int c = tid + NT * i;
-      const int r = c / CPR, kc = (c % CPR) * 8;
-      const int gm = m0 + r, gk = k0 + kc;
-      ra[i] = (gm < M && gk < K) ? ld16(A + (size_t)gm * K + gk) : uint4{0, 0, 0, 0};
+      int gm = m0 + c / CPR, gk = k0 + (c % CPR) * 8;
+      if (EDGE) { gm = min(gm, M - 1); gk = min(gk, K - 8); }
+      xa[i] = ld16(A + (size_t)gm * K + gk);
     }
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
       const int c = tid + NT * i;
-      const int r = c / CPR, kc = (c % CPR) * 8;
-      const int gn = n0 + r, gk = k0 + kc;
-      rw[i] = (gn < N && gk < K) ? ld16(W + (size_t)gn * K + gk) : uint4{0, 0, 0, 0};
+      int gn = n0 + c / CPR, gk = k0 + (c % CPR) * 8;
+      if (EDGE) { gn = min(gn, N - 1); gk = min(gk, K - 8); }
+      xw[i] = ld16(W + (size_t)gn * K + gk);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](const uint4 (&xa)[LA], const uint4 (&xw)[LW], int buf, int k0) {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int c = tid + NT * i;
-      *reinterpret_cast<uint4*>(&As[buf][(c / CPR) * STR + (c % CPR) * 8]) = ra[i];
+      const bool ok = !EDGE || (m0 + c / CPR < M && k0 + (c % CPR) * 8 < K);
+      *reinterpret_cast<uint4*>(&As[buf][(c / CPR) * STR + (c % CPR) * 8]) =
+          ok ? xa[i] : uint4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
       const int c = tid + NT * i;
-      *reinterpret_cast<uint4*>(&Ws[buf][(c / CPR) * STR + (c % CPR) * 8]) = rw[i];
+      const bool ok = !EDGE || (n0 + c / CPR < N && k0 + (c % CPR) * 8 < K);
+      *reinterpret_cast<uint4*>(&Ws[buf][(c / CPR) * STR + (c % CPR) * 8]) =
+          ok ? xw[i] : uint4{0, 0, 0, 0};
     }
   };
 
@@ -110,16 +126,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (K + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
+  const int nk = NKT > 0 ? NKT : (K + BK - 1) / BK;
   const int frow = lane & 31;          // operand row within a 32-row fragment
   const int fk = (lane >> 5) * 8;      // operand k offset within a 16-k step
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * BK);
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 16) {
       bf16x8 af[FM], wf[FN];
@@ -133,7 +143,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
         wf[t] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const uint4*>(
                         &Ws[cur][(wn + 32 * t + frow) * STR + ks + fk]));
-      // D^T tile: rows index output columns n, columns index rows m
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -141,18 +150,65 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i],
                                                               acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      store_tile(cur ^ 1);
-      __syncthreads();
+  };
+  if constexpr (PF == 1) {
+    load_tile(ra[0], rw[0], 0);
+    store_tile(ra[0], rw[0], 0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) load_tile(ra[0], rw[0], (kt + 1) * BK);
+      compute(cur);
+      if (kt + 1 < nk) {
+        store_tile(ra[0], rw[0], cur ^ 1, (kt + 1) * BK);
+        __syncthreads();
+      }
+    }
+  } else {
+    static_assert(PF == 2 && NKT > 0, "the two-step prefetch needs an unrolled K loop");
+    // two tiles in flight: register set (kt & 1) holds tile kt + 2's loads
+    load_tile(ra[0], rw[0], 0);
+    if (nk > 1) load_tile(ra[1], rw[1], BK);
+    store_tile(ra[0], rw[0], 0, 0);
+    __syncthreads();
+    auto step = [&](auto par, int kt) {
+      constexpr int cur = decltype(par)::value;
+      if (kt + 2 < nk) load_tile(ra[cur], rw[cur], (kt + 2) * BK);
+      compute(cur);
+      if (kt + 1 < nk) {
+        store_tile(ra[cur ^ 1], rw[cur ^ 1], cur ^ 1, (kt + 1) * BK);
+        __syncthreads();
+      }
+    };
+#pragma unroll
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
     }
   }
 
   // Epilogue through LDS: each wave stages one 32-row fragment row of its
   // tile at a time as float32 in its own slice of the (now idle) tile
   // buffers, then writes those rows back with 16-byte stores by consecutive
-  // lanes (R added in float32, one rounding to bf16).
+  // lanes (R added in float32, one rounding to bf16).  The residual chunks
+  // of the whole wave tile are loaded first, so their latency overlaps the
+  // staging.
   float* Cs = reinterpret_cast<float*>(smem) + wave * 32 * CSTR;
-  constexpr int CPRO = TN / 8;  // 16-byte output chunks per staged row
+  constexpr int CPRO = TN / 8;          // 16-byte output chunks per staged row
+  constexpr int CPL = 32 * CPRO / 64;   // chunks per lane per fragment row
+  uint4 rres[FM][CPL];
+  if (R) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int c = lane + 64 * q;
+        const int r = c / CPRO, cc = (c % CPRO) * 8;
+        int gm = m0 + wm + 32 * i + r, gn = n0 + wn + cc;
+        if (EDGE) { gm = min(gm, M - 1); gn = min(gn, N - 8); }
+        rres[i][q] = ld16(R + (size_t)gm * N + gn);
+      }
+  }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -167,41 +223,58 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
       }
     __syncthreads();
 #pragma unroll
-    for (int c = lane; c < 32 * CPRO; c += 64) {
+    for (int q = 0; q < CPL; ++q) {
+      const int c = lane + 64 * q;
       const int r = c / CPRO, cc = (c % CPRO) * 8;
       const int gm = m0 + wm + 32 * i + r, gn = n0 + wn + cc;
-      if (gm >= M || gn >= N) continue;
       const float4 lo = *reinterpret_cast<const float4*>(&Cs[r * CSTR + cc]);
       const float4 hi = *reinterpret_cast<const float4*>(&Cs[r * CSTR + cc + 4]);
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      const size_t off = (size_t)gm * N + gn;
       if (R) {
-        const uint4 rr = ld16(R + off);
-        const uint32_t rw4[4] = {rr.x, rr.y, rr.z, rr.w};
+        const uint32_t rw4[4] = {rres[i][q].x, rres[i][q].y, rres[i][q].z, rres[i][q].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[2 * q] += __uint_as_float(rw4[q] << 16);
-          v[2 * q + 1] += __uint_as_float(rw4[q] & 0xffff0000u);
+        for (int t = 0; t < 4; ++t) {
+          v[2 * t] += __uint_as_float(rw4[t] << 16);
+          v[2 * t + 1] += __uint_as_float(rw4[t] & 0xffff0000u);
         }
       }
-      *reinterpret_cast<uint4*>(C + off) =
-          uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      if (!EDGE || (gm < M && gn < N))
+        *reinterpret_cast<uint4*>(C + (size_t)gm * N + gn) =
+            uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
     }
     __syncthreads();
   }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int SITE>
-void run_tiles(const void* A, const void* W, const void* R, void* C, int M,
-               int N, int K, hipStream_t s) {
+template <int BM, int BN, int BK, int WGM, int WGN, int SITE, int PF, bool EDGE,
+          int NKT>
+void launch_tiles(const void* A, const void* W, const void* R, void* C, int M,
+                  int N, int K, hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int total = tiles_m * tiles_n;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  gemm_mfma_bf16<BM, BN, BK, WGM, WGN, SITE><<<per_xcd * kXcds, 64 * WGM * WGN, 0, s>>>(
-      static_cast<const bf16*>(A), static_cast<const bf16*>(W),
-      static_cast<const bf16*>(R), static_cast<bf16*>(C), M, N, K, tiles_n,
-      total, per_xcd);
+  gemm_mfma_bf16<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT>
+      <<<per_xcd * kXcds, 64 * WGM * WGN, 0, s>>>(
+          static_cast<const bf16*>(A), static_cast<const bf16*>(W),
+          static_cast<const bf16*>(R), static_cast<bf16*>(C), M, N, K, tiles_n,
+          total, per_xcd);
+}
+
+// Shapes that are whole tiles with K = 384 or 1536 (the block's projections
+// at C = 384) get the unrolled two-step prefetch; other whole-tile shapes a
+// runtime K loop; ragged shapes the bounds-checked variant.
+template <int BM, int BN, int BK, int WGM, int WGN, int SITE>
+void run_tiles(const void* A, const void* W, const void* R, void* C, int M,
+               int N, int K, hipStream_t s) {
+  if (M % BM || N % BN || K % BK)
+    launch_tiles<BM, BN, BK, WGM, WGN, SITE, 1, true, 0>(A, W, R, C, M, N, K, s);
+  else if (K == 12 * BK)
+    launch_tiles<BM, BN, BK, WGM, WGN, SITE, 2, false, 12>(A, W, R, C, M, N, K, s);
+  else if (K == 48 * BK)
+    launch_tiles<BM, BN, BK, WGM, WGN, SITE, 2, false, 48>(A, W, R, C, M, N, K, s);
+  else
+    launch_tiles<BM, BN, BK, WGM, WGN, SITE, 1, false, 0>(A, W, R, C, M, N, K, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -263,22 +336,13 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ A,
 }
 
 
-// Tile shapes picked by measurement on MI355X for the projection shapes of
-// the block (M = 65536): wide N with K = C favours 256x256 (8 waves) or
-// 128x256 tiles, the C-wide outputs 128x128.
+// One tile shape for every projection: 256x128 with 2x2 waves of 128x64
+// measured best on MI355X for all four projection shapes of the block
+// (M = 65536; N, K = 1152, 384 / 384, 384 / 1536, 384 / 384, 1536).
 template <int SITE>
 void run_mfma(const void* A, const void* W, const void* R, void* C, int M,
               int N, int K, hipStream_t s) {
-  if (N >= 1024 && K <= 512 && M >= 8192) {
-    if (N % 256 == 0)
-      run_tiles<128, 256, 32, 2, 2, SITE>(A, W, R, C, M, N, K, s);
-    else
-      run_tiles<256, 256, 32, 4, 2, SITE>(A, W, R, C, M, N, K, s);
-  } else if (K <= 512) {
-    run_tiles<128, 128, 32, 2, 2, SITE>(A, W, R, C, M, N, K, s);
-  } else {
-    run_tiles<128, 128, 64, 2, 2, SITE>(A, W, R, C, M, N, K, s);
-  }
+  run_tiles<256, 128, 32, 2, 2, SITE>(A, W, R, C, M, N, K, s);
 }
 
 }  // namespace
