@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--keep", type=float, default=0.10)
+    ap.add_argument("--branches", default="3,5",
+                    help="depthwise branch sizes added to the identity")
+    ap.add_argument("--gate-conv", action="store_true",
+                    help="depthwise 3x3 inside the gate's head score")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -125,9 +129,9 @@ def algorithmic_work(name, wl, sel):
     if name == "lin_apply":
         return 2 * C * e * P, (2 * C * d + 3 * C) * P
     if name == "gate_scores":
-        return 3 * C * e * P, 3 * C * P
-    if name == "topk":
-        return wl.batch * wl.num_blocks * 4, 0
+        return 3 * C * e * P, (18 if wl.gate_conv else 1) * 3 * C * P
+    if name in ("topk", "threshold"):
+        return wl.batch * wl.num_blocks * 8, 0
     if name == "sparse_softmax":
         W = window_keys(sel, wl.grid_h, wl.grid_w, Bs, wl.window)
         q = Bs * Bs
@@ -243,7 +247,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    base = scaled(WORKLOADS["block"], keep=args.keep)
+    base = scaled(WORKLOADS["block"], keep=args.keep,
+                  branches=tuple(int(k) for k in args.branches.split(",") if k),
+                  gate_conv=args.gate_conv)
     inp = make_inputs(base)
     x = to_device(inp["x"], base.dtype)
 
@@ -375,7 +381,7 @@ def main():
                    "channels": base.channels, "heads": base.heads,
                    "head_dim": base.head_dim, "branches": list(base.branches),
                    "block": base.block, "window": base.window, "keep": base.keep,
-                   "keep_blocks": base.keep_blocks},
+                   "keep_blocks": base.keep_blocks, "gate_conv": base.gate_conv},
         "roofline": roof,
         "kernels": kernels,
         "sweep": sweep,
