@@ -46,8 +46,11 @@ __all__ = [
     "linear_attention",
     "block_features",
     "gate_scores",
+    "gate_head_scores",
     "select_blocks",
     "select_threshold",
+    "select_threshold_per_head",
+    "refine_per_head",
     "window_bounds",
     "refine_selected",
     "hsmla_module",
@@ -274,6 +277,20 @@ def gate_scores(qkv_hat, gate_w, gate_b, grid_h, grid_w, block, heads,
     over the definition on tiny inputs, and a constant field with a ones
     kernel (closed form at border and interior blocks).
     """
+    g = gate_head_scores(qkv_hat, gate_w, gate_b, grid_h, grid_w, block, heads,
+                         gate_dw=gate_dw)
+    return g.mean(axis=-1)
+
+
+def gate_head_scores(qkv_hat, gate_w, gate_b, grid_h, grid_w, block, heads,
+                     gate_dw=None):
+    """G_b^(h) = sigmoid(w^(h) . f_b^(h) + b^(h)) for every block and head
+    (FT 3.2 head-level score; the features as described in gate_scores).
+    Returns [B, T, H] float64; gate_scores is its mean over heads.
+    Pinned by: zero weights (G^(h) = sigmoid(b^(h)) head by head), one-hot
+    weights on a block-constant feature, and the head mean equal to the
+    hand-worked scores fixture.
+    """
     if gate_dw is not None:
         qkv_hat = dwconv_same(qkv_hat, gate_dw, grid_h, grid_w)
     f = block_features(qkv_hat, grid_h, grid_w, block, heads)
@@ -281,8 +298,7 @@ def gate_scores(qkv_hat, gate_w, gate_b, grid_h, grid_w, block, heads,
     b = np.asarray(gate_b, np.float64)
     logit = np.einsum("bthf,hf->bth", f, w) + b
     with np.errstate(over="ignore"):
-        g = 1.0 / (1.0 + np.exp(-logit))
-    return g.mean(axis=-1)
+        return 1.0 / (1.0 + np.exp(-logit))
 
 
 def select_blocks(scores, keep_blocks):
@@ -329,6 +345,19 @@ def select_threshold(scores, tau):
 # ---------------------------------------------------------------------------
 # step 5: local softmax refinement of the selected blocks
 # ---------------------------------------------------------------------------
+
+def select_threshold_per_head(head_scores, tau):
+    """Per-head routed sets {b : G_b^(h) > tau} (FT 3.2 per-head output
+    routing equation), ascending.  head_scores: [B, T, H].  Returns
+    (sel [B, H, T] int64 padded with -1, counts [B, H]).
+    Pinned by: brute-force membership, and equality with select_threshold
+    when every head has the same scores.
+    """
+    g = np.asarray(head_scores)
+    B, T, H = g.shape
+    sel, counts = select_threshold(np.moveaxis(g, 2, 1).reshape(B * H, T), tau)
+    return sel.reshape(B, H, T), counts.reshape(B, H)
+
 
 def window_bounds(t, grid_h, grid_w, block, window):
     """Token rows/cols [r_lo, r_hi) x [c_lo, c_hi) of the softmax window of
@@ -413,13 +442,43 @@ def refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads, block,
     return out
 
 
+def _head_channels(C, heads, h):
+    """Channel indices of head h's q, k and v inside [Q; K; V] (3C wide)."""
+    d = C // heads
+    return np.concatenate([np.arange(s * C + h * d, s * C + (h + 1) * d)
+                           for s in range(3)])
+
+
+def refine_per_head(qkv, qkv_hat, o_lin, sel_heads, grid_h, grid_w, heads,
+                    block, window, rnd=_identity):
+    """Per-head routing (FT 3.2 per-head output routing equation): head h of
+    the tokens of block b gets the two-path residual when b is in head h's
+    list, and keeps the linear output otherwise.  Each head's refinement is
+    the single-head case of refine_selected on that head's q, k, v channels.
+    sel_heads: [B, H, L] block indices per head, entries < 0 ignored.
+    Pinned by: with equal lists for every head it equals refine_selected.
+    """
+    qkv = np.asarray(qkv, np.float64)
+    qkv_hat = np.asarray(qkv_hat, np.float64)
+    out = np.array(o_lin, np.float64, copy=True)
+    C = out.shape[-1]
+    d = C // heads
+    for h in range(heads):
+        ch = _head_channels(C, heads, h)
+        out[..., h * d:(h + 1) * d] = refine_selected(
+            qkv[..., ch], qkv_hat[..., ch], out[..., h * d:(h + 1) * d],
+            np.asarray(sel_heads)[:, h, :], grid_h, grid_w, 1, block, window,
+            rnd=rnd)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # composition
 # ---------------------------------------------------------------------------
 
 def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
                  keep_blocks, staged=False, sel=None, scores_f32=True,
-                 tau=None):
+                 tau=None, per_head=False):
     """Steps 1-5 of the module (everything before the output projection).
 
     Follows the five inference stages FT 3.6 lists: global linear path,
@@ -432,6 +491,9 @@ def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
     rounding them to float32, the precision the GPU ranks in.  With ``tau``
     set, blocks are routed by the threshold M_t > tau instead of the top
     keep_blocks; ``sel`` is then padded with -1 and "counts" is returned.
+    With ``per_head`` (and ``tau``) each head routes by its own score
+    G_b^(h) > tau: "head_scores" [B, T, H], "sel" [B, H, T] and "counts"
+    [B, H] are returned, and an injected ``sel`` has that shape.
     """
     rnd = round_bf16 if staged else _identity
     C = x.shape[-1]
@@ -443,16 +505,30 @@ def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
                          grid_h, grid_w, block, heads,
                          gate_dw=weights.get("gate_dw"))
     counts = None
+    head_scores = None
     rank_on = scores.astype(np.float32) if scores_f32 else scores
-    if sel is None and tau is not None:
-        sel, counts = select_threshold(rank_on, np.float32(tau) if scores_f32 else tau)
-    elif sel is None:
-        sel = select_blocks(rank_on, keep_blocks)
-    o = refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads,
-                        block, window, rnd=rnd)
+    thr = (np.float32(tau) if scores_f32 else tau) if tau is not None else None
+    if per_head:
+        assert tau is not None or sel is not None
+        head_scores = gate_head_scores(qkv_hat, weights["gate_w"], weights["gate_b"],
+                                       grid_h, grid_w, block, heads,
+                                       gate_dw=weights.get("gate_dw"))
+        if sel is None:
+            hs = head_scores.astype(np.float32) if scores_f32 else head_scores
+            sel, counts = select_threshold_per_head(hs, thr)
+        o = refine_per_head(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads,
+                            block, window, rnd=rnd)
+    else:
+        if sel is None and tau is not None:
+            sel, counts = select_threshold(rank_on, thr)
+        elif sel is None:
+            sel = select_blocks(rank_on, keep_blocks)
+        o = refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads,
+                            block, window, rnd=rnd)
     assert o.shape[-1] == C
     return dict(qkv=qkv, qkv_hat=qkv_hat, Z=Z, D=D, o_lin=o_lin,
-                scores=scores, sel=np.asarray(sel), o=o, counts=counts)
+                scores=scores, sel=np.asarray(sel), o=o, counts=counts,
+                head_scores=head_scores)
 
 
 def hsmla_forward(x, weights, *, staged=False, **kw):

@@ -534,3 +534,121 @@ def test_threshold_module_matches_topk_module():
     assert thr["counts"][0] == k
     np.testing.assert_array_equal(thr["sel"][0, :k], ref["sel"][0])
     np.testing.assert_array_equal(thr["y"], ref["y"])
+
+
+# ---------------------------------------------------------------------------
+# per-head routing
+# ---------------------------------------------------------------------------
+
+def test_head_scores_zero_weights_are_sigmoid_of_each_bias():
+    rng = _rng(21)
+    H, d = 3, 2
+    qkvh = rng.standard_normal((1, 4 * 4, 3 * H * d))
+    b = np.array([0.0, math.log(3.0), -math.log(3.0)])
+    g = O.gate_head_scores(qkvh, np.zeros((H, 3 * d)), b, 4, 4, 2, H)
+    np.testing.assert_allclose(g, np.broadcast_to([0.5, 0.75, 0.25], g.shape),
+                               rtol=0, atol=1e-15)
+
+
+def test_head_scores_one_hot_weight_picks_that_head():
+    H, d, Bs, gh, gw = 2, 2, 2, 4, 6
+    C = H * d
+    T = (gh // Bs) * (gw // Bs)
+    vals = np.arange(T) * 0.1 - 0.2
+    qkvh = np.zeros((1, gh * gw, 3 * C))
+    for n in range(gh * gw):
+        y, x = divmod(n, gw)
+        qkvh[0, n, 2 * C + 1 * d + 0] = vals[(y // Bs) * (gw // Bs) + x // Bs]  # v_0 of head 1
+    w = np.zeros((H, 3 * d)); w[1, 2 * d + 0] = 1.0
+    g = O.gate_head_scores(qkvh, w, np.zeros(H), gh, gw, Bs, H)
+    np.testing.assert_allclose(g[0, :, 0], 0.5, atol=1e-15)
+    np.testing.assert_allclose(g[0, :, 1], 1.0 / (1.0 + np.exp(-vals)), atol=1e-15)
+
+
+def test_head_scores_mean_matches_gate_fixture():
+    fx = _load("gate_2x4.json")
+    g = O.gate_head_scores(np.array(fx["qkv_hat"]), np.array(fx["gate_w"]),
+                           np.array(fx["gate_b"]), grid_h=2, grid_w=4, block=2, heads=2)
+    np.testing.assert_allclose(g.mean(axis=-1)[0], fx["expected"]["scores"], atol=1e-14)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_select_threshold_per_head_brute_force(seed):
+    rng = _rng(40 + seed)
+    B, T, H = 2, 9, 3
+    g = rng.integers(0, 4, size=(B, T, H)) / 4.0
+    tau = 0.5
+    sel, cnt = O.select_threshold_per_head(g, tau)
+    for b in range(B):
+        for h in range(H):
+            want = [t for t in range(T) if g[b, t, h] > tau]
+            assert cnt[b, h] == len(want)
+            assert sel[b, h, :cnt[b, h]].tolist() == want
+            assert np.all(sel[b, h, cnt[b, h]:] == -1)
+
+
+def _small_module_case(seed=3, heads=3):
+    wl = scaled(WORKLOADS["tiny"], name="ph", grid_h=8, grid_w=12, channels=32 * heads,
+                heads=heads, block=4, window=8, seed=seed)
+    return wl, make_inputs(wl)
+
+
+def test_refine_per_head_with_equal_lists_equals_refine_selected():
+    wl, inp = _small_module_case()
+    r = O.hsmla_module(inp["x"], inp, **wl.kwargs())
+    T = wl.num_blocks
+    lst = np.array([[0, 2, 5, -1, -1]])
+    same = np.repeat(lst[:, None, :], wl.heads, axis=1)
+    a = O.refine_per_head(r["qkv"], r["qkv_hat"], r["o_lin"], same, wl.grid_h, wl.grid_w,
+                          wl.heads, wl.block, wl.window)
+    b = O.refine_selected(r["qkv"], r["qkv_hat"], r["o_lin"], lst, wl.grid_h, wl.grid_w,
+                          wl.heads, wl.block, wl.window)
+    assert T > 5
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_refine_per_head_changes_only_the_routed_head():
+    """Head 1 routed on blocks {1, 4}, the others on nothing: only head 1's
+    channels of those blocks' tokens move, by what the all-head refinement
+    of the same blocks gives on head 1."""
+    wl, inp = _small_module_case()
+    r = O.hsmla_module(inp["x"], inp, **wl.kwargs())
+    H, d = wl.heads, wl.head_dim
+    lists = np.full((1, H, 2), -1)
+    lists[0, 1] = [1, 4]
+    got = O.refine_per_head(r["qkv"], r["qkv_hat"], r["o_lin"], lists, wl.grid_h,
+                            wl.grid_w, H, wl.block, wl.window)
+    full = O.refine_selected(r["qkv"], r["qkv_hat"], r["o_lin"], np.array([[1, 4]]),
+                             wl.grid_h, wl.grid_w, H, wl.block, wl.window)
+    want = np.array(r["o_lin"], copy=True)
+    want[..., d:2 * d] = full[..., d:2 * d]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(want[..., d:2 * d], r["o_lin"][..., d:2 * d])
+
+
+def test_per_head_routing_with_equal_heads_equals_threshold_routing():
+    """Heads made identical (the projection columns and depthwise kernels of
+    every head copied from head 0, the same gate weights and bias) give
+    G^(h) = M, so per-head routing must reproduce block routing by M > tau."""
+    wl, inp = _small_module_case(seed=5)
+    inp = dict(inp)
+    C, d = wl.channels, wl.head_dim
+    w_qkv = np.array(inp["w_qkv"], copy=True)
+    dws = [np.array(w, copy=True) for w in inp["dw"]]
+    for s in range(3):
+        for h in range(1, wl.heads):
+            w_qkv[:, s * C + h * d:s * C + (h + 1) * d] = w_qkv[:, s * C:s * C + d]
+            for w in dws:
+                w[s * C + h * d:s * C + (h + 1) * d] = w[s * C:s * C + d]
+    inp.update(w_qkv=w_qkv, dw=dws,
+               gate_w=np.repeat(inp["gate_w"][:1], wl.heads, axis=0),
+               gate_b=np.full(wl.heads, 0.1))
+    blk = O.hsmla_module(inp["x"], inp, **wl.kwargs())
+    tau = float(np.median(blk["scores"]))
+    a = O.hsmla_module(inp["x"], inp, tau=tau, **wl.kwargs())
+    p = O.hsmla_module(inp["x"], inp, tau=tau, per_head=True, **wl.kwargs())
+    for h in range(wl.heads):
+        np.testing.assert_array_equal(p["sel"][:, h], a["sel"])
+        np.testing.assert_array_equal(p["counts"][:, h], a["counts"])
+    assert 0 < a["counts"].sum() < wl.num_blocks * wl.batch
+    np.testing.assert_allclose(p["o"], a["o"], rtol=1e-12, atol=1e-12)
