@@ -30,13 +30,22 @@ inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Dims {
   int B, gh, gw, N, C, H, T, k, Bs, w, kmax;
-  int sw;     // width of a sel row: k (top-k) or T (threshold)
+  int sw;     // sel entries per image: k (top-k), T (threshold), H*T (per head)
+  int nc;     // routed-set counts: B (threshold), B*H (per head)
   size_t P;   // B * N tokens
   size_t e;   // bytes per activation element
   bool bf;
-  bool thr;   // threshold routing
+  bool thr;   // threshold routing (block or per head)
+  bool ph;    // per-head routing
   float tau;
 };
+
+// Where the refinement launch finds each (image, head) list.
+hsmla::SelLayout sel_layout(const Dims& D) {
+  if (D.ph) return {D.H * D.T, D.T, D.H, 1};
+  if (D.thr) return {D.T, 0, 1, 0};
+  return {D.k, 0, 0, 0};
+}
 
 hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
   if (!d) return HSMLA_ERR_NULL;
@@ -58,9 +67,10 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
   const int64_t T = (int64_t)(d->grid_h / d->block) * (d->grid_w / d->block);
   if (T > kMaxBlocks) return HSMLA_ERR_SHAPE;
   if (d->keep_blocks < 0 || d->keep_blocks > T) return HSMLA_ERR_SHAPE;
-  if (d->routing != HSMLA_ROUTE_TOPK && d->routing != HSMLA_ROUTE_THRESHOLD)
+  if (d->routing != HSMLA_ROUTE_TOPK && d->routing != HSMLA_ROUTE_THRESHOLD &&
+      d->routing != HSMLA_ROUTE_HEAD_THRESHOLD)
     return HSMLA_ERR_ARG;
-  if (d->routing == HSMLA_ROUTE_THRESHOLD && isnan(d->tau)) return HSMLA_ERR_ARG;
+  if (d->routing != HSMLA_ROUTE_TOPK && isnan(d->tau)) return HSMLA_ERR_ARG;
   const int64_t N = (int64_t)d->grid_h * d->grid_w;
   // every element index must fit a 32-bit grid dimension and size_t math
   if (N * d->batch * 4 * (int64_t)d->channels > ((int64_t)1 << 40)) return HSMLA_ERR_SHAPE;
@@ -79,9 +89,11 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
     out->kmax = kmax;
     out->P = (size_t)N * d->batch;
     out->bf = d->dtype == HSMLA_BF16;
-    out->thr = d->routing == HSMLA_ROUTE_THRESHOLD;
+    out->thr = d->routing != HSMLA_ROUTE_TOPK;
+    out->ph = d->routing == HSMLA_ROUTE_HEAD_THRESHOLD;
     out->tau = d->tau;
-    out->sw = out->thr ? (int)T : d->keep_blocks;
+    out->sw = out->ph ? d->heads * (int)T : out->thr ? (int)T : d->keep_blocks;
+    out->nc = out->ph ? d->batch * d->heads : d->batch;
     out->e = out->bf ? 2 : 4;
   }
   return HSMLA_OK;
@@ -90,11 +102,12 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
 // Workspace sections, in this order (each start rounded up to 256 bytes):
 //   qkv [P][3C], qkv_hat [P][3C], o [P][C], kv [B][H][d][d] f32,
 //   ksum [B][H][d] f32, kv partials f32, dw taps [kmax^2][3C] f32,
-//   scores [B][T] f32, sel [B][k] i32 (threshold: [B][T] i32, counts [B] i32),
+//   scores [B][T] f32, sel [B][k] i32 (threshold: [B][T] i32, counts [B] i32;
+//   per head: [B][H][T] i32, counts [B][H] i32, head scores [B][T][H] f32),
 //   (block only) xn [P][C], x1 [P][C], h1 [P][4C], h2 [P][4C],
 //   ffn taps [9][4C] f32.
 struct Layout {
-  size_t qkv, qkv_hat, o, kv, ksum, part, taps, scores, sel, counts;
+  size_t qkv, qkv_hat, o, kv, ksum, part, taps, scores, sel, counts, head_scores;
   size_t xn, x1, h1, h2, ffn_taps;
   size_t total;
 };
@@ -125,7 +138,8 @@ Layout layout(const Dims& D, int op) {
     L.taps = take(tap_bytes);
     L.scores = take((size_t)D.B * D.T * 4);
     L.sel = take((size_t)D.B * D.sw * 4 + 4);
-    if (D.thr) L.counts = take((size_t)D.B * 4);
+    if (D.thr) L.counts = take((size_t)D.nc * 4);
+    if (D.ph) L.head_scores = take((size_t)D.B * D.T * D.H * 4);
     if (op == HSMLA_OP_BLOCK) {
       L.xn = take(D.P * D.C * D.e);
       L.x1 = take(D.P * D.C * D.e);
@@ -217,6 +231,7 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
   float* scores = reinterpret_cast<float*>(at(ws, L.scores));
   int32_t* sel = reinterpret_cast<int32_t*>(at(ws, L.sel));
   int32_t* counts = D.thr ? reinterpret_cast<int32_t*>(at(ws, L.counts)) : nullptr;
+  float* hscores = D.ph ? reinterpret_cast<float*>(at(ws, L.head_scores)) : nullptr;
   hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, s, r);
   if (st != HSMLA_OK) return st;
   r.mark("kv_state");
@@ -225,9 +240,13 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
   HSMLA_TRY(hsmla::launch_lin_apply(D.bf, qkvh, kv, ksum, o, D.B, D.N, D.H, s));
   r.mark("gate_scores");
   HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b,
-                                      w->gate_dw, scores, D.B, D.gh, D.gw, D.H,
-                                      D.Bs, s));
-  if (D.thr) {
+                                      w->gate_dw, scores, hscores, D.B, D.gh,
+                                      D.gw, D.H, D.Bs, s));
+  if (D.ph) {
+    r.mark("threshold_heads");
+    HSMLA_TRY(hsmla::launch_threshold_heads(hscores, nullptr, sel, counts, D.B,
+                                            D.T, D.H, D.tau, s));
+  } else if (D.thr) {
     r.mark("threshold");
     HSMLA_TRY(hsmla::launch_threshold(scores, nullptr, sel, counts, D.B, D.T,
                                       D.tau, s));
@@ -237,7 +256,8 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
   }
   r.mark("sparse_softmax");
   HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, sel, counts, o, D.B, D.gh,
-                                 D.gw, D.H, D.Bs, D.w, D.sw, D.sw, s));
+                                 D.gw, D.H, D.Bs, D.w, D.thr ? D.T : D.k,
+                                 sel_layout(D), s));
   return HSMLA_OK;
 }
 
@@ -286,6 +306,7 @@ hsmla_status hsmla_workspace_views(const hsmla_desc* desc, int32_t op,
   v->scores = reinterpret_cast<float*>(at(ws, L.scores));
   v->sel = reinterpret_cast<int32_t*>(at(ws, L.sel));
   v->counts = D.thr ? reinterpret_cast<int32_t*>(at(ws, L.counts)) : nullptr;
+  v->head_scores = D.ph ? reinterpret_cast<float*>(at(ws, L.head_scores)) : nullptr;
   v->x1 = op == HSMLA_OP_BLOCK ? at(ws, L.x1) : nullptr;
   return HSMLA_OK;
 }
@@ -351,7 +372,8 @@ hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
     return hip_status(
         hsmla::launch_topk(scores_in, scores_out, sel, D.B, D.T, D.k, s));
   HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkv_hat, gate_w, gate_b, gate_dw,
-                                      scores_out, D.B, D.gh, D.gw, D.H, D.Bs, s));
+                                      scores_out, nullptr, D.B, D.gh, D.gw, D.H,
+                                      D.Bs, s));
   return hip_status(hsmla::launch_topk(scores_out, nullptr, sel, D.B, D.T, D.k, s));
 }
 
@@ -363,7 +385,7 @@ hsmla_status hsmla_gate_threshold(const hsmla_desc* desc, const void* qkv_hat,
   Dims D;
   const hsmla_status st = check_desc(desc, &D);
   if (st != HSMLA_OK) return st;
-  if (!D.thr) return HSMLA_ERR_ARG;
+  if (!D.thr || D.ph) return HSMLA_ERR_ARG;
   if (!sel || !counts) return HSMLA_ERR_NULL;
   if (!scores_in && (!qkv_hat || !gate_w || !gate_b || !scores_out))
     return HSMLA_ERR_NULL;
@@ -378,9 +400,42 @@ hsmla_status hsmla_gate_threshold(const hsmla_desc* desc, const void* qkv_hat,
     return hip_status(hsmla::launch_threshold(scores_in, scores_out, sel, counts,
                                               D.B, D.T, D.tau, s));
   HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkv_hat, gate_w, gate_b, gate_dw,
-                                      scores_out, D.B, D.gh, D.gw, D.H, D.Bs, s));
+                                      scores_out, nullptr, D.B, D.gh, D.gw, D.H,
+                                      D.Bs, s));
   return hip_status(hsmla::launch_threshold(scores_out, nullptr, sel, counts,
                                             D.B, D.T, D.tau, s));
+}
+
+hsmla_status hsmla_gate_head_threshold(const hsmla_desc* desc,
+                                       const void* qkv_hat,
+                                       const float* gate_w, const float* gate_b,
+                                       const void* gate_dw,
+                                       const float* head_scores_in,
+                                       float* head_scores_out, int32_t* sel,
+                                       int32_t* counts, void* stream) {
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!D.ph) return HSMLA_ERR_ARG;
+  if (!sel || !counts) return HSMLA_ERR_NULL;
+  if (!head_scores_in && (!qkv_hat || !gate_w || !gate_b || !head_scores_out))
+    return HSMLA_ERR_NULL;
+  if ((qkv_hat && !aligned(qkv_hat, 16)) || !aligned(sel, 4) ||
+      !aligned(counts, 4) || (head_scores_in && !aligned(head_scores_in, 4)) ||
+      (head_scores_out && !aligned(head_scores_out, 4)) ||
+      (gate_w && !aligned(gate_w, 4)) || (gate_b && !aligned(gate_b, 4)) ||
+      (gate_dw && !aligned(gate_dw, 16)))
+    return HSMLA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (head_scores_in)
+    return hip_status(hsmla::launch_threshold_heads(
+        head_scores_in, head_scores_out, sel, counts, D.B, D.T, D.H, D.tau, s));
+  // per-head routing needs only G; the block scores M are not written
+  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkv_hat, gate_w, gate_b, gate_dw,
+                                      nullptr, head_scores_out, D.B, D.gh, D.gw,
+                                      D.H, D.Bs, s));
+  return hip_status(hsmla::launch_threshold_heads(
+      head_scores_out, nullptr, sel, counts, D.B, D.T, D.H, D.tau, s));
 }
 
 hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
@@ -396,7 +451,8 @@ hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
     return HSMLA_ERR_ALIGN;
   return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, nullptr, o,
                                          D.B, D.gh, D.gw, D.H, D.Bs, D.w, D.k,
-                                         D.k, static_cast<hipStream_t>(stream)));
+                                         sel_layout(D),
+                                         static_cast<hipStream_t>(stream)));
 }
 
 hsmla_status hsmla_sparse_softmax_counted(const hsmla_desc* desc,
@@ -414,7 +470,8 @@ hsmla_status hsmla_sparse_softmax_counted(const hsmla_desc* desc,
     return HSMLA_ERR_ALIGN;
   return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, counts, o,
                                          D.B, D.gh, D.gw, D.H, D.Bs, D.w, D.T,
-                                         D.T, static_cast<hipStream_t>(stream)));
+                                         sel_layout(D),
+                                         static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -12,7 +12,9 @@
 //              index (the count is fixed, so the grid size is known on the
 //              host), or
 //   threshold: every block with M_t > tau (FT 3.2 gating equation); the
-//              per-image count goes to device memory.
+//              per-image count goes to device memory, or
+//   per head:  for each head h the blocks with G^(h)_t > tau (FT 3.2 per-head
+//              output routing), one list and count per (image, head).
 #include "common.h"
 #include "kernels.h"
 
@@ -24,10 +26,12 @@ constexpr int kXcds = 8;
 
 // Per-head logits from the channel sums of one block (fsum[3C], already in
 // LDS), then M_t; one wave per head, wave reduction in fixed lane order.
+// score (optional) receives M_t, head_score (optional) G^(h) of the block
+// for h = 0 .. heads-1.
 __device__ void gate_tail(const float* fsum, float* gsig,
                           const float* __restrict__ gw,
                           const float* __restrict__ gb, int heads, int C,
-                          float inv_cnt, float* score) {
+                          float inv_cnt, float* score, float* head_score) {
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   for (int h = wave; h < heads; h += blockDim.x / 64) {
     float p = 0.f;
@@ -36,10 +40,14 @@ __device__ void gate_tail(const float* fsum, float* gsig,
       p = fmaf(gw[h * 3 * kD + f], fsum[s * C + h * kD + j] * inv_cnt, p);
     }
     p = wave_sum(p);
-    if (lane == 0) gsig[h] = 1.f / (1.f + expf(-(p + gb[h])));
+    if (lane == 0) {
+      const float g = 1.f / (1.f + expf(-(p + gb[h])));
+      gsig[h] = g;
+      if (head_score) head_score[h] = g;
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && score) {
     float m = 0.f;
     for (int h = 0; h < heads; ++h) m += gsig[h];
     *score = m / (float)heads;
@@ -52,8 +60,8 @@ __device__ void gate_tail(const float* fsum, float* gsig,
 template <typename T>
 __global__ __launch_bounds__(256) void gate_scores_kernel(
     const T* __restrict__ qkvh, const float* __restrict__ gw,
-    const float* __restrict__ gb, float* __restrict__ scores, int gh, int gwid,
-    int heads, int block) {
+    const float* __restrict__ gb, float* __restrict__ scores,
+    float* __restrict__ head_scores, int gh, int gwid, int heads, int block) {
   extern __shared__ float sh[];
   const int C = heads * kD, C3 = 3 * C;
   float* fsum = sh;          // [3C]
@@ -83,7 +91,8 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(
   }
   __syncthreads();
   gate_tail(fsum, gsig, gw, gb, heads, C, 1.f / (float)(block * block),
-            scores + (size_t)b * gridDim.x + t);
+            scores ? scores + (size_t)b * gridDim.x + t : nullptr,
+            head_scores ? head_scores + ((size_t)b * gridDim.x + t) * heads : nullptr);
 }
 
 // Four consecutive channels of one token as float32 (8-byte bf16 or 16-byte
@@ -118,8 +127,8 @@ template <typename T>
 __global__ __launch_bounds__(1024) void gate_scores_conv_kernel(
     const T* __restrict__ qkvh, const T* __restrict__ gdw,
     const float* __restrict__ gw, const float* __restrict__ gb,
-    float* __restrict__ scores, int gh, int gwid, int heads, int block,
-    int nblocks, int total, int per_xcd) {
+    float* __restrict__ scores, float* __restrict__ head_scores, int gh,
+    int gwid, int heads, int block, int nblocks, int total, int per_xcd) {
   extern __shared__ float sh[];
   const int C = heads * kD, C3 = 3 * C;
   float* fsum = sh;       // [3C]
@@ -188,7 +197,8 @@ __global__ __launch_bounds__(1024) void gate_scores_conv_kernel(
   }
   __syncthreads();
   gate_tail(fsum, gsig, gw, gb, heads, C, 1.f / (float)(block * block),
-            scores + (size_t)b * nblocks + t);
+            scores ? scores + (size_t)b * nblocks + t : nullptr,
+            head_scores ? head_scores + ((size_t)b * nblocks + t) * heads : nullptr);
 }
 
 // Workgroup-wide stream compaction (1024 threads, 16 waves): writes every
@@ -282,13 +292,31 @@ __global__ __launch_bounds__(1024) void threshold_kernel(
   if (threadIdx.x == 0) counts[b] = n;
 }
 
+// Per-head routing: grid (heads, batch), 1024 threads.  sel[b][h][0 .. n) =
+// ascending blocks with G^(h) > tau (head scores laid out [b][t][h]),
+// counts[b][h] = n.
+__global__ __launch_bounds__(1024) void threshold_heads_kernel(
+    const float* __restrict__ hs, float* __restrict__ hs_copy,
+    int32_t* __restrict__ sel, int32_t* __restrict__ counts, int nblocks,
+    int heads, float tau) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const float* src = hs + (size_t)b * nblocks * heads + h;
+  if (hs_copy)
+    for (int t = threadIdx.x; t < nblocks; t += blockDim.x)
+      hs_copy[((size_t)b * nblocks + t) * heads + h] = src[(size_t)t * heads];
+  const int n = compact_ascending(
+      [&](int t) { return src[(size_t)t * heads] > tau; }, nblocks,
+      sel + ((size_t)b * heads + h) * nblocks);
+  if (threadIdx.x == 0) counts[b * heads + h] = n;
+}
+
 }  // namespace
 
 hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
                               const float* gate_w, const float* gate_b,
-                              const void* gate_dw, float* scores, int batch,
-                              int gh, int gw, int heads, int block,
-                              hipStream_t s) {
+                              const void* gate_dw, float* scores,
+                              float* head_scores, int batch, int gh, int gw,
+                              int heads, int block, hipStream_t s) {
   const int nblocks = (gh / block) * (gw / block);
   dim3 grid(nblocks, batch);
   const size_t lds = (size_t)(3 * heads * kD + heads) * sizeof(float);
@@ -300,21 +328,23 @@ hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
     if (bf)
       gate_scores_conv_kernel<bf16><<<per_xcd * kXcds, threads, lds, s>>>(
           static_cast<const bf16*>(qkv_hat), static_cast<const bf16*>(gate_dw),
-          gate_w, gate_b, scores, gh, gw, heads, block, nblocks, total, per_xcd);
+          gate_w, gate_b, scores, head_scores, gh, gw, heads, block, nblocks,
+          total, per_xcd);
     else
       gate_scores_conv_kernel<float><<<per_xcd * kXcds, threads, lds, s>>>(
           static_cast<const float*>(qkv_hat), static_cast<const float*>(gate_dw),
-          gate_w, gate_b, scores, gh, gw, heads, block, nblocks, total, per_xcd);
+          gate_w, gate_b, scores, head_scores, gh, gw, heads, block, nblocks,
+          total, per_xcd);
     return hipGetLastError();
   }
   if (bf)
     gate_scores_kernel<bf16><<<grid, 256, lds, s>>>(
-        static_cast<const bf16*>(qkv_hat), gate_w, gate_b, scores, gh, gw, heads,
-        block);
+        static_cast<const bf16*>(qkv_hat), gate_w, gate_b, scores, head_scores,
+        gh, gw, heads, block);
   else
     gate_scores_kernel<float><<<grid, 256, lds, s>>>(
-        static_cast<const float*>(qkv_hat), gate_w, gate_b, scores, gh, gw,
-        heads, block);
+        static_cast<const float*>(qkv_hat), gate_w, gate_b, scores, head_scores,
+        gh, gw, heads, block);
   return hipGetLastError();
 }
 
@@ -334,6 +364,15 @@ hipError_t launch_threshold(const float* scores, float* scores_copy,
                             int nblocks, float tau, hipStream_t s) {
   threshold_kernel<<<batch, 1024, 0, s>>>(scores, scores_copy, sel, counts,
                                           nblocks, tau);
+  return hipGetLastError();
+}
+
+hipError_t launch_threshold_heads(const float* head_scores, float* copy,
+                                  int32_t* sel, int32_t* counts, int batch,
+                                  int nblocks, int heads, float tau,
+                                  hipStream_t s) {
+  threshold_heads_kernel<<<dim3(heads, batch), 1024, 0, s>>>(
+      head_scores, copy, sel, counts, nblocks, heads, tau);
   return hipGetLastError();
 }
 

@@ -26,15 +26,16 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
     const T* __restrict__ qkv, const T* __restrict__ qkvh,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ counts,
     T* __restrict__ o, int gh, int gw, int heads, int block, int window,
-    int stride) {
+    SelLayout lay) {
   __shared__ float ks[kKT][kD];
   __shared__ float vs[kKT][kD];
   __shared__ float fks[kKT][kD];
   __shared__ float vhs[kKT][kD];
   const int b = blockIdx.y, h = blockIdx.z;
   const int C = heads * kD, C3 = 3 * C;
-  if (counts && (int)blockIdx.x >= counts[b]) return;  // beyond the routed set
-  const int t = sel[(size_t)b * stride + blockIdx.x];
+  if (counts && (int)blockIdx.x >= counts[b * lay.cnt_b + h * lay.cnt_h])
+    return;  // beyond the routed set
+  const int t = sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + blockIdx.x];
   const int nbc = gw / block;
   if (t < 0 || t >= (gh / block) * nbc) return;  // invalid entry: no access
   const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
@@ -149,15 +150,16 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ qkvh,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ counts,
     bf16* __restrict__ o, int gh, int gw, int heads, int block, int window,
-    int stride) {
+    SelLayout lay) {
   constexpr int NT = 64 * 2 * NQT;
   __shared__ SparseTile tiles[2];
   __shared__ float linloc[NQT * 32][kD + 1];
 
   const int b = blockIdx.y, h = blockIdx.z;
   const int C = heads * kD, C3 = 3 * C;
-  if (counts && (int)blockIdx.x >= counts[b]) return;  // beyond the routed set
-  const int t = sel[(size_t)b * stride + blockIdx.x];
+  if (counts && (int)blockIdx.x >= counts[b * lay.cnt_b + h * lay.cnt_h])
+    return;  // beyond the routed set
+  const int t = sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + blockIdx.x];
   const int nbc = gw / block;
   if (t < 0 || t >= (gh / block) * nbc) return;  // invalid entry: no access
   const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
@@ -357,12 +359,12 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
 template <typename T>
 hipError_t run(const void* qkv, const void* qkvh, const int32_t* sel,
                const int32_t* counts, void* o, int batch, int gh, int gw,
-               int heads, int block, int window, int entries, int stride,
+               int heads, int block, int window, int entries, SelLayout lay,
                hipStream_t s) {
   dim3 grid(entries, batch, heads);
   sparse_valu_kernel<T><<<grid, block * block, 0, s>>>(
       static_cast<const T*>(qkv), static_cast<const T*>(qkvh), sel, counts,
-      static_cast<T*>(o), gh, gw, heads, block, window, stride);
+      static_cast<T*>(o), gh, gw, heads, block, window, lay);
   return hipGetLastError();
 }
 
@@ -371,7 +373,7 @@ hipError_t run(const void* qkv, const void* qkvh, const int32_t* sel,
 hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
                          const int32_t* sel, const int32_t* counts, void* o,
                          int batch, int gh, int gw, int heads, int block,
-                         int window, int entries, int stride, hipStream_t s) {
+                         int window, int entries, SelLayout lay, hipStream_t s) {
   if (entries == 0) return hipSuccess;
   const int nqt = (block * block + 31) / 32;
   if (bf && nqt <= 4) {
@@ -380,17 +382,17 @@ hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
     const bf16* qh = static_cast<const bf16*>(qkv_hat);
     bf16* out = static_cast<bf16*>(o);
     switch (nqt) {
-      case 1: sparse_mfma_kernel<1><<<grid, 128, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, stride); break;
-      case 2: sparse_mfma_kernel<2><<<grid, 256, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, stride); break;
-      case 3: sparse_mfma_kernel<3><<<grid, 384, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, stride); break;
-      default: sparse_mfma_kernel<4><<<grid, 512, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, stride); break;
+      case 1: sparse_mfma_kernel<1><<<grid, 128, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, lay); break;
+      case 2: sparse_mfma_kernel<2><<<grid, 256, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, lay); break;
+      case 3: sparse_mfma_kernel<3><<<grid, 384, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, lay); break;
+      default: sparse_mfma_kernel<4><<<grid, 512, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, lay); break;
     }
     return hipGetLastError();
   }
   return bf ? run<bf16>(qkv, qkv_hat, sel, counts, o, batch, gh, gw, heads,
-                        block, window, entries, stride, s)
+                        block, window, entries, lay, s)
             : run<float>(qkv, qkv_hat, sel, counts, o, batch, gh, gw, heads,
-                         block, window, entries, stride, s);
+                         block, window, entries, lay, s);
 }
 
 }  // namespace hsmla

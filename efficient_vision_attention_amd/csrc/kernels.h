@@ -46,12 +46,13 @@ hipError_t launch_lin_apply(bool bf, const void* qkv_hat, const float* kv,
 
 // Gate scores per block, then top-k selection.
 // gate_dw: nullptr, or the gate's depthwise 3x3 kernel [3C][3][3] in the
-// activation type (16-byte aligned).
+// activation type (16-byte aligned).  head_scores (optional): G^(h) per
+// block and head, [batch][blocks][heads].
 hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
                               const float* gate_w, const float* gate_b,
-                              const void* gate_dw, float* scores, int batch,
-                              int gh, int gw, int heads, int block,
-                              hipStream_t s);
+                              const void* gate_dw, float* scores,
+                              float* head_scores, int batch, int gh, int gw,
+                              int heads, int block, hipStream_t s);
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
                        int batch, int nblocks, int keep, hipStream_t s);
 // Threshold routing: sel[b][0 .. counts[b]) = ascending blocks with score >
@@ -59,14 +60,26 @@ hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
 hipError_t launch_threshold(const float* scores, float* scores_copy,
                             int32_t* sel, int32_t* counts, int batch,
                             int nblocks, float tau, hipStream_t s);
+// Per-head routing: sel[b][h][0 .. counts[b][h]) = ascending blocks with
+// head_scores[b][t][h] > tau.
+hipError_t launch_threshold_heads(const float* head_scores, float* copy,
+                                  int32_t* sel, int32_t* counts, int batch,
+                                  int nblocks, int heads, float tau,
+                                  hipStream_t s);
 
-// Windowed softmax refinement of the selected blocks, in place on o.  The
-// grid covers `entries` entries of each sel row (row stride `stride`); with
-// counts != nullptr only the first counts[b] of image b are refined.
+// Where the sparse launch finds the list of (image b, head h): entry x is
+// sel[b * sel_b + h * sel_h + x]; with counts != nullptr only entries x <
+// counts[b * cnt_b + h * cnt_h] are refined.
+struct SelLayout {
+  int sel_b, sel_h, cnt_b, cnt_h;
+};
+
+// Windowed softmax refinement of the selected blocks, in place on o; the
+// grid covers `entries` list entries per (image, head).
 hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
                          const int32_t* sel, const int32_t* counts, void* o,
                          int batch, int gh, int gw, int heads, int block,
-                         int window, int entries, int stride, hipStream_t s);
+                         int window, int entries, SelLayout lay, hipStream_t s);
 
 // y = LN(x) . gamma + beta over the channel dimension.
 hipError_t launch_layernorm(bool bf, const void* x, const float* gamma,

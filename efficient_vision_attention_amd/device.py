@@ -33,7 +33,7 @@ class DeviceModel:
 
     shape: mapping with batch, grid_h, grid_w, channels, heads, branches,
     block, window, keep_blocks, dtype, and optionally tau (threshold
-    routing when given).  weights: dict of float64 numpy
+    routing when given) and per_head (route each head by its own score).  weights: dict of float64 numpy
     arrays (w_qkv, w_o, dw list, gate_w, gate_b, optionally gate_dw, and
     for the block ln1_g,
     ln1_b, ln2_g, ln2_b, w1, dw_ffn, w2), dense weights given [in][out]
@@ -87,7 +87,8 @@ class DeviceModel:
         B, N, C, Hh = s["batch"], s["grid_h"] * s["grid_w"], s["channels"], s["heads"]
         T = (s["grid_h"] // s["block"]) * (s["grid_w"] // s["block"])
         thr = s.get("tau") is not None
-        k = T if thr else s["keep_blocks"]
+        ph = thr and s.get("per_head", False)
+        k = Hh * T if ph else T if thr else s["keep_blocks"]
         off = H.hsmla_workspace_views(self.desc, op, ws)
         adt = TORCH_DTYPE[self.dtype]
         esz = torch.tensor([], dtype=adt).element_size()
@@ -105,7 +106,11 @@ class DeviceModel:
             "scores": sl("scores", B * T, torch.float32, 4).view(B, T),
             "sel": sl("sel", B * k, torch.int32, 4).view(B, k),
         }
-        if thr:
+        if ph:
+            out["sel"] = out["sel"].view(B, Hh, T)
+            out["counts"] = sl("counts", B * Hh, torch.int32, 4).view(B, Hh)
+            out["head_scores"] = sl("head_scores", B * T * Hh, torch.float32, 4).view(B, T, Hh)
+        elif thr:
             out["counts"] = sl("counts", B, torch.int32, 4)
         if off.get("x1") is not None:
             out["x1"] = sl("x1", B * N * C, adt, esz).view(B, N, C)

@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhsmla.s
 
 HSMLA_F32, HSMLA_BF16 = 0, 1
 HSMLA_OP_QKV, HSMLA_OP_LINEAR, HSMLA_OP_FORWARD, HSMLA_OP_BLOCK = 0, 1, 2, 3
-HSMLA_ROUTE_TOPK, HSMLA_ROUTE_THRESHOLD = 0, 1
+HSMLA_ROUTE_TOPK, HSMLA_ROUTE_THRESHOLD, HSMLA_ROUTE_HEAD_THRESHOLD = 0, 1, 2
 
 # Every symbol include/hsmla.h declares.
 EXPORTED = (
@@ -28,6 +28,7 @@ EXPORTED = (
     "hsmla_linear_attn",
     "hsmla_gate_select",
     "hsmla_gate_threshold",
+    "hsmla_gate_head_threshold",
     "hsmla_sparse_softmax",
     "hsmla_sparse_softmax_counted",
     "hsmla_forward",
@@ -79,7 +80,7 @@ class hsmla_views(ctypes.Structure):
         ("o", ctypes.c_void_p), ("kv", ctypes.c_void_p),
         ("ksum", ctypes.c_void_p), ("scores", ctypes.c_void_p),
         ("sel", ctypes.c_void_p), ("counts", ctypes.c_void_p),
-        ("x1", ctypes.c_void_p),
+        ("head_scores", ctypes.c_void_p), ("x1", ctypes.c_void_p),
     ]
 
 
@@ -105,6 +106,7 @@ def library():
             "hsmla_linear_attn": [P(hsmla_desc), VP, VP, VP, VP, VP, SZ, VP],
             "hsmla_gate_select": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP],
             "hsmla_gate_threshold": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP, VP],
+            "hsmla_gate_head_threshold": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP, VP],
             "hsmla_sparse_softmax": [P(hsmla_desc), VP, VP, VP, VP, VP],
             "hsmla_sparse_softmax_counted": [P(hsmla_desc), VP, VP, VP, VP, VP, VP],
             "hsmla_forward": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, SZ, VP],
@@ -147,9 +149,9 @@ def _stream():
 
 
 def make_desc(*, batch, grid_h, grid_w, channels, heads, branches, block,
-              window, keep_blocks, dtype, head_dim=32, tau=None):
+              window, keep_blocks, dtype, head_dim=32, tau=None, per_head=False):
     """tau=None: top-k routing (keep_blocks per image); a number: threshold
-    routing (every block with score > tau)."""
+    routing (every block with score > tau), per head when per_head."""
     d = hsmla_desc()
     d.batch, d.grid_h, d.grid_w = batch, grid_h, grid_w
     d.channels, d.heads, d.head_dim = channels, heads, head_dim
@@ -158,7 +160,8 @@ def make_desc(*, batch, grid_h, grid_w, channels, heads, branches, block,
         d.branch_k[i] = k
     d.block, d.window, d.keep_blocks = block, window, keep_blocks
     d.dtype = {"f32": HSMLA_F32, "bf16": HSMLA_BF16}.get(dtype, dtype)
-    d.routing = HSMLA_ROUTE_TOPK if tau is None else HSMLA_ROUTE_THRESHOLD
+    d.routing = (HSMLA_ROUTE_TOPK if tau is None else
+                 HSMLA_ROUTE_HEAD_THRESHOLD if per_head else HSMLA_ROUTE_THRESHOLD)
     d.tau = 0.0 if tau is None else float(tau)
     return d
 
@@ -228,6 +231,14 @@ def hsmla_gate_threshold(desc, qkv_hat, gate_w, gate_b, scores_in, scores_out,
                                           _ptr(scores_in), _ptr(scores_out),
                                           _ptr(sel), _ptr(counts), _stream()),
            "hsmla_gate_threshold")
+
+
+def hsmla_gate_head_threshold(desc, qkv_hat, gate_w, gate_b, head_scores_in,
+                              head_scores_out, sel, counts, gate_dw=None):
+    _check(library().hsmla_gate_head_threshold(
+        ctypes.byref(desc), _ptr(qkv_hat), _ptr(gate_w), _ptr(gate_b), _ptr(gate_dw),
+        _ptr(head_scores_in), _ptr(head_scores_out), _ptr(sel), _ptr(counts),
+        _stream()), "hsmla_gate_head_threshold")
 
 
 def hsmla_sparse_softmax_counted(desc, qkv, qkv_hat, sel, counts, o):

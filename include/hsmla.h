@@ -48,10 +48,10 @@
  *   - Limits: head_dim must be 32; block <= 16; window >= block with
  *     (window - block) even; grid_h and grid_w multiples of block;
  *     0 <= keep_blocks <= number of blocks <= 8192; channels <= 2048;
- *     up to 3 depthwise branches of odd size <= 7; routing is
- *     HSMLA_ROUTE_TOPK or HSMLA_ROUTE_THRESHOLD (otherwise HSMLA_ERR_ARG),
- *     and tau is not NaN under threshold routing (keep_blocks is then
- *     unused but still range-checked).
+ *     up to 3 depthwise branches of odd size <= 7; routing is one of
+ *     hsmla_routing (otherwise HSMLA_ERR_ARG), and tau is not NaN under the
+ *     threshold routings (keep_blocks is then unused but still
+ *     range-checked).
  */
 #ifndef HSMLA_H_
 #define HSMLA_H_
@@ -79,8 +79,14 @@ typedef enum { HSMLA_F32 = 0, HSMLA_BF16 = 1 } hsmla_dtype;
 /* How blocks are routed to the softmax path (FT 3.2).  TOPK keeps the
  * keep_blocks highest scores per image; THRESHOLD keeps every block whose
  * score exceeds desc->tau (the routed set {b : M_b > tau}), a per-image count
- * known only on the device. */
-typedef enum { HSMLA_ROUTE_TOPK = 0, HSMLA_ROUTE_THRESHOLD = 1 } hsmla_routing;
+ * known only on the device; HEAD_THRESHOLD routes each head separately, by
+ * its own head score: head h of block b is refined when G_b^(h) > tau (FT 3.2
+ * per-head output routing), one list and count per (image, head). */
+typedef enum {
+  HSMLA_ROUTE_TOPK = 0,
+  HSMLA_ROUTE_THRESHOLD = 1,
+  HSMLA_ROUTE_HEAD_THRESHOLD = 2
+} hsmla_routing;
 
 /* Which entry point a workspace is sized for. */
 typedef enum {
@@ -100,7 +106,7 @@ typedef struct {
   int32_t keep_blocks;           /* refined blocks per image, 0..T (TOPK)  */
   int32_t dtype;                 /* hsmla_dtype                            */
   int32_t routing;               /* hsmla_routing                          */
-  float tau;                     /* threshold of HSMLA_ROUTE_THRESHOLD     */
+  float tau;                     /* threshold of the threshold routings    */
 } hsmla_desc;
 
 typedef struct {
@@ -129,8 +135,10 @@ typedef struct {
   float* kv;      /* [B][H][d][d] Z                                     */
   float* ksum;    /* [B][H][d]   D                                      */
   float* scores;  /* [B][T] gate scores M                               */
-  int32_t* sel;   /* [B][keep_blocks] (TOPK) or [B][T] (THRESHOLD)      */
-  int32_t* counts; /* THRESHOLD: [B] routed blocks per image; else NULL   */
+  int32_t* sel;   /* [B][keep_blocks] (TOPK), [B][T] (THRESHOLD) or     */
+                  /* [B][H][T] (HEAD_THRESHOLD)                         */
+  int32_t* counts; /* THRESHOLD: [B]; HEAD_THRESHOLD: [B][H]; else NULL  */
+  float* head_scores; /* HEAD_THRESHOLD: [B][T][H] G_b^(h); else NULL     */
   void* x1;       /* block only: [B][N][C] X + HSMLA(LN1(X))            */
 } hsmla_views;
 
@@ -195,6 +203,24 @@ hsmla_status hsmla_gate_threshold(const hsmla_desc* desc, const void* qkv_hat,
                                   float* scores_out, int32_t* sel,
                                   int32_t* counts, void* stream);
 
+/* Step 4 with per-head routing (FT 3.2 head-level score and per-head output
+ * routing equation); desc->routing must be HSMLA_ROUTE_HEAD_THRESHOLD
+ * (HSMLA_ERR_ARG otherwise).  With head_scores_in == NULL the head scores
+ * G [B][T][H] are pooled from qkv_hat (gate_dw as in hsmla_gate_select) and
+ * written to head_scores_out (required); with head_scores_in those float32
+ * scores are thresholded instead (qkv_hat and the gate weights may be NULL)
+ * and copied to head_scores_out if it is not NULL.  sel[b][h][0 ..
+ * counts[b][h]) receives, ascending, every block whose float32 G_b^(h) is
+ * strictly greater than desc->tau; entries beyond the count are left as
+ * they were.  sel [B][H][T], counts [B][H] int32, device memory. */
+hsmla_status hsmla_gate_head_threshold(const hsmla_desc* desc,
+                                       const void* qkv_hat,
+                                       const float* gate_w, const float* gate_b,
+                                       const void* gate_dw,
+                                       const float* head_scores_in,
+                                       float* head_scores_out, int32_t* sel,
+                                       int32_t* counts, void* stream);
+
 /* Step 5, local softmax refinement of the selected blocks with the two-path
  * residual (FT 3.3 local-neighbourhood, lin-local and residual equations;
  * scatter of the sparse residual, FT 3.6 stage 5).  For every block in sel
@@ -211,10 +237,12 @@ hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
 
 /* Step 5 over a device-counted selection (the threshold-routed set, FT 3.3
  * sparse residual over |B_tau| blocks): as hsmla_sparse_softmax, for the
- * first counts[b] entries of sel[b][0 .. T) (T = number of blocks), which
- * hsmla_gate_threshold writes.  desc->routing must be HSMLA_ROUTE_THRESHOLD
- * (HSMLA_ERR_ARG otherwise).  The launch covers T entries per image; work
- * items at or beyond counts[b] exit before reading sel. */
+ * lists hsmla_gate_threshold or hsmla_gate_head_threshold write.  With
+ * HSMLA_ROUTE_THRESHOLD every head of the first counts[b] blocks of
+ * sel[b][0 .. T) is refined; with HSMLA_ROUTE_HEAD_THRESHOLD head h of the
+ * first counts[b][h] blocks of sel[b][h][0 .. T).  Other routings:
+ * HSMLA_ERR_ARG.  The launch covers T entries per (image, head); work items
+ * at or beyond the count exit before reading sel. */
 hsmla_status hsmla_sparse_softmax_counted(const hsmla_desc* desc,
                                           const void* qkv, const void* qkv_hat,
                                           const int32_t* sel,
@@ -224,8 +252,9 @@ hsmla_status hsmla_sparse_softmax_counted(const hsmla_desc* desc,
 /* The whole module: y = HSMLA(x) = O W_o^T, steps 1-5 then the output
  * projection (FT 3.6 stages 1-5).  x, y [B][N][C]; ws sized for
  * HSMLA_OP_FORWARD; intermediates readable through hsmla_workspace_views.
- * desc->routing picks top-k or threshold selection (then the workspace
- * also holds the per-image counts, and sel rows are T wide). */
+ * desc->routing picks top-k, threshold or per-head threshold selection
+ * (the views then also give the counts, and for per-head routing the head
+ * scores). */
 hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
                            const void* x, void* y, void* ws, size_t ws_bytes,
                            void* stream);

@@ -94,8 +94,9 @@ def test_desc_validation(change, status):
 
 def test_routing_validation():
     d = _desc()
-    d.routing = 2
+    d.routing = 3
     assert _ws_bytes(d, H.HSMLA_OP_FORWARD)[0] == -7
+    assert _ws_bytes(_desc(tau=float("nan"), per_head=True), H.HSMLA_OP_FORWARD)[0] == -7
     assert _ws_bytes(_desc(tau=float("nan")), H.HSMLA_OP_FORWARD)[0] == -7
     # tau is not looked at under top-k routing
     d = _desc()
@@ -186,6 +187,15 @@ def test_stage_argument_errors():
                                     FAKE, FAKE, None) == -7
     assert lib.hsmla_sparse_softmax_counted(ctypes.byref(d), FAKE, FAKE, FAKE,
                                             FAKE, FAKE, None) == -7
+    dh = _desc(tau=0.5, per_head=True)
+    assert lib.hsmla_gate_threshold(ctypes.byref(dh), FAKE, FAKE, FAKE, None, None,
+                                    FAKE, FAKE, FAKE, None) == -7
+    assert lib.hsmla_gate_head_threshold(ctypes.byref(dt), FAKE, FAKE, FAKE, None,
+                                         None, FAKE, FAKE, FAKE, None) == -7
+    assert lib.hsmla_gate_head_threshold(ctypes.byref(dh), FAKE, FAKE, FAKE, None,
+                                         None, None, FAKE, FAKE, None) == -1
+    assert lib.hsmla_gate_head_threshold(ctypes.byref(dh), FAKE, FAKE, FAKE, None,
+                                         None, FAKE, FAKE + 2, FAKE, None) == -4
     assert lib.hsmla_gate_threshold(ctypes.byref(dt), FAKE, FAKE, FAKE, None, None, FAKE,
                                     FAKE, None, None) == -1
     assert lib.hsmla_gate_threshold(ctypes.byref(dt), FAKE, FAKE, FAKE, None, None, FAKE,
@@ -219,4 +229,12 @@ def test_workspace_views_layout():
                                              base, ctypes.byref(v)) == 0
     T = (16 // 4) * (32 // 4)
     assert v.counts - v.sel >= 2 * T * 4 and (v.counts - base) % 256 == 0
-    assert v.counts - base < need_t
+    assert v.counts - base < need_t and v.head_scores is None
+    # per head: sel [B][H][T], counts [B][H], head scores [B][T][H]
+    dh = _desc(tau=0.5, per_head=True)
+    st, need_h = _ws_bytes(dh, H.HSMLA_OP_FORWARD)
+    assert H.library().hsmla_workspace_views(ctypes.byref(dh), H.HSMLA_OP_FORWARD,
+                                             base, ctypes.byref(v)) == 0
+    assert v.counts - v.sel >= 2 * 2 * T * 4
+    assert v.head_scores - v.counts >= 2 * 2 * 4
+    assert v.head_scores + 2 * T * 2 * 4 - base <= need_h
