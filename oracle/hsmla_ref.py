@@ -384,7 +384,7 @@ def _tokens(r_lo, r_hi, c_lo, c_hi, grid_w):
 
 
 def refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads, block,
-                    window, rnd=_identity):
+                    window, rnd=_identity, weights=None):
     """O_i = O_lin_i + O_local_i - O_linloc_i for every token i of every
     selected block, every head; all other tokens keep O_lin_i.
 
@@ -401,6 +401,12 @@ def refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads, block,
     (full softmax attention, torch's reference SDPA on the CPU), and keep
     all with window = block (block-diagonal masked attention built
     independently).  ``rnd`` rounds the result (staged bfloat16 mode).
+
+    ``weights`` [B, T] (optional) scales the residual of block t by
+    weights[b, t]: O_i = O_lin_i + w (O_local_i - O_linloc_i), the
+    training-time differentiable mixture of FT 3.3 with w = M_b.  Pinned
+    by w = 1 (the hard routing), w = 0 (the linear path) and per-block
+    weights moving each block along its own residual.
     """
     qkv = np.asarray(qkv, np.float64)
     qkv_hat = np.asarray(qkv_hat, np.float64)
@@ -438,7 +444,11 @@ def refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads, block,
             o_linloc = _guarded_ratio(num, den)
 
             base = out[bi, qi].reshape(nq, heads, d)
-            out[bi, qi] = rnd((base + o_local - o_linloc).reshape(nq, C))
+            if weights is None:
+                out[bi, qi] = rnd((base + o_local - o_linloc).reshape(nq, C))
+            else:
+                w = float(np.asarray(weights)[bi, t])
+                out[bi, qi] = rnd((base + w * (o_local - o_linloc)).reshape(nq, C))
     return out
 
 
@@ -478,7 +488,7 @@ def refine_per_head(qkv, qkv_hat, o_lin, sel_heads, grid_h, grid_w, heads,
 
 def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
                  keep_blocks, staged=False, sel=None, scores_f32=True,
-                 tau=None, per_head=False):
+                 tau=None, per_head=False, soft=False):
     """Steps 1-5 of the module (everything before the output projection).
 
     Follows the five inference stages FT 3.6 lists: global linear path,
@@ -494,6 +504,9 @@ def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
     With ``per_head`` (and ``tau``) each head routes by its own score
     G_b^(h) > tau: "head_scores" [B, T, H], "sel" [B, H, T] and "counts"
     [B, H] are returned, and an injected ``sel`` has that shape.
+    With ``soft`` every block is refined and its residual is scaled by its
+    score M_b (FT 3.3 training-time differentiable mixture, forward only;
+    the scores enter as float32 when ``scores_f32``).
     """
     rnd = round_bf16 if staged else _identity
     C = x.shape[-1]
@@ -508,7 +521,13 @@ def hsmla_module(x, weights, *, grid_h, grid_w, heads, block, window,
     head_scores = None
     rank_on = scores.astype(np.float32) if scores_f32 else scores
     thr = (np.float32(tau) if scores_f32 else tau) if tau is not None else None
-    if per_head:
+    if soft:
+        T = scores.shape[1]
+        sel = np.tile(np.arange(T), (scores.shape[0], 1))
+        o = refine_selected(qkv, qkv_hat, o_lin, sel, grid_h, grid_w, heads,
+                            block, window, rnd=rnd,
+                            weights=rank_on.astype(np.float64))
+    elif per_head:
         assert tau is not None or sel is not None
         head_scores = gate_head_scores(qkv_hat, weights["gate_w"], weights["gate_b"],
                                        grid_h, grid_w, block, heads,

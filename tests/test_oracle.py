@@ -652,3 +652,55 @@ def test_per_head_routing_with_equal_heads_equals_threshold_routing():
         np.testing.assert_array_equal(p["counts"][:, h], a["counts"])
     assert 0 < a["counts"].sum() < wl.num_blocks * wl.batch
     np.testing.assert_allclose(p["o"], a["o"], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# training-time soft mixture
+# ---------------------------------------------------------------------------
+
+def test_soft_mixture_unit_weights_equal_refining_every_block():
+    wl, inp = _small_module_case(seed=7, heads=2)
+    r = O.hsmla_module(inp["x"], inp, **wl.kwargs())
+    T = wl.num_blocks
+    allb = np.tile(np.arange(T), (wl.batch, 1))
+    hard = O.refine_selected(r["qkv"], r["qkv_hat"], r["o_lin"], allb, wl.grid_h,
+                             wl.grid_w, wl.heads, wl.block, wl.window)
+    ones = O.refine_selected(r["qkv"], r["qkv_hat"], r["o_lin"], allb, wl.grid_h,
+                             wl.grid_w, wl.heads, wl.block, wl.window,
+                             weights=np.ones((wl.batch, T)))
+    zeros = O.refine_selected(r["qkv"], r["qkv_hat"], r["o_lin"], allb, wl.grid_h,
+                              wl.grid_w, wl.heads, wl.block, wl.window,
+                              weights=np.zeros((wl.batch, T)))
+    np.testing.assert_allclose(ones, hard, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(zeros, r["o_lin"], rtol=0, atol=0)
+
+
+def test_soft_mixture_moves_each_block_along_its_own_residual():
+    """Block t's tokens end at O_lin + w_t (hard - O_lin): the weight scales
+    only the residual, block by block (checked against the hard result)."""
+    wl, inp = _small_module_case(seed=8, heads=2)
+    r = O.hsmla_module(inp["x"], inp, **wl.kwargs())
+    T = wl.num_blocks
+    allb = np.tile(np.arange(T), (wl.batch, 1))
+    w = _rng(3).uniform(0, 1, size=(wl.batch, T))
+    hard = O.refine_selected(r["qkv"], r["qkv_hat"], r["o_lin"], allb, wl.grid_h,
+                             wl.grid_w, wl.heads, wl.block, wl.window)
+    soft = O.refine_selected(r["qkv"], r["qkv_hat"], r["o_lin"], allb, wl.grid_h,
+                             wl.grid_w, wl.heads, wl.block, wl.window, weights=w)
+    nbc = wl.grid_w // wl.block
+    ys, xs = np.divmod(np.arange(wl.tokens), wl.grid_w)
+    tblk = (ys // wl.block) * nbc + xs // wl.block
+    want = r["o_lin"] + w[:, tblk][..., None] * (hard - r["o_lin"])
+    np.testing.assert_allclose(soft, want, rtol=1e-12, atol=1e-12)
+
+
+def test_soft_module_uses_the_block_scores_as_weights():
+    wl, inp = _small_module_case(seed=9, heads=2)
+    s = O.hsmla_module(inp["x"], inp, soft=True, **wl.kwargs())
+    T = wl.num_blocks
+    allb = np.tile(np.arange(T), (wl.batch, 1))
+    want = O.refine_selected(s["qkv"], s["qkv_hat"], s["o_lin"], allb, wl.grid_h,
+                             wl.grid_w, wl.heads, wl.block, wl.window,
+                             weights=s["scores"].astype(np.float32).astype(np.float64))
+    np.testing.assert_allclose(s["o"], want, rtol=0, atol=0)
+    assert np.all((s["scores"] > 0) & (s["scores"] < 1))
