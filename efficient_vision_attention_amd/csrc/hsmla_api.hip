@@ -37,6 +37,7 @@ struct Dims {
   bool bf;
   bool thr;   // threshold routing (block or per head)
   bool ph;    // per-head routing
+  bool soft;  // every block, residual scaled by its score
   float tau;
 };
 
@@ -68,9 +69,11 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
   if (T > kMaxBlocks) return HSMLA_ERR_SHAPE;
   if (d->keep_blocks < 0 || d->keep_blocks > T) return HSMLA_ERR_SHAPE;
   if (d->routing != HSMLA_ROUTE_TOPK && d->routing != HSMLA_ROUTE_THRESHOLD &&
-      d->routing != HSMLA_ROUTE_HEAD_THRESHOLD)
+      d->routing != HSMLA_ROUTE_HEAD_THRESHOLD && d->routing != HSMLA_ROUTE_SOFT)
     return HSMLA_ERR_ARG;
-  if (d->routing != HSMLA_ROUTE_TOPK && isnan(d->tau)) return HSMLA_ERR_ARG;
+  if ((d->routing == HSMLA_ROUTE_THRESHOLD ||
+       d->routing == HSMLA_ROUTE_HEAD_THRESHOLD) && isnan(d->tau))
+    return HSMLA_ERR_ARG;
   const int64_t N = (int64_t)d->grid_h * d->grid_w;
   // every element index must fit a 32-bit grid dimension and size_t math
   if (N * d->batch * 4 * (int64_t)d->channels > ((int64_t)1 << 40)) return HSMLA_ERR_SHAPE;
@@ -89,10 +92,15 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
     out->kmax = kmax;
     out->P = (size_t)N * d->batch;
     out->bf = d->dtype == HSMLA_BF16;
-    out->thr = d->routing != HSMLA_ROUTE_TOPK;
+    out->thr = d->routing == HSMLA_ROUTE_THRESHOLD ||
+               d->routing == HSMLA_ROUTE_HEAD_THRESHOLD;
     out->ph = d->routing == HSMLA_ROUTE_HEAD_THRESHOLD;
+    out->soft = d->routing == HSMLA_ROUTE_SOFT;
     out->tau = d->tau;
-    out->sw = out->ph ? d->heads * (int)T : out->thr ? (int)T : d->keep_blocks;
+    out->sw = out->ph   ? d->heads * (int)T
+              : out->thr  ? (int)T
+              : out->soft ? 0
+                          : d->keep_blocks;
     out->nc = out->ph ? d->batch * d->heads : d->batch;
     out->e = out->bf ? 2 : 4;
   }
@@ -242,6 +250,13 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
   HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b,
                                       w->gate_dw, scores, hscores, D.B, D.gh,
                                       D.gw, D.H, D.Bs, s));
+  if (D.soft) {
+    r.mark("sparse_softmax");
+    HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, nullptr, nullptr, scores, o,
+                                   D.B, D.gh, D.gw, D.H, D.Bs, D.w, D.T,
+                                   sel_layout(D), s));
+    return HSMLA_OK;
+  }
   if (D.ph) {
     r.mark("threshold_heads");
     HSMLA_TRY(hsmla::launch_threshold_heads(hscores, nullptr, sel, counts, D.B,
@@ -255,8 +270,8 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
     HSMLA_TRY(hsmla::launch_topk(scores, nullptr, sel, D.B, D.T, D.k, s));
   }
   r.mark("sparse_softmax");
-  HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, sel, counts, o, D.B, D.gh,
-                                 D.gw, D.H, D.Bs, D.w, D.thr ? D.T : D.k,
+  HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, sel, counts, nullptr, o, D.B,
+                                 D.gh, D.gw, D.H, D.Bs, D.w, D.thr ? D.T : D.k,
                                  sel_layout(D), s));
   return HSMLA_OK;
 }
@@ -357,7 +372,7 @@ hsmla_status hsmla_gate_select(const hsmla_desc* desc, const void* qkv_hat,
   Dims D;
   const hsmla_status st = check_desc(desc, &D);
   if (st != HSMLA_OK) return st;
-  if (D.thr) return HSMLA_ERR_ARG;
+  if (D.thr || D.soft) return HSMLA_ERR_ARG;
   if (D.k > 0 && !sel) return HSMLA_ERR_NULL;
   if (!scores_in && (!qkv_hat || !gate_w || !gate_b || !scores_out))
     return HSMLA_ERR_NULL;
@@ -444,14 +459,32 @@ hsmla_status hsmla_sparse_softmax(const hsmla_desc* desc, const void* qkv,
   Dims D;
   const hsmla_status st = check_desc(desc, &D);
   if (st != HSMLA_OK) return st;
-  if (D.thr) return HSMLA_ERR_ARG;
+  if (D.thr || D.soft) return HSMLA_ERR_ARG;
   if (!qkv || !qkv_hat || !o || (D.k > 0 && !sel)) return HSMLA_ERR_NULL;
   if (!aligned(qkv, 16) || !aligned(qkv_hat, 16) || !aligned(o, 16) ||
       (sel && !aligned(sel, 4)))
     return HSMLA_ERR_ALIGN;
-  return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, nullptr, o,
-                                         D.B, D.gh, D.gw, D.H, D.Bs, D.w, D.k,
-                                         sel_layout(D),
+  return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, nullptr,
+                                         nullptr, o, D.B, D.gh, D.gw, D.H, D.Bs,
+                                         D.w, D.k, sel_layout(D),
+                                         static_cast<hipStream_t>(stream)));
+}
+
+hsmla_status hsmla_sparse_softmax_weighted(const hsmla_desc* desc,
+                                           const void* qkv, const void* qkv_hat,
+                                           const float* weights, void* o,
+                                           void* stream) {
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!D.soft) return HSMLA_ERR_ARG;
+  if (!qkv || !qkv_hat || !o || !weights) return HSMLA_ERR_NULL;
+  if (!aligned(qkv, 16) || !aligned(qkv_hat, 16) || !aligned(o, 16) ||
+      !aligned(weights, 4))
+    return HSMLA_ERR_ALIGN;
+  return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, nullptr, nullptr,
+                                         weights, o, D.B, D.gh, D.gw, D.H, D.Bs,
+                                         D.w, D.T, sel_layout(D),
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -468,9 +501,9 @@ hsmla_status hsmla_sparse_softmax_counted(const hsmla_desc* desc,
   if (!aligned(qkv, 16) || !aligned(qkv_hat, 16) || !aligned(o, 16) ||
       !aligned(sel, 4) || !aligned(counts, 4))
     return HSMLA_ERR_ALIGN;
-  return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, counts, o,
-                                         D.B, D.gh, D.gw, D.H, D.Bs, D.w, D.T,
-                                         sel_layout(D),
+  return hip_status(hsmla::launch_sparse(D.bf, qkv, qkv_hat, sel, counts,
+                                         nullptr, o, D.B, D.gh, D.gw, D.H, D.Bs,
+                                         D.w, D.T, sel_layout(D),
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -6,6 +6,10 @@
 //   O_linloc_i  = sum_{j in W} (phi(q^_i).phi(k^_j)) v^_j / sum_{j in W} phi(q^_i).phi(k^_j)
 //   O_i        <- O_lin_i + O_local_i - O_linloc_i
 //
+// With per-block weights w (the training-time differentiable mixture of
+// FT 3.3, w = M_b) every block is refined and the residual is scaled:
+//   O_i        <- O_lin_i + w_b (O_local_i - O_linloc_i).
+//
 // W is the window x window square centred on the block, clipped to the grid.
 // The lin-local ratio is evaluated in its pairwise form, which equals
 // phi(q^) Z_W / phi(q^) D_W by associativity.
@@ -25,8 +29,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void sparse_valu_kernel(
     const T* __restrict__ qkv, const T* __restrict__ qkvh,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ counts,
-    T* __restrict__ o, int gh, int gw, int heads, int block, int window,
-    SelLayout lay) {
+    const float* __restrict__ wts, T* __restrict__ o, int gh, int gw,
+    int heads, int block, int window, SelLayout lay) {
   __shared__ float ks[kKT][kD];
   __shared__ float vs[kKT][kD];
   __shared__ float fks[kKT][kD];
@@ -35,7 +39,9 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
   const int C = heads * kD, C3 = 3 * C;
   if (counts && (int)blockIdx.x >= counts[b * lay.cnt_b + h * lay.cnt_h])
     return;  // beyond the routed set
-  const int t = sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + blockIdx.x];
+  // without a list every block is refined (entry x is block x)
+  const int t = sel ? sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + blockIdx.x]
+                    : (int)blockIdx.x;
   const int nbc = gw / block;
   if (t < 0 || t >= (gh / block) * nbc) return;  // invalid entry: no access
   const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
@@ -101,10 +107,12 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
   T* orow = o + (img + qn) * C + h * kD;
   const float inv_l = 1.f / l;
   const float inv_den = den > 0.f ? 1.f / den : 0.f;
+  const float w = wts ? wts[(size_t)b * (gh / block) * nbc + t] : 1.f;
 #pragma unroll
   for (int j = 0; j < kD; ++j) {
     const float lin = den > 0.f ? num[j] * inv_den : 0.f;
-    const float v = to_f32(orow[j]) + acc[j] * inv_l - lin;
+    const float v = wts ? fmaf(w, acc[j] * inv_l - lin, to_f32(orow[j]))
+                        : to_f32(orow[j]) + acc[j] * inv_l - lin;
     orow[j] = from_f32<T>(v);
   }
 }
@@ -149,8 +157,8 @@ template <int NQT>
 __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ qkvh,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ counts,
-    bf16* __restrict__ o, int gh, int gw, int heads, int block, int window,
-    SelLayout lay) {
+    const float* __restrict__ wts, bf16* __restrict__ o, int gh, int gw,
+    int heads, int block, int window, SelLayout lay) {
   constexpr int NT = 64 * 2 * NQT;
   __shared__ SparseTile tiles[2];
   __shared__ float linloc[NQT * 32][kD + 1];
@@ -159,7 +167,9 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
   const int C = heads * kD, C3 = 3 * C;
   if (counts && (int)blockIdx.x >= counts[b * lay.cnt_b + h * lay.cnt_h])
     return;  // beyond the routed set
-  const int t = sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + blockIdx.x];
+  // without a list every block is refined (entry x is block x)
+  const int t = sel ? sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + blockIdx.x]
+                    : (int)blockIdx.x;
   const int nbc = gw / block;
   if (t < 0 || t >= (gh / block) * nbc) return;  // invalid entry: no access
   const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
@@ -336,6 +346,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
   __syncthreads();
   if (path == 0 && q_ok) {
     const float inv = 1.f / total;
+    const float w = wts ? wts[(size_t)b * (gh / block) * nbc + t] : 1.f;
     bf16* orow = o + (img + qn) * C + h * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -346,8 +357,14 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
       v[1] = __uint_as_float(prev.x & 0xffff0000u);
       v[2] = __uint_as_float(prev.y << 16);
       v[3] = __uint_as_float(prev.y & 0xffff0000u);
+      if (wts) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] += oacc[4 * j + i] * inv - linloc[ql][ch + i];
+        for (int i = 0; i < 4; ++i)
+          v[i] = fmaf(w, oacc[4 * j + i] * inv - linloc[ql][ch + i], v[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += oacc[4 * j + i] * inv - linloc[ql][ch + i];
+      }
       uint2 outv;
       outv.x = pack_bf16x2(v[0], v[1]);
       outv.y = pack_bf16x2(v[2], v[3]);
@@ -358,12 +375,12 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
 
 template <typename T>
 hipError_t run(const void* qkv, const void* qkvh, const int32_t* sel,
-               const int32_t* counts, void* o, int batch, int gh, int gw,
-               int heads, int block, int window, int entries, SelLayout lay,
-               hipStream_t s) {
+               const int32_t* counts, const float* wts, void* o, int batch,
+               int gh, int gw, int heads, int block, int window, int entries,
+               SelLayout lay, hipStream_t s) {
   dim3 grid(entries, batch, heads);
   sparse_valu_kernel<T><<<grid, block * block, 0, s>>>(
-      static_cast<const T*>(qkv), static_cast<const T*>(qkvh), sel, counts,
+      static_cast<const T*>(qkv), static_cast<const T*>(qkvh), sel, counts, wts,
       static_cast<T*>(o), gh, gw, heads, block, window, lay);
   return hipGetLastError();
 }
@@ -371,9 +388,10 @@ hipError_t run(const void* qkv, const void* qkvh, const int32_t* sel,
 }  // namespace
 
 hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
-                         const int32_t* sel, const int32_t* counts, void* o,
-                         int batch, int gh, int gw, int heads, int block,
-                         int window, int entries, SelLayout lay, hipStream_t s) {
+                         const int32_t* sel, const int32_t* counts,
+                         const float* wts, void* o, int batch, int gh, int gw,
+                         int heads, int block, int window, int entries,
+                         SelLayout lay, hipStream_t s) {
   if (entries == 0) return hipSuccess;
   const int nqt = (block * block + 31) / 32;
   if (bf && nqt <= 4) {
@@ -382,16 +400,16 @@ hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
     const bf16* qh = static_cast<const bf16*>(qkv_hat);
     bf16* out = static_cast<bf16*>(o);
     switch (nqt) {
-      case 1: sparse_mfma_kernel<1><<<grid, 128, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, lay); break;
-      case 2: sparse_mfma_kernel<2><<<grid, 256, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, lay); break;
-      case 3: sparse_mfma_kernel<3><<<grid, 384, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, lay); break;
-      default: sparse_mfma_kernel<4><<<grid, 512, 0, s>>>(q, qh, sel, counts, out, gh, gw, heads, block, window, lay); break;
+      case 1: sparse_mfma_kernel<1><<<grid, 128, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay); break;
+      case 2: sparse_mfma_kernel<2><<<grid, 256, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay); break;
+      case 3: sparse_mfma_kernel<3><<<grid, 384, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay); break;
+      default: sparse_mfma_kernel<4><<<grid, 512, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay); break;
     }
     return hipGetLastError();
   }
-  return bf ? run<bf16>(qkv, qkv_hat, sel, counts, o, batch, gh, gw, heads,
+  return bf ? run<bf16>(qkv, qkv_hat, sel, counts, wts, o, batch, gh, gw, heads,
                         block, window, entries, lay, s)
-            : run<float>(qkv, qkv_hat, sel, counts, o, batch, gh, gw, heads,
+            : run<float>(qkv, qkv_hat, sel, counts, wts, o, batch, gh, gw, heads,
                          block, window, entries, lay, s);
 }
 

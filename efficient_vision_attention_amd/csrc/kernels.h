@@ -75,11 +75,14 @@ struct SelLayout {
 };
 
 // Windowed softmax refinement of the selected blocks, in place on o; the
-// grid covers `entries` list entries per (image, head).
+// grid covers `entries` list entries per (image, head).  sel == nullptr
+// refines every block (entry x = block x); wts != nullptr ([batch][blocks])
+// scales each block's residual by its weight.
 hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
-                         const int32_t* sel, const int32_t* counts, void* o,
-                         int batch, int gh, int gw, int heads, int block,
-                         int window, int entries, SelLayout lay, hipStream_t s);
+                         const int32_t* sel, const int32_t* counts,
+                         const float* wts, void* o, int batch, int gh, int gw,
+                         int heads, int block, int window, int entries,
+                         SelLayout lay, hipStream_t s);
 
 // y = LN(x) . gamma + beta over the channel dimension.
 hipError_t launch_layernorm(bool bf, const void* x, const float* gamma,

@@ -33,7 +33,8 @@ class DeviceModel:
 
     shape: mapping with batch, grid_h, grid_w, channels, heads, branches,
     block, window, keep_blocks, dtype, and optionally tau (threshold
-    routing when given) and per_head (route each head by its own score).  weights: dict of float64 numpy
+    routing when given), per_head (route each head by its own score) and
+    soft (the training-time mixture over every block).  weights: dict of float64 numpy
     arrays (w_qkv, w_o, dw list, gate_w, gate_b, optionally gate_dw, and
     for the block ln1_g,
     ln1_b, ln2_g, ln2_b, w1, dw_ffn, w2), dense weights given [in][out]
@@ -86,9 +87,10 @@ class DeviceModel:
         s = self.shape
         B, N, C, Hh = s["batch"], s["grid_h"] * s["grid_w"], s["channels"], s["heads"]
         T = (s["grid_h"] // s["block"]) * (s["grid_w"] // s["block"])
-        thr = s.get("tau") is not None
+        soft = s.get("soft", False)
+        thr = s.get("tau") is not None and not soft
         ph = thr and s.get("per_head", False)
-        k = Hh * T if ph else T if thr else s["keep_blocks"]
+        k = 0 if soft else Hh * T if ph else T if thr else s["keep_blocks"]
         off = H.hsmla_workspace_views(self.desc, op, ws)
         adt = TORCH_DTYPE[self.dtype]
         esz = torch.tensor([], dtype=adt).element_size()

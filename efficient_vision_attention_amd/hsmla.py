@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhsmla.s
 
 HSMLA_F32, HSMLA_BF16 = 0, 1
 HSMLA_OP_QKV, HSMLA_OP_LINEAR, HSMLA_OP_FORWARD, HSMLA_OP_BLOCK = 0, 1, 2, 3
-HSMLA_ROUTE_TOPK, HSMLA_ROUTE_THRESHOLD, HSMLA_ROUTE_HEAD_THRESHOLD = 0, 1, 2
+HSMLA_ROUTE_TOPK, HSMLA_ROUTE_THRESHOLD, HSMLA_ROUTE_HEAD_THRESHOLD, HSMLA_ROUTE_SOFT = 0, 1, 2, 3
 
 # Every symbol include/hsmla.h declares.
 EXPORTED = (
@@ -31,6 +31,7 @@ EXPORTED = (
     "hsmla_gate_head_threshold",
     "hsmla_sparse_softmax",
     "hsmla_sparse_softmax_counted",
+    "hsmla_sparse_softmax_weighted",
     "hsmla_forward",
     "hsmla_block_forward",
     "hsmla_forward_timed",
@@ -109,6 +110,7 @@ def library():
             "hsmla_gate_head_threshold": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP, VP],
             "hsmla_sparse_softmax": [P(hsmla_desc), VP, VP, VP, VP, VP],
             "hsmla_sparse_softmax_counted": [P(hsmla_desc), VP, VP, VP, VP, VP, VP],
+            "hsmla_sparse_softmax_weighted": [P(hsmla_desc), VP, VP, VP, VP, VP],
             "hsmla_forward": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, SZ, VP],
             "hsmla_block_forward": [P(hsmla_desc), P(hsmla_weights), P(hsmla_ffn_weights),
                                     VP, VP, VP, SZ, VP],
@@ -149,9 +151,11 @@ def _stream():
 
 
 def make_desc(*, batch, grid_h, grid_w, channels, heads, branches, block,
-              window, keep_blocks, dtype, head_dim=32, tau=None, per_head=False):
+              window, keep_blocks, dtype, head_dim=32, tau=None, per_head=False,
+              soft=False):
     """tau=None: top-k routing (keep_blocks per image); a number: threshold
-    routing (every block with score > tau), per head when per_head."""
+    routing (every block with score > tau), per head when per_head; soft:
+    the training-time mixture (every block, residual scaled by its score)."""
     d = hsmla_desc()
     d.batch, d.grid_h, d.grid_w = batch, grid_h, grid_w
     d.channels, d.heads, d.head_dim = channels, heads, head_dim
@@ -160,7 +164,7 @@ def make_desc(*, batch, grid_h, grid_w, channels, heads, branches, block,
         d.branch_k[i] = k
     d.block, d.window, d.keep_blocks = block, window, keep_blocks
     d.dtype = {"f32": HSMLA_F32, "bf16": HSMLA_BF16}.get(dtype, dtype)
-    d.routing = (HSMLA_ROUTE_TOPK if tau is None else
+    d.routing = (HSMLA_ROUTE_SOFT if soft else HSMLA_ROUTE_TOPK if tau is None else
                  HSMLA_ROUTE_HEAD_THRESHOLD if per_head else HSMLA_ROUTE_THRESHOLD)
     d.tau = 0.0 if tau is None else float(tau)
     return d
@@ -253,6 +257,13 @@ def hsmla_sparse_softmax(desc, qkv, qkv_hat, sel, o):
                                           _ptr(qkv_hat), _ptr(sel), _ptr(o),
                                           _stream()),
            "hsmla_sparse_softmax")
+
+
+def hsmla_sparse_softmax_weighted(desc, qkv, qkv_hat, weights, o):
+    _check(library().hsmla_sparse_softmax_weighted(ctypes.byref(desc), _ptr(qkv),
+                                                   _ptr(qkv_hat), _ptr(weights),
+                                                   _ptr(o), _stream()),
+           "hsmla_sparse_softmax_weighted")
 
 
 def hsmla_forward(desc, weights, x, y, ws):

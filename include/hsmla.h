@@ -81,11 +81,15 @@ typedef enum { HSMLA_F32 = 0, HSMLA_BF16 = 1 } hsmla_dtype;
  * score exceeds desc->tau (the routed set {b : M_b > tau}), a per-image count
  * known only on the device; HEAD_THRESHOLD routes each head separately, by
  * its own head score: head h of block b is refined when G_b^(h) > tau (FT 3.2
- * per-head output routing), one list and count per (image, head). */
+ * per-head output routing), one list and count per (image, head).  SOFT is
+ * the training-time differentiable mixture of FT 3.3, forward only: every
+ * block is refined and its residual is scaled by its score,
+ * O = O_lin + M_b (O_local - O_linloc). */
 typedef enum {
   HSMLA_ROUTE_TOPK = 0,
   HSMLA_ROUTE_THRESHOLD = 1,
-  HSMLA_ROUTE_HEAD_THRESHOLD = 2
+  HSMLA_ROUTE_HEAD_THRESHOLD = 2,
+  HSMLA_ROUTE_SOFT = 3
 } hsmla_routing;
 
 /* Which entry point a workspace is sized for. */
@@ -136,7 +140,7 @@ typedef struct {
   float* ksum;    /* [B][H][d]   D                                      */
   float* scores;  /* [B][T] gate scores M                               */
   int32_t* sel;   /* [B][keep_blocks] (TOPK), [B][T] (THRESHOLD) or     */
-                  /* [B][H][T] (HEAD_THRESHOLD)                         */
+                  /* [B][H][T] (HEAD_THRESHOLD); unused under SOFT      */
   int32_t* counts; /* THRESHOLD: [B]; HEAD_THRESHOLD: [B][H]; else NULL  */
   float* head_scores; /* HEAD_THRESHOLD: [B][T][H] G_b^(h); else NULL     */
   void* x1;       /* block only: [B][N][C] X + HSMLA(LN1(X))            */
@@ -249,12 +253,23 @@ hsmla_status hsmla_sparse_softmax_counted(const hsmla_desc* desc,
                                           const int32_t* counts, void* o,
                                           void* stream);
 
+/* Step 5 of the training-time mixture (FT 3.3 differentiable mixture
+ * equation, forward only): every block of every image is refined and its
+ * residual is scaled by weights[b][t] (float32, [B][T]; the block scores M
+ * in the forward pass): o_i <- o_i + w (softmax part - lin-local part), as
+ * in hsmla_sparse_softmax otherwise.  desc->routing must be
+ * HSMLA_ROUTE_SOFT (HSMLA_ERR_ARG otherwise). */
+hsmla_status hsmla_sparse_softmax_weighted(const hsmla_desc* desc,
+                                           const void* qkv, const void* qkv_hat,
+                                           const float* weights, void* o,
+                                           void* stream);
+
 /* The whole module: y = HSMLA(x) = O W_o^T, steps 1-5 then the output
  * projection (FT 3.6 stages 1-5).  x, y [B][N][C]; ws sized for
  * HSMLA_OP_FORWARD; intermediates readable through hsmla_workspace_views.
- * desc->routing picks top-k, threshold or per-head threshold selection
- * (the views then also give the counts, and for per-head routing the head
- * scores). */
+ * desc->routing picks top-k, threshold, per-head threshold selection or
+ * the soft mixture (the views then also give the counts, and for per-head
+ * routing the head scores). */
 hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
                            const void* x, void* y, void* ws, size_t ws_bytes,
                            void* stream);

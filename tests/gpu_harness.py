@@ -23,12 +23,13 @@ def announce(msg: str):
     sys.stdout.flush()
 
 
-def shape_of(wl: Workload, keep_blocks=None, tau=None, per_head=False) -> dict:
+def shape_of(wl: Workload, keep_blocks=None, tau=None, per_head=False,
+             soft=False) -> dict:
     return dict(batch=wl.batch, grid_h=wl.grid_h, grid_w=wl.grid_w,
                 channels=wl.channels, heads=wl.heads, branches=wl.branches,
                 block=wl.block, window=wl.window,
                 keep_blocks=wl.keep_blocks if keep_blocks is None else keep_blocks,
-                dtype=wl.dtype, tau=tau, per_head=per_head)
+                dtype=wl.dtype, tau=tau, per_head=per_head, soft=soft)
 
 
 def assert_close(gpu, ref, dtype, what=""):
@@ -124,14 +125,14 @@ class Run:
     tau set, the model routes by threshold and the readback holds counts."""
 
     def __init__(self, wl: Workload, inputs: dict, keep_blocks=None, tau=None,
-                 per_head=False):
+                 per_head=False, soft=False):
         self.wl = wl
         self.inputs = inputs
-        self.model = DeviceModel(shape_of(wl, keep_blocks, tau, per_head), inputs)
+        self.model = DeviceModel(shape_of(wl, keep_blocks, tau, per_head, soft), inputs)
         self.desc = self.model.desc
         self.tau = tau
-        self.k = (self.model.shape["keep_blocks"] if tau is None else
-                  f"tau={tau:.6g}{' per head' if per_head else ''}")
+        self.k = ("soft" if soft else self.model.shape["keep_blocks"] if tau is None
+                  else f"tau={tau:.6g}{' per head' if per_head else ''}")
         self.x = to_device(inputs["x"], wl.dtype)
 
     def forward(self):

@@ -94,8 +94,12 @@ def test_desc_validation(change, status):
 
 def test_routing_validation():
     d = _desc()
-    d.routing = 3
+    d.routing = 4
     assert _ws_bytes(d, H.HSMLA_OP_FORWARD)[0] == -7
+    # the soft mixture does not look at tau
+    d = _desc(soft=True)
+    d.tau = float("nan")
+    assert _ws_bytes(d, H.HSMLA_OP_FORWARD)[0] == 0
     assert _ws_bytes(_desc(tau=float("nan"), per_head=True), H.HSMLA_OP_FORWARD)[0] == -7
     assert _ws_bytes(_desc(tau=float("nan")), H.HSMLA_OP_FORWARD)[0] == -7
     # tau is not looked at under top-k routing
@@ -187,6 +191,16 @@ def test_stage_argument_errors():
                                     FAKE, FAKE, None) == -7
     assert lib.hsmla_sparse_softmax_counted(ctypes.byref(d), FAKE, FAKE, FAKE,
                                             FAKE, FAKE, None) == -7
+    ds = _desc(soft=True)
+    assert lib.hsmla_sparse_softmax_weighted(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE,
+                                             None) == -7
+    assert lib.hsmla_sparse_softmax_weighted(ctypes.byref(ds), FAKE, FAKE, None, FAKE,
+                                             None) == -1
+    assert lib.hsmla_sparse_softmax_weighted(ctypes.byref(ds), FAKE, FAKE, FAKE + 2,
+                                             FAKE, None) == -4
+    assert lib.hsmla_sparse_softmax(ctypes.byref(ds), FAKE, FAKE, FAKE, FAKE, None) == -7
+    assert lib.hsmla_gate_select(ctypes.byref(ds), FAKE, FAKE, FAKE, None, None, FAKE,
+                                 FAKE, None) == -7
     dh = _desc(tau=0.5, per_head=True)
     assert lib.hsmla_gate_threshold(ctypes.byref(dh), FAKE, FAKE, FAKE, None, None,
                                     FAKE, FAKE, FAKE, None) == -7
