@@ -10,9 +10,9 @@ batch, i.e. every kernel of the path.  Inputs are seeded synthetic data
 
 Prints one JSON line: tokens/s, the per-kernel breakdown from HIP events
 recorded between the launches of the step, the roofline of the dominant
-kernel, a keep-ratio sweep with two threshold-routing points and the
-exact-gate / three-branch variant, and the CPU oracle timed on a bounded
-crop.
+kernel, a keep-ratio sweep with two threshold-routing points, per-head
+routing, the training-time mixture forward and the exact-gate / three-branch
+variant, and the CPU oracle timed on a bounded crop.
 
     python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
 """
@@ -253,11 +253,11 @@ def main():
     inp = make_inputs(base)
     x = to_device(inp["x"], base.dtype)
 
-    def shape(wl, tau=None):
+    def shape(wl, tau=None, per_head=False, soft=False):
         return dict(batch=wl.batch, grid_h=wl.grid_h, grid_w=wl.grid_w,
                     channels=wl.channels, heads=wl.heads, branches=wl.branches,
                     block=wl.block, window=wl.window, keep_blocks=wl.keep_blocks,
-                    dtype=wl.dtype, tau=tau)
+                    dtype=wl.dtype, tau=tau, per_head=per_head, soft=soft)
 
     def time_steps(model, fn, steps, warmup):
         ws = model.workspace(H.HSMLA_OP_BLOCK)
@@ -347,6 +347,38 @@ def main():
                               module_ms=round(ms_m, 4)))
             del m
 
+        # per-head routing (each head by its own score), tau between two
+        # adjacent head scores of a first per-head run at the 0.7 quantile
+        m = DeviceModel(shape(base, tau=0.5, per_head=True), inp)
+        _, ws_p = time_steps(m, block_step, 1, 0)
+        hs = m.views(H.HSMLA_OP_BLOCK, ws_p)["head_scores"].cpu().numpy()
+        uniq = np.unique(hs.astype(np.float32))
+        i = min(int(0.7 * (uniq.size - 1)), uniq.size - 2)
+        tau = float(np.float32((np.float64(uniq[i]) + np.float64(uniq[i + 1])) / 2))
+        del m
+        m = DeviceModel(shape(base, tau=tau, per_head=True), inp)
+        ms_b, ws_t = time_steps(m, block_step, max(10, args.steps // 2), 3)
+        routed = int(m.views(H.HSMLA_OP_BLOCK, ws_t)["counts"].sum().item())
+        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
+        sweep.append(dict(routing="threshold_per_head", tau=tau,
+                          routed_fraction=round(routed / (base.batch * base.num_blocks
+                                                          * base.heads), 4),
+                          block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
+                          block_ms=round(ms_b, 4),
+                          module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
+                          module_ms=round(ms_m, 4)))
+        del m
+        # the training-time mixture forward: every block refined, residual
+        # scaled by its score
+        m = DeviceModel(shape(base, soft=True), inp)
+        ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 3)
+        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
+        sweep.append(dict(routing="soft_mixture", routed_fraction=1.0,
+                          block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
+                          block_ms=round(ms_b, 4),
+                          module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
+                          module_ms=round(ms_m, 4)))
+        del m
         # the gate's depthwise 3x3 (FT 3.2 head-level score) with the
         # identity + 3x3 + 5x5 + 7x7 branches, top-k at the base keep ratio
         wl = scaled(base, branches=(3, 5, 7), gate_conv=True)
