@@ -9,12 +9,14 @@
 // Selection, written in ascending block order -- the compacted tile list the
 // refinement kernel runs over (FT 3.6 stage 3) -- either
 //   top-k:     the keep largest M_t per image, equal scores to the lower block
-//              index (the count is fixed, so the grid size is known on the
-//              host), or
+//              index, by a bitonic sort in LDS (the count is fixed, so the
+//              grid size is known on the host), or
 //   threshold: every block with M_t > tau (FT 3.2 gating equation); the
 //              per-image count goes to device memory, or
 //   per head:  for each head h the blocks with G^(h)_t > tau (FT 3.2 per-head
 //              output routing), one list and count per (image, head).
+#include <math.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -234,42 +236,67 @@ __device__ int compact_ascending(Pred keep, int n, int32_t* __restrict__ out) {
   return base_all;
 }
 
-// grid (batch), 1024 threads.  rank(t) = #{u : s_u > s_t or (s_u == s_t and
-// u < t)}; block t is kept iff rank(t) < keep.  P = 1024 / T threads share
-// one candidate (each scans a strided part of the scores, combined by a
-// wave reduction).  The slot of a kept block in the output is the number of
-// kept blocks below it, formed with wave ballots and a prefix over the 16
-// wave totals.  Exact and order-independent.
+// grid (batch), 1024 threads.  The scores of one image are sorted in LDS by
+// a bitonic network on one 64-bit key per block: the score mapped to an
+// order-preserving unsigned integer (-0 taken as +0) in the high word and
+// the complement of the block index in the low word, sorted descending --
+// score descending, then block index ascending, a total order.  The first
+// `keep` entries are therefore exactly the blocks whose rank
+// #{u : s_u > s_t or (s_u == s_t and u < t)} is below keep; they are
+// flagged and written out in ascending order by the ballot compaction.  The
+// row is padded to a power of two with key 0, which sorts after every real
+// entry.  O(T log^2 T) comparisons; exact and order-independent.
+__device__ __forceinline__ uint64_t topk_key(float v, int t) {
+  uint32_t u = __float_as_uint(v + 0.f);  // -0 -> +0
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | (0xffffffffu - static_cast<uint32_t>(t));
+}
+
 __global__ __launch_bounds__(1024) void topk_kernel(
     const float* __restrict__ scores, float* __restrict__ scores_copy,
-    int32_t* __restrict__ sel, int nblocks, int keep, int lanes_per) {
-  extern __shared__ float sh[];
-  float* s = sh;                                        // [nblocks]
-  unsigned char* kept = reinterpret_cast<unsigned char*>(sh + nblocks);  // [nblocks]
+    int32_t* __restrict__ sel, int nblocks, int keep, int tpow) {
+  extern __shared__ uint64_t shk[];  // [tpow] keys, later the kept flags
+  constexpr int kMaxPerThread = 8;   // keep <= 8192 = 1024 threads x 8
   const int b = blockIdx.x;
   const float* src = scores + (size_t)b * nblocks;
-  for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
-    const float v = src[t];
-    s[t] = v;
-    if (scores_copy) scores_copy[(size_t)b * nblocks + t] = v;
+  for (int t = threadIdx.x; t < tpow; t += blockDim.x) {
+    if (t < nblocks) {
+      const float v = src[t];
+      shk[t] = topk_key(v, t);
+      if (scores_copy) scores_copy[(size_t)b * nblocks + t] = v;
+    } else {
+      shk[t] = 0;
+    }
   }
   __syncthreads();
-  const int per_pass = blockDim.x / lanes_per;
-  const int part = threadIdx.x % lanes_per;
-  for (int t0 = 0; t0 < nblocks; t0 += per_pass) {
-    const int t = t0 + threadIdx.x / lanes_per;
-    int rank = 0;
-    if (t < nblocks) {
-      // blocks below t count when >= v, blocks above t only when > v
-      const float v = s[t];
-      for (int u = part; u < nblocks; u += lanes_per) {
-        const float w = s[u];
-        rank += u < t ? (w >= v) : (w > v);
+  for (int size = 2; size <= tpow; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (tpow >> 1); i += blockDim.x) {
+        const int a = 2 * stride * (i / stride) + (i % stride), c = a + stride;
+        const uint64_t ka = shk[a], kc = shk[c];
+        // runs with (a & size) == 0 sort descending, the others ascending
+        if ((kc > ka) == ((a & size) == 0)) {
+          shk[a] = kc;
+          shk[c] = ka;
+        }
       }
+      __syncthreads();
     }
-    for (int off = lanes_per >> 1; off >= 1; off >>= 1) rank += __shfl_xor(rank, off, 64);
-    if (t < nblocks && part == 0) kept[t] = rank < keep;
   }
+  // the first keep sorted entries, then the LDS is reused for byte flags
+  int mine[kMaxPerThread];
+#pragma unroll
+  for (int q = 0; q < kMaxPerThread; ++q) {
+    const int r = threadIdx.x + q * blockDim.x;
+    mine[q] = r < keep ? static_cast<int>(0xffffffffu - static_cast<uint32_t>(shk[r])) : -1;
+  }
+  __syncthreads();
+  unsigned char* kept = reinterpret_cast<unsigned char*>(shk);
+  for (int t = threadIdx.x; t < nblocks; t += blockDim.x) kept[t] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kMaxPerThread; ++q)
+    if (mine[q] >= 0) kept[mine[q]] = 1;
   __syncthreads();
   compact_ascending([&](int t) { return kept[t] != 0; }, nblocks,
                     sel + (size_t)b * keep);
@@ -351,11 +378,11 @@ hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
                        int batch, int nblocks, int keep, hipStream_t s) {
   if (keep == 0 && scores_copy == nullptr) return hipSuccess;
-  const size_t lds = (size_t)nblocks * (sizeof(float) + 1);
-  int lanes_per = 1;
-  while (lanes_per < 64 && lanes_per * 2 * nblocks <= 1024) lanes_per *= 2;
+  int tpow = 2;
+  while (tpow < nblocks) tpow <<= 1;
+  const size_t lds = (size_t)tpow * sizeof(uint64_t);  // <= 64 KB for T <= 8192
   topk_kernel<<<batch, 1024, lds, s>>>(scores, scores_copy, sel, nblocks, keep,
-                                       lanes_per);
+                                       tpow);
   return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 // LayerNorm over channels for the block wrapper (FT 3.5 block equation).
 // Biased variance, eps 1e-5 (the usual definition; the pages do not state
-// it).  One wavefront per token row; two passes over registers (mean, then
-// centred variance).
+// it).  Two passes over registers (mean, then centred variance).  Rows of
+// 128, 256, 384 or 512 bf16 channels (or 64 .. 256 float32) take 16 lanes
+// each; other widths one wavefront per row.
 #include "common.h"
 #include "kernels.h"
 
@@ -16,8 +17,9 @@ struct Vec;
 template <>
 struct Vec<bf16> {
   static constexpr int N = 8;
-  __device__ static void load(const bf16* p, float* v) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
+  __device__ static uint4 raw(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void load(const bf16* p, float* v) { cvt(raw(p), v); }
+  __device__ static void cvt(const uint4 u, float* v) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -36,9 +38,11 @@ struct Vec<bf16> {
 template <>
 struct Vec<float> {
   static constexpr int N = 4;
-  __device__ static void load(const float* p, float* v) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
-    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  __device__ static uint4 raw(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void load(const float* p, float* v) { cvt(raw(p), v); }
+  __device__ static void cvt(const uint4 u, float* v) {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
   }
   __device__ static void store(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
@@ -112,6 +116,86 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
   }
 }
 
+// Rows whose 16-byte vectors split evenly over 16 lanes (channels a multiple
+// of 16 vectors, up to 128 per row): 16 lanes per row, so a wave holds 4
+// rows at once with every lane busy, and kSteps of those 4-row groups have
+// all their loads in flight before any reduction (kept as raw 16-byte
+// vectors and converted at each use).  gamma and beta stay in registers
+// across the rows of a wave.  Reductions use xor shuffles inside the 16-lane
+// group, in a fixed order.
+constexpr int kSteps = 4;
+
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void layernorm16_kernel(
+    const T* __restrict__ x, const float* __restrict__ g,
+    const float* __restrict__ be, T* __restrict__ y, int rows, int ch) {
+  constexpr int V = Vec<T>::N;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int grp = lane / 16, gl = lane % 16;
+  const int row_base = (blockIdx.x * 4 + wave) * 4 * kSteps;
+  float gv[NV][V], bv[NV][V];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int c = (gl + 16 * i) * V + j;
+      gv[i][j] = g[c];
+      bv[i][j] = be[c];
+    }
+  uint4 raw[kSteps][NV];
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const int row = min(row_base + 4 * q + grp, rows - 1);
+    const T* xr = x + (size_t)row * ch;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) raw[q][i] = Vec<T>::raw(xr + (gl + 16 * i) * V);
+  }
+  const float inv_ch = 1.f / (float)ch;
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const int row = row_base + 4 * q + grp;
+    float v[NV][V];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) Vec<T>::cvt(raw[q][i], v[i]);
+    float sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < V; ++j) sm += v[i][j];
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) sm += __shfl_xor(sm, off, 16);
+    const float mean = sm * inv_ch;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const float dlt = v[i][j] - mean;
+        sq = fmaf(dlt, dlt, sq);
+      }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 16);
+    const float rstd = rsqrtf(sq * inv_ch + 1e-5f);
+    if (row >= rows) continue;
+    T* yr = y + (size_t)row * ch;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float o[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) o[j] = (v[i][j] - mean) * rstd * gv[i][j] + bv[i][j];
+      Vec<T>::store(yr + (gl + 16 * i) * V, o);
+    }
+  }
+}
+
+template <typename T, int NV>
+hipError_t run_ln16(const T* x, const float* gamma, const float* beta, T* y,
+                    int rows, int ch, hipStream_t s) {
+  const unsigned blocks = (unsigned)((rows + 16 * kSteps - 1) / (16 * kSteps));
+  layernorm16_kernel<T, NV><<<blocks, 256, 0, s>>>(x, gamma, beta, y, rows, ch);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t run_ln(const void* x, const float* gamma, const float* beta, void* y,
                   int rows, int ch, hipStream_t s) {
@@ -119,6 +203,16 @@ hipError_t run_ln(const void* x, const float* gamma, const float* beta, void* y,
   const int ni = (ch / Vec<T>::N + 63) / 64;
   const T* xi = static_cast<const T*>(x);
   T* yo = static_cast<T*>(y);
+  const int nvec = ch / Vec<T>::N;
+  if (nvec % 16 == 0) {
+    switch (nvec / 16) {
+      case 1: return run_ln16<T, 1>(xi, gamma, beta, yo, rows, ch, s);
+      case 2: return run_ln16<T, 2>(xi, gamma, beta, yo, rows, ch, s);
+      case 3: return run_ln16<T, 3>(xi, gamma, beta, yo, rows, ch, s);
+      case 4: return run_ln16<T, 4>(xi, gamma, beta, yo, rows, ch, s);
+      default: break;
+    }
+  }
   if (ni <= 1)
     layernorm_kernel<T, 1><<<blocks, 256, 0, s>>>(xi, gamma, beta, yo, rows, ch);
   else if (ni <= 2)
