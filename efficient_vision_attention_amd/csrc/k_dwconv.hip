@@ -124,13 +124,13 @@ __device__ __forceinline__ void storev<float, 2>(float* p, const float* v) {
 // strip and walks down the input rows of the strip.  For each input row it
 // loads the K horizontal neighbours it needs (the K-fold reuse across
 // neighbouring threads is served by the L1), and the row feeds the K partial
-// output rows it belongs to, kept in registers.  Two rows are in flight at
-// any time; there is no LDS and no barrier, so every wave streams
+// output rows it belongs to, kept in registers.  NB rows of loads are in
+// flight at any time; there is no LDS and no barrier, so every wave streams
 // independently.  A workgroup covers 64 channels x (256 V / 64) columns.
 // Grid: 1-D over (batch, strip, channel tile, column tile) with the column
 // tile fastest, remapped so each XCD walks a contiguous run of neighbouring
 // tiles (their halo columns then hit in that XCD's L2).
-template <typename T, int K, bool GELU, int V>
+template <typename T, int K, bool GELU, int V, int NB>
 __global__ __launch_bounds__(256) void dwconv_stream(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, int gh, int gw, int ch, int col_tiles,
@@ -194,18 +194,18 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   // only tiles touching the left/right border have lanes with invalid taps
   const bool edge_tile = col_t * TW - R < 0 || col_t * TW + TW + R > gw;
 
-  Raw<T, V> ra[K], rb[K];
-  load_row(ra, r_begin);
-  load_row(rb, r_begin + 1);
-  // Rows are processed in groups of 2K so that both the accumulator ring
-  // slot ((row - r_begin) mod K) and the staging buffer (row parity) are
-  // compile-time constants of the unrolled body.
-  for (int r0 = r_begin; r0 < r_end; r0 += 2 * K) {
+  Raw<T, V> rbuf[NB][K];
 #pragma unroll
-    for (int u = 0; u < 2 * K; ++u) {
+  for (int q = 0; q < NB; ++q) load_row(rbuf[q], r_begin + q);
+  // Rows are processed in groups of NB*K so that both the accumulator ring
+  // slot ((row - r_begin) mod K) and the staging buffer ((row - r_begin) mod
+  // NB) are compile-time constants of the unrolled body.
+  for (int r0 = r_begin; r0 < r_end; r0 += NB * K) {
+#pragma unroll
+    for (int u = 0; u < NB * K; ++u) {
       const int r = r0 + u;
       if (r >= r_end) break;
-      Raw<T, V>(&cur)[K] = (u % 2 == 0) ? ra : rb;
+      Raw<T, V>(&cur)[K] = rbuf[u % NB];
       // A halo row outside the grid contributes nothing: skip it (uniform).
       if (r >= 0 && r < gh) {
         float xin[K][V];
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
         // input row r feeds output row r - R + i with vertical tap K - 1 - i
 #pragma unroll
         for (int i = 0; i < K; ++i) {
-          const int slot = (u - R + i + 2 * K) % K;
+          const int slot = (u - R + i + NB * K) % K;
 #pragma unroll
           for (int kx = 0; kx < K; ++kx)
 #pragma unroll
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(256) void dwconv_stream(
         }
       }
       // unconditional (clamped) prefetch keeps the load/wait pattern regular
-      load_row(cur, r + 2);
-      const int done = (u - R + 2 * K) % K;  // slot of output row r - R
+      load_row(cur, r + NB);
+      const int done = (u - R + NB * K) % K;  // slot of output row r - R
       const int yo = r - R;
       if (yo >= y0 && yo < y_end && x < gw && c_ok) {
         float v[V];
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   }
 }
 
-template <typename T, int K, bool GELU, int V>
+template <typename T, int K, bool GELU, int V, int NB = 3>
 hipError_t run_dw(const void* in, void* out, const float* weff, int batch,
                   int gh, int gw, int ch, hipStream_t s) {
   constexpr int TW = 256 / (kWgChannels / V);
@@ -253,22 +253,22 @@ hipError_t run_dw(const void* in, void* out, const float* weff, int batch,
   const int strips = (gh + TH - 1) / TH;
   const int total = col_tiles * ch_tiles * strips * batch;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  dwconv_stream<T, K, GELU, V><<<per_xcd * kXcds, 256, 0, s>>>(
+  dwconv_stream<T, K, GELU, V, NB><<<per_xcd * kXcds, 256, 0, s>>>(
       static_cast<const T*>(in), static_cast<T*>(out), weff, gh, gw, ch,
       col_tiles, ch_tiles, strips, total, per_xcd);
   return hipGetLastError();
 }
 
 // Wider kernels keep fewer channels per thread so their taps fit in
-// registers at useful occupancy.
+// registers at useful occupancy; rows in flight (NB) measured per size.
 template <typename T, bool GELU>
 hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
                       int batch, int gh, int gw, int ch, hipStream_t s) {
   switch (kmax) {
     case 1: return run_dw<T, 1, GELU, 4>(in, out, weff, batch, gh, gw, ch, s);
-    case 3: return run_dw<T, 3, GELU, 4>(in, out, weff, batch, gh, gw, ch, s);
-    case 5: return run_dw<T, 5, GELU, 2>(in, out, weff, batch, gh, gw, ch, s);
-    case 7: return run_dw<T, 7, GELU, 2>(in, out, weff, batch, gh, gw, ch, s);
+    case 3: return run_dw<T, 3, GELU, 4, GELU ? 2 : 3>(in, out, weff, batch, gh, gw, ch, s);
+    case 5: return run_dw<T, 5, GELU, 2, 4>(in, out, weff, batch, gh, gw, ch, s);
+    case 7: return run_dw<T, 7, GELU, 2, 3>(in, out, weff, batch, gh, gw, ch, s);
     default: return hipErrorInvalidValue;
   }
 }
