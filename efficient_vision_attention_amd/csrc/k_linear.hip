@@ -135,7 +135,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kHG = 4;          // heads per workgroup
 constexpr int kTT = 32;         // tokens per tile
 constexpr int kChunkTok = 512;  // tokens per partial (bf16 path)
-constexpr int kApplyTok = 128;  // tokens per wave in the readout
+constexpr int kApplyTok = 256;  // tokens per wave in the readout
 
 __device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
   return (u & 0x8000u) ? 0 : u;
@@ -243,8 +243,8 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
 }
 
 // O^T = Z^T relu(Q^)^T with Z split into bf16 hi + lo parts, normalised by
-// relu(q^) . D.  grid (ceil(tokens/128), ceil(heads/4), batch), 256
-// threads; wave = head, four 32-token tiles per wave, next tile prefetched.
+// relu(q^) . D.  grid (ceil(tokens/256), ceil(heads/4), batch), 256
+// threads; wave = head, eight 32-token tiles per wave, two tiles in flight.
 __global__ __launch_bounds__(256) void lin_apply_mfma(
     const bf16* __restrict__ qkvh, const float* __restrict__ kv,
     const float* __restrict__ ksum, bf16* __restrict__ o, int tokens,
@@ -283,19 +283,21 @@ __global__ __launch_bounds__(256) void lin_apply_mfma(
 
   const int n_base = blockIdx.x * kApplyTok;
   const bf16* qbase = qkvh + (size_t)b * tokens * C3 + h * kD + 8 * g;
-  uint4 st[2];
-  auto issue = [&](int n) {
+  uint4 st[2][2];  // two tiles in flight
+  auto issue = [&](uint4 (&dst)[2], int n) {
     const bool ok = n < tokens;
     const bf16* qrow = qbase + (size_t)(ok ? n : 0) * C3;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      st[ks] = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks) : uint4{0, 0, 0, 0};
+      dst[ks] = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks) : uint4{0, 0, 0, 0};
   };
-  issue(n_base + col);
+  issue(st[0], n_base + col);
+  issue(st[1], n_base + 32 + col);
+#pragma unroll
   for (int tt = 0; tt < kApplyTok / 32; ++tt) {
     const int n = n_base + tt * 32 + col;
-    uint4 cur[2] = {st[0], st[1]};
-    if (tt + 1 < kApplyTok / 32) issue(n + 32);
+    uint4 cur[2] = {st[tt % 2][0], st[tt % 2][1]};
+    if (tt + 2 < kApplyTok / 32) issue(st[tt % 2], n + 64);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
