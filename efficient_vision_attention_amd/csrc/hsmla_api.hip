@@ -112,10 +112,12 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
 //   ksum [B][H][d] f32, kv partials f32, dw taps [kmax^2][3C] f32,
 //   scores [B][T] f32, sel [B][k] i32 (threshold: [B][T] i32, counts [B] i32;
 //   per head: [B][H][T] i32, counts [B][H] i32, head scores [B][T][H] f32),
+//   gate block sums [B][T][3C] f32,
 //   (block only) xn [P][C], x1 [P][C], h1 [P][4C], h2 [P][4C],
 //   ffn taps [9][4C] f32.
 struct Layout {
   size_t qkv, qkv_hat, o, kv, ksum, part, taps, scores, sel, counts, head_scores;
+  size_t bsum;
   size_t xn, x1, h1, h2, ffn_taps;
   size_t total;
 };
@@ -148,6 +150,7 @@ Layout layout(const Dims& D, int op) {
     L.sel = take((size_t)D.B * D.sw * 4 + 4);
     if (D.thr) L.counts = take((size_t)D.nc * 4);
     if (D.ph) L.head_scores = take((size_t)D.B * D.T * D.H * 4);
+    L.bsum = take((size_t)D.B * D.T * 3 * D.C * 4);
     if (op == HSMLA_OP_BLOCK) {
       L.xn = take(D.P * D.C * D.e);
       L.x1 = take(D.P * D.C * D.e);
@@ -209,10 +212,11 @@ hsmla_status check_weights(const hsmla_desc* d, const hsmla_weights* w) {
   return HSMLA_OK;
 }
 
-// Steps 1-2 with caller-provided buffers.
+// Steps 1-2 with caller-provided buffers; with bsum the conv also writes
+// the gate's block sums of qkv_hat.
 hsmla_status run_qkv(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
                      const void* x, void* qkv, void* qkv_hat, float* taps,
-                     hipStream_t s, Rec& r) {
+                     float* bsum, hipStream_t s, Rec& r) {
   r.mark("qkv_gemm");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, x, w->w_qkv, nullptr, qkv, (int)D.P,
                                3 * D.C, D.C, s, hsmla::GemmSite::kQkv));
@@ -221,7 +225,7 @@ hsmla_status run_qkv(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
                                   D.kmax, 3 * D.C, 1, taps, s));
   r.mark("dwconv_qkv");
   HSMLA_TRY(hsmla::launch_dwconv(D.bf, qkv, qkv_hat, taps, D.kmax, D.B, D.gh,
-                                 D.gw, 3 * D.C, false, s));
+                                 D.gw, 3 * D.C, false, bsum, D.Bs, s));
   return HSMLA_OK;
 }
 
@@ -240,16 +244,25 @@ hsmla_status run_module(const Dims& D, const hsmla_desc* d,
   int32_t* sel = reinterpret_cast<int32_t*>(at(ws, L.sel));
   int32_t* counts = D.thr ? reinterpret_cast<int32_t*>(at(ws, L.counts)) : nullptr;
   float* hscores = D.ph ? reinterpret_cast<float*>(at(ws, L.head_scores)) : nullptr;
-  hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, s, r);
+  // the plain gate's block sums come out of the depthwise conv when its
+  // workgroup shape allows; the gate then only forms the logits
+  float* bsum = (!w->gate_dw && hsmla::dwconv_can_pool(D.kmax, D.Bs))
+                    ? reinterpret_cast<float*>(at(ws, L.bsum))
+                    : nullptr;
+  hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, bsum, s, r);
   if (st != HSMLA_OK) return st;
   r.mark("kv_state");
   HSMLA_TRY(hsmla::launch_kv_state(D.bf, qkvh, kv, ksum, part, D.B, D.N, D.H, s));
   r.mark("lin_apply");
   HSMLA_TRY(hsmla::launch_lin_apply(D.bf, qkvh, kv, ksum, o, D.B, D.N, D.H, s));
   r.mark("gate_scores");
-  HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b,
-                                      w->gate_dw, scores, hscores, D.B, D.gh,
-                                      D.gw, D.H, D.Bs, s));
+  if (bsum)
+    HSMLA_TRY(hsmla::launch_gate_from_sums(bsum, w->gate_w, w->gate_b, scores,
+                                           hscores, D.B, D.T, D.H, D.Bs, s));
+  else
+    HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b,
+                                        w->gate_dw, scores, hscores, D.B, D.gh,
+                                        D.gw, D.H, D.Bs, s));
   if (D.soft) {
     r.mark("sparse_softmax");
     HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, nullptr, nullptr, scores, o,
@@ -341,7 +354,7 @@ hsmla_status hsmla_qkv_branches(const hsmla_desc* desc, const hsmla_weights* w,
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
   Rec r;
   return run_qkv(D, desc, w, x, qkv, qkv_hat,
-                 reinterpret_cast<float*>(at(ws, L.taps)),
+                 reinterpret_cast<float*>(at(ws, L.taps)), nullptr,
                  static_cast<hipStream_t>(stream), r);
 }
 
@@ -572,7 +585,7 @@ hsmla_status block_impl(const hsmla_desc* desc, const hsmla_weights* w,
   HSMLA_TRY(hsmla::launch_dw_taps(D.bf, ffn_k, ffn_ks, 1, 3, 4 * C, 0, ftaps, s));
   r.mark("ffn_dwconv_gelu");
   HSMLA_TRY(hsmla::launch_dwconv(D.bf, h1, h2, ftaps, 3, D.B, D.gh, D.gw, 4 * C,
-                                 true, s));
+                                 true, nullptr, 1, s));
   r.mark("ffn2_gemm_residual");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, h2, f->w2, x1, out, P, C, 4 * C, s,
                                hsmla::GemmSite::kFfn2));

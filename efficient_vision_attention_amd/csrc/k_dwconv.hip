@@ -59,6 +59,7 @@ __device__ __forceinline__ float gelu_erf(float x) {
 }
 
 constexpr int TH = 32;   // output rows per workgroup strip
+constexpr int kPoolMinBlock = 4;
 constexpr int kXcds = 8;
 constexpr int kWgChannels = 64;  // channels per workgroup
 
@@ -120,6 +121,27 @@ __device__ __forceinline__ void storev<float, 2>(float* p, const float* v) {
   *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
 }
 
+// Store, and leave in v the values as stored (rounded to T).
+template <typename T, int V>
+__device__ __forceinline__ void storev_round(T* p, float* v) {
+  if constexpr (sizeof(T) == 4) {
+    storev<T, V>(p, v);
+  } else {
+    uint32_t w[V / 2];
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    if constexpr (V == 4)
+      *reinterpret_cast<uint2*>(p) = uint2{w[0], w[1]};
+    else
+      *reinterpret_cast<uint32_t*>(p) = w[0];
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
 // A thread owns one output column x and V consecutive channels of a 32-row
 // strip and walks down the input rows of the strip.  For each input row it
 // loads the K horizontal neighbours it needs (the K-fold reuse across
@@ -130,14 +152,23 @@ __device__ __forceinline__ void storev<float, 2>(float* p, const float* v) {
 // Grid: 1-D over (batch, strip, channel tile, column tile) with the column
 // tile fastest, remapped so each XCD walks a contiguous run of neighbouring
 // tiles (their halo columns then hit in that XCD's L2).
-template <typename T, int K, bool GELU, int V, int NB>
+// With POOL the kernel also writes, for the gate, the sum over every
+// block x block block of the values it stores (as stored, i.e. after
+// rounding to T): bsum[b][t][c].  Each thread adds its column's rows and
+// parks the sum of each finished block row in LDS (its own slot, no
+// barrier); after the strip one barrier, then the block's columns are
+// added in order.  block must divide the workgroup width and the strip
+// height, and be at least kPoolMinBlock (LDS room).
+template <typename T, int K, bool GELU, int V, int NB, bool POOL>
 __global__ __launch_bounds__(256) void dwconv_stream(
     const T* __restrict__ in, T* __restrict__ out,
-    const float* __restrict__ weff, int gh, int gw, int ch, int col_tiles,
-    int ch_tiles, int strips, int total, int per_xcd) {
+    const float* __restrict__ weff, float* __restrict__ bsum, int block,
+    int gh, int gw, int ch, int col_tiles, int ch_tiles, int strips,
+    int total, int per_xcd) {
   constexpr int R = (K - 1) / 2;
   constexpr int CG = kWgChannels / V;  // channel groups per workgroup
   constexpr int TW = 256 / CG;         // columns per workgroup
+  __shared__ float red[POOL ? TH / kPoolMinBlock : 1][POOL ? TW : 1][POOL ? kWgChannels : 1];
   const int bid = blockIdx.x;
   const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
   if (tile >= total) return;
@@ -171,6 +202,9 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   for (int i = 0; i < K; ++i)
 #pragma unroll
     for (int j = 0; j < V; ++j) acc[i][j] = 0.f;
+  float psum[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) psum[j] = 0.f;
 
   const int y_end = min(gh, y0 + TH);
   const int r_begin = y0 - R, r_end = y_end + R;
@@ -236,39 +270,84 @@ __global__ __launch_bounds__(256) void dwconv_stream(
         float v[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) v[j] = GELU ? gelu_erf(acc[done][j]) : acc[done][j];
-        storev<T, V>(out + (img + (size_t)yo * gw + x) * ch + c, v);
+        if constexpr (POOL) {
+          storev_round<T, V>(out + (img + (size_t)yo * gw + x) * ch + c, v);
+#pragma unroll
+          for (int j = 0; j < V; ++j) psum[j] += v[j];
+        } else {
+          storev<T, V>(out + (img + (size_t)yo * gw + x) * ch + c, v);
+        }
+      }
+      if constexpr (POOL) {
+        // end of a block row: park this thread's column sums
+        if (yo >= y0 && yo < y_end && (yo + 1) % block == 0) {
+          const int br = (yo - y0) / block;
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            red[br][tx][tc * V + j] = psum[j];
+            psum[j] = 0.f;
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < V; ++j) acc[done][j] = 0.f;
     }
   }
+  if constexpr (POOL) {
+    __syncthreads();
+    if (tx % block == 0 && x < gw && c_ok) {
+      const int nbc = gw / block;
+      for (int br = 0; br < (y_end - y0) / block; ++br) {
+        const size_t t = (size_t)(y0 / block + br) * nbc + x / block;
+        float* dst = bsum + ((size_t)b * (gh / block) * nbc + t) * ch + c;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          float sm = 0.f;
+          for (int q = 0; q < block; ++q) sm += red[br][tx + q][tc * V + j];
+          dst[j] = sm;
+        }
+      }
+    }
+  }
 }
 
 template <typename T, int K, bool GELU, int V, int NB = 3>
-hipError_t run_dw(const void* in, void* out, const float* weff, int batch,
-                  int gh, int gw, int ch, hipStream_t s) {
+hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
+                  int block, int batch, int gh, int gw, int ch, hipStream_t s) {
   constexpr int TW = 256 / (kWgChannels / V);
   const int col_tiles = (gw + TW - 1) / TW;
   const int ch_tiles = (ch + kWgChannels - 1) / kWgChannels;
   const int strips = (gh + TH - 1) / TH;
   const int total = col_tiles * ch_tiles * strips * batch;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  dwconv_stream<T, K, GELU, V, NB><<<per_xcd * kXcds, 256, 0, s>>>(
-      static_cast<const T*>(in), static_cast<T*>(out), weff, gh, gw, ch,
-      col_tiles, ch_tiles, strips, total, per_xcd);
+  if constexpr (!GELU) {
+    if (bsum) {
+      dwconv_stream<T, K, false, V, NB, true><<<per_xcd * kXcds, 256, 0, s>>>(
+          static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
+          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
+      return hipGetLastError();
+    }
+  }
+    dwconv_stream<T, K, GELU, V, NB, false><<<per_xcd * kXcds, 256, 0, s>>>(
+        static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
+        gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
   return hipGetLastError();
 }
 
 // Wider kernels keep fewer channels per thread so their taps fit in
 // registers at useful occupancy; rows in flight (NB) measured per size.
+// channels per thread for each kernel size (also fixes the workgroup width)
+constexpr int vec_for(int kmax) { return kmax <= 3 ? 4 : 2; }
+
 template <typename T, bool GELU>
 hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
-                      int batch, int gh, int gw, int ch, hipStream_t s) {
+                      float* bsum, int block, int batch, int gh, int gw, int ch,
+                      hipStream_t s) {
   switch (kmax) {
-    case 1: return run_dw<T, 1, GELU, 4>(in, out, weff, batch, gh, gw, ch, s);
-    case 3: return run_dw<T, 3, GELU, 4, GELU ? 2 : 3>(in, out, weff, batch, gh, gw, ch, s);
-    case 5: return run_dw<T, 5, GELU, 2, 4>(in, out, weff, batch, gh, gw, ch, s);
-    case 7: return run_dw<T, 7, GELU, 2, 3>(in, out, weff, batch, gh, gw, ch, s);
+    case 1: return run_dw<T, 1, GELU, vec_for(1)>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
+    case 3: return run_dw<T, 3, GELU, vec_for(3), GELU ? 2 : 3>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
+    case 5: return run_dw<T, 5, GELU, vec_for(5), 4>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
+    case 7: return run_dw<T, 7, GELU, vec_for(7), 3>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -291,14 +370,20 @@ hipError_t launch_dw_taps(bool bf, const void* const* kernels, const int* ks,
   return hipGetLastError();
 }
 
+bool dwconv_can_pool(int kmax, int block) {
+  const int tw = 256 / (kWgChannels / vec_for(kmax));
+  return block >= kPoolMinBlock && tw % block == 0 && TH % block == 0;
+}
+
 hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
                          int kmax, int batch, int gh, int gw, int ch,
-                         bool gelu, hipStream_t s) {
+                         bool gelu, float* bsum, int block, hipStream_t s) {
+  if (bsum && (gelu || !dwconv_can_pool(kmax, block))) return hipErrorInvalidValue;
   if (bf)
-    return gelu ? dispatch_k<bf16, true>(kmax, in, out, weff, batch, gh, gw, ch, s)
-                : dispatch_k<bf16, false>(kmax, in, out, weff, batch, gh, gw, ch, s);
-  return gelu ? dispatch_k<float, true>(kmax, in, out, weff, batch, gh, gw, ch, s)
-              : dispatch_k<float, false>(kmax, in, out, weff, batch, gh, gw, ch, s);
+    return gelu ? dispatch_k<bf16, true>(kmax, in, out, weff, nullptr, 1, batch, gh, gw, ch, s)
+                : dispatch_k<bf16, false>(kmax, in, out, weff, bsum, block, batch, gh, gw, ch, s);
+  return gelu ? dispatch_k<float, true>(kmax, in, out, weff, nullptr, 1, batch, gh, gw, ch, s)
+              : dispatch_k<float, false>(kmax, in, out, weff, bsum, block, batch, gh, gw, ch, s);
 }
 
 }  // namespace hsmla

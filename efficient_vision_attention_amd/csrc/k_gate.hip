@@ -97,6 +97,26 @@ __global__ __launch_bounds__(256) void gate_scores_kernel(
             head_scores ? head_scores + ((size_t)b * gridDim.x + t) * heads : nullptr);
 }
 
+// grid (blocks per image, batch), 256 threads: the scores from block sums
+// already reduced elsewhere (bsum [b][t][3C]).
+__global__ __launch_bounds__(256) void gate_from_sums_kernel(
+    const float* __restrict__ bsum, const float* __restrict__ gw,
+    const float* __restrict__ gb, float* __restrict__ scores,
+    float* __restrict__ head_scores, int heads, float inv_cnt) {
+  extern __shared__ float sh[];
+  const int C = heads * kD, C3 = 3 * C;
+  float* fsum = sh;       // [3C]
+  float* gsig = sh + C3;  // [heads]
+  const int t = blockIdx.x, b = blockIdx.y;
+  const size_t row = (size_t)b * gridDim.x + t;
+  const float4* src = reinterpret_cast<const float4*>(bsum + row * C3);
+  for (int i = threadIdx.x; i < C3 / 4; i += blockDim.x)
+    reinterpret_cast<float4*>(fsum)[i] = src[i];
+  __syncthreads();
+  gate_tail(fsum, gsig, gw, gb, heads, C, inv_cnt, scores ? scores + row : nullptr,
+            head_scores ? head_scores + row * heads : nullptr);
+}
+
 // Four consecutive channels of one token as float32 (8-byte bf16 or 16-byte
 // float32 vector load).
 __device__ __forceinline__ void load4(const bf16* p, float* v) {
@@ -338,6 +358,17 @@ __global__ __launch_bounds__(1024) void threshold_heads_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_gate_from_sums(const float* bsum, const float* gate_w,
+                                 const float* gate_b, float* scores,
+                                 float* head_scores, int batch, int nblocks,
+                                 int heads, int block, hipStream_t s) {
+  const size_t lds = (size_t)(3 * heads * kD + heads) * sizeof(float);
+  gate_from_sums_kernel<<<dim3(nblocks, batch), 256, lds, s>>>(
+      bsum, gate_w, gate_b, scores, head_scores, heads,
+      1.f / (float)(block * block));
+  return hipGetLastError();
+}
 
 hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
                               const float* gate_w, const float* gate_b,

@@ -26,10 +26,14 @@ hipError_t launch_dw_taps(bool bf, const void* const* kernels, const int* ks,
                           hipStream_t s);
 
 // out[b][y][x][c] = act(sum_tap weff[tap][c] * in[b][y+dy-r][x+dx-r][c]),
-// zero padding, r = (kmax-1)/2; act = exact GELU when `gelu`.
+// zero padding, r = (kmax-1)/2; act = exact GELU when `gelu`.  With bsum
+// (no GELU; dwconv_can_pool(kmax, block) must hold) the launch also writes
+// bsum[b][t][c] = sum of the stored out values over block t (block x block
+// tokens, blocks numbered row-major).
+bool dwconv_can_pool(int kmax, int block);
 hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
                          int kmax, int batch, int gh, int gw, int ch,
-                         bool gelu, hipStream_t s);
+                         bool gelu, float* bsum, int block, hipStream_t s);
 
 // Number of token chunks the KV-state reduction splits each image into.
 int kv_chunks(bool bf, int batch, int heads, int tokens);
@@ -48,6 +52,12 @@ hipError_t launch_lin_apply(bool bf, const void* qkv_hat, const float* kv,
 // gate_dw: nullptr, or the gate's depthwise 3x3 kernel [3C][3][3] in the
 // activation type (16-byte aligned).  head_scores (optional): G^(h) per
 // block and head, [batch][blocks][heads].
+// The same scores from block sums (bsum [batch][blocks][3C], e.g. written
+// by launch_dwconv): M_t and optionally G^(h)_t.
+hipError_t launch_gate_from_sums(const float* bsum, const float* gate_w,
+                                 const float* gate_b, float* scores,
+                                 float* head_scores, int batch, int nblocks,
+                                 int heads, int block, hipStream_t s);
 hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
                               const float* gate_w, const float* gate_b,
                               const void* gate_dw, float* scores,
