@@ -4,8 +4,9 @@
 Workload: 2 images of 128 x 256 tokens, C = 384 (12 heads of 32), bf16,
 identity + 3x3 + 5x5 depthwise branches, 8 x 8 blocks, 16 x 16 softmax
 windows, keep ratio 10% (52 of 512 blocks per image), wrapped in the LN /
-FFN-DWConv block.  One step = one call of hsmla_block_forward over the
-batch, i.e. every kernel of the path.  Inputs are seeded synthetic data
+FFN-DWConv block.  One step = one call of hsmla_block_forward_split over
+the batch (the two images on two streams; --streams 1: hsmla_block_forward
+on one), i.e. every kernel of the path.  Inputs are seeded synthetic data
 (street-scene-like smooth field plus noise) already resident in HBM.
 
 Prints one JSON line: tokens/s, the per-kernel breakdown from HIP events
@@ -40,12 +41,15 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--keep", type=float, default=0.10)
     ap.add_argument("--branches", default="3,5",
                     help="depthwise branch sizes added to the identity")
     ap.add_argument("--gate-conv", action="store_true",
                     help="depthwise 3x3 inside the gate's head score")
+    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
+                    help="2: the block's batch split over two streams "
+                         "(hsmla_block_forward_split); 1: one stream")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -274,14 +278,24 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps, ws
 
-    def block_step(m, ws, out):
+    split = H.SplitStreams() if args.streams == 2 else None
+
+    def one_stream_step(m, ws, out):
         H.hsmla_block_forward(m.desc, m.weights, m.ffn, x, out, ws)
+
+    def block_step(m, ws, out):
+        if split is None:
+            H.hsmla_block_forward(m.desc, m.weights, m.ffn, x, out, ws)
+        else:
+            H.hsmla_block_forward_split(m.desc, m.weights, m.ffn, x, out, ws, split)
 
     def module_step(m, ws, out):
         H.hsmla_forward(m.desc, m.weights, x, out, ws)
 
     model = DeviceModel(shape(base), inp)
     ms, ws = time_steps(model, block_step, args.steps, args.warmup)
+    ms_one = (ms if split is None else
+              time_steps(model, one_stream_step, args.steps, args.warmup)[0])
     tokens = base.batch * base.tokens
     base_views = model.views(H.HSMLA_OP_BLOCK, ws)
     sel = base_views["sel"].cpu().numpy()
@@ -413,7 +427,9 @@ def main():
                    "channels": base.channels, "heads": base.heads,
                    "head_dim": base.head_dim, "branches": list(base.branches),
                    "block": base.block, "window": base.window, "keep": base.keep,
-                   "keep_blocks": base.keep_blocks, "gate_conv": base.gate_conv},
+                   "keep_blocks": base.keep_blocks, "gate_conv": base.gate_conv,
+                   "streams": args.streams},
+        "one_stream_ms_per_step": round(ms_one, 4),
         "roofline": roof,
         "kernels": kernels,
         "sweep": sweep,

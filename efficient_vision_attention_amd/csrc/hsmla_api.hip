@@ -212,44 +212,103 @@ hsmla_status check_weights(const hsmla_desc* d, const hsmla_weights* w) {
   return HSMLA_OK;
 }
 
+// Folds the identity and the branch kernels into one tap set.
+hsmla_status fold_qkv_taps(const Dims& D, const hsmla_desc* d,
+                           const hsmla_weights* w, float* taps, hipStream_t s) {
+  HSMLA_TRY(hsmla::launch_dw_taps(D.bf, w->dw, d->branch_k, d->n_branches,
+                                  D.kmax, 3 * D.C, 1, taps, s));
+  return HSMLA_OK;
+}
+
 // Steps 1-2 with caller-provided buffers; with bsum the conv also writes
-// the gate's block sums of qkv_hat.
+// the gate's block sums of qkv_hat.  fold: fold the taps first (otherwise
+// they are already in `taps`).
 hsmla_status run_qkv(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
                      const void* x, void* qkv, void* qkv_hat, float* taps,
-                     float* bsum, hipStream_t s, Rec& r) {
+                     float* bsum, bool fold, hipStream_t s, Rec& r) {
   r.mark("qkv_gemm");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, x, w->w_qkv, nullptr, qkv, (int)D.P,
                                3 * D.C, D.C, s, hsmla::GemmSite::kQkv));
-  r.mark("dw_taps");
-  HSMLA_TRY(hsmla::launch_dw_taps(D.bf, w->dw, d->branch_k, d->n_branches,
-                                  D.kmax, 3 * D.C, 1, taps, s));
+  if (fold) {
+    r.mark("dw_taps");
+    hsmla_status st = fold_qkv_taps(D, d, w, taps, s);
+    if (st != HSMLA_OK) return st;
+  }
   r.mark("dwconv_qkv");
   HSMLA_TRY(hsmla::launch_dwconv(D.bf, qkv, qkv_hat, taps, D.kmax, D.B, D.gh,
                                  D.gw, 3 * D.C, false, bsum, D.Bs, s));
   return HSMLA_OK;
 }
 
-// Steps 1-5 into the workspace views (o holds the refined output).
+// Workspace pointers of images [b0, b0 + nb): every section is laid out
+// image by image, so a range is an offset into each.
+struct Bufs {
+  void *qkv, *qkvh, *o, *xn, *x1, *h1, *h2;
+  float *kv, *ksum, *part, *taps, *ftaps, *scores, *hscores, *bsum;
+  int32_t *sel, *counts;
+};
+
+Bufs bufs_for(const Dims& D, const Layout& L, void* ws, int op, int b0) {
+  const size_t n = (size_t)D.N, c = (size_t)D.C, e = D.e, T = (size_t)D.T;
+  const size_t H = (size_t)D.H, bb = (size_t)b0;
+  const size_t chunks = (size_t)kv_chunks(D.bf, D.B, D.H, D.N);
+  Bufs u{};
+  u.qkv = at(ws, L.qkv + bb * n * 3 * c * e);
+  u.qkvh = at(ws, L.qkv_hat + bb * n * 3 * c * e);
+  u.o = at(ws, L.o + bb * n * c * e);
+  u.kv = reinterpret_cast<float*>(at(ws, L.kv)) + bb * H * kHeadDim * kHeadDim;
+  u.ksum = reinterpret_cast<float*>(at(ws, L.ksum)) + bb * H * kHeadDim;
+  u.part = reinterpret_cast<float*>(at(ws, L.part)) +
+           bb * H * chunks * (kHeadDim * kHeadDim + kHeadDim);
+  u.taps = reinterpret_cast<float*>(at(ws, L.taps));  // shared by all images
+  u.scores = reinterpret_cast<float*>(at(ws, L.scores)) + bb * T;
+  u.sel = reinterpret_cast<int32_t*>(at(ws, L.sel)) + bb * (size_t)D.sw;
+  u.counts = D.thr ? reinterpret_cast<int32_t*>(at(ws, L.counts)) +
+                         bb * (size_t)(D.nc / D.B)
+                   : nullptr;
+  u.hscores = D.ph ? reinterpret_cast<float*>(at(ws, L.head_scores)) + bb * T * H
+                   : nullptr;
+  u.bsum = reinterpret_cast<float*>(at(ws, L.bsum)) + bb * T * 3 * c;
+  if (op == HSMLA_OP_BLOCK) {
+    u.xn = at(ws, L.xn + bb * n * c * e);
+    u.x1 = at(ws, L.x1 + bb * n * c * e);
+    u.h1 = at(ws, L.h1 + bb * n * 4 * c * e);
+    u.h2 = at(ws, L.h2 + bb * n * 4 * c * e);
+    u.ftaps = reinterpret_cast<float*>(at(ws, L.ffn_taps));  // shared
+  }
+  return u;
+}
+
+// The same dims for a range of nb images.
+Dims range_dims(const Dims& D, int nb) {
+  Dims r = D;
+  r.B = nb;
+  r.P = (size_t)D.N * nb;
+  r.nc = D.ph ? nb * D.H : nb;
+  return r;
+}
+
+// Steps 1-5 into the workspace views (o holds the refined output).  D may
+// describe a range of the images (range_dims), u the matching pointers.
 hsmla_status run_module(const Dims& D, const hsmla_desc* d,
-                        const hsmla_weights* w, const void* x, void* ws,
-                        const Layout& L, hipStream_t s, Rec& r) {
-  void* qkv = at(ws, L.qkv);
-  void* qkvh = at(ws, L.qkv_hat);
-  void* o = at(ws, L.o);
-  float* kv = reinterpret_cast<float*>(at(ws, L.kv));
-  float* ksum = reinterpret_cast<float*>(at(ws, L.ksum));
-  float* part = reinterpret_cast<float*>(at(ws, L.part));
-  float* taps = reinterpret_cast<float*>(at(ws, L.taps));
-  float* scores = reinterpret_cast<float*>(at(ws, L.scores));
-  int32_t* sel = reinterpret_cast<int32_t*>(at(ws, L.sel));
-  int32_t* counts = D.thr ? reinterpret_cast<int32_t*>(at(ws, L.counts)) : nullptr;
-  float* hscores = D.ph ? reinterpret_cast<float*>(at(ws, L.head_scores)) : nullptr;
+                        const hsmla_weights* w, const void* x, const Bufs& u,
+                        bool fold, hipStream_t s, Rec& r) {
+  void* qkv = u.qkv;
+  void* qkvh = u.qkvh;
+  void* o = u.o;
+  float* kv = u.kv;
+  float* ksum = u.ksum;
+  float* part = u.part;
+  float* taps = u.taps;
+  float* scores = u.scores;
+  int32_t* sel = u.sel;
+  int32_t* counts = u.counts;
+  float* hscores = u.hscores;
   // the plain gate's block sums come out of the depthwise conv when its
   // workgroup shape allows; the gate then only forms the logits
-  float* bsum = (!w->gate_dw && hsmla::dwconv_can_pool(D.kmax, D.Bs))
-                    ? reinterpret_cast<float*>(at(ws, L.bsum))
-                    : nullptr;
-  hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, bsum, s, r);
+  float* bsum = (!w->gate_dw && hsmla::dwconv_can_pool(D.kmax, D.Bs)) ? u.bsum
+                                                                       : nullptr;
+  hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, bsum, fold, s, r);
   if (st != HSMLA_OK) return st;
   r.mark("kv_state");
   HSMLA_TRY(hsmla::launch_kv_state(D.bf, qkvh, kv, ksum, part, D.B, D.N, D.H, s));
@@ -354,7 +413,7 @@ hsmla_status hsmla_qkv_branches(const hsmla_desc* desc, const hsmla_weights* w,
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
   Rec r;
   return run_qkv(D, desc, w, x, qkv, qkv_hat,
-                 reinterpret_cast<float*>(at(ws, L.taps)), nullptr,
+                 reinterpret_cast<float*>(at(ws, L.taps)), nullptr, true,
                  static_cast<hipStream_t>(stream), r);
 }
 
@@ -535,7 +594,8 @@ hsmla_status forward_impl(const hsmla_desc* desc, const hsmla_weights* w,
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 16)) return HSMLA_ERR_ALIGN;
   const Layout L = layout(D, HSMLA_OP_FORWARD);
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
-  if ((st = run_module(D, desc, w, x, ws, L, s, r)) != HSMLA_OK) return st;
+  const Bufs u = bufs_for(D, L, ws, HSMLA_OP_FORWARD, 0);
+  if ((st = run_module(D, desc, w, x, u, true, s, r)) != HSMLA_OK) return st;
   r.mark("out_proj");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, nullptr, y, (int)D.P,
                                D.C, D.C, s, hsmla::GemmSite::kOut));
@@ -543,11 +603,11 @@ hsmla_status forward_impl(const hsmla_desc* desc, const hsmla_weights* w,
   return r.ok ? HSMLA_OK : HSMLA_ERR_HIP;
 }
 
-hsmla_status block_impl(const hsmla_desc* desc, const hsmla_weights* w,
-                        const hsmla_ffn_weights* f, const void* x, void* out,
-                        void* ws, size_t ws_bytes, hipStream_t s, Rec& r) {
-  Dims D;
-  hsmla_status st = check_desc(desc, &D);
+// Checks of the block entry points; fills D and L.
+hsmla_status check_block(const hsmla_desc* desc, const hsmla_weights* w,
+                         const hsmla_ffn_weights* f, const void* x, void* out,
+                         void* ws, size_t ws_bytes, Dims* D, Layout* L) {
+  hsmla_status st = check_desc(desc, D);
   if (st != HSMLA_OK) return st;
   if (!x || !out || !ws || !f) return HSMLA_ERR_NULL;
   if ((st = check_weights(desc, w)) != HSMLA_OK) return st;
@@ -559,38 +619,103 @@ hsmla_status block_impl(const hsmla_desc* desc, const hsmla_weights* w,
       !aligned(f->ln1_g, 4) || !aligned(f->ln1_b, 4) || !aligned(f->ln2_g, 4) ||
       !aligned(f->ln2_b, 4))
     return HSMLA_ERR_ALIGN;
-  const Layout L = layout(D, HSMLA_OP_BLOCK);
-  if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
-  const int P = (int)D.P, C = D.C;
-  void* xn = at(ws, L.xn);
-  void* x1 = at(ws, L.x1);
-  void* h1 = at(ws, L.h1);
-  void* h2 = at(ws, L.h2);
-  float* ftaps = reinterpret_cast<float*>(at(ws, L.ffn_taps));
-  r.mark("layernorm1");
-  HSMLA_TRY(hsmla::launch_layernorm(D.bf, x, f->ln1_g, f->ln1_b, xn, P, C, s));
-  if ((st = run_module(D, desc, w, xn, ws, L, s, r)) != HSMLA_OK) return st;
-  // x1 = x + O W_o (residual fused into the projection epilogue)
-  r.mark("out_proj_residual");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, x, x1, P, C, C, s,
-                               hsmla::GemmSite::kOut));
-  r.mark("layernorm2");
-  HSMLA_TRY(hsmla::launch_layernorm(D.bf, x1, f->ln2_g, f->ln2_b, xn, P, C, s));
-  r.mark("ffn1_gemm");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, xn, f->w1, nullptr, h1, P, 4 * C, C, s,
-                               hsmla::GemmSite::kFfn1));
+  *L = layout(*D, HSMLA_OP_BLOCK);
+  if (ws_bytes < L->total) return HSMLA_ERR_WORKSPACE;
+  return HSMLA_OK;
+}
+
+hsmla_status fold_ffn_taps(const Dims& D, const hsmla_ffn_weights* f,
+                           float* ftaps, hipStream_t s) {
   const void* ffn_k[1] = {f->dw_ffn};
   const int ffn_ks[1] = {3};
-  r.mark("ffn_dw_taps");
-  HSMLA_TRY(hsmla::launch_dw_taps(D.bf, ffn_k, ffn_ks, 1, 3, 4 * C, 0, ftaps, s));
+  HSMLA_TRY(hsmla::launch_dw_taps(D.bf, ffn_k, ffn_ks, 1, 3, 4 * D.C, 0, ftaps, s));
+  return HSMLA_OK;
+}
+
+// The block over the images that D (a range, see range_dims) and u cover;
+// x and out point at the range's first image.  fold: fold both tap sets in
+// line (otherwise they are already in the workspace).
+hsmla_status block_range(const Dims& D, const hsmla_desc* desc,
+                         const hsmla_weights* w, const hsmla_ffn_weights* f,
+                         const void* x, void* out, const Bufs& u, bool fold,
+                         hipStream_t s, Rec& r) {
+  const int P = (int)D.P, C = D.C;
+  r.mark("layernorm1");
+  HSMLA_TRY(hsmla::launch_layernorm(D.bf, x, f->ln1_g, f->ln1_b, u.xn, P, C, s));
+  hsmla_status st = run_module(D, desc, w, u.xn, u, fold, s, r);
+  if (st != HSMLA_OK) return st;
+  // x1 = x + O W_o (residual fused into the projection epilogue)
+  r.mark("out_proj_residual");
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, u.o, w->w_o, x, u.x1, P, C, C, s,
+                               hsmla::GemmSite::kOut));
+  r.mark("layernorm2");
+  HSMLA_TRY(hsmla::launch_layernorm(D.bf, u.x1, f->ln2_g, f->ln2_b, u.xn, P, C, s));
+  r.mark("ffn1_gemm");
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, u.xn, f->w1, nullptr, u.h1, P, 4 * C, C, s,
+                               hsmla::GemmSite::kFfn1));
+  if (fold) {
+    r.mark("ffn_dw_taps");
+    if ((st = fold_ffn_taps(D, f, u.ftaps, s)) != HSMLA_OK) return st;
+  }
   r.mark("ffn_dwconv_gelu");
-  HSMLA_TRY(hsmla::launch_dwconv(D.bf, h1, h2, ftaps, 3, D.B, D.gh, D.gw, 4 * C,
-                                 true, nullptr, 1, s));
+  HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.h1, u.h2, u.ftaps, 3, D.B, D.gh, D.gw,
+                                 4 * C, true, nullptr, 1, s));
   r.mark("ffn2_gemm_residual");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, h2, f->w2, x1, out, P, C, 4 * C, s,
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, u.h2, f->w2, u.x1, out, P, C, 4 * C, s,
                                hsmla::GemmSite::kFfn2));
+  return HSMLA_OK;
+}
+
+hsmla_status block_impl(const hsmla_desc* desc, const hsmla_weights* w,
+                        const hsmla_ffn_weights* f, const void* x, void* out,
+                        void* ws, size_t ws_bytes, hipStream_t s, Rec& r) {
+  Dims D;
+  Layout L;
+  hsmla_status st = check_block(desc, w, f, x, out, ws, ws_bytes, &D, &L);
+  if (st != HSMLA_OK) return st;
+  const Bufs u = bufs_for(D, L, ws, HSMLA_OP_BLOCK, 0);
+  if ((st = block_range(D, desc, w, f, x, out, u, true, s, r)) != HSMLA_OK)
+    return st;
   r.end();
   return r.ok ? HSMLA_OK : HSMLA_ERR_HIP;
+}
+
+// Two image ranges on two streams.  Every kernel of the block works image
+// by image with a tiling that does not depend on the batch (bf16 path), so
+// each range reproduces the single-stream result bit for bit.
+hsmla_status block_split_impl(const hsmla_desc* desc, const hsmla_weights* w,
+                              const hsmla_ffn_weights* f, const void* x,
+                              void* out, void* ws, size_t ws_bytes,
+                              hipStream_t s, hipStream_t aux, hipEvent_t fork,
+                              hipEvent_t join) {
+  Dims D;
+  Layout L;
+  hsmla_status st = check_block(desc, w, f, x, out, ws, ws_bytes, &D, &L);
+  if (st != HSMLA_OK) return st;
+  Rec r;
+  // float32 chunks the K/V reduction by batch size: one stream keeps the
+  // result independent of the split
+  if (D.B < 2 || !D.bf) {
+    const Bufs u = bufs_for(D, L, ws, HSMLA_OP_BLOCK, 0);
+    return block_range(D, desc, w, f, x, out, u, true, s, r);
+  }
+  const Bufs u0 = bufs_for(D, L, ws, HSMLA_OP_BLOCK, 0);
+  if ((st = fold_qkv_taps(D, desc, w, u0.taps, s)) != HSMLA_OK) return st;
+  if ((st = fold_ffn_taps(D, f, u0.ftaps, s)) != HSMLA_OK) return st;
+  HSMLA_TRY(hipEventRecord(fork, s));
+  HSMLA_TRY(hipStreamWaitEvent(aux, fork, 0));
+  const int nb0 = (D.B + 1) / 2, nb1 = D.B - nb0;
+  const size_t img = (size_t)D.N * D.C * D.e;
+  const Dims D0 = range_dims(D, nb0), D1 = range_dims(D, nb1);
+  const Bufs u1 = bufs_for(D, L, ws, HSMLA_OP_BLOCK, nb0);
+  if ((st = block_range(D0, desc, w, f, x, out, u0, false, s, r)) != HSMLA_OK)
+    return st;
+  if ((st = block_range(D1, desc, w, f, at(const_cast<void*>(x), nb0 * img),
+                        at(out, nb0 * img), u1, false, aux, r)) != HSMLA_OK)
+    return st;
+  HSMLA_TRY(hipEventRecord(join, aux));
+  HSMLA_TRY(hipStreamWaitEvent(s, join, 0));
+  return HSMLA_OK;
 }
 
 Rec make_rec(void* const* events, const char** names, int32_t n_events,
@@ -622,6 +747,22 @@ hsmla_status hsmla_block_forward(const hsmla_desc* desc, const hsmla_weights* w,
   Rec r;
   return block_impl(desc, w, f, x, out, ws, ws_bytes,
                     static_cast<hipStream_t>(stream), r);
+}
+
+hsmla_status hsmla_block_forward_split(const hsmla_desc* desc,
+                                       const hsmla_weights* w,
+                                       const hsmla_ffn_weights* f,
+                                       const void* x, void* out, void* ws,
+                                       size_t ws_bytes, void* stream,
+                                       void* aux_stream, void* fork_event,
+                                       void* join_event) {
+  if (!fork_event || !join_event) return HSMLA_ERR_NULL;
+  if (aux_stream == stream) return HSMLA_ERR_ARG;
+  return block_split_impl(desc, w, f, x, out, ws, ws_bytes,
+                          static_cast<hipStream_t>(stream),
+                          static_cast<hipStream_t>(aux_stream),
+                          static_cast<hipEvent_t>(fork_event),
+                          static_cast<hipEvent_t>(join_event));
 }
 
 hsmla_status hsmla_forward_timed(const hsmla_desc* desc, const hsmla_weights* w,

@@ -18,6 +18,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhsmla.s
 
 HSMLA_F32, HSMLA_BF16 = 0, 1
 HSMLA_OP_QKV, HSMLA_OP_LINEAR, HSMLA_OP_FORWARD, HSMLA_OP_BLOCK = 0, 1, 2, 3
+(HSMLA_OK, HSMLA_ERR_NULL, HSMLA_ERR_SHAPE, HSMLA_ERR_DTYPE, HSMLA_ERR_ALIGN,
+ HSMLA_ERR_WORKSPACE, HSMLA_ERR_HIP, HSMLA_ERR_ARG) = 0, -1, -2, -3, -4, -5, -6, -7
 HSMLA_ROUTE_TOPK, HSMLA_ROUTE_THRESHOLD, HSMLA_ROUTE_HEAD_THRESHOLD, HSMLA_ROUTE_SOFT = 0, 1, 2, 3
 
 # Every symbol include/hsmla.h declares.
@@ -34,6 +36,7 @@ EXPORTED = (
     "hsmla_sparse_softmax_weighted",
     "hsmla_forward",
     "hsmla_block_forward",
+    "hsmla_block_forward_split",
     "hsmla_forward_timed",
     "hsmla_block_forward_timed",
     "hsmla_status_string",
@@ -114,6 +117,9 @@ def library():
             "hsmla_forward": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, SZ, VP],
             "hsmla_block_forward": [P(hsmla_desc), P(hsmla_weights), P(hsmla_ffn_weights),
                                     VP, VP, VP, SZ, VP],
+            "hsmla_block_forward_split": [P(hsmla_desc), P(hsmla_weights),
+                                          P(hsmla_ffn_weights), VP, VP, VP, SZ, VP,
+                                          VP, VP, VP],
             "hsmla_forward_timed": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, SZ, VP,
                                     P(VP), P(ctypes.c_char_p), I32, P(I32)],
             "hsmla_block_forward_timed": [P(hsmla_desc), P(hsmla_weights),
@@ -279,6 +285,27 @@ def hsmla_block_forward(desc, weights, ffn, x, out, ws):
                                          _ptr(ws), ws.numel() * ws.element_size(),
                                          _stream()),
            "hsmla_block_forward")
+
+
+class SplitStreams:
+    """The second stream and the fork/join events hsmla_block_forward_split
+    takes (default stream priority; events without timing)."""
+
+    def __init__(self):
+        self.aux = torch.cuda.Stream()
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+        # torch creates the underlying events on their first record
+        self.fork.record()
+        self.join.record()
+
+
+def hsmla_block_forward_split(desc, weights, ffn, x, out, ws, split: SplitStreams):
+    _check(library().hsmla_block_forward_split(
+        ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(ffn), _ptr(x),
+        _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(),
+        split.aux.cuda_stream, split.fork.cuda_event, split.join.cuda_event),
+        "hsmla_block_forward_split")
 
 
 def _timed(fn, where, args, events):

@@ -286,6 +286,29 @@ hsmla_status hsmla_block_forward(const hsmla_desc* desc,
                                  void* out, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* hsmla_block_forward with the batch split in two image ranges, the first
+ * on `stream` and the second on `aux_stream`, so that the kernels of one
+ * half fill the chip while those of the other half drain.  Each image's
+ * result does not depend on the batch it is computed in, so `out` and the
+ * workspace views equal those of hsmla_block_forward bit for bit (the
+ * split is a scheduling choice, not a change of the block of FT 3.5).
+ * fork_event, join_event: hipEvent_t handles owned by the caller (created
+ * with default flags or hipEventDisableTiming); the call records fork_event
+ * on `stream` and makes aux_stream wait on it, records join_event on
+ * aux_stream at the end and makes `stream` wait on it, so work queued on
+ * `stream` afterwards sees the whole output.  aux_stream must differ from
+ * `stream`; both keep the default priority.  float32 descriptors and
+ * batches of one image run on `stream` alone.  Concurrent calls must not
+ * share the events or the workspace.  HSMLA_ERR_ARG when aux_stream equals
+ * stream; otherwise the errors of hsmla_block_forward. */
+hsmla_status hsmla_block_forward_split(const hsmla_desc* desc,
+                                       const hsmla_weights* w,
+                                       const hsmla_ffn_weights* f,
+                                       const void* x, void* out, void* ws,
+                                       size_t ws_bytes, void* stream,
+                                       void* aux_stream, void* fork_event,
+                                       void* join_event);
+
 /* Same work, kernels and stream order as hsmla_forward /
  * hsmla_block_forward, plus an event recorded on `stream` before each kernel
  * launch and one after the last, for per-kernel timing by the caller.
