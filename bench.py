@@ -335,8 +335,8 @@ def main():
         for r in (0.0, 0.05, 0.10, 0.25, 0.50):
             wl = scaled(base, keep=r)
             m = DeviceModel(shape(wl), inp)
-            ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 3)
-            ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
+            ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 10)
+            ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
             sweep.append(dict(keep=r, keep_blocks=keep_blocks_for(r, wl.num_blocks),
                               block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
                               block_ms=round(ms_b, 4),
@@ -350,9 +350,9 @@ def main():
             i = min(int(q * (uniq.size - 1)), uniq.size - 2)
             tau = float(np.float32((np.float64(uniq[i]) + np.float64(uniq[i + 1])) / 2))
             m = DeviceModel(shape(base, tau=tau), inp)
-            ms_b, ws_t = time_steps(m, block_step, max(10, args.steps // 2), 3)
+            ms_b, ws_t = time_steps(m, block_step, max(10, args.steps // 2), 10)
             routed = int(m.views(H.HSMLA_OP_BLOCK, ws_t)["counts"].sum().item())
-            ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
+            ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
             sweep.append(dict(routing="threshold", tau=tau,
                               routed_fraction=round(routed / (base.batch * base.num_blocks), 4),
                               block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
@@ -371,9 +371,9 @@ def main():
         tau = float(np.float32((np.float64(uniq[i]) + np.float64(uniq[i + 1])) / 2))
         del m
         m = DeviceModel(shape(base, tau=tau, per_head=True), inp)
-        ms_b, ws_t = time_steps(m, block_step, max(10, args.steps // 2), 3)
+        ms_b, ws_t = time_steps(m, block_step, max(10, args.steps // 2), 10)
         routed = int(m.views(H.HSMLA_OP_BLOCK, ws_t)["counts"].sum().item())
-        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
+        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
         sweep.append(dict(routing="threshold_per_head", tau=tau,
                           routed_fraction=round(routed / (base.batch * base.num_blocks
                                                           * base.heads), 4),
@@ -385,8 +385,8 @@ def main():
         # the training-time mixture forward: every block refined, residual
         # scaled by its score
         m = DeviceModel(shape(base, soft=True), inp)
-        ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 3)
-        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
+        ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 10)
+        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
         sweep.append(dict(routing="soft_mixture", routed_fraction=1.0,
                           block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
                           block_ms=round(ms_b, 4),
@@ -397,8 +397,8 @@ def main():
         # identity + 3x3 + 5x5 + 7x7 branches, top-k at the base keep ratio
         wl = scaled(base, branches=(3, 5, 7), gate_conv=True)
         m = DeviceModel(shape(wl), make_inputs(wl))
-        ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 3)
-        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 3)
+        ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 10)
+        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
         sweep.append(dict(variant="gate_dwconv3x3+branches_3_5_7", keep=base.keep,
                           keep_blocks=base.keep_blocks,
                           block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
