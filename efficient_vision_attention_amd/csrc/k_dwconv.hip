@@ -7,10 +7,13 @@
 // channel before the convolution runs.  The FFN's 3x3 depthwise conv (FT 3.5
 // block equation) uses the same kernel with a GELU epilogue.
 //
-// Kernel shape: a workgroup owns 16 columns x 64 channels of a strip of 32
-// output rows; each thread handles 4 consecutive channels of one column
-// (8-byte bf16 accesses, 128 contiguous bytes per 16 lanes) and keeps the
-// kmax partial output rows that the current input row feeds in registers.
+// Two kernel shapes, both walking down a strip of 32 output rows with the
+// kmax partial output rows that the current input row feeds kept in
+// registers: up to 3x3 the workgroup stages each input row in LDS and every
+// thread reads its horizontal neighbours there (dwconv_lds); the 5x5 and 7x7
+// tap sets take so many registers that a register-only kernel, each thread
+// loading its neighbours through L1, keeps more loads in flight
+// (dwconv_stream).
 #include "common.h"
 #include "kernels.h"
 
@@ -61,12 +64,36 @@ __device__ __forceinline__ float gelu_erf(float x) {
 constexpr int TH = 32;   // output rows per workgroup strip
 constexpr int kPoolMinBlock = 4;
 constexpr int kXcds = 8;
-constexpr int kWgChannels = 64;  // channels per workgroup
 
-// V consecutive channels as loaded from memory (V = 2 or 4), converted to
-// float at use.
+// V consecutive channels as loaded (V = 2, 4 or 8), converted to float at
+// use.
 template <typename T, int V>
 struct Raw;
+template <>
+struct Raw<bf16, 8> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void cvt(float* f) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct Raw<float, 8> {
+  float4 u, v;
+  __device__ __forceinline__ void load(const float* p) {
+    u = *reinterpret_cast<const float4*>(p);
+    v = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void cvt(float* f) const {
+    f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+    f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
+  }
+};
 template <>
 struct Raw<bf16, 4> {
   uint2 u;
@@ -142,9 +169,12 @@ __device__ __forceinline__ void storev_round(T* p, float* v) {
   }
 }
 
-// A thread owns one output column x and V consecutive channels of a 32-row
-// strip and walks down the input rows of the strip.  For each input row it
-// loads the K horizontal neighbours it needs (the K-fold reuse across
+constexpr int kStreamChannels = 64;  // channels per workgroup
+
+// Register-streaming variant (the wider kernels, whose taps take most of the
+// registers).  A thread owns one output column x and V consecutive channels
+// of a 32-row strip and walks down the input rows of the strip.  For each
+// input row it loads the K horizontal neighbours it needs (the K-fold reuse across
 // neighbouring threads is served by the L1), and the row feeds the K partial
 // output rows it belongs to, kept in registers.  NB rows of loads are in
 // flight at any time; there is no LDS and no barrier, so every wave streams
@@ -166,9 +196,9 @@ __global__ __launch_bounds__(256) void dwconv_stream(
     int gh, int gw, int ch, int col_tiles, int ch_tiles, int strips,
     int total, int per_xcd) {
   constexpr int R = (K - 1) / 2;
-  constexpr int CG = kWgChannels / V;  // channel groups per workgroup
+  constexpr int CG = kStreamChannels / V;  // channel groups per workgroup
   constexpr int TW = 256 / CG;         // columns per workgroup
-  __shared__ float red[POOL ? TH / kPoolMinBlock : 1][POOL ? TW : 1][POOL ? kWgChannels : 1];
+  __shared__ float red[POOL ? TH / kPoolMinBlock : 1][POOL ? TW : 1][POOL ? kStreamChannels : 1];
   const int bid = blockIdx.x;
   const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
   if (tile >= total) return;
@@ -183,7 +213,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   const int tc = threadIdx.x % CG;
   const int tx = threadIdx.x / CG;
   const int x = col_t * TW + tx;
-  const int c = ch_t * kWgChannels + tc * V;
+  const int c = ch_t * kStreamChannels + tc * V;
   const bool c_ok = c < ch;
   const int y0 = strip * TH;
   const size_t img = (size_t)b * gh * gw;
@@ -311,43 +341,321 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   }
 }
 
-template <typename T, int K, bool GELU, int V, int NB = 3>
+// Buffer-resource loads and stores (raw, stride 0): an offset past the
+// resource's byte count reads zeros and drops stores in hardware, so edge
+// lanes need no branch and every memory instruction is unconditional (the
+// compiler's wait counts then stay exact).
+constexpr int kOob = INT32_MIN;  // an offset no resource here reaches
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base,
+                                                          int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           bytes, 0x00020000);
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int V>
+__device__ __forceinline__ void store_buf(__amdgpu_buffer_rsrc_t r, int off,
+                                          const float* v) {
+  if constexpr (sizeof(T) == 2 && V == 8) {
+    const i32x4 d = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]),
+                     (int)pack_bf16x2(v[4], v[5]), (int)pack_bf16x2(v[6], v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+  } else if constexpr (sizeof(T) == 4 && V == 8) {
+    const i32x4 d0 = {__float_as_int(v[0]), __float_as_int(v[1]),
+                      __float_as_int(v[2]), __float_as_int(v[3])};
+    const i32x4 d1 = {__float_as_int(v[4]), __float_as_int(v[5]),
+                      __float_as_int(v[6]), __float_as_int(v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(d0, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(d1, r, off + (off == kOob ? 0 : 16), 0, 0);
+  } else if constexpr (sizeof(T) == 2 && V == 4) {
+    const i32x2 d = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 0);
+  } else if constexpr (sizeof(T) == 2 && V == 2) {
+    __builtin_amdgcn_raw_buffer_store_b32((int)pack_bf16x2(v[0], v[1]), r, off, 0, 0);
+  } else if constexpr (V == 4) {
+    const i32x4 d = {__float_as_int(v[0]), __float_as_int(v[1]),
+                     __float_as_int(v[2]), __float_as_int(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+  } else {
+    const i32x2 d = {__float_as_int(v[0]), __float_as_int(v[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 0);
+  }
+}
+
+// Round v to T in place (the values as stored).
+template <typename T, int V>
+__device__ __forceinline__ void round_to(float* v) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      const uint32_t w = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+      v[2 * i] = __uint_as_float(w << 16);
+      v[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+    }
+  }
+}
+
+// LDS-staged variant.  The workgroup (TW columns x 64 channels of a TH-row
+// strip, as above) loads each input row once, TW + 2R columns wide, with
+// 16-byte loads spread over all 256 threads (at most a few chunks each), and
+// keeps P rows of those loads in flight in registers.  Rows pass through
+// two LDS slots; one barrier per row orders "row r written" before "row r
+// read" and "row r - 1 read" before "slot reused".  Each thread then reads
+// its K horizontal neighbours from LDS instead of from L1, and accumulates
+// as above (K partial output rows in registers).  Compared with the
+// register-only kernel the bytes in flight per workgroup no longer scale
+// with the per-thread tap registers.
+template <typename T, int K, bool GELU, int V, int P, bool POOL, int WC>
+__global__ __launch_bounds__(256) void dwconv_lds(
+    const T* __restrict__ in, T* __restrict__ out,
+    const float* __restrict__ weff, float* __restrict__ bsum, int block,
+    int gh, int gw, int ch, int col_tiles, int ch_tiles, int strips,
+    int total, int per_xcd) {
+  constexpr int R = (K - 1) / 2;
+  constexpr int CG = WC / V;  // channel groups per workgroup
+  constexpr int TW = 256 / CG;         // columns per workgroup
+  constexpr int LC = TW + 2 * R;       // columns per staged row
+  constexpr int EPC = 16 / (int)sizeof(T);       // elements per 16-byte chunk
+  constexpr int CPC = WC / EPC;         // chunks per column
+  constexpr int CHUNKS = LC * CPC;               // chunks per row
+  constexpr int LPT = (CHUNKS + 255) / 256;      // chunks per thread
+  constexpr int SLOT = LPT * 256 * 16;           // bytes per LDS row slot
+  constexpr int CB = WC * (int)sizeof(T);  // bytes per staged column
+  // group of rows after which every register index repeats
+  constexpr int G = (K % P == 0) ? K : (P % K == 0 ? P : K * P);
+  __shared__ __attribute__((aligned(16))) char ring[2 * SLOT];
+  __shared__ float red[POOL ? TH / kPoolMinBlock : 1][POOL ? TW : 1][POOL ? WC : 1];
+  const int bid = blockIdx.x;
+  const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
+  if (tile >= total) return;
+  int rest = tile;
+  const int col_t = rest % col_tiles;
+  rest /= col_tiles;
+  const int ch_t = rest % ch_tiles;
+  rest /= ch_tiles;
+  const int strip = rest % strips;
+  const int b = rest / strips;
+
+  const int tid = threadIdx.x;
+  const int tc = tid % CG;
+  const int tx = tid / CG;
+  const int x0 = col_t * TW;
+  const int x = x0 + tx;
+  const int c0 = ch_t * WC;
+  const int c = c0 + tc * V;
+  const bool c_ok = c < ch;
+  const int y0 = strip * TH;
+  const size_t img = (size_t)b * gh * gw;
+
+  float w[K][K][V];
+#pragma unroll
+  for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+    for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        w[ky][kx][j] = c_ok ? weff[(size_t)(ky * K + kx) * ch + c + j] : 0.f;
+
+  // This thread's chunks of a staged row: byte offset from the row's first
+  // in-grid staged column, or kOob for chunks outside the grid (read as 0).
+  const int lx0 = max(x0 - R, 0);
+  const int lx1 = min(gw, x0 + TW + R);
+  const int row_bytes = (lx1 - lx0) * ch * (int)sizeof(T);
+  int ld_off[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int q = tid + 256 * i;
+    const int col = q / CPC, part = q % CPC;
+    const int xg = x0 - R + col;
+    const int cg = c0 + part * EPC;
+    const bool ok = q < CHUNKS && xg >= 0 && xg < gw && cg < ch;
+    ld_off[i] = ok ? ((xg - lx0) * ch + cg) * (int)sizeof(T) : kOob;
+  }
+  auto load_row = [&](uint4 (&d)[LPT], int r) {
+    const bool in_grid = r >= 0 && r < gh;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
+        in + (img + (size_t)min(max(r, 0), gh - 1) * gw + lx0) * ch,
+        in_grid ? row_bytes : 0);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, ld_off[i], 0, 0);
+      d[i] = uint4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
+    }
+  };
+  // every thread writes (chunks past the row land in the slot's spare room)
+  auto store_row = [&](const uint4 (&d)[LPT], int slot) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i)
+      *reinterpret_cast<uint4*>(ring + slot * SLOT + (tid + 256 * i) * 16) = d[i];
+  };
+  // output: this thread's byte offset within its output row segment
+  const int ox1 = min(gw, x0 + TW);
+  const int out_bytes = (ox1 - x0) * ch * (int)sizeof(T);
+  const int st_off = (x < gw && c_ok) ? (tx * ch + c) * (int)sizeof(T) : kOob;
+
+  float acc[K][V];
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[i][j] = 0.f;
+  float psum[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) psum[j] = 0.f;
+
+  const int y_end = min(gh, y0 + TH);
+  const int r_begin = y0 - R;
+  const int nrows = y_end + R - r_begin;
+
+  uint4 pre[P][LPT];
+#pragma unroll
+  for (int q = 0; q < P; ++q) load_row(pre[q], r_begin + q);
+  store_row(pre[0], 0);
+  load_row(pre[0], r_begin + P);
+  const char* my = ring + tx * CB + tc * V * (int)sizeof(T);
+  for (int u0 = 0; u0 < nrows; u0 += G) {
+#pragma unroll
+    for (int v = 0; v < G; ++v) {
+      const int u = u0 + v;
+      if (u >= nrows) break;
+      const int r = r_begin + u;
+      __syncthreads();
+      if (r >= 0 && r < gh) {
+        float xin[K][V];
+#pragma unroll
+        for (int kx = 0; kx < K; ++kx) {
+          Raw<T, V> rr;
+          rr.load(reinterpret_cast<const T*>(my + (u & 1) * SLOT + kx * CB));
+          rr.cvt(xin[kx]);
+        }
+        // input row r feeds output row r - R + i with vertical tap K - 1 - i
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          const int slot = (v - R + i + G) % K;
+#pragma unroll
+          for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+              acc[slot][j] = fmaf(w[K - 1 - i][kx][j], xin[kx][j], acc[slot][j]);
+        }
+      }
+      // stage row r + 1 (its loads were issued P - 1 rows ago) and issue
+      // the loads of row r + 1 + P
+      store_row(pre[(v + 1) % P], (u + 1) & 1);
+      load_row(pre[(v + 1) % P], r + 1 + P);
+      const int done = (v - R + G) % K;  // slot of output row r - R
+      const int yo = r - R;
+      const bool row_out = yo >= y0 && yo < y_end;  // uniform
+      {
+        float o[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) o[j] = GELU ? gelu_erf(acc[done][j]) : acc[done][j];
+        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
+            out + (img + (size_t)min(max(yo, 0), gh - 1) * gw + x0) * ch,
+            row_out ? out_bytes : 0);
+        store_buf<T, V>(rs, st_off, o);
+        if constexpr (POOL) {
+          round_to<T, V>(o);
+          const bool mine = row_out && st_off != kOob;
+#pragma unroll
+          for (int j = 0; j < V; ++j) psum[j] += mine ? o[j] : 0.f;
+        }
+      }
+      if constexpr (POOL) {
+        if (yo >= y0 && yo < y_end && (yo + 1) % block == 0) {
+          const int br = (yo - y0) / block;
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            red[br][tx][tc * V + j] = psum[j];
+            psum[j] = 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[done][j] = 0.f;
+    }
+  }
+  if constexpr (POOL) {
+    __syncthreads();
+    if (tx % block == 0 && x < gw && c_ok) {
+      const int nbc = gw / block;
+      for (int br = 0; br < (y_end - y0) / block; ++br) {
+        const size_t t = (size_t)(y0 / block + br) * nbc + x / block;
+        float* dst = bsum + ((size_t)b * (gh / block) * nbc + t) * ch + c;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          float sm = 0.f;
+          for (int q = 0; q < block; ++q) sm += red[br][tx + q][tc * V + j];
+          dst[j] = sm;
+        }
+      }
+    }
+  }
+}
+
+// Per kernel size: channels per thread V, rows of loads in flight P and
+// channels per workgroup WC (the workgroup is 256 / (WC / V) columns wide).
+// Sizes up to 3 take the LDS-staged kernel, 5 and 7 the register-streaming
+// one (measured: at 25 or 49 taps per channel the taps' registers leave the
+// LDS kernel too few waves, while the streaming kernel keeps enough loads in
+// flight with 2 channels per thread).
+struct DwCfg {
+  int v, p, wc;
+};
+constexpr DwCfg dw_cfg(int k, bool gelu) {
+  return k <= 3 ? DwCfg{4, 4, 64} : DwCfg{2, k == 5 ? 4 : 3, kStreamChannels};
+  (void)gelu;
+}
+constexpr int dw_width(int k, bool gelu) {
+  return 256 / (dw_cfg(k, gelu).wc / dw_cfg(k, gelu).v);
+}
+
+template <typename T, int K, bool GELU>
 hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
                   int block, int batch, int gh, int gw, int ch, hipStream_t s) {
-  constexpr int TW = 256 / (kWgChannels / V);
+  constexpr DwCfg cf = dw_cfg(K, GELU);
+  constexpr int TW = dw_width(K, GELU);
   const int col_tiles = (gw + TW - 1) / TW;
-  const int ch_tiles = (ch + kWgChannels - 1) / kWgChannels;
+  const int ch_tiles = (ch + cf.wc - 1) / cf.wc;
   const int strips = (gh + TH - 1) / TH;
   const int total = col_tiles * ch_tiles * strips * batch;
   const int per_xcd = (total + kXcds - 1) / kXcds;
+  if constexpr (K >= 5) {
+    if (bsum && !GELU)
+      dwconv_stream<T, K, false, cf.v, cf.p, true><<<per_xcd * kXcds, 256, 0, s>>>(
+          static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
+          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
+    else
+      dwconv_stream<T, K, GELU, cf.v, cf.p, false><<<per_xcd * kXcds, 256, 0, s>>>(
+          static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
+          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
+    return hipGetLastError();
+  }
   if constexpr (!GELU) {
     if (bsum) {
-      dwconv_stream<T, K, false, V, NB, true><<<per_xcd * kXcds, 256, 0, s>>>(
+      dwconv_lds<T, K, false, cf.v, cf.p, true, cf.wc><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
           gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
       return hipGetLastError();
     }
   }
-    dwconv_stream<T, K, GELU, V, NB, false><<<per_xcd * kXcds, 256, 0, s>>>(
-        static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
-        gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
+  dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc><<<per_xcd * kXcds, 256, 0, s>>>(
+      static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
+      gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
   return hipGetLastError();
 }
-
-// Wider kernels keep fewer channels per thread so their taps fit in
-// registers at useful occupancy; rows in flight (NB) measured per size.
-// channels per thread for each kernel size (also fixes the workgroup width)
-constexpr int vec_for(int kmax) { return kmax <= 3 ? 4 : 2; }
 
 template <typename T, bool GELU>
 hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
                       float* bsum, int block, int batch, int gh, int gw, int ch,
                       hipStream_t s) {
   switch (kmax) {
-    case 1: return run_dw<T, 1, GELU, vec_for(1)>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
-    case 3: return run_dw<T, 3, GELU, vec_for(3), GELU ? 2 : 3>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
-    case 5: return run_dw<T, 5, GELU, vec_for(5), 4>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
-    case 7: return run_dw<T, 7, GELU, vec_for(7), 3>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
+    case 1: return run_dw<T, 1, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
+    case 3: return run_dw<T, 3, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
+    case 5: return run_dw<T, 5, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
+    case 7: return run_dw<T, 7, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -371,7 +679,7 @@ hipError_t launch_dw_taps(bool bf, const void* const* kernels, const int* ks,
 }
 
 bool dwconv_can_pool(int kmax, int block) {
-  const int tw = 256 / (kWgChannels / vec_for(kmax));
+  const int tw = dw_width(kmax, false);
   return block >= kPoolMinBlock && tw % block == 0 && TH % block == 0;
 }
 
