@@ -65,6 +65,21 @@ constexpr int TH = 32;   // output rows per workgroup strip
 constexpr int kPoolMinBlock = 4;
 constexpr int kXcds = 8;
 
+// Buffer-resource loads and stores (raw, stride 0): an offset past the
+// resource's byte count reads zeros and drops stores in hardware, so edge
+// lanes need no branch and every memory instruction is unconditional (the
+// compiler's wait counts then stay exact).
+constexpr int kOob = INT32_MIN;  // an offset no resource here reaches
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base,
+                                                          int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           bytes, 0x00020000);
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 // V consecutive channels as loaded (V = 2, 4 or 8), converted to float at
 // use.
 template <typename T, int V>
@@ -73,6 +88,10 @@ template <>
 struct Raw<bf16, 8> {
   uint4 u;
   __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int off) {
+    const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    u = uint4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
+  }
   __device__ __forceinline__ void cvt(float* f) const {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -89,6 +108,12 @@ struct Raw<float, 8> {
     u = *reinterpret_cast<const float4*>(p);
     v = *reinterpret_cast<const float4*>(p + 4);
   }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int off) {
+    const i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const i32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off == kOob ? off : off + 16, 0, 0);
+    u = make_float4(__int_as_float(a.x), __int_as_float(a.y), __int_as_float(a.z), __int_as_float(a.w));
+    v = make_float4(__int_as_float(b.x), __int_as_float(b.y), __int_as_float(b.z), __int_as_float(b.w));
+  }
   __device__ __forceinline__ void cvt(float* f) const {
     f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
     f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
@@ -98,6 +123,10 @@ template <>
 struct Raw<bf16, 4> {
   uint2 u;
   __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int off) {
+    const i32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    u = uint2{(uint32_t)t.x, (uint32_t)t.y};
+  }
   __device__ __forceinline__ void cvt(float* f) const {
     f[0] = __uint_as_float(u.x << 16);
     f[1] = __uint_as_float(u.x & 0xffff0000u);
@@ -109,6 +138,9 @@ template <>
 struct Raw<bf16, 2> {
   uint32_t u;
   __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int off) {
+    u = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
   __device__ __forceinline__ void cvt(float* f) const {
     f[0] = __uint_as_float(u << 16);
     f[1] = __uint_as_float(u & 0xffff0000u);
@@ -118,6 +150,10 @@ template <>
 struct Raw<float, 4> {
   float4 u;
   __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int off) {
+    const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    u = make_float4(__int_as_float(t.x), __int_as_float(t.y), __int_as_float(t.z), __int_as_float(t.w));
+  }
   __device__ __forceinline__ void cvt(float* f) const {
     f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
   }
@@ -126,45 +162,51 @@ template <>
 struct Raw<float, 2> {
   float2 u;
   __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float2*>(p); }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, int off) {
+    const i32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    u = make_float2(__int_as_float(t.x), __int_as_float(t.y));
+  }
   __device__ __forceinline__ void cvt(float* f) const { f[0] = u.x; f[1] = u.y; }
 };
 
 template <typename T, int V>
-__device__ __forceinline__ void storev(T* p, const float* v);
-template <>
-__device__ __forceinline__ void storev<bf16, 4>(bf16* p, const float* v) {
-  *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-}
-template <>
-__device__ __forceinline__ void storev<bf16, 2>(bf16* p, const float* v) {
-  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v[0], v[1]);
-}
-template <>
-__device__ __forceinline__ void storev<float, 4>(float* p, const float* v) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-template <>
-__device__ __forceinline__ void storev<float, 2>(float* p, const float* v) {
-  *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+__device__ __forceinline__ void store_buf(__amdgpu_buffer_rsrc_t r, int off,
+                                          const float* v) {
+  if constexpr (sizeof(T) == 2 && V == 8) {
+    const i32x4 d = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]),
+                     (int)pack_bf16x2(v[4], v[5]), (int)pack_bf16x2(v[6], v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+  } else if constexpr (sizeof(T) == 4 && V == 8) {
+    const i32x4 d0 = {__float_as_int(v[0]), __float_as_int(v[1]),
+                      __float_as_int(v[2]), __float_as_int(v[3])};
+    const i32x4 d1 = {__float_as_int(v[4]), __float_as_int(v[5]),
+                      __float_as_int(v[6]), __float_as_int(v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(d0, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(d1, r, off + (off == kOob ? 0 : 16), 0, 0);
+  } else if constexpr (sizeof(T) == 2 && V == 4) {
+    const i32x2 d = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 0);
+  } else if constexpr (sizeof(T) == 2 && V == 2) {
+    __builtin_amdgcn_raw_buffer_store_b32((int)pack_bf16x2(v[0], v[1]), r, off, 0, 0);
+  } else if constexpr (V == 4) {
+    const i32x4 d = {__float_as_int(v[0]), __float_as_int(v[1]),
+                     __float_as_int(v[2]), __float_as_int(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+  } else {
+    const i32x2 d = {__float_as_int(v[0]), __float_as_int(v[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 0);
+  }
 }
 
-// Store, and leave in v the values as stored (rounded to T).
+// Round v to T in place (the values as stored).
 template <typename T, int V>
-__device__ __forceinline__ void storev_round(T* p, float* v) {
-  if constexpr (sizeof(T) == 4) {
-    storev<T, V>(p, v);
-  } else {
-    uint32_t w[V / 2];
-#pragma unroll
-    for (int i = 0; i < V / 2; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    if constexpr (V == 4)
-      *reinterpret_cast<uint2*>(p) = uint2{w[0], w[1]};
-    else
-      *reinterpret_cast<uint32_t*>(p) = w[0];
+__device__ __forceinline__ void round_to(float* v) {
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int i = 0; i < V / 2; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      const uint32_t w = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+      v[2 * i] = __uint_as_float(w << 16);
+      v[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
     }
   }
 }
@@ -239,24 +281,29 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   const int y_end = min(gh, y0 + TH);
   const int r_begin = y0 - R, r_end = y_end + R;
 
-  // Branch-free row loads: addresses are clamped into the tensor and the
-  // values of out-of-grid taps are zeroed afterwards.
-  const int cc = c_ok ? c : ch - V;
-  bool col_ok[K];
+  // Row loads through a buffer resource over the workgroup's in-grid
+  // columns of the row: taps outside the grid (and rows outside it) read
+  // zeros, with no branch and no select.
+  const int x0 = col_t * TW;
+  const int lx0 = max(x0 - R, 0);
+  const int row_bytes = (min(gw, x0 + TW + R) - lx0) * ch * (int)sizeof(T);
   int col_off[K];
 #pragma unroll
   for (int kx = 0; kx < K; ++kx) {
     const int xx = x + kx - R;
-    col_ok[kx] = xx >= 0 && xx < gw;
-    col_off[kx] = min(max(xx, 0), gw - 1) * ch + cc;
+    col_off[kx] = (xx >= 0 && xx < gw && c_ok) ? ((xx - lx0) * ch + c) * (int)sizeof(T)
+                                               : kOob;
   }
   auto load_row = [&](Raw<T, V> (&rr)[K], int r) {
-    const T* base = in + (img + (size_t)min(max(r, 0), gh - 1) * gw) * ch;
+    const bool in_grid = r >= 0 && r < gh;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
+        in + (img + (size_t)min(max(r, 0), gh - 1) * gw + lx0) * ch,
+        in_grid ? row_bytes : 0);
 #pragma unroll
-    for (int kx = 0; kx < K; ++kx) rr[kx].load(base + col_off[kx]);
+    for (int kx = 0; kx < K; ++kx) rr[kx].load_buf(rs, col_off[kx]);
   };
-  // only tiles touching the left/right border have lanes with invalid taps
-  const bool edge_tile = col_t * TW - R < 0 || col_t * TW + TW + R > gw;
+  const int out_bytes = (min(gw, x0 + TW) - x0) * ch * (int)sizeof(T);
+  const int st_off = (x < gw && c_ok) ? (tx * ch + c) * (int)sizeof(T) : kOob;
 
   Raw<T, V> rbuf[NB][K];
 #pragma unroll
@@ -275,12 +322,6 @@ __global__ __launch_bounds__(256) void dwconv_stream(
         float xin[K][V];
 #pragma unroll
         for (int kx = 0; kx < K; ++kx) cur[kx].cvt(xin[kx]);
-        if (edge_tile) {
-#pragma unroll
-          for (int kx = 0; kx < K; ++kx)
-#pragma unroll
-            for (int j = 0; j < V; ++j) xin[kx][j] = col_ok[kx] ? xin[kx][j] : 0.f;
-        }
         // input row r feeds output row r - R + i with vertical tap K - 1 - i
 #pragma unroll
         for (int i = 0; i < K; ++i) {
@@ -296,16 +337,20 @@ __global__ __launch_bounds__(256) void dwconv_stream(
       load_row(cur, r + NB);
       const int done = (u - R + NB * K) % K;  // slot of output row r - R
       const int yo = r - R;
-      if (yo >= y0 && yo < y_end && x < gw && c_ok) {
+      const bool row_out = yo >= y0 && yo < y_end;  // uniform
+      {
         float v[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) v[j] = GELU ? gelu_erf(acc[done][j]) : acc[done][j];
+        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
+            out + (img + (size_t)min(max(yo, 0), gh - 1) * gw + x0) * ch,
+            row_out ? out_bytes : 0);
+        store_buf<T, V>(rs, st_off, v);
         if constexpr (POOL) {
-          storev_round<T, V>(out + (img + (size_t)yo * gw + x) * ch + c, v);
+          round_to<T, V>(v);
+          const bool mine = row_out && st_off != kOob;
 #pragma unroll
-          for (int j = 0; j < V; ++j) psum[j] += v[j];
-        } else {
-          storev<T, V>(out + (img + (size_t)yo * gw + x) * ch + c, v);
+          for (int j = 0; j < V; ++j) psum[j] += mine ? v[j] : 0.f;
         }
       }
       if constexpr (POOL) {
@@ -337,63 +382,6 @@ __global__ __launch_bounds__(256) void dwconv_stream(
           dst[j] = sm;
         }
       }
-    }
-  }
-}
-
-// Buffer-resource loads and stores (raw, stride 0): an offset past the
-// resource's byte count reads zeros and drops stores in hardware, so edge
-// lanes need no branch and every memory instruction is unconditional (the
-// compiler's wait counts then stay exact).
-constexpr int kOob = INT32_MIN;  // an offset no resource here reaches
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base,
-                                                          int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           bytes, 0x00020000);
-}
-
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-template <typename T, int V>
-__device__ __forceinline__ void store_buf(__amdgpu_buffer_rsrc_t r, int off,
-                                          const float* v) {
-  if constexpr (sizeof(T) == 2 && V == 8) {
-    const i32x4 d = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]),
-                     (int)pack_bf16x2(v[4], v[5]), (int)pack_bf16x2(v[6], v[7])};
-    __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
-  } else if constexpr (sizeof(T) == 4 && V == 8) {
-    const i32x4 d0 = {__float_as_int(v[0]), __float_as_int(v[1]),
-                      __float_as_int(v[2]), __float_as_int(v[3])};
-    const i32x4 d1 = {__float_as_int(v[4]), __float_as_int(v[5]),
-                      __float_as_int(v[6]), __float_as_int(v[7])};
-    __builtin_amdgcn_raw_buffer_store_b128(d0, r, off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(d1, r, off + (off == kOob ? 0 : 16), 0, 0);
-  } else if constexpr (sizeof(T) == 2 && V == 4) {
-    const i32x2 d = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
-    __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 0);
-  } else if constexpr (sizeof(T) == 2 && V == 2) {
-    __builtin_amdgcn_raw_buffer_store_b32((int)pack_bf16x2(v[0], v[1]), r, off, 0, 0);
-  } else if constexpr (V == 4) {
-    const i32x4 d = {__float_as_int(v[0]), __float_as_int(v[1]),
-                     __float_as_int(v[2]), __float_as_int(v[3])};
-    __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
-  } else {
-    const i32x2 d = {__float_as_int(v[0]), __float_as_int(v[1])};
-    __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 0);
-  }
-}
-
-// Round v to T in place (the values as stored).
-template <typename T, int V>
-__device__ __forceinline__ void round_to(float* v) {
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int i = 0; i < V / 2; ++i) {
-      const uint32_t w = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-      v[2 * i] = __uint_as_float(w << 16);
-      v[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
     }
   }
 }
