@@ -288,63 +288,95 @@ Dims range_dims(const Dims& D, int nb) {
   return r;
 }
 
-// Steps 1-5 into the workspace views (o holds the refined output).  D may
-// describe a range of the images (range_dims), u the matching pointers.
-hsmla_status run_module(const Dims& D, const hsmla_desc* d,
-                        const hsmla_weights* w, const void* x, const Bufs& u,
-                        bool fold, hipStream_t s, Rec& r) {
-  void* qkv = u.qkv;
-  void* qkvh = u.qkvh;
-  void* o = u.o;
-  float* kv = u.kv;
-  float* ksum = u.ksum;
-  float* part = u.part;
-  float* taps = u.taps;
-  float* scores = u.scores;
-  int32_t* sel = u.sel;
-  int32_t* counts = u.counts;
-  float* hscores = u.hscores;
+// Steps 1-5 into the workspace views (o holds the refined output), as
+// numbered stages of one or two launches each, so that two image ranges can
+// interleave their launches (module_stage(0..kModuleStages-1) in order is
+// the whole module).  D may describe a range of the images (range_dims), u
+// the matching pointers.  fold: fold the branch taps in line (otherwise
+// they are already in u.taps).
+constexpr int kModuleStages = 8;
+
+hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
+                          const hsmla_weights* w, const void* x, const Bufs& u,
+                          bool fold, hipStream_t s, Rec& r) {
   // the plain gate's block sums come out of the depthwise conv when its
   // workgroup shape allows; the gate then only forms the logits
   float* bsum = (!w->gate_dw && hsmla::dwconv_can_pool(D.kmax, D.Bs)) ? u.bsum
                                                                        : nullptr;
-  hsmla_status st = run_qkv(D, d, w, x, qkv, qkvh, taps, bsum, fold, s, r);
-  if (st != HSMLA_OK) return st;
-  r.mark("kv_state");
-  HSMLA_TRY(hsmla::launch_kv_state(D.bf, qkvh, kv, ksum, part, D.B, D.N, D.H, s));
-  r.mark("lin_apply");
-  HSMLA_TRY(hsmla::launch_lin_apply(D.bf, qkvh, kv, ksum, o, D.B, D.N, D.H, s));
-  r.mark("gate_scores");
-  if (bsum)
-    HSMLA_TRY(hsmla::launch_gate_from_sums(bsum, w->gate_w, w->gate_b, scores,
-                                           hscores, D.B, D.T, D.H, D.Bs, s));
-  else
-    HSMLA_TRY(hsmla::launch_gate_scores(D.bf, qkvh, w->gate_w, w->gate_b,
-                                        w->gate_dw, scores, hscores, D.B, D.gh,
-                                        D.gw, D.H, D.Bs, s));
-  if (D.soft) {
-    r.mark("sparse_softmax");
-    HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, nullptr, nullptr, scores, o,
-                                   D.B, D.gh, D.gw, D.H, D.Bs, D.w, D.T,
-                                   sel_layout(D), s));
-    return HSMLA_OK;
+  switch (st) {
+    case 0:
+      r.mark("qkv_gemm");
+      HSMLA_TRY(hsmla::launch_gemm(D.bf, x, w->w_qkv, nullptr, u.qkv, (int)D.P,
+                                   3 * D.C, D.C, s, hsmla::GemmSite::kQkv));
+      return HSMLA_OK;
+    case 1:
+      if (!fold) return HSMLA_OK;
+      r.mark("dw_taps");
+      return fold_qkv_taps(D, d, w, u.taps, s);
+    case 2:
+      r.mark("dwconv_qkv");
+      HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.qkv, u.qkvh, u.taps, D.kmax, D.B, D.gh,
+                                     D.gw, 3 * D.C, false, bsum, D.Bs, s));
+      return HSMLA_OK;
+    case 3:
+      r.mark("kv_state");
+      HSMLA_TRY(hsmla::launch_kv_state(D.bf, u.qkvh, u.kv, u.ksum, u.part, D.B,
+                                       D.N, D.H, s));
+      return HSMLA_OK;
+    case 4:
+      r.mark("lin_apply");
+      HSMLA_TRY(hsmla::launch_lin_apply(D.bf, u.qkvh, u.kv, u.ksum, u.o, D.B,
+                                        D.N, D.H, s));
+      return HSMLA_OK;
+    case 5:
+      r.mark("gate_scores");
+      if (bsum)
+        HSMLA_TRY(hsmla::launch_gate_from_sums(bsum, w->gate_w, w->gate_b,
+                                               u.scores, u.hscores, D.B, D.T,
+                                               D.H, D.Bs, s));
+      else
+        HSMLA_TRY(hsmla::launch_gate_scores(D.bf, u.qkvh, w->gate_w, w->gate_b,
+                                            w->gate_dw, u.scores, u.hscores,
+                                            D.B, D.gh, D.gw, D.H, D.Bs, s));
+      return HSMLA_OK;
+    case 6:
+      if (D.soft) return HSMLA_OK;  // every block, weighted: no list
+      if (D.ph) {
+        r.mark("threshold_heads");
+        HSMLA_TRY(hsmla::launch_threshold_heads(u.hscores, nullptr, u.sel,
+                                                u.counts, D.B, D.T, D.H, D.tau, s));
+      } else if (D.thr) {
+        r.mark("threshold");
+        HSMLA_TRY(hsmla::launch_threshold(u.scores, nullptr, u.sel, u.counts, D.B,
+                                          D.T, D.tau, s));
+      } else {
+        r.mark("topk");
+        HSMLA_TRY(hsmla::launch_topk(u.scores, nullptr, u.sel, D.B, D.T, D.k, s));
+      }
+      return HSMLA_OK;
+    case 7:
+      r.mark("sparse_softmax");
+      if (D.soft)
+        HSMLA_TRY(hsmla::launch_sparse(D.bf, u.qkv, u.qkvh, nullptr, nullptr,
+                                       u.scores, u.o, D.B, D.gh, D.gw, D.H, D.Bs,
+                                       D.w, D.T, sel_layout(D), s));
+      else
+        HSMLA_TRY(hsmla::launch_sparse(D.bf, u.qkv, u.qkvh, u.sel, u.counts,
+                                       nullptr, u.o, D.B, D.gh, D.gw, D.H, D.Bs,
+                                       D.w, D.thr ? D.T : D.k, sel_layout(D), s));
+      return HSMLA_OK;
+    default:
+      return HSMLA_ERR_ARG;
   }
-  if (D.ph) {
-    r.mark("threshold_heads");
-    HSMLA_TRY(hsmla::launch_threshold_heads(hscores, nullptr, sel, counts, D.B,
-                                            D.T, D.H, D.tau, s));
-  } else if (D.thr) {
-    r.mark("threshold");
-    HSMLA_TRY(hsmla::launch_threshold(scores, nullptr, sel, counts, D.B, D.T,
-                                      D.tau, s));
-  } else {
-    r.mark("topk");
-    HSMLA_TRY(hsmla::launch_topk(scores, nullptr, sel, D.B, D.T, D.k, s));
+}
+
+hsmla_status run_module(const Dims& D, const hsmla_desc* d,
+                        const hsmla_weights* w, const void* x, const Bufs& u,
+                        bool fold, hipStream_t s, Rec& r) {
+  for (int st = 0; st < kModuleStages; ++st) {
+    const hsmla_status e = module_stage(st, D, d, w, x, u, fold, s, r);
+    if (e != HSMLA_OK) return e;
   }
-  r.mark("sparse_softmax");
-  HSMLA_TRY(hsmla::launch_sparse(D.bf, qkv, qkvh, sel, counts, nullptr, o, D.B,
-                                 D.gh, D.gw, D.H, D.Bs, D.w, D.thr ? D.T : D.k,
-                                 sel_layout(D), s));
   return HSMLA_OK;
 }
 
@@ -632,37 +664,65 @@ hsmla_status fold_ffn_taps(const Dims& D, const hsmla_ffn_weights* f,
   return HSMLA_OK;
 }
 
-// The block over the images that D (a range, see range_dims) and u cover;
-// x and out point at the range's first image.  fold: fold both tap sets in
-// line (otherwise they are already in the workspace).
-hsmla_status block_range(const Dims& D, const hsmla_desc* desc,
+// The block over the images that D (a range, see range_dims) and u cover,
+// as numbered stages (block_stage(0..kBlockStages-1) in order is the whole
+// block); x and out point at the range's first image.  fold: fold both tap
+// sets in line (otherwise they are already in the workspace).
+constexpr int kBlockStages = kModuleStages + 6;
+
+hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
                          const hsmla_weights* w, const hsmla_ffn_weights* f,
                          const void* x, void* out, const Bufs& u, bool fold,
                          hipStream_t s, Rec& r) {
   const int P = (int)D.P, C = D.C;
-  r.mark("layernorm1");
-  HSMLA_TRY(hsmla::launch_layernorm(D.bf, x, f->ln1_g, f->ln1_b, u.xn, P, C, s));
-  hsmla_status st = run_module(D, desc, w, u.xn, u, fold, s, r);
-  if (st != HSMLA_OK) return st;
-  // x1 = x + O W_o (residual fused into the projection epilogue)
-  r.mark("out_proj_residual");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, u.o, w->w_o, x, u.x1, P, C, C, s,
-                               hsmla::GemmSite::kOut));
-  r.mark("layernorm2");
-  HSMLA_TRY(hsmla::launch_layernorm(D.bf, u.x1, f->ln2_g, f->ln2_b, u.xn, P, C, s));
-  r.mark("ffn1_gemm");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, u.xn, f->w1, nullptr, u.h1, P, 4 * C, C, s,
-                               hsmla::GemmSite::kFfn1));
-  if (fold) {
-    r.mark("ffn_dw_taps");
-    if ((st = fold_ffn_taps(D, f, u.ftaps, s)) != HSMLA_OK) return st;
+  if (st >= 1 && st <= kModuleStages)
+    return module_stage(st - 1, D, desc, w, u.xn, u, fold, s, r);
+  switch (st) {
+    case 0:
+      r.mark("layernorm1");
+      HSMLA_TRY(hsmla::launch_layernorm(D.bf, x, f->ln1_g, f->ln1_b, u.xn, P, C, s));
+      return HSMLA_OK;
+    case kModuleStages + 1:
+      // x1 = x + O W_o (residual fused into the projection epilogue)
+      r.mark("out_proj_residual");
+      HSMLA_TRY(hsmla::launch_gemm(D.bf, u.o, w->w_o, x, u.x1, P, C, C, s,
+                                   hsmla::GemmSite::kOut));
+      return HSMLA_OK;
+    case kModuleStages + 2:
+      r.mark("layernorm2");
+      HSMLA_TRY(hsmla::launch_layernorm(D.bf, u.x1, f->ln2_g, f->ln2_b, u.xn, P,
+                                        C, s));
+      return HSMLA_OK;
+    case kModuleStages + 3:
+      r.mark("ffn1_gemm");
+      HSMLA_TRY(hsmla::launch_gemm(D.bf, u.xn, f->w1, nullptr, u.h1, P, 4 * C, C,
+                                   s, hsmla::GemmSite::kFfn1));
+      return HSMLA_OK;
+    case kModuleStages + 4:
+      if (!fold) return HSMLA_OK;
+      r.mark("ffn_dw_taps");
+      return fold_ffn_taps(D, f, u.ftaps, s);
+    case kModuleStages + 5:
+      r.mark("ffn_dwconv_gelu");
+      HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.h1, u.h2, u.ftaps, 3, D.B, D.gh,
+                                     D.gw, 4 * C, true, nullptr, 1, s));
+      r.mark("ffn2_gemm_residual");
+      HSMLA_TRY(hsmla::launch_gemm(D.bf, u.h2, f->w2, u.x1, out, P, C, 4 * C, s,
+                                   hsmla::GemmSite::kFfn2));
+      return HSMLA_OK;
+    default:
+      return HSMLA_ERR_ARG;
   }
-  r.mark("ffn_dwconv_gelu");
-  HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.h1, u.h2, u.ftaps, 3, D.B, D.gh, D.gw,
-                                 4 * C, true, nullptr, 1, s));
-  r.mark("ffn2_gemm_residual");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, u.h2, f->w2, u.x1, out, P, C, 4 * C, s,
-                               hsmla::GemmSite::kFfn2));
+}
+
+hsmla_status block_range(const Dims& D, const hsmla_desc* desc,
+                         const hsmla_weights* w, const hsmla_ffn_weights* f,
+                         const void* x, void* out, const Bufs& u, bool fold,
+                         hipStream_t s, Rec& r) {
+  for (int st = 0; st < kBlockStages; ++st) {
+    const hsmla_status e = block_stage(st, D, desc, w, f, x, out, u, fold, s, r);
+    if (e != HSMLA_OK) return e;
+  }
   return HSMLA_OK;
 }
 
@@ -708,11 +768,16 @@ hsmla_status block_split_impl(const hsmla_desc* desc, const hsmla_weights* w,
   const size_t img = (size_t)D.N * D.C * D.e;
   const Dims D0 = range_dims(D, nb0), D1 = range_dims(D, nb1);
   const Bufs u1 = bufs_for(D, L, ws, HSMLA_OP_BLOCK, nb0);
-  if ((st = block_range(D0, desc, w, f, x, out, u0, false, s, r)) != HSMLA_OK)
-    return st;
-  if ((st = block_range(D1, desc, w, f, at(const_cast<void*>(x), nb0 * img),
-                        at(out, nb0 * img), u1, false, aux, r)) != HSMLA_OK)
-    return st;
+  const void* x1 = at(const_cast<void*>(x), nb0 * img);
+  void* out1 = at(out, nb0 * img);
+  // the two ranges' launches are enqueued alternately, stage by stage, so
+  // both streams have work from the start
+  for (int k = 0; k < kBlockStages; ++k) {
+    if ((st = block_stage(k, D0, desc, w, f, x, out, u0, false, s, r)) != HSMLA_OK)
+      return st;
+    if ((st = block_stage(k, D1, desc, w, f, x1, out1, u1, false, aux, r)) != HSMLA_OK)
+      return st;
+  }
   HSMLA_TRY(hipEventRecord(join, aux));
   HSMLA_TRY(hipStreamWaitEvent(s, join, 0));
   return HSMLA_OK;
