@@ -171,43 +171,50 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
       }
     }
   } else {
-    static_assert(PF == 2 && NKT > 0, "the two-step prefetch needs an unrolled K loop");
-    // two tiles in flight: register set (kt & 1) holds tile kt + 2's loads
+    static_assert(PF == 2 && NKT > 0 && NKT % 2 == 0,
+                  "the two-tile prefetch needs an unrolled K loop");
+    // Two tiles in flight: register set kt % 2 holds tile kt + 2's loads;
+    // LDS buffer kt % 2 holds tile kt (measured: a third tile in flight
+    // gains nothing).
     load_tile(ra[0], rw[0], 0);
-    if (nk > 1) load_tile(ra[1], rw[1], BK);
+#pragma unroll
+    for (int q = 1; q < PF; ++q) load_tile(ra[q], rw[q], q * BK);
     store_tile(ra[0], rw[0], 0, 0);
     __syncthreads();
-    // Within a step: issue tile kt + 2's loads first, then the first 16 k
-    // of MFMAs, then write tile kt + 1 (loaded a step earlier) into the
-    // other LDS buffer -- free since the barrier that ended step kt - 1 --
-    // so the writes overlap the second half's MFMAs; one barrier ends the
-    // step.  Scheduling barriers keep the compiler from sinking the loads
-    // and writes behind the MFMAs (measured: a few percent on every
-    // projection; reading both halves' fragments up front was slower).
+    // Within a step: issue tile kt + PF's loads first, then the first 16 k
+    // of MFMAs, then write tile kt + 1 (loaded earlier) into the other LDS
+    // buffer -- free since the barrier that ended step kt - 1 -- so the
+    // writes overlap the second half's MFMAs; one barrier ends the step.
+    // Scheduling barriers keep the compiler from sinking the loads and
+    // writes behind the MFMAs (measured: a few percent on every projection;
+    // reading both halves' fragments up front was slower).
     static_assert(BK == 32, "two 16-k halves per step");
-    auto step = [&](auto par, int kt) {
-      constexpr int cur = decltype(par)::value;
-      if (kt + 2 < nk) load_tile(ra[cur], rw[cur], (kt + 2) * BK);
+    auto step = [&](auto set_c, auto buf_c, int kt) {
+      constexpr int set = decltype(set_c)::value, nset = (set + 1) % PF;
+      constexpr int buf = decltype(buf_c)::value;
+      if (kt + PF < nk) load_tile(ra[set], rw[set], (kt + PF) * BK);
       __builtin_amdgcn_sched_barrier(0);
       {
         bf16x8 af[FM], wf[FN];
-        read_frags(cur, 0, af, wf);
+        read_frags(buf, 0, af, wf);
         mfma_frags(af, wf);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nk) store_tile(ra[cur ^ 1], rw[cur ^ 1], cur ^ 1, (kt + 1) * BK);
+      if (kt + 1 < nk) store_tile(ra[nset], rw[nset], buf ^ 1, (kt + 1) * BK);
       __builtin_amdgcn_sched_barrier(0);
       {
         bf16x8 af[FM], wf[FN];
-        read_frags(cur, 16, af, wf);
+        read_frags(buf, 16, af, wf);
         mfma_frags(af, wf);
       }
       if (kt + 1 < nk) __syncthreads();
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
 #pragma unroll
-    for (int kt = 0; kt < nk; kt += 2) {
-      step(std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    for (int kt = 0; kt < nk; kt += 2) {  // register set and buffer repeat
+      step(I0{}, I0{}, kt);
+      step(I1{}, I1{}, kt + 1);
     }
   }
 
@@ -216,7 +223,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
   // buffers, then writes those rows back with 16-byte stores by consecutive
   // lanes (R added in float32, one rounding to bf16).  The residual chunks
   // of the whole wave tile are loaded first, so their latency overlaps the
-  // staging.
+  // staging.  One workgroup barrier (the tile buffers are free); after it
+  // each wave works in its own slice.
   float* Cs = reinterpret_cast<float*>(smem) + wave * 32 * CSTR;
   constexpr int CPRO = TN / 8;          // 16-byte output chunks per staged row
   constexpr int CPL = 32 * CPRO / 64;   // chunks per lane per fragment row
@@ -245,7 +253,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
             make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                         acc[i][j][4 * g + 3]);
       }
-    __syncthreads();
+    // the slice is this wave's own: ordering the wave's LDS accesses is
+    // enough (no workgroup barrier)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
       const int c = lane + 64 * q;
@@ -267,7 +278,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
             uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
