@@ -760,8 +760,18 @@ hsmla_status block_split_impl(const hsmla_desc* desc, const hsmla_weights* w,
     return block_range(D, desc, w, f, x, out, u, true, s, r);
   }
   const Bufs u0 = bufs_for(D, L, ws, HSMLA_OP_BLOCK, 0);
-  if ((st = fold_qkv_taps(D, desc, w, u0.taps, s)) != HSMLA_OK) return st;
-  if ((st = fold_ffn_taps(D, f, u0.ftaps, s)) != HSMLA_OK) return st;
+  {
+    // both tap sets in one launch before the fork
+    hsmla::TapSpec q{{nullptr, nullptr, nullptr}, {0, 0, 0}, desc->n_branches,
+                     D.kmax, 3 * D.C, 1, u0.taps};
+    for (int i = 0; i < desc->n_branches; ++i) {
+      q.kernels[i] = w->dw[i];
+      q.ks[i] = desc->branch_k[i];
+    }
+    const hsmla::TapSpec ff{{f->dw_ffn, nullptr, nullptr}, {3, 0, 0}, 1, 3,
+                            4 * D.C, 0, u0.ftaps};
+    HSMLA_TRY(hsmla::launch_dw_taps2(D.bf, q, &ff, s));
+  }
   HSMLA_TRY(hipEventRecord(fork, s));
   HSMLA_TRY(hipStreamWaitEvent(aux, fork, 0));
   const int nb0 = (D.B + 1) / 2, nb1 = D.B - nb0;

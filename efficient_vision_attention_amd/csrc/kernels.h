@@ -25,6 +25,16 @@ hipError_t launch_dw_taps(bool bf, const void* const* kernels, const int* ks,
                           int nk, int kmax, int ch, int identity, float* weff,
                           hipStream_t s);
 
+// Two tap sets folded by one launch (second may be NULL).
+struct TapSpec {
+  const void* kernels[3];
+  int ks[3];
+  int nk, kmax, ch, identity;
+  float* weff;
+};
+hipError_t launch_dw_taps2(bool bf, const TapSpec& first, const TapSpec* second,
+                           hipStream_t s);
+
 // out[b][y][x][c] = act(sum_tap weff[tap][c] * in[b][y+dy-r][x+dx-r][c]),
 // zero padding, r = (kmax-1)/2; act = exact GELU when `gelu`.  With bsum
 // (no GELU; dwconv_can_pool(kmax, block) must hold) the launch also writes
