@@ -244,7 +244,7 @@ constexpr int kStreamChannels = 64;  // channels per workgroup
 // barrier); after the strip one barrier, then the block's columns are
 // added in order.  block must divide the workgroup width and the strip
 // height, and be at least kPoolMinBlock (LDS room).
-template <typename T, int K, bool GELU, int V, int NB, bool POOL>
+template <typename T, int K, bool GELU, int V, int NB, bool POOL, bool TL>
 __global__ __launch_bounds__(256) void dwconv_stream(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, float* __restrict__ bsum, int block,
@@ -273,14 +273,42 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   const int y0 = strip * TH;
   const size_t img = (size_t)b * gh * gw;
 
-  float w[K][K][V];
+  // Taps: in registers, or (TL) in LDS, read at every use -- the lanes of
+  // one channel group read the same 16 bytes (a broadcast), which frees
+  // the K*K*V tap registers for more channels per thread.
+  float w[TL ? 1 : K][TL ? 1 : K][V];
+  __shared__ __attribute__((aligned(16))) float wl[TL ? K * K : 1][TL ? kStreamChannels : 1];
+  if constexpr (TL) {
+    for (int idx = threadIdx.x; idx < K * K * kStreamChannels; idx += 256) {
+      const int tap = idx / kStreamChannels, cc = idx % kStreamChannels;
+      const int cg = ch_t * kStreamChannels + cc;
+      wl[tap][cc] = cg < ch ? weff[(size_t)tap * ch + cg] : 0.f;
+    }
+    __syncthreads();
+  } else {
 #pragma unroll
-  for (int ky = 0; ky < K; ++ky)
+    for (int ky = 0; ky < K; ++ky)
 #pragma unroll
-    for (int kx = 0; kx < K; ++kx)
+      for (int kx = 0; kx < K; ++kx)
 #pragma unroll
-      for (int j = 0; j < V; ++j)
-        w[ky][kx][j] = c_ok ? weff[(size_t)(ky * K + kx) * ch + c + j] : 0.f;
+        for (int j = 0; j < V; ++j)
+          w[ky][kx][j] = c_ok ? weff[(size_t)(ky * K + kx) * ch + c + j] : 0.f;
+  }
+  auto tap = [&](int ky, int kx, float (&t)[V]) {
+    if constexpr (TL) {
+      const float* p = &wl[ky * K + kx][tc * V];
+      if constexpr (V == 4) {
+        const float4 q = *reinterpret_cast<const float4*>(p);
+        t[0] = q.x; t[1] = q.y; t[2] = q.z; t[3] = q.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) t[j] = p[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j) t[j] = w[ky][kx][j];
+    }
+  };
 
   float acc[K][V];
 #pragma unroll
@@ -340,10 +368,12 @@ __global__ __launch_bounds__(256) void dwconv_stream(
         for (int i = 0; i < K; ++i) {
           const int slot = (u - R + i + NB * K) % K;
 #pragma unroll
-          for (int kx = 0; kx < K; ++kx)
+          for (int kx = 0; kx < K; ++kx) {
+            float t[V];
+            tap(K - 1 - i, kx, t);
 #pragma unroll
-            for (int j = 0; j < V; ++j)
-              acc[slot][j] = fmaf(w[K - 1 - i][kx][j], xin[kx][j], acc[slot][j]);
+            for (int j = 0; j < V; ++j) acc[slot][j] = fmaf(t[j], xin[kx][j], acc[slot][j]);
+          }
         }
       }
       // unconditional (clamped) prefetch keeps the load/wait pattern regular
@@ -598,15 +628,17 @@ __global__ __launch_bounds__(256) void dwconv_lds(
 
 // Per kernel size: channels per thread V, rows of loads in flight P and
 // channels per workgroup WC (the workgroup is 256 / (WC / V) columns wide).
-// Sizes up to 3 take the LDS-staged kernel, 5 and 7 the register-streaming
-// one (measured: at 25 or 49 taps per channel the taps' registers leave the
-// LDS kernel too few waves, while the streaming kernel keeps enough loads in
-// flight with 2 channels per thread).
+// Sizes up to 3 take the LDS-staged kernel, 5 and 7 the streaming one with
+// the taps in LDS and 4 channels per thread (measured on the folded 5x5:
+// 2 channels per thread with the taps in registers 128 us, 4 channels with
+// the taps in LDS 123 us with 2 rows in flight, more rows slower; the
+// LDS-staged kernel 137 us at best).
 struct DwCfg {
   int v, p, wc;
+  bool tl;  // streaming kernel: taps in LDS
 };
 constexpr DwCfg dw_cfg(int k, bool gelu) {
-  return k <= 3 ? DwCfg{4, 4, 64} : DwCfg{2, k == 5 ? 4 : 3, kStreamChannels};
+  return k <= 3 ? DwCfg{4, 4, 64, false} : DwCfg{4, k == 5 ? 2 : 3, kStreamChannels, true};
   (void)gelu;
 }
 constexpr int dw_width(int k, bool gelu) {
@@ -625,11 +657,11 @@ hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
   const int per_xcd = (total + kXcds - 1) / kXcds;
   if constexpr (K >= 5) {
     if (bsum && !GELU)
-      dwconv_stream<T, K, false, cf.v, cf.p, true><<<per_xcd * kXcds, 256, 0, s>>>(
+      dwconv_stream<T, K, false, cf.v, cf.p, true, cf.tl><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
           gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
     else
-      dwconv_stream<T, K, GELU, cf.v, cf.p, false><<<per_xcd * kXcds, 256, 0, s>>>(
+      dwconv_stream<T, K, GELU, cf.v, cf.p, false, cf.tl><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
           gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
     return hipGetLastError();
