@@ -43,6 +43,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ float relu(float x) { return x > 0.f ? x : 0.f; }
 
+// Buffer-resource loads and stores (raw, stride 0): an offset past the
+// resource's byte count reads zeros and drops stores in hardware, so edge
+// lanes need no branch and every memory instruction is unconditional (the
+// compiler's wait counts then stay exact).
+constexpr int kOob = INT32_MIN;  // an offset no resource here reaches
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base,
+                                                          int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           bytes, 0x00020000);
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return uint4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
+}
+
 // Sum over a 64-lane wavefront (result valid in every lane).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -78,21 +78,6 @@ constexpr int TH = 32;   // output rows per workgroup strip
 constexpr int kPoolMinBlock = 4;
 constexpr int kXcds = 8;
 
-// Buffer-resource loads and stores (raw, stride 0): an offset past the
-// resource's byte count reads zeros and drops stores in hardware, so edge
-// lanes need no branch and every memory instruction is unconditional (the
-// compiler's wait counts then stay exact).
-constexpr int kOob = INT32_MIN;  // an offset no resource here reaches
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base,
-                                                          int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           bytes, 0x00020000);
-}
-
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 // V consecutive channels as loaded (V = 2, 4 or 8), converted to float at
 // use.
 template <typename T, int V>
