@@ -206,27 +206,45 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     }
   }
 
-  // tile loader: 64 keys x (K, K^, V, V^) x 32 channels = 1024 chunks of 8
+  // tile loader: 64 keys x (K, K^, V, V^) x 32 channels = 1024 chunks of 8.
+  // Loads are unconditional (keys past the window re-read its last key and
+  // are zeroed when staged), so no load sits under a branch and the wait
+  // before staging covers exactly one tile.  Each thread's keys advance by
+  // 64 window positions per tile, so their (row, column) in the window is
+  // stepped instead of divided.
   constexpr int kLoads = (1024 + NT - 1) / NT;
   uint4 stg[kLoads];
+  const int step_r = KT / wcols, step_c = KT % wcols;
+  int kr[kLoads], kc[kLoads];  // window row / column of this thread's keys
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int key = (min(tid + NT * i, 1023) >> 2) & 63;
+    kr[i] = key / wcols;
+    kc[i] = key % wcols;
+  }
+  const size_t tok_last = img + (size_t)(rhi - 1) * gw + chi - 1;
   auto issue = [&](int w0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int cidx = tid + NT * i;
+      const int cidx = min(tid + NT * i, 1023);
       const int tensor = cidx >> 8;      // 0 K, 1 K^, 2 V, 3 V^
       const int key = (cidx >> 2) & 63, cg = cidx & 3;
-      const int wi = w0 + key;
-      uint4 u = {0, 0, 0, 0};
-      if (cidx < 1024 && wi < nwin) {
-        const size_t tok = img + (size_t)(rlo + wi / wcols) * gw + clo + wi % wcols;
-        const bf16* base = (tensor & 1) ? qkvh : qkv;
-        const int comp = (tensor < 2) ? 1 : 2;
-        u = *reinterpret_cast<const uint4*>(base + tok * C3 + comp * C + h * kD + 8 * cg);
+      const size_t tok = w0 + key < nwin
+                             ? img + (size_t)(rlo + kr[i]) * gw + clo + kc[i]
+                             : tok_last;
+      const bf16* base = (tensor & 1) ? qkvh : qkv;
+      const int comp = (tensor < 2) ? 1 : 2;
+      stg[i] = *reinterpret_cast<const uint4*>(base + tok * C3 + comp * C + h * kD + 8 * cg);
+      // advance to the same key of the next tile
+      kr[i] += step_r;
+      kc[i] += step_c;
+      if (kc[i] >= wcols) {
+        kc[i] -= wcols;
+        ++kr[i];
       }
-      stg[i] = u;
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](int buf, int w0) {
     SparseTile& T = tiles[buf];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -234,7 +252,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
       if (cidx >= 1024) break;
       const int tensor = cidx >> 8;
       const int key = (cidx >> 2) & 63, cg = cidx & 3;
-      uint4 u = stg[i];
+      uint4 u = w0 + key < nwin ? stg[i] : uint4{0, 0, 0, 0};
       if (tensor == 0) {
         *reinterpret_cast<uint4*>(&T.k[key * KS + 8 * cg]) = u;
       } else if (tensor == 1) {
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
 
   const int ntiles = (nwin + KT - 1) / KT;
   issue(0);
-  commit(0);
+  commit(0, 0);
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
@@ -330,7 +348,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
       }
     }
     // tiles[buf ^ 1] was last read before the previous barrier
-    if (it + 1 < ntiles) commit(buf ^ 1);
+    if (it + 1 < ntiles) commit(buf ^ 1, (it + 1) * KT);
     __syncthreads();
   }
 
