@@ -244,18 +244,28 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
 
 // O^T = Z^T relu(Q^)^T with Z split into bf16 hi + lo parts, normalised by
 // relu(q^) . D.  grid (ceil(tokens/256), ceil(heads/4), batch), 256
-// threads; wave = head, eight 32-token tiles per wave, two tiles in flight.
+// threads; wave = head of a 4-head group, eight 32-token tiles per
+// workgroup.  Each tile's Q^ rows (32 tokens x 4 heads x 64 bytes) are
+// loaded with 16-byte loads over whole 256-byte rows into LDS, read back in
+// the MFMA operand layout (lane = token), and the normalised output goes
+// back through LDS to 256-byte row stores: per-lane token-major global
+// accesses would touch 32-byte pieces of 32 rows per instruction.  The next
+// tile's loads are in flight while a tile is computed.
+constexpr int kRowB = kHG * kD * 2 + 16;  // LDS bytes per staged token row
+
 __global__ __launch_bounds__(256) void lin_apply_mfma(
     const bf16* __restrict__ qkvh, const float* __restrict__ kv,
     const float* __restrict__ ksum, bf16* __restrict__ o, int tokens,
     int heads) {
+  __shared__ __attribute__((aligned(16))) char qs[kTT * kRowB];
+  __shared__ __attribute__((aligned(16))) char os[kTT * kRowB];
   const int hg = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = hg * kHG + wave;
-  if (h >= heads) return;
+  const bool h_ok = h < heads;  // every wave takes part in the staging
   const int C = heads * kD, C3 = 3 * C;
   const int g = lane >> 5, col = lane & 31;
-  const size_t bh = (size_t)b * heads + h;
+  const size_t bh = (size_t)b * heads + (h_ok ? h : 0);
   const float* Z = kv + bh * kD * kD;
   const float* Dv = ksum + bh * kD;
 
@@ -281,23 +291,42 @@ __global__ __launch_bounds__(256) void lin_apply_mfma(
     zlo[ks] = __builtin_bit_cast(bf16x8, uint4{lw[0], lw[1], lw[2], lw[3]});
   }
 
+  // This group's channels of a token row: heads * 32 may end inside the
+  // group, and tokens may end inside a tile; both read zeros / store
+  // nothing through per-tile buffer resources (which also keep every
+  // offset small).
   const int n_base = blockIdx.x * kApplyTok;
-  const bf16* qbase = qkvh + (size_t)b * tokens * C3 + h * kD + 8 * g;
-  uint4 st[2][2];  // two tiles in flight
-  auto issue = [&](uint4 (&dst)[2], int n) {
-    const bool ok = n < tokens;
-    const bf16* qrow = qbase + (size_t)(ok ? n : 0) * C3;
+  const int gch = min(kHG * kD, C - hg * kHG * kD);  // channels of this group
+  // thread's two 16-byte chunks of a tile: token tid / 16 (+ 16), part tid % 16
+  const int part = tid & 15, trow = tid >> 4;
+  const bool part_ok = part * 8 < gch;
+  auto tile_rows = [&](int n0) { return max(0, min(kTT, tokens - n0)); };
+  auto issue = [&](uint4 (&d)[2], int n0) {
+    const __amdgpu_buffer_rsrc_t rs =
+        buf_rsrc(qkvh + ((size_t)b * tokens + n0) * C3, tile_rows(n0) * C3 * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int off = part_ok ? ((trow + 16 * i) * C3 + hg * kHG * kD + part * 8) * 2 : kOob;
+      d[i] = buf_load16(rs, off);
+    }
+  };
+  uint4 st[2][2];
+  issue(st[0], n_base);
+#pragma unroll
+  for (int tt = 0; tt < kApplyTok / kTT; ++tt) {
+    const int n0 = n_base + tt * kTT;
+    if (tt + 1 < kApplyTok / kTT) issue(st[(tt + 1) & 1], n0 + kTT);
+    // stage this tile's rows (the previous tile's readers have passed the
+    // barrier that ended their iteration)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4*>(qs + (trow + 16 * i) * kRowB + part * 16) = st[tt & 1][i];
+    __syncthreads();
+    uint4 cur[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      dst[ks] = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks) : uint4{0, 0, 0, 0};
-  };
-  issue(st[0], n_base + col);
-  issue(st[1], n_base + 32 + col);
-#pragma unroll
-  for (int tt = 0; tt < kApplyTok / 32; ++tt) {
-    const int n = n_base + tt * 32 + col;
-    uint4 cur[2] = {st[tt % 2][0], st[tt % 2][1]};
-    if (tt + 2 < kApplyTok / 32) issue(st[tt % 2], n + 64);
+      cur[ks] = *reinterpret_cast<const uint4*>(qs + col * kRowB + wave * kD * 2 +
+                                                (16 * ks + 8 * g) * 2);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -315,18 +344,27 @@ __global__ __launch_bounds__(256) void lin_apply_mfma(
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zlo[ks], qb, acc, 0, 0, 0);
     }
     den += __shfl_xor(den, 32, 64);
-    if (n >= tokens) continue;
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    bf16* orow = o + ((size_t)b * tokens + n) * C + h * kD;
+    // acc[4j + e]: feature 8j + 4g + e of token col
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = 8 * j + 4 * g;
       uint2 w;
       w.x = pack_bf16x2(acc[4 * j + 0] * inv, acc[4 * j + 1] * inv);
       w.y = pack_bf16x2(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + c) = w;
+      *reinterpret_cast<uint2*>(os + col * kRowB + wave * kD * 2 + (8 * j + 4 * g) * 2) = w;
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t ors =
+        buf_rsrc(o + ((size_t)b * tokens + n0) * C, tile_rows(n0) * C * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(os + (trow + 16 * i) * kRowB + part * 16);
+      const int off = part_ok ? ((trow + 16 * i) * C + hg * kHG * kD + part * 8) * 2 : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, ors, off, 0, 0);
     }
   }
+  (void)h_ok;
 }
 
 }  // namespace
