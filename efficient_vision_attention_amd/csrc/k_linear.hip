@@ -73,15 +73,15 @@ __global__ __launch_bounds__(64) void kv_combine_kernel(
   const float* p = part + (size_t)bh * nchunks * kPart;
   const int e = blockIdx.y * 64 + threadIdx.x;
   if (e < kPart) {
-    // loads issued 8 at a time, added strictly in chunk order
+    // loads issued 32 at a time, added strictly in chunk order
     float s = 0.f;
     int c = 0;
-    for (; c + 8 <= nchunks; c += 8) {
-      float v[8];
+    for (; c + 32 <= nchunks; c += 32) {
+      float v[32];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = p[(size_t)(c + i) * kPart + e];
+      for (int i = 0; i < 32; ++i) v[i] = p[(size_t)(c + i) * kPart + e];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s += v[i];
+      for (int i = 0; i < 32; ++i) s += v[i];
     }
     for (; c < nchunks; ++c) s += p[(size_t)c * kPart + e];
     if (e < kD * kD)
@@ -141,26 +141,32 @@ __device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
   return (u & 0x8000u) ? 0 : u;
 }
 
-// One wave per head, tiles of 32 tokens, no LDS and no barrier.  A tile is
-// loaded token-major (lane = token, 8 consecutive features per 16 bytes),
-// which is the MFMA A-operand layout; multiplying it by the 32x32 identity
-// returns it in the accumulator layout, where a lane owns one feature and 16
-// tokens -- i.e. transposed, exactly (one nonzero product per output).  The
-// transposed relu(K^) and V^ tiles then feed Z += relu(K^)^T V^ with the
-// token order the accumulator layout already has.
+// One wave per head of a 4-head group, tiles of 32 tokens.  Each tile's
+// K^ and V^ rows (32 tokens x 4 heads x 64 bytes each) are loaded with
+// 16-byte loads over whole 256-byte rows into one of two LDS buffers (one
+// barrier per tile), then every wave reads its head in token-major form
+// (lane = token, 8 consecutive features per 16 bytes), which is the MFMA
+// A-operand layout; multiplying it by the 32x32 identity returns it in the
+// accumulator layout, where a lane owns one feature and 16 tokens -- i.e.
+// transposed, exactly (one nonzero product per output).  The transposed
+// relu(K^) and V^ tiles then feed Z += relu(K^)^T V^ with the token order
+// the accumulator already has.  Tokens past the chunk read zeros (which add
+// nothing) through per-tile buffer resources.
 // grid (chunks, ceil(heads/4), batch), 256 threads = 4 heads.
+constexpr int kKvRowB = 2 * kHG * kD * 2 + 16;  // LDS bytes per token row: K^ | V^
+
 __global__ __launch_bounds__(256) void kv_partial_mfma(
     const bf16* __restrict__ qkvh, float* __restrict__ part, int tokens,
     int heads, int nchunks) {
+  __shared__ __attribute__((aligned(16))) char ts[2][kTT * kKvRowB];
   const int chunk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = hg * kHG + wave;
-  if (h >= heads) return;
+  const int h = hg * kHG + wave;  // h >= heads: stages, computes nothing kept
   const int C = heads * kD, C3 = 3 * C;
   const int g = lane >> 5, col = lane & 31;
   const int n_begin = chunk * kChunkTok;
   const int n_end = min(tokens, n_begin + kChunkTok);
-  const bf16* base = qkvh + (size_t)b * tokens * C3 + h * kD + 8 * g;
+  const int gch = min(kHG * kD, C - hg * kHG * kD);  // channels of this group
 
   // identity as the B operand: column col, k = 16 ks + 8 g + e
   bf16x8 eye[2];
@@ -172,30 +178,48 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
     eye[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(e16));
   }
 
-  // staged loads of one tile: [K^ ks0, K^ ks1, V^ ks0, V^ ks1]
-  uint4 st[4];
-  auto issue = [&](int n0) {
-    const int n = n0 + col;
-    const bool ok = n < n_end;
-    const bf16* row = base + (size_t)(ok ? n : n_begin) * C3;
+  // thread's four 16-byte chunks of a tile: token tid / 16 (+ 16),
+  // part tid % 16 of K^ and of V^
+  const int prt = tid & 15, trow = tid >> 4;
+  const bool part_ok = prt * 8 < gch;
+  auto issue = [&](uint4 (&d)[4], int n0) {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
+        qkvh + ((size_t)b * tokens + n0) * C3, max(0, min(kTT, n_end - n0)) * C3 * 2);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        st[2 * t + ks] = ok ? *reinterpret_cast<const uint4*>(row + (1 + t) * C + 16 * ks)
-                            : uint4{0, 0, 0, 0};
+      for (int tv = 0; tv < 2; ++tv) {
+        const int off =
+            part_ok ? ((trow + 16 * i) * C3 + (1 + tv) * C + hg * kHG * kD + prt * 8) * 2
+                    : kOob;
+        d[2 * i + tv] = buf_load16(rs, off);
+      }
   };
 
   f32x16 z;
 #pragma unroll
   for (int r = 0; r < 16; ++r) z[r] = 0.f;
   float dacc = 0.f;
-  issue(n_begin);
-  for (int n0 = n_begin; n0 < n_end; n0 += kTT) {
-    uint4 cur[4];
+  uint4 st[4];
+  issue(st, n_begin);
+  int buf = 0;
+  for (int n0 = n_begin; n0 < n_end; n0 += kTT, buf ^= 1) {
+    char* T = ts[buf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cur[i] = st[i];
-    if (n0 + kTT < n_end) issue(n0 + kTT);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int tv = 0; tv < 2; ++tv)
+        *reinterpret_cast<uint4*>(T + (trow + 16 * i) * kKvRowB + tv * kHG * kD * 2 +
+                                  prt * 16) = st[2 * i + tv];
+    if (n0 + kTT < n_end) issue(st, n0 + kTT);
+    __syncthreads();
+    uint4 cur[4];  // [K^ ks0, K^ ks1, V^ ks0, V^ ks1]
+#pragma unroll
+    for (int tv = 0; tv < 2; ++tv)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        cur[2 * tv + ks] = *reinterpret_cast<const uint4*>(
+            T + col * kKvRowB + tv * kHG * kD * 2 + wave * kD * 2 + (16 * ks + 8 * g) * 2);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {  // relu on K^ (bf16 sign bit)
       uint16_t* hv = reinterpret_cast<uint16_t*>(&cur[ks]);
@@ -231,6 +255,7 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
                                                   0, 0, 0);
     }
   }
+  if (h >= heads) return;
   dacc += __shfl_xor(dacc, 32, 64);
   // z[r] = Z[i][c] with c = col, i = 8(r/4) + 4g + r%4
   float* out = part + ((size_t)(b * heads + h) * nchunks + chunk) * kPart;
