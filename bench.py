@@ -151,7 +151,7 @@ def algorithmic_work(name, wl, sel):
         return 8 * C * e * P, 2 * 4 * C * P * 9
     if name == "ffn2_gemm_residual":
         return P * 6 * C * e + 4 * C * C * e, 2 * P * 4 * C * C
-    if name in ("dw_taps", "ffn_dw_taps"):
+    if name in ("dw_taps", "ffn_dw_taps", "prep"):
         return 0, 0
     raise KeyError(name)
 

@@ -114,13 +114,24 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
 //   per head: [B][H][T] i32, counts [B][H] i32, head scores [B][T][H] f32),
 //   gate block sums [B][T][3C] f32,
 //   (block only) xn [P][C], x1 [P][C], h1 [P][4C], h2 [P][4C],
-//   ffn taps [9][4C] f32.
+//   ffn taps [9][4C] f32,
+//   tile-blocked copies of W_qkv, W_o (and, block only, W1, W2) when the
+//   weights fit the GEMM tile (bf16; see blocked_weights).
 struct Layout {
   size_t qkv, qkv_hat, o, kv, ksum, part, taps, scores, sel, counts, head_scores;
   size_t bsum;
   size_t xn, x1, h1, h2, ffn_taps;
+  size_t wq, wo, w1, w2;  // 0 when not made
   size_t total;
 };
+
+// Tile-blocked weight copies are made when every projection's weight fits
+// the GEMM tile (output rows a multiple of kGemmTileN, inputs of
+// kGemmTileK); a GEMM then reads them whenever its token count also fits.
+bool blocked_weights(const Dims& D) {
+  return D.bf && (3 * D.C) % hsmla::kGemmTileN == 0 && D.C % hsmla::kGemmTileN == 0 &&
+         D.C % hsmla::kGemmTileK == 0;
+}
 
 Layout layout(const Dims& D, int op) {
   Layout L{};
@@ -157,6 +168,15 @@ Layout layout(const Dims& D, int op) {
       L.h1 = take(D.P * 4 * D.C * D.e);
       L.h2 = take(D.P * 4 * D.C * D.e);
       L.ffn_taps = take((size_t)9 * 4 * D.C * 4);
+    }
+    if (blocked_weights(D)) {
+      const size_t c2 = (size_t)D.C * D.C * D.e;
+      L.wq = take(3 * c2);
+      L.wo = take(c2);
+      if (op == HSMLA_OP_BLOCK) {
+        L.w1 = take(4 * c2);
+        L.w2 = take(4 * c2);
+      }
     }
   }
   L.total = off;
@@ -220,23 +240,20 @@ hsmla_status fold_qkv_taps(const Dims& D, const hsmla_desc* d,
   return HSMLA_OK;
 }
 
-// Steps 1-2 with caller-provided buffers; with bsum the conv also writes
-// the gate's block sums of qkv_hat.  fold: fold the taps first (otherwise
-// they are already in `taps`).
+// Steps 1-2 with caller-provided buffers (plain weights, taps folded into
+// `taps` first).
 hsmla_status run_qkv(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
                      const void* x, void* qkv, void* qkv_hat, float* taps,
-                     float* bsum, bool fold, hipStream_t s, Rec& r) {
+                     hipStream_t s, Rec& r) {
   r.mark("qkv_gemm");
   HSMLA_TRY(hsmla::launch_gemm(D.bf, x, w->w_qkv, nullptr, qkv, (int)D.P,
                                3 * D.C, D.C, s, hsmla::GemmSite::kQkv));
-  if (fold) {
-    r.mark("dw_taps");
-    hsmla_status st = fold_qkv_taps(D, d, w, taps, s);
-    if (st != HSMLA_OK) return st;
-  }
+  r.mark("dw_taps");
+  hsmla_status st = fold_qkv_taps(D, d, w, taps, s);
+  if (st != HSMLA_OK) return st;
   r.mark("dwconv_qkv");
   HSMLA_TRY(hsmla::launch_dwconv(D.bf, qkv, qkv_hat, taps, D.kmax, D.B, D.gh,
-                                 D.gw, 3 * D.C, false, bsum, D.Bs, s));
+                                 D.gw, 3 * D.C, false, nullptr, D.Bs, s));
   return HSMLA_OK;
 }
 
@@ -246,6 +263,7 @@ struct Bufs {
   void *qkv, *qkvh, *o, *xn, *x1, *h1, *h2;
   float *kv, *ksum, *part, *taps, *ftaps, *scores, *hscores, *bsum;
   int32_t *sel, *counts;
+  void *wq, *wo, *w1, *w2;  // tile-blocked weights (shared), or null
 };
 
 Bufs bufs_for(const Dims& D, const Layout& L, void* ws, int op, int b0) {
@@ -276,7 +294,60 @@ Bufs bufs_for(const Dims& D, const Layout& L, void* ws, int op, int b0) {
     u.h2 = at(ws, L.h2 + bb * n * 4 * c * e);
     u.ftaps = reinterpret_cast<float*>(at(ws, L.ffn_taps));  // shared
   }
+  if (L.wq) {
+    u.wq = at(ws, L.wq);
+    u.wo = at(ws, L.wo);
+    if (op == HSMLA_OP_BLOCK) {
+      u.w1 = at(ws, L.w1);
+      u.w2 = at(ws, L.w2);
+    }
+  }
   return u;
+}
+
+// A projection's weights: the tile-blocked copy when the GEMM takes its
+// whole-tile path for this shape, else the caller's row-major weights.
+struct WSel {
+  const void* w;
+  bool blocked;
+};
+WSel pick_w(const void* plain, const void* blocked, int M, int N, int K) {
+  if (blocked && hsmla::gemm_whole_tiles(M, N, K)) return {blocked, true};
+  return {plain, false};
+}
+
+// One launch before the stages: the folded branch taps (and the FFN's, for
+// the block) and the blocked weight copies.
+hsmla_status prep(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
+                  const hsmla_ffn_weights* f, const Bufs& u, hipStream_t s,
+                  Rec& r) {
+  hsmla::TapSpec taps[2];
+  int ntaps = 0;
+  {
+    hsmla::TapSpec& q = taps[ntaps++];
+    q = hsmla::TapSpec{{nullptr, nullptr, nullptr}, {0, 0, 0}, d->n_branches,
+                       D.kmax, 3 * D.C, 1, u.taps};
+    for (int i = 0; i < d->n_branches; ++i) {
+      q.kernels[i] = w->dw[i];
+      q.ks[i] = d->branch_k[i];
+    }
+  }
+  if (f)
+    taps[ntaps++] = hsmla::TapSpec{{f->dw_ffn, nullptr, nullptr}, {3, 0, 0}, 1, 3,
+                                   4 * D.C, 0, u.ftaps};
+  hsmla::BlockJob jobs[4];
+  int njobs = 0;
+  if (u.wq) {
+    jobs[njobs++] = {w->w_qkv, u.wq, 3 * D.C, D.C, hsmla::kGemmTileN};
+    jobs[njobs++] = {w->w_o, u.wo, D.C, D.C, hsmla::kGemmTileN};
+    if (f && u.w1) {
+      jobs[njobs++] = {f->w1, u.w1, 4 * D.C, D.C, hsmla::kGemmTileN};
+      jobs[njobs++] = {f->w2, u.w2, D.C, 4 * D.C, hsmla::kGemmTileN};
+    }
+  }
+  r.mark("prep");
+  HSMLA_TRY(hsmla::launch_prep(D.bf, taps, ntaps, jobs, njobs, s));
+  return HSMLA_OK;
 }
 
 // The same dims for a range of nb images.
@@ -291,44 +362,42 @@ Dims range_dims(const Dims& D, int nb) {
 // Steps 1-5 into the workspace views (o holds the refined output), as
 // numbered stages of one or two launches each, so that two image ranges can
 // interleave their launches (module_stage(0..kModuleStages-1) in order is
-// the whole module).  D may describe a range of the images (range_dims), u
-// the matching pointers.  fold: fold the branch taps in line (otherwise
-// they are already in u.taps).
-constexpr int kModuleStages = 8;
+// the whole module, after prep).  D may describe a range of the images
+// (range_dims), u the matching pointers.
+constexpr int kModuleStages = 7;
 
 hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
                           const hsmla_weights* w, const void* x, const Bufs& u,
-                          bool fold, hipStream_t s, Rec& r) {
+                          hipStream_t s, Rec& r) {
+  (void)d;
   // the plain gate's block sums come out of the depthwise conv when its
   // workgroup shape allows; the gate then only forms the logits
   float* bsum = (!w->gate_dw && hsmla::dwconv_can_pool(D.kmax, D.Bs)) ? u.bsum
                                                                        : nullptr;
   switch (st) {
-    case 0:
+    case 0: {
       r.mark("qkv_gemm");
-      HSMLA_TRY(hsmla::launch_gemm(D.bf, x, w->w_qkv, nullptr, u.qkv, (int)D.P,
-                                   3 * D.C, D.C, s, hsmla::GemmSite::kQkv));
+      const WSel q = pick_w(w->w_qkv, u.wq, (int)D.P, 3 * D.C, D.C);
+      HSMLA_TRY(hsmla::launch_gemm(D.bf, x, q.w, nullptr, u.qkv, (int)D.P, 3 * D.C,
+                                   D.C, s, hsmla::GemmSite::kQkv, false, q.blocked));
       return HSMLA_OK;
+    }
     case 1:
-      if (!fold) return HSMLA_OK;
-      r.mark("dw_taps");
-      return fold_qkv_taps(D, d, w, u.taps, s);
-    case 2:
       r.mark("dwconv_qkv");
       HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.qkv, u.qkvh, u.taps, D.kmax, D.B, D.gh,
                                      D.gw, 3 * D.C, false, bsum, D.Bs, s));
       return HSMLA_OK;
-    case 3:
+    case 2:
       r.mark("kv_state");
       HSMLA_TRY(hsmla::launch_kv_state(D.bf, u.qkvh, u.kv, u.ksum, u.part, D.B,
                                        D.N, D.H, s));
       return HSMLA_OK;
-    case 4:
+    case 3:
       r.mark("lin_apply");
       HSMLA_TRY(hsmla::launch_lin_apply(D.bf, u.qkvh, u.kv, u.ksum, u.o, D.B,
                                         D.N, D.H, s));
       return HSMLA_OK;
-    case 5:
+    case 4:
       r.mark("gate_scores");
       if (bsum)
         HSMLA_TRY(hsmla::launch_gate_from_sums(bsum, w->gate_w, w->gate_b,
@@ -339,7 +408,7 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
                                             w->gate_dw, u.scores, u.hscores,
                                             D.B, D.gh, D.gw, D.H, D.Bs, s));
       return HSMLA_OK;
-    case 6:
+    case 5:
       if (D.soft) return HSMLA_OK;  // every block, weighted: no list
       if (D.ph) {
         r.mark("threshold_heads");
@@ -354,7 +423,7 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
         HSMLA_TRY(hsmla::launch_topk(u.scores, nullptr, u.sel, D.B, D.T, D.k, s));
       }
       return HSMLA_OK;
-    case 7:
+    case 6:
       r.mark("sparse_softmax");
       if (D.soft)
         HSMLA_TRY(hsmla::launch_sparse(D.bf, u.qkv, u.qkvh, nullptr, nullptr,
@@ -372,9 +441,9 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
 
 hsmla_status run_module(const Dims& D, const hsmla_desc* d,
                         const hsmla_weights* w, const void* x, const Bufs& u,
-                        bool fold, hipStream_t s, Rec& r) {
+                        hipStream_t s, Rec& r) {
   for (int st = 0; st < kModuleStages; ++st) {
-    const hsmla_status e = module_stage(st, D, d, w, x, u, fold, s, r);
+    const hsmla_status e = module_stage(st, D, d, w, x, u, s, r);
     if (e != HSMLA_OK) return e;
   }
   return HSMLA_OK;
@@ -445,7 +514,7 @@ hsmla_status hsmla_qkv_branches(const hsmla_desc* desc, const hsmla_weights* w,
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
   Rec r;
   return run_qkv(D, desc, w, x, qkv, qkv_hat,
-                 reinterpret_cast<float*>(at(ws, L.taps)), nullptr, true,
+                 reinterpret_cast<float*>(at(ws, L.taps)),
                  static_cast<hipStream_t>(stream), r);
 }
 
@@ -627,10 +696,12 @@ hsmla_status forward_impl(const hsmla_desc* desc, const hsmla_weights* w,
   const Layout L = layout(D, HSMLA_OP_FORWARD);
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
   const Bufs u = bufs_for(D, L, ws, HSMLA_OP_FORWARD, 0);
-  if ((st = run_module(D, desc, w, x, u, true, s, r)) != HSMLA_OK) return st;
+  if ((st = prep(D, desc, w, nullptr, u, s, r)) != HSMLA_OK) return st;
+  if ((st = run_module(D, desc, w, x, u, s, r)) != HSMLA_OK) return st;
   r.mark("out_proj");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, at(ws, L.o), w->w_o, nullptr, y, (int)D.P,
-                               D.C, D.C, s, hsmla::GemmSite::kOut));
+  const WSel wo = pick_w(w->w_o, u.wo, (int)D.P, D.C, D.C);
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, u.o, wo.w, nullptr, y, (int)D.P, D.C, D.C, s,
+                               hsmla::GemmSite::kOut, false, wo.blocked));
   r.end();
   return r.ok ? HSMLA_OK : HSMLA_ERR_HIP;
 }
@@ -656,60 +727,53 @@ hsmla_status check_block(const hsmla_desc* desc, const hsmla_weights* w,
   return HSMLA_OK;
 }
 
-hsmla_status fold_ffn_taps(const Dims& D, const hsmla_ffn_weights* f,
-                           float* ftaps, hipStream_t s) {
-  const void* ffn_k[1] = {f->dw_ffn};
-  const int ffn_ks[1] = {3};
-  HSMLA_TRY(hsmla::launch_dw_taps(D.bf, ffn_k, ffn_ks, 1, 3, 4 * D.C, 0, ftaps, s));
-  return HSMLA_OK;
-}
-
 // The block over the images that D (a range, see range_dims) and u cover,
-// as numbered stages (block_stage(0..kBlockStages-1) in order is the whole
-// block); x and out point at the range's first image.  fold: fold both tap
-// sets in line (otherwise they are already in the workspace).
-constexpr int kBlockStages = kModuleStages + 6;
+// as numbered stages (prep, then block_stage(0..kBlockStages-1) in order is
+// the whole block); x and out point at the range's first image.
+constexpr int kBlockStages = kModuleStages + 5;
 
 hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
                          const hsmla_weights* w, const hsmla_ffn_weights* f,
-                         const void* x, void* out, const Bufs& u, bool fold,
-                         hipStream_t s, Rec& r) {
+                         const void* x, void* out, const Bufs& u, hipStream_t s,
+                         Rec& r) {
   const int P = (int)D.P, C = D.C;
   if (st >= 1 && st <= kModuleStages)
-    return module_stage(st - 1, D, desc, w, u.xn, u, fold, s, r);
+    return module_stage(st - 1, D, desc, w, u.xn, u, s, r);
   switch (st) {
     case 0:
       r.mark("layernorm1");
       HSMLA_TRY(hsmla::launch_layernorm(D.bf, x, f->ln1_g, f->ln1_b, u.xn, P, C, s));
       return HSMLA_OK;
-    case kModuleStages + 1:
+    case kModuleStages + 1: {
       // x1 = x + O W_o (residual fused into the projection epilogue)
       r.mark("out_proj_residual");
-      HSMLA_TRY(hsmla::launch_gemm(D.bf, u.o, w->w_o, x, u.x1, P, C, C, s,
-                                   hsmla::GemmSite::kOut));
+      const WSel wo = pick_w(w->w_o, u.wo, P, C, C);
+      HSMLA_TRY(hsmla::launch_gemm(D.bf, u.o, wo.w, x, u.x1, P, C, C, s,
+                                   hsmla::GemmSite::kOut, false, wo.blocked));
       return HSMLA_OK;
+    }
     case kModuleStages + 2:
       r.mark("layernorm2");
       HSMLA_TRY(hsmla::launch_layernorm(D.bf, u.x1, f->ln2_g, f->ln2_b, u.xn, P,
                                         C, s));
       return HSMLA_OK;
-    case kModuleStages + 3:
+    case kModuleStages + 3: {
       r.mark("ffn1_gemm");
-      HSMLA_TRY(hsmla::launch_gemm(D.bf, u.xn, f->w1, nullptr, u.h1, P, 4 * C, C,
-                                   s, hsmla::GemmSite::kFfn1));
+      const WSel w1 = pick_w(f->w1, u.w1, P, 4 * C, C);
+      HSMLA_TRY(hsmla::launch_gemm(D.bf, u.xn, w1.w, nullptr, u.h1, P, 4 * C, C, s,
+                                   hsmla::GemmSite::kFfn1, false, w1.blocked));
       return HSMLA_OK;
-    case kModuleStages + 4:
-      if (!fold) return HSMLA_OK;
-      r.mark("ffn_dw_taps");
-      return fold_ffn_taps(D, f, u.ftaps, s);
-    case kModuleStages + 5:
+    }
+    case kModuleStages + 4: {
       r.mark("ffn_dwconv_gelu");
       HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.h1, u.h2, u.ftaps, 3, D.B, D.gh,
                                      D.gw, 4 * C, true, nullptr, 1, s));
       r.mark("ffn2_gemm_residual");
-      HSMLA_TRY(hsmla::launch_gemm(D.bf, u.h2, f->w2, u.x1, out, P, C, 4 * C, s,
-                                   hsmla::GemmSite::kFfn2));
+      const WSel w2 = pick_w(f->w2, u.w2, P, C, 4 * C);
+      HSMLA_TRY(hsmla::launch_gemm(D.bf, u.h2, w2.w, u.x1, out, P, C, 4 * C, s,
+                                   hsmla::GemmSite::kFfn2, false, w2.blocked));
       return HSMLA_OK;
+    }
     default:
       return HSMLA_ERR_ARG;
   }
@@ -717,10 +781,10 @@ hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
 
 hsmla_status block_range(const Dims& D, const hsmla_desc* desc,
                          const hsmla_weights* w, const hsmla_ffn_weights* f,
-                         const void* x, void* out, const Bufs& u, bool fold,
-                         hipStream_t s, Rec& r) {
+                         const void* x, void* out, const Bufs& u, hipStream_t s,
+                         Rec& r) {
   for (int st = 0; st < kBlockStages; ++st) {
-    const hsmla_status e = block_stage(st, D, desc, w, f, x, out, u, fold, s, r);
+    const hsmla_status e = block_stage(st, D, desc, w, f, x, out, u, s, r);
     if (e != HSMLA_OK) return e;
   }
   return HSMLA_OK;
@@ -734,8 +798,8 @@ hsmla_status block_impl(const hsmla_desc* desc, const hsmla_weights* w,
   hsmla_status st = check_block(desc, w, f, x, out, ws, ws_bytes, &D, &L);
   if (st != HSMLA_OK) return st;
   const Bufs u = bufs_for(D, L, ws, HSMLA_OP_BLOCK, 0);
-  if ((st = block_range(D, desc, w, f, x, out, u, true, s, r)) != HSMLA_OK)
-    return st;
+  if ((st = prep(D, desc, w, f, u, s, r)) != HSMLA_OK) return st;
+  if ((st = block_range(D, desc, w, f, x, out, u, s, r)) != HSMLA_OK) return st;
   r.end();
   return r.ok ? HSMLA_OK : HSMLA_ERR_HIP;
 }
@@ -755,23 +819,9 @@ hsmla_status block_split_impl(const hsmla_desc* desc, const hsmla_weights* w,
   Rec r;
   // float32 chunks the K/V reduction by batch size: one stream keeps the
   // result independent of the split
-  if (D.B < 2 || !D.bf) {
-    const Bufs u = bufs_for(D, L, ws, HSMLA_OP_BLOCK, 0);
-    return block_range(D, desc, w, f, x, out, u, true, s, r);
-  }
   const Bufs u0 = bufs_for(D, L, ws, HSMLA_OP_BLOCK, 0);
-  {
-    // both tap sets in one launch before the fork
-    hsmla::TapSpec q{{nullptr, nullptr, nullptr}, {0, 0, 0}, desc->n_branches,
-                     D.kmax, 3 * D.C, 1, u0.taps};
-    for (int i = 0; i < desc->n_branches; ++i) {
-      q.kernels[i] = w->dw[i];
-      q.ks[i] = desc->branch_k[i];
-    }
-    const hsmla::TapSpec ff{{f->dw_ffn, nullptr, nullptr}, {3, 0, 0}, 1, 3,
-                            4 * D.C, 0, u0.ftaps};
-    HSMLA_TRY(hsmla::launch_dw_taps2(D.bf, q, &ff, s));
-  }
+  if ((st = prep(D, desc, w, f, u0, s, r)) != HSMLA_OK) return st;
+  if (D.B < 2 || !D.bf) return block_range(D, desc, w, f, x, out, u0, s, r);
   HSMLA_TRY(hipEventRecord(fork, s));
   HSMLA_TRY(hipStreamWaitEvent(aux, fork, 0));
   const int nb0 = (D.B + 1) / 2, nb1 = D.B - nb0;
@@ -783,10 +833,8 @@ hsmla_status block_split_impl(const hsmla_desc* desc, const hsmla_weights* w,
   // the two ranges' launches are enqueued alternately, stage by stage, so
   // both streams have work from the start
   for (int k = 0; k < kBlockStages; ++k) {
-    if ((st = block_stage(k, D0, desc, w, f, x, out, u0, false, s, r)) != HSMLA_OK)
-      return st;
-    if ((st = block_stage(k, D1, desc, w, f, x1, out1, u1, false, aux, r)) != HSMLA_OK)
-      return st;
+    if ((st = block_stage(k, D0, desc, w, f, x, out, u0, s, r)) != HSMLA_OK) return st;
+    if ((st = block_stage(k, D1, desc, w, f, x1, out1, u1, aux, r)) != HSMLA_OK) return st;
   }
   HSMLA_TRY(hipEventRecord(join, aux));
   HSMLA_TRY(hipStreamWaitEvent(s, join, 0));

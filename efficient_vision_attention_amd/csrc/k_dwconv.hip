@@ -20,38 +20,6 @@
 namespace hsmla {
 namespace {
 
-struct KernelSet {
-  const void* p[3];
-  int k[3];
-  int nk, kmax, ch, identity;
-  float* weff;
-  int count() const { return kmax * kmax * ch; }
-};
-
-// One (tap, channel) per thread of kmax*kmax taps x ch channels; a second
-// tap set (count 0 when absent) takes the threads after the first's.
-template <typename T>
-__global__ void dw_taps_kernel(KernelSet a, KernelSet b) {
-  int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const int na = a.kmax * a.kmax * a.ch;
-  const bool second = idx >= na;
-  if (second) idx -= na;
-  const KernelSet& ks = second ? b : a;
-  const int kmax = ks.kmax, ch = ks.ch, nk = ks.nk;
-  if (idx >= kmax * kmax * ch) return;
-  const int c = idx % ch, tap = idx / ch;
-  const int dy = tap / kmax, dx = tap % kmax;
-  const int rmax = (kmax - 1) / 2;
-  float v = (ks.identity && dy == rmax && dx == rmax) ? 1.f : 0.f;
-  for (int i = 0; i < nk; ++i) {
-    const int k = ks.k[i], r = (k - 1) / 2;
-    const int ky = dy - rmax + r, kx = dx - rmax + r;
-    if (ky >= 0 && ky < k && kx >= 0 && kx < k)
-      v += to_f32(static_cast<const T*>(ks.p[i])[((size_t)c * k + ky) * k + kx]);
-  }
-  ks.weff[idx] = v;
-}
-
 // GELU(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)) with erf from
 // Abramowitz & Stegun 7.1.28:
 //   erf(z) = 1 - (1 + a1 z + a2 z^2 + ... + a6 z^6)^-16,  z >= 0,
@@ -679,46 +647,6 @@ hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
 }
 
 }  // namespace
-
-namespace {
-KernelSet tap_set(const TapSpec& t) {
-  KernelSet set{};
-  for (int i = 0; i < t.nk; ++i) {
-    set.p[i] = t.kernels[i];
-    set.k[i] = t.ks[i];
-  }
-  set.nk = t.nk;
-  set.kmax = t.kmax;
-  set.ch = t.ch;
-  set.identity = t.identity;
-  set.weff = t.weff;
-  return set;
-}
-}  // namespace
-
-hipError_t launch_dw_taps2(bool bf, const TapSpec& first, const TapSpec* second,
-                           hipStream_t s) {
-  const KernelSet a = tap_set(first);
-  KernelSet b{};
-  if (second) b = tap_set(*second);
-  const unsigned blocks = (unsigned)((a.count() + b.count() + 255) / 256);
-  if (bf)
-    dw_taps_kernel<bf16><<<blocks, 256, 0, s>>>(a, b);
-  else
-    dw_taps_kernel<float><<<blocks, 256, 0, s>>>(a, b);
-  return hipGetLastError();
-}
-
-hipError_t launch_dw_taps(bool bf, const void* const* kernels, const int* ks,
-                          int nk, int kmax, int ch, int identity, float* weff,
-                          hipStream_t s) {
-  TapSpec t{{nullptr, nullptr, nullptr}, {0, 0, 0}, nk, kmax, ch, identity, weff};
-  for (int i = 0; i < nk; ++i) {
-    t.kernels[i] = kernels[i];
-    t.ks[i] = ks[i];
-  }
-  return launch_dw_taps2(bf, t, nullptr, s);
-}
 
 bool dwconv_can_pool(int kmax, int block) {
   const int tw = dw_width(kmax, false);

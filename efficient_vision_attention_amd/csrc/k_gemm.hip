@@ -48,7 +48,8 @@ __device__ __forceinline__ uint4 ld16(const bf16* p) {
 
 // SITE only names the call site (one kernel symbol per projection, so
 // profiles tell the four GEMMs apart); the code is the same.
-template <int BM, int BN, int BK, int WGM, int WGN, int SITE, int PF, bool EDGE, int NKT>
+template <int BM, int BN, int BK, int WGM, int WGN, int SITE, int PF, bool EDGE, int NKT,
+          int BLK>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
     const bf16* __restrict__ A, const bf16* __restrict__ W,
     const bf16* __restrict__ R, bf16* __restrict__ C, int M, int N, int K,
@@ -89,16 +90,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int c = tid + NT * i;
-      int gm = m0 + c / CPR, gk = k0 + (c % CPR) * 8;
-      if (EDGE) { gm = min(gm, M - 1); gk = min(gk, K - 8); }
-      xa[i] = ld16(A + (size_t)gm * K + gk);
+      if constexpr ((BLK & 1) != 0) {
+        // tile-blocked A: this tile's K step is one contiguous block
+        xa[i] = ld16(A + ((size_t)(m0 / BM) * (K / BK) + k0 / BK) * (BM * BK) + (size_t)c * 8);
+      } else {
+        int gm = m0 + c / CPR, gk = k0 + (c % CPR) * 8;
+        if (EDGE) { gm = min(gm, M - 1); gk = min(gk, K - 8); }
+        xa[i] = ld16(A + (size_t)gm * K + gk);
+      }
     }
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
       const int c = tid + NT * i;
-      int gn = n0 + c / CPR, gk = k0 + (c % CPR) * 8;
-      if (EDGE) { gn = min(gn, N - 1); gk = min(gk, K - 8); }
-      xw[i] = ld16(W + (size_t)gn * K + gk);
+      if constexpr ((BLK & 2) != 0) {
+        xw[i] = ld16(W + ((size_t)(n0 / BN) * (K / BK) + k0 / BK) * (BN * BK) + (size_t)c * 8);
+      } else {
+        int gn = n0 + c / CPR, gk = k0 + (c % CPR) * 8;
+        if (EDGE) { gn = min(gn, N - 1); gk = min(gk, K - 8); }
+        xw[i] = ld16(W + (size_t)gn * K + gk);
+      }
     }
   };
   auto store_tile = [&](const uint4 (&xa)[LA], const uint4 (&xw)[LW], int buf, int k0) {
@@ -284,13 +294,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int SITE, int PF, bool EDGE,
-          int NKT>
+          int NKT, int BLK = 0>
 void launch_tiles(const void* A, const void* W, const void* R, void* C, int M,
                   int N, int K, hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int total = tiles_m * tiles_n;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  gemm_mfma_bf16<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT>
+  gemm_mfma_bf16<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, BLK>
       <<<per_xcd * kXcds, 64 * WGM * WGN, 0, s>>>(
           static_cast<const bf16*>(A), static_cast<const bf16*>(W),
           static_cast<const bf16*>(R), static_cast<bf16*>(C), M, N, K, tiles_n,
@@ -299,18 +309,33 @@ void launch_tiles(const void* A, const void* W, const void* R, void* C, int M,
 
 // Shapes that are whole tiles with K = 384 or 1536 (the block's projections
 // at C = 384) get the unrolled two-step prefetch; other whole-tile shapes a
-// runtime K loop; ragged shapes the bounds-checked variant.
+// runtime K loop; ragged shapes the bounds-checked variant (plain layouts
+// only).  blk: bit 0 A tile-blocked, bit 1 W tile-blocked.
+template <int BM, int BN, int BK, int WGM, int WGN, int SITE, int PF, bool EDGE, int NKT>
+void launch_blk(int blk, const void* A, const void* W, const void* R, void* C,
+                int M, int N, int K, hipStream_t s) {
+  switch (blk) {
+    case 1: launch_tiles<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, 1>(A, W, R, C, M, N, K, s); break;
+    case 2: launch_tiles<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, 2>(A, W, R, C, M, N, K, s); break;
+    case 3: launch_tiles<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, 3>(A, W, R, C, M, N, K, s); break;
+    default: launch_tiles<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, 0>(A, W, R, C, M, N, K, s); break;
+  }
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN, int SITE>
-void run_tiles(const void* A, const void* W, const void* R, void* C, int M,
-               int N, int K, hipStream_t s) {
-  if (M % BM || N % BN || K % BK)
+hipError_t run_tiles(const void* A, const void* W, const void* R, void* C, int M,
+                     int N, int K, int blk, hipStream_t s) {
+  if (M % BM || N % BN || K % BK) {
+    if (blk) return hipErrorInvalidValue;
     launch_tiles<BM, BN, BK, WGM, WGN, SITE, 1, true, 0>(A, W, R, C, M, N, K, s);
-  else if (K == 12 * BK)
-    launch_tiles<BM, BN, BK, WGM, WGN, SITE, 2, false, 12>(A, W, R, C, M, N, K, s);
-  else if (K == 48 * BK)
-    launch_tiles<BM, BN, BK, WGM, WGN, SITE, 2, false, 48>(A, W, R, C, M, N, K, s);
-  else
-    launch_tiles<BM, BN, BK, WGM, WGN, SITE, 1, false, 0>(A, W, R, C, M, N, K, s);
+  } else if (K == 12 * BK) {
+    launch_blk<BM, BN, BK, WGM, WGN, SITE, 2, false, 12>(blk, A, W, R, C, M, N, K, s);
+  } else if (K == 48 * BK) {
+    launch_blk<BM, BN, BK, WGM, WGN, SITE, 2, false, 48>(blk, A, W, R, C, M, N, K, s);
+  } else {
+    launch_blk<BM, BN, BK, WGM, WGN, SITE, 1, false, 0>(blk, A, W, R, C, M, N, K, s);
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -376,23 +401,31 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ A,
 // measured best on MI355X for all four projection shapes of the block
 // (M = 65536; N, K = 1152, 384 / 384, 384 / 1536, 384 / 384, 1536).
 template <int SITE>
-void run_mfma(const void* A, const void* W, const void* R, void* C, int M,
-              int N, int K, hipStream_t s) {
-  run_tiles<256, 128, 32, 2, 2, SITE>(A, W, R, C, M, N, K, s);
+hipError_t run_mfma(const void* A, const void* W, const void* R, void* C, int M,
+                    int N, int K, int blk, hipStream_t s) {
+  static_assert(kGemmTileM == 256 && kGemmTileN == 128 && kGemmTileK == 32,
+                "the blocked layout follows the tile");
+  return run_tiles<256, 128, 32, 2, 2, SITE>(A, W, R, C, M, N, K, blk, s);
 }
 
 }  // namespace
 
+bool gemm_whole_tiles(int M, int N, int K) {
+  return M % kGemmTileM == 0 && N % kGemmTileN == 0 && K % kGemmTileK == 0;
+}
+
 hipError_t launch_gemm(bool bf, const void* A, const void* W, const void* R,
                        void* C, int M, int N, int K, hipStream_t s,
-                       GemmSite site) {
+                       GemmSite site, bool a_blocked, bool w_blocked) {
   if (M == 0 || N == 0) return hipSuccess;
+  const int blk = (a_blocked ? 1 : 0) | (w_blocked ? 2 : 0);
+  if (blk && (!bf || !gemm_whole_tiles(M, N, K))) return hipErrorInvalidValue;
   if (bf) {
     switch (site) {
-      case GemmSite::kQkv: run_mfma<0>(A, W, R, C, M, N, K, s); break;
-      case GemmSite::kOut: run_mfma<1>(A, W, R, C, M, N, K, s); break;
-      case GemmSite::kFfn1: run_mfma<2>(A, W, R, C, M, N, K, s); break;
-      default: run_mfma<3>(A, W, R, C, M, N, K, s); break;
+      case GemmSite::kQkv: return run_mfma<0>(A, W, R, C, M, N, K, blk, s);
+      case GemmSite::kOut: return run_mfma<1>(A, W, R, C, M, N, K, blk, s);
+      case GemmSite::kFfn1: return run_mfma<2>(A, W, R, C, M, N, K, blk, s);
+      default: return run_mfma<3>(A, W, R, C, M, N, K, blk, s);
     }
   } else {
     dim3 grid((N + kTN - 1) / kTN, (M + kTM - 1) / kTM);

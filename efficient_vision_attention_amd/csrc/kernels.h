@@ -12,11 +12,22 @@ namespace hsmla {
 // Which projection a GEMM launch is (only used to name the kernel symbol).
 enum class GemmSite { kQkv, kOut, kFfn1, kFfn2 };
 
-// C[M][N] = A[M][K] . W[N][K]^T (+ R[M][N] when R != nullptr), row-major.
-// N and K must be multiples of 32 (8-element chunks are loaded whole).
+// Tile shape of the bf16 GEMM.  Its whole-tile path (M, N, K multiples of
+// the tile) can read "tile-blocked" operands: element (r, k) of a row-major
+// [R][K] matrix stored at ((r / TR) * (K / 32) + k / 32) * TR * 32 +
+// (r % TR) * 32 + k % 32, so one K step of one tile is one contiguous block;
+// TR = kGemmTileM for A, kGemmTileN for W.
+constexpr int kGemmTileM = 256, kGemmTileN = 128, kGemmTileK = 32;
+bool gemm_whole_tiles(int M, int N, int K);
+
+// C[M][N] = A[M][K] . W[N][K]^T (+ R[M][N] when R != nullptr), row-major C
+// and R.  N and K must be multiples of 32 (8-element chunks are loaded
+// whole).  a_blocked / w_blocked: A / W are tile-blocked (bf16 and
+// gemm_whole_tiles(M, N, K) only; otherwise hipErrorInvalidValue).
 hipError_t launch_gemm(bool bf, const void* A, const void* W, const void* R,
                        void* C, int M, int N, int K, hipStream_t s,
-                       GemmSite site);
+                       GemmSite site, bool a_blocked = false,
+                       bool w_blocked = false);
 
 // Effective depthwise taps: weff[tap][ch] (float32, kmax x kmax taps) =
 // identity (centre tap += 1 when `identity`) + sum of the given kernels,
@@ -25,15 +36,21 @@ hipError_t launch_dw_taps(bool bf, const void* const* kernels, const int* ks,
                           int nk, int kmax, int ch, int identity, float* weff,
                           hipStream_t s);
 
-// Two tap sets folded by one launch (second may be NULL).
+// One launch folding up to two tap sets (as launch_dw_taps) and writing
+// tile-blocked copies of up to four bf16 matrices (see launch_gemm).
 struct TapSpec {
   const void* kernels[3];
   int ks[3];
   int nk, kmax, ch, identity;
   float* weff;
 };
-hipError_t launch_dw_taps2(bool bf, const TapSpec& first, const TapSpec* second,
-                           hipStream_t s);
+struct BlockJob {
+  const void* src;  // [rows][cols] row-major bf16
+  void* dst;        // tile-blocked copy
+  int rows, cols, tile_rows;
+};
+hipError_t launch_prep(bool bf, const TapSpec* taps, int ntaps,
+                       const BlockJob* jobs, int njobs, hipStream_t s);
 
 // out[b][y][x][c] = act(sum_tap weff[tap][c] * in[b][y+dy-r][x+dx-r][c]),
 // zero padding, r = (kmax-1)/2; act = exact GELU when `gelu`.  With bsum
