@@ -366,9 +366,10 @@ Dims range_dims(const Dims& D, int nb) {
 // (range_dims), u the matching pointers.
 constexpr int kModuleStages = 7;
 
+// x_blk: x is tile-blocked (written so by the block's LayerNorm).
 hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
                           const hsmla_weights* w, const void* x, const Bufs& u,
-                          hipStream_t s, Rec& r) {
+                          hipStream_t s, Rec& r, bool x_blk = false) {
   (void)d;
   // the plain gate's block sums come out of the depthwise conv when its
   // workgroup shape allows; the gate then only forms the logits
@@ -379,7 +380,7 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
       r.mark("qkv_gemm");
       const WSel q = pick_w(w->w_qkv, u.wq, (int)D.P, 3 * D.C, D.C);
       HSMLA_TRY(hsmla::launch_gemm(D.bf, x, q.w, nullptr, u.qkv, (int)D.P, 3 * D.C,
-                                   D.C, s, hsmla::GemmSite::kQkv, false, q.blocked));
+                                   D.C, s, hsmla::GemmSite::kQkv, x_blk, q.blocked));
       return HSMLA_OK;
     }
     case 1:
@@ -737,12 +738,22 @@ hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
                          const void* x, void* out, const Bufs& u, hipStream_t s,
                          Rec& r) {
   const int P = (int)D.P, C = D.C;
+  // The LayerNorms and the FFN conv write their outputs tile-blocked when
+  // the GEMM that reads them takes its whole-tile path (each K step of an A
+  // tile is then one contiguous block).
+  const bool ln1_blk = hsmla::layernorm_can_block(D.bf, P, C) &&
+                       hsmla::gemm_whole_tiles(P, 3 * C, C);
+  const bool ln2_blk = hsmla::layernorm_can_block(D.bf, P, C) &&
+                       hsmla::gemm_whole_tiles(P, 4 * C, C);
+  const bool h2_blk = hsmla::dwconv_can_block_out(D.bf, 3, true, D.B, D.gh, D.gw, 4 * C) &&
+                      hsmla::gemm_whole_tiles(P, C, 4 * C);
   if (st >= 1 && st <= kModuleStages)
-    return module_stage(st - 1, D, desc, w, u.xn, u, s, r);
+    return module_stage(st - 1, D, desc, w, u.xn, u, s, r, ln1_blk);
   switch (st) {
     case 0:
       r.mark("layernorm1");
-      HSMLA_TRY(hsmla::launch_layernorm(D.bf, x, f->ln1_g, f->ln1_b, u.xn, P, C, s));
+      HSMLA_TRY(hsmla::launch_layernorm(D.bf, x, f->ln1_g, f->ln1_b, u.xn, P, C, s,
+                                        ln1_blk));
       return HSMLA_OK;
     case kModuleStages + 1: {
       // x1 = x + O W_o (residual fused into the projection epilogue)
@@ -755,23 +766,23 @@ hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
     case kModuleStages + 2:
       r.mark("layernorm2");
       HSMLA_TRY(hsmla::launch_layernorm(D.bf, u.x1, f->ln2_g, f->ln2_b, u.xn, P,
-                                        C, s));
+                                        C, s, ln2_blk));
       return HSMLA_OK;
     case kModuleStages + 3: {
       r.mark("ffn1_gemm");
       const WSel w1 = pick_w(f->w1, u.w1, P, 4 * C, C);
       HSMLA_TRY(hsmla::launch_gemm(D.bf, u.xn, w1.w, nullptr, u.h1, P, 4 * C, C, s,
-                                   hsmla::GemmSite::kFfn1, false, w1.blocked));
+                                   hsmla::GemmSite::kFfn1, ln2_blk, w1.blocked));
       return HSMLA_OK;
     }
     case kModuleStages + 4: {
       r.mark("ffn_dwconv_gelu");
       HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.h1, u.h2, u.ftaps, 3, D.B, D.gh,
-                                     D.gw, 4 * C, true, nullptr, 1, s));
+                                     D.gw, 4 * C, true, nullptr, 1, s, h2_blk));
       r.mark("ffn2_gemm_residual");
       const WSel w2 = pick_w(f->w2, u.w2, P, C, 4 * C);
       HSMLA_TRY(hsmla::launch_gemm(D.bf, u.h2, w2.w, u.x1, out, P, C, 4 * C, s,
-                                   hsmla::GemmSite::kFfn2, false, w2.blocked));
+                                   hsmla::GemmSite::kFfn2, h2_blk, w2.blocked));
       return HSMLA_OK;
     }
     default:

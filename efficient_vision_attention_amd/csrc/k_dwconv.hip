@@ -392,12 +392,15 @@ __global__ __launch_bounds__(256) void dwconv_stream(
 // as above (K partial output rows in registers).  Compared with the
 // register-only kernel the bytes in flight per workgroup no longer scale
 // with the per-thread tap registers.
-template <typename T, int K, bool GELU, int V, int P, bool POOL, int WC>
+// BO: out is written tile-blocked for the GEMM (token m of the launch,
+// channel k at ((m / 256) * (ch / 32) + k / 32) * 8192 + (m % 256) * 32 +
+// k % 32); out_bytes_all is then the whole output's size in bytes.
+template <typename T, int K, bool GELU, int V, int P, bool POOL, int WC, bool BO>
 __global__ __launch_bounds__(256) void dwconv_lds(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, float* __restrict__ bsum, int block,
     int gh, int gw, int ch, int col_tiles, int ch_tiles, int strips,
-    int total, int per_xcd) {
+    int total, int per_xcd, int out_bytes_all) {
   constexpr int R = (K - 1) / 2;
   constexpr int CG = WC / V;  // channel groups per workgroup
   constexpr int TW = 256 / CG;         // columns per workgroup
@@ -536,10 +539,22 @@ __global__ __launch_bounds__(256) void dwconv_lds(
         float o[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) o[j] = GELU ? gelu_erf(acc[done][j]) : acc[done][j];
-        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
-            out + (img + (size_t)min(max(yo, 0), gh - 1) * gw + x0) * ch,
-            row_out ? out_bytes : 0);
-        store_buf<T, V>(rs, st_off, o);
+        if constexpr (BO) {
+          const int m = (b * gh + yo) * gw + x;
+          const int off =
+              (row_out && x < gw && c_ok)
+                  ? (((m / kGemmTileM) * (ch / kGemmTileK) + c / kGemmTileK) *
+                         (kGemmTileM * kGemmTileK) +
+                     (m % kGemmTileM) * kGemmTileK + c % kGemmTileK) *
+                        (int)sizeof(T)
+                  : kOob;
+          store_buf<T, V>(buf_rsrc(out, out_bytes_all), off, o);
+        } else {
+          const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
+              out + (img + (size_t)min(max(yo, 0), gh - 1) * gw + x0) * ch,
+              row_out ? out_bytes : 0);
+          store_buf<T, V>(rs, st_off, o);
+        }
         if constexpr (POOL) {
           round_to<T, V>(o);
           const bool mine = row_out && st_off != kOob;
@@ -600,7 +615,8 @@ constexpr int dw_width(int k, bool gelu) {
 
 template <typename T, int K, bool GELU>
 hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
-                  int block, int batch, int gh, int gw, int ch, hipStream_t s) {
+                  int block, int batch, int gh, int gw, int ch, bool out_blocked,
+                  hipStream_t s) {
   constexpr DwCfg cf = dw_cfg(K, GELU);
   constexpr int TW = dw_width(K, GELU);
   const int col_tiles = (gw + TW - 1) / TW;
@@ -621,27 +637,33 @@ hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
   }
   if constexpr (!GELU) {
     if (bsum) {
-      dwconv_lds<T, K, false, cf.v, cf.p, true, cf.wc><<<per_xcd * kXcds, 256, 0, s>>>(
+      dwconv_lds<T, K, false, cf.v, cf.p, true, cf.wc, false><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
-          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
+          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0);
       return hipGetLastError();
     }
   }
-  dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc><<<per_xcd * kXcds, 256, 0, s>>>(
-      static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
-      gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
+  if (out_blocked)
+    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, true><<<per_xcd * kXcds, 256, 0, s>>>(
+        static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
+        gw, ch, col_tiles, ch_tiles, strips, total, per_xcd,
+        (int)((size_t)batch * gh * gw * ch * sizeof(T)));
+  else
+    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, false><<<per_xcd * kXcds, 256, 0, s>>>(
+        static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
+        gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0);
   return hipGetLastError();
 }
 
 template <typename T, bool GELU>
 hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
                       float* bsum, int block, int batch, int gh, int gw, int ch,
-                      hipStream_t s) {
+                      bool out_blocked, hipStream_t s) {
   switch (kmax) {
-    case 1: return run_dw<T, 1, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
-    case 3: return run_dw<T, 3, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
-    case 5: return run_dw<T, 5, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
-    case 7: return run_dw<T, 7, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, s);
+    case 1: return run_dw<T, 1, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s);
+    case 3: return run_dw<T, 3, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s);
+    case 5: return run_dw<T, 5, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s);
+    case 7: return run_dw<T, 7, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -653,15 +675,29 @@ bool dwconv_can_pool(int kmax, int block) {
   return block >= kPoolMinBlock && tw % block == 0 && TH % block == 0;
 }
 
+bool dwconv_can_block_out(bool bf, int kmax, bool gelu, int batch, int gh, int gw,
+                          int ch) {
+  const size_t tokens = (size_t)batch * gh * gw;
+  return bf && gelu && kmax <= 3 && tokens % kGemmTileM == 0 && ch % kGemmTileK == 0 &&
+         tokens * ch * 2 < ((size_t)1 << 31);
+}
+
 hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
                          int kmax, int batch, int gh, int gw, int ch,
-                         bool gelu, float* bsum, int block, hipStream_t s) {
+                         bool gelu, float* bsum, int block, hipStream_t s,
+                         bool out_blocked) {
   if (bsum && (gelu || !dwconv_can_pool(kmax, block))) return hipErrorInvalidValue;
+  if (out_blocked && !dwconv_can_block_out(bf, kmax, gelu, batch, gh, gw, ch))
+    return hipErrorInvalidValue;
   if (bf)
-    return gelu ? dispatch_k<bf16, true>(kmax, in, out, weff, nullptr, 1, batch, gh, gw, ch, s)
-                : dispatch_k<bf16, false>(kmax, in, out, weff, bsum, block, batch, gh, gw, ch, s);
-  return gelu ? dispatch_k<float, true>(kmax, in, out, weff, nullptr, 1, batch, gh, gw, ch, s)
-              : dispatch_k<float, false>(kmax, in, out, weff, bsum, block, batch, gh, gw, ch, s);
+    return gelu ? dispatch_k<bf16, true>(kmax, in, out, weff, nullptr, 1, batch, gh, gw, ch,
+                                         out_blocked, s)
+                : dispatch_k<bf16, false>(kmax, in, out, weff, bsum, block, batch, gh, gw,
+                                          ch, false, s);
+  return gelu ? dispatch_k<float, true>(kmax, in, out, weff, nullptr, 1, batch, gh, gw, ch,
+                                        false, s)
+              : dispatch_k<float, false>(kmax, in, out, weff, bsum, block, batch, gh, gw, ch,
+                                         false, s);
 }
 
 }  // namespace hsmla

@@ -125,7 +125,9 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
 // group, in a fixed order.
 constexpr int kSteps = 4;
 
-template <typename T, int NV>
+// BLK: y is written tile-blocked for the GEMM (row r, channel k at
+// ((r / 256) * (ch / 32) + k / 32) * 8192 + (r % 256) * 32 + k % 32).
+template <typename T, int NV, bool BLK>
 __global__ __launch_bounds__(256) void layernorm16_kernel(
     const T* __restrict__ x, const float* __restrict__ g,
     const float* __restrict__ be, T* __restrict__ y, int rows, int ch) {
@@ -183,22 +185,32 @@ __global__ __launch_bounds__(256) void layernorm16_kernel(
       float o[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) o[j] = (v[i][j] - mean) * rstd * gv[i][j] + bv[i][j];
-      Vec<T>::store(yr + (gl + 16 * i) * V, o);
+      const int k = (gl + 16 * i) * V;
+      if constexpr (BLK)
+        Vec<T>::store(y + ((size_t)(row / kGemmTileM) * (ch / kGemmTileK) + k / kGemmTileK) *
+                              (kGemmTileM * kGemmTileK) +
+                          (row % kGemmTileM) * kGemmTileK + k % kGemmTileK,
+                      o);
+      else
+        Vec<T>::store(yr + k, o);
     }
   }
 }
 
 template <typename T, int NV>
 hipError_t run_ln16(const T* x, const float* gamma, const float* beta, T* y,
-                    int rows, int ch, hipStream_t s) {
+                    int rows, int ch, bool blocked, hipStream_t s) {
   const unsigned blocks = (unsigned)((rows + 16 * kSteps - 1) / (16 * kSteps));
-  layernorm16_kernel<T, NV><<<blocks, 256, 0, s>>>(x, gamma, beta, y, rows, ch);
+  if (blocked)
+    layernorm16_kernel<T, NV, true><<<blocks, 256, 0, s>>>(x, gamma, beta, y, rows, ch);
+  else
+    layernorm16_kernel<T, NV, false><<<blocks, 256, 0, s>>>(x, gamma, beta, y, rows, ch);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t run_ln(const void* x, const float* gamma, const float* beta, void* y,
-                  int rows, int ch, hipStream_t s) {
+                  int rows, int ch, bool blocked, hipStream_t s) {
   const unsigned blocks = (unsigned)((rows + 4 * kRows - 1) / (4 * kRows));
   const int ni = (ch / Vec<T>::N + 63) / 64;
   const T* xi = static_cast<const T*>(x);
@@ -206,13 +218,14 @@ hipError_t run_ln(const void* x, const float* gamma, const float* beta, void* y,
   const int nvec = ch / Vec<T>::N;
   if (nvec % 16 == 0) {
     switch (nvec / 16) {
-      case 1: return run_ln16<T, 1>(xi, gamma, beta, yo, rows, ch, s);
-      case 2: return run_ln16<T, 2>(xi, gamma, beta, yo, rows, ch, s);
-      case 3: return run_ln16<T, 3>(xi, gamma, beta, yo, rows, ch, s);
-      case 4: return run_ln16<T, 4>(xi, gamma, beta, yo, rows, ch, s);
+      case 1: return run_ln16<T, 1>(xi, gamma, beta, yo, rows, ch, blocked, s);
+      case 2: return run_ln16<T, 2>(xi, gamma, beta, yo, rows, ch, blocked, s);
+      case 3: return run_ln16<T, 3>(xi, gamma, beta, yo, rows, ch, blocked, s);
+      case 4: return run_ln16<T, 4>(xi, gamma, beta, yo, rows, ch, blocked, s);
       default: break;
     }
   }
+  if (blocked) return hipErrorInvalidValue;
   if (ni <= 1)
     layernorm_kernel<T, 1><<<blocks, 256, 0, s>>>(xi, gamma, beta, yo, rows, ch);
   else if (ni <= 2)
@@ -227,11 +240,18 @@ hipError_t run_ln(const void* x, const float* gamma, const float* beta, void* y,
 
 }  // namespace
 
+bool layernorm_can_block(bool bf, int rows, int ch) {
+  const int nvec = ch / 8;
+  return bf && ch % 8 == 0 && nvec % 16 == 0 && nvec / 16 <= 4 &&
+         rows % kGemmTileM == 0 && ch % kGemmTileK == 0;
+}
+
 hipError_t launch_layernorm(bool bf, const void* x, const float* gamma,
                             const float* beta, void* y, int rows, int ch,
-                            hipStream_t s) {
-  return bf ? run_ln<bf16>(x, gamma, beta, y, rows, ch, s)
-            : run_ln<float>(x, gamma, beta, y, rows, ch, s);
+                            hipStream_t s, bool blocked) {
+  if (blocked && !layernorm_can_block(bf, rows, ch)) return hipErrorInvalidValue;
+  return bf ? run_ln<bf16>(x, gamma, beta, y, rows, ch, blocked, s)
+            : run_ln<float>(x, gamma, beta, y, rows, ch, blocked, s);
 }
 
 }  // namespace hsmla

@@ -60,7 +60,12 @@ hipError_t launch_prep(bool bf, const TapSpec* taps, int ntaps,
 bool dwconv_can_pool(int kmax, int block);
 hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
                          int kmax, int batch, int gh, int gw, int ch,
-                         bool gelu, float* bsum, int block, hipStream_t s);
+                         bool gelu, float* bsum, int block, hipStream_t s,
+                         bool out_blocked = false);
+// Whether launch_dwconv can write out tile-blocked as the GEMM's A operand
+// (bf16 3x3 with GELU, token count a multiple of kGemmTileM, under 2 GiB).
+bool dwconv_can_block_out(bool bf, int kmax, bool gelu, int batch, int gh, int gw,
+                          int ch);
 
 // Number of token chunks the KV-state reduction splits each image into.
 int kv_chunks(bool bf, int batch, int heads, int tokens);
@@ -124,6 +129,9 @@ hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
 // y = LN(x) . gamma + beta over the channel dimension.
 hipError_t launch_layernorm(bool bf, const void* x, const float* gamma,
                             const float* beta, void* y, int rows, int ch,
-                            hipStream_t s);
+                            hipStream_t s, bool blocked = false);
+// Whether launch_layernorm can write y tile-blocked as the GEMM's A operand
+// (bf16, rows a multiple of kGemmTileM, rows of 128..512 channels).
+bool layernorm_can_block(bool bf, int rows, int ch);
 
 }  // namespace hsmla
