@@ -23,6 +23,7 @@ namespace hsmla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
@@ -283,10 +284,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
           v[2 * t + 1] += __uint_as_float(rw4[t] & 0xffff0000u);
         }
       }
-      if (!EDGE || (gm < M && gn < N))
-        *reinterpret_cast<uint4*>(C + (size_t)gm * N + gn) =
-            uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      if (!EDGE || (gm < M && gn < N)) {
+        const u32x4 vv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+        u32x4* dst = reinterpret_cast<u32x4*>(C + (size_t)gm * N + gn);
+        // the FFN projections stream their outputs past the caches
+        // (measured: FFN1 -8 us, and the conv reading its output is no
+        // slower; the QKV output is left cached for the conv that follows)
+        if constexpr (SITE >= 2)
+          __builtin_nontemporal_store(vv, dst);
+        else
+          *dst = vv;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
