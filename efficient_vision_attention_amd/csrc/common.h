@@ -58,8 +58,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base,
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes, streamed (non-temporal: the readers of whole staged rows use
+// each byte once; measured faster for the K/V state and no slower for the
+// readout and the FFN conv).
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
   return uint4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
 }
 
