@@ -249,7 +249,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
         const int r = c / CPRO, cc = (c % CPRO) * 8;
         int gm = m0 + wm + 32 * i + r, gn = n0 + wn + cc;
         if (EDGE) { gm = min(gm, M - 1); gn = min(gn, N - 8); }
-        rres[i][q] = ld16(R + (size_t)gm * N + gn);
+        // read once: streamed past the caches
+        rres[i][q] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                                   reinterpret_cast<const u32x4*>(
+                                                       R + (size_t)gm * N + gn)));
       }
   }
   __syncthreads();
