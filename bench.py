@@ -4,9 +4,9 @@
 Workload: 2 images of 128 x 256 tokens, C = 384 (12 heads of 32), bf16,
 identity + 3x3 + 5x5 depthwise branches, 8 x 8 blocks, 16 x 16 softmax
 windows, keep ratio 10% (52 of 512 blocks per image), wrapped in the LN /
-FFN-DWConv block.  One step = one call of hsmla_block_forward_split over
-the batch (the two images on two streams; --streams 1: hsmla_block_forward
-on one), i.e. every kernel of the path.  Inputs are seeded synthetic data
+FFN-DWConv block.  One step = one call of hsmla_block_forward over the batch
+on one stream (--streams 2: hsmla_block_forward_split, the two images on two
+streams), i.e. every kernel of the path; the other mode is timed beside it.  Inputs are seeded synthetic data
 (street-scene-like smooth field plus noise) already resident in HBM.
 
 Prints one JSON line: tokens/s, the per-kernel breakdown from HIP events
@@ -47,9 +47,10 @@ def parse():
                     help="depthwise branch sizes added to the identity")
     ap.add_argument("--gate-conv", action="store_true",
                     help="depthwise 3x3 inside the gate's head score")
-    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
-                    help="2: the block's batch split over two streams "
-                         "(hsmla_block_forward_split); 1: one stream")
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
+                    help="1: one stream (hsmla_block_forward); 2: the block's "
+                         "batch split over two streams "
+                         "(hsmla_block_forward_split)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -278,10 +279,14 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps, ws
 
-    split = H.SplitStreams() if args.streams == 2 else None
+    two = H.SplitStreams()
+    split = two if args.streams == 2 else None
 
     def one_stream_step(m, ws, out):
         H.hsmla_block_forward(m.desc, m.weights, m.ffn, x, out, ws)
+
+    def two_stream_step(m, ws, out):
+        H.hsmla_block_forward_split(m.desc, m.weights, m.ffn, x, out, ws, two)
 
     def block_step(m, ws, out):
         if split is None:
@@ -294,8 +299,8 @@ def main():
 
     model = DeviceModel(shape(base), inp)
     ms, ws = time_steps(model, block_step, args.steps, args.warmup)
-    ms_one = (ms if split is None else
-              time_steps(model, one_stream_step, args.steps, args.warmup)[0])
+    ms_alt = time_steps(model, one_stream_step if split is not None else
+                        two_stream_step, args.steps, args.warmup)[0]
     tokens = base.batch * base.tokens
     base_views = model.views(H.HSMLA_OP_BLOCK, ws)
     sel = base_views["sel"].cpu().numpy()
@@ -429,7 +434,8 @@ def main():
                    "block": base.block, "window": base.window, "keep": base.keep,
                    "keep_blocks": base.keep_blocks, "gate_conv": base.gate_conv,
                    "streams": args.streams},
-        "one_stream_ms_per_step": round(ms_one, 4),
+        ("one_stream_ms_per_step" if split is not None else
+         "two_stream_ms_per_step"): round(ms_alt, 4),
         "roofline": roof,
         "kernels": kernels,
         "sweep": sweep,
