@@ -265,7 +265,10 @@ __device__ int compact_ascending(Pred keep, int n, int32_t* __restrict__ out) {
 // #{u : s_u > s_t or (s_u == s_t and u < t)} is below keep; they are
 // flagged and written out in ascending order by the ballot compaction.  The
 // row is padded to a power of two with key 0, which sorts after every real
-// entry.  O(T log^2 T) comparisons; exact and order-independent.
+// entry.  O(T log^2 T) comparisons; exact and order-independent.  Up to
+// 1024 blocks the rank is counted directly instead (same keys, same
+// result): T^2 comparisons in one pass cost less than the sort's
+// log^2 T / 2 barrier-separated stages.
 __device__ __forceinline__ uint64_t topk_key(float v, int t) {
   uint32_t u = __float_as_uint(v + 0.f);  // -0 -> +0
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -289,6 +292,40 @@ __global__ __launch_bounds__(1024) void topk_kernel(
     }
   }
   __syncthreads();
+  if (tpow <= (int)blockDim.x) {
+    // Up to one key per thread: rank by counting.  rank(t) = #{u : key_u >
+    // key_t}, the keys being distinct; the key range is split into `parts`
+    // runs of at least 64 keys, one thread per (t, run), and the runs'
+    // counts are added in LDS.  Every thread of a wave reads the same keys
+    // (a broadcast).  T^2 comparisons, but no barrier between them.
+    __shared__ int rank[1024];
+    const int parts = min((int)blockDim.x / tpow, max(1, tpow / 64));
+    const int t = threadIdx.x % tpow, q = threadIdx.x / tpow;
+    if (threadIdx.x < tpow) rank[threadIdx.x] = 0;
+    __syncthreads();
+    const int len = tpow / parts;
+    if (q < parts && t < nblocks) {
+      const uint64_t kt = shk[t];
+      const uint64_t* ku = shk + q * len;
+      int cnt = 0;
+      if (len % 16 == 0) {
+        for (int u = 0; u < len; u += 16) {
+          uint64_t v[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = ku[u + i];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) cnt += v[i] > kt;
+        }
+      } else {
+        for (int u = 0; u < len; ++u) cnt += ku[u] > kt;
+      }
+      atomicAdd(&rank[t], cnt);
+    }
+    __syncthreads();
+    compact_ascending([&](int u) { return rank[u] < keep; }, nblocks,
+                      sel + (size_t)b * keep);
+    return;
+  }
   for (int size = 2; size <= tpow; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = threadIdx.x; i < (tpow >> 1); i += blockDim.x) {

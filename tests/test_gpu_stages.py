@@ -129,13 +129,23 @@ def test_gate_select_pooled(name):
 
 
 @pytest.mark.parametrize("T,k,levels", [(16, 4, 3), (45, 14, 5), (1024, 52, 9),
-                                         (2000, 700, 17), (7, 7, 2), (64, 0, 4)])
+                                         (2000, 700, 17), (7, 7, 2), (64, 0, 4),
+                                         (512, 52, 9), (1025, 100, 3),
+                                         (8192, 819, 33), (300, 100, -4)])
 def test_gate_select_injected_scores_exact(T, k, levels):
     """Exact float32 scores with many ties: the index list must equal the
-    oracle's bit for bit (ties to the lower block index, ascending)."""
+    oracle's bit for bit (ties to the lower block index, ascending).  Up to
+    1024 blocks the kernel counts ranks, above it sorts; levels < 0 draws
+    signed scores with -0 and +0 mixed (equal scores)."""
     rng = np.random.default_rng(T + k)
     B = 3
-    scores = (rng.integers(0, levels, size=(B, T)) / levels).astype(np.float32)
+    if levels > 0:
+        scores = (rng.integers(0, levels, size=(B, T)) / levels).astype(np.float32)
+    else:
+        n = -levels
+        scores = (rng.integers(-n, n + 1, size=(B, T)) / n).astype(np.float32)
+        zero = scores == 0
+        scores[zero & (rng.random((B, T)) < 0.5)] = np.float32(-0.0)
     desc = H.make_desc(batch=B, grid_h=1, grid_w=T, channels=32, heads=1,
                        branches=(), block=1, window=1, keep_blocks=k, dtype="bf16")
     s_in = torch.from_numpy(scores).cuda()
