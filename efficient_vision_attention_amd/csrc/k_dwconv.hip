@@ -182,15 +182,23 @@ __device__ __forceinline__ void round_to(float* v) {
 }
 
 constexpr int kStreamChannels = 64;  // channels per workgroup
+// Streaming kernel (5x5, 7x7): channels and output columns per thread, rows
+// of loads in flight.  Measured on the folded 5x5 (7x7) with gate sums:
+// 1 column of 4 channels 116 (196) us, 2 columns 100, 4 columns of 4
+// channels 97, 4 columns of 2 channels 93 (139), 8 columns about the same
+// as 4 but no longer dividing 4 x 4 gate blocks.
+constexpr int kStreamV = 2, kStreamCols = 4, kStreamRows = 2;
 
 // Register-streaming variant (the wider kernels, whose taps take most of the
-// registers).  A thread owns one output column x and V consecutive channels
-// of a 32-row strip and walks down the input rows of the strip.  For each
-// input row it loads the K horizontal neighbours it needs (the K-fold reuse across
-// neighbouring threads is served by the L1), and the row feeds the K partial
-// output rows it belongs to, kept in registers.  NB rows of loads are in
-// flight at any time; there is no LDS and no barrier, so every wave streams
-// independently.  A workgroup covers 64 channels x (256 V / 64) columns.
+// registers).  A thread owns CX adjacent output columns x .. x + CX - 1 and
+// V consecutive channels of a 32-row strip and walks down the input rows of
+// the strip.  For each input row it loads the K + CX - 1 horizontal
+// neighbours it needs (the reuse across neighbouring threads is served by
+// the L1) and converts each once; every tap read serves the CX columns, and
+// the row feeds the K partial output rows it belongs to, kept in
+// registers.  NB rows of loads are in flight at any time; there is no
+// barrier in the row loop, so every wave streams independently.  A
+// workgroup covers 64 channels x (256 V CX / 64) columns.
 // Grid: 1-D over (batch, strip, channel tile, column tile) with the column
 // tile fastest, remapped so each XCD walks a contiguous run of neighbouring
 // tiles (their halo columns then hit in that XCD's L2).
@@ -200,8 +208,8 @@ constexpr int kStreamChannels = 64;  // channels per workgroup
 // parks the sum of each finished block row in LDS (its own slot, no
 // barrier); after the strip one barrier, then the block's columns are
 // added in order.  block must divide the workgroup width and the strip
-// height, and be at least kPoolMinBlock (LDS room).
-template <typename T, int K, bool GELU, int V, int NB, bool POOL, bool TL>
+// height, be a multiple of CX, and be at least kPoolMinBlock (LDS room).
+template <typename T, int K, bool GELU, int V, int NB, bool POOL, bool TL, int CX = 1>
 __global__ __launch_bounds__(256) void dwconv_stream(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, float* __restrict__ bsum, int block,
@@ -209,8 +217,10 @@ __global__ __launch_bounds__(256) void dwconv_stream(
     int total, int per_xcd) {
   constexpr int R = (K - 1) / 2;
   constexpr int CG = kStreamChannels / V;  // channel groups per workgroup
-  constexpr int TW = 256 / CG;         // columns per workgroup
-  __shared__ float red[POOL ? TH / kPoolMinBlock : 1][POOL ? TW : 1][POOL ? kStreamChannels : 1];
+  constexpr int TT = 256 / CG;             // column groups per workgroup
+  constexpr int TW = TT * CX;              // columns per workgroup
+  constexpr int KL = K + CX - 1;           // input columns per thread
+  __shared__ float red[POOL ? TH / kPoolMinBlock : 1][POOL ? TT : 1][POOL ? kStreamChannels : 1];
   const int bid = blockIdx.x;
   const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
   if (tile >= total) return;
@@ -223,8 +233,8 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   const int b = rest / strips;
 
   const int tc = threadIdx.x % CG;
-  const int tx = threadIdx.x / CG;
-  const int x = col_t * TW + tx;
+  const int tx = threadIdx.x / CG;  // column group
+  const int x = col_t * TW + tx * CX;
   const int c = ch_t * kStreamChannels + tc * V;
   const bool c_ok = c < ch;
   const int y0 = strip * TH;
@@ -267,11 +277,13 @@ __global__ __launch_bounds__(256) void dwconv_stream(
     }
   };
 
-  float acc[K][V];
+  float acc[K][CX][V];
 #pragma unroll
   for (int i = 0; i < K; ++i)
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[i][j] = 0.f;
+    for (int cx = 0; cx < CX; ++cx)
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[i][cx][j] = 0.f;
   float psum[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) psum[j] = 0.f;
@@ -285,25 +297,28 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   const int x0 = col_t * TW;
   const int lx0 = max(x0 - R, 0);
   const int row_bytes = (min(gw, x0 + TW + R) - lx0) * ch * (int)sizeof(T);
-  int col_off[K];
+  int col_off[KL];
 #pragma unroll
-  for (int kx = 0; kx < K; ++kx) {
+  for (int kx = 0; kx < KL; ++kx) {
     const int xx = x + kx - R;
     col_off[kx] = (xx >= 0 && xx < gw && c_ok) ? ((xx - lx0) * ch + c) * (int)sizeof(T)
                                                : kOob;
   }
-  auto load_row = [&](Raw<T, V> (&rr)[K], int r) {
+  auto load_row = [&](Raw<T, V> (&rr)[KL], int r) {
     const bool in_grid = r >= 0 && r < gh;
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
         in + (img + (size_t)min(max(r, 0), gh - 1) * gw + lx0) * ch,
         in_grid ? row_bytes : 0);
 #pragma unroll
-    for (int kx = 0; kx < K; ++kx) rr[kx].load_buf(rs, col_off[kx]);
+    for (int kx = 0; kx < KL; ++kx) rr[kx].load_buf(rs, col_off[kx]);
   };
   const int out_bytes = (min(gw, x0 + TW) - x0) * ch * (int)sizeof(T);
-  const int st_off = (x < gw && c_ok) ? (tx * ch + c) * (int)sizeof(T) : kOob;
+  int st_off[CX];
+#pragma unroll
+  for (int cx = 0; cx < CX; ++cx)
+    st_off[cx] = (x + cx < gw && c_ok) ? ((tx * CX + cx) * ch + c) * (int)sizeof(T) : kOob;
 
-  Raw<T, V> rbuf[NB][K];
+  Raw<T, V> rbuf[NB][KL];
 #pragma unroll
   for (int q = 0; q < NB; ++q) load_row(rbuf[q], r_begin + q);
   // Rows are processed in groups of NB*K so that both the accumulator ring
@@ -314,12 +329,12 @@ __global__ __launch_bounds__(256) void dwconv_stream(
     for (int u = 0; u < NB * K; ++u) {
       const int r = r0 + u;
       if (r >= r_end) break;
-      Raw<T, V>(&cur)[K] = rbuf[u % NB];
+      Raw<T, V>(&cur)[KL] = rbuf[u % NB];
       // A halo row outside the grid contributes nothing: skip it (uniform).
       if (r >= 0 && r < gh) {
-        float xin[K][V];
+        float xin[KL][V];
 #pragma unroll
-        for (int kx = 0; kx < K; ++kx) cur[kx].cvt(xin[kx]);
+        for (int kx = 0; kx < KL; ++kx) cur[kx].cvt(xin[kx]);
         // input row r feeds output row r - R + i with vertical tap K - 1 - i
 #pragma unroll
         for (int i = 0; i < K; ++i) {
@@ -329,7 +344,10 @@ __global__ __launch_bounds__(256) void dwconv_stream(
             float t[V];
             tap(K - 1 - i, kx, t);
 #pragma unroll
-            for (int j = 0; j < V; ++j) acc[slot][j] = fmaf(t[j], xin[kx][j], acc[slot][j]);
+            for (int cx = 0; cx < CX; ++cx)
+#pragma unroll
+              for (int j = 0; j < V; ++j)
+                acc[slot][cx][j] = fmaf(t[j], xin[cx + kx][j], acc[slot][cx][j]);
           }
         }
       }
@@ -339,20 +357,26 @@ __global__ __launch_bounds__(256) void dwconv_stream(
       const int yo = r - R;
       const bool row_out = yo >= y0 && yo < y_end;  // uniform
       {
-        float v[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) v[j] = GELU ? gelu_erf(acc[done][j]) : acc[done][j];
         const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
             out + (img + (size_t)min(max(yo, 0), gh - 1) * gw + x0) * ch,
             row_out ? out_bytes : 0);
-        // streamed past the caches (measured: 124 -> 114 us on the folded
-        // 5x5, its readers no slower)
-        store_buf<T, V, kStoreStream>(rs, st_off, v);
-        if constexpr (POOL) {
-          round_to<T, V>(v);
-          const bool mine = row_out && st_off != kOob;
 #pragma unroll
-          for (int j = 0; j < V; ++j) psum[j] += mine ? v[j] : 0.f;
+        for (int cx = 0; cx < CX; ++cx) {
+          float v[V];
+#pragma unroll
+          for (int j = 0; j < V; ++j)
+            v[j] = GELU ? gelu_erf(acc[done][cx][j]) : acc[done][cx][j];
+          // streamed past the caches (measured: 124 -> 114 us on the folded
+          // 5x5, its readers no slower)
+          store_buf<T, V, kStoreStream>(rs, st_off[cx], v);
+          // lanes outside the grid add values that the block reduction never
+          // reads (it reads in-grid blocks only); rows outside the strip
+          // are skipped (uniform)
+          if (POOL && row_out) {
+            round_to<T, V>(v);
+#pragma unroll
+            for (int j = 0; j < V; ++j) psum[j] += v[j];
+          }
         }
       }
       if constexpr (POOL) {
@@ -367,12 +391,15 @@ __global__ __launch_bounds__(256) void dwconv_stream(
         }
       }
 #pragma unroll
-      for (int j = 0; j < V; ++j) acc[done][j] = 0.f;
+      for (int cx = 0; cx < CX; ++cx)
+#pragma unroll
+        for (int j = 0; j < V; ++j) acc[done][cx][j] = 0.f;
     }
   }
   if constexpr (POOL) {
     __syncthreads();
-    if (tx % block == 0 && x < gw && c_ok) {
+    // a thread's CX columns lie in one block (block is a multiple of CX)
+    if (x % block == 0 && x < gw && c_ok) {
       const int nbc = gw / block;
       for (int br = 0; br < (y_end - y0) / block; ++br) {
         const size_t t = (size_t)(y0 / block + br) * nbc + x / block;
@@ -380,7 +407,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
 #pragma unroll
         for (int j = 0; j < V; ++j) {
           float sm = 0.f;
-          for (int q = 0; q < block; ++q) sm += red[br][tx + q][tc * V + j];
+          for (int q = 0; q < block / CX; ++q) sm += red[br][tx + q][tc * V + j];
           dst[j] = sm;
         }
       }
@@ -600,23 +627,24 @@ __global__ __launch_bounds__(256) void dwconv_lds(
   }
 }
 
-// Per kernel size: channels per thread V, rows of loads in flight P and
-// channels per workgroup WC (the workgroup is 256 / (WC / V) columns wide).
-// Sizes up to 3 take the LDS-staged kernel, 5 and 7 the streaming one with
-// the taps in LDS and 4 channels per thread (measured on the folded 5x5:
-// 2 channels per thread with the taps in registers 128 us, 4 channels with
-// the taps in LDS 123 us with 2 rows in flight, more rows slower; the
-// LDS-staged kernel 137 us at best).
+// Per kernel size: channels per thread V, rows of loads in flight P,
+// channels per workgroup WC and output columns per thread CX (the
+// workgroup is 256 CX / (WC / V) columns wide).  Sizes up to 3 take the
+// LDS-staged kernel, 5 and 7 the streaming one with the taps in LDS (the
+// LDS-staged kernel measured 130-170 us on the folded 5x5 in every shape
+// tried, against the figures given with kStreamV).
 struct DwCfg {
   int v, p, wc;
   bool tl;  // streaming kernel: taps in LDS
+  int cx;   // streaming kernel: output columns per thread
 };
 constexpr DwCfg dw_cfg(int k, bool gelu) {
-  return k <= 3 ? DwCfg{4, 4, 64, false} : DwCfg{4, k == 5 ? 2 : 3, kStreamChannels, true};
+  return k <= 3 ? DwCfg{4, 4, 64, false, 1}
+                : DwCfg{kStreamV, kStreamRows, kStreamChannels, true, kStreamCols};
   (void)gelu;
 }
 constexpr int dw_width(int k, bool gelu) {
-  return 256 / (dw_cfg(k, gelu).wc / dw_cfg(k, gelu).v);
+  return 256 / (dw_cfg(k, gelu).wc / dw_cfg(k, gelu).v) * dw_cfg(k, gelu).cx;
 }
 
 template <typename T, int K, bool GELU>
@@ -632,11 +660,11 @@ hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
   const int per_xcd = (total + kXcds - 1) / kXcds;
   if constexpr (K >= 5) {
     if (bsum && !GELU)
-      dwconv_stream<T, K, false, cf.v, cf.p, true, cf.tl><<<per_xcd * kXcds, 256, 0, s>>>(
+      dwconv_stream<T, K, false, cf.v, cf.p, true, cf.tl, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
           gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
     else
-      dwconv_stream<T, K, GELU, cf.v, cf.p, false, cf.tl><<<per_xcd * kXcds, 256, 0, s>>>(
+      dwconv_stream<T, K, GELU, cf.v, cf.p, false, cf.tl, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
           gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
     return hipGetLastError();
@@ -678,7 +706,8 @@ hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
 
 bool dwconv_can_pool(int kmax, int block) {
   const int tw = dw_width(kmax, false);
-  return block >= kPoolMinBlock && tw % block == 0 && TH % block == 0;
+  return block >= kPoolMinBlock && tw % block == 0 && TH % block == 0 &&
+         block % dw_cfg(kmax, false).cx == 0;
 }
 
 bool dwconv_can_block_out(bool bf, int kmax, bool gelu, int batch, int gh, int gw,

@@ -223,16 +223,18 @@ __global__ __launch_bounds__(1024) void gate_scores_conv_kernel(
             head_scores ? head_scores + ((size_t)b * nblocks + t) * heads : nullptr);
 }
 
-// Workgroup-wide stream compaction (1024 threads, 16 waves): writes every
-// t in [0, n) with keep(t) to out[0 ..) in ascending order and returns the
-// number written (same value in every thread).  The slot of a kept t is the
-// number of kept entries below it: a wave ballot gives the rank inside the
-// wave, a prefix over the 16 wave totals the offset of the wave.
+// Workgroup-wide stream compaction (any multiple of 64 threads up to
+// 1024): writes every t in [0, n) with keep(t) to out[0 ..) in ascending
+// order and returns the number written (same value in every thread).  The
+// slot of a kept t is the number of kept entries below it: a wave ballot
+// gives the rank inside the wave, a prefix over the wave totals the offset
+// of the wave.
 template <typename Pred>
 __device__ int compact_ascending(Pred keep, int n, int32_t* __restrict__ out) {
   __shared__ int wave_tot[16];
   __shared__ int base_all;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
   if (threadIdx.x == 0) base_all = 0;
   __syncthreads();
   for (int t0 = 0; t0 < n; t0 += blockDim.x) {
@@ -248,7 +250,7 @@ __device__ int compact_ascending(Pred keep, int n, int32_t* __restrict__ out) {
     __syncthreads();
     if (threadIdx.x == 0) {
       int tot = 0;
-      for (int w2 = 0; w2 < 16; ++w2) tot += wave_tot[w2];
+      for (int w2 = 0; w2 < nwaves; ++w2) tot += wave_tot[w2];
       base_all += tot;
     }
     __syncthreads();
@@ -275,6 +277,41 @@ __device__ __forceinline__ uint64_t topk_key(float v, int t) {
   return (static_cast<uint64_t>(u) << 32) | (0xffffffffu - static_cast<uint32_t>(t));
 }
 
+// Top-k of one image by counting ranks (tpow <= blockDim keys): shk[0 ..
+// tpow) holds the keys (padding 0), rank[] has room for tpow ints.  rank(t)
+// = #{u : key_u > key_t}, the keys being distinct; the key range is split
+// into `parts` runs of at least 64 keys, one thread per (t, run), and the
+// runs' counts are added in LDS.  Every thread of a wave reads the same keys
+// (a broadcast).  T^2 comparisons, but no barrier between them.  The blocks
+// of rank below keep are written to sel in ascending order.
+__device__ void rank_select(const uint64_t* shk, int* rank, int nblocks, int tpow,
+                            int keep, int32_t* __restrict__ sel) {
+  const int parts = min((int)blockDim.x / tpow, max(1, tpow / 64));
+  const int t = threadIdx.x % tpow, q = threadIdx.x / tpow;
+  if (threadIdx.x < tpow) rank[threadIdx.x] = 0;
+  __syncthreads();
+  const int len = tpow / parts;
+  if (q < parts && t < nblocks) {
+    const uint64_t kt = shk[t];
+    const uint64_t* ku = shk + q * len;
+    int cnt = 0;
+    if (len % 16 == 0) {
+      for (int u = 0; u < len; u += 16) {
+        uint64_t v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = ku[u + i];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cnt += v[i] > kt;
+      }
+    } else {
+      for (int u = 0; u < len; ++u) cnt += ku[u] > kt;
+    }
+    atomicAdd(&rank[t], cnt);
+  }
+  __syncthreads();
+  compact_ascending([&](int u) { return rank[u] < keep; }, nblocks, sel);
+}
+
 __global__ __launch_bounds__(1024) void topk_kernel(
     const float* __restrict__ scores, float* __restrict__ scores_copy,
     int32_t* __restrict__ sel, int nblocks, int keep, int tpow) {
@@ -293,37 +330,8 @@ __global__ __launch_bounds__(1024) void topk_kernel(
   }
   __syncthreads();
   if (tpow <= (int)blockDim.x) {
-    // Up to one key per thread: rank by counting.  rank(t) = #{u : key_u >
-    // key_t}, the keys being distinct; the key range is split into `parts`
-    // runs of at least 64 keys, one thread per (t, run), and the runs'
-    // counts are added in LDS.  Every thread of a wave reads the same keys
-    // (a broadcast).  T^2 comparisons, but no barrier between them.
     __shared__ int rank[1024];
-    const int parts = min((int)blockDim.x / tpow, max(1, tpow / 64));
-    const int t = threadIdx.x % tpow, q = threadIdx.x / tpow;
-    if (threadIdx.x < tpow) rank[threadIdx.x] = 0;
-    __syncthreads();
-    const int len = tpow / parts;
-    if (q < parts && t < nblocks) {
-      const uint64_t kt = shk[t];
-      const uint64_t* ku = shk + q * len;
-      int cnt = 0;
-      if (len % 16 == 0) {
-        for (int u = 0; u < len; u += 16) {
-          uint64_t v[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) v[i] = ku[u + i];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) cnt += v[i] > kt;
-        }
-      } else {
-        for (int u = 0; u < len; ++u) cnt += ku[u] > kt;
-      }
-      atomicAdd(&rank[t], cnt);
-    }
-    __syncthreads();
-    compact_ascending([&](int u) { return rank[u] < keep; }, nblocks,
-                      sel + (size_t)b * keep);
+    rank_select(shk, rank, nblocks, tpow, keep, sel + (size_t)b * keep);
     return;
   }
   for (int size = 2; size <= tpow; size <<= 1) {
