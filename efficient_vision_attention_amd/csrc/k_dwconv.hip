@@ -23,23 +23,30 @@ namespace {
 // GELU(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)) with erf from
 // Abramowitz & Stegun 7.1.28:
 //   erf(z) = 1 - (1 + a1 z + a2 z^2 + ... + a6 z^6)^-16,  z >= 0,
-//   |error| <= 3e-7 (about 2e-6 evaluated in float32),
-// extended to z < 0 by oddness.  One reciprocal and four squarings: no
-// exponential, so one transcendental per element instead of two.  Far
-// below the bfloat16 output precision.
+//   |error| <= 3e-7,
+// extended to z < 0 by oddness.  Written as
+//   GELU(x) = max(x, 0) - |x| erfc(|x| / sqrt 2) / 2
+//           = max(x, 0) - |x| / P(|x|)^16,
+// with P's coefficients c_i = a_i 2^(-i/2) 2^(1/16) (c_0 = 2^(1/16)), so
+// that P(|x|)^16 = 2 (1 + a1 z + ... + a6 z^6)^16: six FMAs in |x|, four
+// squarings, one reciprocal, a max and an FMA.  No cancellation for x < 0
+// (the result is the small term itself); measured against float64 erf on
+// [-8, 8]: absolute error <= 7e-7, far below the bfloat16 output
+// precision.  (Infinite x gives NaN; the inputs are sums of finite
+// products.)
 __device__ __forceinline__ float gelu_erf(float x) {
-  constexpr float a1 = 0.0705230784f, a2 = 0.0422820123f, a3 = 0.0092705272f,
-                  a4 = 0.0001520143f, a5 = 0.0002765672f, a6 = 0.0000430638f;
-  const float z = fabsf(x) * 0.70710678118654752f;
-  float p = fmaf(fmaf(fmaf(fmaf(fmaf(a6, z, a5), z, a4), z, a3), z, a2), z, a1);
-  p = fmaf(p, z, 1.f);
+  constexpr float c0 = 1.0442737824e+00f, c1 = 5.2075163037e-02f,
+                  c2 = 2.2076998457e-02f, c3 = 3.4227392389e-03f,
+                  c4 = 3.9686137011e-05f, c5 = 5.1055209009e-05f,
+                  c6 = 5.6212996640e-06f;
+  const float ax = fabsf(x);
+  float p = fmaf(fmaf(fmaf(fmaf(fmaf(fmaf(c6, ax, c5), ax, c4), ax, c3), ax, c2), ax, c1),
+                 ax, c0);
   p *= p;
   p *= p;
   p *= p;
   p *= p;
-  const float erf_abs = 1.f - __builtin_amdgcn_rcpf(p);
-  const float hx = 0.5f * x;
-  return fmaf(hx, copysignf(erf_abs, x), hx);
+  return fmaf(-ax, __builtin_amdgcn_rcpf(p), fmaxf(x, 0.f));
 }
 
 constexpr int TH = 32;   // output rows per workgroup strip
@@ -188,6 +195,8 @@ constexpr int kStreamChannels = 64;  // channels per workgroup
 // channels 97, 4 columns of 2 channels 93 (139), 8 columns about the same
 // as 4 but no longer dividing 4 x 4 gate blocks.
 constexpr int kStreamV = 2, kStreamCols = 4, kStreamRows = 2;
+// LDS-staged kernel (up to 3x3): output columns per thread.
+constexpr int kLdsCols = 2;
 
 // Register-streaming variant (the wider kernels, whose taps take most of the
 // registers).  A thread owns CX adjacent output columns x .. x + CX - 1 and
@@ -421,14 +430,16 @@ __global__ __launch_bounds__(256) void dwconv_stream(
 // keeps P rows of those loads in flight in registers.  Rows pass through
 // two LDS slots; one barrier per row orders "row r written" before "row r
 // read" and "row r - 1 read" before "slot reused".  Each thread then reads
-// its K horizontal neighbours from LDS instead of from L1, and accumulates
-// as above (K partial output rows in registers).  Compared with the
+// the K + CX - 1 horizontal neighbours of its CX columns from LDS instead
+// of from L1, and accumulates as above (K partial output rows in
+// registers).  Compared with the
 // register-only kernel the bytes in flight per workgroup no longer scale
 // with the per-thread tap registers.
 // BO: out is written tile-blocked for the GEMM (token m of the launch,
 // channel k at ((m / 256) * (ch / 32) + k / 32) * 8192 + (m % 256) * 32 +
 // k % 32); out_bytes_all is then the whole output's size in bytes.
-template <typename T, int K, bool GELU, int V, int P, bool POOL, int WC, bool BO>
+template <typename T, int K, bool GELU, int V, int P, bool POOL, int WC, bool BO,
+          int CX = 1>
 __global__ __launch_bounds__(256) void dwconv_lds(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, float* __restrict__ bsum, int block,
@@ -436,7 +447,9 @@ __global__ __launch_bounds__(256) void dwconv_lds(
     int total, int per_xcd, int out_bytes_all) {
   constexpr int R = (K - 1) / 2;
   constexpr int CG = WC / V;  // channel groups per workgroup
-  constexpr int TW = 256 / CG;         // columns per workgroup
+  constexpr int TT = 256 / CG;         // column groups per workgroup
+  constexpr int TW = TT * CX;          // columns per workgroup
+  constexpr int KL = K + CX - 1;       // input columns per thread
   constexpr int LC = TW + 2 * R;       // columns per staged row
   constexpr int EPC = 16 / (int)sizeof(T);       // elements per 16-byte chunk
   constexpr int CPC = WC / EPC;         // chunks per column
@@ -447,7 +460,7 @@ __global__ __launch_bounds__(256) void dwconv_lds(
   // group of rows after which every register index repeats
   constexpr int G = (K % P == 0) ? K : (P % K == 0 ? P : K * P);
   __shared__ __attribute__((aligned(16))) char ring[2 * SLOT];
-  __shared__ float red[POOL ? TH / kPoolMinBlock : 1][POOL ? TW : 1][POOL ? WC : 1];
+  __shared__ float red[POOL ? TH / kPoolMinBlock : 1][POOL ? TT : 1][POOL ? WC : 1];
   const int bid = blockIdx.x;
   const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
   if (tile >= total) return;
@@ -463,7 +476,7 @@ __global__ __launch_bounds__(256) void dwconv_lds(
   const int tc = tid % CG;
   const int tx = tid / CG;
   const int x0 = col_t * TW;
-  const int x = x0 + tx;
+  const int x = x0 + tx * CX;
   const int c0 = ch_t * WC;
   const int c = c0 + tc * V;
   const bool c_ok = c < ch;
@@ -514,13 +527,18 @@ __global__ __launch_bounds__(256) void dwconv_lds(
   // output: this thread's byte offset within its output row segment
   const int ox1 = min(gw, x0 + TW);
   const int out_bytes = (ox1 - x0) * ch * (int)sizeof(T);
-  const int st_off = (x < gw && c_ok) ? (tx * ch + c) * (int)sizeof(T) : kOob;
+  int st_off[CX];
+#pragma unroll
+  for (int cx = 0; cx < CX; ++cx)
+    st_off[cx] = (x + cx < gw && c_ok) ? ((tx * CX + cx) * ch + c) * (int)sizeof(T) : kOob;
 
-  float acc[K][V];
+  float acc[K][CX][V];
 #pragma unroll
   for (int i = 0; i < K; ++i)
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[i][j] = 0.f;
+    for (int cx = 0; cx < CX; ++cx)
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[i][cx][j] = 0.f;
   float psum[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) psum[j] = 0.f;
@@ -534,7 +552,7 @@ __global__ __launch_bounds__(256) void dwconv_lds(
   for (int q = 0; q < P; ++q) load_row(pre[q], r_begin + q);
   store_row(pre[0], 0);
   load_row(pre[0], r_begin + P);
-  const char* my = ring + tx * CB + tc * V * (int)sizeof(T);
+  const char* my = ring + tx * CX * CB + tc * V * (int)sizeof(T);
   for (int u0 = 0; u0 < nrows; u0 += G) {
 #pragma unroll
     for (int v = 0; v < G; ++v) {
@@ -543,9 +561,9 @@ __global__ __launch_bounds__(256) void dwconv_lds(
       const int r = r_begin + u;
       __syncthreads();
       if (r >= 0 && r < gh) {
-        float xin[K][V];
+        float xin[KL][V];
 #pragma unroll
-        for (int kx = 0; kx < K; ++kx) {
+        for (int kx = 0; kx < KL; ++kx) {
           Raw<T, V> rr;
           rr.load(reinterpret_cast<const T*>(my + (u & 1) * SLOT + kx * CB));
           rr.cvt(xin[kx]);
@@ -557,8 +575,10 @@ __global__ __launch_bounds__(256) void dwconv_lds(
 #pragma unroll
           for (int kx = 0; kx < K; ++kx)
 #pragma unroll
-            for (int j = 0; j < V; ++j)
-              acc[slot][j] = fmaf(w[K - 1 - i][kx][j], xin[kx][j], acc[slot][j]);
+            for (int cx = 0; cx < CX; ++cx)
+#pragma unroll
+              for (int j = 0; j < V; ++j)
+                acc[slot][cx][j] = fmaf(w[K - 1 - i][kx][j], xin[cx + kx][j], acc[slot][cx][j]);
         }
       }
       // stage row r + 1 (its loads were issued P - 1 rows ago) and issue
@@ -568,14 +588,16 @@ __global__ __launch_bounds__(256) void dwconv_lds(
       const int done = (v - R + G) % K;  // slot of output row r - R
       const int yo = r - R;
       const bool row_out = yo >= y0 && yo < y_end;  // uniform
-      {
+#pragma unroll
+      for (int cx = 0; cx < CX; ++cx) {
         float o[V];
 #pragma unroll
-        for (int j = 0; j < V; ++j) o[j] = GELU ? gelu_erf(acc[done][j]) : acc[done][j];
+        for (int j = 0; j < V; ++j)
+          o[j] = GELU ? gelu_erf(acc[done][cx][j]) : acc[done][cx][j];
         if constexpr (BO) {
-          const int m = (b * gh + yo) * gw + x;
+          const int m = (b * gh + yo) * gw + x + cx;
           const int off =
-              (row_out && x < gw && c_ok)
+              (row_out && x + cx < gw && c_ok)
                   ? (((m / kGemmTileM) * (ch / kGemmTileK) + c / kGemmTileK) *
                          (kGemmTileM * kGemmTileK) +
                      (m % kGemmTileM) * kGemmTileK + c % kGemmTileK) *
@@ -586,13 +608,14 @@ __global__ __launch_bounds__(256) void dwconv_lds(
           const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
               out + (img + (size_t)min(max(yo, 0), gh - 1) * gw + x0) * ch,
               row_out ? out_bytes : 0);
-          store_buf<T, V>(rs, st_off, o);
+          store_buf<T, V>(rs, st_off[cx], o);
         }
-        if constexpr (POOL) {
+        // lanes outside the grid add values that the block reduction never
+        // reads; rows outside the strip are skipped (uniform)
+        if (POOL && row_out) {
           round_to<T, V>(o);
-          const bool mine = row_out && st_off != kOob;
 #pragma unroll
-          for (int j = 0; j < V; ++j) psum[j] += mine ? o[j] : 0.f;
+          for (int j = 0; j < V; ++j) psum[j] += o[j];
         }
       }
       if constexpr (POOL) {
@@ -606,12 +629,15 @@ __global__ __launch_bounds__(256) void dwconv_lds(
         }
       }
 #pragma unroll
-      for (int j = 0; j < V; ++j) acc[done][j] = 0.f;
+      for (int cx = 0; cx < CX; ++cx)
+#pragma unroll
+        for (int j = 0; j < V; ++j) acc[done][cx][j] = 0.f;
     }
   }
   if constexpr (POOL) {
     __syncthreads();
-    if (tx % block == 0 && x < gw && c_ok) {
+    // a thread's CX columns lie in one block (block is a multiple of CX)
+    if (x % block == 0 && x < gw && c_ok) {
       const int nbc = gw / block;
       for (int br = 0; br < (y_end - y0) / block; ++br) {
         const size_t t = (size_t)(y0 / block + br) * nbc + x / block;
@@ -619,7 +645,7 @@ __global__ __launch_bounds__(256) void dwconv_lds(
 #pragma unroll
         for (int j = 0; j < V; ++j) {
           float sm = 0.f;
-          for (int q = 0; q < block; ++q) sm += red[br][tx + q][tc * V + j];
+          for (int q = 0; q < block / CX; ++q) sm += red[br][tx + q][tc * V + j];
           dst[j] = sm;
         }
       }
@@ -639,7 +665,7 @@ struct DwCfg {
   int cx;   // streaming kernel: output columns per thread
 };
 constexpr DwCfg dw_cfg(int k, bool gelu) {
-  return k <= 3 ? DwCfg{4, 4, 64, false, 1}
+  return k <= 3 ? DwCfg{4, 4, 64, false, kLdsCols}
                 : DwCfg{kStreamV, kStreamRows, kStreamChannels, true, kStreamCols};
   (void)gelu;
 }
@@ -671,19 +697,19 @@ hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
   }
   if constexpr (!GELU) {
     if (bsum) {
-      dwconv_lds<T, K, false, cf.v, cf.p, true, cf.wc, false><<<per_xcd * kXcds, 256, 0, s>>>(
+      dwconv_lds<T, K, false, cf.v, cf.p, true, cf.wc, false, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
           gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0);
       return hipGetLastError();
     }
   }
   if (out_blocked)
-    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, true><<<per_xcd * kXcds, 256, 0, s>>>(
+    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, true, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
         static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
         gw, ch, col_tiles, ch_tiles, strips, total, per_xcd,
         (int)((size_t)batch * gh * gw * ch * sizeof(T)));
   else
-    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, false><<<per_xcd * kXcds, 256, 0, s>>>(
+    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, false, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
         static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
         gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0);
   return hipGetLastError();
