@@ -108,6 +108,31 @@ def test_block_forward(keep):
     assert_close(g["out"], _oracle_ffn(g["x1"], inp, wl), wl.dtype, "out")
 
 
+def test_block_forward_layernorm_params():
+    """LayerNorm scale and shift away from 1 and 0 in both norms (the
+    synthetic block has 1 and 0): the per-channel gamma and beta reach the
+    tile-blocked outputs that feed the projections."""
+    wl = STAGE_CASES["block_small"]
+    inp = dict(make_inputs(wl))
+    rng = np.random.default_rng(7)
+    C = wl.channels
+    for k in ("ln1", "ln2"):
+        inp[k + "_g"] = rng.uniform(0.5, 1.5, C)
+        inp[k + "_b"] = rng.normal(0.0, 0.3, C)
+    g = Run(wl, inp).block_forward()
+    kw = oracle_kwargs(wl)
+    ref = O.hsmla_block_forward(inp["x"], inp, staged=True, **kw)
+    kk = kw["keep_blocks"]
+    if not np.array_equal(g["sel"][:, :kk], ref["sel"]):
+        selection_band_check(ref["scores"], g["scores"], ref["sel"],
+                             g["sel"][:, :kk], kk)
+        ref = O.hsmla_block_forward(inp["x"], inp, staged=True,
+                                    sel=g["sel"][:, :kk], **kw)
+    for key in ("qkv", "qkv_hat", "x1"):
+        assert_close(g[key], ref[key], wl.dtype, key)
+    assert_close(g["out"], _oracle_ffn(g["x1"], inp, wl), wl.dtype, "out")
+
+
 def _oracle_ffn(x1, inp, wl):
     r = O.round_bf16
     xn2 = r(O.layer_norm(x1, inp["ln2_g"], inp["ln2_b"]))
