@@ -119,7 +119,7 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
 //   weights fit the GEMM tile (bf16; see blocked_weights).
 struct Layout {
   size_t qkv, qkv_hat, o, kv, ksum, part, taps, scores, sel, counts, head_scores;
-  size_t bsum;
+  size_t bsum, rankp;
   size_t xn, x1, h1, h2, ffn_taps;
   size_t wq, wo, w1, w2;  // 0 when not made
   size_t total;
@@ -162,6 +162,7 @@ Layout layout(const Dims& D, int op) {
     if (D.thr) L.counts = take((size_t)D.nc * 4);
     if (D.ph) L.head_scores = take((size_t)D.B * D.T * D.H * 4);
     L.bsum = take((size_t)D.B * D.T * 3 * D.C * 4);
+    L.rankp = take((size_t)D.B * hsmla::topk_parts_bytes(D.T));
     if (op == HSMLA_OP_BLOCK) {
       L.xn = take(D.P * D.C * D.e);
       L.x1 = take(D.P * D.C * D.e);
@@ -263,6 +264,7 @@ struct Bufs {
   void *qkv, *qkvh, *o, *xn, *x1, *h1, *h2;
   float *kv, *ksum, *part, *taps, *ftaps, *scores, *hscores, *bsum;
   int32_t *sel, *counts;
+  int32_t* rankp;           // top-k partial ranks
   void *wq, *wo, *w1, *w2;  // tile-blocked weights (shared), or null
 };
 
@@ -287,6 +289,9 @@ Bufs bufs_for(const Dims& D, const Layout& L, void* ws, int op, int b0) {
   u.hscores = D.ph ? reinterpret_cast<float*>(at(ws, L.head_scores)) + bb * T * H
                    : nullptr;
   u.bsum = reinterpret_cast<float*>(at(ws, L.bsum)) + bb * T * 3 * c;
+  u.rankp = hsmla::topk_parts_bytes(D.T)
+                ? reinterpret_cast<int32_t*>(at(ws, L.rankp + bb * hsmla::topk_parts_bytes(D.T)))
+                : nullptr;
   if (op == HSMLA_OP_BLOCK) {
     u.xn = at(ws, L.xn + bb * n * c * e);
     u.x1 = at(ws, L.x1 + bb * n * c * e);
@@ -421,7 +426,7 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
                                           D.T, D.tau, s));
       } else {
         r.mark("topk");
-        HSMLA_TRY(hsmla::launch_topk(u.scores, nullptr, u.sel, D.B, D.T, D.k, s));
+        HSMLA_TRY(hsmla::launch_topk(u.scores, nullptr, u.sel, D.B, D.T, D.k, s, u.rankp));
       }
       return HSMLA_OK;
     case 6:

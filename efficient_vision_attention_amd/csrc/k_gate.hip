@@ -367,6 +367,53 @@ __global__ __launch_bounds__(1024) void topk_kernel(
                     sel + (size_t)b * keep);
 }
 
+// The same ranks over more CUs (up to 1024 blocks): grid (kRankParts,
+// batch), tpow threads.  Workgroup s counts, for every block t of its
+// image, the keys of run s (tpow / kRankParts keys) above key_t and writes
+// part[b][s][t]; rank_final_kernel adds the runs and compacts.  The counts
+// are exact integers, so the ranks equal rank_select's.
+constexpr int kRankParts = 8;
+__global__ __launch_bounds__(1024) void rank_part_kernel(const float* __restrict__ scores,
+                                                         int32_t* __restrict__ part,
+                                                         int nblocks, int tpow) {
+  __shared__ uint64_t keys[1024 / kRankParts];
+  const int s = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int len = tpow / kRankParts;
+  const float* src = scores + (size_t)b * nblocks;
+  for (int i = t; i < len; i += blockDim.x) {
+    const int u = s * len + i;
+    keys[i] = u < nblocks ? topk_key(src[u], u) : 0;
+  }
+  const uint64_t kt = t < nblocks ? topk_key(src[t], t) : ~0ull;
+  __syncthreads();
+  int cnt = 0;
+  for (int i = 0; i < len; i += 16) {  // len is a multiple of 16
+    uint64_t v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = keys[i + q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) cnt += v[q] > kt;
+  }
+  if (t < nblocks) part[((size_t)b * kRankParts + s) * tpow + t] = cnt;
+}
+
+// grid (batch), 1024 threads: rank(t) = sum of the runs' counts, then the
+// blocks of rank below keep in ascending order.
+__global__ __launch_bounds__(1024) void rank_final_kernel(const int32_t* __restrict__ part,
+                                                          int32_t* __restrict__ sel,
+                                                          int nblocks, int keep, int tpow) {
+  __shared__ int rank[1024];
+  const int b = blockIdx.x;
+  for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
+    int r = 0;
+#pragma unroll
+    for (int q = 0; q < kRankParts; ++q) r += part[((size_t)b * kRankParts + q) * tpow + t];
+    rank[t] = r;
+  }
+  __syncthreads();
+  compact_ascending([&](int u) { return rank[u] < keep; }, nblocks, sel + (size_t)b * keep);
+}
+
 // grid (batch), 1024 threads: sel[b][0 .. n) = ascending blocks with
 // M_t > tau, counts[b] = n.  Float32 comparison, so a score equal to tau is
 // not routed.
@@ -451,11 +498,23 @@ hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
   return hipGetLastError();
 }
 
+size_t topk_parts_bytes(int nblocks) {
+  int tpow = 2;
+  while (tpow < nblocks) tpow <<= 1;
+  return tpow <= 1024 ? (size_t)kRankParts * tpow * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
-                       int batch, int nblocks, int keep, hipStream_t s) {
+                       int batch, int nblocks, int keep, hipStream_t s,
+                       int32_t* parts) {
   if (keep == 0 && scores_copy == nullptr) return hipSuccess;
   int tpow = 2;
   while (tpow < nblocks) tpow <<= 1;
+  if (parts && !scores_copy && tpow >= 16 * kRankParts && tpow <= 1024) {
+    rank_part_kernel<<<dim3(kRankParts, batch), tpow, 0, s>>>(scores, parts, nblocks, tpow);
+    rank_final_kernel<<<batch, 1024, 0, s>>>(parts, sel, nblocks, keep, tpow);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)tpow * sizeof(uint64_t);  // <= 64 KB for T <= 8192
   topk_kernel<<<batch, 1024, lds, s>>>(scores, scores_copy, sel, nblocks, keep,
                                        tpow);

@@ -95,8 +95,13 @@ hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
                               const void* gate_dw, float* scores,
                               float* head_scores, int batch, int gh, int gw,
                               int heads, int block, hipStream_t s);
+// parts (optional, batch * topk_parts_bytes(nblocks) bytes; ignored with
+// scores_copy): scratch that lets 128 .. 1024 blocks per image be ranked
+// over several workgroups per image (two launches).
+size_t topk_parts_bytes(int nblocks);
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
-                       int batch, int nblocks, int keep, hipStream_t s);
+                       int batch, int nblocks, int keep, hipStream_t s,
+                       int32_t* parts = nullptr);
 // Threshold routing: sel[b][0 .. counts[b]) = ascending blocks with score >
 // tau; sel rows are nblocks wide.
 hipError_t launch_threshold(const float* scores, float* scores_copy,
