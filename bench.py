@@ -137,6 +137,10 @@ def algorithmic_work(name, wl, sel):
         return 3 * C * e * P, (18 if wl.gate_conv else 1) * 3 * C * P
     if name in ("topk", "threshold"):
         return wl.batch * wl.num_blocks * 8, 0
+    if name == "gate_topk":
+        # the gate's partial logits (3 per head and block, formed by the S2
+        # conv) in, scores and the selection out
+        return wl.batch * wl.num_blocks * (3 * H * 4 + 8), 0
     if name == "sparse_softmax":
         W = window_keys(sel, wl.grid_h, wl.grid_w, Bs, wl.window)
         q = Bs * Bs

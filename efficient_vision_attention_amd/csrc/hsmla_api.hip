@@ -380,6 +380,10 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
   // workgroup shape allows; the gate then only forms the logits
   float* bsum = (!w->gate_dw && hsmla::dwconv_can_pool(D.kmax, D.Bs)) ? u.bsum
                                                                        : nullptr;
+  // with top-k routing the conv reduces the sums further, into the gate's
+  // partial logits, and the top-k launch forms the scores (no gate launch)
+  const bool gate_parts = bsum && !D.soft && !D.thr && u.rankp &&
+                          hsmla::gate_topk_from_parts_ok(D.T);
   switch (st) {
     case 0: {
       r.mark("qkv_gemm");
@@ -391,7 +395,8 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
     case 1:
       r.mark("dwconv_qkv");
       HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.qkv, u.qkvh, u.taps, D.kmax, D.B, D.gh,
-                                     D.gw, 3 * D.C, false, bsum, D.Bs, s));
+                                     D.gw, 3 * D.C, false, bsum, D.Bs, s, false,
+                                     gate_parts ? w->gate_w : nullptr, D.H));
       return HSMLA_OK;
     case 2:
       r.mark("kv_state");
@@ -404,6 +409,7 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
                                         D.N, D.H, s));
       return HSMLA_OK;
     case 4:
+      if (gate_parts) return HSMLA_OK;  // scores formed with the selection
       r.mark("gate_scores");
       if (bsum)
         HSMLA_TRY(hsmla::launch_gate_from_sums(bsum, w->gate_w, w->gate_b,
@@ -424,6 +430,10 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
         r.mark("threshold");
         HSMLA_TRY(hsmla::launch_threshold(u.scores, nullptr, u.sel, u.counts, D.B,
                                           D.T, D.tau, s));
+      } else if (gate_parts) {
+        r.mark("gate_topk");
+        HSMLA_TRY(hsmla::launch_gate_topk_parts(bsum, w->gate_b, u.scores, u.sel, u.rankp,
+                                                D.B, D.T, D.H, D.Bs, D.k, s));
       } else {
         r.mark("topk");
         HSMLA_TRY(hsmla::launch_topk(u.scores, nullptr, u.sel, D.B, D.T, D.k, s, u.rankp));

@@ -188,6 +188,77 @@ __device__ __forceinline__ void round_to(float* v) {
   }
 }
 
+// Sum over aligned groups of N (8 or 16) lanes by DPP moves (neighbour
+// swap, pair swap, mirror in 8, mirror in 16); every lane of a group ends
+// with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float sum_lanes(float v) {
+  static_assert(N == 8 || N == 16, "8 or 16 lanes");
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  if constexpr (N == 16) v += dpp_mov<0x140>(v);  // row_mirror
+  return v;
+}
+
+// End of a strip with POOL (after the barrier): the block sums parked in
+// red[block row][column group][channel] leave the workgroup either whole,
+// bsum[b][t][c] (gate_w == nullptr), or already reduced into the gate's
+// partial logits of each 32-channel head slice (channel c = s C + 32 h + j,
+// C = 32 heads):
+//   plog[b][t][s][h] = sum_j gate_w[h][32 s + j] * blocksum(s C + 32 h + j),
+// summed over the 32 / V lanes that hold the slice (one aligned DPP group,
+// fixed order), written to bsum's memory.  A thread's CX columns lie in one
+// block (block is a multiple of CX).
+template <int V, int CX, int TT, int WC>
+__device__ __forceinline__ void pool_store(const float (&red)[TH / kPoolMinBlock][TT][WC],
+                                           float* bsum, const float* gate_w, int heads,
+                                           int block, int b, int gh, int gw, int ch, int x,
+                                           int tx, int tc, int c, bool c_ok, int y0,
+                                           int y_end) {
+  const int nbc = gw / block, T = (gh / block) * nbc;
+  if (x % block != 0 || x >= gw) return;  // uniform over each lane group
+  if (!gate_w) {
+    if (!c_ok) return;
+    for (int br = 0; br < (y_end - y0) / block; ++br) {
+      const size_t t = (size_t)(y0 / block + br) * nbc + x / block;
+      float* dst = bsum + ((size_t)b * T + t) * ch + c;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        float sm = 0.f;
+        for (int q = 0; q < block / CX; ++q) sm += red[br][tx + q][tc * V + j];
+        dst[j] = sm;
+      }
+    }
+    return;
+  }
+  static_assert(32 % V == 0 && WC % 32 == 0, "head slices of 32 channels");
+  constexpr int L = 32 / V;  // lanes per head slice
+  const int C = 32 * heads;
+  const int sc = c / C, h = (c % C) / 32;
+  float gwt[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) gwt[j] = c_ok ? gate_w[h * 96 + sc * 32 + (c % 32) + j] : 0.f;
+  for (int br = 0; br < (y_end - y0) / block; ++br) {
+    float p = 0.f;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      float sm = 0.f;
+      for (int q = 0; q < block / CX; ++q) sm += red[br][tx + q][tc * V + j];
+      p = fmaf(gwt[j], sm, p);
+    }
+    p = sum_lanes<L>(p);
+    if (tc % L == 0 && c_ok) {
+      const size_t t = (size_t)(y0 / block + br) * nbc + x / block;
+      bsum[(((size_t)b * T + t) * 3 + sc) * heads + h] = p;
+    }
+  }
+}
+
 constexpr int kStreamChannels = 64;  // channels per workgroup
 // Streaming kernel (5x5, 7x7): channels and output columns per thread, rows
 // of loads in flight.  Measured on the folded 5x5 (7x7) with gate sums:
@@ -223,7 +294,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, float* __restrict__ bsum, int block,
     int gh, int gw, int ch, int col_tiles, int ch_tiles, int strips,
-    int total, int per_xcd) {
+    int total, int per_xcd, const float* __restrict__ gate_w, int heads) {
   constexpr int R = (K - 1) / 2;
   constexpr int CG = kStreamChannels / V;  // channel groups per workgroup
   constexpr int TT = 256 / CG;             // column groups per workgroup
@@ -407,20 +478,8 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   }
   if constexpr (POOL) {
     __syncthreads();
-    // a thread's CX columns lie in one block (block is a multiple of CX)
-    if (x % block == 0 && x < gw && c_ok) {
-      const int nbc = gw / block;
-      for (int br = 0; br < (y_end - y0) / block; ++br) {
-        const size_t t = (size_t)(y0 / block + br) * nbc + x / block;
-        float* dst = bsum + ((size_t)b * (gh / block) * nbc + t) * ch + c;
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          float sm = 0.f;
-          for (int q = 0; q < block / CX; ++q) sm += red[br][tx + q][tc * V + j];
-          dst[j] = sm;
-        }
-      }
-    }
+    pool_store<V, CX, TT, kStreamChannels>(red, bsum, gate_w, heads, block, b, gh, gw, ch, x,
+                                           tx, tc, c, c_ok, y0, y_end);
   }
 }
 
@@ -444,7 +503,8 @@ __global__ __launch_bounds__(256) void dwconv_lds(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, float* __restrict__ bsum, int block,
     int gh, int gw, int ch, int col_tiles, int ch_tiles, int strips,
-    int total, int per_xcd, int out_bytes_all) {
+    int total, int per_xcd, int out_bytes_all, const float* __restrict__ gate_w,
+    int heads) {
   constexpr int R = (K - 1) / 2;
   constexpr int CG = WC / V;  // channel groups per workgroup
   constexpr int TT = 256 / CG;         // column groups per workgroup
@@ -636,20 +696,8 @@ __global__ __launch_bounds__(256) void dwconv_lds(
   }
   if constexpr (POOL) {
     __syncthreads();
-    // a thread's CX columns lie in one block (block is a multiple of CX)
-    if (x % block == 0 && x < gw && c_ok) {
-      const int nbc = gw / block;
-      for (int br = 0; br < (y_end - y0) / block; ++br) {
-        const size_t t = (size_t)(y0 / block + br) * nbc + x / block;
-        float* dst = bsum + ((size_t)b * (gh / block) * nbc + t) * ch + c;
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          float sm = 0.f;
-          for (int q = 0; q < block / CX; ++q) sm += red[br][tx + q][tc * V + j];
-          dst[j] = sm;
-        }
-      }
-    }
+    pool_store<V, CX, TT, WC>(red, bsum, gate_w, heads, block, b, gh, gw, ch, x, tx, tc, c,
+                              c_ok, y0, y_end);
   }
 }
 
@@ -676,7 +724,7 @@ constexpr int dw_width(int k, bool gelu) {
 template <typename T, int K, bool GELU>
 hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
                   int block, int batch, int gh, int gw, int ch, bool out_blocked,
-                  hipStream_t s) {
+                  hipStream_t s, const float* gate_w, int heads) {
   constexpr DwCfg cf = dw_cfg(K, GELU);
   constexpr int TW = dw_width(K, GELU);
   const int col_tiles = (gw + TW - 1) / TW;
@@ -688,18 +736,18 @@ hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
     if (bsum && !GELU)
       dwconv_stream<T, K, false, cf.v, cf.p, true, cf.tl, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
-          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
+          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, gate_w, heads);
     else
       dwconv_stream<T, K, GELU, cf.v, cf.p, false, cf.tl, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
-          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd);
+          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, nullptr, 0);
     return hipGetLastError();
   }
   if constexpr (!GELU) {
     if (bsum) {
       dwconv_lds<T, K, false, cf.v, cf.p, true, cf.wc, false, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
-          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0);
+          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0, gate_w, heads);
       return hipGetLastError();
     }
   }
@@ -707,23 +755,23 @@ hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
     dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, true, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
         static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
         gw, ch, col_tiles, ch_tiles, strips, total, per_xcd,
-        (int)((size_t)batch * gh * gw * ch * sizeof(T)));
+        (int)((size_t)batch * gh * gw * ch * sizeof(T)), nullptr, 0);
   else
     dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, false, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
         static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
-        gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0);
+        gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0, nullptr, 0);
   return hipGetLastError();
 }
 
 template <typename T, bool GELU>
 hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
                       float* bsum, int block, int batch, int gh, int gw, int ch,
-                      bool out_blocked, hipStream_t s) {
+                      bool out_blocked, hipStream_t s, const float* gate_w, int heads) {
   switch (kmax) {
-    case 1: return run_dw<T, 1, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s);
-    case 3: return run_dw<T, 3, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s);
-    case 5: return run_dw<T, 5, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s);
-    case 7: return run_dw<T, 7, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s);
+    case 1: return run_dw<T, 1, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s, gate_w, heads);
+    case 3: return run_dw<T, 3, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s, gate_w, heads);
+    case 5: return run_dw<T, 5, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s, gate_w, heads);
+    case 7: return run_dw<T, 7, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked, s, gate_w, heads);
     default: return hipErrorInvalidValue;
   }
 }
@@ -746,19 +794,20 @@ bool dwconv_can_block_out(bool bf, int kmax, bool gelu, int batch, int gh, int g
 hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
                          int kmax, int batch, int gh, int gw, int ch,
                          bool gelu, float* bsum, int block, hipStream_t s,
-                         bool out_blocked) {
+                         bool out_blocked, const float* gate_w, int heads) {
   if (bsum && (gelu || !dwconv_can_pool(kmax, block))) return hipErrorInvalidValue;
+  if (gate_w && (!bsum || heads <= 0 || ch != 3 * 32 * heads)) return hipErrorInvalidValue;
   if (out_blocked && !dwconv_can_block_out(bf, kmax, gelu, batch, gh, gw, ch))
     return hipErrorInvalidValue;
   if (bf)
     return gelu ? dispatch_k<bf16, true>(kmax, in, out, weff, nullptr, 1, batch, gh, gw, ch,
-                                         out_blocked, s)
+                                         out_blocked, s, nullptr, 0)
                 : dispatch_k<bf16, false>(kmax, in, out, weff, bsum, block, batch, gh, gw,
-                                          ch, false, s);
+                                          ch, false, s, gate_w, heads);
   return gelu ? dispatch_k<float, true>(kmax, in, out, weff, nullptr, 1, batch, gh, gw, ch,
-                                        false, s)
+                                        false, s, nullptr, 0)
               : dispatch_k<float, false>(kmax, in, out, weff, bsum, block, batch, gh, gw, ch,
-                                         false, s);
+                                         false, s, gate_w, heads);
 }
 
 }  // namespace hsmla

@@ -372,19 +372,60 @@ __global__ __launch_bounds__(1024) void topk_kernel(
 // image, the keys of run s (tpow / kRankParts keys) above key_t and writes
 // part[b][s][t]; rank_final_kernel adds the runs and compacts.  The counts
 // are exact integers, so the ranks equal rank_select's.
+// With FROM_PARTS the scores are first formed from the gate's partial
+// logits (plog[b][t][s][h], see launch_dwconv): M_t = mean_h sigmoid((P_0 +
+// P_1 + P_2) inv_cnt + b_h); workgroup 0 of each image stores them.
 constexpr int kRankParts = 8;
+__device__ __forceinline__ float score_from_parts(const float* __restrict__ P,
+                                                  const float* __restrict__ gb, int heads,
+                                                  float inv_cnt) {
+  float m = 0.f;
+  if (heads % 4 == 0) {  // 16-byte loads of the three rows (16-byte aligned)
+    for (int h = 0; h < heads; h += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(P + h);
+      const float4 k = *reinterpret_cast<const float4*>(P + heads + h);
+      const float4 v = *reinterpret_cast<const float4*>(P + 2 * heads + h);
+      const float pa[4] = {a.x, a.y, a.z, a.w}, pk[4] = {k.x, k.y, k.z, k.w},
+                  pv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float p = ((pa[q] + pk[q]) + pv[q]) * inv_cnt;
+        m += 1.f / (1.f + expf(-(p + gb[h + q])));
+      }
+    }
+  } else {
+    for (int h = 0; h < heads; ++h) {
+      const float p = ((P[h] + P[heads + h]) + P[2 * heads + h]) * inv_cnt;
+      m += 1.f / (1.f + expf(-(p + gb[h])));
+    }
+  }
+  return m / (float)heads;
+}
+template <bool FROM_PARTS>
 __global__ __launch_bounds__(1024) void rank_part_kernel(const float* __restrict__ scores,
                                                          int32_t* __restrict__ part,
-                                                         int nblocks, int tpow) {
+                                                         int nblocks, int tpow,
+                                                         const float* __restrict__ gb,
+                                                         int heads, float inv_cnt,
+                                                         float* __restrict__ scores_out) {
   __shared__ uint64_t keys[1024 / kRankParts];
   const int s = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int len = tpow / kRankParts;
-  const float* src = scores + (size_t)b * nblocks;
+  auto score = [&](int u) {
+    if constexpr (FROM_PARTS)
+      return score_from_parts(scores + ((size_t)b * nblocks + u) * 3 * heads, gb, heads,
+                              inv_cnt);
+    else
+      return scores[(size_t)b * nblocks + u];
+  };
   for (int i = t; i < len; i += blockDim.x) {
     const int u = s * len + i;
-    keys[i] = u < nblocks ? topk_key(src[u], u) : 0;
+    keys[i] = u < nblocks ? topk_key(score(u), u) : 0;
   }
-  const uint64_t kt = t < nblocks ? topk_key(src[t], t) : ~0ull;
+  float st = 0.f;
+  if (t < nblocks) st = score(t);
+  if (FROM_PARTS && s == 0 && t < nblocks) scores_out[(size_t)b * nblocks + t] = st;
+  const uint64_t kt = t < nblocks ? topk_key(st, t) : ~0ull;
   __syncthreads();
   int cnt = 0;
   for (int i = 0; i < len; i += 16) {  // len is a multiple of 16
@@ -511,13 +552,32 @@ hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
   int tpow = 2;
   while (tpow < nblocks) tpow <<= 1;
   if (parts && !scores_copy && tpow >= 16 * kRankParts && tpow <= 1024) {
-    rank_part_kernel<<<dim3(kRankParts, batch), tpow, 0, s>>>(scores, parts, nblocks, tpow);
+    rank_part_kernel<false><<<dim3(kRankParts, batch), tpow, 0, s>>>(
+        scores, parts, nblocks, tpow, nullptr, 0, 0.f, nullptr);
     rank_final_kernel<<<batch, 1024, 0, s>>>(parts, sel, nblocks, keep, tpow);
     return hipGetLastError();
   }
   const size_t lds = (size_t)tpow * sizeof(uint64_t);  // <= 64 KB for T <= 8192
   topk_kernel<<<batch, 1024, lds, s>>>(scores, scores_copy, sel, nblocks, keep,
                                        tpow);
+  return hipGetLastError();
+}
+
+bool gate_topk_from_parts_ok(int nblocks) {
+  int tpow = 2;
+  while (tpow < nblocks) tpow <<= 1;
+  return tpow >= 16 * kRankParts && tpow <= 1024;
+}
+
+hipError_t launch_gate_topk_parts(const float* plog, const float* gate_b, float* scores,
+                                  int32_t* sel, int32_t* parts, int batch, int nblocks,
+                                  int heads, int block, int keep, hipStream_t s) {
+  if (!parts || !gate_topk_from_parts_ok(nblocks)) return hipErrorInvalidValue;
+  int tpow = 2;
+  while (tpow < nblocks) tpow <<= 1;
+  rank_part_kernel<true><<<dim3(kRankParts, batch), tpow, 0, s>>>(
+      plog, parts, nblocks, tpow, gate_b, heads, 1.f / (float)(block * block), scores);
+  rank_final_kernel<<<batch, 1024, 0, s>>>(parts, sel, nblocks, keep, tpow);
   return hipGetLastError();
 }
 

@@ -58,10 +58,15 @@ hipError_t launch_prep(bool bf, const TapSpec* taps, int ntaps,
 // bsum[b][t][c] = sum of the stored out values over block t (block x block
 // tokens, blocks numbered row-major).
 bool dwconv_can_pool(int kmax, int block);
+// With gate_w ([heads][96], the gate's per-head weights; ch = 3 * 32 *
+// heads) the pooled sums go straight into the gate's partial logits,
+// bsum[b][t][s][h] = sum_j gate_w[h][32 s + j] * blocksum(s C + 32 h + j)
+// (s: Q, K, V; C = 32 heads), instead of bsum[b][t][c].
 hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
                          int kmax, int batch, int gh, int gw, int ch,
                          bool gelu, float* bsum, int block, hipStream_t s,
-                         bool out_blocked = false);
+                         bool out_blocked = false, const float* gate_w = nullptr,
+                         int heads = 0);
 // Whether launch_dwconv can write out tile-blocked as the GEMM's A operand
 // (bf16 3x3 with GELU, token count a multiple of kGemmTileM, under 2 GiB).
 bool dwconv_can_block_out(bool bf, int kmax, bool gelu, int batch, int gh, int gw,
@@ -99,6 +104,15 @@ hipError_t launch_gate_scores(bool bf, const void* qkv_hat,
 // scores_copy): scratch that lets 128 .. 1024 blocks per image be ranked
 // over several workgroups per image (two launches).
 size_t topk_parts_bytes(int nblocks);
+// Top-k from the gate's partial logits (written by launch_dwconv with
+// gate_w): M_t = mean_h sigmoid((plog[t][0][h] + plog[t][1][h] +
+// plog[t][2][h]) / block^2 + gate_b[h]) into scores, then the selection as
+// launch_topk with parts (required; 128 .. 1024 blocks per image, see
+// gate_topk_from_parts_ok).
+bool gate_topk_from_parts_ok(int nblocks);
+hipError_t launch_gate_topk_parts(const float* plog, const float* gate_b, float* scores,
+                                  int32_t* sel, int32_t* parts, int batch, int nblocks,
+                                  int heads, int block, int keep, hipStream_t s);
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
                        int batch, int nblocks, int keep, hipStream_t s,
                        int32_t* parts = nullptr);

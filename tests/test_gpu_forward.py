@@ -61,6 +61,34 @@ def test_keep_zero_is_linear_attention(name):
     np.testing.assert_array_equal(ref["o"], ref["o_lin"])
 
 
+_GATE_PARTS = {
+    # 5x5 stream conv (16-lane head slices); C = 96: the last 64-channel
+    # tile holds one slice inside the channels and one outside
+    "branches35_c96": scaled(WORKLOADS["street"], name="gp35", batch=2, grid_h=40,
+                             grid_w=48, channels=96, heads=3, block=4, window=10,
+                             keep=0.2),
+    # 3x3 only: the LDS-staged conv (8-lane head slices)
+    "branches3_c128": scaled(WORKLOADS["street"], name="gp3", batch=1, grid_h=32,
+                             grid_w=64, channels=128, heads=4, branches=(3,),
+                             block=4, window=12, keep=0.15),
+}
+
+
+@pytest.mark.parametrize("name", list(_GATE_PARTS))
+def test_gate_scores_from_conv_partial_logits(name):
+    """Top-k routing with the conv's pooled sums reduced into the gate's
+    partial logits (128..1024 blocks per image): scores within 5e-5 of the
+    oracle and the selection as the oracle ranks the GPU's own scores."""
+    wl = _GATE_PARTS[name]
+    assert 64 < wl.num_blocks <= 1024
+    inp = make_inputs(wl)
+    g = Run(wl, inp).forward()
+    _check_module(wl, inp, g)
+    kk = wl.keep_blocks
+    np.testing.assert_array_equal(g["sel"][:, :kk],
+                                  O.select_blocks(g["scores"].astype(np.float32), kk))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_keep_all_covering_window_is_full_softmax(dtype):
     """Every block refined with a window covering the grid: the linear terms
