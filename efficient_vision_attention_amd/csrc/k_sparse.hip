@@ -304,11 +304,19 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
       // lane holds keys kbase + 8(r/4) + 4g + r%4 of its query
       if (path == 0) {
         float mx = -INFINITY;
+        if (kbase + 32 <= nwin) {  // a whole tile of keys (uniform)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
-          s[r] = key < nwin ? s[r] * sc : -INFINITY;
-          mx = fmaxf(mx, s[r]);
+          for (int r = 0; r < 16; ++r) {
+            s[r] *= sc;
+            mx = fmaxf(mx, s[r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
+            s[r] = key < nwin ? s[r] * sc : -INFINITY;
+            mx = fmaxf(mx, s[r]);
+          }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mnew = fmaxf(run_max, mx);
