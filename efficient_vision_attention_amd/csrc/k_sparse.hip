@@ -320,12 +320,15 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mnew = fmaxf(run_max, mx);
-        const float corr = exp2f(run_max - mnew);
+        // arguments are <= 0: the hardware exp2 (results below 2^-126, i.e.
+        // probabilities negligible against the row maximum's 1, flush to 0;
+        // -inf gives 0) instead of the library's denormal-preserving form
+        const float corr = __builtin_amdgcn_exp2f(run_max - mnew);
         run_max = mnew;
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[r] = exp2f(s[r] - mnew);
+          s[r] = __builtin_amdgcn_exp2f(s[r] - mnew);
           ps += s[r];
         }
         run_sum = run_sum * corr + ps;
