@@ -71,14 +71,25 @@ _GATE_PARTS = {
     "branches3_c128": scaled(WORKLOADS["street"], name="gp3", batch=1, grid_h=32,
                              grid_w=64, channels=128, heads=4, branches=(3,),
                              block=4, window=12, keep=0.15),
+    # the upper end: 1024 blocks per image
+    "blocks1024": scaled(WORKLOADS["street"], name="gp1024", batch=1, grid_h=128,
+                         grid_w=128, channels=64, heads=2, block=4, window=8,
+                         keep=0.05),
+    # the exact gate (its 3x3 inside the head score) pools no sums in the
+    # conv: scores from the gate kernel, ranked over 8 workgroups per image
+    "exact_gate_T192": scaled(WORKLOADS["street"], name="gpx", batch=2, grid_h=48,
+                              grid_w=64, channels=96, heads=3, block=4, window=10,
+                              keep=0.2, gate_conv=True),
 }
 
 
 @pytest.mark.parametrize("name", list(_GATE_PARTS))
-def test_gate_scores_from_conv_partial_logits(name):
-    """Top-k routing with the conv's pooled sums reduced into the gate's
-    partial logits (128..1024 blocks per image): scores within 5e-5 of the
-    oracle and the selection as the oracle ranks the GPU's own scores."""
+def test_topk_over_workgroups(name):
+    """Top-k routing over 65..1024 blocks per image, ranked over several
+    workgroups per image; with the conv's pooled sums reduced into the
+    gate's partial logits, or (exact gate) from the gate kernel's scores:
+    scores within 5e-5 of the oracle and the selection as the oracle ranks
+    the GPU's own scores."""
     wl = _GATE_PARTS[name]
     assert 64 < wl.num_blocks <= 1024
     inp = make_inputs(wl)
