@@ -42,9 +42,30 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------------------
 
 constexpr int kXcds = 8;
+// Tile-blocked A and W with the unrolled K loop: load each K step straight
+// into LDS (see the kernel).
+constexpr bool kDirectLds = true;
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; a field at its maximum does not wait)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 __device__ __forceinline__ uint4 ld16(const bf16* p) {
   return *reinterpret_cast<const uint4*>(p);
+}
+
+// A pointer every lane holds the same value of, made visibly wave-uniform
+// (scalar registers): the direct-to-LDS copies take a scalar base address.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // SITE only names the call site (one kernel symbol per projection, so
@@ -66,8 +87,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
   constexpr int CSTR = TN + 4;                 // floats per staged row
   constexpr int kTileBytes = 2 * (BM + BN) * STR * 2;
   constexpr int kStageBytes = WGM * WGN * 32 * CSTR * 4;
-  __shared__ __attribute__((aligned(16)))
-      char smem[kTileBytes > kStageBytes ? kTileBytes : kStageBytes];
+  // direct-to-LDS path: three unpadded buffers of one K step each
+  constexpr bool kDma = kDirectLds && NKT > 0 && !EDGE && BK == 32;
+  constexpr int kDmaBuf = (BM + BN) * BK * 2;
+  constexpr int kDmaBytes = kDma ? 3 * kDmaBuf : 0;
+  constexpr int kSmem0 = kTileBytes > kStageBytes ? kTileBytes : kStageBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem0 > kDmaBytes ? kSmem0 : kDmaBytes];
   bf16 (*As)[BM * STR] = reinterpret_cast<bf16 (*)[BM * STR]>(smem);
   bf16 (*Ws)[BN * STR] = reinterpret_cast<bf16 (*)[BN * STR]>(smem + 2 * BM * STR * 2);
 
@@ -168,7 +193,93 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
       mfma_frags(af, wf);
     }
   };
-  if constexpr (PF == 1) {
+  if constexpr (kDma) {
+    // Each K step of the A (W) tile is 16 (8) KB; every wave copies its
+    // 1 KB units (16 rows x 64 bytes) straight into LDS
+    // (global_load_lds_dwordx4: lane i's 16 bytes, from its own address,
+    // land at the unit's base + 16 i), so no registers stage the tiles and
+    // no LDS stores are issued.  A tile-blocked operand's unit is one
+    // contiguous 1 KB of its K-step block; a row-major one's is 16 row
+    // pieces of 64 bytes.
+    // The LDS rows are unpadded (64 bytes); to keep the fragment reads free
+    // of bank conflicts, slot i of a unit takes the chunk (row r, k-chunk
+    // kc ^ ((r >> 2) & 3)) -- an XOR swizzle applied by choosing which
+    // global chunk each lane loads, so the blocked layout itself is
+    // unchanged and each unit still reads one contiguous 1 KB.  Three
+    // buffers: tile kt is computed while tiles kt + 1 and kt + 2 load.
+    // The waits are explicit (vmcnt counts this wave's copies in issue
+    // order) and the barriers are plain s_barrier: a workgroup fence would
+    // make the compiler wait for every copy in flight.
+    static_assert(BM * BK * 2 % (1024 * WGM * WGN) == 0 && BN * BK * 2 % (1024 * WGM * WGN) == 0,
+                  "whole 1 KB units per wave");
+    constexpr int UA = BM * BK * 2 / 1024 / (WGM * WGN);  // A units per wave
+    constexpr int UW = BN * BK * 2 / 1024 / (WGM * WGN);  // W units per wave
+    constexpr int kPerTile = UA + UW;                        // copies per wave per tile
+    // this lane's chunk of a unit: its row and (swizzled) k-chunk
+    auto swz_row = [&](int unit) { return (unit * 64 + lane) >> 2; };
+    auto swz_kc = [&](int unit) {
+      const int p = unit * 64 + lane;
+      return (p & 3) ^ ((p >> 4) & 3);
+    };
+    auto issue = [&](int kt, int buf) {
+      char* base = smem + buf * kDmaBuf;
+      const bf16* Ab = (BLK & 1) ? uniform_ptr(A + ((size_t)(m0 / BM) * (K / BK) + kt) * (BM * BK))
+                                 : uniform_ptr(A + (size_t)m0 * K + kt * BK);
+      const bf16* Wb = (BLK & 2) ? uniform_ptr(W + ((size_t)(n0 / BN) * (K / BK) + kt) * (BN * BK))
+                                 : uniform_ptr(W + (size_t)n0 * K + kt * BK);
+      const int a_stride = (BLK & 1) ? BK : K, w_stride = (BLK & 2) ? BK : K;
+#pragma unroll
+      for (int i = 0; i < UA; ++i) {
+        const int unit = wave * UA + i;
+        __builtin_amdgcn_global_load_lds(
+            (global_void_ptr)(Ab + swz_row(unit) * a_stride + swz_kc(unit) * 8),
+            (lds_void_ptr)(base + unit * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < UW; ++i) {
+        const int unit = wave * UW + i;
+        __builtin_amdgcn_global_load_lds(
+            (global_void_ptr)(Wb + swz_row(unit) * w_stride + swz_kc(unit) * 8),
+            (lds_void_ptr)(base + BM * BK * 2 + unit * 1024), 16, 0, 0);
+      }
+    };
+    auto frag = [&](const char* buf_base, int row, int kc) {
+      return __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(
+                      buf_base + row * 64 + ((kc ^ ((row >> 2) & 3)) * 16)));
+    };
+    issue(0, 0);
+    issue(1, 1);
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      // tile kt has landed (this wave's copies of tile kt + 1 may be in
+      // flight), then everyone's has, and everyone is done with kt - 1
+      // (scheduling barriers: no copy may move across the wait + barrier)
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < NKT)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPerTile));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 2 < NKT) issue(kt + 2, (kt + 2) % 3);
+      const char* bA = smem + (kt % 3) * kDmaBuf;
+      const char* bW = bA + BM * BK * 2;
+#pragma unroll
+      for (int ks = 0; ks < BK; ks += 16) {
+        bf16x8 af[FM], wf[FN];
+        const int kc = ks / 8 + (lane >> 5);
+#pragma unroll
+        for (int t = 0; t < FM; ++t) af[t] = frag(bA, wm + 32 * t + frow, kc);
+#pragma unroll
+        for (int t = 0; t < FN; ++t) wf[t] = frag(bW, wn + 32 * t + frow, kc);
+        mfma_frags(af, wf);
+      }
+    }
+    // the epilogue reuses the buffers: every wave's fragment reads are done
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  } else if constexpr (PF == 1) {
     load_tile(ra[0], rw[0], 0);
     store_tile(ra[0], rw[0], 0, 0);
     __syncthreads();
