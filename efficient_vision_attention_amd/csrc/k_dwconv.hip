@@ -713,7 +713,7 @@ struct DwCfg {
   int cx;   // streaming kernel: output columns per thread
 };
 constexpr DwCfg dw_cfg(int k, bool gelu) {
-  return k <= 3 ? DwCfg{4, 4, 64, false, kLdsCols}
+  return k <= 3 ? DwCfg{4, 3, 64, false, kLdsCols}
                 : DwCfg{kStreamV, kStreamRows, kStreamChannels, true, kStreamCols};
   (void)gelu;
 }
