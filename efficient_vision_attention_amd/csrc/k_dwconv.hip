@@ -264,8 +264,10 @@ constexpr int kStreamChannels = 64;  // channels per workgroup
 // of loads in flight.  Measured on the folded 5x5 (7x7) with gate sums:
 // 1 column of 4 channels 116 (196) us, 2 columns 100, 4 columns of 4
 // channels 97, 4 columns of 2 channels 93 (139), 8 columns about the same
-// as 4 but no longer dividing 4 x 4 gate blocks.
-constexpr int kStreamV = 2, kStreamCols = 4, kStreamRows = 2;
+// as 4 but no longer dividing 4 x 4 gate blocks; then one row of loads in
+// flight instead of two 85 us (fewer registers: 5 waves per SIMD, not 4;
+// three or four rows slower).
+constexpr int kStreamV = 2, kStreamCols = 4, kStreamRows = 1;
 // LDS-staged kernel (up to 3x3): output columns per thread.
 constexpr int kLdsCols = 2;
 
