@@ -286,7 +286,8 @@ constexpr int kLdsCols = 2;
 // tiles (their halo columns then hit in that XCD's L2).
 // With POOL the kernel also writes, for the gate, the sum over every
 // block x block block of the values it stores (as stored, i.e. after
-// rounding to T): bsum[b][t][c].  Each thread adds its column's rows and
+// rounding to T): bsum[b][t][c], or those sums already reduced into the
+// gate's partial logits (pool_store).  Each thread adds its column's rows and
 // parks the sum of each finished block row in LDS (its own slot, no
 // barrier); after the strip one barrier, then the block's columns are
 // added in order.  block must divide the workgroup width and the strip

@@ -9,8 +9,10 @@
 // Selection, written in ascending block order -- the compacted tile list the
 // refinement kernel runs over (FT 3.6 stage 3) -- either
 //   top-k:     the keep largest M_t per image, equal scores to the lower block
-//              index, by a bitonic sort in LDS (the count is fixed, so the
-//              grid size is known on the host), or
+//              index: each block's rank counted against every other
+//              block's key (up to 1024 blocks; over several workgroups per
+//              image from 128), or a bitonic sort in LDS above that (the
+//              count is fixed, so the grid size is known on the host), or
 //   threshold: every block with M_t > tau (FT 3.2 gating equation); the
 //              per-image count goes to device memory, or
 //   per head:  for each head h the blocks with G^(h)_t > tau (FT 3.2 per-head

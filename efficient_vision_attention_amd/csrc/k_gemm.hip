@@ -9,10 +9,11 @@
 //
 // bfloat16: 256x128 output tile per 256-thread workgroup (2x2 waves of
 // 128x64, each a 4x2 grid of 32x32x16 MFMAs: the tall wave tile reads fewer
-// LDS bytes per MFMA than a square 64x64 one), K staged through
-// double-buffered LDS in steps of 32 with the global loads of two steps in
-// flight, workgroups mapped so that each XCD walks whole row panels of A
-// (its L2 then serves the A panel to every column tile).
+// LDS bytes per MFMA than a square 64x64 one), K staged through LDS in
+// steps of 32 with two steps in flight -- copied straight into three LDS
+// buffers (global_load_lds) when the K loop is unrolled, else through
+// registers into two -- and workgroups mapped so that each XCD walks whole
+// row panels of A (its L2 then serves the A panel to every column tile).
 // float32: a plain LDS-tiled FMA kernel (small shapes only).
 #include <type_traits>
 
@@ -42,8 +43,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------------------
 
 constexpr int kXcds = 8;
-// Tile-blocked A and W with the unrolled K loop: load each K step straight
-// into LDS (see the kernel).
+// With the unrolled K loop, each K step is copied straight into LDS (see
+// the kernel); the register-staged pipeline serves the other shapes.
 constexpr bool kDirectLds = true;
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
