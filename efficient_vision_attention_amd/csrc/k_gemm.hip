@@ -403,10 +403,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
         const u32x4 vv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
         u32x4* dst = reinterpret_cast<u32x4*>(C + (size_t)gm * N + gn);
-        // the FFN projections stream their outputs past the caches
-        // (measured: FFN1 -8 us, and the conv reading its output is no
-        // slower; the QKV output is left cached for the conv that follows)
-        if constexpr (SITE >= 2)
+        // the QKV and FFN projections stream their outputs past the caches
+        // (measured: FFN1 -8 us and QKV -2.5 us, the convs reading them
+        // at most 1 us slower; the output projection's x1, read twice
+        // more, gained nothing)
+        if constexpr (SITE != 1)
           __builtin_nontemporal_store(vv, dst);
         else
           *dst = vv;
