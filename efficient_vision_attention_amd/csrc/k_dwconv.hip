@@ -20,35 +20,6 @@
 namespace hsmla {
 namespace {
 
-// GELU(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)) with erf from
-// Abramowitz & Stegun 7.1.28:
-//   erf(z) = 1 - (1 + a1 z + a2 z^2 + ... + a6 z^6)^-16,  z >= 0,
-//   |error| <= 3e-7,
-// extended to z < 0 by oddness.  Written as
-//   GELU(x) = max(x, 0) - |x| erfc(|x| / sqrt 2) / 2
-//           = max(x, 0) - |x| / P(|x|)^16,
-// with P's coefficients c_i = a_i 2^(-i/2) 2^(1/16) (c_0 = 2^(1/16)), so
-// that P(|x|)^16 = 2 (1 + a1 z + ... + a6 z^6)^16: six FMAs in |x|, four
-// squarings, one reciprocal, a max and an FMA.  No cancellation for x < 0
-// (the result is the small term itself); measured against float64 erf on
-// [-8, 8]: absolute error <= 7e-7, far below the bfloat16 output
-// precision.  (Infinite x gives NaN; the inputs are sums of finite
-// products.)
-__device__ __forceinline__ float gelu_erf(float x) {
-  constexpr float c0 = 1.0442737824e+00f, c1 = 5.2075163037e-02f,
-                  c2 = 2.2076998457e-02f, c3 = 3.4227392389e-03f,
-                  c4 = 3.9686137011e-05f, c5 = 5.1055209009e-05f,
-                  c6 = 5.6212996640e-06f;
-  const float ax = fabsf(x);
-  float p = fmaf(fmaf(fmaf(fmaf(fmaf(fmaf(c6, ax, c5), ax, c4), ax, c3), ax, c2), ax, c1),
-                 ax, c0);
-  p *= p;
-  p *= p;
-  p *= p;
-  p *= p;
-  return fmaf(-ax, __builtin_amdgcn_rcpf(p), fmaxf(x, 0.f));
-}
-
 constexpr int TH = 32;   // output rows per workgroup strip
 constexpr int kPoolMinBlock = 4;
 constexpr int kXcds = 8;
@@ -497,10 +468,13 @@ __global__ __launch_bounds__(256) void dwconv_stream(
 // registers).  Compared with the
 // register-only kernel the bytes in flight per workgroup no longer scale
 // with the per-thread tap registers.
-// BO: out is written tile-blocked for the GEMM (token m of the launch,
+// BO > 0: out is written tile-blocked for the GEMM (token m of the launch,
 // channel k at ((m / 256) * (ch / 32) + k / 32) * 8192 + (m % 256) * 32 +
-// k % 32); out_bytes_all is then the whole output's size in bytes.
-template <typename T, int K, bool GELU, int V, int P, bool POOL, int WC, bool BO,
+// k % 32); out_bytes_all is then the whole output's size in bytes.  BO = 2
+// when gw is a multiple of 256: grid row yo is then whole tiles, one
+// contiguous gw * ch run, so the offset within the row is fixed per thread
+// and the row is a scalar base.
+template <typename T, int K, bool GELU, int V, int P, bool POOL, int WC, int BO,
           int CX = 1>
 __global__ __launch_bounds__(256) void dwconv_lds(
     const T* __restrict__ in, T* __restrict__ out,
@@ -592,8 +566,19 @@ __global__ __launch_bounds__(256) void dwconv_lds(
   const int out_bytes = (ox1 - x0) * ch * (int)sizeof(T);
   int st_off[CX];
 #pragma unroll
-  for (int cx = 0; cx < CX; ++cx)
-    st_off[cx] = (x + cx < gw && c_ok) ? ((tx * CX + cx) * ch + c) * (int)sizeof(T) : kOob;
+  for (int cx = 0; cx < CX; ++cx) {
+    const int xc = x + cx;
+    const bool ok = xc < gw && c_ok;
+    if (BO == 2)
+      st_off[cx] = ok
+                       ? (((xc / kGemmTileM) * (ch / kGemmTileK) + c / kGemmTileK) *
+                              (kGemmTileM * kGemmTileK) +
+                          (xc % kGemmTileM) * kGemmTileK + c % kGemmTileK) *
+                             (int)sizeof(T)
+                       : kOob;
+    else
+      st_off[cx] = ok ? ((tx * CX + cx) * ch + c) * (int)sizeof(T) : kOob;
+  }
 
   float acc[K][CX][V];
 #pragma unroll
@@ -623,7 +608,8 @@ __global__ __launch_bounds__(256) void dwconv_lds(
       if (u >= nrows) break;
       const int r = r_begin + u;
       __syncthreads();
-      if (r >= 0 && r < gh) {
+      {
+        // rows outside the grid were staged as zeros (empty resource)
         float xin[KL][V];
 #pragma unroll
         for (int kx = 0; kx < KL; ++kx) {
@@ -631,7 +617,9 @@ __global__ __launch_bounds__(256) void dwconv_lds(
           rr.load(reinterpret_cast<const T*>(my + (u & 1) * SLOT + kx * CB));
           rr.cvt(xin[kx]);
         }
-        // input row r feeds output row r - R + i with vertical tap K - 1 - i
+        // input row r feeds output row r - R + i with vertical tap K - 1 - i;
+        // for i = K - 1 it is that output row's first input row, whose first
+        // product starts the slot (freed by the row stored just before)
 #pragma unroll
         for (int i = 0; i < K; ++i) {
           const int slot = (v - R + i + G) % K;
@@ -641,7 +629,10 @@ __global__ __launch_bounds__(256) void dwconv_lds(
             for (int cx = 0; cx < CX; ++cx)
 #pragma unroll
               for (int j = 0; j < V; ++j)
-                acc[slot][cx][j] = fmaf(w[K - 1 - i][kx][j], xin[cx + kx][j], acc[slot][cx][j]);
+                acc[slot][cx][j] = (i == K - 1 && kx == 0)
+                                       ? w[K - 1 - i][kx][j] * xin[cx + kx][j]
+                                       : fmaf(w[K - 1 - i][kx][j], xin[cx + kx][j],
+                                              acc[slot][cx][j]);
         }
       }
       // stage row r + 1 (its loads were issued P - 1 rows ago) and issue
@@ -657,7 +648,12 @@ __global__ __launch_bounds__(256) void dwconv_lds(
 #pragma unroll
         for (int j = 0; j < V; ++j)
           o[j] = GELU ? gelu_erf(acc[done][cx][j]) : acc[done][cx][j];
-        if constexpr (BO) {
+        if constexpr (BO == 2) {
+          const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
+              out + (img + (size_t)min(max(yo, 0), gh - 1) * gw) * ch,
+              row_out ? gw * ch * (int)sizeof(T) : 0);
+          store_buf<T, V>(rs, st_off[cx], o);
+        } else if constexpr (BO == 1) {
           const int m = (b * gh + yo) * gw + x + cx;
           const int off =
               (row_out && x + cx < gw && c_ok)
@@ -691,10 +687,6 @@ __global__ __launch_bounds__(256) void dwconv_lds(
           }
         }
       }
-#pragma unroll
-      for (int cx = 0; cx < CX; ++cx)
-#pragma unroll
-        for (int j = 0; j < V; ++j) acc[done][cx][j] = 0.f;
     }
   }
   if constexpr (POOL) {
@@ -725,6 +717,12 @@ constexpr int dw_width(int k, bool gelu) {
 }
 
 template <typename T, int K, bool GELU>
+hipError_t run_dw_lds(const void* in, void* out, const float* weff, float* bsum,
+                      int block, int batch, int gh, int gw, int ch, bool out_blocked,
+                      hipStream_t s, const float* gate_w, int heads, int col_tiles,
+                      int ch_tiles, int strips, int total, int per_xcd);
+
+template <typename T, int K, bool GELU>
 hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
                   int block, int batch, int gh, int gw, int ch, bool out_blocked,
                   hipStream_t s, const float* gate_w, int heads) {
@@ -745,22 +743,38 @@ hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
           static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
           gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, nullptr, 0);
     return hipGetLastError();
+  } else {
+    return run_dw_lds<T, K, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked,
+                                  s, gate_w, heads, col_tiles, ch_tiles, strips, total, per_xcd);
   }
+}
+
+template <typename T, int K, bool GELU>
+hipError_t run_dw_lds(const void* in, void* out, const float* weff, float* bsum,
+                      int block, int batch, int gh, int gw, int ch, bool out_blocked,
+                      hipStream_t s, const float* gate_w, int heads, int col_tiles,
+                      int ch_tiles, int strips, int total, int per_xcd) {
+  constexpr DwCfg cf = dw_cfg(K, GELU);
   if constexpr (!GELU) {
     if (bsum) {
-      dwconv_lds<T, K, false, cf.v, cf.p, true, cf.wc, false, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
+      dwconv_lds<T, K, false, cf.v, cf.p, true, cf.wc, 0, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
           gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0, gate_w, heads);
       return hipGetLastError();
     }
   }
-  if (out_blocked)
-    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, true, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
+  if (out_blocked && gw % kGemmTileM == 0)
+    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, 2, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
+        static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
+        gw, ch, col_tiles, ch_tiles, strips, total, per_xcd,
+        (int)((size_t)batch * gh * gw * ch * sizeof(T)), nullptr, 0);
+  else if (out_blocked)
+    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, 1, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
         static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
         gw, ch, col_tiles, ch_tiles, strips, total, per_xcd,
         (int)((size_t)batch * gh * gw * ch * sizeof(T)), nullptr, 0);
   else
-    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, false, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
+    dwconv_lds<T, K, GELU, cf.v, cf.p, false, cf.wc, 0, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
         static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
         gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, 0, nullptr, 0);
   return hipGetLastError();

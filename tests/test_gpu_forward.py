@@ -172,6 +172,25 @@ def test_block_forward_layernorm_params():
     assert_close(g["out"], _oracle_ffn(g["x1"], inp, wl), wl.dtype, "out")
 
 
+# More block shapes at C = 384: a 256-wide grid (two images, the rows at
+# the top and bottom of each) and a 128-wide one.
+_BLOCK_SHAPES = {
+    "w256_b2": scaled(WORKLOADS["block"], name="bs256", batch=2, grid_h=8, grid_w=256,
+                      keep=0.25),
+    "w128_b1": scaled(WORKLOADS["block"], name="bs128", batch=1, grid_h=24, grid_w=128,
+                      keep=0.1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_BLOCK_SHAPES))
+def test_block_forward_shapes(name):
+    wl = _BLOCK_SHAPES[name]
+    inp = make_inputs(wl)
+    print(f"[case] block forward {name}", flush=True)
+    g = Run(wl, inp).block_forward()
+    assert_close(g["out"], _oracle_ffn(g["x1"], inp, wl), wl.dtype, "out")
+
+
 def _oracle_ffn(x1, inp, wl):
     r = O.round_bf16
     xn2 = r(O.layer_norm(x1, inp["ln2_g"], inp["ln2_b"]))
