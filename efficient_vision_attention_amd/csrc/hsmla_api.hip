@@ -762,6 +762,12 @@ hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
                        hsmla::gemm_whole_tiles(P, 4 * C, C);
   const bool h2_blk = hsmla::dwconv_can_block_out(D.bf, 3, true, D.B, D.gh, D.gw, 4 * C) &&
                       hsmla::gemm_whole_tiles(P, C, 4 * C);
+  // FFN1 writes h1 channel-planar (64-channel planes: each wave's output
+  // rows one contiguous run) when the FFN conv can read it so
+  const bool h1_planar =
+      h2_blk && ln2_blk && pick_w(f->w1, u.w1, P, 4 * C, C).blocked &&
+      hsmla::gemm_planar_ok(D.bf, P, 4 * C, C, true, true) &&
+      hsmla::dwconv_planar_ok(D.bf, D.B, D.gh, D.gw, 4 * C);
   if (st >= 1 && st <= kModuleStages)
     return module_stage(st - 1, D, desc, w, u.xn, u, s, r, ln1_blk);
   switch (st) {
@@ -787,13 +793,17 @@ hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
       r.mark("ffn1_gemm");
       const WSel w1 = pick_w(f->w1, u.w1, P, 4 * C, C);
       HSMLA_TRY(hsmla::launch_gemm(D.bf, u.xn, w1.w, nullptr, u.h1, P, 4 * C, C, s,
-                                   hsmla::GemmSite::kFfn1, ln2_blk, w1.blocked));
+                                   hsmla::GemmSite::kFfn1, ln2_blk, w1.blocked, h1_planar));
       return HSMLA_OK;
     }
     case kModuleStages + 4: {
       r.mark("ffn_dwconv_gelu");
-      HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.h1, u.h2, u.ftaps, 3, D.B, D.gh,
-                                     D.gw, 4 * C, true, nullptr, 1, s, h2_blk));
+      if (h1_planar)
+        HSMLA_TRY(hsmla::launch_dwconv_gelu_planar(u.h1, u.h2, u.ftaps, D.B, D.gh, D.gw,
+                                                   4 * C, s));
+      else
+        HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.h1, u.h2, u.ftaps, 3, D.B, D.gh,
+                                       D.gw, 4 * C, true, nullptr, 1, s, h2_blk));
       r.mark("ffn2_gemm_residual");
       const WSel w2 = pick_w(f->w2, u.w2, P, C, 4 * C);
       HSMLA_TRY(hsmla::launch_gemm(D.bf, u.h2, w2.w, u.x1, out, P, C, 4 * C, s,

@@ -384,12 +384,15 @@ __global__ __launch_bounds__(256) void dwconv_stream(
       const int r = r0 + u;
       if (r >= r_end) break;
       Raw<T, V>(&cur)[KL] = rbuf[u % NB];
-      // A halo row outside the grid contributes nothing: skip it (uniform).
+      // A halo row outside the grid contributes nothing: skip it (uniform),
+      // but start the output row it would have started.
       if (r >= 0 && r < gh) {
         float xin[KL][V];
 #pragma unroll
         for (int kx = 0; kx < KL; ++kx) cur[kx].cvt(xin[kx]);
-        // input row r feeds output row r - R + i with vertical tap K - 1 - i
+        // input row r feeds output row r - R + i with vertical tap K - 1 - i;
+        // for i = K - 1 it is that output row's first input row, whose first
+        // product starts the slot (freed by the row stored just before)
 #pragma unroll
         for (int i = 0; i < K; ++i) {
           const int slot = (u - R + i + NB * K) % K;
@@ -401,9 +404,17 @@ __global__ __launch_bounds__(256) void dwconv_stream(
             for (int cx = 0; cx < CX; ++cx)
 #pragma unroll
               for (int j = 0; j < V; ++j)
-                acc[slot][cx][j] = fmaf(t[j], xin[cx + kx][j], acc[slot][cx][j]);
+                acc[slot][cx][j] = (i == K - 1 && kx == 0)
+                                       ? t[j] * xin[cx + kx][j]
+                                       : fmaf(t[j], xin[cx + kx][j], acc[slot][cx][j]);
           }
         }
+      } else {
+        const int slot = (u - R + K - 1 + NB * K) % K;
+#pragma unroll
+        for (int cx = 0; cx < CX; ++cx)
+#pragma unroll
+          for (int j = 0; j < V; ++j) acc[slot][cx][j] = 0.f;
       }
       // unconditional (clamped) prefetch keeps the load/wait pattern regular
       load_row(cur, r + NB);
@@ -444,10 +455,6 @@ __global__ __launch_bounds__(256) void dwconv_stream(
           }
         }
       }
-#pragma unroll
-      for (int cx = 0; cx < CX; ++cx)
-#pragma unroll
-        for (int j = 0; j < V; ++j) acc[done][cx][j] = 0.f;
     }
   }
   if constexpr (POOL) {
@@ -474,8 +481,11 @@ __global__ __launch_bounds__(256) void dwconv_stream(
 // when gw is a multiple of 256: grid row yo is then whole tiles, one
 // contiguous gw * ch run, so the offset within the row is fixed per thread
 // and the row is a scalar base.
+// PIN: in is channel-planar (64-channel planes, element (m, c) of the
+// launch's tokens at (c / 64) * tokens * 64 + m * 64 + c % 64; WC = 64):
+// a staged row is then one contiguous run of the workgroup's plane.
 template <typename T, int K, bool GELU, int V, int P, bool POOL, int WC, int BO,
-          int CX = 1>
+          int CX = 1, bool PIN = false>
 __global__ __launch_bounds__(256) void dwconv_lds(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, float* __restrict__ bsum, int block,
@@ -533,7 +543,16 @@ __global__ __launch_bounds__(256) void dwconv_lds(
   // in-grid staged column, or kOob for chunks outside the grid (read as 0).
   const int lx0 = max(x0 - R, 0);
   const int lx1 = min(gw, x0 + TW + R);
-  const int row_bytes = (lx1 - lx0) * ch * (int)sizeof(T);
+  // column stride of the input (elements), its channel base
+  static_assert(!PIN || WC == 64, "64-channel planes");
+  const int cs = PIN ? WC : ch;
+  const int cb = PIN ? c0 : 0;
+  const T* inb = in;
+  if constexpr (PIN) {
+    const int batch = total / (col_tiles * ch_tiles * strips);
+    inb = in + (size_t)ch_t * ((size_t)batch * gh * gw * WC);
+  }
+  const int row_bytes = (lx1 - lx0) * cs * (int)sizeof(T);
   int ld_off[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
@@ -542,12 +561,12 @@ __global__ __launch_bounds__(256) void dwconv_lds(
     const int xg = x0 - R + col;
     const int cg = c0 + part * EPC;
     const bool ok = q < CHUNKS && xg >= 0 && xg < gw && cg < ch;
-    ld_off[i] = ok ? ((xg - lx0) * ch + cg) * (int)sizeof(T) : kOob;
+    ld_off[i] = ok ? ((xg - lx0) * cs + cg - cb) * (int)sizeof(T) : kOob;
   }
   auto load_row = [&](uint4 (&d)[LPT], int r) {
     const bool in_grid = r >= 0 && r < gh;
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
-        in + (img + (size_t)min(max(r, 0), gh - 1) * gw + lx0) * ch,
+        inb + (img + (size_t)min(max(r, 0), gh - 1) * gw + lx0) * cs,
         in_grid ? row_bytes : 0);
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
@@ -794,6 +813,29 @@ hipError_t dispatch_k(int kmax, const void* in, void* out, const float* weff,
 }
 
 }  // namespace
+
+bool dwconv_planar_ok(bool bf, int batch, int gh, int gw, int ch) {
+  return dwconv_can_block_out(bf, 3, true, batch, gh, gw, ch) && gw % kGemmTileM == 0 &&
+         ch % 64 == 0 && dw_cfg(3, true).wc == 64;
+}
+
+hipError_t launch_dwconv_gelu_planar(const void* in, void* out, const float* weff, int batch,
+                                     int gh, int gw, int ch, hipStream_t s) {
+  if (!dwconv_planar_ok(true, batch, gh, gw, ch)) return hipErrorInvalidValue;
+  constexpr DwCfg cf = dw_cfg(3, true);
+  constexpr int TW = dw_width(3, true);
+  const int col_tiles = (gw + TW - 1) / TW;
+  const int ch_tiles = ch / cf.wc;
+  const int strips = (gh + TH - 1) / TH;
+  const int total = col_tiles * ch_tiles * strips * batch;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  dwconv_lds<bf16, 3, true, cf.v, cf.p, false, cf.wc, 2, cf.cx, true>
+      <<<per_xcd * kXcds, 256, 0, s>>>(
+          static_cast<const bf16*>(in), static_cast<bf16*>(out), weff, nullptr, 1, gh, gw, ch,
+          col_tiles, ch_tiles, strips, total, per_xcd,
+          (int)((size_t)batch * gh * gw * ch * sizeof(bf16)), nullptr, 0);
+  return hipGetLastError();
+}
 
 bool dwconv_can_pool(int kmax, int block) {
   const int tw = dw_width(kmax, false);

@@ -402,7 +402,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
       if (!EDGE || (gm < M && gn < N)) {
         const u32x4 vv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-        u32x4* dst = reinterpret_cast<u32x4*>(C + (size_t)gm * N + gn);
+        // BLK bit 2: C channel-planar, element (m, n) at
+        // (n / 64) * M * 64 + m * 64 + n % 64 (a wave tile's 64 columns are
+        // one plane, so its rows are one contiguous run)
+        u32x4* dst = reinterpret_cast<u32x4*>(
+            (BLK & 4) ? C + (size_t)(gn / 64) * ((size_t)M * 64) + (size_t)gm * 64 + gn % 64
+                      : C + (size_t)gm * N + gn);
         // the QKV and FFN projections stream their outputs past the caches
         // (measured: FFN1 -8 us and QKV -2.5 us, the convs reading them
         // at most 1 us slower; the output projection's x1, read twice
@@ -443,6 +448,10 @@ void launch_blk(int blk, const void* A, const void* W, const void* R, void* C,
     case 1: launch_tiles<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, 1>(A, W, R, C, M, N, K, s); break;
     case 2: launch_tiles<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, 2>(A, W, R, C, M, N, K, s); break;
     case 3: launch_tiles<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, 3>(A, W, R, C, M, N, K, s); break;
+    case 7:
+      if constexpr (!EDGE && NKT > 0 && BN / WGN == 64)
+        launch_tiles<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, 7>(A, W, R, C, M, N, K, s);
+      break;
     default: launch_tiles<BM, BN, BK, WGM, WGN, SITE, PF, EDGE, NKT, 0>(A, W, R, C, M, N, K, s); break;
   }
 }
@@ -539,12 +548,19 @@ bool gemm_whole_tiles(int M, int N, int K) {
   return M % kGemmTileM == 0 && N % kGemmTileN == 0 && K % kGemmTileK == 0;
 }
 
+bool gemm_planar_ok(bool bf, int M, int N, int K, bool a_blocked, bool w_blocked) {
+  return bf && a_blocked && w_blocked && gemm_whole_tiles(M, N, K) &&
+         (K == 12 * kGemmTileK || K == 48 * kGemmTileK);
+}
+
 hipError_t launch_gemm(bool bf, const void* A, const void* W, const void* R,
                        void* C, int M, int N, int K, hipStream_t s,
-                       GemmSite site, bool a_blocked, bool w_blocked) {
+                       GemmSite site, bool a_blocked, bool w_blocked, bool c_planar) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int blk = (a_blocked ? 1 : 0) | (w_blocked ? 2 : 0);
+  const int blk = (a_blocked ? 1 : 0) | (w_blocked ? 2 : 0) | (c_planar ? 4 : 0);
   if (blk && (!bf || !gemm_whole_tiles(M, N, K))) return hipErrorInvalidValue;
+  if (c_planar && !gemm_planar_ok(bf, M, N, K, a_blocked, w_blocked))
+    return hipErrorInvalidValue;
   if (bf) {
     switch (site) {
       case GemmSite::kQkv: return run_mfma<0>(A, W, R, C, M, N, K, blk, s);

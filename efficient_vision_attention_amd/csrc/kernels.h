@@ -24,10 +24,14 @@ bool gemm_whole_tiles(int M, int N, int K);
 // and R.  N and K must be multiples of 32 (8-element chunks are loaded
 // whole).  a_blocked / w_blocked: A / W are tile-blocked (bf16 and
 // gemm_whole_tiles(M, N, K) only; otherwise hipErrorInvalidValue).
+// c_planar: C written channel-planar, element (m, n) at
+// (n / 64) * M * 64 + m * 64 + n % 64 (only where gemm_planar_ok: bf16,
+// tile-blocked A and W, whole tiles, K = 384 or 1536).
 hipError_t launch_gemm(bool bf, const void* A, const void* W, const void* R,
                        void* C, int M, int N, int K, hipStream_t s,
                        GemmSite site, bool a_blocked = false,
-                       bool w_blocked = false);
+                       bool w_blocked = false, bool c_planar = false);
+bool gemm_planar_ok(bool bf, int M, int N, int K, bool a_blocked, bool w_blocked);
 
 // Effective depthwise taps: weff[tap][ch] (float32, kmax x kmax taps) =
 // identity (centre tap += 1 when `identity`) + sum of the given kernels,
@@ -71,6 +75,14 @@ hipError_t launch_dwconv(bool bf, const void* in, void* out, const float* weff,
 // (bf16 3x3 with GELU, token count a multiple of kGemmTileM, under 2 GiB).
 bool dwconv_can_block_out(bool bf, int kmax, bool gelu, int batch, int gh, int gw,
                           int ch);
+
+// The FFN's conv + GELU from a channel-planar input (as launch_gemm writes
+// it with c_planar) to the tile-blocked output of launch_dwconv; only where
+// dwconv_planar_ok (bf16, out_blocked possible, gw a multiple of 256, ch a
+// multiple of 64).
+bool dwconv_planar_ok(bool bf, int batch, int gh, int gw, int ch);
+hipError_t launch_dwconv_gelu_planar(const void* in, void* out, const float* weff, int batch,
+                                     int gh, int gw, int ch, hipStream_t s);
 
 // Number of token chunks the KV-state reduction splits each image into.
 int kv_chunks(bool bf, int batch, int heads, int tokens);
