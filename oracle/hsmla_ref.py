@@ -585,6 +585,11 @@ def hsmla_block_forward(x, weights, *, staged=False, **kw):
     LN gamma/beta come from ``weights``; no biases elsewhere.  In staged mode
     the residual sums are rounded once, after the add, as the GPU stores
     them.  Returns the module intermediates plus xn1, x1, xn2, h1, h2, out.
+
+    Pinned by closed forms of the composition: W2 = 0 or a zero FFN kernel
+    leave out = X1; constant LN rows (gamma = 0) give X1 = X + v W_o and
+    out = X1 + GELU(u * S) W2 with S the in-grid tap sums; X = 0 pins LN2's
+    input as X1 against a library LayerNorm.
     """
     rnd = round_bf16 if staged else _identity
     x = np.asarray(x, np.float64)

@@ -475,19 +475,125 @@ def test_staged_mode_rounds_and_stays_close():
         np.testing.assert_allclose(st[key], ex[key], rtol=3e-2, atol=3e-2)
 
 
-def test_block_forward_keep_zero_composition():
+def _block_case(keep=0.1, seed=5):
     wl = scaled(WORKLOADS["block"], batch=1, grid_h=16, grid_w=16,
-                channels=64, heads=2, keep=0.0)
-    inp = make_inputs(wl)
+                channels=64, heads=2, keep=keep, seed=seed)
+    return wl, make_inputs(wl)
+
+
+@pytest.mark.parametrize("staged", [False, True])
+def test_block_forward_zero_w2_leaves_x1(staged):
+    # FT 3.5 block equation: the FFN branch enters the output only through
+    # W2, so W2 = 0 gives out = X1 exactly, whatever the rest computes
+    wl, inp = _block_case()
+    inp = dict(inp, w2=np.zeros_like(inp["w2"]))
+    r = O.hsmla_block_forward(inp["x"], inp, staged=staged, **wl.kwargs())
+    np.testing.assert_array_equal(r["out"], r["x1"])
+    assert np.abs(r["x1"] - inp["x"]).max() > 1e-2  # the attention did act
+
+
+def test_block_forward_zero_ffn_conv_leaves_x1():
+    # a zero depthwise kernel zeroes the conv, GELU(0) = 0, so out = X1
+    wl, inp = _block_case()
+    inp = dict(inp, dw_ffn=np.zeros_like(inp["dw_ffn"]))
     r = O.hsmla_block_forward(inp["x"], inp, **wl.kwargs())
-    xn1 = O.layer_norm(inp["x"], 1.0, 0.0)
-    lin, _, _ = O.linear_attention(
-        O.multiscale_branches(xn1 @ inp["w_qkv"], inp["dw"], 16, 16), 2)
-    x1 = inp["x"] + lin @ inp["w_o"]
-    np.testing.assert_allclose(r["x1"], x1, atol=1e-12)
-    h = O.gelu(O.dwconv_same(O.layer_norm(x1, 1.0, 0.0) @ inp["w1"],
-                             inp["dw_ffn"], 16, 16))
-    np.testing.assert_allclose(r["out"], x1 + h @ inp["w2"], atol=1e-12)
+    np.testing.assert_array_equal(r["out"], r["x1"])
+
+
+def _phi_cdf(z):
+    return 0.5 * (1.0 + math.erf(z / math.sqrt(2.0)))
+
+
+@pytest.mark.parametrize("keep", [0.0, 0.25, 1.0])
+def test_block_forward_constant_attention_rows_closed_form(keep):
+    """LN with gamma = 0 returns beta on every token.  With LN1 so and no
+    depthwise branch acting (dw = 0), Q^ = Q, K^ = K, V^ = V are one row
+    r = c1 W_qkv at every token; every head's linear path is then
+    relu(q).N relu(k)^T v / relu(q).N relu(k) = v, and any window's softmax
+    over identical keys is v while its linear estimate is v as well, so the
+    residual vanishes and X1 = X + v W_o for every keep ratio (FT 3.3 and the
+    FT 3.5 block equation).  LN2 keeps a non-trivial gamma, so swapping the
+    two norms' parameters fails here."""
+    wl, inp = _block_case(keep=keep)
+    rng = _rng(77)
+    C = wl.channels
+    c1 = rng.standard_normal(C)
+    inp = dict(inp, dw=[np.zeros_like(k) for k in inp["dw"]],
+               ln1_g=np.zeros(C), ln1_b=c1,
+               ln2_g=1.0 + 0.5 * rng.standard_normal(C), ln2_b=rng.standard_normal(C))
+    # keep every head's relu(q).relu(k) away from 0 (a positive q and k)
+    w = inp["w_qkv"].copy()
+    w[:, :2 * C] = np.abs(w[:, :2 * C]) * np.sign(c1)[:, None]
+    inp["w_qkv"] = w
+    r = O.hsmla_block_forward(inp["x"], inp, **wl.kwargs())
+    v = (c1 @ w)[2 * C:]
+    np.testing.assert_allclose(r["x1"], inp["x"] + v @ inp["w_o"], rtol=0, atol=1e-10)
+
+
+def test_block_forward_constant_ffn_rows_closed_form():
+    """With LN2's gamma = 0 and beta = c2, h1 = u = c2 W1 at every token, and
+    the zero-padded 3x3 cross-correlation at (y, x) is u times the sum S of
+    the taps g[dy][dx] whose neighbour (y + dy - 1, x + dx - 1) lies in the
+    grid: 4 taps at a corner, 6 on an edge, all 9 inside.  Then
+    out = X1 + GELU(u * S(y, x)) W2 (the FFN-DWConv sandwich of the block).
+    LN1 keeps a non-trivial gamma."""
+    wl, inp = _block_case(keep=0.25)
+    rng = _rng(78)
+    C, gh, gw = wl.channels, wl.grid_h, wl.grid_w
+    c2 = rng.standard_normal(C)
+    inp = dict(inp, ln1_g=1.0 + 0.5 * rng.standard_normal(C),
+               ln1_b=rng.standard_normal(C), ln2_g=np.zeros(C), ln2_b=c2)
+    r = O.hsmla_block_forward(inp["x"], inp, **wl.kwargs())
+    u = c2 @ inp["w1"]
+    g = inp["dw_ffn"]  # [4C, 3, 3]
+    for (y, x) in [(0, 0), (0, gw - 1), (gh - 1, 0), (gh - 1, gw - 1),
+                   (0, 5), (7, 0), (gh - 1, 9), (4, gw - 1), (8, 8), (3, 11)]:
+        rows = [dy for dy in range(3) if 0 <= y + dy - 1 < gh]
+        cols = [dx for dx in range(3) if 0 <= x + dx - 1 < gw]
+        edge_y, edge_x = y in (0, gh - 1), x in (0, gw - 1)
+        assert len(rows) * len(cols) == (4 if edge_y and edge_x else
+                                         6 if edge_y or edge_x else 9)
+        S = sum(g[:, dy, dx] for dy in rows for dx in cols)
+        h2 = np.array([z * _phi_cdf(z) for z in u * S])
+        n = y * gw + x
+        np.testing.assert_allclose(r["out"][0, n] - r["x1"][0, n], h2 @ inp["w2"],
+                                   rtol=0, atol=1e-10)
+
+
+def test_block_forward_zero_input_closed_form():
+    """X = 0: LN1 returns beta1 on every token (zero variance), so with no
+    depthwise branch acting the attention output is v = (beta1 W_qkv)_V on
+    every token (as in the constant-rows case above) and X1 = a = v W_o, one
+    row everywhere.  LN2 of that row is a library LayerNorm of a, h1 is
+    u = LN2(a) W1 everywhere, and the zero-padded conv makes
+    out = a + GELU(u * S(y, x)) W2 with S the in-grid tap sums.  Applying
+    LN2 to X instead of X1, or dropping the first residual, fails here."""
+    wl, inp = _block_case(keep=0.25)
+    rng = _rng(79)
+    C, gh, gw = wl.channels, wl.grid_h, wl.grid_w
+    c1 = rng.standard_normal(C)
+    g2, b2 = 1.0 + 0.5 * rng.standard_normal(C), rng.standard_normal(C)
+    inp = dict(inp, x=np.zeros_like(inp["x"]),
+               dw=[np.zeros_like(k) for k in inp["dw"]],
+               ln1_g=1.0 + 0.5 * rng.standard_normal(C), ln1_b=c1, ln2_g=g2, ln2_b=b2)
+    w = inp["w_qkv"].copy()
+    w[:, :2 * C] = np.abs(w[:, :2 * C]) * np.sign(c1)[:, None]
+    inp["w_qkv"] = w
+    r = O.hsmla_block_forward(inp["x"], inp, **wl.kwargs())
+    a = (c1 @ w)[2 * C:] @ inp["w_o"]
+    np.testing.assert_allclose(r["x1"][0], np.tile(a, (gh * gw, 1)), rtol=0, atol=1e-10)
+    z = torch.nn.functional.layer_norm(torch.from_numpy(a)[None], (C,),
+                                       torch.from_numpy(g2), torch.from_numpy(b2),
+                                       eps=1e-5).numpy()[0]
+    u = z @ inp["w1"]
+    g = inp["dw_ffn"]
+    for (y, x) in [(0, 0), (gh - 1, gw - 1), (0, 6), (9, 0), (5, 7)]:
+        rows = [dy for dy in range(3) if 0 <= y + dy - 1 < gh]
+        cols = [dx for dx in range(3) if 0 <= x + dx - 1 < gw]
+        S = sum(g[:, dy, dx] for dy in rows for dx in cols)
+        h2 = np.array([q * _phi_cdf(q) for q in u * S])
+        np.testing.assert_allclose(r["out"][0, y * gw + x], a + h2 @ inp["w2"],
+                                   rtol=0, atol=1e-9)
 
 
 # ---------------------------------------------------------------------------
