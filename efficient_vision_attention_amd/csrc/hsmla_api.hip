@@ -38,6 +38,8 @@ struct Dims {
   bool thr;   // threshold routing (block or per head)
   bool ph;    // per-head routing
   bool soft;  // every block, residual scaled by its score
+  bool wblk;  // the GEMM's weight copies are tile-blocked (see weights_blocked)
+  bool prepared;  // taps and weight copies already in the workspace
   float tau;
 };
 
@@ -97,12 +99,20 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
     out->ph = d->routing == HSMLA_ROUTE_HEAD_THRESHOLD;
     out->soft = d->routing == HSMLA_ROUTE_SOFT;
     out->tau = d->tau;
+    out->prepared = d->prepared != 0;
     out->sw = out->ph   ? d->heads * (int)T
               : out->thr  ? (int)T
               : out->soft ? 0
                           : d->keep_blocks;
     out->nc = out->ph ? d->batch * d->heads : d->batch;
     out->e = out->bf ? 2 : 4;
+    // Tile-blocked weight copies when every projection of every image range
+    // is whole GEMM tiles: output widths (3C, C, 4C) multiples of
+    // kGemmTileN, input widths of kGemmTileK, and each image's token count a
+    // multiple of kGemmTileM (so any range of images is too).
+    out->wblk = out->bf && (3 * out->C) % hsmla::kGemmTileN == 0 &&
+                out->C % hsmla::kGemmTileN == 0 && out->C % hsmla::kGemmTileK == 0 &&
+                out->N % hsmla::kGemmTileM == 0;
   }
   return HSMLA_OK;
 }
@@ -115,23 +125,16 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
 //   gate block sums [B][T][3C] f32,
 //   (block only) xn [P][C], x1 [P][C], h1 [P][4C], h2 [P][4C],
 //   ffn taps [9][4C] f32,
-//   tile-blocked copies of W_qkv, W_o (and, block only, W1, W2) when the
-//   weights fit the GEMM tile (bf16; see blocked_weights).
+//   the GEMM's copies of W_qkv, W_o (and, block only, W1, W2): transposed
+//   to [out][in], tile-blocked when Dims::wblk, else row-major.
+// hsmla_qkv_branches' workspace holds the taps and the W_qkv copy only.
 struct Layout {
   size_t qkv, qkv_hat, o, kv, ksum, part, taps, scores, sel, counts, head_scores;
   size_t bsum, rankp;
   size_t xn, x1, h1, h2, ffn_taps;
-  size_t wq, wo, w1, w2;  // 0 when not made
+  size_t wq, wo, w1, w2;  // 0 when not part of the op
   size_t total;
 };
-
-// Tile-blocked weight copies are made when every projection's weight fits
-// the GEMM tile (output rows a multiple of kGemmTileN, inputs of
-// kGemmTileK); a GEMM then reads them whenever its token count also fits.
-bool blocked_weights(const Dims& D) {
-  return D.bf && (3 * D.C) % hsmla::kGemmTileN == 0 && D.C % hsmla::kGemmTileN == 0 &&
-         D.C % hsmla::kGemmTileK == 0;
-}
 
 Layout layout(const Dims& D, int op) {
   Layout L{};
@@ -145,8 +148,10 @@ Layout layout(const Dims& D, int op) {
   const size_t part_bytes =
       bh * kv_chunks(D.bf, D.B, D.H, D.N) * (kHeadDim * kHeadDim + kHeadDim) * 4;
   const size_t tap_bytes = (size_t)D.kmax * D.kmax * 3 * D.C * 4;
+  const size_t c2 = (size_t)D.C * D.C * D.e;
   if (op == HSMLA_OP_QKV) {
     L.taps = take(tap_bytes);
+    L.wq = take(3 * c2);
   } else if (op == HSMLA_OP_LINEAR) {
     L.part = take(part_bytes);
   } else {
@@ -170,14 +175,11 @@ Layout layout(const Dims& D, int op) {
       L.h2 = take(D.P * 4 * D.C * D.e);
       L.ffn_taps = take((size_t)9 * 4 * D.C * 4);
     }
-    if (blocked_weights(D)) {
-      const size_t c2 = (size_t)D.C * D.C * D.e;
-      L.wq = take(3 * c2);
-      L.wo = take(c2);
-      if (op == HSMLA_OP_BLOCK) {
-        L.w1 = take(4 * c2);
-        L.w2 = take(4 * c2);
-      }
+    L.wq = take(3 * c2);
+    L.wo = take(c2);
+    if (op == HSMLA_OP_BLOCK) {
+      L.w1 = take(4 * c2);
+      L.w2 = take(4 * c2);
     }
   }
   L.total = off;
@@ -233,31 +235,6 @@ hsmla_status check_weights(const hsmla_desc* d, const hsmla_weights* w) {
   return HSMLA_OK;
 }
 
-// Folds the identity and the branch kernels into one tap set.
-hsmla_status fold_qkv_taps(const Dims& D, const hsmla_desc* d,
-                           const hsmla_weights* w, float* taps, hipStream_t s) {
-  HSMLA_TRY(hsmla::launch_dw_taps(D.bf, w->dw, d->branch_k, d->n_branches,
-                                  D.kmax, 3 * D.C, 1, taps, s));
-  return HSMLA_OK;
-}
-
-// Steps 1-2 with caller-provided buffers (plain weights, taps folded into
-// `taps` first).
-hsmla_status run_qkv(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
-                     const void* x, void* qkv, void* qkv_hat, float* taps,
-                     hipStream_t s, Rec& r) {
-  r.mark("qkv_gemm");
-  HSMLA_TRY(hsmla::launch_gemm(D.bf, x, w->w_qkv, nullptr, qkv, (int)D.P,
-                               3 * D.C, D.C, s, hsmla::GemmSite::kQkv));
-  r.mark("dw_taps");
-  hsmla_status st = fold_qkv_taps(D, d, w, taps, s);
-  if (st != HSMLA_OK) return st;
-  r.mark("dwconv_qkv");
-  HSMLA_TRY(hsmla::launch_dwconv(D.bf, qkv, qkv_hat, taps, D.kmax, D.B, D.gh,
-                                 D.gw, 3 * D.C, false, nullptr, D.Bs, s));
-  return HSMLA_OK;
-}
-
 // Workspace pointers of images [b0, b0 + nb): every section is laid out
 // image by image, so a range is an offset into each.
 struct Bufs {
@@ -265,7 +242,7 @@ struct Bufs {
   float *kv, *ksum, *part, *taps, *ftaps, *scores, *hscores, *bsum;
   int32_t *sel, *counts;
   int32_t* rankp;           // top-k partial ranks
-  void *wq, *wo, *w1, *w2;  // tile-blocked weights (shared), or null
+  void *wq, *wo, *w1, *w2;  // the GEMM's weight copies (shared), or null
 };
 
 Bufs bufs_for(const Dims& D, const Layout& L, void* ws, int op, int b0) {
@@ -273,6 +250,11 @@ Bufs bufs_for(const Dims& D, const Layout& L, void* ws, int op, int b0) {
   const size_t H = (size_t)D.H, bb = (size_t)b0;
   const size_t chunks = (size_t)kv_chunks(D.bf, D.B, D.H, D.N);
   Bufs u{};
+  if (op == HSMLA_OP_QKV) {  // taps and the W_qkv copy only
+    u.taps = reinterpret_cast<float*>(at(ws, L.taps));
+    u.wq = at(ws, L.wq);
+    return u;
+  }
   u.qkv = at(ws, L.qkv + bb * n * 3 * c * e);
   u.qkvh = at(ws, L.qkv_hat + bb * n * 3 * c * e);
   u.o = at(ws, L.o + bb * n * c * e);
@@ -299,33 +281,30 @@ Bufs bufs_for(const Dims& D, const Layout& L, void* ws, int op, int b0) {
     u.h2 = at(ws, L.h2 + bb * n * 4 * c * e);
     u.ftaps = reinterpret_cast<float*>(at(ws, L.ffn_taps));  // shared
   }
-  if (L.wq) {
-    u.wq = at(ws, L.wq);
-    u.wo = at(ws, L.wo);
-    if (op == HSMLA_OP_BLOCK) {
-      u.w1 = at(ws, L.w1);
-      u.w2 = at(ws, L.w2);
-    }
+  u.wq = at(ws, L.wq);
+  u.wo = at(ws, L.wo);
+  if (op == HSMLA_OP_BLOCK) {
+    u.w1 = at(ws, L.w1);
+    u.w2 = at(ws, L.w2);
   }
   return u;
 }
 
-// A projection's weights: the tile-blocked copy when the GEMM takes its
-// whole-tile path for this shape, else the caller's row-major weights.
+// A projection's weights for the GEMM: the prepared copy, tile-blocked when
+// Dims::wblk (every GEMM of the call, over any image range, is then whole
+// tiles).
 struct WSel {
   const void* w;
   bool blocked;
 };
-WSel pick_w(const void* plain, const void* blocked, int M, int N, int K) {
-  if (blocked && hsmla::gemm_whole_tiles(M, N, K)) return {blocked, true};
-  return {plain, false};
-}
+WSel wsel(const Dims& D, const void* copy) { return {copy, D.wblk}; }
 
-// One launch before the stages: the folded branch taps (and the FFN's, for
-// the block) and the blocked weight copies.
+// One launch before the stages (or once, by hsmla_prepare): the folded
+// branch taps (and the FFN's, for the block) and the GEMM's weight copies.
+// f == nullptr: the module's operands only; qkv_only: the taps and W_qkv.
 hsmla_status prep(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
                   const hsmla_ffn_weights* f, const Bufs& u, hipStream_t s,
-                  Rec& r) {
+                  Rec& r, bool qkv_only = false) {
   hsmla::TapSpec taps[2];
   int ntaps = 0;
   {
@@ -342,12 +321,13 @@ hsmla_status prep(const Dims& D, const hsmla_desc* d, const hsmla_weights* w,
                                    4 * D.C, 0, u.ftaps};
   hsmla::BlockJob jobs[4];
   int njobs = 0;
-  if (u.wq) {
-    jobs[njobs++] = {w->w_qkv, u.wq, 3 * D.C, D.C, hsmla::kGemmTileN};
-    jobs[njobs++] = {w->w_o, u.wo, D.C, D.C, hsmla::kGemmTileN};
-    if (f && u.w1) {
-      jobs[njobs++] = {f->w1, u.w1, 4 * D.C, D.C, hsmla::kGemmTileN};
-      jobs[njobs++] = {f->w2, u.w2, D.C, 4 * D.C, hsmla::kGemmTileN};
+  const int tr = D.wblk ? hsmla::kGemmTileN : 0;
+  jobs[njobs++] = {w->w_qkv, u.wq, 3 * D.C, D.C, tr};
+  if (!qkv_only) {
+    jobs[njobs++] = {w->w_o, u.wo, D.C, D.C, tr};
+    if (f) {
+      jobs[njobs++] = {f->w1, u.w1, 4 * D.C, D.C, tr};
+      jobs[njobs++] = {f->w2, u.w2, D.C, 4 * D.C, tr};
     }
   }
   r.mark("prep");
@@ -387,7 +367,7 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
   switch (st) {
     case 0: {
       r.mark("qkv_gemm");
-      const WSel q = pick_w(w->w_qkv, u.wq, (int)D.P, 3 * D.C, D.C);
+      const WSel q = wsel(D, u.wq);
       HSMLA_TRY(hsmla::launch_gemm(D.bf, x, q.w, nullptr, u.qkv, (int)D.P, 3 * D.C,
                                    D.C, s, hsmla::GemmSite::kQkv, x_blk, q.blocked));
       return HSMLA_OK;
@@ -529,9 +509,39 @@ hsmla_status hsmla_qkv_branches(const hsmla_desc* desc, const hsmla_weights* w,
   const Layout L = layout(D, HSMLA_OP_QKV);
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
   Rec r;
-  return run_qkv(D, desc, w, x, qkv, qkv_hat,
-                 reinterpret_cast<float*>(at(ws, L.taps)),
-                 static_cast<hipStream_t>(stream), r);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Bufs u = bufs_for(D, L, ws, HSMLA_OP_QKV, 0);
+  if (!D.prepared && (st = prep(D, desc, w, nullptr, u, s, r, true)) != HSMLA_OK)
+    return st;
+  const WSel q = wsel(D, u.wq);
+  HSMLA_TRY(hsmla::launch_gemm(D.bf, x, q.w, nullptr, qkv, (int)D.P, 3 * D.C, D.C, s,
+                               hsmla::GemmSite::kQkv, false, q.blocked));
+  HSMLA_TRY(hsmla::launch_dwconv(D.bf, qkv, qkv_hat, u.taps, D.kmax, D.B, D.gh, D.gw,
+                                 3 * D.C, false, nullptr, D.Bs, s));
+  return HSMLA_OK;
+}
+
+hsmla_status hsmla_prepare(const hsmla_desc* desc, int32_t op,
+                           const hsmla_weights* w, const hsmla_ffn_weights* f,
+                           void* ws, size_t ws_bytes, void* stream) {
+  Dims D;
+  hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (op != HSMLA_OP_QKV && op != HSMLA_OP_FORWARD && op != HSMLA_OP_BLOCK)
+    return HSMLA_ERR_ARG;
+  if (!ws || (op == HSMLA_OP_BLOCK && !f)) return HSMLA_ERR_NULL;
+  if ((st = check_weights(desc, w)) != HSMLA_OK) return st;
+  if (op == HSMLA_OP_BLOCK && (!f->w1 || !f->w2 || !f->dw_ffn)) return HSMLA_ERR_NULL;
+  if (!aligned(ws, 16) ||
+      (op == HSMLA_OP_BLOCK &&
+       (!aligned(f->w1, 16) || !aligned(f->w2, 16) || !aligned(f->dw_ffn, 4))))
+    return HSMLA_ERR_ALIGN;
+  const Layout L = layout(D, op);
+  if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
+  Rec r;
+  const Bufs u = bufs_for(D, L, ws, op, 0);
+  return prep(D, desc, w, op == HSMLA_OP_BLOCK ? f : nullptr, u,
+              static_cast<hipStream_t>(stream), r, op == HSMLA_OP_QKV);
 }
 
 hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
@@ -712,10 +722,10 @@ hsmla_status forward_impl(const hsmla_desc* desc, const hsmla_weights* w,
   const Layout L = layout(D, HSMLA_OP_FORWARD);
   if (ws_bytes < L.total) return HSMLA_ERR_WORKSPACE;
   const Bufs u = bufs_for(D, L, ws, HSMLA_OP_FORWARD, 0);
-  if ((st = prep(D, desc, w, nullptr, u, s, r)) != HSMLA_OK) return st;
+  if (!D.prepared && (st = prep(D, desc, w, nullptr, u, s, r)) != HSMLA_OK) return st;
   if ((st = run_module(D, desc, w, x, u, s, r)) != HSMLA_OK) return st;
   r.mark("out_proj");
-  const WSel wo = pick_w(w->w_o, u.wo, (int)D.P, D.C, D.C);
+  const WSel wo = wsel(D, u.wo);
   HSMLA_TRY(hsmla::launch_gemm(D.bf, u.o, wo.w, nullptr, y, (int)D.P, D.C, D.C, s,
                                hsmla::GemmSite::kOut, false, wo.blocked));
   r.end();
@@ -765,7 +775,7 @@ hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
   // FFN1 writes h1 channel-planar (64-channel planes: each wave's output
   // rows one contiguous run) when the FFN conv can read it so
   const bool h1_planar =
-      h2_blk && ln2_blk && pick_w(f->w1, u.w1, P, 4 * C, C).blocked &&
+      h2_blk && ln2_blk && D.wblk &&
       hsmla::gemm_planar_ok(D.bf, P, 4 * C, C, true, true) &&
       hsmla::dwconv_planar_ok(D.bf, D.B, D.gh, D.gw, 4 * C);
   if (st >= 1 && st <= kModuleStages)
@@ -779,7 +789,7 @@ hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
     case kModuleStages + 1: {
       // x1 = x + O W_o (residual fused into the projection epilogue)
       r.mark("out_proj_residual");
-      const WSel wo = pick_w(w->w_o, u.wo, P, C, C);
+      const WSel wo = wsel(D, u.wo);
       HSMLA_TRY(hsmla::launch_gemm(D.bf, u.o, wo.w, x, u.x1, P, C, C, s,
                                    hsmla::GemmSite::kOut, false, wo.blocked));
       return HSMLA_OK;
@@ -791,7 +801,7 @@ hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
       return HSMLA_OK;
     case kModuleStages + 3: {
       r.mark("ffn1_gemm");
-      const WSel w1 = pick_w(f->w1, u.w1, P, 4 * C, C);
+      const WSel w1 = wsel(D, u.w1);
       HSMLA_TRY(hsmla::launch_gemm(D.bf, u.xn, w1.w, nullptr, u.h1, P, 4 * C, C, s,
                                    hsmla::GemmSite::kFfn1, ln2_blk, w1.blocked, h1_planar));
       return HSMLA_OK;
@@ -805,7 +815,7 @@ hsmla_status block_stage(int st, const Dims& D, const hsmla_desc* desc,
         HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.h1, u.h2, u.ftaps, 3, D.B, D.gh,
                                        D.gw, 4 * C, true, nullptr, 1, s, h2_blk));
       r.mark("ffn2_gemm_residual");
-      const WSel w2 = pick_w(f->w2, u.w2, P, C, 4 * C);
+      const WSel w2 = wsel(D, u.w2);
       HSMLA_TRY(hsmla::launch_gemm(D.bf, u.h2, w2.w, u.x1, out, P, C, 4 * C, s,
                                    hsmla::GemmSite::kFfn2, h2_blk, w2.blocked));
       return HSMLA_OK;
@@ -834,7 +844,7 @@ hsmla_status block_impl(const hsmla_desc* desc, const hsmla_weights* w,
   hsmla_status st = check_block(desc, w, f, x, out, ws, ws_bytes, &D, &L);
   if (st != HSMLA_OK) return st;
   const Bufs u = bufs_for(D, L, ws, HSMLA_OP_BLOCK, 0);
-  if ((st = prep(D, desc, w, f, u, s, r)) != HSMLA_OK) return st;
+  if (!D.prepared && (st = prep(D, desc, w, f, u, s, r)) != HSMLA_OK) return st;
   if ((st = block_range(D, desc, w, f, x, out, u, s, r)) != HSMLA_OK) return st;
   r.end();
   return r.ok ? HSMLA_OK : HSMLA_ERR_HIP;
@@ -856,7 +866,7 @@ hsmla_status block_split_impl(const hsmla_desc* desc, const hsmla_weights* w,
   // float32 chunks the K/V reduction by batch size: one stream keeps the
   // result independent of the split
   const Bufs u0 = bufs_for(D, L, ws, HSMLA_OP_BLOCK, 0);
-  if ((st = prep(D, desc, w, f, u0, s, r)) != HSMLA_OK) return st;
+  if (!D.prepared && (st = prep(D, desc, w, f, u0, s, r)) != HSMLA_OK) return st;
   if (D.B < 2 || !D.bf) return block_range(D, desc, w, f, x, out, u0, s, r);
   HSMLA_TRY(hipEventRecord(fork, s));
   HSMLA_TRY(hipStreamWaitEvent(aux, fork, 0));

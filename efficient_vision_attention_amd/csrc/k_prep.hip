@@ -1,14 +1,16 @@
-// Per-call preparation of constant operands, in one launch: the folded
-// depthwise tap sets and the tile-blocked copies of the projection weights.
+// Preparation of constant operands, in one launch: the folded depthwise tap
+// sets and the projection weights in the layout the GEMM reads.
 //
 // Folded taps (abstract and EX section 2: the identity plus depthwise
 // kernels of several sizes; FT 3.5 block equation for the FFN's 3x3): every
 // branch is linear, so weff[tap][c] = identity (centre tap, when set) + the
 // sum of the branch kernels zero-padded to kmax x kmax, in branch order.
 //
-// Blocked weights: the whole-tile GEMM path reads one K step of one tile as
-// one contiguous block (see launch_gemm); a blocked copy of an [R][K]
-// row-major matrix is a plain permutation of its elements.
+// Weights: a projection y = x . W takes W as [in][out] row-major; the GEMM
+// reads eight consecutive input channels of one output column per lane, so
+// the copy is the transpose [out][in], stored row-major or tile-blocked
+// (one K step of one tile as one contiguous block, see launch_gemm).  Both
+// are plain permutations of the elements.
 #include "common.h"
 #include "kernels.h"
 
@@ -49,15 +51,24 @@ __device__ void fold_tap(const TapSet& ks, int idx) {
   ks.weff[idx] = v;
 }
 
-// one 16-byte chunk (8 bf16) of a row-major [rows][cols] matrix per thread
-__device__ void block_chunk(const BlockJob& j, int idx) {
-  const int cpr = j.cols / 8;
-  const int r = idx / cpr, k = (idx % cpr) * 8;
-  const size_t dst = ((size_t)(r / j.tile_rows) * (j.cols / kGemmTileK) + k / kGemmTileK) *
-                         ((size_t)j.tile_rows * kGemmTileK) +
-                     (size_t)(r % j.tile_rows) * kGemmTileK + k % kGemmTileK;
-  *reinterpret_cast<uint4*>(static_cast<bf16*>(j.dst) + dst) =
-      *reinterpret_cast<const uint4*>(static_cast<const bf16*>(j.src) + (size_t)r * j.cols + k);
+// Eight consecutive input channels k0..k0+7 of output column n of the
+// transposed copy per thread; consecutive threads take consecutive n, so
+// each of the eight source reads is one contiguous run across the wave.
+template <typename T>
+__device__ void weight_chunk(const BlockJob& j, int idx) {
+  const int n = idx % j.rows, k0 = (idx / j.rows) * 8;
+  const T* src = static_cast<const T*>(j.src) + (size_t)k0 * j.rows + n;
+  T v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = src[(size_t)i * j.rows];
+  const size_t dst =
+      j.tile_rows ? ((size_t)(n / j.tile_rows) * (j.cols / kGemmTileK) + k0 / kGemmTileK) *
+                            ((size_t)j.tile_rows * kGemmTileK) +
+                        (size_t)(n % j.tile_rows) * kGemmTileK + k0 % kGemmTileK
+                  : (size_t)n * j.cols + k0;
+  T* d = static_cast<T*>(j.dst) + dst;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) d[i] = v[i];
 }
 
 // Threads [0, tap_end[0]) fold the first tap set, the next range the
@@ -75,7 +86,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   }
   for (int t = 0; t < a.njobs; ++t) {
     if (idx < a.job_end[t]) {
-      block_chunk(a.jobs[t], idx - base);
+      weight_chunk<T>(a.jobs[t], idx - base);
       return;
     }
     base = a.job_end[t];
@@ -86,8 +97,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 
 hipError_t launch_prep(bool bf, const TapSpec* taps, int ntaps,
                        const BlockJob* jobs, int njobs, hipStream_t s) {
-  if (ntaps > kMaxTapSets || njobs > kMaxBlockJobs || (njobs > 0 && !bf))
-    return hipErrorInvalidValue;
+  if (ntaps > kMaxTapSets || njobs > kMaxBlockJobs) return hipErrorInvalidValue;
   PrepArgs a{};
   int total = 0;
   for (int t = 0; t < ntaps; ++t) {
@@ -105,6 +115,9 @@ hipError_t launch_prep(bool bf, const TapSpec* taps, int ntaps,
     a.tap_end[t] = total;
   }
   for (int t = 0; t < njobs; ++t) {
+    if (jobs[t].cols % (jobs[t].tile_rows ? kGemmTileK : 8) ||
+        (jobs[t].tile_rows && (!bf || jobs[t].rows % jobs[t].tile_rows)))
+      return hipErrorInvalidValue;
     a.jobs[t] = jobs[t];
     total += jobs[t].rows * (jobs[t].cols / 8);
     a.job_end[t] = total;

@@ -40,8 +40,12 @@ hipError_t launch_dw_taps(bool bf, const void* const* kernels, const int* ks,
                           int nk, int kmax, int ch, int identity, float* weff,
                           hipStream_t s);
 
-// One launch folding up to two tap sets (as launch_dw_taps) and writing
-// tile-blocked copies of up to four bf16 matrices (see launch_gemm).
+// One launch folding up to two tap sets (as launch_dw_taps) and writing the
+// GEMM's copies of up to four projection weights: src is [cols][rows]
+// row-major ([in][out], y = x . src), dst its transpose [rows][cols] =
+// [out][in], row-major (tile_rows = 0; cols a multiple of 8) or tile-blocked
+// with tile_rows = kGemmTileN (bf16 only; rows a multiple of tile_rows, cols
+// of kGemmTileK).
 struct TapSpec {
   const void* kernels[3];
   int ks[3];
@@ -49,8 +53,8 @@ struct TapSpec {
   float* weff;
 };
 struct BlockJob {
-  const void* src;  // [rows][cols] row-major bf16
-  void* dst;        // tile-blocked copy
+  const void* src;  // [cols][rows] row-major
+  void* dst;        // [rows][cols]: row-major or tile-blocked
   int rows, cols, tile_rows;
 };
 hipError_t launch_prep(bool bf, const TapSpec* taps, int ntaps,

@@ -37,9 +37,8 @@ class DeviceModel:
     soft (the training-time mixture over every block).  weights: dict of float64 numpy
     arrays (w_qkv, w_o, dw list, gate_w, gate_b, optionally gate_dw, and
     for the block ln1_g,
-    ln1_b, ln2_g, ln2_b, w1, dw_ffn, w2), dense weights given [in][out]
-    (y = x @ W); they are stored on the device transposed, as the library
-    expects.
+    ln1_b, ln2_g, ln2_b, w1, dw_ffn, w2), dense weights [in][out]
+    (y = x @ W), the library's layout.
     """
 
     def __init__(self, shape: dict, weights: dict, device="cuda"):
@@ -48,10 +47,9 @@ class DeviceModel:
         self.device = device
         self.desc = H.make_desc(**self.shape)
         dt = self.dtype
-        # dense weights go to the device as [out][in] (x @ W == x @ (W^T)^T)
         self.t = {
-            "w_qkv": to_device(np.asarray(weights["w_qkv"]).T, dt, device),
-            "w_o": to_device(np.asarray(weights["w_o"]).T, dt, device),
+            "w_qkv": to_device(weights["w_qkv"], dt, device),
+            "w_o": to_device(weights["w_o"], dt, device),
             "dw": [to_device(w, dt, device) for w in weights["dw"]],
             "gate_w": to_f32(weights["gate_w"], device),
             "gate_b": to_f32(weights["gate_b"], device),
@@ -65,8 +63,8 @@ class DeviceModel:
         if "w1" in weights:
             for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b"):
                 self.t[k] = to_f32(weights[k], device)
-            self.t["w1"] = to_device(np.asarray(weights["w1"]).T, dt, device)
-            self.t["w2"] = to_device(np.asarray(weights["w2"]).T, dt, device)
+            self.t["w1"] = to_device(weights["w1"], dt, device)
+            self.t["w2"] = to_device(weights["w2"], dt, device)
             self.t["dw_ffn"] = to_device(weights["dw_ffn"], dt, device)
             self.ffn = H.make_ffn_weights(*(self.t[k] for k in (
                 "ln1_g", "ln1_b", "ln2_g", "ln2_b", "w1", "dw_ffn", "w2")))

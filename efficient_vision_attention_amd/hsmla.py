@@ -26,6 +26,7 @@ HSMLA_ROUTE_TOPK, HSMLA_ROUTE_THRESHOLD, HSMLA_ROUTE_HEAD_THRESHOLD, HSMLA_ROUTE
 EXPORTED = (
     "hsmla_workspace_bytes",
     "hsmla_workspace_views",
+    "hsmla_prepare",
     "hsmla_qkv_branches",
     "hsmla_linear_attn",
     "hsmla_gate_select",
@@ -58,6 +59,7 @@ class hsmla_desc(ctypes.Structure):
         ("block", ctypes.c_int32), ("window", ctypes.c_int32),
         ("keep_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("routing", ctypes.c_int32), ("tau", ctypes.c_float),
+        ("prepared", ctypes.c_int32),
     ]
 
 
@@ -106,6 +108,8 @@ def library():
         sigs = {
             "hsmla_workspace_bytes": [P(hsmla_desc), I32, P(SZ)],
             "hsmla_workspace_views": [P(hsmla_desc), I32, VP, P(hsmla_views)],
+            "hsmla_prepare": [P(hsmla_desc), I32, P(hsmla_weights), P(hsmla_ffn_weights),
+                              VP, SZ, VP],
             "hsmla_qkv_branches": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, VP, SZ, VP],
             "hsmla_linear_attn": [P(hsmla_desc), VP, VP, VP, VP, VP, SZ, VP],
             "hsmla_gate_select": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP],
@@ -158,10 +162,11 @@ def _stream():
 
 def make_desc(*, batch, grid_h, grid_w, channels, heads, branches, block,
               window, keep_blocks, dtype, head_dim=32, tau=None, per_head=False,
-              soft=False):
+              soft=False, prepared=False):
     """tau=None: top-k routing (keep_blocks per image); a number: threshold
     routing (every block with score > tau), per head when per_head; soft:
-    the training-time mixture (every block, residual scaled by its score)."""
+    the training-time mixture (every block, residual scaled by its score);
+    prepared: the workspace holds what hsmla_prepare wrote."""
     d = hsmla_desc()
     d.batch, d.grid_h, d.grid_w = batch, grid_h, grid_w
     d.channels, d.heads, d.head_dim = channels, heads, head_dim
@@ -173,6 +178,7 @@ def make_desc(*, batch, grid_h, grid_w, channels, heads, branches, block,
     d.routing = (HSMLA_ROUTE_SOFT if soft else HSMLA_ROUTE_TOPK if tau is None else
                  HSMLA_ROUTE_HEAD_THRESHOLD if per_head else HSMLA_ROUTE_THRESHOLD)
     d.tau = 0.0 if tau is None else float(tau)
+    d.prepared = 1 if prepared else 0
     return d
 
 
@@ -209,6 +215,13 @@ def hsmla_workspace_views(desc, op, ws):
     base = ws.data_ptr()
     return {name: (getattr(v, name) - base) if getattr(v, name) else None
             for name, _ in hsmla_views._fields_}
+
+
+def hsmla_prepare(desc, op, weights, ffn, ws):
+    _check(library().hsmla_prepare(ctypes.byref(desc), op, ctypes.byref(weights),
+                                   ctypes.byref(ffn) if ffn is not None else None,
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream()),
+           "hsmla_prepare")
 
 
 def hsmla_qkv_branches(desc, weights, x, qkv, qkv_hat, ws):

@@ -9,7 +9,7 @@
  *        "Technische Samenvatting".
  *
  * Module computed (FT 3.1-3.3, 3.5, 3.6):
- *   QKV     = X W_qkv^T                                (projection, no bias)
+ *   QKV     = X W_qkv                                  (projection, no bias)
  *   T_hat   = T + sum_s DWConv_{k_s}(T)  for T in Q,K,V (multi-scale branches)
  *   Z, D    = sum_j relu(K_hat_j)^T V_hat_j, sum_j relu(K_hat_j)   (per head)
  *   O_lin   = relu(Q_hat) Z / (relu(Q_hat) . D)           (0 when the sum is 0)
@@ -18,7 +18,7 @@
  *   sel     = the keep_blocks blocks with the largest M_t (ties -> lower t),
  *             or, with threshold routing, every block with M_t > tau
  *   O_i     = O_lin_i + softmax-attn(q_i, K_W, V_W) - lin-local_i  on sel
- *   Y       = O W_o^T
+ *   Y       = O W_o
  *
  * Conventions shared by every entry point:
  *   - Layout: a token grid of grid_h x grid_w tokens, token n = y*grid_w + x.
@@ -39,8 +39,11 @@
  *   - Errors: argument errors are detected on the host before any HIP call
  *     and returned as a negative hsmla_status; nothing is launched then.  A
  *     failed launch returns HSMLA_ERR_HIP.  No exception crosses the ABI.
- *   - Weights of the dense projections are [out][in] row-major (the layout
- *     of torch.nn.Linear.weight) and are applied as y = x . W^T.
+ *   - Weights of the dense projections are [in][out] row-major and are
+ *     applied as y = x . W.  The library keeps its own copy of each in the
+ *     workspace in the layout its matrix-core kernels read (written by a
+ *     preparation launch at the start of every call, or once by
+ *     hsmla_prepare when desc->prepared is set).
  *   - Alignment: activation, weight and workspace pointers must be 16-byte
  *     aligned; float32 parameter and index pointers 4-byte aligned.
  *   - Threading: no mutable global state; calls on different streams may
@@ -111,11 +114,15 @@ typedef struct {
   int32_t dtype;                 /* hsmla_dtype                            */
   int32_t routing;               /* hsmla_routing                          */
   float tau;                     /* threshold of the threshold routings    */
+  int32_t prepared;              /* nonzero: the workspace already holds  */
+                                 /* the operands hsmla_prepare wrote for  */
+                                 /* these weights; the call skips its own */
+                                 /* preparation launch                    */
 } hsmla_desc;
 
 typedef struct {
-  const void* w_qkv;   /* [3C][C]: qkv = x . w_qkv^T                    */
-  const void* w_o;     /* [C][C]:  y = o . w_o^T                        */
+  const void* w_qkv;   /* [C][3C]: qkv = x . w_qkv                      */
+  const void* w_o;     /* [C][C]:  y = o . w_o                          */
   const void* dw[3];   /* branch s: [3C][k_s][k_s] cross-correlation     */
   const float* gate_w; /* [H][3*head_dim]: weights on [q; k; v] means    */
   const float* gate_b; /* [H]                                            */
@@ -126,9 +133,9 @@ typedef struct {
 typedef struct {
   const float* ln1_g; const float* ln1_b; /* [C] LayerNorm before HSMLA */
   const float* ln2_g; const float* ln2_b; /* [C] LayerNorm before FFN   */
-  const void* w1;      /* [4C][C]                                       */
+  const void* w1;      /* [C][4C]: h1 = LN2(x1) . w1                    */
   const void* dw_ffn;  /* [4C][3][3]                                    */
-  const void* w2;      /* [C][4C]                                       */
+  const void* w2;      /* [4C][C]: out = x1 + h2 . w2                   */
 } hsmla_ffn_weights;
 
 /* Pointers into a forward/block workspace, for inspection. */
@@ -156,8 +163,25 @@ hsmla_status hsmla_workspace_bytes(const hsmla_desc* desc, int32_t op,
 hsmla_status hsmla_workspace_views(const hsmla_desc* desc, int32_t op,
                                    void* ws, hsmla_views* views);
 
+/* Writes the operands that depend only on the weights into the workspace
+ * `ws` sized for `op` (HSMLA_OP_QKV, HSMLA_OP_FORWARD or HSMLA_OP_BLOCK;
+ * HSMLA_ERR_ARG otherwise): the identity and depthwise branch kernels folded
+ * into one tap set per channel (abstract, EX section 2; and the FFN's 3x3 of
+ * the FT 3.5 sandwich for the block), and the dense projection weights
+ * transposed, tile-blocked where the shape allows.  These are the same
+ * values every call writes for itself when desc->prepared is 0.  A later
+ * call of the same op with desc->prepared != 0, the same descriptor
+ * otherwise and the same weights, on a stream ordered after this one, then
+ * skips that launch; the weight sections of `ws` must not be written in
+ * between (the views of hsmla_workspace_views never overlap them).  f is
+ * required for HSMLA_OP_BLOCK (its w1, dw_ffn, w2) and ignored otherwise.
+ * Asynchronous on `stream`, like every call. */
+hsmla_status hsmla_prepare(const hsmla_desc* desc, int32_t op,
+                           const hsmla_weights* w, const hsmla_ffn_weights* f,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* Steps 1-2 (FT 3.1 projection; abstract and EX section 2 for the
- * multi-scale depthwise branches): qkv = x W_qkv^T and
+ * multi-scale depthwise branches): qkv = x W_qkv and
  * qkv_hat = qkv + sum_s DWConv_{k_s}(qkv), zero padding (k-1)/2, no bias.
  * x [B][N][C]; qkv, qkv_hat [B][N][3C]; ws sized for HSMLA_OP_QKV. */
 hsmla_status hsmla_qkv_branches(const hsmla_desc* desc,
@@ -264,7 +288,7 @@ hsmla_status hsmla_sparse_softmax_weighted(const hsmla_desc* desc,
                                            const float* weights, void* o,
                                            void* stream);
 
-/* The whole module: y = HSMLA(x) = O W_o^T, steps 1-5 then the output
+/* The whole module: y = HSMLA(x) = O W_o, steps 1-5 then the output
  * projection (FT 3.6 stages 1-5).  x, y [B][N][C]; ws sized for
  * HSMLA_OP_FORWARD; intermediates readable through hsmla_workspace_views.
  * desc->routing picks top-k, threshold, per-head threshold selection or
@@ -277,7 +301,7 @@ hsmla_status hsmla_forward(const hsmla_desc* desc, const hsmla_weights* w,
 /* One block (FT 3.5 block equation, with its depthwise and FFN steps fused
  * into one FFN-DWConv sandwich):
  *   x1  = x + HSMLA(LN1(x))
- *   out = x1 + GELU(DWConv3x3(LN2(x1) W1^T)) W2^T
+ *   out = x1 + GELU(DWConv3x3(LN2(x1) W1)) W2
  * LayerNorm: biased variance, eps 1e-5; GELU: exact erf form.  x, out
  * [B][N][C] (must not overlap); ws sized for HSMLA_OP_BLOCK. */
 hsmla_status hsmla_block_forward(const hsmla_desc* desc,

@@ -225,6 +225,36 @@ def test_stage_argument_errors():
                                    None) == -1
 
 
+@cpu_only
+def test_prepare_argument_errors():
+    lib = H.library()
+    d = _desc()
+    st, need = _ws_bytes(d, H.HSMLA_OP_FORWARD)
+    w = _weights()
+    f = lib.hsmla_prepare
+    assert f(ctypes.byref(d), H.HSMLA_OP_LINEAR, ctypes.byref(w), None, FAKE, need,
+             None) == -7
+    assert f(ctypes.byref(d), 9, ctypes.byref(w), None, FAKE, need, None) == -7
+    assert f(ctypes.byref(d), H.HSMLA_OP_FORWARD, ctypes.byref(w), None, FAKE,
+             need - 1, None) == -5
+    assert f(ctypes.byref(d), H.HSMLA_OP_FORWARD, ctypes.byref(w), None, None,
+             need, None) == -1
+    assert f(ctypes.byref(d), H.HSMLA_OP_FORWARD, ctypes.byref(w), None, FAKE + 4,
+             need, None) == -4
+    assert f(ctypes.byref(d), H.HSMLA_OP_FORWARD, None, None, FAKE, need, None) == -1
+    st, need_b = _ws_bytes(d, H.HSMLA_OP_BLOCK)
+    # the block needs the FFN weights
+    assert f(ctypes.byref(d), H.HSMLA_OP_BLOCK, ctypes.byref(w), None, FAKE, need_b,
+             None) == -1
+    ffn = H.hsmla_ffn_weights()
+    ffn.w1 = ffn.w2 = ffn.dw_ffn = FAKE
+    assert f(ctypes.byref(d), H.HSMLA_OP_BLOCK, ctypes.byref(w), ctypes.byref(ffn),
+             FAKE, need, None) == -5
+    ffn.w2 = FAKE + 8
+    assert f(ctypes.byref(d), H.HSMLA_OP_BLOCK, ctypes.byref(w), ctypes.byref(ffn),
+             FAKE, need_b, None) == -4
+
+
 def test_workspace_views_layout():
     d = _desc()
     st, need = _ws_bytes(d, H.HSMLA_OP_FORWARD)

@@ -7,9 +7,11 @@ import pytest
 import torch
 
 import oracle as O
+from efficient_vision_attention_amd import hsmla as H
+from efficient_vision_attention_amd.device import to_host
 from workloads import WORKLOADS, make_inputs, scaled
 
-from gpu_harness import (Run, assert_close, oracle_kwargs,
+from gpu_harness import (TOL, Run, announce, assert_close, oracle_kwargs,
                          selection_band_check, staged)
 from test_gpu_stages import STAGE_CASES
 
@@ -56,7 +58,6 @@ def test_keep_zero_is_linear_attention(name):
     wl = STAGE_CASES[name]
     inp = make_inputs(wl)
     g = Run(wl, inp, keep_blocks=0).forward()
-    np.testing.assert_array_equal(g["o"], g["o"])  # readable
     ref = _check_module(wl, inp, g, k=0)
     np.testing.assert_array_equal(ref["o"], ref["o_lin"])
 
@@ -126,11 +127,15 @@ def test_window_equal_block_keep_all():
     _check_module(wl, inp, Run(wl, inp).forward())
 
 
-@pytest.mark.parametrize("keep", [0.0, 0.05, 0.5, 1.0])
-def test_block_forward(keep):
-    wl = scaled(STAGE_CASES["block_small"], keep=keep)
-    inp = make_inputs(wl)
-    g = Run(wl, inp).block_forward()
+def _check_block(wl, inp, g):
+    """The block against the oracle end to end (FT 3.5 block equation):
+    every module intermediate and X1 within the bf16 bound, and `out` within
+    the same bound element by element.  An element of `out` outside it is
+    accepted only for its stated cause: the GPU's X1 differs from the
+    oracle's (by its own bf16 rounding, inside the bound) somewhere in that
+    token's 3x3 neighbourhood -- the FFN conv's reach -- and the FFN applied
+    to the GPU's own X1 matches there.  The stage-wise FFN check holds on
+    every element in any case."""
     kw = oracle_kwargs(wl)
     ref = O.hsmla_block_forward(inp["x"], inp, staged=True, **kw)
     kk = kw["keep_blocks"]
@@ -141,10 +146,32 @@ def test_block_forward(keep):
                                     sel=g["sel"][:, :kk], **kw)
     for key in ("qkv", "qkv_hat", "o", "x1"):
         assert_close(g[key], ref[key], wl.dtype, key)
-    # The FFN sandwich is checked on the GPU's own x1 (same inputs on both
-    # sides), so bfloat16 rounding differences of the module stages are not
-    # carried through four more rounded stages.
-    assert_close(g["out"], _oracle_ffn(g["x1"], inp, wl), wl.dtype, "out")
+    assert_close(g["out"], _oracle_ffn(g["x1"], inp, wl), wl.dtype, "out (FFN of GPU x1)")
+    atol, rtol = TOL[wl.dtype]
+    bad = np.abs(g["out"] - ref["out"]) > atol + rtol * np.abs(ref["out"])
+    n_bad = int(bad.sum())
+    if n_bad:
+        B, gh, gw = wl.batch, wl.grid_h, wl.grid_w
+        x1_diff = np.any(g["x1"] != ref["x1"], axis=-1).reshape(B, gh, gw)
+        near = np.zeros_like(x1_diff)
+        pad = np.pad(x1_diff, ((0, 0), (1, 1), (1, 1)))
+        for dy in range(3):
+            for dx in range(3):
+                near |= pad[:, dy:dy + gh, dx:dx + gw]
+        bad_tok = bad.any(axis=-1).reshape(B, gh, gw)
+        assert np.all(near[bad_tok]), (
+            f"{int((bad_tok & ~near).sum())} tokens of out outside the bound "
+            f"with X1 equal to the oracle's in their 3x3 neighbourhood")
+        print(f"[block] {n_bad} of {bad.size} out elements outside the bound, "
+              f"each next to an X1 rounding difference", flush=True)
+    return ref
+
+
+@pytest.mark.parametrize("keep", [0.0, 0.05, 0.5, 1.0])
+def test_block_forward(keep):
+    wl = scaled(STAGE_CASES["block_small"], keep=keep)
+    inp = make_inputs(wl)
+    _check_block(wl, inp, Run(wl, inp).block_forward())
 
 
 def test_block_forward_layernorm_params():
@@ -158,22 +185,12 @@ def test_block_forward_layernorm_params():
     for k in ("ln1", "ln2"):
         inp[k + "_g"] = rng.uniform(0.5, 1.5, C)
         inp[k + "_b"] = rng.normal(0.0, 0.3, C)
-    g = Run(wl, inp).block_forward()
-    kw = oracle_kwargs(wl)
-    ref = O.hsmla_block_forward(inp["x"], inp, staged=True, **kw)
-    kk = kw["keep_blocks"]
-    if not np.array_equal(g["sel"][:, :kk], ref["sel"]):
-        selection_band_check(ref["scores"], g["scores"], ref["sel"],
-                             g["sel"][:, :kk], kk)
-        ref = O.hsmla_block_forward(inp["x"], inp, staged=True,
-                                    sel=g["sel"][:, :kk], **kw)
-    for key in ("qkv", "qkv_hat", "x1"):
-        assert_close(g[key], ref[key], wl.dtype, key)
-    assert_close(g["out"], _oracle_ffn(g["x1"], inp, wl), wl.dtype, "out")
+    _check_block(wl, inp, Run(wl, inp).block_forward())
 
 
 # More block shapes at C = 384: a 256-wide grid (two images, the rows at
-# the top and bottom of each) and a 128-wide one.
+# the top and bottom of each; the planar FFN hidden-tensor path) and a
+# 128-wide one.
 _BLOCK_SHAPES = {
     "w256_b2": scaled(WORKLOADS["block"], name="bs256", batch=2, grid_h=8, grid_w=256,
                       keep=0.25),
@@ -187,8 +204,26 @@ def test_block_forward_shapes(name):
     wl = _BLOCK_SHAPES[name]
     inp = make_inputs(wl)
     print(f"[case] block forward {name}", flush=True)
-    g = Run(wl, inp).block_forward()
-    assert_close(g["out"], _oracle_ffn(g["x1"], inp, wl), wl.dtype, "out")
+    _check_block(wl, inp, Run(wl, inp).block_forward())
+
+
+def test_block_forward_prepared_weights():
+    """hsmla_prepare once, then blocks with desc.prepared: bit for bit the
+    output of the block that prepares its own operands, twice in a row."""
+    wl = _BLOCK_SHAPES["w256_b2"]
+    inp = make_inputs(wl)
+    r = Run(wl, inp)
+    ref = r.block_forward()
+    m = r.model
+    ws = m.workspace(H.HSMLA_OP_BLOCK)
+    announce("hsmla_prepare + hsmla_block_forward(prepared) w256_b2")
+    H.hsmla_prepare(m.desc, H.HSMLA_OP_BLOCK, m.weights, m.ffn, ws)
+    d = H.make_desc(**dict(m.shape, prepared=True))
+    for _ in range(2):
+        out = m.act()
+        H.hsmla_block_forward(d, m.weights, m.ffn, r.x, out, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(out), ref["out"])
 
 
 def _oracle_ffn(x1, inp, wl):
@@ -197,6 +232,17 @@ def _oracle_ffn(x1, inp, wl):
     h1 = r(xn2 @ inp["w1"])
     h2 = r(O.gelu(O.dwconv_same(h1, inp["dw_ffn"], wl.grid_h, wl.grid_w)))
     return r(x1 + h2 @ inp["w2"])
+
+
+@pytest.mark.parametrize("block,window,gh,gw", [(12, 16, 24, 36), (16, 20, 32, 48)])
+def test_forward_bf16_large_blocks(block, window, gh, gw):
+    """bf16 blocks of more than 128 tokens (144 and 256) take the
+    refinement's general kernel (one thread per query)."""
+    wl = scaled(WORKLOADS["street"], name=f"bf16_block{block}", batch=2, grid_h=gh,
+                grid_w=gw, channels=64, heads=2, block=block, window=window, keep=0.34)
+    inp = make_inputs(wl)
+    assert wl.keep_blocks >= 2
+    _check_module(wl, inp, Run(wl, inp).forward())
 
 
 def test_block_forward_f32():

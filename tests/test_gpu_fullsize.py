@@ -26,6 +26,24 @@ def _rows(n, count):
     return np.sort(RNG.choice(n, size=min(n, count), replace=False))
 
 
+def _border_tokens(gh, gw, count):
+    """The four corners plus tokens drawn from the two outermost rows and
+    columns on each side (the 5x5 and 7x7 branches' zero padding reaches
+    three tokens in)."""
+    toks = {0, gw - 1, (gh - 1) * gw, gh * gw - 1}
+    for _ in range(count):
+        side = RNG.integers(4)
+        depth = int(RNG.integers(3))
+        if side < 2:  # top or bottom rows
+            y = depth if side == 0 else gh - 1 - depth
+            x = int(RNG.integers(gw))
+        else:
+            x = depth if side == 2 else gw - 1 - depth
+            y = int(RNG.integers(gh))
+        toks.add(y * gw + x)
+    return np.array(sorted(toks))
+
+
 def _sampled_branches(qkv, kernels, gh, gw, b, tokens):
     """qkv + sum of depthwise branches at the given tokens of image b, from
     zero-padded crops around each token (same result as the full grid)."""
@@ -55,7 +73,7 @@ def _check_module_fullsize(wl, inp, g, tau=None):
                      f"qkv image {b}")
     # S2 on sampled tokens (GPU qkv in)
     for b in range(B):
-        toks = _rows(N, 96)
+        toks = np.union1d(_rows(N, 96), _border_tokens(wl.grid_h, wl.grid_w, 64))
         ref = rnd(_sampled_branches(g["qkv"], inp["dw"], wl.grid_h, wl.grid_w, b, toks))
         assert_close(g["qkv_hat"][b, toks], ref, "bf16", f"qkv_hat image {b}")
     # S3a over everything (GPU qkv_hat in)
