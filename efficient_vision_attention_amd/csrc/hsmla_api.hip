@@ -9,7 +9,17 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
+
+// Device memory of hsmla_linear_attn_noalloc: the K/V-state chunk partials
+// of callers that cannot allocate.  Each GPU holds its own copy of this
+// array from the library's load until the process ends; host code must use
+// the per-device address hipGetSymbolAddress returns (scratch_address), not
+// the array's name.
+static constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -459,6 +469,7 @@ const char* hsmla_status_string(int32_t status) {
     case HSMLA_ERR_WORKSPACE: return "workspace too small";
     case HSMLA_ERR_HIP: return "HIP launch failed";
     case HSMLA_ERR_ARG: return "invalid argument";
+    case HSMLA_ERR_SCRATCH: return "sizes exceed the allocation-free scratch";
     default: return "unknown status";
   }
 }
@@ -542,6 +553,57 @@ hsmla_status hsmla_prepare(const hsmla_desc* desc, int32_t op,
   const Bufs u = bufs_for(D, L, ws, op, 0);
   return prep(D, desc, w, op == HSMLA_OP_BLOCK ? f : nullptr, u,
               static_cast<hipStream_t>(stream), r, op == HSMLA_OP_QKV);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // per device, set once
+
+// The current device's address of `scratch`, looked up on the first call
+// on that device (with it current) and kept.
+hsmla_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+    return HSMLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return HSMLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HSMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hsmla_status hsmla_linear_attn_noalloc(const hsmla_desc* desc, const void* qkv_hat,
+                                       void* o, float* kv, float* ksum,
+                                       void* stream) {
+  Dims D;
+  const hsmla_status st = check_desc(desc, &D);
+  if (st != HSMLA_OK) return st;
+  if (!qkv_hat || !o || !kv || !ksum) return HSMLA_ERR_NULL;
+  if (!aligned(qkv_hat, 16) || !aligned(o, 16) || !aligned(kv, 4) || !aligned(ksum, 4))
+    return HSMLA_ERR_ALIGN;
+  // the chunk partials are the only scratch; every entry the combine reads
+  // is written first by the partial launch, so nothing needs clearing
+  if (layout(D, HSMLA_OP_LINEAR).total > kScratchBytes) return HSMLA_ERR_SCRATCH;
+  void* part = nullptr;
+  const hsmla_status sa = scratch_address(&part);
+  if (sa != HSMLA_OK) return sa;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HSMLA_TRY(hsmla::launch_kv_state(D.bf, qkv_hat, kv, ksum, static_cast<float*>(part),
+                                   D.B, D.N, D.H, s));
+  return hip_status(
+      hsmla::launch_lin_apply(D.bf, qkv_hat, kv, ksum, o, D.B, D.N, D.H, s));
 }
 
 hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,

@@ -19,7 +19,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhsmla.s
 HSMLA_F32, HSMLA_BF16 = 0, 1
 HSMLA_OP_QKV, HSMLA_OP_LINEAR, HSMLA_OP_FORWARD, HSMLA_OP_BLOCK = 0, 1, 2, 3
 (HSMLA_OK, HSMLA_ERR_NULL, HSMLA_ERR_SHAPE, HSMLA_ERR_DTYPE, HSMLA_ERR_ALIGN,
- HSMLA_ERR_WORKSPACE, HSMLA_ERR_HIP, HSMLA_ERR_ARG) = 0, -1, -2, -3, -4, -5, -6, -7
+ HSMLA_ERR_WORKSPACE, HSMLA_ERR_HIP, HSMLA_ERR_ARG,
+ HSMLA_ERR_SCRATCH) = 0, -1, -2, -3, -4, -5, -6, -7, -8
 HSMLA_ROUTE_TOPK, HSMLA_ROUTE_THRESHOLD, HSMLA_ROUTE_HEAD_THRESHOLD, HSMLA_ROUTE_SOFT = 0, 1, 2, 3
 
 # Every symbol include/hsmla.h declares.
@@ -29,6 +30,7 @@ EXPORTED = (
     "hsmla_prepare",
     "hsmla_qkv_branches",
     "hsmla_linear_attn",
+    "hsmla_linear_attn_noalloc",
     "hsmla_gate_select",
     "hsmla_gate_threshold",
     "hsmla_gate_head_threshold",
@@ -112,6 +114,7 @@ def library():
                               VP, SZ, VP],
             "hsmla_qkv_branches": [P(hsmla_desc), P(hsmla_weights), VP, VP, VP, VP, SZ, VP],
             "hsmla_linear_attn": [P(hsmla_desc), VP, VP, VP, VP, VP, SZ, VP],
+            "hsmla_linear_attn_noalloc": [P(hsmla_desc), VP, VP, VP, VP, VP],
             "hsmla_gate_select": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP],
             "hsmla_gate_threshold": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP, VP],
             "hsmla_gate_head_threshold": [P(hsmla_desc), VP, VP, VP, VP, VP, VP, VP, VP, VP],
@@ -236,6 +239,13 @@ def hsmla_linear_attn(desc, qkv_hat, o, kv, ksum, ws):
                                        _ptr(kv), _ptr(ksum), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream()),
            "hsmla_linear_attn")
+
+
+def hsmla_linear_attn_noalloc(desc, qkv_hat, o, kv, ksum):
+    _check(library().hsmla_linear_attn_noalloc(ctypes.byref(desc), _ptr(qkv_hat),
+                                               _ptr(o), _ptr(kv), _ptr(ksum),
+                                               _stream()),
+           "hsmla_linear_attn_noalloc")
 
 
 def hsmla_gate_select(desc, qkv_hat, gate_w, gate_b, scores_in, scores_out, sel,

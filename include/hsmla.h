@@ -74,7 +74,9 @@ typedef enum {
   HSMLA_ERR_ALIGN = -4,     /* a pointer is not aligned as required        */
   HSMLA_ERR_WORKSPACE = -5, /* workspace smaller than hsmla_workspace_bytes */
   HSMLA_ERR_HIP = -6,       /* a kernel launch failed                      */
-  HSMLA_ERR_ARG = -7        /* other invalid argument (e.g. unknown op)    */
+  HSMLA_ERR_ARG = -7,       /* other invalid argument (e.g. unknown op)    */
+  HSMLA_ERR_SCRATCH = -8    /* sizes exceed hsmla_linear_attn_noalloc's    */
+                            /* static scratch                              */
 } hsmla_status;
 
 typedef enum { HSMLA_F32 = 0, HSMLA_BF16 = 1 } hsmla_dtype;
@@ -198,6 +200,23 @@ hsmla_status hsmla_qkv_branches(const hsmla_desc* desc,
 hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
                                void* o, float* kv, float* ksum, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* hsmla_linear_attn for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results, bit for bit, with the chunk
+ * partials of the K/V-state reduction in a static device array of the
+ * library (16 MiB per GPU, held from the library's load until the process
+ * ends) instead of a caller workspace.  The call allocates nothing.  Sizes
+ * whose partials exceed the array (hsmla_workspace_bytes(desc,
+ * HSMLA_OP_LINEAR) > 16 MiB; e.g. bf16 batch * heads * ceil(N / 512) above
+ * 3971) return HSMLA_ERR_SCRATCH before any launch.  Every call on one GPU
+ * uses that GPU's one array: calls that can overlap on a GPU (different
+ * streams, or other threads) race and must be serialised by the caller.
+ * The first call on each device looks up the array's address with that
+ * device current (a HIP runtime query, no allocation). */
+hsmla_status hsmla_linear_attn_noalloc(const hsmla_desc* desc, const void* qkv_hat,
+                                       void* o, float* kv, float* ksum,
+                                       void* stream);
 
 /* Step 4, block gate and selection (FT 3.2 head-level score and block-level
  * aggregation; gate shared by all heads per EX section 2).  With

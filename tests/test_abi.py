@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert H.status_string(code)
     assert H.status_string(-99) == "unknown status"
 
