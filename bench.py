@@ -4,18 +4,27 @@
 Workload: 2 images of 128 x 256 tokens, C = 384 (12 heads of 32), bf16,
 identity + 3x3 + 5x5 depthwise branches, 8 x 8 blocks, 16 x 16 softmax
 windows, keep ratio 10% (52 of 512 blocks per image), wrapped in the LN /
-FFN-DWConv block.  One step = one call of hsmla_block_forward over the batch
-on one stream (--streams 2: hsmla_block_forward_split, the two images on two
-streams), i.e. every kernel of the path; the other mode is timed beside it.  Inputs are seeded synthetic data
+FFN-DWConv block.  One step = one call of hsmla_block_forward over the
+batch on one stream (--streams 2: hsmla_block_forward_split, the two
+images on two streams), i.e. every kernel of the path, with the weights'
+GEMM layouts and folded taps written once by hsmla_prepare (the call
+without it is timed beside).  Inputs are seeded synthetic data
 (street-scene-like smooth field plus noise) already resident in HBM.
+Before the warm-up steps the block runs back to back for 200 ms so the
+clocks have left their idle state.
 
-Prints one JSON line: tokens/s, the per-kernel breakdown from HIP events
-recorded between the launches of the step, the roofline of the dominant
-kernel, a keep-ratio sweep with two threshold-routing points, per-head
-routing, the training-time mixture forward and the exact-gate / three-branch
-variant, and the CPU oracle timed on a bounded crop.
+Prints one JSON line: tokens/s; per-kernel durations from HIP events
+recorded between the launches of the step, each with the fraction of the
+roofline that bounds it (the refinement also against the union of its
+windows' bytes); the dominant kernel's roofline; achievable-peak probes (a
+1 GiB device copy, a large library GEMM); the street, CT, pathology and
+tiny workloads' module forward (tokens/s, per-kernel fractions, and the
+oracle on a crop); a keep-ratio sweep with two threshold-routing points,
+per-head routing, the training-time mixture forward and the exact-gate /
+three-branch variant; and the CPU oracle timed on a bounded crop.
 
-    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-configs]
+                    [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -52,12 +61,12 @@ def parse():
                          "batch split over two streams "
                          "(hsmla_block_forward_split)")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the street / CT / pathology / tiny module runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="first copy 1 GiB with a plain device copy (a known "
-                         "byte count for calibrating HBM traffic counters)")
-    ap.add_argument("--cpu-rows", type=int, default=128,
-                    help="token rows of the crop the CPU oracle is timed on")
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="token rows of the one-image crop the CPU oracle is "
+                         "timed on")
     return ap.parse_args()
 
 
@@ -161,20 +170,54 @@ def algorithmic_work(name, wl, sel):
     raise KeyError(name)
 
 
-def roofline_entry(name, wl, sel, avg_ms):
-    by, fl = algorithmic_work(name, wl, sel)
+MFMA_SITES = ("qkv_gemm", "out_proj", "out_proj_residual", "ffn1_gemm",
+              "ffn2_gemm_residual", "sparse_softmax")
+
+
+def union_window_bytes(wl, sel):
+    """S5's minimum HBM bytes: every token of the union of the selected
+    blocks' clipped windows read once as raw and hatted K and V (4 C
+    elements), and every selected token's q, q^ read and o read and written
+    (4 C elements), per image; the no-reuse per-window sum is
+    algorithmic_work's figure."""
+    e = 2 if wl.dtype == "bf16" else 4
+    C, Bs, nbc = wl.channels, wl.block, wl.grid_w // wl.block
+    p = (wl.window - Bs) // 2
+    sel = np.asarray(sel).reshape(wl.batch, -1)
+    total = 0
+    for b in range(wl.batch):
+        cover = np.zeros((wl.grid_h, wl.grid_w), dtype=bool)
+        for t in sel[b].tolist():
+            if t < 0:
+                continue
+            r0, c0 = (t // nbc) * Bs, (t % nbc) * Bs
+            cover[max(0, r0 - p):r0 + Bs + p, max(0, c0 - p):c0 + Bs + p] = True
+        q_tokens = int(np.sum(sel[b] >= 0)) * Bs * Bs
+        total += (int(cover.sum()) * 4 * C + q_tokens * 4 * C) * e
+    return total
+
+
+def roofline_entry(name, wl, sel, avg_ms, by=None):
+    """Fraction of the roofline that bounds kernel `name`: its algorithmic
+    bytes (or `by`) over the HBM peak, or its flops over the bf16 MFMA peak
+    when that takes longer (the dense contractions and the refinement)."""
+    by0, fl = algorithmic_work(name, wl, sel)
+    by = by0 if by is None else by
     t_hbm = by / (HBM_PEAK_GBS * 1e9)
     t_mfma = fl / (MFMA_BF16_TFLOPS * 1e12)
     sec = avg_ms * 1e-3
-    if name in ("qkv_gemm", "out_proj", "out_proj_residual", "ffn1_gemm",
-                "ffn2_gemm_residual", "sparse_softmax") and t_mfma > t_hbm:
+    if name in MFMA_SITES and t_mfma > t_hbm:
         ach = fl / sec / 1e12
         return dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_TFLOPS,
                     unit="TFLOP/s", frac=round(ach / MFMA_BF16_TFLOPS, 4),
                     traffic=None)
     ach = by / sec / 1e9
-    return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
-                unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+    out = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
+               unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+    if name in MFMA_SITES and fl:
+        # matrix-core use at the same duration (flops / time / peak)
+        out["mfma_frac"] = round(fl / sec / 1e12 / MFMA_BF16_TFLOPS, 4)
+    return out
 
 
 def measured_traffic(launch):
@@ -210,29 +253,81 @@ def measured_traffic(launch):
 # CPU oracle baseline (bounded crop of the same workload)
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, rows):
-    import oracle as O  # test infrastructure, timed here as a baseline only
-    from workloads import make_inputs, scaled
-    crop = scaled(wl, grid_h=rows)
-    inp = make_inputs(crop)
-    t0 = time.perf_counter()
-    O.hsmla_block_forward(inp["x"], inp, staged=True, **crop.kwargs())
-    dt = time.perf_counter() - t0
+def _blas_threads():
     try:
         import threadpoolctl
-        cores = max(i["num_threads"] for i in threadpoolctl.threadpool_info())
+        return max(i["num_threads"] for i in threadpoolctl.threadpool_info())
     except Exception:
-        cores = os.cpu_count()
+        return os.cpu_count()
+
+
+def cpu_baseline(wl, rows, images=1, runs=3, forward=False):
+    """The CPU oracle as it stands, on a crop of `images` images of `rows`
+    token rows of the workload: one warm-up, then `runs` timed runs (one if
+    a run takes over 60 s), median."""
+    import oracle as O  # test infrastructure, timed here as a baseline only
+    from workloads import make_inputs, scaled
+    crop = scaled(wl, batch=min(images, wl.batch), grid_h=min(rows, wl.grid_h))
+    inp = make_inputs(crop)
+    fn = O.hsmla_forward if forward else O.hsmla_block_forward
+    staged = crop.dtype == "bf16"
+    times = []
+    for i in range(runs + 1):
+        t0 = time.perf_counter()
+        fn(inp["x"], inp, staged=staged, **crop.kwargs())
+        times.append(time.perf_counter() - t0)
+        if times[-1] > 60.0:
+            break
+    timed = times[1:] or times
+    dt = float(np.median(timed))
+    what = "module forward" if forward else "block forward"
     return dict(value=round(crop.batch * crop.tokens / dt, 1), unit="tokens/s",
-                cores=cores,
+                cores=_blas_threads(), os_cpu_count=os.cpu_count(),
                 kind="oracle",
-                sample=(f"{crop.batch} images of {rows}x{wl.grid_w} tokens "
+                sample=(f"{crop.batch} image(s) of {crop.grid_h}x{crop.grid_w} tokens "
                         f"({crop.batch * crop.tokens} tokens, keep {crop.keep_blocks} of "
-                        f"{crop.num_blocks} blocks), float64 bf16-staged block "
-                        f"forward, one run of {dt:.1f} s"))
+                        f"{crop.num_blocks} blocks per image), float64 "
+                        f"{'bf16-staged ' if staged else ''}{what}, median of "
+                        f"{len(timed)} run(s) after a warm-up: {dt:.2f} s"))
 
 
 # ---------------------------------------------------------------------------
+
+def probes(torch):
+    """Achievable peaks on this machine: a plain 1 GiB device copy (read + write
+    bytes / time) and a large bf16 library GEMM (hipBLASLt through torch)."""
+    out = {}
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 10
+    out["copy_1GiB_gbs"] = round(2 * src.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    n = 8192
+    x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    w = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        y = x @ w
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(10):
+        y = x @ w
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 10
+    out["gemm_bf16_8192_tflops"] = round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    del x, w, y
+    torch.cuda.empty_cache()
+    return out
+
 
 def main():
     args = parse()
@@ -249,13 +344,7 @@ def main():
     from workloads import WORKLOADS, keep_blocks_for, make_inputs, scaled
 
     torch.cuda.set_device(0)
-    if args.copy_probe:
-        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    probe = probes(torch)
     base = scaled(WORKLOADS["block"], keep=args.keep,
                   branches=tuple(int(k) for k in args.branches.split(",") if k),
                   gate_conv=args.gate_conv)
@@ -268,90 +357,185 @@ def main():
                     block=wl.block, window=wl.window, keep_blocks=wl.keep_blocks,
                     dtype=wl.dtype, tau=tau, per_head=per_head, soft=soft)
 
-    def time_steps(model, fn, steps, warmup):
-        ws = model.workspace(H.HSMLA_OP_BLOCK)
-        out = model.act()
+    class Bound:
+        """A model with its workspace; `prepared` runs hsmla_prepare once
+        and calls with desc.prepared (the weight-only operands are then not
+        rewritten by every call)."""
+
+        def __init__(self, model, op, prepared):
+            self.m, self.op = model, op
+            self.ws = model.workspace(op)
+            self.out = model.act()
+            self.desc = model.desc
+            if prepared:
+                H.hsmla_prepare(model.desc, op, model.weights,
+                                model.ffn if op == H.HSMLA_OP_BLOCK else None, self.ws)
+                self.desc = H.make_desc(**dict(model.shape, prepared=True))
+
+        def block(self, xx):
+            H.hsmla_block_forward(self.desc, self.m.weights, self.m.ffn, xx, self.out,
+                                  self.ws)
+
+        def block_split(self, xx, two):
+            H.hsmla_block_forward_split(self.desc, self.m.weights, self.m.ffn, xx,
+                                        self.out, self.ws, two)
+
+        def forward(self, xx):
+            H.hsmla_forward(self.desc, self.m.weights, xx, self.out, self.ws)
+
+    def spin_up(fn, ms=200.0):
+        """Back-to-back untimed steps for `ms` of wall time, so that the
+        clocks have left their idle state before warm-up and timing (the
+        steps right after the GPU idled for a while ran about 10% slower)."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+
+    def time_steps(fn, steps, warmup):
         for _ in range(warmup):
-            fn(model, ws, out)
+            fn()
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record()
         for _ in range(steps):
-            fn(model, ws, out)
+            fn()
         end.record()
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / steps, ws
+        return start.elapsed_time(end) / steps
+
+    hev = HipEvents()
+
+    def per_kernel(bound, xx, wl, sel, steps, warmup, block=True):
+        """Average duration of every launch of one step, from HIP events
+        recorded on the launch stream between the launches (the steps run
+        back to back; the events are read after the last)."""
+        def timed(evs):
+            if block:
+                return H.hsmla_block_forward_timed(bound.desc, bound.m.weights,
+                                                   bound.m.ffn, xx, bound.out,
+                                                   bound.ws, evs)
+            return H.hsmla_forward_timed(bound.desc, bound.m.weights, xx,
+                                         bound.out, bound.ws, evs)
+        probe_ev = hev.create(40)
+        names = timed(probe_ev)
+        L = len(names)
+        evsets = [hev.create(L) for _ in range(steps)]
+        for _ in range(warmup):
+            timed(probe_ev)
+        for i in range(steps):
+            timed(evsets[i])
+        torch.cuda.synchronize()
+        per = {}
+        for evs in evsets:
+            for j in range(L - 1):
+                per.setdefault(names[j], []).append(hev.elapsed_ms(evs[j], evs[j + 1]))
+        hev.destroy(probe_ev)
+        for evs in evsets:
+            hev.destroy(evs)
+        kernels = {}
+        for n, v in per.items():
+            avg = float(np.mean(v))
+            by, fl = algorithmic_work(n, wl, sel)
+            k = dict(avg_us=round(avg * 1e3, 2), bytes=int(by), flops=int(fl))
+            if by or fl:
+                k["roofline"] = roofline_entry(n, wl, sel, avg)
+            if n == "sparse_softmax":
+                ub = union_window_bytes(wl, sel)
+                k["union_bytes"] = int(ub)
+                k["roofline_union"] = roofline_entry(n, wl, sel, avg, by=ub)
+            kernels[n] = k
+        return kernels
 
     two = H.SplitStreams()
-    split = two if args.streams == 2 else None
-
-    def one_stream_step(m, ws, out):
-        H.hsmla_block_forward(m.desc, m.weights, m.ffn, x, out, ws)
-
-    def two_stream_step(m, ws, out):
-        H.hsmla_block_forward_split(m.desc, m.weights, m.ffn, x, out, ws, two)
-
-    def block_step(m, ws, out):
-        if split is None:
-            H.hsmla_block_forward(m.desc, m.weights, m.ffn, x, out, ws)
-        else:
-            H.hsmla_block_forward_split(m.desc, m.weights, m.ffn, x, out, ws, split)
-
-    def module_step(m, ws, out):
-        H.hsmla_forward(m.desc, m.weights, x, out, ws)
-
     model = DeviceModel(shape(base), inp)
-    ms, ws = time_steps(model, block_step, args.steps, args.warmup)
-    ms_alt = time_steps(model, one_stream_step if split is not None else
-                        two_stream_step, args.steps, args.warmup)[0]
+    head = Bound(model, H.HSMLA_OP_BLOCK, prepared=True)
+    plain = Bound(model, H.HSMLA_OP_BLOCK, prepared=False)
+    spin_up(lambda: head.block(x))
+    if args.streams == 2:
+        ms = time_steps(lambda: head.block_split(x, two), args.steps, args.warmup)
+        ms_alt = time_steps(lambda: head.block(x), args.steps, args.warmup)
+    else:
+        ms = time_steps(lambda: head.block(x), args.steps, args.warmup)
+        ms_alt = time_steps(lambda: head.block_split(x, two), args.steps, args.warmup)
+    ms_plain = time_steps(lambda: plain.block(x), args.steps, args.warmup)
     tokens = base.batch * base.tokens
-    base_views = model.views(H.HSMLA_OP_BLOCK, ws)
+    head.block(x)
+    torch.cuda.synchronize()
+    spin_up(lambda: head.block(x), 50.0)
+    base_views = model.views(H.HSMLA_OP_BLOCK, head.ws)
     sel = base_views["sel"].cpu().numpy()
     base_scores = base_views["scores"].cpu().numpy()
-
-    # per-kernel durations from events recorded between the launches
-    hev = HipEvents()
-    evs = hev.create(32)
-    out = model.act()
-    per = {}
-    names = None
-    for i in range(args.warmup + args.steps):
-        names = H.hsmla_block_forward_timed(model.desc, model.weights, model.ffn,
-                                            x, out, ws, evs)
-        if i < args.warmup:
-            continue
-        hev.sync(evs[len(names) - 1])
-        for j in range(len(names) - 1):
-            per.setdefault(names[j], []).append(hev.elapsed_ms(evs[j], evs[j + 1]))
-    torch.cuda.synchronize()
-    hev.destroy(evs)
-    kernels = {}
-    for n, v in per.items():
-        avg = float(np.mean(v))
-        by, fl = algorithmic_work(n, base, sel)
-        kernels[n] = dict(avg_us=round(avg * 1e3, 2), bytes=int(by), flops=int(fl),
-                          gbs=round(by / (avg * 1e-3) / 1e9, 1) if by else None)
+    kernels = per_kernel(head, x, base, sel, args.steps, args.warmup)
+    prep_us = per_kernel(plain, x, base, sel, 5, 2)["prep"]["avg_us"]
     dominant = max(kernels, key=lambda n: kernels[n]["avg_us"])
-    roof = roofline_entry(dominant, base, sel, kernels[dominant]["avg_us"] * 1e-3)
+    roof = dict(kernels[dominant]["roofline"])
     roof["kernel"] = dominant
     roof["traffic"] = measured_traffic(dominant)
     by, fl = algorithmic_work(dominant, base, sel)
     roof["work_per_launch"] = {"bytes": int(by), "flops": int(fl)}
+    # the k-th / (k+1)-th score gap per image (the margin of the selection)
+    gaps = []
+    for b in range(base.batch):
+        srt = np.sort(base_scores[b].astype(np.float64))[::-1]
+        k = base.keep_blocks
+        gaps.append(float(srt[k - 1] - srt[k]) if 0 < k < srt.size else None)
+
+    # the other workloads: the module forward (prepared weights) per config
+    configs = []
+    crops = {"tiny": (16, 1), "street": (64, 1), "ct": (64, 1), "pathology": (32, 1)}
+    for name in () if args.no_configs else ("tiny", "street", "ct", "pathology"):
+        wl = WORKLOADS[name]
+        winp = make_inputs(wl)
+        wx = to_device(winp["x"], wl.dtype)
+        bd = Bound(DeviceModel(shape(wl), winp), H.HSMLA_OP_FORWARD, prepared=True)
+        spin_up(lambda: bd.forward(wx), 100.0)
+        msf = time_steps(lambda: bd.forward(wx), args.steps, args.warmup)
+        bd.forward(wx)
+        torch.cuda.synchronize()
+        wsel = bd.m.views(H.HSMLA_OP_FORWARD, bd.ws)["sel"].cpu().numpy()
+        entry = dict(workload=name, batch=wl.batch, grid=[wl.grid_h, wl.grid_w],
+                     tokens=wl.batch * wl.tokens, channels=wl.channels,
+                     heads=wl.heads, dtype=wl.dtype, block=wl.block,
+                     window=wl.window, keep=wl.keep, keep_blocks=wl.keep_blocks,
+                     ms_per_forward=round(msf, 4))
+        if name == "tiny":
+            entry["latency_us"] = round(msf * 1e3, 2)  # launch-bound: latency only
+        else:
+            entry["tokens_per_s"] = round(wl.batch * wl.tokens / (msf * 1e-3), 1)
+            entry["kernels"] = per_kernel(bd, wx, wl, wsel, args.steps, args.warmup,
+                                          block=False)
+        if not args.no_cpu_baseline:
+            rows, imgs = crops[name]
+            entry["cpu_baseline"] = cpu_baseline(wl, rows, imgs, forward=True)
+        configs.append(entry)
+        del bd
 
     sweep = []
     if not args.no_sweep:
+        n_sw = max(10, args.steps // 2)
         for r in (0.0, 0.05, 0.10, 0.25, 0.50):
             wl = scaled(base, keep=r)
             m = DeviceModel(shape(wl), inp)
-            ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 10)
-            ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
+            bb = Bound(m, H.HSMLA_OP_BLOCK, prepared=True)
+            spin_up(lambda: bb.block(x), 50.0)
+            ms_b = time_steps(lambda: bb.block(x), n_sw, 10)
+            bf = Bound(m, H.HSMLA_OP_FORWARD, prepared=True)
+            ms_m = time_steps(lambda: bf.forward(x), n_sw, 10)
+            bb.block(x)
+            torch.cuda.synchronize()
+            s_sel = m.views(H.HSMLA_OP_BLOCK, bb.ws)["sel"].cpu().numpy()
+            sp = per_kernel(bb, x, wl, s_sel, 5, 2).get("sparse_softmax")
             sweep.append(dict(keep=r, keep_blocks=keep_blocks_for(r, wl.num_blocks),
                               block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
                               block_ms=round(ms_b, 4),
                               module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
-                              module_ms=round(ms_m, 4)))
-            del m
+                              module_ms=round(ms_m, 4),
+                              sparse_softmax=sp))
+            del m, bb, bf
         # threshold routing (blocks with score > tau), tau placed between two
         # adjacent scores of the run above at the given quantile
         uniq = np.unique(base_scores.astype(np.float32))
@@ -359,30 +543,36 @@ def main():
             i = min(int(q * (uniq.size - 1)), uniq.size - 2)
             tau = float(np.float32((np.float64(uniq[i]) + np.float64(uniq[i + 1])) / 2))
             m = DeviceModel(shape(base, tau=tau), inp)
-            ms_b, ws_t = time_steps(m, block_step, max(10, args.steps // 2), 10)
-            routed = int(m.views(H.HSMLA_OP_BLOCK, ws_t)["counts"].sum().item())
-            ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
+            bb = Bound(m, H.HSMLA_OP_BLOCK, prepared=True)
+            ms_b = time_steps(lambda: bb.block(x), n_sw, 10)
+            routed = int(m.views(H.HSMLA_OP_BLOCK, bb.ws)["counts"].sum().item())
+            bf = Bound(m, H.HSMLA_OP_FORWARD, prepared=True)
+            ms_m = time_steps(lambda: bf.forward(x), n_sw, 10)
             sweep.append(dict(routing="threshold", tau=tau,
                               routed_fraction=round(routed / (base.batch * base.num_blocks), 4),
                               block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
                               block_ms=round(ms_b, 4),
                               module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
                               module_ms=round(ms_m, 4)))
-            del m
+            del m, bb, bf
 
         # per-head routing (each head by its own score), tau between two
         # adjacent head scores of a first per-head run at the 0.7 quantile
         m = DeviceModel(shape(base, tau=0.5, per_head=True), inp)
-        _, ws_p = time_steps(m, block_step, 1, 0)
-        hs = m.views(H.HSMLA_OP_BLOCK, ws_p)["head_scores"].cpu().numpy()
+        bb = Bound(m, H.HSMLA_OP_BLOCK, prepared=True)
+        bb.block(x)
+        torch.cuda.synchronize()
+        hs = m.views(H.HSMLA_OP_BLOCK, bb.ws)["head_scores"].cpu().numpy()
         uniq = np.unique(hs.astype(np.float32))
         i = min(int(0.7 * (uniq.size - 1)), uniq.size - 2)
         tau = float(np.float32((np.float64(uniq[i]) + np.float64(uniq[i + 1])) / 2))
-        del m
+        del m, bb
         m = DeviceModel(shape(base, tau=tau, per_head=True), inp)
-        ms_b, ws_t = time_steps(m, block_step, max(10, args.steps // 2), 10)
-        routed = int(m.views(H.HSMLA_OP_BLOCK, ws_t)["counts"].sum().item())
-        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
+        bb = Bound(m, H.HSMLA_OP_BLOCK, prepared=True)
+        ms_b = time_steps(lambda: bb.block(x), n_sw, 10)
+        routed = int(m.views(H.HSMLA_OP_BLOCK, bb.ws)["counts"].sum().item())
+        bf = Bound(m, H.HSMLA_OP_FORWARD, prepared=True)
+        ms_m = time_steps(lambda: bf.forward(x), n_sw, 10)
         sweep.append(dict(routing="threshold_per_head", tau=tau,
                           routed_fraction=round(routed / (base.batch * base.num_blocks
                                                           * base.heads), 4),
@@ -390,31 +580,35 @@ def main():
                           block_ms=round(ms_b, 4),
                           module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
                           module_ms=round(ms_m, 4)))
-        del m
+        del m, bb, bf
         # the training-time mixture forward: every block refined, residual
         # scaled by its score
         m = DeviceModel(shape(base, soft=True), inp)
-        ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 10)
-        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
+        bb = Bound(m, H.HSMLA_OP_BLOCK, prepared=True)
+        ms_b = time_steps(lambda: bb.block(x), n_sw, 10)
+        bf = Bound(m, H.HSMLA_OP_FORWARD, prepared=True)
+        ms_m = time_steps(lambda: bf.forward(x), n_sw, 10)
         sweep.append(dict(routing="soft_mixture", routed_fraction=1.0,
                           block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
                           block_ms=round(ms_b, 4),
                           module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
                           module_ms=round(ms_m, 4)))
-        del m
+        del m, bb, bf
         # the gate's depthwise 3x3 (FT 3.2 head-level score) with the
         # identity + 3x3 + 5x5 + 7x7 branches, top-k at the base keep ratio
         wl = scaled(base, branches=(3, 5, 7), gate_conv=True)
         m = DeviceModel(shape(wl), make_inputs(wl))
-        ms_b, _ = time_steps(m, block_step, max(10, args.steps // 2), 10)
-        ms_m, _ = time_steps(m, module_step, max(10, args.steps // 2), 10)
+        bb = Bound(m, H.HSMLA_OP_BLOCK, prepared=True)
+        ms_b = time_steps(lambda: bb.block(x), n_sw, 10)
+        bf = Bound(m, H.HSMLA_OP_FORWARD, prepared=True)
+        ms_m = time_steps(lambda: bf.forward(x), n_sw, 10)
         sweep.append(dict(variant="gate_dwconv3x3+branches_3_5_7", keep=base.keep,
                           keep_blocks=base.keep_blocks,
                           block_tokens_per_s=round(tokens / (ms_b * 1e-3), 1),
                           block_ms=round(ms_b, 4),
                           module_tokens_per_s=round(tokens / (ms_m * 1e-3), 1),
                           module_ms=round(ms_m, 4)))
-        del m
+        del m, bb, bf
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(base, args.cpu_rows)
 
@@ -437,11 +631,17 @@ def main():
                    "head_dim": base.head_dim, "branches": list(base.branches),
                    "block": base.block, "window": base.window, "keep": base.keep,
                    "keep_blocks": base.keep_blocks, "gate_conv": base.gate_conv,
-                   "streams": args.streams},
-        ("one_stream_ms_per_step" if split is not None else
+                   "streams": args.streams, "weights_prepared": True},
+        ("one_stream_ms_per_step" if args.streams == 2 else
          "two_stream_ms_per_step"): round(ms_alt, 4),
+        "unprepared_ms_per_step": round(ms_plain, 4),
+        "spinup_ms": 200,
+        "prep_us": prep_us,
         "roofline": roof,
         "kernels": kernels,
+        "selection_gap": gaps,
+        "probes": probe,
+        "configs": configs,
         "sweep": sweep,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),

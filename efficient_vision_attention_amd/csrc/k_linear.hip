@@ -64,26 +64,43 @@ __global__ __launch_bounds__(256) void kv_partial_kernel(
   if (tid % 8 == 0) out[kD * kD + i] = dacc;
 }
 
-// grid (batch * heads, ceil(kPart / 64)), 64 threads: one entry per thread,
-// chunk partials added in chunk order.
-__global__ __launch_bounds__(64) void kv_combine_kernel(
+// grid (batch * heads, ceil(kPart / 64)), 256 threads: entry e of the
+// workgroup's 64 per group of 64 threads; group q adds chunks
+// [q nc/4, (q+1) nc/4) in chunk order, then the four group sums are added in
+// group order (a fixed association: bitwise reproducible).
+__global__ __launch_bounds__(256) void kv_combine_kernel(
     const float* __restrict__ part, float* __restrict__ kv,
     float* __restrict__ ksum, int nchunks) {
+  __shared__ float red[4][64];
   const int bh = blockIdx.x;
   const float* p = part + (size_t)bh * nchunks * kPart;
-  const int e = blockIdx.y * 64 + threadIdx.x;
+  const int t = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int e = blockIdx.y * 64 + t;
+  const int c0 = (nchunks * q) / 4, c1 = (nchunks * (q + 1)) / 4;
+  float s = 0.f;
   if (e < kPart) {
-    // loads issued 32 at a time, added strictly in chunk order
-    float s = 0.f;
-    int c = 0;
-    for (; c + 32 <= nchunks; c += 32) {
-      float v[32];
+    // loads issued 16 (then 4) at a time, added strictly in chunk order
+    int c = c0;
+    for (; c + 16 <= c1; c += 16) {
+      float v[16];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = p[(size_t)(c + i) * kPart + e];
+      for (int i = 0; i < 16; ++i) v[i] = p[(size_t)(c + i) * kPart + e];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) s += v[i];
+      for (int i = 0; i < 16; ++i) s += v[i];
     }
-    for (; c < nchunks; ++c) s += p[(size_t)c * kPart + e];
+    for (; c + 4 <= c1; c += 4) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = p[(size_t)(c + i) * kPart + e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s += v[i];
+    }
+    for (; c < c1; ++c) s += p[(size_t)c * kPart + e];
+  }
+  red[q][t] = s;
+  __syncthreads();
+  if (q == 0 && e < kPart) {
+    s = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
     if (e < kD * kD)
       kv[(size_t)bh * kD * kD + e] = s;
     else
@@ -144,16 +161,30 @@ __device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
 // One wave per head of a 4-head group, tiles of 32 tokens.  Each tile's
 // K^ and V^ rows (32 tokens x 4 heads x 64 bytes each) are loaded with
 // 16-byte loads over whole 256-byte rows into one of two LDS buffers (one
-// barrier per tile), then every wave reads its head in token-major form
-// (lane = token, 8 consecutive features per 16 bytes), which is the MFMA
-// A-operand layout; multiplying it by the 32x32 identity returns it in the
-// accumulator layout, where a lane owns one feature and 16 tokens -- i.e.
-// transposed, exactly (one nonzero product per output).  The transposed
-// relu(K^) and V^ tiles then feed Z += relu(K^)^T V^ with the token order
-// the accumulator already has.  Tokens past the chunk read zeros (which add
-// nothing) through per-tile buffer resources.
+// barrier per tile), token-major as they lie in HBM.  Z += relu(K^)^T V^
+// contracts over tokens, so both MFMA operands need eight consecutive tokens
+// of one feature per lane: gfx950's transposing LDS read (ds_read_b64_tr_b16)
+// supplies them.  Within each group of 16 lanes, lane j receives element
+// j % 4 of the four 16-bit values that lane 4e + j / 4 addresses, e = 0..3;
+// so when lane k of the group addresses features f0 + 4 (k % 4) .. + 3 of
+// token t0 + k / 4, lane j gets feature f0 + j of tokens t0 .. t0 + 3.  Two
+// such reads give a lane its eight tokens, the matrix cores do only the
+// contraction, relu is a packed 16-bit integer max with 0 on the loaded
+// K^ values (the bf16 sign bit is the int16 sign), and D sums them.  Tokens
+// past the chunk read zeros (which add nothing) through per-tile buffer
+// resources.
 // grid (chunks, ceil(heads/4), batch), 256 threads = 4 heads.
-constexpr int kKvRowB = 2 * kHG * kD * 2 + 16;  // LDS bytes per token row: K^ | V^
+constexpr int kKvRowB = 2 * kHG * kD * 2 + 32;  // LDS bytes per token row: K^ | V^
+
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
+  const i16x2 v = __builtin_bit_cast(i16x2, w);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, (i16x2){0, 0}));
+}
 
 __global__ __launch_bounds__(256) void kv_partial_mfma(
     const bf16* __restrict__ qkvh, float* __restrict__ part, int tokens,
@@ -167,16 +198,6 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
   const int n_begin = chunk * kChunkTok;
   const int n_end = min(tokens, n_begin + kChunkTok);
   const int gch = min(kHG * kD, C - hg * kHG * kD);  // channels of this group
-
-  // identity as the B operand: column col, k = 16 ks + 8 g + e
-  bf16x8 eye[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    uint16_t e16[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) e16[e] = (16 * ks + 8 * g + e == col) ? 0x3f80 : 0;
-    eye[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(e16));
-  }
 
   // thread's four 16-byte chunks of a tile: token tid / 16 (+ 16),
   // part tid % 16 of K^ and of V^
@@ -194,6 +215,19 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
                     : kOob;
         d[2 * i + tv] = buf_load16(rs, off);
       }
+  };
+  // this lane's transposed reads: lane k of its 16-lane group addresses
+  // token 8 g + k / 4 (+ 4 for the second read, + 16 ks for the k-step) and
+  // features 16 ((lane / 16) % 2) + 4 (k % 4) .. + 3 of head `wave`; the
+  // group's lanes then hold features col of four consecutive tokens
+  const int kq = lane & 15;
+  const int tr_off = (8 * g + (kq >> 2)) * kKvRowB + wave * kD * 2 +
+                     (16 * ((lane >> 4) & 1) + 4 * (kq & 3)) * 2;
+  auto tr_read = [&](const char* T, int tv, int ks, int half) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)((lds_char*)T + tr_off + (16 * ks + 4 * half) * kKvRowB +
+                     tv * kHG * kD * 2));
+    return __builtin_bit_cast(uint2, v);
   };
 
   f32x16 z;
@@ -213,46 +247,21 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
                                   prt * 16) = st[2 * i + tv];
     if (n0 + kTT < n_end) issue(st, n0 + kTT);
     __syncthreads();
-    uint4 cur[4];  // [K^ ks0, K^ ks1, V^ ks0, V^ ks1]
-#pragma unroll
-    for (int tv = 0; tv < 2; ++tv)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        cur[2 * tv + ks] = *reinterpret_cast<const uint4*>(
-            T + col * kKvRowB + tv * kHG * kD * 2 + wave * kD * 2 + (16 * ks + 8 * g) * 2);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {  // relu on K^ (bf16 sign bit)
-      uint16_t* hv = reinterpret_cast<uint16_t*>(&cur[ks]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = relu_bits(hv[e]);
-    }
-    f32x16 kt, vt;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) kt[r] = vt[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      kt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur[ks]),
-                                                   eye[ks], kt, 0, 0, 0);
-      vt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur[2 + ks]),
-                                                   eye[ks], vt, 0, 0, 0);
-    }
-    // kt[r], vt[r]: feature col of token 8(r/4) + 4g + r%4
+      // relu(K^)^T: row = feature col, k = tokens 16 ks + 8 g .. + 7;
+      // V^: column = feature col, the same tokens
+      const uint2 k0 = tr_read(T, 0, ks, 0), k1 = tr_read(T, 0, ks, 1);
+      const uint2 v0 = tr_read(T, 1, ks, 0), v1 = tr_read(T, 1, ks, 1);
+      const uint32_t aw[4] = {relu_bf16x2(k0.x), relu_bf16x2(k0.y), relu_bf16x2(k1.x),
+                              relu_bf16x2(k1.y)};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dacc += kt[r];
-#pragma unroll
-    for (int slab = 0; slab < 2; ++slab) {
-      uint4 ka, vb;
-      ka.x = pack_bf16x2(kt[8 * slab + 0], kt[8 * slab + 1]);
-      ka.y = pack_bf16x2(kt[8 * slab + 2], kt[8 * slab + 3]);
-      ka.z = pack_bf16x2(kt[8 * slab + 4], kt[8 * slab + 5]);
-      ka.w = pack_bf16x2(kt[8 * slab + 6], kt[8 * slab + 7]);
-      vb.x = pack_bf16x2(vt[8 * slab + 0], vt[8 * slab + 1]);
-      vb.y = pack_bf16x2(vt[8 * slab + 2], vt[8 * slab + 3]);
-      vb.z = pack_bf16x2(vt[8 * slab + 4], vt[8 * slab + 5]);
-      vb.w = pack_bf16x2(vt[8 * slab + 6], vt[8 * slab + 7]);
-      z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka),
-                                                  __builtin_bit_cast(bf16x8, vb), z,
-                                                  0, 0, 0);
+      for (int e = 0; e < 4; ++e)
+        dacc += __uint_as_float(aw[e] << 16) + __uint_as_float(aw[e] & 0xffff0000u);
+      const uint4 a = {aw[0], aw[1], aw[2], aw[3]};
+      const uint4 v = {v0.x, v0.y, v1.x, v1.y};
+      z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, v), z, 0, 0, 0);
     }
   }
   if (h >= heads) return;
@@ -423,7 +432,7 @@ hipError_t launch_kv_state(bool bf, const void* qkv_hat, float* kv,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 cgrid(batch * heads, (kPart + 63) / 64);
-  kv_combine_kernel<<<cgrid, 64, 0, s>>>(partials, kv, ksum, chunks);
+  kv_combine_kernel<<<cgrid, 256, 0, s>>>(partials, kv, ksum, chunks);
   return hipGetLastError();
 }
 
