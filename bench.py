@@ -61,6 +61,8 @@ def parse():
                          "batch split over two streams "
                          "(hsmla_block_forward_split)")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--spinup-ms", type=float, default=200.0,
+                    help="back-to-back untimed steps before the warm-up")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the street / CT / pathology / tiny module runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -454,7 +456,7 @@ def main():
     model = DeviceModel(shape(base), inp)
     head = Bound(model, H.HSMLA_OP_BLOCK, prepared=True)
     plain = Bound(model, H.HSMLA_OP_BLOCK, prepared=False)
-    spin_up(lambda: head.block(x))
+    spin_up(lambda: head.block(x), args.spinup_ms)
     if args.streams == 2:
         ms = time_steps(lambda: head.block_split(x, two), args.steps, args.warmup)
         ms_alt = time_steps(lambda: head.block(x), args.steps, args.warmup)
@@ -635,7 +637,7 @@ def main():
         ("one_stream_ms_per_step" if args.streams == 2 else
          "two_stream_ms_per_step"): round(ms_alt, 4),
         "unprepared_ms_per_step": round(ms_plain, 4),
-        "spinup_ms": 200,
+        "spinup_ms": args.spinup_ms,
         "prep_us": prep_us,
         "roofline": roof,
         "kernels": kernels,
