@@ -213,6 +213,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
     // make the compiler wait for every copy in flight.
     static_assert(BM * BK * 2 % (1024 * WGM * WGN) == 0 && BN * BK * 2 % (1024 * WGM * WGN) == 0,
                   "whole 1 KB units per wave");
+    static_assert(kGemmTileM % BM == 0, "A tiles split the blocked layout's row blocks");
     constexpr int UA = BM * BK * 2 / 1024 / (WGM * WGN);  // A units per wave
     constexpr int UW = BN * BK * 2 / 1024 / (WGM * WGN);  // W units per wave
     constexpr int kPerTile = UA + UW;                        // copies per wave per tile
@@ -222,13 +223,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
       const int p = unit * 64 + lane;
       return (p & 3) ^ ((p >> 4) & 3);
     };
+    // Tile-blocked operands hold kGemmTileM (A) and kGemmTileN (W) rows per
+    // block.  An A tile of BM rows is a contiguous part of its block's K
+    // step; a W unit (16 rows) lies in one block even where a tile of
+    // another width starts mid-block.
+    auto w_unit = [&](int kt, int unit) {
+      if constexpr ((BLK & 2) != 0) {
+        const int r0 = n0 + 16 * unit;
+        const bf16* Wb = uniform_ptr(
+            W + ((size_t)(r0 / kGemmTileN) * (K / BK) + kt) * (kGemmTileN * BK) +
+            (size_t)(r0 % kGemmTileN) * BK);
+        return Wb + (swz_row(unit) - 16 * unit) * BK + swz_kc(unit) * 8;
+      } else {
+        return uniform_ptr(W + (size_t)n0 * K + kt * BK) + swz_row(unit) * K +
+               swz_kc(unit) * 8;
+      }
+    };
     auto issue = [&](int kt, int buf) {
       char* base = smem + buf * kDmaBuf;
-      const bf16* Ab = (BLK & 1) ? uniform_ptr(A + ((size_t)(m0 / BM) * (K / BK) + kt) * (BM * BK))
-                                 : uniform_ptr(A + (size_t)m0 * K + kt * BK);
-      const bf16* Wb = (BLK & 2) ? uniform_ptr(W + ((size_t)(n0 / BN) * (K / BK) + kt) * (BN * BK))
-                                 : uniform_ptr(W + (size_t)n0 * K + kt * BK);
-      const int a_stride = (BLK & 1) ? BK : K, w_stride = (BLK & 2) ? BK : K;
+      const bf16* Ab =
+          (BLK & 1) ? uniform_ptr(A + ((size_t)(m0 / kGemmTileM) * (K / BK) + kt) *
+                                          (kGemmTileM * BK) +
+                                  (size_t)(m0 % kGemmTileM) * BK)
+                    : uniform_ptr(A + (size_t)m0 * K + kt * BK);
+      const int a_stride = (BLK & 1) ? BK : K;
 #pragma unroll
       for (int i = 0; i < UA; ++i) {
         const int unit = wave * UA + i;
@@ -239,9 +257,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
 #pragma unroll
       for (int i = 0; i < UW; ++i) {
         const int unit = wave * UW + i;
-        __builtin_amdgcn_global_load_lds(
-            (global_void_ptr)(Wb + swz_row(unit) * w_stride + swz_kc(unit) * 8),
-            (lds_void_ptr)(base + BM * BK * 2 + unit * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((global_void_ptr)w_unit(kt, unit),
+                                         (lds_void_ptr)(base + BM * BK * 2 + unit * 1024), 16,
+                                         0, 0);
       }
     };
     auto frag = [&](const char* buf_base, int row, int kc) {
@@ -266,16 +284,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_bf16(
       if (kt + 2 < NKT) issue(kt + 2, (kt + 2) % 3);
       const char* bA = smem + (kt % 3) * kDmaBuf;
       const char* bW = bA + BM * BK * 2;
+      // The second 16-k half's fragment reads are interleaved with the
+      // first half's MFMAs, and the wave's priority is raised while it
+      // issues them (measured: QKV and FFN1 2-3 us faster).
+      static_assert(BK == 32, "two 16-k halves per step");
+      __builtin_amdgcn_s_setprio(1);
+      {
+        bf16x8 af0[FM], wf0[FN], af1[FM], wf1[FN];
+        const int kc0 = lane >> 5, kc1 = 2 + (lane >> 5);
 #pragma unroll
-      for (int ks = 0; ks < BK; ks += 16) {
-        bf16x8 af[FM], wf[FN];
-        const int kc = ks / 8 + (lane >> 5);
+        for (int t = 0; t < FM; ++t) af0[t] = frag(bA, wm + 32 * t + frow, kc0);
 #pragma unroll
-        for (int t = 0; t < FM; ++t) af[t] = frag(bA, wm + 32 * t + frow, kc);
+        for (int t = 0; t < FN; ++t) wf0[t] = frag(bW, wn + 32 * t + frow, kc0);
 #pragma unroll
-        for (int t = 0; t < FN; ++t) wf[t] = frag(bW, wn + 32 * t + frow, kc);
-        mfma_frags(af, wf);
+        for (int t = 0; t < FM; ++t) af1[t] = frag(bA, wm + 32 * t + frow, kc1);
+#pragma unroll
+        for (int t = 0; t < FN; ++t) wf1[t] = frag(bW, wn + 32 * t + frow, kc1);
+        mfma_frags(af0, wf0);
+        mfma_frags(af1, wf1);
+        // the first half's reads, then MFMA / read pairs, then the rest
+        __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+        for (int i = 0; i < FM + FN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * FM * FN - (FM + FN), 0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     // the epilogue reuses the buffers: every wave's fragment reads are done
     __builtin_amdgcn_sched_barrier(0);

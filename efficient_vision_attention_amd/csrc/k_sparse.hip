@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kD = 32;
 constexpr int kKT = 64;  // window keys staged per LDS tile
+constexpr int kXcds = 8;
 
 // grid (entries, batch, heads); one thread per query of the block.
 template <typename T>
@@ -158,18 +159,24 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ qkvh,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ counts,
     const float* __restrict__ wts, bf16* __restrict__ o, int gh, int gw,
-    int heads, int block, int window, SelLayout lay) {
+    int heads, int block, int window, SelLayout lay, int entries, int total,
+    int per_xcd) {
   constexpr int NT = 64 * 2 * NQT;
   __shared__ SparseTile tiles[2];
   __shared__ float linloc[NQT * 32][kD + 1];
 
-  const int b = blockIdx.y, h = blockIdx.z;
+  // Work item (image b, list entry e, head h), numbered with h fastest and
+  // remapped so that each XCD takes a contiguous run: the heads of a block
+  // (which share the cache lines of every window row) and the neighbouring
+  // selected blocks (whose windows overlap) then meet in that XCD's L2.
+  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (item >= total) return;
+  const int h = item % heads, e = (item / heads) % entries, b = item / heads / entries;
   const int C = heads * kD, C3 = 3 * C;
-  if (counts && (int)blockIdx.x >= counts[b * lay.cnt_b + h * lay.cnt_h])
+  if (counts && e >= counts[b * lay.cnt_b + h * lay.cnt_h])
     return;  // beyond the routed set
   // without a list every block is refined (entry x is block x)
-  const int t = sel ? sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + blockIdx.x]
-                    : (int)blockIdx.x;
+  const int t = sel ? sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + e] : e;
   const int nbc = gw / block;
   if (t < 0 || t >= (gh / block) * nbc) return;  // invalid entry: no access
   const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
@@ -424,15 +431,18 @@ hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
   if (entries == 0) return hipSuccess;
   const int nqt = (block * block + 31) / 32;
   if (bf && nqt <= 4) {
-    dim3 grid(entries, batch, heads);
+    if ((int64_t)entries * batch * heads > INT32_MAX / 2) return hipErrorInvalidValue;
+    const int total = entries * batch * heads;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const dim3 grid(per_xcd * kXcds);
     const bf16* q = static_cast<const bf16*>(qkv);
     const bf16* qh = static_cast<const bf16*>(qkv_hat);
     bf16* out = static_cast<bf16*>(o);
     switch (nqt) {
-      case 1: sparse_mfma_kernel<1><<<grid, 128, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay); break;
-      case 2: sparse_mfma_kernel<2><<<grid, 256, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay); break;
-      case 3: sparse_mfma_kernel<3><<<grid, 384, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay); break;
-      default: sparse_mfma_kernel<4><<<grid, 512, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay); break;
+      case 1: sparse_mfma_kernel<1><<<grid, 128, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd); break;
+      case 2: sparse_mfma_kernel<2><<<grid, 256, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd); break;
+      case 3: sparse_mfma_kernel<3><<<grid, 384, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd); break;
+      default: sparse_mfma_kernel<4><<<grid, 512, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd); break;
     }
     return hipGetLastError();
   }
