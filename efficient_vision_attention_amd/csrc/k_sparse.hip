@@ -159,7 +159,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ qkvh,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ counts,
     const float* __restrict__ wts, bf16* __restrict__ o, int gh, int gw,
-    int heads, int block, int window, SelLayout lay, int entries, int total,
+    int heads, int block, int window, SelLayout lay, int entries, int n_items,
     int per_xcd) {
   constexpr int NT = 64 * 2 * NQT;
   __shared__ SparseTile tiles[2];
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
   // (which share the cache lines of every window row) and the neighbouring
   // selected blocks (whose windows overlap) then meet in that XCD's L2.
   const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (item >= total) return;
+  if (item >= n_items) return;
   const int h = item % heads, e = (item / heads) % entries, b = item / heads / entries;
   const int C = heads * kD, C3 = 3 * C;
   if (counts && e >= counts[b * lay.cnt_b + h * lay.cnt_h])
