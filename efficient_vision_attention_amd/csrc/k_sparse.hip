@@ -130,9 +130,14 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
 // Every 32x32 accumulator tile holds one query per lane column, so row
 // statistics of a query live in one lane pair (l, l ^ 32).  The P^T / A^T
 // accumulator registers are fed back as the B operand of the next MFMA with
-// the key order they already have; V and V^ are staged transposed in LDS in
-// that same order.  Keys are streamed in tiles of 64 through double-buffered
-// LDS.  Path 1 hands its normalised result to path 0 through LDS, and path 0
+// the key order they already have; V and V^ are staged key-major in LDS (as
+// they lie in HBM) and read as the A operand V^T in that same key order with
+// gfx950's transposing LDS read (ds_read_b64_tr_b16: within each group of
+// 16 lanes, lane j receives element j % 4 of the four 16-bit values that
+// lane 4e + j / 4 addresses, e = 0..3; so when lane k addresses channels
+// f0 + 4 (k % 4) .. + 3 of key t0 + k / 4, lane j receives channel f0 + j of
+// keys t0 .. t0 + 3).  Keys are streamed in tiles of 64 through
+// double-buffered LDS.  Path 1 hands its normalised result to path 0 through LDS, and path 0
 // writes O_lin + O_local - O_linloc.
 // ---------------------------------------------------------------------------
 
@@ -140,14 +145,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int KT = 64;            // keys per LDS tile
-constexpr int KS = kD + 8;        // bf16 stride of key-major rows
-constexpr int VS = KT + 8;        // bf16 stride of channel-major rows
+constexpr int KS = kD + 8;        // bf16 stride of K rows (80 bytes)
+constexpr int VS = kD + 16;       // bf16 stride of V rows (96 bytes: a transposing
+                                  // read's four 32-byte pieces in distinct banks)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
 
 struct __attribute__((aligned(16))) SparseTile {
   bf16 k[KT * KS];    // raw K,   [key][channel]
   bf16 kh[KT * KS];   // K_hat,   [key][channel]
-  bf16 vt[kD * VS];   // raw V,   [channel][key]
-  bf16 vht[kD * VS];  // V_hat,   [channel][key]
+  bf16 v[KT * VS];    // raw V,   [key][channel]
+  bf16 vh[KT * VS];   // V_hat,   [key][channel]
 };
 
 __device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
@@ -163,7 +173,10 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     int per_xcd) {
   constexpr int NT = 64 * 2 * NQT;
   __shared__ SparseTile tiles[2];
-  __shared__ float linloc[NQT * 32][kD + 1];
+  // path 1's normalised result for path 0, written after the key loop has
+  // ended (its last barrier passed): it reuses the tile buffers
+  static_assert(sizeof(float) * NQT * 32 * (kD + 1) <= sizeof(SparseTile) * 2, "linloc fits");
+  float (*linloc)[kD + 1] = reinterpret_cast<float (*)[kD + 1]>(&tiles[0]);
 
   // Work item (image b, list entry e, head h), numbered with h fastest and
   // remapped so that each XCD takes a contiguous run: the heads of a block
@@ -268,10 +281,8 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
         for (int j = 0; j < 8; ++j) hv[j] = relu_bits(hv[j]);
         *reinterpret_cast<uint4*>(&T.kh[key * KS + 8 * cg]) = u;
       } else {
-        bf16* dst = tensor == 2 ? T.vt : T.vht;
-        const uint16_t* hv = reinterpret_cast<const uint16_t*>(&u);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dst[(8 * cg + j) * VS + key].u = hv[j];
+        bf16* dst = tensor == 2 ? T.v : T.vh;
+        *reinterpret_cast<uint4*>(&dst[key * VS + 8 * cg]) = u;
       }
     }
   };
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     if (it + 1 < ntiles) issue((it + 1) * KT);
     const SparseTile& T = tiles[buf];
     const bf16* kmat = path == 0 ? T.k : T.kh;
-    const bf16* vmat = path == 0 ? T.vt : T.vht;
+    const bf16* vmat = path == 0 ? T.v : T.vh;
 #pragma unroll
     for (int sub = 0; sub < KT / 32; ++sub) {
       const int kbase = it * KT + sub * 32;
@@ -355,10 +366,15 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
         pb.y = pack_bf16x2(s[8 * slab + 2], s[8 * slab + 3]);
         pb.z = pack_bf16x2(s[8 * slab + 4], s[8 * slab + 5]);
         pb.w = pack_bf16x2(s[8 * slab + 6], s[8 * slab + 7]);
-        const bf16* vrow = &vmat[(lane & 31) * VS + sub * 32 + 16 * slab + 4 * g];
+        // V^T operand: channel lane % 32, keys sub*32 + 16 slab + 4 g + 0..3
+        // and + 8 .. + 11 (two transposing reads, see above)
+        const bf16* vrow = &vmat[(sub * 32 + 16 * slab + 4 * g + ((lane & 15) >> 2)) * VS +
+                                 16 * ((lane >> 4) & 1) + 4 * (lane & 3)];
+        const uint2 lo = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)vrow));
+        const uint2 hi = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)(vrow + 8 * VS)));
         uint4 va;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
         va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
         oacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb), oacc,
