@@ -226,6 +226,36 @@ def test_block_forward_prepared_weights():
         np.testing.assert_array_equal(to_host(out), ref["out"])
 
 
+@pytest.mark.parametrize("name", ["street_small", "ragged_f32"])
+def test_forward_and_qkv_prepared_weights(name):
+    """hsmla_prepare for the module and for the QKV step, then calls with
+    desc.prepared: bit for bit the outputs of the calls that prepare their
+    own operands (tile-blocked copies for the whole-tile bf16 shape,
+    row-major ones for the ragged float32 shape)."""
+    wl = STAGE_CASES[name]
+    inp = make_inputs(wl)
+    r = Run(wl, inp)
+    ref = r.forward()
+    m = r.model
+    d = H.make_desc(**dict(m.shape, prepared=True))
+    ws = m.workspace(H.HSMLA_OP_FORWARD)
+    announce(f"hsmla_prepare + hsmla_forward(prepared) {name}")
+    H.hsmla_prepare(m.desc, H.HSMLA_OP_FORWARD, m.weights, None, ws)
+    y = m.act()
+    H.hsmla_forward(d, m.weights, r.x, y, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(y), ref["y"])
+    wq = m.workspace(H.HSMLA_OP_QKV)
+    q0, h0, q1, h1 = m.act(3), m.act(3), m.act(3), m.act(3)
+    announce(f"hsmla_prepare + hsmla_qkv_branches(prepared) {name}")
+    H.hsmla_qkv_branches(m.desc, m.weights, r.x, q0, h0, wq)
+    H.hsmla_prepare(m.desc, H.HSMLA_OP_QKV, m.weights, None, wq)
+    H.hsmla_qkv_branches(d, m.weights, r.x, q1, h1, wq)
+    torch.cuda.synchronize()
+    assert torch.equal(q0, q1) and torch.equal(h0, h1)
+    np.testing.assert_array_equal(to_host(q1), ref["qkv"])
+
+
 def _oracle_ffn(x1, inp, wl):
     r = O.round_bf16
     xn2 = r(O.layer_norm(x1, inp["ln2_g"], inp["ln2_b"]))
