@@ -160,8 +160,15 @@ struct __attribute__((aligned(16))) SparseTile {
   bf16 vh[KT * VS];   // V_hat,   [key][channel]
 };
 
-__device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
-  return (u & 0x8000u) ? 0 : u;  // bf16 max(x, 0); -0 and negatives -> +0
+// bf16 max(x, 0) on two packed values: a packed 16-bit integer max with 0
+// (a bf16 with the sign bit set is a negative int16; -0 and negatives -> +0)
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t u) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, u),
+                                                                s16x2{0, 0}));
+}
+__device__ __forceinline__ uint4 relu_bf16x8(uint4 u) {
+  return uint4{relu_bf16x2(u.x), relu_bf16x2(u.y), relu_bf16x2(u.z), relu_bf16x2(u.w)};
 }
 
 template <int NQT>
@@ -217,11 +224,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     for (int ks = 0; ks < 2; ++ks) {
       uint4 u = q_ok ? *reinterpret_cast<const uint4*>(src + 16 * ks + 8 * g)
                      : uint4{0, 0, 0, 0};
-      if (path == 1) {  // relu on the hatted query
-        uint16_t* hv = reinterpret_cast<uint16_t*>(&u);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hv[i] = relu_bits(hv[i]);
-      }
+      if (path == 1) u = relu_bf16x8(u);  // relu on the hatted query
       qf[ks] = __builtin_bit_cast(bf16x8, u);
     }
   }
@@ -229,57 +232,61 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
   // tile loader: 64 keys x (K, K^, V, V^) x 32 channels = 1024 chunks of 8.
   // Loads are unconditional (keys past the window re-read its last key and
   // are zeroed when staged), so no load sits under a branch and the wait
-  // before staging covers exactly one tile.  Each thread's keys advance by
-  // 64 window positions per tile, so their (row, column) in the window is
-  // stepped instead of divided.
+  // before staging covers exactly one tile.  Each chunk keeps a pointer to
+  // its tensor's head slice in the image and the 32-bit element offset of its
+  // key's token, both formed once: a tile advances every key by 64 window
+  // positions, i.e. a fixed offset step plus one row's wrap when its column
+  // passes the window's edge (the launcher keeps an image's offsets below
+  // 2^31 elements).
   constexpr int kLoads = (1024 + NT - 1) / NT;
+  __builtin_assume(tid < NT);
   uint4 stg[kLoads];
   const int step_r = KT / wcols, step_c = KT % wcols;
-  int kr[kLoads], kc[kLoads];  // window row / column of this thread's keys
+  const uint32_t d_off = (uint32_t)((step_r * gw + step_c) * C3);
+  const uint32_t wrap_off = (uint32_t)((gw - wcols) * C3);
+  const uint32_t off_last = (uint32_t)(((rhi - 1) * gw + chi - 1) * C3);
+  int kc[kLoads];            // window column of this thread's keys
+  uint32_t koff[kLoads];     // element offset of their token in the image
+  const bf16* kptr[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    const int key = (min(tid + NT * i, 1023) >> 2) & 63;
-    kr[i] = key / wcols;
+    const int cidx = min(tid + NT * i, 1023);
+    const int tensor = cidx >> 8;      // 0 K, 1 K^, 2 V, 3 V^
+    const int key = (cidx >> 2) & 63, cg = cidx & 3;
+    const int kr = key / wcols;
     kc[i] = key % wcols;
+    koff[i] = (uint32_t)(((rlo + kr) * gw + clo + kc[i]) * C3);
+    kptr[i] = ((tensor & 1) ? qkvh : qkv) + img * C3 + (tensor < 2 ? 1 : 2) * C + h * kD + 8 * cg;
   }
-  const size_t tok_last = img + (size_t)(rhi - 1) * gw + chi - 1;
   auto issue = [&](int w0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int cidx = min(tid + NT * i, 1023);
-      const int tensor = cidx >> 8;      // 0 K, 1 K^, 2 V, 3 V^
-      const int key = (cidx >> 2) & 63, cg = cidx & 3;
-      const size_t tok = w0 + key < nwin
-                             ? img + (size_t)(rlo + kr[i]) * gw + clo + kc[i]
-                             : tok_last;
-      const bf16* base = (tensor & 1) ? qkvh : qkv;
-      const int comp = (tensor < 2) ? 1 : 2;
-      stg[i] = *reinterpret_cast<const uint4*>(base + tok * C3 + comp * C + h * kD + 8 * cg);
+      const int key = (min(tid + NT * i, 1023) >> 2) & 63;
+      stg[i] = *reinterpret_cast<const uint4*>(kptr[i] + (w0 + key < nwin ? koff[i] : off_last));
       // advance to the same key of the next tile
-      kr[i] += step_r;
+      koff[i] += d_off;
       kc[i] += step_c;
       if (kc[i] >= wcols) {
         kc[i] -= wcols;
-        ++kr[i];
+        koff[i] += wrap_off;
       }
     }
   };
   auto commit = [&](int buf, int w0) {
     SparseTile& T = tiles[buf];
+    const bool whole = w0 + KT <= nwin;  // uniform: no key past the window
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int cidx = tid + NT * i;
       if (cidx >= 1024) break;
       const int tensor = cidx >> 8;
       const int key = (cidx >> 2) & 63, cg = cidx & 3;
-      uint4 u = w0 + key < nwin ? stg[i] : uint4{0, 0, 0, 0};
+      uint4 u = stg[i];
+      if (!whole && w0 + key >= nwin) u = uint4{0, 0, 0, 0};
       if (tensor == 0) {
         *reinterpret_cast<uint4*>(&T.k[key * KS + 8 * cg]) = u;
       } else if (tensor == 1) {
-        uint16_t* hv = reinterpret_cast<uint16_t*>(&u);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) hv[j] = relu_bits(hv[j]);
-        *reinterpret_cast<uint4*>(&T.kh[key * KS + 8 * cg]) = u;
+        *reinterpret_cast<uint4*>(&T.kh[key * KS + 8 * cg]) = relu_bf16x8(u);
       } else {
         bf16* dst = tensor == 2 ? T.v : T.vh;
         *reinterpret_cast<uint4*>(&dst[key * VS + 8 * cg]) = u;
@@ -321,22 +328,21 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
       }
       // lane holds keys kbase + 8(r/4) + 4g + r%4 of its query
       if (path == 0) {
+        // the maximum of the raw scores, scaled once (sc > 0, and rounding
+        // is monotonic, so this is the maximum of the scaled scores)
         float mx = -INFINITY;
         if (kbase + 32 <= nwin) {  // a whole tile of keys (uniform)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[r] *= sc;
-            mx = fmaxf(mx, s[r]);
-          }
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
-            s[r] = key < nwin ? s[r] * sc : -INFINITY;
+            s[r] = key < nwin ? s[r] : -INFINITY;
             mx = fmaxf(mx, s[r]);
           }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
         const float mnew = fmaxf(run_max, mx);
         // arguments are <= 0: the hardware exp2 (results below 2^-126, i.e.
         // probabilities negligible against the row maximum's 1, flush to 0;
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[r] = __builtin_amdgcn_exp2f(s[r] - mnew);
+          s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, -mnew));
           ps += s[r];
         }
         run_sum = run_sum * corr + ps;
@@ -446,7 +452,8 @@ hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
                          SelLayout lay, hipStream_t s) {
   if (entries == 0) return hipSuccess;
   const int nqt = (block * block + 31) / 32;
-  if (bf && nqt <= 4) {
+  // the MFMA kernel forms an image's token offsets in 32 bits
+  if (bf && nqt <= 4 && (int64_t)gh * gw * 3 * heads * kD < INT32_MAX) {
     if ((int64_t)entries * batch * heads > INT32_MAX / 2) return hipErrorInvalidValue;
     const int total = entries * batch * heads;
     const int per_xcd = (total + kXcds - 1) / kXcds;
