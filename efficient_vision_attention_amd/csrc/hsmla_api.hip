@@ -40,6 +40,7 @@ inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Dims {
   int B, gh, gw, N, C, H, T, k, Bs, w, kmax;
+  int Bk;     // images of the whole call (a range keeps it): the K/V chunking
   int sw;     // sel entries per image: k (top-k), T (threshold), H*T (per head)
   int nc;     // routed-set counts: B (threshold), B*H (per head)
   size_t P;   // B * N tokens
@@ -92,6 +93,7 @@ hsmla_status check_desc(const hsmla_desc* d, Dims* out) {
   if (N * d->batch > INT32_MAX / 2) return HSMLA_ERR_SHAPE;
   if (out) {
     out->B = d->batch;
+    out->Bk = d->batch;
     out->gh = d->grid_h;
     out->gw = d->grid_w;
     out->N = (int)N;
@@ -156,7 +158,7 @@ Layout layout(const Dims& D, int op) {
   };
   const size_t bh = (size_t)D.B * D.H;
   const size_t part_bytes =
-      bh * kv_chunks(D.bf, D.B, D.H, D.N) * (kHeadDim * kHeadDim + kHeadDim) * 4;
+      bh * kv_chunks(D.bf, D.Bk, D.H, D.N) * (kHeadDim * kHeadDim + kHeadDim) * 4;
   const size_t tap_bytes = (size_t)D.kmax * D.kmax * 3 * D.C * 4;
   const size_t c2 = (size_t)D.C * D.C * D.e;
   if (op == HSMLA_OP_QKV) {
@@ -258,7 +260,7 @@ struct Bufs {
 Bufs bufs_for(const Dims& D, const Layout& L, void* ws, int op, int b0) {
   const size_t n = (size_t)D.N, c = (size_t)D.C, e = D.e, T = (size_t)D.T;
   const size_t H = (size_t)D.H, bb = (size_t)b0;
-  const size_t chunks = (size_t)kv_chunks(D.bf, D.B, D.H, D.N);
+  const size_t chunks = (size_t)kv_chunks(D.bf, D.Bk, D.H, D.N);
   Bufs u{};
   if (op == HSMLA_OP_QKV) {  // taps and the W_qkv copy only
     u.taps = reinterpret_cast<float*>(at(ws, L.taps));
@@ -391,7 +393,7 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
     case 2:
       r.mark("kv_state");
       HSMLA_TRY(hsmla::launch_kv_state(D.bf, u.qkvh, u.kv, u.ksum, u.part, D.B,
-                                       D.N, D.H, s));
+                                       D.N, D.H, s, D.Bk));
       return HSMLA_OK;
     case 3:
       r.mark("lin_apply");

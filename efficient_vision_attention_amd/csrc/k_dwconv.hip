@@ -14,6 +14,8 @@
 // tap sets take so many registers that a register-only kernel, each thread
 // loading its neighbours through L1, keeps more loads in flight
 // (dwconv_stream).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -185,8 +187,8 @@ __device__ __forceinline__ float sum_lanes(float v) {
 // summed over the 32 / V lanes that hold the slice (one aligned DPP group,
 // fixed order), written to bsum's memory.  A thread's CX columns lie in one
 // block (block is a multiple of CX).
-template <int V, int CX, int TT, int WC>
-__device__ __forceinline__ void pool_store(const float (&red)[TH / kPoolMinBlock][TT][WC],
+template <int V, int CX, int TT, int WC, int RB>
+__device__ __forceinline__ void pool_store(const float (&red)[RB][TT][WC],
                                            float* bsum, const float* gate_w, int heads,
                                            int block, int b, int gh, int gw, int ch, int x,
                                            int tx, int tc, int c, bool c_ok, int y0,
@@ -239,6 +241,13 @@ constexpr int kStreamChannels = 64;  // channels per workgroup
 // flight instead of two 85 us (fewer registers: 5 waves per SIMD, not 4;
 // three or four rows slower).
 constexpr int kStreamV = 2, kStreamCols = 4, kStreamRows = 1;
+// Strip heights TH, TH / 2 or TH / 4 (kMinStrip): the tallest that still
+// gives kStreamMinWgs workgroups (two per CU).  Shorter strips re-read more
+// halo rows and load the taps more often, so they only pay where CUs would
+// idle (measured on the folded 5x5 with gate sums: 4 x 64x128 tokens at
+// C = 256, 384 workgroups, 51.8 -> 45.8 us with strips of 8 rows; 8 x
+// 128x128 at C = 128, 768 workgroups, 59.9 -> 70.8 us with 16 rows).
+constexpr int kMinStrip = TH / 4, kStreamMinWgs = 512;
 // LDS-staged kernel (up to 3x3): output columns per thread.
 constexpr int kLdsCols = 2;
 
@@ -263,7 +272,8 @@ constexpr int kLdsCols = 2;
 // barrier); after the strip one barrier, then the block's columns are
 // added in order.  block must divide the workgroup width and the strip
 // height, be a multiple of CX, and be at least kPoolMinBlock (LDS room).
-template <typename T, int K, bool GELU, int V, int NB, bool POOL, bool TL, int CX = 1>
+template <typename T, int K, bool GELU, int V, int NB, bool POOL, bool TL, int CX = 1,
+          int SH = TH>
 __global__ __launch_bounds__(256) void dwconv_stream(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, float* __restrict__ bsum, int block,
@@ -274,7 +284,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   constexpr int TT = 256 / CG;             // column groups per workgroup
   constexpr int TW = TT * CX;              // columns per workgroup
   constexpr int KL = K + CX - 1;           // input columns per thread
-  __shared__ float red[POOL ? TH / kPoolMinBlock : 1][POOL ? TT : 1][POOL ? kStreamChannels : 1];
+  __shared__ float red[POOL ? SH / kPoolMinBlock : 1][POOL ? TT : 1][POOL ? kStreamChannels : 1];
   const int bid = blockIdx.x;
   const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
   if (tile >= total) return;
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   const int x = col_t * TW + tx * CX;
   const int c = ch_t * kStreamChannels + tc * V;
   const bool c_ok = c < ch;
-  const int y0 = strip * TH;
+  const int y0 = strip * SH;
   const size_t img = (size_t)b * gh * gw;
 
   // Taps: in registers, or (TL) in LDS, read at every use -- the lanes of
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
 #pragma unroll
   for (int j = 0; j < V; ++j) psum[j] = 0.f;
 
-  const int y_end = min(gh, y0 + TH);
+  const int y_end = min(gh, y0 + SH);
   const int r_begin = y0 - R, r_end = y_end + R;
 
   // Row loads through a buffer resource over the workgroup's in-grid
@@ -753,14 +763,33 @@ hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
   const int total = col_tiles * ch_tiles * strips * batch;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   if constexpr (K >= 5) {
-    if (bsum && !GELU)
-      dwconv_stream<T, K, false, cf.v, cf.p, true, cf.tl, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
-          static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
-          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, gate_w, heads);
+    // Shorter strips where TH-row strips give too few workgroups to fill
+    // the chip (each output is summed in the same order whatever the
+    // strip, and pooled block rows stay inside one strip).
+    int sh = TH;
+    while (sh > kMinStrip && (sh / 2) % (bsum ? block : 1) == 0 &&
+           col_tiles * ch_tiles * ((gh + sh - 1) / sh) * batch < kStreamMinWgs)
+      sh /= 2;
+    auto go = [&](auto sh_c) {
+      constexpr int SH = decltype(sh_c)::value;
+      const int st = (gh + SH - 1) / SH;
+      const int tot = col_tiles * ch_tiles * st * batch;
+      const int px = (tot + kXcds - 1) / kXcds;
+      if (bsum && !GELU)
+        dwconv_stream<T, K, false, cf.v, cf.p, true, cf.tl, cf.cx, SH><<<px * kXcds, 256, 0, s>>>(
+            static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
+            gw, ch, col_tiles, ch_tiles, st, tot, px, gate_w, heads);
+      else
+        dwconv_stream<T, K, GELU, cf.v, cf.p, false, cf.tl, cf.cx, SH><<<px * kXcds, 256, 0, s>>>(
+            static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
+            gw, ch, col_tiles, ch_tiles, st, tot, px, nullptr, 0);
+    };
+    if (sh == TH)
+      go(std::integral_constant<int, TH>{});
+    else if (sh == TH / 2)
+      go(std::integral_constant<int, TH / 2>{});
     else
-      dwconv_stream<T, K, GELU, cf.v, cf.p, false, cf.tl, cf.cx><<<per_xcd * kXcds, 256, 0, s>>>(
-          static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
-          gw, ch, col_tiles, ch_tiles, strips, total, per_xcd, nullptr, 0);
+      go(std::integral_constant<int, TH / 4>{});
     return hipGetLastError();
   } else {
     return run_dw_lds<T, K, GELU>(in, out, weff, bsum, block, batch, gh, gw, ch, out_blocked,

@@ -473,9 +473,10 @@ void launch_tiles(const void* A, const void* W, const void* R, void* C, int M,
           total, per_xcd);
 }
 
-// Shapes that are whole tiles with K = 384 or 1536 (the block's projections
-// at C = 384) get the unrolled two-step prefetch; other whole-tile shapes a
-// runtime K loop; ragged shapes the bounds-checked variant (plain layouts
+// Shapes that are whole tiles with K = 128, 256, 384 or 1536 (the block's
+// projections at C = 384, the module's at C = 128 and 256) get the unrolled
+// K loop with copies straight into LDS; other whole-tile shapes a runtime K
+// loop; ragged shapes the bounds-checked variant (plain layouts
 // only).  blk: bit 0 A tile-blocked, bit 1 W tile-blocked.
 template <int BM, int BN, int BK, int WGM, int WGN, int SITE, int PF, bool EDGE, int NKT>
 void launch_blk(int blk, const void* A, const void* W, const void* R, void* C,
@@ -502,6 +503,10 @@ hipError_t run_tiles(const void* A, const void* W, const void* R, void* C, int M
     launch_blk<BM, BN, BK, WGM, WGN, SITE, 2, false, 12>(blk, A, W, R, C, M, N, K, s);
   } else if (K == 48 * BK) {
     launch_blk<BM, BN, BK, WGM, WGN, SITE, 2, false, 48>(blk, A, W, R, C, M, N, K, s);
+  } else if (K == 8 * BK) {
+    launch_blk<BM, BN, BK, WGM, WGN, SITE, 2, false, 8>(blk, A, W, R, C, M, N, K, s);
+  } else if (K == 4 * BK) {
+    launch_blk<BM, BN, BK, WGM, WGN, SITE, 2, false, 4>(blk, A, W, R, C, M, N, K, s);
   } else {
     launch_blk<BM, BN, BK, WGM, WGN, SITE, 1, false, 0>(blk, A, W, R, C, M, N, K, s);
   }

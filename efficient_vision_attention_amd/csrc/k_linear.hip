@@ -151,7 +151,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kHG = 4;          // heads per workgroup
 constexpr int kTT = 32;         // tokens per tile
-constexpr int kChunkTok = 512;  // tokens per partial (bf16 path)
+constexpr int kChunkTok = 512;  // tokens per partial (bf16 path), at most
+constexpr int kMinChunkTok = 128;
+// Partials are kept at kChunkTok tokens while the launch yields at least one
+// workgroup per CU; smaller launches halve the chunk (down to kMinChunkTok).
+// Smaller chunks cost partial traffic and a longer combine, so they only pay
+// where CUs would idle (measured: 4 x 64x128 tokens, 8 heads 19.4 -> 14.7
+// us; 8 x 128x128 at 4 heads 21.5 -> 24.9 us with four times the chunks).
+// The decision takes the batch of the whole call, so a call split over
+// image ranges sums the same chunks.
+constexpr int kChunkMinWgs = 256;
 constexpr int kApplyTok = 256;  // tokens per wave in the readout
 
 __device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
@@ -188,15 +197,15 @@ __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
 
 __global__ __launch_bounds__(256) void kv_partial_mfma(
     const bf16* __restrict__ qkvh, float* __restrict__ part, int tokens,
-    int heads, int nchunks) {
+    int heads, int nchunks, int chunk_tok) {
   __shared__ __attribute__((aligned(16))) char ts[2][kTT * kKvRowB];
   const int chunk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = hg * kHG + wave;  // h >= heads: stages, computes nothing kept
   const int C = heads * kD, C3 = 3 * C;
   const int g = lane >> 5, col = lane & 31;
-  const int n_begin = chunk * kChunkTok;
-  const int n_end = min(tokens, n_begin + kChunkTok);
+  const int n_begin = chunk * chunk_tok;
+  const int n_end = min(tokens, n_begin + chunk_tok);
   const int gch = min(kHG * kD, C - hg * kHG * kD);  // channels of this group
 
   // thread's four 16-byte chunks of a tile: token tid / 16 (+ 16),
@@ -403,8 +412,19 @@ __global__ __launch_bounds__(256) void lin_apply_mfma(
 
 }  // namespace
 
+// tokens per bf16 partial for a call of `batch` images of `tokens` tokens
+int kv_chunk_tokens(int batch, int heads, int tokens) {
+  const int64_t hg = (heads + kHG - 1) / kHG;
+  int ct = kChunkTok;
+  while (ct > kMinChunkTok && ((tokens + ct - 1) / ct) * hg * batch < kChunkMinWgs) ct /= 2;
+  return ct;
+}
+
 int kv_chunks(bool bf, int batch, int heads, int tokens) {
-  if (bf) return (tokens + kChunkTok - 1) / kChunkTok;
+  if (bf) {
+    const int ct = kv_chunk_tokens(batch, heads, tokens);
+    return (tokens + ct - 1) / ct;
+  }
   // Enough workgroups to cover the chip (256 CUs) several times over, but
   // never chunks shorter than one LDS tile.
   const int bh = batch * heads;
@@ -417,12 +437,15 @@ int kv_chunks(bool bf, int batch, int heads, int tokens) {
 
 hipError_t launch_kv_state(bool bf, const void* qkv_hat, float* kv,
                            float* ksum, float* partials, int batch, int tokens,
-                           int heads, hipStream_t s) {
-  const int chunks = kv_chunks(bf, batch, heads, tokens);
+                           int heads, hipStream_t s, int chunk_batch) {
+  if (chunk_batch <= 0) chunk_batch = batch;
+  if (bf && chunk_batch < batch) return hipErrorInvalidValue;
+  const int chunks = kv_chunks(bf, bf ? chunk_batch : batch, heads, tokens);
   if (bf) {
     dim3 grid(chunks, (heads + kHG - 1) / kHG, batch);
     kv_partial_mfma<<<grid, 256, 0, s>>>(static_cast<const bf16*>(qkv_hat),
-                                         partials, tokens, heads, chunks);
+                                         partials, tokens, heads, chunks,
+                                         kv_chunk_tokens(chunk_batch, heads, tokens));
   } else {
     const int chunk_len = (tokens + chunks - 1) / chunks;
     dim3 grid(chunks, heads, batch);

@@ -88,13 +88,17 @@ bool dwconv_planar_ok(bool bf, int batch, int gh, int gw, int ch);
 hipError_t launch_dwconv_gelu_planar(const void* in, void* out, const float* weff, int batch,
                                      int gh, int gw, int ch, hipStream_t s);
 
-// Number of token chunks the KV-state reduction splits each image into.
+// Number of token chunks the KV-state reduction splits each image into, for
+// a call of `batch` images.
 int kv_chunks(bool bf, int batch, int heads, int tokens);
 
 // Z/D partials per chunk, then a fixed-order combine into kv and ksum.
+// chunk_batch: the batch of the whole call whose images [.., + batch) this
+// launch covers (bf16 chunks by it; 0 = batch); partials hold
+// kv_chunks(bf, chunk_batch, ...) chunks per (image, head).
 hipError_t launch_kv_state(bool bf, const void* qkv_hat, float* kv,
                            float* ksum, float* partials, int batch, int tokens,
-                           int heads, hipStream_t s);
+                           int heads, hipStream_t s, int chunk_batch = 0);
 
 // o = relu(q_hat) Z / (relu(q_hat) . D), zero when the denominator is 0.
 hipError_t launch_lin_apply(bool bf, const void* qkv_hat, const float* kv,
