@@ -185,3 +185,27 @@ def test_block_forward_full_size_exact_gate_three_branches():
     g = Run(wl, inp).block_forward()
     xn1 = O.round_bf16(O.layer_norm(inp["x"], inp["ln1_g"], inp["ln1_b"]))
     _check_module_fullsize(wl, dict(inp, x=xn1), g)
+
+
+def test_block_forward_full_size_every_element():
+    """The benchmark's block workload (keep 10%), each projection and the FFN
+    checked on every element, stage-wise on the GPU's own inputs (FT 3.5
+    block equation): qkv = LN1(x) W_qkv on every row (every output tile of
+    the projection's persistent tile loop), x1 = x + o W_o on every row, and
+    out = x1 + FFN(LN2(x1)) on every token from the GPU's x1."""
+    wl = scaled(WORKLOADS["block"], keep=0.10)
+    inp = make_inputs(wl)
+    g = Run(wl, inp).block_forward()
+    rnd = O.round_bf16
+    B, C = wl.batch, wl.channels
+    xn1 = rnd(O.layer_norm(inp["x"], inp["ln1_g"], inp["ln1_b"]))
+    assert_close(g["qkv"], rnd(xn1 @ inp["w_qkv"]), "bf16", "qkv, every row")
+    assert_close(g["x1"], rnd(inp["x"] + g["o"] @ inp["w_o"]), "bf16", "x1, every row")
+    for b in range(B):  # one image at a time keeps the host arrays small
+        x1 = g["x1"][b:b + 1]
+        xn2 = rnd(O.layer_norm(x1, inp["ln2_g"], inp["ln2_b"]))
+        h1 = rnd(xn2 @ inp["w1"])
+        h2 = rnd(O.gelu(O.dwconv_same(h1, inp["dw_ffn"], wl.grid_h, wl.grid_w)))
+        del h1
+        assert_close(g["out"][b:b + 1], rnd(x1 + h2 @ inp["w2"]), "bf16",
+                     f"out image {b}, every token")
