@@ -574,12 +574,31 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ A,
 
 // One tile shape for every projection: 256x128 with 2x2 waves of 128x64
 // measured best on MI355X for all four projection shapes of the block
-// (M = 65536; N, K = 1152, 384 / 384, 384 / 1536, 384 / 384, 1536).
+// (M = 65536; N, K = 1152, 384 / 384, 384 / 1536, 384 / 384, 1536); 128x128
+// only where 256x128 tiles would leave CUs idle.
+constexpr int kSmallTileBelow = 512;
 template <int SITE>
 hipError_t run_mfma(const void* A, const void* W, const void* R, void* C, int M,
                     int N, int K, int blk, hipStream_t s) {
   static_assert(kGemmTileM == 256 && kGemmTileN == 128 && kGemmTileK == 32,
                 "the blocked layout follows the tile");
+  // Launches that would give fewer than two 256x128 tiles per CU take
+  // 128x128 tiles (2x2 waves of 64x64): twice the workgroups, where the
+  // larger tile's lower LDS traffic per flop no longer matters.
+  if (M % 128 == 0 && N % 128 == 0 && (int64_t)(M / 256) * (N / 128) < kSmallTileBelow) {
+    if (K == 4 * kGemmTileK) {
+      launch_blk<128, 128, 32, 2, 2, SITE, 2, false, 4>(blk, A, W, R, C, M, N, K, s);
+      return hipGetLastError();
+    }
+    if (K == 8 * kGemmTileK) {
+      launch_blk<128, 128, 32, 2, 2, SITE, 2, false, 8>(blk, A, W, R, C, M, N, K, s);
+      return hipGetLastError();
+    }
+    if (K == 12 * kGemmTileK) {
+      launch_blk<128, 128, 32, 2, 2, SITE, 2, false, 12>(blk, A, W, R, C, M, N, K, s);
+      return hipGetLastError();
+    }
+  }
   return run_tiles<256, 128, 32, 2, 2, SITE>(A, W, R, C, M, N, K, blk, s);
 }
 

@@ -161,7 +161,11 @@ constexpr int kMinChunkTok = 128;
 // The decision takes the batch of the whole call, so a call split over
 // image ranges sums the same chunks.
 constexpr int kChunkMinWgs = 256;
-constexpr int kApplyTok = 256;  // tokens per wave in the readout
+constexpr int kApplyTok = 256;  // tokens per workgroup in the readout, at most
+// A readout launch with fewer than this many workgroups takes 128 tokens per
+// workgroup instead (the Z setup of a workgroup is then amortised over half
+// the tokens, which only pays where CUs would otherwise idle).
+constexpr int kApplyMinWgs = 512;
 
 __device__ __forceinline__ uint16_t relu_bits(uint16_t u) {
   return (u & 0x8000u) ? 0 : u;
@@ -286,9 +290,9 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
 }
 
 // O^T = Z^T relu(Q^)^T with Z split into bf16 hi + lo parts, normalised by
-// relu(q^) . D.  grid (ceil(tokens/256), ceil(heads/4), batch), 256
-// threads; wave = head of a 4-head group, eight 32-token tiles per
-// workgroup.  Each tile's Q^ rows (32 tokens x 4 heads x 64 bytes) are
+// relu(q^) . D.  grid (ceil(tokens/APPLY_TOK), ceil(heads/4), batch), 256
+// threads; wave = head of a 4-head group, APPLY_TOK / 32 tiles of 32 tokens
+// per workgroup.  Each tile's Q^ rows (32 tokens x 4 heads x 64 bytes) are
 // loaded with 16-byte loads over whole 256-byte rows into LDS, read back in
 // the MFMA operand layout (lane = token), and the normalised output goes
 // back through LDS to 256-byte row stores: per-lane token-major global
@@ -296,6 +300,7 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
 // tile's loads are in flight while a tile is computed.
 constexpr int kRowB = kHG * kD * 2 + 16;  // LDS bytes per staged token row
 
+template <int APPLY_TOK>
 __global__ __launch_bounds__(256) void lin_apply_mfma(
     const bf16* __restrict__ qkvh, const float* __restrict__ kv,
     const float* __restrict__ ksum, bf16* __restrict__ o, int tokens,
@@ -338,7 +343,7 @@ __global__ __launch_bounds__(256) void lin_apply_mfma(
   // group, and tokens may end inside a tile; both read zeros / store
   // nothing through per-tile buffer resources (which also keep every
   // offset small).
-  const int n_base = blockIdx.x * kApplyTok;
+  const int n_base = blockIdx.x * APPLY_TOK;
   const int gch = min(kHG * kD, C - hg * kHG * kD);  // channels of this group
   // thread's two 16-byte chunks of a tile: token tid / 16 (+ 16), part tid % 16
   const int part = tid & 15, trow = tid >> 4;
@@ -356,9 +361,9 @@ __global__ __launch_bounds__(256) void lin_apply_mfma(
   uint4 st[2][2];
   issue(st[0], n_base);
 #pragma unroll
-  for (int tt = 0; tt < kApplyTok / kTT; ++tt) {
+  for (int tt = 0; tt < APPLY_TOK / kTT; ++tt) {
     const int n0 = n_base + tt * kTT;
-    if (tt + 1 < kApplyTok / kTT) issue(st[(tt + 1) & 1], n0 + kTT);
+    if (tt + 1 < APPLY_TOK / kTT) issue(st[(tt + 1) & 1], n0 + kTT);
     // stage this tile's rows (the previous tile's readers have passed the
     // barrier that ended their iteration)
 #pragma unroll
@@ -463,9 +468,18 @@ hipError_t launch_lin_apply(bool bf, const void* qkv_hat, const float* kv,
                             const float* ksum, void* o, int batch, int tokens,
                             int heads, hipStream_t s) {
   if (bf) {
-    dim3 grid((tokens + kApplyTok - 1) / kApplyTok, (heads + kHG - 1) / kHG, batch);
-    lin_apply_mfma<<<grid, 256, 0, s>>>(static_cast<const bf16*>(qkv_hat), kv,
-                                        ksum, static_cast<bf16*>(o), tokens, heads);
+    const int hg = (heads + kHG - 1) / kHG;
+    const int64_t wgs = (int64_t)((tokens + kApplyTok - 1) / kApplyTok) * hg * batch;
+    if (wgs >= kApplyMinWgs) {
+      dim3 grid((tokens + kApplyTok - 1) / kApplyTok, hg, batch);
+      lin_apply_mfma<kApplyTok><<<grid, 256, 0, s>>>(static_cast<const bf16*>(qkv_hat), kv,
+                                                     ksum, static_cast<bf16*>(o), tokens, heads);
+    } else {
+      constexpr int kHalf = kApplyTok / 2;
+      dim3 grid((tokens + kHalf - 1) / kHalf, hg, batch);
+      lin_apply_mfma<kHalf><<<grid, 256, 0, s>>>(static_cast<const bf16*>(qkv_hat), kv, ksum,
+                                                 static_cast<bf16*>(o), tokens, heads);
+    }
     return hipGetLastError();
   }
   dim3 grid((tokens + 63) / 64, heads, batch);
