@@ -15,6 +15,8 @@
 // phi(q^) Z_W / phi(q^) D_W by associativity.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -24,6 +26,9 @@ namespace {
 constexpr int kD = 32;
 constexpr int kKT = 64;  // window keys staged per LDS tile
 constexpr int kXcds = 8;
+constexpr int kCusPerXcd = 32;
+// resident workgroups per CU of the MFMA kernel (45 KB of LDS each)
+constexpr int kSparseWgsPerCu = 3;
 
 // grid (entries, batch, heads); one thread per query of the block.
 template <typename T>
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ counts,
     const float* __restrict__ wts, bf16* __restrict__ o, int gh, int gw,
     int heads, int block, int window, SelLayout lay, int entries, int n_items,
-    int per_xcd) {
+    int per_xcd, int wgs_per_xcd) {
   constexpr int NT = 64 * 2 * NQT;
   __shared__ SparseTile tiles[2];
   // path 1's normalised result for path 0, written after the key loop has
@@ -185,249 +190,280 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
   static_assert(sizeof(float) * NQT * 32 * (kD + 1) <= sizeof(SparseTile) * 2, "linloc fits");
   float (*linloc)[kD + 1] = reinterpret_cast<float (*)[kD + 1]>(&tiles[0]);
 
-  // Work item (image b, list entry e, head h), numbered with h fastest and
-  // remapped so that each XCD takes a contiguous run: the heads of a block
-  // (which share the cache lines of every window row) and the neighbouring
-  // selected blocks (whose windows overlap) then meet in that XCD's L2.
-  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (item >= n_items) return;
-  const int h = item % heads, e = (item / heads) % entries, b = item / heads / entries;
+  // Work items (image b, list entry e, head h), walked by a grid of at most
+  // three workgroups per CU; workgroup blockIdx.x runs on XCD
+  // blockIdx.x % 8 and takes that XCD's local items lw, lw + wgs_per_xcd, ...
+  // Fixed-length lists: each XCD takes a contiguous run of items numbered
+  // with h fastest, so the heads of a block (which share the cache lines of
+  // every window row) and the neighbouring selected blocks (whose windows
+  // overlap) meet in that XCD's L2.  Counted lists (threshold routings),
+  // whose valid entries are the first count of each list: the entries are
+  // dealt to the XCDs in turn (entry e on XCD e % 8, its heads together), so
+  // the routed work spreads over the whole chip, and a workgroup stops at
+  // the largest count instead of every surplus entry taking a workgroup.
+  const int xcd = blockIdx.x % kXcds, lw = blockIdx.x / kXcds;
+  const int batch = n_items / (entries * heads);
   const int C = heads * kD, C3 = 3 * C;
-  if (counts && e >= counts[b * lay.cnt_b + h * lay.cnt_h])
-    return;  // beyond the routed set
-  // without a list every block is refined (entry x is block x)
-  const int t = sel ? sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + e] : e;
   const int nbc = gw / block;
-  if (t < 0 || t >= (gh / block) * nbc) return;  // invalid entry: no access
-  const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
-  const int p = (window - block) / 2;
-  const int rlo = max(0, r0 - p), rhi = min(gh, r0 + block + p);
-  const int clo = max(0, c0 - p), chi = min(gw, c0 + block + p);
-  const int wcols = chi - clo;
-  const int nwin = (rhi - rlo) * wcols;
-  const int nq = block * block;
-  const size_t img = (size_t)b * gh * gw;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int qt = wave % NQT, path = wave / NQT;
-  const int g = lane >> 5;           // lane group (0/1)
-  const int ql = qt * 32 + (lane & 31);  // query index within the block
-  const bool q_ok = ql < nq;
-  const int qn = q_ok ? (r0 + ql / block) * gw + c0 + ql % block : 0;
-
-  // B operand of S^T: this lane's query, channels 8g..8g+7 and 16+8g..
-  bf16x8 qf[2];
-  {
-    const bf16* src = (path == 0 ? qkv : qkvh) + (img + qn) * C3 + h * kD;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 u = q_ok ? *reinterpret_cast<const uint4*>(src + 16 * ks + 8 * g)
-                     : uint4{0, 0, 0, 0};
-      if (path == 1) u = relu_bf16x8(u);  // relu on the hatted query
-      qf[ks] = __builtin_bit_cast(bf16x8, u);
-    }
+  int max_cnt = entries;
+  if (counts) {
+    max_cnt = 0;
+    for (int b = 0; b < batch; ++b)
+      for (int h = 0; h < (lay.cnt_h ? heads : 1); ++h)
+        max_cnt = max(max_cnt, counts[b * lay.cnt_b + h * lay.cnt_h]);
+    max_cnt = min(max_cnt, entries);
   }
-
-  // tile loader: 64 keys x (K, K^, V, V^) x 32 channels = 1024 chunks of 8.
-  // Loads are unconditional (keys past the window re-read its last key and
-  // are zeroed when staged), so no load sits under a branch and the wait
-  // before staging covers exactly one tile.  Each chunk keeps a pointer to
-  // its tensor's head slice in the image and the 32-bit element offset of its
-  // key's token, both formed once: a tile advances every key by 64 window
-  // positions, i.e. a fixed offset step plus one row's wrap when its column
-  // passes the window's edge (the launcher keeps an image's offsets below
-  // 2^31 elements).
-  constexpr int kLoads = (1024 + NT - 1) / NT;
-  __builtin_assume(tid < NT);
-  uint4 stg[kLoads];
-  const int step_r = KT / wcols, step_c = KT % wcols;
-  const uint32_t d_off = (uint32_t)((step_r * gw + step_c) * C3);
-  const uint32_t wrap_off = (uint32_t)((gw - wcols) * C3);
-  const uint32_t off_last = (uint32_t)(((rhi - 1) * gw + chi - 1) * C3);
-  int kc[kLoads];            // window column of this thread's keys
-  uint32_t koff[kLoads];     // element offset of their token in the image
-  const bf16* kptr[kLoads];
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int cidx = min(tid + NT * i, 1023);
-    const int tensor = cidx >> 8;      // 0 K, 1 K^, 2 V, 3 V^
-    const int key = (cidx >> 2) & 63, cg = cidx & 3;
-    const int kr = key / wcols;
-    kc[i] = key % wcols;
-    koff[i] = (uint32_t)(((rlo + kr) * gw + clo + kc[i]) * C3);
-    kptr[i] = ((tensor & 1) ? qkvh : qkv) + img * C3 + (tensor < 2 ? 1 : 2) * C + h * kD + 8 * cg;
-  }
-  auto issue = [&](int w0) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int key = (min(tid + NT * i, 1023) >> 2) & 63;
-      stg[i] = *reinterpret_cast<const uint4*>(kptr[i] + (w0 + key < nwin ? koff[i] : off_last));
-      // advance to the same key of the next tile
-      koff[i] += d_off;
-      kc[i] += step_c;
-      if (kc[i] >= wcols) {
-        kc[i] -= wcols;
-        koff[i] += wrap_off;
-      }
+  for (int j = lw;; j += wgs_per_xcd) {
+    int h, e, b;
+    if (counts) {
+      h = j % heads;
+      b = (j / heads) % batch;
+      e = (j / heads / batch) * kXcds + xcd;
+      if (e >= max_cnt) break;
+    } else {
+      const int item = xcd * per_xcd + j;
+      if (j >= per_xcd || item >= n_items) break;
+      h = item % heads;
+      e = (item / heads) % entries;
+      b = item / heads / entries;
     }
-  };
-  auto commit = [&](int buf, int w0) {
-    SparseTile& T = tiles[buf];
-    const bool whole = w0 + KT <= nwin;  // uniform: no key past the window
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int cidx = tid + NT * i;
-      if (cidx >= 1024) break;
-      const int tensor = cidx >> 8;
-      const int key = (cidx >> 2) & 63, cg = cidx & 3;
-      uint4 u = stg[i];
-      if (!whole && w0 + key >= nwin) u = uint4{0, 0, 0, 0};
-      if (tensor == 0) {
-        *reinterpret_cast<uint4*>(&T.k[key * KS + 8 * cg]) = u;
-      } else if (tensor == 1) {
-        *reinterpret_cast<uint4*>(&T.kh[key * KS + 8 * cg]) = relu_bf16x8(u);
-      } else {
-        bf16* dst = tensor == 2 ? T.v : T.vh;
-        *reinterpret_cast<uint4*>(&dst[key * VS + 8 * cg]) = u;
-      }
-    }
-  };
+    if (counts && e >= counts[b * lay.cnt_b + h * lay.cnt_h])
+      continue;  // beyond the routed set
+    // without a list every block is refined (entry x is block x)
+    const int t = sel ? sel[(size_t)b * lay.sel_b + (size_t)h * lay.sel_h + e] : e;
+    if (t < 0 || t >= (gh / block) * nbc) continue;  // invalid entry: no access
+    const int r0 = (t / nbc) * block, c0 = (t % nbc) * block;
+    const int p = (window - block) / 2;
+    const int rlo = max(0, r0 - p), rhi = min(gh, r0 + block + p);
+    const int clo = max(0, c0 - p), chi = min(gw, c0 + block + p);
+    const int wcols = chi - clo;
+    const int nwin = (rhi - rlo) * wcols;
+    const int nq = block * block;
+    const size_t img = (size_t)b * gh * gw;
 
-  f32x16 oacc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) oacc[r] = 0.f;
-  float run_max = -INFINITY;  // softmax path: running max (shared by l, l^32)
-  float run_sum = 0.f;        // this lane's share of the column sum
-  const float sc = 1.4426950408889634f / sqrtf((float)kD);  // log2(e)/sqrt(d)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int qt = wave % NQT, path = wave / NQT;
+    const int g = lane >> 5;           // lane group (0/1)
+    const int ql = qt * 32 + (lane & 31);  // query index within the block
+    const bool q_ok = ql < nq;
+    const int qn = q_ok ? (r0 + ql / block) * gw + c0 + ql % block : 0;
 
-  const int ntiles = (nwin + KT - 1) / KT;
-  issue(0);
-  commit(0, 0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) issue((it + 1) * KT);
-    const SparseTile& T = tiles[buf];
-    const bf16* kmat = path == 0 ? T.k : T.kh;
-    const bf16* vmat = path == 0 ? T.v : T.vh;
-#pragma unroll
-    for (int sub = 0; sub < KT / 32; ++sub) {
-      const int kbase = it * KT + sub * 32;
-      if (kbase >= nwin) break;
-      // S^T (or A^T) tile: rows = 32 keys, columns = 32 queries
-      f32x16 s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    // B operand of S^T: this lane's query, channels 8g..8g+7 and 16+8g..
+    bf16x8 qf[2];
+    {
+      const bf16* src = (path == 0 ? qkv : qkvh) + (img + qn) * C3 + h * kD;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(
-                        &kmat[(sub * 32 + (lane & 31)) * KS + 16 * ks + 8 * g]));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+        uint4 u = q_ok ? *reinterpret_cast<const uint4*>(src + 16 * ks + 8 * g)
+                       : uint4{0, 0, 0, 0};
+        if (path == 1) u = relu_bf16x8(u);  // relu on the hatted query
+        qf[ks] = __builtin_bit_cast(bf16x8, u);
       }
-      // lane holds keys kbase + 8(r/4) + 4g + r%4 of its query
-      if (path == 0) {
-        // the maximum of the raw scores, scaled once (sc > 0, and rounding
-        // is monotonic, so this is the maximum of the scaled scores)
-        float mx = -INFINITY;
-        if (kbase + 32 <= nwin) {  // a whole tile of keys (uniform)
+    }
+
+    // tile loader: 64 keys x (K, K^, V, V^) x 32 channels = 1024 chunks of 8.
+    // Loads are unconditional (keys past the window re-read its last key and
+    // are zeroed when staged), so no load sits under a branch and the wait
+    // before staging covers exactly one tile.  Each chunk keeps a pointer to
+    // its tensor's head slice in the image and the 32-bit element offset of its
+    // key's token, both formed once: a tile advances every key by 64 window
+    // positions, i.e. a fixed offset step plus one row's wrap when its column
+    // passes the window's edge (the launcher keeps an image's offsets below
+    // 2^31 elements).
+    constexpr int kLoads = (1024 + NT - 1) / NT;
+    __builtin_assume(tid < NT);
+    uint4 stg[kLoads];
+    const int step_r = KT / wcols, step_c = KT % wcols;
+    const uint32_t d_off = (uint32_t)((step_r * gw + step_c) * C3);
+    const uint32_t wrap_off = (uint32_t)((gw - wcols) * C3);
+    const uint32_t off_last = (uint32_t)(((rhi - 1) * gw + chi - 1) * C3);
+    int kc[kLoads];            // window column of this thread's keys
+    uint32_t koff[kLoads];     // element offset of their token in the image
+    const bf16* kptr[kLoads];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    for (int i = 0; i < kLoads; ++i) {
+      const int cidx = min(tid + NT * i, 1023);
+      const int tensor = cidx >> 8;      // 0 K, 1 K^, 2 V, 3 V^
+      const int key = (cidx >> 2) & 63, cg = cidx & 3;
+      const int kr = key / wcols;
+      kc[i] = key % wcols;
+      koff[i] = (uint32_t)(((rlo + kr) * gw + clo + kc[i]) * C3);
+      kptr[i] = ((tensor & 1) ? qkvh : qkv) + img * C3 + (tensor < 2 ? 1 : 2) * C + h * kD + 8 * cg;
+    }
+    auto issue = [&](int w0) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int key = (min(tid + NT * i, 1023) >> 2) & 63;
+        stg[i] = *reinterpret_cast<const uint4*>(kptr[i] + (w0 + key < nwin ? koff[i] : off_last));
+        // advance to the same key of the next tile
+        koff[i] += d_off;
+        kc[i] += step_c;
+        if (kc[i] >= wcols) {
+          kc[i] -= wcols;
+          koff[i] += wrap_off;
+        }
+      }
+    };
+    auto commit = [&](int buf, int w0) {
+      SparseTile& T = tiles[buf];
+      const bool whole = w0 + KT <= nwin;  // uniform: no key past the window
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int cidx = tid + NT * i;
+        if (cidx >= 1024) break;
+        const int tensor = cidx >> 8;
+        const int key = (cidx >> 2) & 63, cg = cidx & 3;
+        uint4 u = stg[i];
+        if (!whole && w0 + key >= nwin) u = uint4{0, 0, 0, 0};
+        if (tensor == 0) {
+          *reinterpret_cast<uint4*>(&T.k[key * KS + 8 * cg]) = u;
+        } else if (tensor == 1) {
+          *reinterpret_cast<uint4*>(&T.kh[key * KS + 8 * cg]) = relu_bf16x8(u);
         } else {
+          bf16* dst = tensor == 2 ? T.v : T.vh;
+          *reinterpret_cast<uint4*>(&dst[key * VS + 8 * cg]) = u;
+        }
+      }
+    };
+
+    f32x16 oacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[r] = 0.f;
+    float run_max = -INFINITY;  // softmax path: running max (shared by l, l^32)
+    float run_sum = 0.f;        // this lane's share of the column sum
+    const float sc = 1.4426950408889634f / sqrtf((float)kD);  // log2(e)/sqrt(d)
+
+    const int ntiles = (nwin + KT - 1) / KT;
+    issue(0);
+    commit(0, 0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < ntiles) issue((it + 1) * KT);
+      const SparseTile& T = tiles[buf];
+      const bf16* kmat = path == 0 ? T.k : T.kh;
+      const bf16* vmat = path == 0 ? T.v : T.vh;
+#pragma unroll
+      for (int sub = 0; sub < KT / 32; ++sub) {
+        const int kbase = it * KT + sub * 32;
+        if (kbase >= nwin) break;
+        // S^T (or A^T) tile: rows = 32 keys, columns = 32 queries
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 kf = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const uint4*>(
+                          &kmat[(sub * 32 + (lane & 31)) * KS + 16 * ks + 8 * g]));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+        }
+        // lane holds keys kbase + 8(r/4) + 4g + r%4 of its query
+        if (path == 0) {
+          // the maximum of the raw scores, scaled once (sc > 0, and rounding
+          // is monotonic, so this is the maximum of the scaled scores)
+          float mx = -INFINITY;
+          if (kbase + 32 <= nwin) {  // a whole tile of keys (uniform)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
+              s[r] = key < nwin ? s[r] : -INFINITY;
+              mx = fmaxf(mx, s[r]);
+            }
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
+          const float mnew = fmaxf(run_max, mx);
+          // arguments are <= 0: the hardware exp2 (results below 2^-126, i.e.
+          // probabilities negligible against the row maximum's 1, flush to 0;
+          // -inf gives 0) instead of the library's denormal-preserving form
+          const float corr = __builtin_amdgcn_exp2f(run_max - mnew);
+          run_max = mnew;
+          float ps = 0.f;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
-            s[r] = key < nwin ? s[r] : -INFINITY;
-            mx = fmaxf(mx, s[r]);
+            s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, -mnew));
+            ps += s[r];
           }
+          run_sum = run_sum * corr + ps;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[r] *= corr;
+        } else {
+          float ps = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ps += s[r];
+          run_sum += ps;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
-        const float mnew = fmaxf(run_max, mx);
-        // arguments are <= 0: the hardware exp2 (results below 2^-126, i.e.
-        // probabilities negligible against the row maximum's 1, flush to 0;
-        // -inf gives 0) instead of the library's denormal-preserving form
-        const float corr = __builtin_amdgcn_exp2f(run_max - mnew);
-        run_max = mnew;
-        float ps = 0.f;
+        // O^T += V^T P^T over two 16-key slabs, keys in accumulator order
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, -mnew));
-          ps += s[r];
+        for (int slab = 0; slab < 2; ++slab) {
+          uint4 pb;
+          pb.x = pack_bf16x2(s[8 * slab + 0], s[8 * slab + 1]);
+          pb.y = pack_bf16x2(s[8 * slab + 2], s[8 * slab + 3]);
+          pb.z = pack_bf16x2(s[8 * slab + 4], s[8 * slab + 5]);
+          pb.w = pack_bf16x2(s[8 * slab + 6], s[8 * slab + 7]);
+          // V^T operand: channel lane % 32, keys sub*32 + 16 slab + 4 g + 0..3
+          // and + 8 .. + 11 (two transposing reads, see above)
+          const bf16* vrow = &vmat[(sub * 32 + 16 * slab + 4 * g + ((lane & 15) >> 2)) * VS +
+                                   16 * ((lane >> 4) & 1) + 4 * (lane & 3)];
+          const uint2 lo = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)vrow));
+          const uint2 hi = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)(vrow + 8 * VS)));
+          uint4 va;
+          va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
+          oacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb), oacc,
+              0, 0, 0);
         }
-        run_sum = run_sum * corr + ps;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[r] *= corr;
-      } else {
-        float ps = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ps += s[r];
-        run_sum += ps;
       }
-      // O^T += V^T P^T over two 16-key slabs, keys in accumulator order
-#pragma unroll
-      for (int slab = 0; slab < 2; ++slab) {
-        uint4 pb;
-        pb.x = pack_bf16x2(s[8 * slab + 0], s[8 * slab + 1]);
-        pb.y = pack_bf16x2(s[8 * slab + 2], s[8 * slab + 3]);
-        pb.z = pack_bf16x2(s[8 * slab + 4], s[8 * slab + 5]);
-        pb.w = pack_bf16x2(s[8 * slab + 6], s[8 * slab + 7]);
-        // V^T operand: channel lane % 32, keys sub*32 + 16 slab + 4 g + 0..3
-        // and + 8 .. + 11 (two transposing reads, see above)
-        const bf16* vrow = &vmat[(sub * 32 + 16 * slab + 4 * g + ((lane & 15) >> 2)) * VS +
-                                 16 * ((lane >> 4) & 1) + 4 * (lane & 3)];
-        const uint2 lo = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)vrow));
-        const uint2 hi = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)(vrow + 8 * VS)));
-        uint4 va;
-        va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
-        oacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb), oacc,
-            0, 0, 0);
-      }
+      // tiles[buf ^ 1] was last read before the previous barrier
+      if (it + 1 < ntiles) commit(buf ^ 1, (it + 1) * KT);
+      __syncthreads();
     }
-    // tiles[buf ^ 1] was last read before the previous barrier
-    if (it + 1 < ntiles) commit(buf ^ 1, (it + 1) * KT);
-    __syncthreads();
-  }
 
-  // column totals over both lane groups
-  const float total = run_sum + __shfl_xor(run_sum, 32, 64);
-  // lane holds channels 8(r/4) + 4g + r%4 of query ql
-  if (path == 1) {
-    const float inv = total > 0.f ? 1.f / total : 0.f;
+    // column totals over both lane groups
+    const float total = run_sum + __shfl_xor(run_sum, 32, 64);
+    // lane holds channels 8(r/4) + 4g + r%4 of query ql
+    if (path == 1) {
+      const float inv = total > 0.f ? 1.f / total : 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      linloc[ql][8 * (r >> 2) + 4 * g + (r & 3)] = total > 0.f ? oacc[r] * inv : 0.f;
-  }
-  __syncthreads();
-  if (path == 0 && q_ok) {
-    const float inv = 1.f / total;
-    const float w = wts ? wts[(size_t)b * (gh / block) * nbc + t] : 1.f;
-    bf16* orow = o + (img + qn) * C + h * kD;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ch = 8 * j + 4 * g;
-      const uint2 prev = *reinterpret_cast<const uint2*>(orow + ch);
-      float v[4];
-      v[0] = __uint_as_float(prev.x << 16);
-      v[1] = __uint_as_float(prev.x & 0xffff0000u);
-      v[2] = __uint_as_float(prev.y << 16);
-      v[3] = __uint_as_float(prev.y & 0xffff0000u);
-      if (wts) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[i] = fmaf(w, oacc[4 * j + i] * inv - linloc[ql][ch + i], v[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += oacc[4 * j + i] * inv - linloc[ql][ch + i];
-      }
-      uint2 outv;
-      outv.x = pack_bf16x2(v[0], v[1]);
-      outv.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(orow + ch) = outv;
+      for (int r = 0; r < 16; ++r)
+        linloc[ql][8 * (r >> 2) + 4 * g + (r & 3)] = total > 0.f ? oacc[r] * inv : 0.f;
     }
+    __syncthreads();
+    if (path == 0 && q_ok) {
+      const float inv = 1.f / total;
+      const float w = wts ? wts[(size_t)b * (gh / block) * nbc + t] : 1.f;
+      bf16* orow = o + (img + qn) * C + h * kD;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ch = 8 * j + 4 * g;
+        const uint2 prev = *reinterpret_cast<const uint2*>(orow + ch);
+        float v[4];
+        v[0] = __uint_as_float(prev.x << 16);
+        v[1] = __uint_as_float(prev.x & 0xffff0000u);
+        v[2] = __uint_as_float(prev.y << 16);
+        v[3] = __uint_as_float(prev.y & 0xffff0000u);
+        if (wts) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] = fmaf(w, oacc[4 * j + i] * inv - linloc[ql][ch + i], v[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += oacc[4 * j + i] * inv - linloc[ql][ch + i];
+        }
+        uint2 outv;
+        outv.x = pack_bf16x2(v[0], v[1]);
+        outv.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(orow + ch) = outv;
+      }
+    }
+    // the next item stages its first key tile over linloc
+    __syncthreads();
   }
 }
 
@@ -457,15 +493,19 @@ hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
     if ((int64_t)entries * batch * heads > INT32_MAX / 2) return hipErrorInvalidValue;
     const int total = entries * batch * heads;
     const int per_xcd = (total + kXcds - 1) / kXcds;
-    const dim3 grid(per_xcd * kXcds);
+    // local items per XCD: a contiguous run, or (counted lists) the entries
+    // e = xcd, xcd + 8, ... of every (image, head)
+    const int local = counts ? (entries + kXcds - 1) / kXcds * batch * heads : per_xcd;
+    const int wgs_per_xcd = std::min(local, kSparseWgsPerCu * kCusPerXcd);
+    const dim3 grid(wgs_per_xcd * kXcds);
     const bf16* q = static_cast<const bf16*>(qkv);
     const bf16* qh = static_cast<const bf16*>(qkv_hat);
     bf16* out = static_cast<bf16*>(o);
     switch (nqt) {
-      case 1: sparse_mfma_kernel<1><<<grid, 128, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd); break;
-      case 2: sparse_mfma_kernel<2><<<grid, 256, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd); break;
-      case 3: sparse_mfma_kernel<3><<<grid, 384, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd); break;
-      default: sparse_mfma_kernel<4><<<grid, 512, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd); break;
+      case 1: sparse_mfma_kernel<1><<<grid, 128, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd, wgs_per_xcd); break;
+      case 2: sparse_mfma_kernel<2><<<grid, 256, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd, wgs_per_xcd); break;
+      case 3: sparse_mfma_kernel<3><<<grid, 384, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd, wgs_per_xcd); break;
+      default: sparse_mfma_kernel<4><<<grid, 512, 0, s>>>(q, qh, sel, counts, wts, out, gh, gw, heads, block, window, lay, entries, total, per_xcd, wgs_per_xcd); break;
     }
     return hipGetLastError();
   }
