@@ -175,6 +175,23 @@ def algorithmic_work(name, wl, sel):
 MFMA_SITES = ("qkv_gemm", "out_proj", "out_proj_residual", "ffn1_gemm",
               "ffn2_gemm_residual", "sparse_softmax")
 
+# float32 FMA issue of the vector ALUs without packed instructions (which the
+# build switches off): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
+VALU_F32_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
+def alu_flops(name, wl):
+    """FMA flops the depthwise convolutions execute: the folded tap set
+    (kmax^2 taps per output for the module's branches, 9 for the FFN's
+    3x3; the GELU's instructions are not counted), or None."""
+    P, C = wl.batch * wl.tokens, wl.channels
+    if name == "dwconv_qkv":
+        kmax = max((1,) + tuple(wl.branches))
+        return 2 * 3 * C * P * kmax * kmax
+    if name == "ffn_dwconv_gelu":
+        return 2 * 4 * C * P * 9
+    return None
+
 
 def union_window_bytes(wl, sel):
     """S5's minimum HBM bytes: every token of the union of the selected
@@ -213,9 +230,17 @@ def roofline_entry(name, wl, sel, avg_ms, by=None):
         return dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_TFLOPS,
                     unit="TFLOP/s", frac=round(ach / MFMA_BF16_TFLOPS, 4),
                     traffic=None)
+    fa = alu_flops(name, wl)
+    if fa and fa / (VALU_F32_TFLOPS * 1e12) > t_hbm:
+        ach = fa / sec / 1e12
+        return dict(bound="alu", achieved=round(ach, 2), peak=round(VALU_F32_TFLOPS, 1),
+                    unit="TFLOP/s", frac=round(ach / VALU_F32_TFLOPS, 4), traffic=None,
+                    hbm_frac=round(by / sec / 1e9 / HBM_PEAK_GBS, 4))
     ach = by / sec / 1e9
     out = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
                unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+    if fa:
+        out["alu_frac"] = round(fa / sec / 1e12 / VALU_F32_TFLOPS, 4)
     if name in MFMA_SITES and fl:
         # matrix-core use at the same duration (flops / time / peak)
         out["mfma_frac"] = round(fl / sec / 1e12 / MFMA_BF16_TFLOPS, 4)
@@ -455,6 +480,8 @@ def main():
                 k["avg_us_step"] = round(avg * 1e3, 2)
             if by or fl:
                 k["roofline"] = roofline_entry(n, wl, sel, avg)
+                if block:  # the committed counters cover the headline block's launches
+                    k["roofline"]["traffic"] = measured_traffic(n)
             if n == "sparse_softmax":
                 ub = union_window_bytes(wl, sel)
                 k["union_bytes"] = int(ub)
