@@ -30,7 +30,13 @@ constexpr int kCusPerXcd = 32;
 // resident workgroups per CU of the MFMA kernel (45 KB of LDS each)
 constexpr int kSparseWgsPerCu = 3;
 
-// grid (entries, batch, heads); one thread per query of the block.
+// grid (entries, batch, heads); block^2 x G threads: thread (q, g) =
+// (tid % block^2, tid / block^2) takes query q and the window keys r with
+// r % G == g, keeping its own online-softmax state; the G states of a query
+// are merged at the end (maxima first, then the rescaled sums through LDS).
+// G = 1 is one thread per query.  Splitting the keys shortens each thread's
+// dependent chain of 32-term dot products G-fold: the kernel serves the
+// float32 path and large bf16 blocks, whose launches are small.
 template <typename T>
 __global__ __launch_bounds__(256) void sparse_valu_kernel(
     const T* __restrict__ qkv, const T* __restrict__ qkvh,
@@ -41,6 +47,7 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
   __shared__ float vs[kKT][kD];
   __shared__ float fks[kKT][kD];
   __shared__ float vhs[kKT][kD];
+  __shared__ float st_m[256], st_l[256], st_d[256];
   const int b = blockIdx.y, h = blockIdx.z;
   const int C = heads * kD, C3 = 3 * C;
   if (counts && (int)blockIdx.x >= counts[b * lay.cnt_b + h * lay.cnt_h])
@@ -58,9 +65,11 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
   const int nwin = (rhi - rlo) * wcols;
   const int nthr = blockDim.x;
   const int tid = threadIdx.x;
+  const int nq = block * block, G = nthr / nq;
+  const int qi = tid % nq, g = tid / nq;
   const size_t img = (size_t)b * gh * gw;
 
-  const int qn = (r0 + tid / block) * gw + c0 + tid % block;
+  const int qn = (r0 + qi / block) * gw + c0 + qi % block;
   const T* qrow = qkv + (img + qn) * C3 + h * kD;
   const T* qhrow = qkvh + (img + qn) * C3 + h * kD;
   const float scale = 1.f / sqrtf((float)kD);
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
       vhs[r][c] = to_f32(rowh[2 * C + c]);
     }
     __syncthreads();
-    for (int r = 0; r < cnt; ++r) {
+    for (int r = g; r < cnt; r += G) {
       float s = 0.f, a = 0.f;
 #pragma unroll
       for (int j = 0; j < kD; ++j) {
@@ -110,13 +119,59 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
     __syncthreads();
   }
 
+  // merge the G states of each query (in g order): the maxima, then the
+  // sums rescaled to the common maximum, the vectors through LDS (the key
+  // tiles are free now)
+  float L = l, Dn = den;
+  if (G > 1) {
+    st_m[tid] = m;
+    st_l[tid] = l;
+    st_d[tid] = den;
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int u = 0; u < G; ++u) mx = fmaxf(mx, st_m[qi + nq * u]);
+    L = 0.f;
+    Dn = 0.f;
+    for (int u = 0; u < G; ++u) {
+      const float mu = st_m[qi + nq * u];
+      L += mu == -INFINITY ? 0.f : st_l[qi + nq * u] * expf(mu - mx);
+      Dn += st_d[qi + nq * u];
+    }
+    const float c = m == -INFINITY ? 0.f : expf(m - mx);
+    float* buf = &ks[0][0];  // 64 x 32 floats: 256 threads x 8, per pass
+    static_assert(kKT * kD == 256 * 8, "merge buffer");
+    // unrolled, so every register index is static
+#pragma unroll
+    for (int part = 0; part < 2 * kD / 8; ++part) {  // 8 of the 64 values per pass
+      const bool is_num = part >= kD / 8;
+      const int j0 = (part % (kD / 8)) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        buf[tid * 8 + j] = is_num ? num[j0 + j] : acc[j0 + j] * c;
+      __syncthreads();
+      if (g == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float sm = 0.f;
+          for (int u = 0; u < G; ++u) sm += buf[(qi + nq * u) * 8 + j];
+          if (is_num)
+            num[j0 + j] = sm;
+          else
+            acc[j0 + j] = sm;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (g != 0) return;
+
   T* orow = o + (img + qn) * C + h * kD;
-  const float inv_l = 1.f / l;
-  const float inv_den = den > 0.f ? 1.f / den : 0.f;
+  const float inv_l = 1.f / L;
+  const float inv_den = Dn > 0.f ? 1.f / Dn : 0.f;
   const float w = wts ? wts[(size_t)b * (gh / block) * nbc + t] : 1.f;
 #pragma unroll
   for (int j = 0; j < kD; ++j) {
-    const float lin = den > 0.f ? num[j] * inv_den : 0.f;
+    const float lin = Dn > 0.f ? num[j] * inv_den : 0.f;
     const float v = wts ? fmaf(w, acc[j] * inv_l - lin, to_f32(orow[j]))
                         : to_f32(orow[j]) + acc[j] * inv_l - lin;
     orow[j] = from_f32<T>(v);
@@ -473,7 +528,12 @@ hipError_t run(const void* qkv, const void* qkvh, const int32_t* sel,
                int gh, int gw, int heads, int block, int window, int entries,
                SelLayout lay, hipStream_t s) {
   dim3 grid(entries, batch, heads);
-  sparse_valu_kernel<T><<<grid, block * block, 0, s>>>(
+  // key groups per query: as many as fit 256 threads, at most 16 (a
+  // power of two, so that block^2 x G divides into whole merge passes)
+  const int nq = block * block;
+  int G = 1;
+  while (G < 16 && nq * G * 2 <= 256) G *= 2;
+  sparse_valu_kernel<T><<<grid, nq * G, 0, s>>>(
       static_cast<const T*>(qkv), static_cast<const T*>(qkvh), sel, counts, wts,
       static_cast<T*>(o), gh, gw, heads, block, window, lay);
   return hipGetLastError();
