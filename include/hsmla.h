@@ -208,8 +208,10 @@ hsmla_status hsmla_linear_attn(const hsmla_desc* desc, const void* qkv_hat,
  * library (16 MiB per GPU, held from the library's load until the process
  * ends) instead of a caller workspace.  The call allocates nothing.  Sizes
  * whose partials exceed the array (hsmla_workspace_bytes(desc,
- * HSMLA_OP_LINEAR) > 16 MiB; e.g. bf16 batch * heads * ceil(N / 512) above
- * 3971) return HSMLA_ERR_SCRATCH before any launch.  Every call on one GPU
+ * HSMLA_OP_LINEAR) > 16 MiB; in bf16, batch * heads * chunks above 3971,
+ * chunks = ceil(N / 512) -- or ceil(N / 256), ceil(N / 128) for calls of
+ * fewer than 256 partial workgroups) return HSMLA_ERR_SCRATCH before any
+ * launch.  Every call on one GPU
  * uses that GPU's one array: calls that can overlap on a GPU (different
  * streams, or other threads) race and must be serialised by the caller.
  * The first call on each device looks up the array's address with that
