@@ -372,10 +372,13 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
   // workgroup shape allows; the gate then only forms the logits
   float* bsum = (!w->gate_dw && hsmla::dwconv_can_pool(D.kmax, D.Bs)) ? u.bsum
                                                                        : nullptr;
-  // with top-k routing the conv reduces the sums further, into the gate's
-  // partial logits, and the top-k launch forms the scores (no gate launch)
+  // the conv reduces the sums further, into the gate's partial logits: the
+  // top-k launch forms the scores itself (no gate launch), the other
+  // routings form them in one small launch
   const bool gate_parts = bsum && !D.soft && !D.thr && u.rankp &&
                           hsmla::gate_topk_from_parts_ok(D.T);
+  const bool gate_plog = bsum && hsmla::gate_topk_from_parts_ok(D.T) &&
+                         (gate_parts || D.soft || D.thr);
   switch (st) {
     case 0: {
       r.mark("qkv_gemm");
@@ -388,7 +391,7 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
       r.mark("dwconv_qkv");
       HSMLA_TRY(hsmla::launch_dwconv(D.bf, u.qkv, u.qkvh, u.taps, D.kmax, D.B, D.gh,
                                      D.gw, 3 * D.C, false, bsum, D.Bs, s, false,
-                                     gate_parts ? w->gate_w : nullptr, D.H));
+                                     gate_plog ? w->gate_w : nullptr, D.H));
       return HSMLA_OK;
     case 2:
       r.mark("kv_state");
@@ -403,7 +406,10 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
     case 4:
       if (gate_parts) return HSMLA_OK;  // scores formed with the selection
       r.mark("gate_scores");
-      if (bsum)
+      if (gate_plog)
+        HSMLA_TRY(hsmla::launch_gate_from_parts(bsum, w->gate_b, u.scores, u.hscores, D.B,
+                                                D.T, D.H, D.Bs, s));
+      else if (bsum)
         HSMLA_TRY(hsmla::launch_gate_from_sums(bsum, w->gate_w, w->gate_b,
                                                u.scores, u.hscores, D.B, D.T,
                                                D.H, D.Bs, s));

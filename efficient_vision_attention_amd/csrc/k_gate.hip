@@ -468,6 +468,32 @@ __global__ __launch_bounds__(1024) void gate_topk_direct_kernel(
   rank_select(shk, rank, nblocks, tpow, keep, sel + (size_t)b * keep);
 }
 
+// grid ceil(batch * nblocks / 16), 16 * heads threads: thread (block, h) =
+// (tid / heads, tid % heads) forms G^(h); the block's first thread then
+// adds its heads' values in head order, as score_from_parts does, so M_t
+// equals the top-k path's bit for bit.
+__global__ __launch_bounds__(1024) void gate_from_parts_kernel(
+    const float* __restrict__ plog, const float* __restrict__ gb, float* __restrict__ scores,
+    float* __restrict__ head_scores, int total, int heads, float inv_cnt) {
+  __shared__ float gs[1024];
+  const int blk = blockIdx.x * 16 + threadIdx.x / heads, h = threadIdx.x % heads;
+  const bool ok = blk < total;
+  float g = 0.f;
+  if (ok) {
+    const float* P = plog + (size_t)blk * 3 * heads;
+    const float p = ((P[h] + P[heads + h]) + P[2 * heads + h]) * inv_cnt;
+    g = 1.f / (1.f + expf(-(p + gb[h])));
+    if (head_scores) head_scores[(size_t)blk * heads + h] = g;
+  }
+  gs[threadIdx.x] = g;
+  __syncthreads();
+  if (ok && h == 0) {
+    float m = 0.f;
+    for (int u = 0; u < heads; ++u) m += gs[threadIdx.x + u];
+    scores[blk] = m / (float)heads;
+  }
+}
+
 // grid (batch), 1024 threads: rank(t) = sum of the runs' counts, then the
 // blocks of rank below keep in ascending order.
 __global__ __launch_bounds__(1024) void rank_final_kernel(const int32_t* __restrict__ part,
@@ -613,6 +639,17 @@ hipError_t launch_gate_topk_parts(const float* plog, const float* gate_b, float*
   rank_part_kernel<true><<<dim3(kRankParts, batch), tpow, 0, s>>>(
       plog, parts, nblocks, tpow, gate_b, heads, 1.f / (float)(block * block), scores);
   rank_final_kernel<<<batch, 1024, 0, s>>>(parts, sel, nblocks, keep, tpow);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_from_parts(const float* plog, const float* gate_b, float* scores,
+                                  float* head_scores, int batch, int nblocks, int heads,
+                                  int block, hipStream_t s) {
+  const int total = batch * nblocks;
+  if (total == 0) return hipSuccess;
+  if (heads > 64) return hipErrorInvalidValue;  // 16 blocks x heads threads
+  gate_from_parts_kernel<<<(total + 15) / 16, 16 * heads, 0, s>>>(
+      plog, gate_b, scores, head_scores, total, heads, 1.f / (float)(block * block));
   return hipGetLastError();
 }
 

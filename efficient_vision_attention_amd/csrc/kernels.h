@@ -133,6 +133,14 @@ bool gate_topk_from_parts_ok(int nblocks);
 hipError_t launch_gate_topk_parts(const float* plog, const float* gate_b, float* scores,
                                   int32_t* sel, int32_t* parts, int batch, int nblocks,
                                   int heads, int block, int keep, hipStream_t s);
+// The scores alone from the same partial logits (the threshold routings and
+// the soft mixture): M_t into scores and, when head_scores is not null,
+// G^(h)_t = sigmoid((plog[t][0][h] + plog[t][1][h] + plog[t][2][h]) /
+// block^2 + gate_b[h]) into head_scores [batch][blocks][heads]; the block
+// scores equal launch_gate_topk_parts' bit for bit.
+hipError_t launch_gate_from_parts(const float* plog, const float* gate_b, float* scores,
+                                  float* head_scores, int batch, int nblocks, int heads,
+                                  int block, hipStream_t s);
 hipError_t launch_topk(const float* scores, float* scores_copy, int32_t* sel,
                        int batch, int nblocks, int keep, hipStream_t s,
                        int32_t* parts = nullptr);

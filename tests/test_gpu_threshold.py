@@ -196,6 +196,27 @@ def test_threshold_equals_topk_between_kth_and_next():
         assert np.array_equal(thr[key], top[key]), key
 
 
+def test_threshold_equals_topk_from_partial_logits():
+    """The same with 256 blocks per image, where both routings form their
+    scores from the S2 conv's partial logits (top-k inside its ranking
+    launch, the threshold routing in a launch of its own, both adding the
+    heads' sigmoids in head order): scores, lists and forwards are bitwise
+    equal."""
+    wl = scaled(WORKLOADS["pathology"], batch=1, grid_h=128, grid_w=128)
+    assert wl.num_blocks == 256
+    inp = make_inputs(wl)
+    k = wl.keep_blocks
+    top = Run(wl, inp).forward()
+    s = np.sort(top["scores"][0].astype(np.float32))[::-1]
+    assert s[k - 1] > s[k], "k-th and (k+1)-th scores tie; pick another case"
+    tau = float(np.float32((np.float64(s[k - 1]) + np.float64(s[k])) / 2))
+    thr = Run(wl, inp, tau=tau).forward()
+    assert int(thr["counts"][0]) == k
+    np.testing.assert_array_equal(thr["sel"][0, :k], top["sel"][0, :k])
+    for key in ("scores", "o", "y"):
+        assert np.array_equal(thr[key], top[key]), key
+
+
 @pytest.mark.parametrize("name", ["tiny", "ragged_bf16"])
 def test_threshold_extremes(name):
     """tau above every score: nothing routed, o is the linear path; tau below
