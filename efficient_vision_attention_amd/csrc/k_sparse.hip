@@ -181,8 +181,10 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
 // ---------------------------------------------------------------------------
 // bfloat16 MFMA kernel
 //
-// Workgroup = one (selected block, head); 2 * nqt waves for nqt tiles of 32
-// queries.  Wave w works on query tile w % nqt along one of two paths:
+// A workgroup refines one (selected block, head) at a time (a grid of at
+// most three workgroups per CU walks the work items, see the kernel); 2 *
+// nqt waves for nqt tiles of 32 queries.  Wave w works on query tile
+// w % nqt along one of two paths:
 //   path 0 (softmax): S^T = K Q^T tile by tile, online softmax per query,
 //                     O_local^T += V^T P^T;
 //   path 1 (linear):  A^T = relu(K^) relu(Q^)^T, den += column sums,
