@@ -191,8 +191,8 @@ def test_block_forward_full_size_every_element():
     """The benchmark's block workload (keep 10%), each projection and the FFN
     checked on every element, stage-wise on the GPU's own inputs (FT 3.5
     block equation): qkv = LN1(x) W_qkv on every row (every output tile of
-    the projection's persistent tile loop), x1 = x + o W_o on every row, and
-    out = x1 + FFN(LN2(x1)) on every token from the GPU's x1."""
+    the projection), x1 = x + O W_o on every row, and out = x1 +
+    FFN(LN2(x1)) on every token from the GPU's x1."""
     wl = scaled(WORKLOADS["block"], keep=0.10)
     inp = make_inputs(wl)
     g = Run(wl, inp).block_forward()
@@ -209,3 +209,28 @@ def test_block_forward_full_size_every_element():
         del h1
         assert_close(g["out"][b:b + 1], rnd(x1 + h2 @ inp["w2"]), "bf16",
                      f"out image {b}, every token")
+
+
+def test_block_forward_full_size_every_element_attention():
+    """The same block workload, the attention stages on every element,
+    stage-wise on the GPU's own inputs (FT 3.1 and 3.3): Q^K^V^ = the
+    depthwise branches of the GPU's qkv on every token of both images, and
+    O = the linear readout of the GPU's Q^K^V^ with the GPU-selected blocks
+    refined (two-path residual over the window) on every token."""
+    wl = scaled(WORKLOADS["block"], keep=0.10)
+    inp = make_inputs(wl)
+    g = Run(wl, inp).block_forward()
+    rnd = O.round_bf16
+    C = wl.channels
+    for b in range(wl.batch):
+        ref = rnd(O.multiscale_branches(g["qkv"][b:b + 1], inp["dw"], wl.grid_h, wl.grid_w))
+        assert_close(g["qkv_hat"][b:b + 1], ref, "bf16", f"qkv_hat image {b}, every token")
+        del ref
+    Z, D = O.kv_state(g["qkv_hat"][..., C:2 * C], g["qkv_hat"][..., 2 * C:], wl.heads)
+    o_lin = rnd(O.linear_readout(g["qkv_hat"][..., :C], Z, D, wl.heads))
+    sel = g["sel"][:, :wl.keep_blocks]
+    np.testing.assert_array_equal(sel, O.select_blocks(g["scores"].astype(np.float32),
+                                                       wl.keep_blocks))
+    ref_o = O.refine_selected(g["qkv"], g["qkv_hat"], o_lin, sel, wl.grid_h, wl.grid_w,
+                              wl.heads, wl.block, wl.window, rnd=rnd)
+    assert_close(g["o"], ref_o, "bf16", "o, every token")
