@@ -83,6 +83,11 @@ def _ws_bytes(desc, op):
     (dict(branches=(9,)), -2),            # kernel > 7
     (dict(dtype=7), -3),
     (dict(batch=0), -2),
+    # maximum sizes: just past each limit of the header
+    (dict(channels=2080, heads=65), -2),                      # channels > 2048
+    (dict(grid_h=368, grid_w=368, window=8), -2),             # 92 x 92 blocks > 8192
+    (dict(batch=1024, grid_h=1024, grid_w=2048, block=16,     # 2^31 tokens in one call
+          window=16, keep_blocks=4), -2),
 ])
 def test_desc_validation(change, status):
     d = _desc(**{k: v for k, v in change.items() if k != "head_dim"})
@@ -90,6 +95,19 @@ def test_desc_validation(change, status):
         d.head_dim = change["head_dim"]
     st, _ = _ws_bytes(d, H.HSMLA_OP_FORWARD)
     assert st == status
+
+
+@pytest.mark.parametrize("change", [
+    dict(channels=2048, heads=64),                            # channels at the limit
+    dict(grid_h=512, grid_w=256, window=8),                   # 128 x 64 = 8192 blocks
+    dict(batch=511, grid_h=1024, grid_w=2048, block=16,       # just under 2^30 tokens
+         window=16, keep_blocks=4),
+])
+def test_desc_at_the_limits(change):
+    """Descriptors exactly at the header's size limits are accepted (the
+    workspace size is formed without overflow)."""
+    st, n = _ws_bytes(_desc(**change), H.HSMLA_OP_BLOCK)
+    assert st == 0 and n > 0
 
 
 def test_routing_validation():
