@@ -852,17 +852,21 @@ hipError_t launch_dwconv_gelu_planar(const void* in, void* out, const float* wef
                                      int gh, int gw, int ch, hipStream_t s) {
   if (!dwconv_planar_ok(true, batch, gh, gw, ch)) return hipErrorInvalidValue;
   constexpr DwCfg cf = dw_cfg(3, true);
-  constexpr int TW = dw_width(3, true);
+  // each staged row is one contiguous run here: two rows of loads in
+  // flight measured 1.5-2 us faster than three (which the row-major input
+  // needs).  Four output columns per thread (64-column tiles): each staged
+  // row serves twice the outputs per LDS read and the horizontal halo is
+  // half as wide (measured on the block's hidden tensor, 2 x 128x256 tokens
+  // x 1536 channels: 91.7 -> 87.0 us; 64-row strips 91.9 with two columns
+  // and 108 with four, where 384 workgroups leave CUs idle).
+  constexpr int kPlanarRows = 2, kPlanarCols = 4;
+  constexpr int TW = 256 / (cf.wc / cf.v) * kPlanarCols;
   const int col_tiles = (gw + TW - 1) / TW;
   const int ch_tiles = ch / cf.wc;
   const int strips = (gh + TH - 1) / TH;
   const int total = col_tiles * ch_tiles * strips * batch;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  // each staged row is one contiguous run here: two rows of loads in
-  // flight measured 1.5-2 us faster than three (which the row-major input
-  // needs)
-  constexpr int kPlanarRows = 2;
-  dwconv_lds<bf16, 3, true, cf.v, kPlanarRows, false, cf.wc, 2, cf.cx, true>
+  dwconv_lds<bf16, 3, true, cf.v, kPlanarRows, false, cf.wc, 2, kPlanarCols, true>
       <<<per_xcd * kXcds, 256, 0, s>>>(
           static_cast<const bf16*>(in), static_cast<bf16*>(out), weff, nullptr, 1, gh, gw, ch,
           col_tiles, ch_tiles, strips, total, per_xcd,
