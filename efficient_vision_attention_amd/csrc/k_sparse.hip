@@ -306,6 +306,19 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     const bool q_ok = ql < nq;
     const int qn = q_ok ? (r0 + ql / block) * gw + c0 + ql % block : 0;
 
+    // This query's O_lin values (read back and overwritten at the end):
+    // loaded now, so their latency overlaps the first key tile's instead of
+    // adding to the item's tail.  Every lane loads (lanes without a query
+    // read token 0's row, never used), so no load sits under a branch; no
+    // other work item writes these rows.
+    uint2 prev[4];
+    {
+      const bf16* orow = o + (img + qn) * C + h * kD;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        prev[j] = *reinterpret_cast<const uint2*>(orow + 8 * j + 4 * g);
+    }
+
     // B operand of S^T: this lane's query, channels 8g..8g+7 and 16+8g..
     bf16x8 qf[2];
     {
@@ -499,12 +512,11 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ch = 8 * j + 4 * g;
-        const uint2 prev = *reinterpret_cast<const uint2*>(orow + ch);
         float v[4];
-        v[0] = __uint_as_float(prev.x << 16);
-        v[1] = __uint_as_float(prev.x & 0xffff0000u);
-        v[2] = __uint_as_float(prev.y << 16);
-        v[3] = __uint_as_float(prev.y & 0xffff0000u);
+        v[0] = __uint_as_float(prev[j].x << 16);
+        v[1] = __uint_as_float(prev[j].x & 0xffff0000u);
+        v[2] = __uint_as_float(prev[j].y << 16);
+        v[3] = __uint_as_float(prev[j].y & 0xffff0000u);
         if (wts) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
