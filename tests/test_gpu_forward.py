@@ -196,6 +196,10 @@ _BLOCK_SHAPES = {
                       keep=0.25),
     "w128_b1": scaled(WORKLOADS["block"], name="bs128", batch=1, grid_h=24, grid_w=128,
                       keep=0.1),
+    # channel-planar FFN path with two 32-row strips, the second ragged (40
+    # rows), and eight 64-column conv tiles per row
+    "w512_h40": scaled(WORKLOADS["block"], name="bs512", batch=1, grid_h=40, grid_w=512,
+                       keep=0.1),
 }
 
 
