@@ -440,11 +440,13 @@ def main():
         """Average duration of every launch of one step, from HIP events
         recorded on the launch stream between the launches (the steps run
         back to back; the events are read after the last).  Each event
-        between two launches adds a short gap (about 2 us), so with step_ms
-        (the same step timed without events) every launch's share is also
-        scaled to that step time (avg_us_step): the figure the roofline
+        between two launches adds a gap of about the same length (2-3 us),
+        so with step_ms (the same step timed without events) the gaps'
+        total, the event-timed step minus step_ms, is taken off the
+        launches in equal parts (avg_us_step): the figure the roofline
         fractions use, and the one a kernel trace of the plain step
-        reproduces."""
+        reproduces (a proportional scaling instead charged the short
+        launches too much of the gaps)."""
         def timed(evs):
             if block:
                 return H.hsmla_block_forward_timed(bound.desc, bound.m.weights,
@@ -470,10 +472,10 @@ def main():
             hev.destroy(evs)
         kernels = {}
         total = sum(float(np.mean(v)) for v in per.values())
-        scale = step_ms / total if step_ms else 1.0
+        gap = (total - step_ms) / len(per) if step_ms else 0.0
         for n, v in per.items():
             raw = float(np.mean(v))
-            avg = raw * scale
+            avg = max(raw - gap, 0.5 * raw)
             by, fl = algorithmic_work(n, wl, sel)
             k = dict(avg_us=round(raw * 1e3, 2), bytes=int(by), flops=int(fl))
             if step_ms:
