@@ -152,6 +152,11 @@ def algorithmic_work(name, wl, sel):
         # the gate's partial logits (3 per head and block, formed by the S2
         # conv) in, scores and the selection out
         return wl.batch * wl.num_blocks * (3 * H * 4 + 8), 0
+    if name == "kv_state_gate_topk":
+        # the K/V state with the gate's top-k in its partial-sum launch
+        kb, kf = algorithmic_work("kv_state", wl, sel)
+        gb, _ = algorithmic_work("gate_topk", wl, sel)
+        return kb + gb, kf
     if name == "sparse_softmax":
         W = window_keys(sel, wl.grid_h, wl.grid_w, Bs, wl.window)
         q = Bs * Bs

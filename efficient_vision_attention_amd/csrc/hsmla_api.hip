@@ -394,6 +394,15 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
                                      gate_plog ? w->gate_w : nullptr, D.H));
       return HSMLA_OK;
     case 2:
+      if (gate_parts && D.bf) {
+        // the top-k runs in the partial-sum launch (it only reads the
+        // conv's outputs, like the K/V state)
+        r.mark("kv_state_gate_topk");
+        HSMLA_TRY(hsmla::launch_kv_state_topk(u.qkvh, u.kv, u.ksum, u.part, D.B, D.N, D.H, s,
+                                              D.Bk, bsum, w->gate_b, u.scores, u.sel, u.rankp,
+                                              D.T, D.Bs, D.k));
+        return HSMLA_OK;
+      }
       r.mark("kv_state");
       HSMLA_TRY(hsmla::launch_kv_state(D.bf, u.qkvh, u.kv, u.ksum, u.part, D.B,
                                        D.N, D.H, s, D.Bk));
@@ -429,6 +438,7 @@ hsmla_status module_stage(int st, const Dims& D, const hsmla_desc* d,
         HSMLA_TRY(hsmla::launch_threshold(u.scores, nullptr, u.sel, u.counts, D.B,
                                           D.T, D.tau, s));
       } else if (gate_parts) {
+        if (D.bf) return HSMLA_OK;  // selected in the K/V-state launch
         r.mark("gate_topk");
         HSMLA_TRY(hsmla::launch_gate_topk_parts(bsum, w->gate_b, u.scores, u.sel, u.rankp,
                                                 D.B, D.T, D.H, D.Bs, D.k, s));

@@ -20,6 +20,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "gate_select.h"
 #include "kernels.h"
 
 namespace hsmla {
@@ -225,60 +226,6 @@ __global__ __launch_bounds__(1024) void gate_scores_conv_kernel(
             head_scores ? head_scores + ((size_t)b * nblocks + t) * heads : nullptr);
 }
 
-// Workgroup-wide stream compaction (any multiple of 64 threads up to
-// 1024): writes every t in [0, n) with keep(t) to out[0 ..) in ascending
-// order and returns the number written (same value in every thread).  The
-// slot of a kept t is the number of kept entries below it: a wave ballot
-// gives the rank inside the wave, a prefix over the wave totals the offset
-// of the wave.
-template <typename Pred>
-__device__ int compact_ascending(Pred keep, int n, int32_t* __restrict__ out) {
-  __shared__ int wave_tot[16];
-  __shared__ int base_all;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  if (threadIdx.x == 0) base_all = 0;
-  __syncthreads();
-  for (int t0 = 0; t0 < n; t0 += blockDim.x) {
-    const int t = t0 + threadIdx.x;
-    const bool k = t < n && keep(t);
-    const uint64_t m = __ballot(k);
-    const int below = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tot[wave] = __popcll(m);
-    __syncthreads();
-    int off = base_all;
-    for (int w2 = 0; w2 < wave; ++w2) off += wave_tot[w2];
-    if (k) out[off + below] = t;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int tot = 0;
-      for (int w2 = 0; w2 < nwaves; ++w2) tot += wave_tot[w2];
-      base_all += tot;
-    }
-    __syncthreads();
-  }
-  return base_all;
-}
-
-// grid (batch), 1024 threads.  The scores of one image are sorted in LDS by
-// a bitonic network on one 64-bit key per block: the score mapped to an
-// order-preserving unsigned integer (-0 taken as +0) in the high word and
-// the complement of the block index in the low word, sorted descending --
-// score descending, then block index ascending, a total order.  The first
-// `keep` entries are therefore exactly the blocks whose rank
-// #{u : s_u > s_t or (s_u == s_t and u < t)} is below keep; they are
-// flagged and written out in ascending order by the ballot compaction.  The
-// row is padded to a power of two with key 0, which sorts after every real
-// entry.  O(T log^2 T) comparisons; exact and order-independent.  Up to
-// 1024 blocks the rank is counted directly instead (same keys, same
-// result): T^2 comparisons in one pass cost less than the sort's
-// log^2 T / 2 barrier-separated stages.
-__device__ __forceinline__ uint64_t topk_key(float v, int t) {
-  uint32_t u = __float_as_uint(v + 0.f);  // -0 -> +0
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(u) << 32) | (0xffffffffu - static_cast<uint32_t>(t));
-}
-
 // Top-k of one image by counting ranks (tpow <= blockDim keys): shk[0 ..
 // tpow) holds the keys (padding 0), rank[] has room for tpow ints.  rank(t)
 // = #{u : key_u > key_t}, the keys being distinct; the key range is split
@@ -314,6 +261,19 @@ __device__ void rank_select(const uint64_t* shk, int* rank, int nblocks, int tpo
   compact_ascending([&](int u) { return rank[u] < keep; }, nblocks, sel);
 }
 
+// grid (batch), 1024 threads.  The scores of one image are sorted in LDS by
+// a bitonic network on one 64-bit key per block: the score mapped to an
+// order-preserving unsigned integer (-0 taken as +0) in the high word and
+// the complement of the block index in the low word, sorted descending --
+// score descending, then block index ascending, a total order.  The first
+// `keep` entries are therefore exactly the blocks whose rank
+// #{u : s_u > s_t or (s_u == s_t and u < t)} is below keep; they are
+// flagged and written out in ascending order by the ballot compaction.  The
+// row is padded to a power of two with key 0, which sorts after every real
+// entry.  O(T log^2 T) comparisons; exact and order-independent.  Up to
+// 1024 blocks the rank is counted directly instead (same keys, same
+// result): T^2 comparisons in one pass cost less than the sort's
+// log^2 T / 2 barrier-separated stages.
 __global__ __launch_bounds__(1024) void topk_kernel(
     const float* __restrict__ scores, float* __restrict__ scores_copy,
     int32_t* __restrict__ sel, int nblocks, int keep, int tpow) {
@@ -370,39 +330,9 @@ __global__ __launch_bounds__(1024) void topk_kernel(
 }
 
 // The same ranks over more CUs (up to 1024 blocks): grid (kRankParts,
-// batch), tpow threads.  Workgroup s counts, for every block t of its
-// image, the keys of run s (tpow / kRankParts keys) above key_t and writes
-// part[b][s][t]; rank_final_kernel adds the runs and compacts.  The counts
-// are exact integers, so the ranks equal rank_select's.
-// With FROM_PARTS the scores are first formed from the gate's partial
-// logits (plog[b][t][s][h], see launch_dwconv): M_t = mean_h sigmoid((P_0 +
-// P_1 + P_2) inv_cnt + b_h); workgroup 0 of each image stores them.
-constexpr int kRankParts = 8;
-__device__ __forceinline__ float score_from_parts(const float* __restrict__ P,
-                                                  const float* __restrict__ gb, int heads,
-                                                  float inv_cnt) {
-  float m = 0.f;
-  if (heads % 4 == 0) {  // 16-byte loads of the three rows (16-byte aligned)
-    for (int h = 0; h < heads; h += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(P + h);
-      const float4 k = *reinterpret_cast<const float4*>(P + heads + h);
-      const float4 v = *reinterpret_cast<const float4*>(P + 2 * heads + h);
-      const float pa[4] = {a.x, a.y, a.z, a.w}, pk[4] = {k.x, k.y, k.z, k.w},
-                  pv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float p = ((pa[q] + pk[q]) + pv[q]) * inv_cnt;
-        m += 1.f / (1.f + expf(-(p + gb[h + q])));
-      }
-    }
-  } else {
-    for (int h = 0; h < heads; ++h) {
-      const float p = ((P[h] + P[heads + h]) + P[2 * heads + h]) * inv_cnt;
-      m += 1.f / (1.f + expf(-(p + gb[h])));
-    }
-  }
-  return m / (float)heads;
-}
+// batch), tpow threads, workgroup s counting run s (rank_part_wg);
+// rank_final_kernel adds the runs and compacts.  The counts are exact
+// integers, so the ranks equal rank_select's.
 template <bool FROM_PARTS>
 __global__ __launch_bounds__(1024) void rank_part_kernel(const float* __restrict__ scores,
                                                          int32_t* __restrict__ part,
@@ -411,33 +341,8 @@ __global__ __launch_bounds__(1024) void rank_part_kernel(const float* __restrict
                                                          int heads, float inv_cnt,
                                                          float* __restrict__ scores_out) {
   __shared__ uint64_t keys[1024 / kRankParts];
-  const int s = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int len = tpow / kRankParts;
-  auto score = [&](int u) {
-    if constexpr (FROM_PARTS)
-      return score_from_parts(scores + ((size_t)b * nblocks + u) * 3 * heads, gb, heads,
-                              inv_cnt);
-    else
-      return scores[(size_t)b * nblocks + u];
-  };
-  for (int i = t; i < len; i += blockDim.x) {
-    const int u = s * len + i;
-    keys[i] = u < nblocks ? topk_key(score(u), u) : 0;
-  }
-  float st = 0.f;
-  if (t < nblocks) st = score(t);
-  if (FROM_PARTS && s == 0 && t < nblocks) scores_out[(size_t)b * nblocks + t] = st;
-  const uint64_t kt = t < nblocks ? topk_key(st, t) : ~0ull;
-  __syncthreads();
-  int cnt = 0;
-  for (int i = 0; i < len; i += 16) {  // len is a multiple of 16
-    uint64_t v[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = keys[i + q];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) cnt += v[q] > kt;
-  }
-  if (t < nblocks) part[((size_t)b * kRankParts + s) * tpow + t] = cnt;
+  rank_part_wg<FROM_PARTS>(scores, part, nblocks, tpow, gb, heads, inv_cnt, scores_out,
+                           blockIdx.x, blockIdx.y, keys);
 }
 
 // Up to kDirectTopk blocks per image the same scores and ranks in one
@@ -495,20 +400,12 @@ __global__ __launch_bounds__(1024) void gate_from_parts_kernel(
 }
 
 // grid (batch), 1024 threads: rank(t) = sum of the runs' counts, then the
-// blocks of rank below keep in ascending order.
+// blocks of rank below keep in ascending order (rank_final_wg).
 __global__ __launch_bounds__(1024) void rank_final_kernel(const int32_t* __restrict__ part,
                                                           int32_t* __restrict__ sel,
                                                           int nblocks, int keep, int tpow) {
   __shared__ int rank[1024];
-  const int b = blockIdx.x;
-  for (int t = threadIdx.x; t < nblocks; t += blockDim.x) {
-    int r = 0;
-#pragma unroll
-    for (int q = 0; q < kRankParts; ++q) r += part[((size_t)b * kRankParts + q) * tpow + t];
-    rank[t] = r;
-  }
-  __syncthreads();
-  compact_ascending([&](int u) { return rank[u] < keep; }, nblocks, sel + (size_t)b * keep);
+  rank_final_wg(part, sel, nblocks, keep, tpow, blockIdx.x, rank);
 }
 
 // grid (batch), 1024 threads: sel[b][0 .. n) = ascending blocks with

@@ -9,6 +9,7 @@
 // head); stage 2 adds the chunk partials in chunk order, so the result does
 // not depend on scheduling (no float atomics).
 #include "common.h"
+#include "gate_select.h"
 #include "kernels.h"
 
 namespace hsmla {
@@ -68,14 +69,12 @@ __global__ __launch_bounds__(256) void kv_partial_kernel(
 // workgroup's 64 per group of 64 threads; group q adds chunks
 // [q nc/4, (q+1) nc/4) in chunk order, then the four group sums are added in
 // group order (a fixed association: bitwise reproducible).
-__global__ __launch_bounds__(256) void kv_combine_kernel(
-    const float* __restrict__ part, float* __restrict__ kv,
-    float* __restrict__ ksum, int nchunks) {
+__device__ void kv_combine_body(const float* __restrict__ part, float* __restrict__ kv,
+                                float* __restrict__ ksum, int nchunks, int bh, int grp) {
   __shared__ float red[4][64];
-  const int bh = blockIdx.x;
   const float* p = part + (size_t)bh * nchunks * kPart;
   const int t = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int e = blockIdx.y * 64 + t;
+  const int e = grp * 64 + t;
   const int c0 = (nchunks * q) / 4, c1 = (nchunks * (q + 1)) / 4;
   float s = 0.f;
   if (e < kPart) {
@@ -106,6 +105,14 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(
     else
       ksum[(size_t)bh * kD + (e - kD * kD)] = s;
   }
+}
+
+constexpr int kCombineGroups = (kPart + 63) / 64;  // entry groups per (image, head)
+
+__global__ __launch_bounds__(256) void kv_combine_kernel(
+    const float* __restrict__ part, float* __restrict__ kv,
+    float* __restrict__ ksum, int nchunks) {
+  kv_combine_body(part, kv, ksum, nchunks, blockIdx.x, blockIdx.y);
 }
 
 // grid (ceil(tokens/64), heads, batch), 64 threads: one token per thread.
@@ -208,11 +215,10 @@ __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, (i16x2){0, 0}));
 }
 
-__global__ __launch_bounds__(256) void kv_partial_mfma(
-    const bf16* __restrict__ qkvh, float* __restrict__ part, int tokens,
-    int heads, int nchunks, int chunk_tok) {
+__device__ void kv_partial_body(const bf16* __restrict__ qkvh, float* __restrict__ part,
+                                int tokens, int heads, int nchunks, int chunk_tok, int chunk,
+                                int hg, int b) {
   __shared__ __attribute__((aligned(16))) char ts[2][kTT * kKvRowB];
-  const int chunk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = hg * kHG + wave;  // h >= heads: stages, computes nothing kept
   const int C = heads * kD, C3 = 3 * C;
@@ -296,6 +302,59 @@ __global__ __launch_bounds__(256) void kv_partial_mfma(
     out[i * kD + col] = z[r];
   }
   if (g == 0) out[kD * kD + col] = dacc;
+}
+
+__global__ __launch_bounds__(256) void kv_partial_mfma(
+    const bf16* __restrict__ qkvh, float* __restrict__ part, int tokens,
+    int heads, int nchunks, int chunk_tok) {
+  kv_partial_body(qkvh, part, tokens, heads, nchunks, chunk_tok, blockIdx.x, blockIdx.y,
+                  blockIdx.z);
+}
+
+// The K/V state with the gate's top-k beside it (FT 3.2 selection; both
+// only read the S2 conv's outputs), in the same two launches: the selection
+// is latency-bound work of a few workgroups, which then overlaps the
+// bandwidth-bound reduction instead of taking launches of its own.
+// Launch 1: workgroups 0 .. batch * kRankParts - 1 count the rank runs of
+// the gate's scores formed from its partial logits (rank_part_wg, run
+// bid % kRankParts of image bid / kRankParts), the others are the
+// partial-sum workgroups of kv_partial_mfma, numbered chunk fastest, then
+// head group, then image.
+__global__ __launch_bounds__(256) void kv_partial_rank_kernel(
+    const bf16* __restrict__ qkvh, float* __restrict__ part, int tokens, int heads,
+    int nchunks, int chunk_tok, int batch, const float* __restrict__ plog,
+    const float* __restrict__ gb, float* __restrict__ scores, int32_t* __restrict__ rankp,
+    int nblocks, int tpow, float inv_cnt) {
+  __shared__ uint64_t keys[1024 / kRankParts];
+  const int bid = blockIdx.x;
+  if (bid < batch * kRankParts) {
+    rank_part_wg<true>(plog, rankp, nblocks, tpow, gb, heads, inv_cnt, scores,
+                       bid % kRankParts, bid / kRankParts, keys);
+    return;
+  }
+  const int w = bid - batch * kRankParts;
+  const int hgs = (heads + kHG - 1) / kHG;
+  kv_partial_body(qkvh, part, tokens, heads, nchunks, chunk_tok, w % nchunks,
+                  (w / nchunks) % hgs, w / (nchunks * hgs));
+}
+
+// Launch 2: workgroups 0 .. batch - 1 add the runs and write each image's
+// ascending list (rank_final_wg; the ranks are exact counts, so the list
+// equals the gate's own top-k launches'), the others combine the chunk
+// partials as kv_combine_kernel: workgroup w takes entry group
+// w % kCombineGroups of (image, head) w / kCombineGroups.
+__global__ __launch_bounds__(256) void kv_combine_final_kernel(
+    const float* __restrict__ part, float* __restrict__ kv, float* __restrict__ ksum,
+    int nchunks, int batch, const int32_t* __restrict__ rankp, int32_t* __restrict__ sel,
+    int nblocks, int keep, int tpow) {
+  __shared__ int rank[1024];
+  const int bid = blockIdx.x;
+  if (bid < batch) {
+    rank_final_wg(rankp, sel, nblocks, keep, tpow, bid, rank);
+    return;
+  }
+  const int w = bid - batch;
+  kv_combine_body(part, kv, ksum, nchunks, w / kCombineGroups, w % kCombineGroups);
 }
 
 // O^T = Z^T relu(Q^)^T with Z split into bf16 hi + lo parts, normalised by
@@ -468,8 +527,31 @@ hipError_t launch_kv_state(bool bf, const void* qkv_hat, float* kv,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 cgrid(batch * heads, (kPart + 63) / 64);
+  dim3 cgrid(batch * heads, kCombineGroups);
   kv_combine_kernel<<<cgrid, 256, 0, s>>>(partials, kv, ksum, chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_state_topk(const void* qkv_hat, float* kv, float* ksum, float* partials,
+                                int batch, int tokens, int heads, hipStream_t s,
+                                int chunk_batch, const float* plog, const float* gate_b,
+                                float* scores, int32_t* sel, int32_t* rankp, int nblocks,
+                                int block, int keep) {
+  if (chunk_batch <= 0) chunk_batch = batch;
+  if (chunk_batch < batch || nblocks <= 0 || !rankp) return hipErrorInvalidValue;
+  int tpow = 2;
+  while (tpow < nblocks) tpow <<= 1;
+  if (tpow < 16 * kRankParts || tpow > 1024) return hipErrorInvalidValue;
+  const int chunks = kv_chunks(true, chunk_batch, heads, tokens);
+  const int hgs = (heads + kHG - 1) / kHG;
+  kv_partial_rank_kernel<<<batch * kRankParts + chunks * hgs * batch, 256, 0, s>>>(
+      static_cast<const bf16*>(qkv_hat), partials, tokens, heads, chunks,
+      kv_chunk_tokens(chunk_batch, heads, tokens), batch, plog, gate_b, scores, rankp, nblocks,
+      tpow, 1.f / (float)(block * block));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  kv_combine_final_kernel<<<batch + batch * heads * kCombineGroups, 256, 0, s>>>(
+      partials, kv, ksum, chunks, batch, rankp, sel, nblocks, keep, tpow);
   return hipGetLastError();
 }
 

@@ -100,6 +100,16 @@ hipError_t launch_kv_state(bool bf, const void* qkv_hat, float* kv,
                            float* ksum, float* partials, int batch, int tokens,
                            int heads, hipStream_t s, int chunk_batch = 0);
 
+// launch_kv_state (bfloat16) with the gate's top-k from its partial logits
+// in the same two launches (as launch_gate_topk_parts: scores and the
+// ascending list of the keep best blocks of each image; rankp as its parts,
+// 128 .. 1024 blocks per image, see gate_topk_from_parts_ok).
+hipError_t launch_kv_state_topk(const void* qkv_hat, float* kv, float* ksum, float* partials,
+                                int batch, int tokens, int heads, hipStream_t s,
+                                int chunk_batch, const float* plog, const float* gate_b,
+                                float* scores, int32_t* sel, int32_t* rankp, int nblocks,
+                                int block, int keep);
+
 // o = relu(q_hat) Z / (relu(q_hat) . D), zero when the denominator is 0.
 hipError_t launch_lin_apply(bool bf, const void* qkv_hat, const float* kv,
                             const float* ksum, void* o, int batch, int tokens,
