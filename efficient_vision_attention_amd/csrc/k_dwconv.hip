@@ -248,6 +248,7 @@ constexpr int kStreamV = 2, kStreamCols = 4, kStreamRows = 1;
 // C = 256, 384 workgroups, 51.8 -> 45.8 us with strips of 8 rows; 8 x
 // 128x128 at C = 128, 768 workgroups, 59.9 -> 70.8 us with 16 rows).
 constexpr int kMinStrip = TH / 4, kStreamMinWgs = 512;
+constexpr int kCus = 256;  // compute units of an MI355X
 // LDS-staged kernel (up to 3x3): output columns per thread.
 constexpr int kLdsCols = 2;
 
@@ -278,16 +279,28 @@ __global__ __launch_bounds__(256) void dwconv_stream(
     const T* __restrict__ in, T* __restrict__ out,
     const float* __restrict__ weff, float* __restrict__ bsum, int block,
     int gh, int gw, int ch, int col_tiles, int ch_tiles, int strips,
-    int total, int per_xcd, const float* __restrict__ gate_w, int heads) {
+    int total, int per_xcd, const float* __restrict__ gate_w, int heads, int nwhole) {
   constexpr int R = (K - 1) / 2;
   constexpr int CG = kStreamChannels / V;  // channel groups per workgroup
   constexpr int TT = 256 / CG;             // column groups per workgroup
   constexpr int TW = TT * CX;              // columns per workgroup
   constexpr int KL = K + CX - 1;           // input columns per thread
   __shared__ float red[POOL ? SH / kPoolMinBlock : 1][POOL ? TT : 1][POOL ? kStreamChannels : 1];
+  // Tiles [0, nwhole) run whole, on the first per_xcd * 8 workgroups
+  // (XCD-remapped); each later tile runs as two half-height strips, on one
+  // workgroup each, after them (see run_dw).
   const int bid = blockIdx.x;
-  const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
-  if (tile >= total) return;
+  int tile, y_off = 0, y_len = SH;
+  if (bid < per_xcd * kXcds) {
+    tile = (bid % kXcds) * per_xcd + bid / kXcds;
+    if (tile >= nwhole) return;
+  } else {
+    const int j = bid - per_xcd * kXcds;
+    tile = nwhole + j / 2;
+    if (tile >= total) return;
+    y_off = (j % 2) * (SH / 2);
+    y_len = SH / 2;
+  }
   int rest = tile;
   const int col_t = rest % col_tiles;
   rest /= col_tiles;
@@ -301,7 +314,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
   const int x = col_t * TW + tx * CX;
   const int c = ch_t * kStreamChannels + tc * V;
   const bool c_ok = c < ch;
-  const int y0 = strip * SH;
+  const int y0 = strip * SH + y_off;
   const size_t img = (size_t)b * gh * gw;
 
   // Taps: in registers, or (TL) in LDS, read at every use -- the lanes of
@@ -352,7 +365,7 @@ __global__ __launch_bounds__(256) void dwconv_stream(
 #pragma unroll
   for (int j = 0; j < V; ++j) psum[j] = 0.f;
 
-  const int y_end = min(gh, y0 + SH);
+  const int y_end = min(gh, y0 + y_len);
   const int r_begin = y0 - R, r_end = y_end + R;
 
   // Row loads through a buffer resource over the workgroup's in-grid
@@ -774,15 +787,28 @@ hipError_t run_dw(const void* in, void* out, const float* weff, float* bsum,
       constexpr int SH = decltype(sh_c)::value;
       const int st = (gh + SH - 1) / SH;
       const int tot = col_tiles * ch_tiles * st * batch;
-      const int px = (tot + kXcds - 1) / kXcds;
+      // The conv is bound by VALU issue and every workgroup of a launch is
+      // resident at once (five per CU), so a CU's time is its workgroups'
+      // total work.  Where the tiles are a whole number of workgroups per
+      // CU plus at most half a round (the block's 1152 on 256 CUs: half
+      // the CUs would run five, half four), the remainder tiles run as two
+      // half-height strips each, one more per CU: every CU then runs four
+      // whole tiles and one half.  Outputs are summed in the same order
+      // whatever the strip, and pooled block rows stay inside a half strip.
+      const int rem = tot % kCus;
+      const bool halves = rem > 0 && 2 * rem <= kCus && (SH / 2) % (bsum ? block : 1) == 0 &&
+                          SH / 2 >= kMinStrip;
+      const int nwhole = halves ? tot - rem : tot;
+      const int px = (nwhole + kXcds - 1) / kXcds;
+      const int grid = px * kXcds + 2 * (tot - nwhole);
       if (bsum && !GELU)
-        dwconv_stream<T, K, false, cf.v, cf.p, true, cf.tl, cf.cx, SH><<<px * kXcds, 256, 0, s>>>(
+        dwconv_stream<T, K, false, cf.v, cf.p, true, cf.tl, cf.cx, SH><<<grid, 256, 0, s>>>(
             static_cast<const T*>(in), static_cast<T*>(out), weff, bsum, block, gh,
-            gw, ch, col_tiles, ch_tiles, st, tot, px, gate_w, heads);
+            gw, ch, col_tiles, ch_tiles, st, tot, px, gate_w, heads, nwhole);
       else
-        dwconv_stream<T, K, GELU, cf.v, cf.p, false, cf.tl, cf.cx, SH><<<px * kXcds, 256, 0, s>>>(
+        dwconv_stream<T, K, GELU, cf.v, cf.p, false, cf.tl, cf.cx, SH><<<grid, 256, 0, s>>>(
             static_cast<const T*>(in), static_cast<T*>(out), weff, nullptr, 1, gh,
-            gw, ch, col_tiles, ch_tiles, st, tot, px, nullptr, 0);
+            gw, ch, col_tiles, ch_tiles, st, tot, px, nullptr, 0, nwhole);
     };
     if (sh == TH)
       go(std::integral_constant<int, TH>{});
