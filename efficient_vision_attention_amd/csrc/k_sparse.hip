@@ -27,8 +27,9 @@ constexpr int kD = 32;
 constexpr int kKT = 64;  // window keys staged per LDS tile
 constexpr int kXcds = 8;
 constexpr int kCusPerXcd = 32;
-// resident workgroups per CU of the MFMA kernel (45 KB of LDS each)
-constexpr int kSparseWgsPerCu = 3;
+// resident workgroups per CU of the MFMA kernel (22.5 KB of LDS and one wave
+// of at most 128 VGPRs per SIMD each)
+constexpr int kSparseWgsPerCu = 4;
 
 // grid (entries, batch, heads); block^2 x G threads: thread (q, g) =
 // (tid % block^2, tid / block^2) takes query q and the window keys r with
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
 // bfloat16 MFMA kernel
 //
 // A workgroup refines one (selected block, head) at a time (a grid of at
-// most three workgroups per CU walks the work items, see the kernel); 2 *
+// most four workgroups per CU walks the work items, see the kernel); 2 *
 // nqt waves for nqt tiles of 32 queries.  Wave w works on query tile
 // w % nqt along one of two paths:
 //   path 0 (softmax): S^T = K Q^T tile by tile, online softmax per query,
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
 // 16 lanes, lane j receives element j % 4 of the four 16-bit values that
 // lane 4e + j / 4 addresses, e = 0..3; so when lane k addresses channels
 // f0 + 4 (k % 4) .. + 3 of key t0 + k / 4, lane j receives channel f0 + j of
-// keys t0 .. t0 + 3).  Keys are streamed in tiles of 64 through
+// keys t0 .. t0 + 3).  Keys are streamed in tiles of 32 through
 // double-buffered LDS.  Path 1 hands its normalised result to path 0 through LDS, and path 0
 // writes O_lin + O_local - O_linloc.
 // ---------------------------------------------------------------------------
@@ -206,7 +207,10 @@ __global__ __launch_bounds__(256) void sparse_valu_kernel(
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int KT = 64;            // keys per LDS tile
+// keys per LDS tile: 32 keys (two buffers, 22.5 KB) let four workgroups
+// share a CU where 64 (45 KB) allowed three (measured on the block
+// workload: keep 50% 102.3 -> 99.2 us, keep 10% unchanged)
+constexpr int KT = 32;
 constexpr int KS = kD + 8;        // bf16 stride of K rows (80 bytes)
 constexpr int VS = kD + 16;       // bf16 stride of V rows (96 bytes: a transposing
                                   // read's four 32-byte pieces in distinct banks)
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
   float (*linloc)[kD + 1] = reinterpret_cast<float (*)[kD + 1]>(&tiles[0]);
 
   // Work items (image b, list entry e, head h), walked by a grid of at most
-  // three workgroups per CU; workgroup blockIdx.x runs on XCD
+  // four workgroups per CU; workgroup blockIdx.x runs on XCD
   // blockIdx.x % 8 and takes that XCD's local items lw, lw + wgs_per_xcd, ...
   // Fixed-length lists: each XCD takes a contiguous run of items numbered
   // with h fastest, so the heads of a block (which share the cache lines of
@@ -332,16 +336,17 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
       }
     }
 
-    // tile loader: 64 keys x (K, K^, V, V^) x 32 channels = 1024 chunks of 8.
+    // tile loader: KT keys x (K, K^, V, V^) x 32 channels = 16 KT chunks of 8.
     // Loads are unconditional (keys past the window re-read its last key and
     // are zeroed when staged), so no load sits under a branch and the wait
     // before staging covers exactly one tile.  Each chunk keeps a pointer to
     // its tensor's head slice in the image and the 32-bit element offset of its
-    // key's token, both formed once: a tile advances every key by 64 window
+    // key's token, both formed once: a tile advances every key by KT window
     // positions, i.e. a fixed offset step plus one row's wrap when its column
     // passes the window's edge (the launcher keeps an image's offsets below
     // 2^31 elements).
-    constexpr int kLoads = (1024 + NT - 1) / NT;
+    constexpr int kChunks = KT * 16;  // KT keys x 4 tensors x 4 chunks of 8
+    constexpr int kLoads = (kChunks + NT - 1) / NT;
     __builtin_assume(tid < NT);
     uint4 stg[kLoads];
     const int step_r = KT / wcols, step_c = KT % wcols;
@@ -353,9 +358,9 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     const bf16* kptr[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int cidx = min(tid + NT * i, 1023);
-      const int tensor = cidx >> 8;      // 0 K, 1 K^, 2 V, 3 V^
-      const int key = (cidx >> 2) & 63, cg = cidx & 3;
+      const int cidx = min(tid + NT * i, kChunks - 1);
+      const int tensor = cidx / (KT * 4);  // 0 K, 1 K^, 2 V, 3 V^
+      const int key = (cidx >> 2) % KT, cg = cidx & 3;
       const int kr = key / wcols;
       kc[i] = key % wcols;
       koff[i] = (uint32_t)(((rlo + kr) * gw + clo + kc[i]) * C3);
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
     auto issue = [&](int w0) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        const int key = (min(tid + NT * i, 1023) >> 2) & 63;
+        const int key = (min(tid + NT * i, kChunks - 1) >> 2) % KT;
         stg[i] = *reinterpret_cast<const uint4*>(kptr[i] + (w0 + key < nwin ? koff[i] : off_last));
         // advance to the same key of the next tile
         koff[i] += d_off;
@@ -381,9 +386,9 @@ __global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int cidx = tid + NT * i;
-        if (cidx >= 1024) break;
-        const int tensor = cidx >> 8;
-        const int key = (cidx >> 2) & 63, cg = cidx & 3;
+        if (cidx >= kChunks) break;
+        const int tensor = cidx / (KT * 4);
+        const int key = (cidx >> 2) % KT, cg = cidx & 3;
         uint4 u = stg[i];
         if (!whole && w0 + key >= nwin) u = uint4{0, 0, 0, 0};
         if (tensor == 0) {
