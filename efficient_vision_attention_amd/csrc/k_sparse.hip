@@ -237,8 +237,14 @@ __device__ __forceinline__ uint4 relu_bf16x8(uint4 u) {
   return uint4{relu_bf16x2(u.x), relu_bf16x2(u.y), relu_bf16x2(u.z), relu_bf16x2(u.w)};
 }
 
+// The two-query-tile form (8x8 blocks, the workloads' shape) is compiled for
+// five waves per SIMD (at most 102 VGPRs; the compiler spills a few values
+// to scratch) so that five workgroups share a CU: on the block workload at
+// keep 10%, 1248 work items then fit in one round of 1280 workgroups
+// (28.1 -> 26.5 us; keep 50% unchanged).  The other forms keep four.
 template <int NQT>
-__global__ __launch_bounds__(64 * 2 * NQT) void sparse_mfma_kernel(
+__global__ __launch_bounds__(64 * 2 * NQT)
+__attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ qkvh,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ counts,
     const float* __restrict__ wts, bf16* __restrict__ o, int gh, int gw,
@@ -575,7 +581,8 @@ hipError_t launch_sparse(bool bf, const void* qkv, const void* qkv_hat,
     // local items per XCD: a contiguous run, or (counted lists) the entries
     // e = xcd, xcd + 8, ... of every (image, head)
     const int local = counts ? (entries + kXcds - 1) / kXcds * batch * heads : per_xcd;
-    const int wgs_per_xcd = std::min(local, kSparseWgsPerCu * kCusPerXcd);
+    const int per_cu = nqt == 2 ? kSparseWgsPerCu + 1 : kSparseWgsPerCu;
+    const int wgs_per_xcd = std::min(local, per_cu * kCusPerXcd);
     const dim3 grid(wgs_per_xcd * kXcds);
     const bf16* q = static_cast<const bf16*>(qkv);
     const bf16* qh = static_cast<const bf16*>(qkv_hat);
