@@ -355,13 +355,18 @@ hsmla_status hsmla_block_forward_split(const hsmla_desc* desc,
                                        void* join_event);
 
 /* Same work, kernels and stream order as hsmla_forward /
- * hsmla_block_forward, plus an event recorded on `stream` before each kernel
- * launch and one after the last, for per-kernel timing by the caller.
+ * hsmla_block_forward, plus an event recorded on `stream` before each
+ * launch step and one after the last, for per-step timing by the caller.
+ * A step is one kernel launch or two dependent ones under one name: the
+ * K/V state ("kv_state": partial sums, then their combine; in bfloat16 runs
+ * with top-k routing "kv_state_gate_topk", whose two launches also rank the
+ * gate's scores and write the block lists) and the top-k ("gate_topk" or
+ * "topk") where it runs on its own.
  * events: n_events hipEvent_t handles created by the caller; names
  * (nullable): receives a static name per recorded event ("end" for the
- * last).  *n_launches receives the number of kernel launches L; events
- * 0..L are recorded when n_events >= L + 1, otherwise only the first
- * n_events and HSMLA_ERR_ARG is returned after the work is enqueued. */
+ * last).  *n_launches receives the number of steps L; events 0..L are
+ * recorded when n_events >= L + 1, otherwise only the first n_events and
+ * HSMLA_ERR_ARG is returned after the work is enqueued. */
 hsmla_status hsmla_forward_timed(const hsmla_desc* desc,
                                  const hsmla_weights* w, const void* x,
                                  void* y, void* ws, size_t ws_bytes,
