@@ -81,6 +81,11 @@ _GATE_PARTS = {
     "exact_gate_T192": scaled(WORKLOADS["street"], name="gpx", batch=2, grid_h=48,
                               grid_w=64, channels=96, heads=3, block=4, window=10,
                               keep=0.2, gate_conv=True),
+    # the lower end (72 blocks: runs of 16 keys) over three images, whose
+    # rank workgroups precede the K/V partial-sum workgroups in one launch
+    "blocks72_b3": scaled(WORKLOADS["street"], name="gp72", batch=3, grid_h=24,
+                          grid_w=48, channels=64, heads=2, block=4, window=8,
+                          keep=0.25),
 }
 
 
