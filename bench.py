@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the street / CT / pathology / tiny module runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power-s", type=float, default=1.0,
+                    help="seconds of back-to-back steps over which board power "
+                         "and the shader clock are sampled")
     ap.add_argument("--cpu-rows", type=int, default=64,
                     help="token rows of the one-image crop the CPU oracle is "
                          "timed on")
@@ -361,6 +364,66 @@ def probes(torch):
     return out
 
 
+class PowerSampler:
+    """Board power (hwmon power1_input, W) and the shader clock level
+    (pp_dpm_sclk, MHz) sampled every few ms on a host thread while the GPU
+    runs; None where the sensors cannot be read."""
+
+    def __init__(self):
+        import glob
+        self.pw = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+        self.cap = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_cap"))
+        self.sclk = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+        self._stop = False
+
+    def _read(self):
+        row = [None, None]
+        try:
+            row[0] = int(open(self.pw[0]).read()) / 1e6
+        except (OSError, IndexError, ValueError):
+            pass
+        try:
+            cur = [l for l in open(self.sclk[0]).read().splitlines() if l.endswith("*")]
+            row[1] = int(cur[0].split(":")[1].strip().split("M")[0]) if cur else None
+        except (OSError, IndexError, ValueError):
+            pass
+        return row
+
+    def __enter__(self):
+        import threading
+
+        def loop():
+            while not self._stop:
+                self.samples.append(self._read())
+                time.sleep(0.004)
+        self._t = threading.Thread(target=loop, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop = True
+        self._t.join()
+
+    def summary(self):
+        w = [r[0] for r in self.samples if r[0] is not None]
+        c = [r[1] for r in self.samples if r[1] is not None]
+        cap = None
+        try:
+            cap = int(open(self.cap[0]).read()) / 1e6
+        except (OSError, IndexError, ValueError):
+            pass
+        if not w and not c:
+            return None
+        # the second half of the window: the clocks have settled by then
+        w, c = w[len(w) // 2:], c[len(c) // 2:]
+        return {"board_w_mean": round(float(np.mean(w)), 1) if w else None,
+                "cap_w": cap,
+                "sclk_mhz_median": float(np.median(c)) if c else None,
+                "samples": len(w) or len(c),
+                "window": "back-to-back headline steps after the timed ones"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -508,6 +571,18 @@ def main():
         ms = time_steps(lambda: head.block(x), args.steps, args.warmup)
         ms_alt = time_steps(lambda: head.block_split(x, two), args.steps, args.warmup)
     ms_plain = time_steps(lambda: plain.block(x), args.steps, args.warmup)
+    # board power and clock over a second of back-to-back headline steps
+    # (the sensor averages over a window, so a short burst under-reads it),
+    # with that window's own step time beside them
+    with PowerSampler() as power:
+        torch.cuda.synchronize()
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < args.power_s:
+            for _ in range(20):
+                head.block(x)
+            torch.cuda.synchronize()
+            n += 20
+        steady_ms = (time.perf_counter() - t0) / max(n, 1) * 1e3
     tokens = base.batch * base.tokens
     head.block(x)
     torch.cuda.synchronize()
@@ -689,6 +764,8 @@ def main():
         "kernels": kernels,
         "selection_gap": gaps,
         "probes": probe,
+        "power": dict(power.summary() or {}, steady_ms_per_step=round(steady_ms, 4),
+                      seconds=args.power_s),
         "configs": configs,
         "sweep": sweep,
         "cpu_baseline": cpu,
