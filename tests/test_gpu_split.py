@@ -30,6 +30,11 @@ SPLIT_CASES = {
     "block_b2_soft": (scaled(_B, batch=2, grid_h=24, grid_w=40), {"soft": True}),
     "block_b2_exact_gate": (scaled(_B, batch=2, grid_h=24, grid_w=40,
                                    branches=(3, 5, 7), gate_conv=True), {}),
+    # 160 blocks per image: the gate's top-k runs inside the K/V-state
+    # launches of each image range
+    "block_b3_ranked": (scaled(_B, name="block_ranked", batch=3, grid_h=40,
+                               grid_w=64, channels=96, heads=3, block=4,
+                               window=10, keep=0.15), {}),
     "block_f32": (scaled(_B, name="block_f32", batch=2, grid_h=12, grid_w=28,
                          channels=96, heads=3, dtype="f32", block=4, window=10,
                          keep=0.4), {}),
