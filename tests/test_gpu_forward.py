@@ -107,6 +107,22 @@ def test_topk_over_workgroups(name):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("grid,block,window", [(4, 4, 8), (8, 8, 16)])
+def test_single_block_images(dtype, grid, block, window):
+    """Images of a single block (T = 1) with it selected: the gate ranks one
+    score, the refinement's window is the whole image, and the forward
+    matches the oracle end to end."""
+    wl = scaled(WORKLOADS["street"], name=f"one{grid}", batch=2, grid_h=grid, grid_w=grid,
+                channels=64, heads=2, block=block, window=window, keep=1.0, dtype=dtype)
+    assert wl.num_blocks == 1 and wl.keep_blocks == 1
+    inp = make_inputs(wl)
+    announce(f"hsmla_forward single-block images {dtype} {grid}x{grid}")
+    g = Run(wl, inp).forward()
+    _check_module(wl, inp, g)
+    assert np.array_equal(g["sel"][:, :1], np.zeros((2, 1), np.int32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_keep_all_covering_window_is_full_softmax(dtype):
     """Every block refined with a window covering the grid: the linear terms
     cancel and the module output is softmax attention over raw Q, K, V."""
