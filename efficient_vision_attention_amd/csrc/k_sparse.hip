@@ -16,6 +16,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -241,7 +242,10 @@ __device__ __forceinline__ uint4 relu_bf16x8(uint4 u) {
 // five waves per SIMD (at most 102 VGPRs; the compiler spills a few values
 // to scratch) so that five workgroups share a CU: on the block workload at
 // keep 10%, 1248 work items then fit in one round of 1280 workgroups
-// (28.1 -> 26.5 us; keep 50% unchanged).  The other forms keep four.
+// (28.1 -> 26.5 us; keep 50% unchanged).  The other forms keep four.  Two
+// key tiles are in flight; the item's O_lin rows are read at its end (read
+// with the queries, they cost the registers of the second tile: 26.7 ->
+// 26.1 us at keep 10%, 98.1 -> 95.6 at keep 50%).
 template <int NQT>
 __global__ __launch_bounds__(64 * 2 * NQT)
 __attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
@@ -316,19 +320,6 @@ __attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
     const bool q_ok = ql < nq;
     const int qn = q_ok ? (r0 + ql / block) * gw + c0 + ql % block : 0;
 
-    // This query's O_lin values (read back and overwritten at the end):
-    // loaded now, so their latency overlaps the first key tile's instead of
-    // adding to the item's tail.  Every lane loads (lanes without a query
-    // read token 0's row, never used), so no load sits under a branch; no
-    // other work item writes these rows.
-    uint2 prev[4];
-    {
-      const bf16* orow = o + (img + qn) * C + h * kD;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        prev[j] = *reinterpret_cast<const uint2*>(orow + 8 * j + 4 * g);
-    }
-
     // B operand of S^T: this lane's query, channels 8g..8g+7 and 16+8g..
     bf16x8 qf[2];
     {
@@ -354,7 +345,7 @@ __attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
     constexpr int kChunks = KT * 16;  // KT keys x 4 tensors x 4 chunks of 8
     constexpr int kLoads = (kChunks + NT - 1) / NT;
     __builtin_assume(tid < NT);
-    uint4 stg[kLoads];
+    uint4 stg[2][kLoads];  // two tiles in flight: tile t in set t % 2
     const int step_r = KT / wcols, step_c = KT % wcols;
     const uint32_t d_off = (uint32_t)((step_r * gw + step_c) * C3);
     const uint32_t wrap_off = (uint32_t)((gw - wcols) * C3);
@@ -372,11 +363,12 @@ __attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
       koff[i] = (uint32_t)(((rlo + kr) * gw + clo + kc[i]) * C3);
       kptr[i] = ((tensor & 1) ? qkvh : qkv) + img * C3 + (tensor < 2 ? 1 : 2) * C + h * kD + 8 * cg;
     }
-    auto issue = [&](int w0) {
+    auto issue = [&](auto set_c, int w0) {
+      constexpr int set = decltype(set_c)::value;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int key = (min(tid + NT * i, kChunks - 1) >> 2) % KT;
-        stg[i] = *reinterpret_cast<const uint4*>(kptr[i] + (w0 + key < nwin ? koff[i] : off_last));
+        stg[set][i] = *reinterpret_cast<const uint4*>(kptr[i] + (w0 + key < nwin ? koff[i] : off_last));
         // advance to the same key of the next tile
         koff[i] += d_off;
         kc[i] += step_c;
@@ -386,7 +378,8 @@ __attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
         }
       }
     };
-    auto commit = [&](int buf, int w0) {
+    auto commit = [&](auto set_c, int buf, int w0) {
+      constexpr int set = decltype(set_c)::value;
       SparseTile& T = tiles[buf];
       const bool whole = w0 + KT <= nwin;  // uniform: no key past the window
 #pragma unroll
@@ -395,7 +388,7 @@ __attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
         if (cidx >= kChunks) break;
         const int tensor = cidx / (KT * 4);
         const int key = (cidx >> 2) % KT, cg = cidx & 3;
-        uint4 u = stg[i];
+        uint4 u = stg[set][i];
         if (!whole && w0 + key >= nwin) u = uint4{0, 0, 0, 0};
         if (tensor == 0) {
           *reinterpret_cast<uint4*>(&T.k[key * KS + 8 * cg]) = u;
@@ -415,13 +408,23 @@ __attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
     float run_sum = 0.f;        // this lane's share of the column sum
     const float sc = 1.4426950408889634f / sqrtf((float)kD);  // log2(e)/sqrt(d)
 
+    // Two tiles in flight: while tile it is computed from LDS buffer it % 2,
+    // tiles it + 1 and it + 2 load into the two register sets; after the
+    // compute, tile it + 1 is staged into the other buffer and tile it + 3
+    // issued into the set it leaves.  Issues past the window re-read its
+    // last key (in bounds, never staged), so none sits under a branch.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
     const int ntiles = (nwin + KT - 1) / KT;
-    issue(0);
-    commit(0, 0);
+    issue(S0{}, 0);
+    issue(S1{}, KT);
+    commit(S0{}, 0, 0);
+    issue(S0{}, 2 * KT);
     __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < ntiles) issue((it + 1) * KT);
+    auto step = [&](auto par_c, int it) {
+      constexpr int par = decltype(par_c)::value;  // it % 2
+      using Next = std::integral_constant<int, 1 - par>;
+      const int buf = par;
       const SparseTile& T = tiles[buf];
       const bf16* kmat = path == 0 ? T.k : T.kh;
       const bf16* vmat = path == 0 ? T.v : T.vh;
@@ -502,8 +505,15 @@ __attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
         }
       }
       // tiles[buf ^ 1] was last read before the previous barrier
-      if (it + 1 < ntiles) commit(buf ^ 1, (it + 1) * KT);
+      if (it + 1 < ntiles) commit(Next{}, buf ^ 1, (it + 1) * KT);
+      issue(Next{}, (it + 3) * KT);
       __syncthreads();
+    };
+    // in pairs, so that the register sets are static; a step past the last
+    // tile computes and stages nothing
+    for (int it = 0; it < ntiles; it += 2) {
+      step(S0{}, it);
+      step(S1{}, it + 1);
     }
 
     // column totals over both lane groups
@@ -523,11 +533,12 @@ __attribute__((amdgpu_waves_per_eu(NQT == 2 ? 5 : 4))) void sparse_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ch = 8 * j + 4 * g;
+        const uint2 pv = *reinterpret_cast<const uint2*>(orow + ch);
         float v[4];
-        v[0] = __uint_as_float(prev[j].x << 16);
-        v[1] = __uint_as_float(prev[j].x & 0xffff0000u);
-        v[2] = __uint_as_float(prev[j].y << 16);
-        v[3] = __uint_as_float(prev[j].y & 0xffff0000u);
+        v[0] = __uint_as_float(pv.x << 16);
+        v[1] = __uint_as_float(pv.x & 0xffff0000u);
+        v[2] = __uint_as_float(pv.y << 16);
+        v[3] = __uint_as_float(pv.y & 0xffff0000u);
         if (wts) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
